@@ -1,0 +1,208 @@
+"""CPU oracle of the sparse MoE FFN layer forward (test infrastructure).
+
+Only the tests, ``__graft_entry__.smoke()`` and the benchmark's CPU-baseline
+leg may import this package.  The arithmetic lives in ``moe_oracle.c`` (plain
+C, double accumulation); this module only marshals numpy arrays through
+ctypes.  It shares nothing with the HIP path.
+
+Array conventions: fp32 arrays are ``np.float32``; bfloat16 arrays are the
+raw bit patterns as ``np.uint16``.  torch CPU tensors are accepted and viewed
+the same way.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "moe_oracle.c")
+_LIB = os.path.join(_HERE, "libmoe_oracle.so")
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FP contraction)."""
+    if force or not os.path.exists(_LIB):
+        cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+               "-shared", "-fPIC", "-Wall", "-o", _LIB + ".tmp", _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(_LIB + ".tmp", _LIB)
+    return _LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB):
+            build(force=True)
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        i32, i64, f32, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
+        L.oracle_num_threads.restype = i32
+        L.oracle_capacity.argtypes = [i64, i64, i64, f64]
+        L.oracle_capacity.restype = i64
+        L.oracle_router_logits.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        L.oracle_scores.argtypes = [i32, i32, P, P, f32, P]
+        L.oracle_topk.argtypes = [i32, i32, i32, P, P, P]
+        L.oracle_dispatch.argtypes = [i32, i32, i32, i64, i32, f32, P, P] + [P] * 12
+        L.oracle_ffn_rows.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P]
+        L.oracle_layer_tokens.argtypes = [i32, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
+        L.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        for f in (L.oracle_router_logits, L.oracle_scores, L.oracle_topk, L.oracle_dispatch,
+                  L.oracle_ffn_rows, L.oracle_layer_tokens, L.oracle_combine):
+            f.restype = None
+        _lib = L
+    return _lib
+
+
+def _np(a):
+    """numpy view of an array-like; torch bf16 becomes its uint16 bits."""
+    if a is None:
+        return None
+    if not isinstance(a, np.ndarray):
+        import torch  # only for tensors handed in by a caller
+        if isinstance(a, torch.Tensor):
+            t = a.detach().cpu().contiguous()
+            if t.dtype == torch.bfloat16:
+                return t.view(torch.int16).numpy().view(np.uint16)
+            return t.numpy()
+        a = np.asarray(a)
+    return np.ascontiguousarray(a)
+
+
+def _dt(a: np.ndarray) -> int:
+    if a.dtype == np.float32:
+        return 0
+    if a.dtype == np.uint16:
+        return 1
+    raise TypeError(f"oracle element type must be float32 or bf16 bits, got {a.dtype}")
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads() -> int:
+    return lib().oracle_num_threads()
+
+
+def capacity(T: int, k: int, E: int, cf: float) -> int:
+    return int(lib().oracle_capacity(T, k, E, float(np.float32(cf))))
+
+
+def router_logits(x, wr, bias=None) -> np.ndarray:
+    x, wr = _np(x), _np(wr)
+    bias = None if bias is None else _np(bias).astype(np.float32)
+    T, d = x.shape
+    E = wr.shape[0]
+    assert wr.shape == (E, d) and x.dtype == wr.dtype
+    raw = np.empty((T, E), np.float32)
+    lib().oracle_router_logits(T, d, E, _dt(x), _p(x), _p(wr), _p(bias), _p(raw))
+    return raw
+
+
+def scores(raw, load=None, lam: float = 0.0) -> np.ndarray:
+    raw = _np(raw).astype(np.float32)
+    load = None if load is None else _np(load).astype(np.float32)
+    T, E = raw.shape
+    s = np.empty_like(raw)
+    lib().oracle_scores(T, E, _p(raw), _p(load), float(np.float32(lam)), _p(s))
+    return s
+
+
+def topk(s, K: int):
+    s = _np(s).astype(np.float32)
+    T, E = s.shape
+    cand = np.empty((T, K), np.int32)
+    cs = np.empty((T, K), np.float32)
+    lib().oracle_topk(T, E, K, _p(s), _p(cand), _p(cs))
+    return cand, cs
+
+
+def route(raw, k: int, load=None, lam: float = 0.0):
+    """Scores and top-(k+1) candidates from fp32 router logits."""
+    s = scores(raw, load, lam)
+    return topk(s, k + 1)
+
+
+def dispatch(cand, cand_score, E: int, k: int, C: int, reroute: int = 1, aux_coef: float = 0.01) -> dict:
+    cand = _np(cand).astype(np.int32)
+    cs = _np(cand_score).astype(np.float32)
+    T = cand.shape[0]
+    assert cand.shape == (T, k + 1) and cs.shape == (T, k + 1)
+    cap_rows = min(T * k, E * C)
+    o = dict(
+        eid=np.empty((T, k), np.int32), pos=np.empty((T, k), np.int32),
+        flag=np.empty((T, k), np.uint8), row=np.empty((T, k), np.int32),
+        gate=np.empty((T, k), np.float32), gate64=np.empty((T, k), np.float64),
+        offsets=np.empty(E + 1, np.int32), token_of_row=np.empty(max(cap_rows, 0), np.int32),
+        demand=np.empty(E, np.int32), kept=np.empty(E, np.int32),
+        totals=np.empty(3, np.int32), aux_loss=np.empty(1, np.float32),
+    )
+    lib().oracle_dispatch(T, E, k, C, int(reroute), float(np.float32(aux_coef)), _p(cand), _p(cs),
+                          _p(o["eid"]), _p(o["pos"]), _p(o["flag"]), _p(o["row"]), _p(o["gate"]),
+                          _p(o["gate64"]), _p(o["offsets"]), _p(o["token_of_row"]),
+                          _p(o["demand"]), _p(o["kept"]), _p(o["totals"]), _p(o["aux_loss"]))
+    return o
+
+
+def ffn_rows(expert, src, x, w1, w3, w2, want_h: bool = False):
+    """y[i] = FFN_{expert[i]}(x[src[i]]) in double; optionally the SwiGLU h."""
+    expert = _np(expert).astype(np.int32)
+    src = _np(src).astype(np.int32)
+    x, w1, w3, w2 = _np(x), _np(w1), _np(w3), _np(w2)
+    E, d_ff, d = w1.shape
+    assert w3.shape == w1.shape and w2.shape == (E, d, d_ff) and x.shape[1] == d
+    assert x.dtype == w1.dtype == w3.dtype == w2.dtype
+    n = expert.shape[0]
+    y = np.empty((n, d), np.float64)
+    h = np.empty((n, d_ff), np.float64) if want_h else None
+    lib().oracle_ffn_rows(n, _p(expert), _p(src), d, d_ff, _dt(x), _p(x), _p(w1), _p(w3), _p(w2),
+                          _p(y), _p(h))
+    return (y, h) if want_h else y
+
+
+def layer_tokens(tokens, x, w1, w3, w2, eid, gate64) -> np.ndarray:
+    """Layer output rows (double) for the listed tokens, from a routing."""
+    tokens = _np(tokens).astype(np.int32)
+    x, w1, w3, w2 = _np(x), _np(w1), _np(w3), _np(w2)
+    eid = _np(eid).astype(np.int32)
+    gate64 = _np(gate64).astype(np.float64)
+    E, d_ff, d = w1.shape
+    k = eid.shape[1]
+    n = tokens.shape[0]
+    y = np.empty((n, d), np.float64)
+    lib().oracle_layer_tokens(n, _p(tokens), k, d, d_ff, _dt(x), _p(x), _p(w1), _p(w3), _p(w2),
+                              _p(eid), _p(gate64), _p(y))
+    return y
+
+
+def combine(row, gate, y_rows) -> np.ndarray:
+    row = _np(row).astype(np.int32)
+    gate = _np(gate).astype(np.float32)
+    y_rows = _np(y_rows)
+    T, k = row.shape
+    d = y_rows.shape[1]
+    y = np.empty((T, d), np.float64)
+    lib().oracle_combine(T, k, d, _dt(y_rows), _p(row), _p(gate), _p(y_rows), _p(y))
+    return y
+
+
+def forward(x, wr, bias, w1, w3, w2, E: int, k: int, cf: float, load=None, lam: float = 0.0,
+            reroute: int = 1, aux_coef: float = 0.01, raw=None) -> dict:
+    """The whole layer.  `raw` replaces the oracle's own router logits (parity
+    mode: the oracle routes from the same fp32 logits as the device)."""
+    x = _np(x)
+    T = x.shape[0]
+    if raw is None:
+        raw = router_logits(x, wr, bias)
+    cand, cs = route(raw, k, load, lam)
+    C = capacity(T, k, E, cf)
+    disp = dispatch(cand, cs, E, k, C, reroute, aux_coef)
+    y = layer_tokens(np.arange(T, dtype=np.int32), x, w1, w3, w2, disp["eid"], disp["gate64"])
+    out = dict(raw=raw, cand=cand, cand_score=cs, C=C, y=y)
+    out.update(disp)
+    return out

@@ -1,0 +1,398 @@
+/*
+ * moe_oracle.c -- plain, slow CPU oracle of the sparse Mixture-of-Experts FFN
+ * layer forward pass.
+ *
+ * TEST INFRASTRUCTURE.  Only the tests, the smoke check and the benchmark's
+ * CPU-baseline leg may load this library.  It shares no code, header, table or
+ * helper with the HIP path (the package under sparse_mixture_experts_gemm_amd/).
+ *
+ * Precision: every dot product is accumulated in double; the penalised score
+ * and the top-k order are taken in fp32 because the routing decision must be
+ * reproduced bit for bit from the same fp32 router logits.
+ *
+ * Sources (the five web pages on MoE sparse activation):
+ *   P1 "GPT-4稀疏激活真相：万亿参数模型的MoE工程落地实践"
+ *   P2 "MoE架构揭秘：逐Token路由与活跃参数量的工程真相"
+ *   P3 "MoE稀疏激活原理与工程实践：从2%激活率到高效推理"
+ *   P5 the page at 2kiu.com whose body covers the router and expert capacity
+ * Where the pages leave a step open, the reading taken is stated at the step.
+ *
+ * Element types: dt = 0 means fp32 elements, dt = 1 means bfloat16 bit
+ * patterns (uint16), widened exactly to float.
+ *
+ * Parity status: every function below is pinned by a CPU test (worked values
+ * printed on the pages, closed forms, brute force, or special cases that reduce
+ * to a textbook routine).  None is "parity unpinned".
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+static double elem(const void *p, size_t i, int dt)
+{
+    if (dt == 0)
+        return (double)((const float *)p)[i];
+    uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Expert capacity.  Reading: C = ceil(T*k/E * cf) evaluated in double in that
+ * order (the expert_capacity formula of P2 §5.2, which gives 2 for 64 experts,
+ * top-2, batch 32 and factor 1.3).  cf <= 0 means uncapped.  C never exceeds T:
+ * an expert can receive at most one request per token.
+ */
+int64_t oracle_capacity(int64_t T, int64_t k, int64_t E, double cf)
+{
+    if (cf <= 0.0)
+        return T;
+    double c = ceil((double)T * (double)k / (double)E * cf);
+    int64_t C = (int64_t)c;
+    if (C > T)
+        C = T;
+    if (C < 0)
+        C = 0;
+    return C;
+}
+
+/*
+ * Router logits: raw[t][e] = fp32(sum_i x[t][i] * Wr[e][i]) + bias[e]
+ * (P2 §3.1: z = h . W_router with one weight vector per expert; a per-expert
+ * bias added to the gate, as in the router-bias discussion of the page at
+ * adg.csdn.net §3.1).  Wr is stored [E][d].  bias may be NULL.
+ */
+void oracle_router_logits(int T, int d, int E, int dt, const void *x, const void *wr,
+                          const float *bias, float *raw)
+{
+    for (int t = 0; t < T; t++)
+        for (int e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int i = 0; i < d; i++)
+                acc += elem(x, (size_t)t * d + i, dt) * elem(wr, (size_t)e * d + i, dt);
+            float r = (float)acc;
+            if (bias)
+                r = r + bias[e];
+            raw[(size_t)t * E + e] = r;
+        }
+}
+
+/*
+ * Load-aware penalty (P1 §2.3: score_i = raw_i - lambda * load_i).  Taken as
+ * one fused multiply-add in fp32, fmaf(-lambda, load, raw), so that both sides
+ * round once.  load == NULL means no penalty (s = raw).
+ */
+void oracle_scores(int T, int E, const float *raw, const float *load, float lambda, float *s)
+{
+    for (int t = 0; t < T; t++)
+        for (int e = 0; e < E; e++) {
+            size_t i = (size_t)t * E + e;
+            s[i] = load ? fmaf(-lambda, load[e], raw[i]) : raw[i];
+        }
+}
+
+/*
+ * Ranked candidates (P2 §3.1: softmax, then the top-2 indices).  Softmax is
+ * monotone, so ranking by the fp32 score s is the same order without the
+ * rounding of exp; ties go to the lower expert index.  K columns are produced
+ * (k chosen experts plus the fallback candidate); ranks >= E are -1 with score
+ * -inf.
+ */
+void oracle_topk(int T, int E, int K, const float *s, int32_t *cand, float *cand_score)
+{
+    unsigned char *taken = (unsigned char *)malloc((size_t)E);
+    for (int t = 0; t < T; t++) {
+        const float *st = s + (size_t)t * E;
+        memset(taken, 0, (size_t)E);
+        for (int r = 0; r < K; r++) {
+            int best = -1;
+            for (int e = 0; e < E; e++) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || st[e] > st[best])
+                    best = e;
+            }
+            cand[(size_t)t * K + r] = best;
+            cand_score[(size_t)t * K + r] = best >= 0 ? st[best] : -INFINITY;
+            if (best >= 0)
+                taken[best] = 1;
+        }
+    }
+    free(taken);
+}
+
+/*
+ * Capacity-capped dispatch.
+ *
+ * Queue semantics (P1 §2.3: an expert whose queue has reached the limit sends
+ * the token to its third-ranked candidate; P5 §2: once an expert is full, later
+ * tokens go to the next-best expert; P2 §3.3: overflow is dropped or
+ * re-routed).  Readings taken where the pages are open:
+ *   - arrival order is rank-major: every token's rank-0 choice in token order,
+ *     then every rank-1 choice, ..., then one fallback round in token order;
+ *   - a token with at least one overflowed slot sends its lowest-rank
+ *     overflowed slot to its rank-k candidate (the third-ranked expert for
+ *     top-2); any further overflowed slot is dropped;
+ *   - rows are packed per expert in arrival order; offsets is the exclusive
+ *     scan of the kept counts.
+ * Gates: the softmax of the chosen scores renormalised over the kept slots
+ * (P2 §3.1 uses softmax probabilities p1, p2); a dropped slot gets 0.
+ * Load-balancing loss: aux_coef * sum_e (demand[e] / T)^2 with demand the
+ * pre-cap rank < k selections (the balance loss of the MoELayer example in P3
+ * §4.2, whose usage is normalised by the token count).
+ *
+ * cand, cand_score: [T][k+1].  Outputs eid, pos, row: [T][k] (-1 when dropped);
+ * flag [T][k]: 0 kept, 1 re-routed, 2 dropped; gate [T][k] (fp32) and gate64
+ * (double, may be NULL); offsets [E+1]; token_of_row [min(T*k, E*C)] (-1 past
+ * the last row); demand, kept [E]; totals = {rows, dropped, rerouted}.
+ */
+void oracle_dispatch(int T, int E, int k, int64_t C, int reroute, float aux_coef,
+                     const int32_t *cand, const float *cand_score,
+                     int32_t *eid, int32_t *pos, uint8_t *flag, int32_t *row, float *gate,
+                     double *gate64, int32_t *offsets, int32_t *token_of_row,
+                     int32_t *demand, int32_t *kept, int32_t *totals, float *aux_loss)
+{
+    const int K = k + 1;
+    int64_t *fill = (int64_t *)calloc((size_t)E, sizeof(int64_t));
+    int *src_rank = (int *)malloc((size_t)T * k * sizeof(int));
+
+    for (int e = 0; e < E; e++)
+        demand[e] = 0;
+    for (int t = 0; t < T; t++)
+        for (int r = 0; r < k; r++)
+            demand[cand[(size_t)t * K + r]]++;
+
+    /* primary rounds */
+    for (int r = 0; r < k; r++)
+        for (int t = 0; t < T; t++) {
+            size_t j = (size_t)t * k + r;
+            int e = cand[(size_t)t * K + r];
+            src_rank[j] = r;
+            if (fill[e] < C) {
+                eid[j] = e;
+                pos[j] = (int32_t)fill[e]++;
+                flag[j] = 0;
+            } else {
+                eid[j] = -1;
+                pos[j] = -1;
+                flag[j] = 2;
+            }
+        }
+
+    /* fallback round */
+    if (reroute && k < E)
+        for (int t = 0; t < T; t++) {
+            int rs = -1;
+            for (int r = 0; r < k; r++)
+                if (flag[(size_t)t * k + r] == 2) {
+                    rs = r;
+                    break;
+                }
+            if (rs < 0)
+                continue;
+            int f = cand[(size_t)t * K + k];
+            if (fill[f] < C) {
+                size_t j = (size_t)t * k + rs;
+                eid[j] = f;
+                pos[j] = (int32_t)fill[f]++;
+                flag[j] = 1;
+                src_rank[j] = k;
+            }
+        }
+
+    /* packed rows */
+    int64_t acc = 0;
+    for (int e = 0; e < E; e++) {
+        kept[e] = (int32_t)fill[e];
+        offsets[e] = (int32_t)acc;
+        acc += fill[e];
+    }
+    offsets[E] = (int32_t)acc;
+    int64_t cap_rows = (int64_t)T * k;
+    if ((int64_t)E * C < cap_rows)
+        cap_rows = (int64_t)E * C;
+    for (int64_t i = 0; i < cap_rows; i++)
+        token_of_row[i] = -1;
+    int rerouted = 0;
+    for (int t = 0; t < T; t++)
+        for (int r = 0; r < k; r++) {
+            size_t j = (size_t)t * k + r;
+            if (flag[j] == 2) {
+                row[j] = -1;
+                continue;
+            }
+            row[j] = offsets[eid[j]] + pos[j];
+            token_of_row[row[j]] = t;
+            if (flag[j] == 1)
+                rerouted++;
+        }
+
+    /* gates: softmax over the kept slots' scores */
+    for (int t = 0; t < T; t++) {
+        double m = -INFINITY;
+        for (int r = 0; r < k; r++) {
+            size_t j = (size_t)t * k + r;
+            if (flag[j] != 2) {
+                double sv = cand_score[(size_t)t * K + src_rank[j]];
+                if (sv > m)
+                    m = sv;
+            }
+        }
+        double z = 0.0;
+        for (int r = 0; r < k; r++) {
+            size_t j = (size_t)t * k + r;
+            if (flag[j] != 2)
+                z += exp((double)cand_score[(size_t)t * K + src_rank[j]] - m);
+        }
+        for (int r = 0; r < k; r++) {
+            size_t j = (size_t)t * k + r;
+            double g = 0.0;
+            if (flag[j] != 2)
+                g = exp((double)cand_score[(size_t)t * K + src_rank[j]] - m) / z;
+            gate[j] = (float)g;
+            if (gate64)
+                gate64[j] = g;
+        }
+    }
+
+    totals[0] = (int32_t)acc;
+    totals[1] = (int32_t)((int64_t)T * k - acc);
+    totals[2] = rerouted;
+
+    double l = 0.0;
+    for (int e = 0; e < E; e++) {
+        double u = (double)demand[e] / (double)T;
+        l += u * u;
+    }
+    *aux_loss = (float)((double)aux_coef * l);
+
+    free(fill);
+    free(src_rank);
+}
+
+/*
+ * One expert FFN application (P1 §3.1: Linear -> SwiGLU -> Linear per expert;
+ * P5 §1: each expert is the W1/W2/W3 matrices of an FFN).  Reading:
+ * h = silu(x W1^T) * (x W3^T), y = h W2^T, silu(a) = a / (1 + exp(-a)), no
+ * biases.  W1, W3: [E][d_ff][d]; W2: [E][d][d_ff].  xrow points at element
+ * offset xo of x.  h (scratch, d_ff doubles) is left holding the SwiGLU
+ * activations; ye receives the d outputs.
+ */
+static void ffn_one(int e, size_t xo, int d, int d_ff, int dt, const void *x, const void *w1,
+                    const void *w3, const void *w2, double *h, double *ye)
+{
+    size_t wo = (size_t)e * d_ff * d;
+    for (int j = 0; j < d_ff; j++) {
+        double a = 0.0, b = 0.0;
+        size_t ro = wo + (size_t)j * d;
+        for (int q = 0; q < d; q++) {
+            double xv = elem(x, xo + q, dt);
+            a += xv * elem(w1, ro + q, dt);
+            b += xv * elem(w3, ro + q, dt);
+        }
+        h[j] = a / (1.0 + exp(-a)) * b;
+    }
+    size_t w2o = (size_t)e * d * d_ff;
+    for (int q = 0; q < d; q++) {
+        double acc = 0.0;
+        size_t ro = w2o + (size_t)q * d_ff;
+        for (int j = 0; j < d_ff; j++)
+            acc += h[j] * elem(w2, ro + j, dt);
+        ye[q] = acc;
+    }
+}
+
+/*
+ * Expert FFN on a list of rows: row i applies expert[i] to input row
+ * x[src[i]].  y [n][d] and h [n][d_ff] (h may be NULL) are double.
+ */
+void oracle_ffn_rows(int n, const int32_t *expert, const int32_t *src, int d, int d_ff, int dt,
+                     const void *x, const void *w1, const void *w3, const void *w2,
+                     double *y, double *h_out)
+{
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)d_ff * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < n; i++) {
+            ffn_one(expert[i], (size_t)src[i] * d, d, d_ff, dt, x, w1, w3, w2, h,
+                    y + (size_t)i * d);
+            if (h_out)
+                memcpy(h_out + (size_t)i * d_ff, h, (size_t)d_ff * sizeof(double));
+        }
+        free(h);
+    }
+}
+
+/*
+ * Layer output for a list of tokens: y_t = sum over kept slots j of
+ * gate[t][j] * FFN_{eid[t][j]}(x_t) (P5 §3, step 5: the experts' results are
+ * put back in token order; P1 §4.3: weighted fusion of the experts' outputs).
+ * A token with no kept slot gets a zero row.  gate64 and eid are [T][k];
+ * y [n][d].
+ */
+void oracle_layer_tokens(int n, const int32_t *tokens, int k, int d, int d_ff, int dt,
+                         const void *x, const void *w1, const void *w3, const void *w2,
+                         const int32_t *eid, const double *gate64, double *y)
+{
+#pragma omp parallel
+    {
+        double *h = (double *)malloc((size_t)d_ff * sizeof(double));
+        double *ye = (double *)malloc((size_t)d * sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < n; i++) {
+            int t = tokens[i];
+            double *yt = y + (size_t)i * d;
+            for (int q = 0; q < d; q++)
+                yt[q] = 0.0;
+            for (int r = 0; r < k; r++) {
+                int e = eid[(size_t)t * k + r];
+                if (e < 0)
+                    continue;
+                ffn_one(e, (size_t)t * d, d, d_ff, dt, x, w1, w3, w2, h, ye);
+                double g = gate64[(size_t)t * k + r];
+                for (int q = 0; q < d; q++)
+                    yt[q] += g * ye[q];
+            }
+        }
+        free(h);
+        free(ye);
+    }
+}
+
+/*
+ * Combine from given per-row expert outputs: y[t] = sum over kept slots of
+ * gate[t][j] * y_rows[row[t][j]] (row == -1: slot dropped).  y_rows has element
+ * type dt; gate is fp32 as produced by dispatch; y [T][d] double.
+ */
+void oracle_combine(int T, int k, int d, int dt, const int32_t *row, const float *gate,
+                    const void *y_rows, double *y)
+{
+    for (int t = 0; t < T; t++) {
+        double *yt = y + (size_t)t * d;
+        for (int q = 0; q < d; q++)
+            yt[q] = 0.0;
+        for (int r = 0; r < k; r++) {
+            int rw = row[(size_t)t * k + r];
+            if (rw < 0)
+                continue;
+            double g = gate[(size_t)t * k + r];
+            for (int q = 0; q < d; q++)
+                yt[q] += g * elem(y_rows, (size_t)rw * d + q, dt);
+        }
+    }
+}

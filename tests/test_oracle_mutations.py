@@ -1,0 +1,92 @@
+"""Plant plausible mistakes in a copy of the oracle and check the pins catch them.
+
+Each mutation edits the C source text in a temporary directory, builds a
+separate library, points the oracle wrapper at it, and runs the pin checks of
+tests/test_oracle_pins.py.  At least one check must fail for every mutation.
+The committed oracle is never modified.
+"""
+import os
+import shutil
+import subprocess
+import sys
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+MUTATIONS = {
+    "ties_to_higher_index": ("st[e] > st[best]", "st[e] >= st[best]"),
+    "penalty_two_roundings": ("fmaf(-lambda, load[e], raw[i])", "raw[i] - lambda * load[e]"),
+    "capacity_floor": ("ceil((double)T", "floor((double)T"),
+    "queue_limit_off_by_one": ("if (fill[e] < C) {", "if (fill[e] <= C) {"),
+    "token_major_order": ("    for (int r = 0; r < k; r++)\n        for (int t = 0; t < T; t++) {\n            size_t j",
+                          "    for (int t = 0; t < T; t++)\n        for (int r = 0; r < k; r++) {\n            size_t j"),
+    "fallback_wrong_rank": ("int f = cand[(size_t)t * K + k];", "int f = cand[(size_t)t * K + k - 1];"),
+    "silu_on_w3": ("h[j] = a / (1.0 + exp(-a)) * b;", "h[j] = b / (1.0 + exp(-b)) * a;"),
+    "w2_transposed": ("acc += h[j] * elem(w2, ro + j, dt);", "acc += h[j] * elem(w2, w2o + (size_t)j * d + q, dt);"),
+    "gate_not_renormalised": ("            if (flag[j] != 2)\n                z += exp(", "            if (1)\n                z += exp("),
+    "aux_loss_over_Tk": ("double u = (double)demand[e] / (double)T;", "double u = (double)demand[e] / ((double)T * k);"),
+    "bias_dropped": ("r = r + bias[e];", "r = r;"),
+    "gate_uses_primary_score": ("                src_rank[j] = k;\n", ""),
+    "router_weight_transposed": ("elem(wr, (size_t)e * d + i, dt)", "elem(wr, (size_t)i * E + e, dt)"),
+}
+
+CHECKS = [
+    pins.check_capacity, pins.check_router_logits, pins.check_scores, pins.check_topk,
+    pins.check_dispatch_exhaustive, pins.check_dispatch_invariants, pins.check_aux_loss,
+    lambda o: pins.check_dense_equivalence(o, "f32"), pins.check_identical_experts,
+    pins.check_expert_relabel,
+]
+
+
+RUNNER = r"""
+import sys
+sys.path.insert(0, {root!r})
+import oracle
+from tests import test_oracle_mutations as m
+oracle._LIB = {so!r}
+oracle._lib = None
+oracle.lib()
+for name, chk in m.named_checks():
+    try:
+        chk(oracle)
+        print("PASS", name, flush=True)
+    except (AssertionError, IndexError, ValueError) as exc:
+        print("FAIL", name, flush=True)
+"""
+
+
+def named_checks():
+    names = ["capacity", "router_logits", "scores", "topk", "dispatch_exhaustive",
+             "dispatch_invariants", "aux_loss", "dense_equivalence", "identical_experts",
+             "expert_relabel"]
+    return list(zip(names, CHECKS))
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    d = tempfile.mkdtemp(prefix="oracle_mut_")
+    yield d
+    shutil.rmtree(d, ignore_errors=True)
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_mutation_is_caught(name, workdir):
+    """The mutated library runs in a child process: a planted out-of-bounds
+    write must not corrupt this test process."""
+    old, new = MUTATIONS[name]
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "moe_oracle.c")).read()
+    assert src.count(old) >= 1, f"mutation pattern not found: {name}"
+    c = os.path.join(workdir, f"{name}.c")
+    so = os.path.join(workdir, f"lib_{name}.so")
+    open(c, "w").write(src.replace(old, new))
+    subprocess.check_call(["gcc", "-O2", "-std=c99", "-fopenmp", "-ffp-contract=off", "-shared",
+                           "-fPIC", "-o", so, c, "-lm"])
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    proc = subprocess.run([sys.executable, "-c", RUNNER.format(root=root, so=so)],
+                          capture_output=True, text=True, timeout=600)
+    failed = [ln.split()[1] for ln in proc.stdout.splitlines() if ln.startswith("FAIL")]
+    crashed = proc.returncode != 0
+    assert failed or crashed, f"no pin catches mutation {name}: {proc.stdout}{proc.stderr}"
