@@ -275,7 +275,7 @@ void oracle_dispatch(int T, int E, int k, int64_t C, int reroute, float aux_coef
 
     double l = 0.0;
     for (int e = 0; e < E; e++) {
-        double u = (double)demand[e] / (double)T;
+        double u = T > 0 ? (double)demand[e] / (double)T : 0.0; /* empty batch: no load */
         l += u * u;
     }
     *aux_loss = (float)((double)aux_coef * l);

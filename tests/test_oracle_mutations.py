@@ -27,7 +27,7 @@ MUTATIONS = {
     "silu_on_w3": ("h[j] = a / (1.0 + exp(-a)) * b;", "h[j] = b / (1.0 + exp(-b)) * a;"),
     "w2_transposed": ("acc += h[j] * elem(w2, ro + j, dt);", "acc += h[j] * elem(w2, w2o + (size_t)j * d + q, dt);"),
     "gate_not_renormalised": ("            if (flag[j] != 2)\n                z += exp(", "            if (1)\n                z += exp("),
-    "aux_loss_over_Tk": ("double u = (double)demand[e] / (double)T;", "double u = (double)demand[e] / ((double)T * k);"),
+    "aux_loss_over_Tk": ("(double)demand[e] / (double)T :", "(double)demand[e] / ((double)T * k) :"),
     "bias_dropped": ("r = r + bias[e];", "r = r;"),
     "gate_uses_primary_score": ("                src_rank[j] = k;\n", ""),
     "router_weight_transposed": ("elem(wr, (size_t)e * d + i, dt)", "elem(wr, (size_t)i * E + e, dt)"),
