@@ -1,0 +1,192 @@
+/*
+ * moe.h -- C ABI of the single-GPU sparse Mixture-of-Experts FFN layer
+ * forward pass for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (the computation the MoE pages describe; page titles cited):
+ *   1. route:    router GEMM, optional per-expert bias and load-aware penalty,
+ *                ranking of the experts with ties to the lower index;
+ *   2. dispatch: capacity-capped assignment of each token's top-k choices to
+ *                expert queues, re-route of overflow to the next-ranked
+ *                candidate or drop, gates, router statistics and the
+ *                load-balancing loss, and the permutation of token rows into
+ *                per-expert groups;
+ *   3. expert_ffn: SwiGLU FFN of every expert over its group of rows;
+ *   4. combine:  gate-weighted sum of each token's expert outputs, in token
+ *                order;
+ *   5. forward:  1-4 on one stream.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named x, w_*, bias, load, logits, y, h, x_perm, y_perm,
+ *     workspace and every member of moe_routing are DEVICE pointers, allocated
+ *     and owned by the caller.  The library never allocates or frees memory
+ *     and never synchronises: work is enqueued on `stream` (a hipStream_t; NULL
+ *     is the legacy default stream) and outputs are valid once the stream has
+ *     reached that point.  `p` is a host pointer read during the call only.
+ *   - All matrices are row-major.  bf16 means IEEE bfloat16 bit patterns;
+ *     conversions from fp32 round to nearest even.  Accumulation is fp32.
+ *   - Elements of x, w_router, w1, w3, w2, x_perm and y have the element type
+ *     p->dtype.  logits, bias, load, cand_score, gate and y_perm are fp32
+ *     (y_perm holds the down-projection at accumulator precision, so the layer
+ *     output is rounded to the element type once).  The SwiGLU activations h
+ *     are fp16 in a bf16 layer (saturated at +-65504) and fp32 in an fp32
+ *     layer.
+ *   - Every output element listed for an entry point is written on every call.
+ *   - NaN or Inf inputs are outside the contract.
+ *   - Calls on different streams that share no output buffer may run
+ *     concurrently; the library has no global mutable state.
+ *
+ * Return codes: MOE_OK (0) on success, or a negative MOE_ERR_* code; nothing
+ * is enqueued when an argument check fails.  moe_strerror() names the code.
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_ERR_INVALID_ARG (-1) /* null pointer, size out of range, workspace too small */
+#define MOE_ERR_UNSUPPORTED (-2) /* dtype, alignment or a dimension the kernels do not take */
+#define MOE_ERR_HIP (-3)         /* a kernel launch failed */
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+/*
+ * Problem statement: T tokens of hidden size d, E experts, top-k, capacity
+ * factor, SwiGLU intermediate size d_ff (the parameters in which the MoE
+ * pages state the problem; "MoE架构揭秘" §5.2 names num_experts_per_tok,
+ * expert_capacity and the capacity factor).
+ *
+ * Limits: 0 <= T <= 2^20 (T = 0 is an empty batch); 1 <= E <= 256;
+ * 1 <= k <= min(E, 8); d and d_ff positive multiples of 64; d <= 16384 for
+ * bf16 and d <= 8192 for fp32.  Other values return MOE_ERR_INVALID_ARG (sizes)
+ * or MOE_ERR_UNSUPPORTED (dtype, multiples, d too large).
+ */
+typedef struct moe_params {
+    int32_t T, d, E, k, d_ff;
+    /* capacity C = min(T, ceil(T*k/E * capacity_factor)), evaluated in double
+     * in that order ("MoE架构揭秘" §5.2 expert_capacity); capacity_factor <= 0
+     * means uncapped (C = T). */
+    float capacity_factor;
+    /* 1: a token whose chosen expert is full sends its lowest-rank overflowed
+     * slot to its rank-k candidate (the third-ranked expert for top-2), else
+     * that slot is dropped ("GPT-4稀疏激活真相" §2.3); 0: overflow is dropped. */
+    int32_t reroute;
+    /* load-aware penalty s = fmaf(-lambda, load[e], raw) ("GPT-4稀疏激活真相"
+     * §2.3); ignored when load == NULL. */
+    float lambda;
+    /* load-balancing loss coefficient; the loss is aux_coef * sum_e
+     * (demand[e]/T)^2 ("MoE稀疏激活原理与工程实践" §4.2, coefficient 0.01). */
+    float aux_coef;
+    int32_t dtype; /* moe_dtype */
+} moe_params;
+
+/*
+ * Routing arrays (all device pointers, caller-allocated, int32 unless noted).
+ * K1 = k + 1 candidate columns; R = moe_max_rows(p) = min(T*k, E*C).
+ * Arrays with a T dimension may be NULL when T = 0, token_of_row when R = 0;
+ * offsets, demand, kept, totals and aux_loss are always required.
+ */
+typedef struct moe_routing {
+    int32_t *cand;       /* [T][K1] experts by (score desc, index asc); -1 past E   */
+    float *cand_score;   /* [T][K1] penalised fp32 scores; -inf past E              */
+    int32_t *eid;        /* [T][k]  final expert of slot j, -1 when dropped         */
+    int32_t *pos;        /* [T][k]  position in that expert's queue, -1 if dropped  */
+    int32_t *row;        /* [T][k]  row in the permuted layout, -1 if dropped       */
+    uint8_t *flag;       /* [T][k]  0 kept, 1 re-routed, 2 dropped                  */
+    float *gate;         /* [T][k]  softmax of the kept slots' scores; 0 if dropped */
+    int32_t *offsets;    /* [E+1]   exclusive scan of kept; offsets[E] = rows       */
+    int32_t *token_of_row; /* [R]   token of each permuted row; -1 past offsets[E]  */
+    int32_t *demand;     /* [E]     rank < k selections before the cap              */
+    int32_t *kept;       /* [E]     rows kept per expert (<= C)                     */
+    int32_t *totals;     /* [3]     rows, dropped slots, re-routed slots            */
+    float *aux_loss;     /* [1]     load-balancing loss                             */
+} moe_routing;
+
+/* Host-side, pure: capacity C (see moe_params.capacity_factor); -1 if p is
+ * invalid. */
+int64_t moe_capacity(const moe_params *p);
+
+/* Host-side, pure: R = min(T*k, E*C), the row bound of the permuted layout;
+ * -1 if p is invalid. */
+int64_t moe_max_rows(const moe_params *p);
+
+/* Host-side, pure: bytes of scratch moe_dispatch needs. */
+size_t moe_dispatch_workspace_bytes(const moe_params *p);
+
+/* Host-side, pure: bytes of workspace moe_forward needs: the dispatch scratch
+ * plus x_perm [R][d], h [R][d_ff] and y_perm [R][d] (fp32), each 256-byte
+ * aligned. */
+size_t moe_workspace_bytes(const moe_params *p);
+
+/*
+ * Stage 1, route.  raw[t][e] = sum_i x[t][i] * w_router[e][i] + bias[e]
+ * ("MoE架构揭秘" §3.1: z = h . W_router), s = fmaf(-lambda, load[e], raw)
+ * (or raw when load is NULL), then the K1 best experts by (s desc, e asc)
+ * ("MoE架构揭秘" §3.1: softmax then top-k; softmax is monotone, so the ranking
+ * is taken on s).
+ *   x [T][d], w_router [E][d] (dtype); bias [E] fp32 or NULL; load [E] fp32 or
+ *   NULL.  Writes logits [T][E] (raw, fp32), r->cand and r->cand_score.
+ */
+int moe_route(const moe_params *p, const void *x, const void *w_router, const float *bias,
+              const float *load, float *logits, moe_routing *r, void *stream);
+
+/*
+ * Stage 2, dispatch.  Reads r->cand and r->cand_score; writes every other
+ * member of r and x_perm [R][d] (rows past offsets[E] are left untouched).
+ * Queue order is rank-major (all rank-0 choices in token order, then rank 1,
+ * ..., then one fallback round in token order); a slot is kept while its
+ * expert holds fewer than C rows ("GPT-4稀疏激活真相" §2.3; "MoE架构揭秘"
+ * §3.3).  Gates are the softmax of the kept slots' scores renormalised over
+ * the kept slots.  Deterministic: no atomics.
+ *   workspace: at least moe_dispatch_workspace_bytes(p) bytes, 256-B aligned.
+ */
+int moe_dispatch(const moe_params *p, const void *x, moe_routing *r, void *x_perm,
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Stage 3, expert SwiGLU FFN as a grouped GEMM over the permuted rows
+ * ("GPT-4稀疏激活真相" §3.1: Linear -> SwiGLU -> Linear per expert):
+ *   for rows i in [offsets[e], offsets[e+1]):
+ *     h[i]      = silu(x_perm[i] . W1[e]^T) * (x_perm[i] . W3[e]^T)
+ *     y_perm[i] = h[i] . W2[e]^T
+ *   x_perm [R][d]; w1, w3 [E][d_ff][d]; w2 [E][d][d_ff]; h [R][d_ff] (fp16
+ *   for bf16, fp32 for fp32);
+ *   y_perm [R][d] fp32.  offsets [E+1] is read on the device.  Rows past
+ *   offsets[E] of h and y_perm are left untouched.
+ */
+int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                   const void *w1, const void *w3, const void *w2, void *h, void *y_perm,
+                   void *stream);
+
+/*
+ * Stage 4, combine ("企业官网建设流程全解析" page §3, step 5: results are put
+ * back in token order; "GPT-4稀疏激活真相" §4.3: weighted fusion):
+ *   y[t] = sum over slots j with row[t][j] >= 0 of gate[t][j] * y_perm[row[t][j]]
+ * accumulated in fp32 and rounded once; a token with no kept slot gets zeros.
+ *   y_perm [R][d] fp32; row, gate [T][k]; y [T][d].
+ */
+int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
+                void *y, void *stream);
+
+/*
+ * Stages 1-4 on one stream with no host synchronisation.  workspace holds at
+ * least moe_workspace_bytes(p) bytes (256-B aligned) and is carved into the
+ * dispatch scratch, x_perm, h and y_perm.
+ */
+int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                const float *load, const void *w1, const void *w3, const void *w2, void *y,
+                float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
+
+/* Static description of a return code. */
+const char *moe_strerror(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */

@@ -1,0 +1,205 @@
+"""Python binding of the MI355X MoE FFN layer library (libmoe_hip.so).
+
+Argument marshalling only: every stage runs in the library's HIP kernels.
+torch provides device memory and streams.  The binding refuses to run when
+the library is missing; there is no fallback.
+
+Entry points mirror the C ABI in include/moe.h: route, dispatch, expert_ffn,
+combine, forward, plus capacity / max_rows / workspace sizing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch  # load torch's HIP runtime before the library binds to it
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_hip.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, -1, -2, -3
+MOE_F32, MOE_BF16 = 0, 1
+
+
+class MoEError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what} failed: {code} ({strerror(code)})")
+        self.code = code
+
+
+class MoeParams(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
+                ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("capacity_factor", ctypes.c_float), ("reroute", ctypes.c_int32),
+                ("lam", ctypes.c_float), ("aux_coef", ctypes.c_float), ("dtype", ctypes.c_int32)]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("cand", "cand_score", "eid", "pos", "row", "flag", "gate", "offsets",
+                 "token_of_row", "demand", "kept", "totals", "aux_loss")]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        PP = ctypes.POINTER(MoeParams)
+        PR = ctypes.POINTER(MoeRouting)
+        L.moe_capacity.argtypes = [PP]
+        L.moe_capacity.restype = ctypes.c_int64
+        L.moe_max_rows.argtypes = [PP]
+        L.moe_max_rows.restype = ctypes.c_int64
+        L.moe_dispatch_workspace_bytes.argtypes = [PP]
+        L.moe_dispatch_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_workspace_bytes.argtypes = [PP]
+        L.moe_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_route.argtypes = [PP, P, P, P, P, P, PR, P]
+        L.moe_dispatch.argtypes = [PP, P, PR, P, P, ctypes.c_size_t, P]
+        L.moe_expert_ffn.argtypes = [PP, P, P, P, P, P, P, P, P]
+        L.moe_combine.argtypes = [PP, P, P, P, P, P]
+        L.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P]
+        for f in (L.moe_route, L.moe_dispatch, L.moe_expert_ffn, L.moe_combine, L.moe_forward):
+            f.restype = ctypes.c_int
+        L.moe_strerror.argtypes = [ctypes.c_int]
+        L.moe_strerror.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def strerror(code: int) -> str:
+    return lib().moe_strerror(code).decode()
+
+
+@dataclass
+class Params:
+    T: int
+    d: int
+    E: int
+    k: int
+    d_ff: int
+    capacity_factor: float = 1.0
+    reroute: int = 1
+    lam: float = 0.0
+    aux_coef: float = 0.01
+    dtype: int = MOE_BF16
+
+    def c(self) -> MoeParams:
+        return MoeParams(self.T, self.d, self.E, self.k, self.d_ff, self.capacity_factor,
+                         self.reroute, self.lam, self.aux_coef, self.dtype)
+
+    @property
+    def torch_dtype(self):
+        return torch.bfloat16 if self.dtype == MOE_BF16 else torch.float32
+
+
+def capacity(p: Params) -> int:
+    return int(lib().moe_capacity(ctypes.byref(p.c())))
+
+
+def max_rows(p: Params) -> int:
+    return int(lib().moe_max_rows(ctypes.byref(p.c())))
+
+
+def dispatch_workspace_bytes(p: Params) -> int:
+    return int(lib().moe_dispatch_workspace_bytes(ctypes.byref(p.c())))
+
+
+def workspace_bytes(p: Params) -> int:
+    return int(lib().moe_workspace_bytes(ctypes.byref(p.c())))
+
+
+class Routing:
+    """Device tensors of the routing arrays (layouts as in include/moe.h)."""
+
+    NAMES = ("cand", "cand_score", "eid", "pos", "row", "flag", "gate", "offsets",
+             "token_of_row", "demand", "kept", "totals", "aux_loss")
+
+    def __init__(self, p: Params, device="cuda"):
+        T, E, k = p.T, p.E, p.k
+        R = max(max_rows(p), 0)
+        i32, f32 = torch.int32, torch.float32
+        self.cand = torch.empty((T, k + 1), dtype=i32, device=device)
+        self.cand_score = torch.empty((T, k + 1), dtype=f32, device=device)
+        self.eid = torch.empty((T, k), dtype=i32, device=device)
+        self.pos = torch.empty((T, k), dtype=i32, device=device)
+        self.row = torch.empty((T, k), dtype=i32, device=device)
+        self.flag = torch.empty((T, k), dtype=torch.uint8, device=device)
+        self.gate = torch.empty((T, k), dtype=f32, device=device)
+        self.offsets = torch.empty(E + 1, dtype=i32, device=device)
+        self.token_of_row = torch.empty(max(R, 1), dtype=i32, device=device)
+        self.demand = torch.empty(E, dtype=i32, device=device)
+        self.kept = torch.empty(E, dtype=i32, device=device)
+        self.totals = torch.empty(3, dtype=i32, device=device)
+        self.aux_loss = torch.empty(1, dtype=f32, device=device)
+        self.R = R
+
+    def c(self) -> MoeRouting:
+        return MoeRouting(*[getattr(self, n).data_ptr() for n in self.NAMES])
+
+    def cpu(self) -> dict:
+        out = {n: getattr(self, n).cpu() for n in self.NAMES}
+        out["token_of_row"] = out["token_of_row"][: self.R]
+        return out
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check(rc: int, what: str):
+    if rc != MOE_OK:
+        raise MoEError(rc, what)
+
+
+def route(p: Params, x, w_router, bias, load, logits, r: Routing, stream=None):
+    rc = lib().moe_route(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(load),
+                         _ptr(logits), ctypes.byref(r.c()), _stream(stream))
+    _check(rc, "moe_route")
+
+
+def dispatch(p: Params, x, r: Routing, x_perm, workspace, stream=None):
+    rc = lib().moe_dispatch(ctypes.byref(p.c()), _ptr(x), ctypes.byref(r.c()), _ptr(x_perm),
+                            _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "moe_dispatch")
+
+
+def expert_ffn(p: Params, x_perm, offsets, w1, w3, w2, h, y_perm, stream=None):
+    rc = lib().moe_expert_ffn(ctypes.byref(p.c()), _ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3),
+                              _ptr(w2), _ptr(h), _ptr(y_perm), _stream(stream))
+    _check(rc, "moe_expert_ffn")
+
+
+def combine(p: Params, y_perm, row, gate, y, stream=None):
+    rc = lib().moe_combine(ctypes.byref(p.c()), _ptr(y_perm), _ptr(row), _ptr(gate), _ptr(y),
+                           _stream(stream))
+    _check(rc, "moe_combine")
+
+
+def forward(p: Params, x, w_router, bias, load, w1, w3, w2, y, logits, r: Routing, workspace,
+            stream=None):
+    rc = lib().moe_forward(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(load),
+                           _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y), _ptr(logits), ctypes.byref(r.c()),
+                           _ptr(workspace), workspace.numel() * workspace.element_size(),
+                           _stream(stream))
+    _check(rc, "moe_forward")
+
+
+def alloc_workspace(p: Params, device="cuda", dispatch_only: bool = False) -> torch.Tensor:
+    n = dispatch_workspace_bytes(p) if dispatch_only else workspace_bytes(p)
+    return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

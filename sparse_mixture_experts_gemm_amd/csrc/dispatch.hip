@@ -1,0 +1,320 @@
+// Stage 2: capacity-capped dispatch, deterministic and atomics-free.
+//
+// What it computes ("GPT-4稀疏激活真相" §2.3: an expert whose queue has reached
+// the limit sends the token to its third-ranked candidate; "MoE架构揭秘" §3.3:
+// overflow is dropped or re-routed; "企业官网建设流程全解析" page §2: once an
+// expert is full, later tokens go to the next-best expert):
+//   arrival order is rank-major: all rank-0 choices in token order, then rank
+//   1, ..., then one fallback round in token order.  A request is kept while
+//   its expert holds fewer than C rows.  A token with an overflowed slot sends
+//   its lowest overflowed slot to its rank-k candidate; further overflowed
+//   slots are dropped.  Gates are the softmax of the kept slots' scores.
+//
+// Because a primary request's queue position depends only on how many earlier
+// requests chose the same expert, positions are counting problems: per-block
+// expert histograms, an exclusive prefix over blocks, and an in-block rank from
+// wave ballots (mbcnt over the lanes holding the same expert).  The fallback
+// round depends on the primary overflow, so it takes a second histogram pass.
+// Kernels (one token per thread, 1024 tokens per block):
+//   hist      per-block counts of each primary round
+//   primary   queue positions of the primary rounds, fallback histograms
+//   finalize  fallback positions, packed rows, gates, statistics, loss
+//   gather    copy of each token's x row to its kept rows (x_perm)
+// Each block recomputes the prefix it needs from the per-block histograms, so
+// no grid-wide synchronisation or atomic is needed.
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+static_assert(kThreads == kDispatchBlock, "one token per thread");
+
+// Rank of this lane among the lanes of its wave holding the same key (keys
+// < 0 are ignored), and the per-key lane counts of the wave, written to
+// wave_cnt[key].  One ballot per distinct key in the wave.
+__device__ __forceinline__ int wave_rank_count(int key, int *wave_cnt) {
+    const int lane = threadIdx.x & 63;
+    uint64_t active = ballot64(key >= 0);
+    int rank = 0;
+    while (active) {
+        const int leader = __builtin_ctzll(active);
+        const int lk = __builtin_amdgcn_readlane(key, leader);
+        const uint64_t m = ballot64(key == lk);
+        if (key == lk) rank = rank_below(m);
+        if (lane == leader) wave_cnt[lk] = __popcll(m);
+        active &= ~m;
+    }
+    return rank;
+}
+
+__device__ __forceinline__ void zero_lds(int *a, int n) {
+    for (int i = threadIdx.x; i < n; i += kThreads) a[i] = 0;
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_hist(const int32_t *__restrict__ cand, int T,
+                                                          int E, int k, int32_t *__restrict__ hist) {
+    __shared__ int wcnt[kWaves][kMaxExperts];
+    const int K1 = k + 1;
+    const int b = blockIdx.x;
+    const int t = b * kThreads + threadIdx.x;
+    const int wave = threadIdx.x >> 6;
+    for (int r = 0; r < k; r++) {
+        zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
+        __syncthreads();
+        const int key = t < T ? cand[(size_t)t * K1 + r] : -1;
+        wave_rank_count(key, wcnt[wave]);
+        __syncthreads();
+        for (int e = threadIdx.x; e < E; e += kThreads) {
+            int s = 0;
+            for (int w = 0; w < kWaves; w++) s += wcnt[w][e];
+            hist[((size_t)b * k + r) * E + e] = s;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_primary(
+    const int32_t *__restrict__ cand, int T, int E, int k, int C, int nb, int use_fallback,
+    const int32_t *__restrict__ hist, int32_t *__restrict__ fill_prim, int32_t *__restrict__ eid,
+    int32_t *__restrict__ pos, uint8_t *__restrict__ flag, int32_t *__restrict__ fb_hist) {
+    __shared__ int base[kMaxTopK][kMaxExperts];
+    __shared__ int tot[kMaxTopK][kMaxExperts];
+    __shared__ int wcnt[kWaves][kMaxExperts];
+    const int K1 = k + 1;
+    const int b = blockIdx.x;
+    const int t = b * kThreads + threadIdx.x;
+    const int wave = threadIdx.x >> 6;
+
+    // requests before this block, and in total, per (round, expert)
+    for (int i = threadIdx.x; i < k * E; i += kThreads) {
+        const int r = i / E, e = i % E;
+        int pre = 0, all = 0;
+        for (int bb = 0; bb < nb; bb++) {
+            const int v = hist[((size_t)bb * k + r) * E + e];
+            all += v;
+            pre += bb < b ? v : 0;
+        }
+        base[r][e] = pre;
+        tot[r][e] = all;
+    }
+    __syncthreads();
+    // queue fill before each round: fill_{r+1} = min(C, fill_r + requests_r)
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        int fill = 0;
+        for (int r = 0; r < k; r++) {
+            base[r][e] += fill;
+            fill = min(C, fill + tot[r][e]);
+        }
+        if (b == 0) fill_prim[e] = fill;
+    }
+
+    int first_over = -1;
+    for (int r = 0; r < k; r++) {
+        zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
+        __syncthreads();
+        const int key = t < T ? cand[(size_t)t * K1 + r] : -1;
+        const int rank = wave_rank_count(key, wcnt[wave]);
+        __syncthreads();
+        if (t < T) {
+            int p = base[r][key] + rank;
+            for (int w = 0; w < wave; w++) p += wcnt[w][key];
+            const size_t j = (size_t)t * k + r;
+            if (p < C) {
+                eid[j] = key;
+                pos[j] = p;
+                flag[j] = 0;
+            } else {
+                eid[j] = -1;
+                pos[j] = -1;
+                flag[j] = 2;
+                if (first_over < 0) first_over = r;
+            }
+        }
+        __syncthreads();
+    }
+
+    // fallback requests of this block, per expert
+    zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
+    __syncthreads();
+    const int fkey = (t < T && use_fallback && first_over >= 0) ? cand[(size_t)t * K1 + k] : -1;
+    wave_rank_count(fkey, wcnt[wave]);
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        int s = 0;
+        for (int w = 0; w < kWaves; w++) s += wcnt[w][e];
+        fb_hist[(size_t)b * E + e] = s;
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void dispatch_finalize(
+    const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k,
+    int C, int nb, int use_fallback, float aux_coef, int cap_rows, const int32_t *__restrict__ hist,
+    const int32_t *__restrict__ fill_prim, const int32_t *__restrict__ fb_hist,
+    int32_t *__restrict__ eid, int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
+    int32_t *__restrict__ row, float *__restrict__ gate, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand, int32_t *__restrict__ kept,
+    int32_t *__restrict__ totals, float *__restrict__ aux_loss) {
+    __shared__ int fbase[kMaxExperts];
+    __shared__ int kcnt[kMaxExperts];
+    __shared__ int offs[kMaxExperts + 1];
+    __shared__ int scan_tmp[2][kMaxExperts];
+    __shared__ int wcnt[kWaves][kMaxExperts];
+    const int K1 = k + 1;
+    const int b = blockIdx.x;
+    const int t = b * kThreads + threadIdx.x;
+    const int wave = threadIdx.x >> 6;
+
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+        int pre = 0, all = 0;
+        for (int bb = 0; bb < nb; bb++) {
+            const int v = fb_hist[(size_t)bb * E + e];
+            all += v;
+            pre += bb < b ? v : 0;
+        }
+        const int fp = fill_prim[e];
+        fbase[e] = fp + pre;
+        const int kc = min(C, fp + all);
+        kcnt[e] = kc;
+        scan_tmp[0][e] = kc;
+    }
+    __syncthreads();
+    // inclusive Hillis-Steele scan over the experts, then shift to exclusive
+    int src = 0;
+    for (int step = 1; step < E; step <<= 1) {
+        for (int e = threadIdx.x; e < E; e += kThreads)
+            scan_tmp[src ^ 1][e] = scan_tmp[src][e] + (e >= step ? scan_tmp[src][e - step] : 0);
+        __syncthreads();
+        src ^= 1;
+    }
+    for (int e = threadIdx.x; e < E; e += kThreads) offs[e + 1] = scan_tmp[src][e];
+    if (threadIdx.x == 0) offs[0] = 0;
+
+    // fallback positions
+    zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
+    __syncthreads();
+    int first_over = -1;
+    if (t < T)
+        for (int r = 0; r < k; r++)
+            if (flag[(size_t)t * k + r] == 2) {
+                first_over = r;
+                break;
+            }
+    const int fkey = (t < T && use_fallback && first_over >= 0) ? cand[(size_t)t * K1 + k] : -1;
+    const int rank = wave_rank_count(fkey, wcnt[wave]);
+    __syncthreads();
+    if (fkey >= 0) {
+        int p = fbase[fkey] + rank;
+        for (int w = 0; w < wave; w++) p += wcnt[w][fkey];
+        if (p < C) {
+            const size_t j = (size_t)t * k + first_over;
+            eid[j] = fkey;
+            pos[j] = p;
+            flag[j] = 1;
+        }
+    }
+
+    // packed rows and gates
+    if (t < T) {
+        float sc[kMaxTopK];
+        int e_s[kMaxTopK], p_s[kMaxTopK], f_s[kMaxTopK];
+        float m = -INFINITY;
+        for (int r = 0; r < k; r++) {
+            const size_t j = (size_t)t * k + r;
+            f_s[r] = flag[j];
+            e_s[r] = eid[j];
+            p_s[r] = pos[j];
+            sc[r] = f_s[r] == 2 ? -INFINITY : cand_score[(size_t)t * K1 + (f_s[r] == 1 ? k : r)];
+            if (f_s[r] != 2) m = fmaxf(m, sc[r]);
+        }
+        float z = 0.0f;
+        for (int r = 0; r < k; r++)
+            if (f_s[r] != 2) z += expf(sc[r] - m);
+        for (int r = 0; r < k; r++) {
+            const size_t j = (size_t)t * k + r;
+            if (f_s[r] == 2) {
+                row[j] = -1;
+                gate[j] = 0.0f;
+            } else {
+                const int rw = offs[e_s[r]] + p_s[r];
+                row[j] = rw;
+                token_of_row[rw] = t;
+                gate[j] = expf(sc[r] - m) / z;
+            }
+        }
+    }
+
+    // rows past the last kept row carry no token
+    const int rows = offs[E];
+    for (int i = rows + b * kThreads + threadIdx.x; i < cap_rows; i += nb * kThreads) token_of_row[i] = -1;
+
+    if (b == 0) {
+        for (int e = threadIdx.x; e <= E; e += kThreads) offsets[e] = offs[e];
+        for (int e = threadIdx.x; e < E; e += kThreads) {
+            int dem = 0;
+            for (int bb = 0; bb < nb; bb++)
+                for (int r = 0; r < k; r++) dem += hist[((size_t)bb * k + r) * E + e];
+            demand[e] = dem;
+            kept[e] = kcnt[e];
+            scan_tmp[0][e] = dem;  // reuse for the loss below
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            int rer = 0;
+            double l = 0.0;
+            for (int e = 0; e < E; e++) {
+                rer += kcnt[e] - fill_prim[e];
+                const double u = T > 0 ? (double)scan_tmp[0][e] / (double)T : 0.0;
+                l += u * u;
+            }
+            totals[0] = rows;
+            totals[1] = T * k - rows;
+            totals[2] = rer;
+            aux_loss[0] = (float)((double)aux_coef * l);
+        }
+    }
+}
+
+// x_perm[row[t][j]] = x[t] for every kept slot: the token row is read once.
+__global__ __launch_bounds__(256) void dispatch_gather(const uint4 *__restrict__ x,
+                                                       const int32_t *__restrict__ row, int k,
+                                                       int chunks, uint4 *__restrict__ x_perm) {
+    const int t = blockIdx.x;
+    int rws[kMaxTopK];
+    for (int r = 0; r < k; r++) rws[r] = row[(size_t)t * k + r];
+    for (int c = threadIdx.x; c < chunks; c += 256) {
+        const uint4 v = x[(size_t)t * chunks + c];
+        for (int r = 0; r < k; r++)
+            if (rws[r] >= 0) x_perm[(size_t)rws[r] * chunks + c] = v;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
+                           void *x_perm, const DispatchScratch &ws, hipStream_t st) {
+    const int T = p.T, E = p.E, k = p.k;
+    const int nb = (int)ceil_div(T > 0 ? T : 1, kThreads);
+    const int use_fb = (p.reroute && k < E) ? 1 : 0;
+    int64_t cap_rows = (int64_t)T * k;
+    if ((int64_t)E * C < cap_rows) cap_rows = (int64_t)E * C;
+    hipLaunchKernelGGL(dispatch_hist, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, ws.hist);
+    hipLaunchKernelGGL(dispatch_primary, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, (int)C,
+                       nb, use_fb, ws.hist, ws.fill_prim, r.eid, r.pos, r.flag, ws.fb_hist);
+    hipLaunchKernelGGL(dispatch_finalize, dim3(nb), dim3(kThreads), 0, st, r.cand, r.cand_score, T,
+                       E, k, (int)C, nb, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim,
+                       ws.fb_hist, r.eid, r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row,
+                       r.demand, r.kept, r.totals, r.aux_loss);
+    if (T > 0) {
+        const int esz = p.dtype == MOE_BF16 ? 2 : 4;
+        const int chunks = p.d * esz / 16;
+        hipLaunchKernelGGL(dispatch_gather, dim3(T), dim3(256), 0, st,
+                           static_cast<const uint4 *>(x), r.row, k, chunks,
+                           static_cast<uint4 *>(x_perm));
+    }
+    return hipGetLastError();
+}
+
+}  // namespace moe

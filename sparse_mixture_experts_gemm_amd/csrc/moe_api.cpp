@@ -1,0 +1,188 @@
+// C ABI of the MoE layer: argument checks, capacity, workspace carving and
+// kernel launches on the caller's stream.  No allocation, no synchronisation.
+#include <math.h>
+#include <string.h>
+
+#include "moe_internal.h"
+
+using namespace moe;
+
+namespace {
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+// Shape checks shared by every entry point.
+int check_params(const moe_params *p) {
+    if (!p) return MOE_ERR_INVALID_ARG;
+    if (p->T < 0 || p->T > (1 << 20)) return MOE_ERR_INVALID_ARG;
+    if (p->E < 1 || p->E > kMaxExperts) return MOE_ERR_INVALID_ARG;
+    if (p->k < 1 || p->k > kMaxTopK || p->k > p->E) return MOE_ERR_INVALID_ARG;
+    if (p->d < 1 || p->d_ff < 1) return MOE_ERR_INVALID_ARG;
+    if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
+    if (p->d % 64 != 0 || p->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
+    if (p->d > (p->dtype == MOE_BF16 ? 16384 : 8192)) return MOE_ERR_UNSUPPORTED;
+    if (!(p->lambda == p->lambda) || !(p->capacity_factor == p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+int64_t capacity_of(const moe_params &p) {
+    if (p.capacity_factor <= 0.0f) return p.T;
+    const double c = ceil((double)p.T * (double)p.k / (double)p.E * (double)p.capacity_factor);
+    int64_t C = (int64_t)c;
+    if (C > p.T) C = p.T;
+    if (C < 0) C = 0;
+    return C;
+}
+
+int64_t max_rows_of(const moe_params &p) {
+    const int64_t C = capacity_of(p);
+    const int64_t a = (int64_t)p.T * p.k, b = (int64_t)p.E * C;
+    return a < b ? a : b;
+}
+
+size_t esize(const moe_params &p) { return p.dtype == MOE_BF16 ? 2 : 4; }
+
+// Per-token arrays may be NULL for an empty batch, token_of_row when R = 0.
+int routing_ok(const moe_routing *r, const moe_params &p) {
+    if (!r) return 0;
+    if (!(r->offsets && r->demand && r->kept && r->totals && r->aux_loss)) return 0;
+    if (p.T > 0 && !(r->cand && r->cand_score && r->eid && r->pos && r->row && r->flag && r->gate))
+        return 0;
+    if (max_rows_of(p) > 0 && !r->token_of_row) return 0;
+    return 1;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+// Workspace layout of moe_forward.
+struct ForwardWs {
+    void *dispatch, *x_perm, *h, *y_perm;
+};
+
+size_t forward_ws_bytes(const moe_params &p) {
+    const size_t R = (size_t)max_rows_of(p);
+    return align256(dispatch_scratch_bytes(p.T, p.E, p.k)) + align256(R * p.d * esize(p)) +
+           align256(R * p.d_ff * esize(p)) + align256(R * p.d * sizeof(float));
+}
+
+ForwardWs carve_forward(void *ws, const moe_params &p) {
+    const size_t R = (size_t)max_rows_of(p);
+    char *c = static_cast<char *>(ws);
+    ForwardWs f;
+    f.dispatch = c;
+    c += align256(dispatch_scratch_bytes(p.T, p.E, p.k));
+    f.x_perm = c;
+    c += align256(R * p.d * esize(p));
+    f.h = c;
+    c += align256(R * p.d_ff * esize(p));
+    f.y_perm = c;
+    return f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t moe_capacity(const moe_params *p) {
+    if (check_params(p) != MOE_OK) return -1;
+    return capacity_of(*p);
+}
+
+int64_t moe_max_rows(const moe_params *p) {
+    if (check_params(p) != MOE_OK) return -1;
+    return max_rows_of(*p);
+}
+
+size_t moe_dispatch_workspace_bytes(const moe_params *p) {
+    if (check_params(p) != MOE_OK) return 0;
+    return dispatch_scratch_bytes(p->T, p->E, p->k);
+}
+
+size_t moe_workspace_bytes(const moe_params *p) {
+    if (check_params(p) != MOE_OK) return 0;
+    return forward_ws_bytes(*p);
+}
+
+int moe_route(const moe_params *p, const void *x, const void *w_router, const float *bias,
+              const float *load, float *logits, moe_routing *r, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    if (!routing_ok(r, *p) || (p->T > 0 && (!x || !logits)) || !w_router) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_route(*p, x, w_router, bias, load, logits, r->cand, r->cand_score,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+int moe_dispatch(const moe_params *p, const void *x, moe_routing *r, void *x_perm,
+                 void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    if (!routing_ok(r, *p) || !workspace || (p->T > 0 && (!x || !x_perm))) return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < dispatch_scratch_bytes(p->T, p->E, p->k)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(x_perm) || !aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
+    const DispatchScratch s = carve_dispatch(workspace, p->T, p->E, p->k);
+    return hip_status(launch_dispatch(*p, capacity_of(*p), x, *r, x_perm, s,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                   const void *w1, const void *w3, const void *w2, void *h, void *y_perm,
+                   void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    const int64_t R = max_rows_of(*p);
+    if (!offsets || !w1 || !w3 || !w2) return MOE_ERR_INVALID_ARG;
+    if (R > 0 && (!x_perm || !h || !y_perm)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(h) ||
+        !aligned16(y_perm))
+        return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_expert_ffn(*p, R, x_perm, offsets, w1, w3, w2, h, y_perm,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
+                void *y, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    if (p->T > 0 && (!row || !gate || !y || (max_rows_of(*p) > 0 && !y_perm))) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_combine(*p, y_perm, row, gate, y, static_cast<hipStream_t>(stream)));
+}
+
+int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                const float *load, const void *w1, const void *w3, const void *w2, void *y,
+                float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    if (!routing_ok(r, *p) || !w_router || !w1 || !w3 || !w2 || !workspace ||
+        (p->T > 0 && (!x || !y || !logits)))
+        return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < forward_ws_bytes(*p)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w3) ||
+        !aligned16(w2) || !aligned16(y) || !aligned16(workspace))
+        return MOE_ERR_UNSUPPORTED;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const ForwardWs f = carve_forward(workspace, *p);
+    const int64_t C = capacity_of(*p);
+    const int64_t R = max_rows_of(*p);
+    hipError_t e = launch_route(*p, x, w_router, bias, load, logits, r->cand, r->cand_score, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = launch_dispatch(*p, C, x, *r, f.x_perm, carve_dispatch(f.dispatch, p->T, p->E, p->k), st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = launch_expert_ffn(*p, R, f.x_perm, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    e = launch_combine(*p, f.y_perm, r->row, r->gate, y, st);
+    return hip_status(e);
+}
+
+const char *moe_strerror(int code) {
+    switch (code) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, size out of range or workspace too small)";
+        case MOE_ERR_UNSUPPORTED: return "unsupported dtype, alignment or dimension";
+        case MOE_ERR_HIP: return "HIP kernel launch failed";
+        default: return "unknown error code";
+    }
+}
+
+}  // extern "C"

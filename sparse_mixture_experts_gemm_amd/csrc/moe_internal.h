@@ -1,0 +1,58 @@
+// Internal interface between the C ABI (moe_api.cpp) and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+
+namespace moe {
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+constexpr int kDispatchBlock = 1024;  // tokens per dispatch block
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+// Dispatch scratch: per-block histograms of the primary rounds and of the
+// fallback round, and the per-expert fill after the primary rounds.
+struct DispatchScratch {
+    int32_t *hist;       // [NB][k][E]
+    int32_t *fb_hist;    // [NB][E]
+    int32_t *fill_prim;  // [E]
+};
+
+inline size_t dispatch_scratch_bytes(int T, int E, int k) {
+    int64_t nb = ceil_div(T > 0 ? T : 1, kDispatchBlock);
+    return align256(sizeof(int32_t) * nb * k * E) + align256(sizeof(int32_t) * nb * E) +
+           align256(sizeof(int32_t) * E);
+}
+
+inline DispatchScratch carve_dispatch(void *ws, int T, int E, int k) {
+    int64_t nb = ceil_div(T > 0 ? T : 1, kDispatchBlock);
+    char *p = static_cast<char *>(ws);
+    DispatchScratch s;
+    s.hist = reinterpret_cast<int32_t *>(p);
+    p += align256(sizeof(int32_t) * nb * k * E);
+    s.fb_hist = reinterpret_cast<int32_t *>(p);
+    p += align256(sizeof(int32_t) * nb * E);
+    s.fill_prim = reinterpret_cast<int32_t *>(p);
+    return s;
+}
+
+hipError_t launch_route(const moe_params &p, const void *x, const void *wr, const float *bias,
+                        const float *load, float *logits, int32_t *cand, float *cand_score,
+                        hipStream_t st);
+
+hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
+                           void *x_perm, const DispatchScratch &ws, hipStream_t st);
+
+hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *x_perm,
+                             const int32_t *offsets, const void *w1, const void *w3,
+                             const void *w2, void *h, void *y_perm, hipStream_t st);
+
+hipError_t launch_combine(const moe_params &p, const void *y_perm, const int32_t *row,
+                          const float *gate, void *y, hipStream_t st);
+
+}  // namespace moe

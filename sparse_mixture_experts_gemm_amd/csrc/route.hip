@@ -1,0 +1,259 @@
+// Stage 1: router GEMM + bias + load penalty + top-(k+1) ranking, one kernel.
+//
+// What it computes ("MoE架构揭秘" §3.1; "GPT-4稀疏激活真相" §2.3):
+//   raw[t][e] = sum_i x[t][i] * Wr[e][i] + bias[e]
+//   s[t][e]   = fmaf(-lambda, load[e], raw[t][e])      (raw when load == NULL)
+//   cand[t]   = the k+1 experts with the largest s, ties to the lower index.
+//
+// Mapping on CDNA4.  The router is a skinny GEMM (N = E is 8..256), so it runs
+// on the vector ALU, not MFMA: a wave owns TPW tokens and holds their x rows
+// in registers, 16-byte chunks strided over the 64 lanes.  The gate vectors
+// are staged in LDS in chunks of experts and read conflict-free (consecutive
+// lanes read consecutive 16-byte chunks).  bf16 products are accumulated with
+// v_dot2_f32_bf16.  Each lane ends with 32 partial sums (TPW tokens x EA
+// experts); a butterfly reduce-scatter over the 64 lanes (DPP inside rows of
+// 16, ds_bpermute across rows) leaves one full sum per lane pair, so the
+// cross-lane cost is one shuffle per logit.  Ranking is k+1 wave argmax
+// reductions on (score, index), also DPP/bpermute butterflies.
+//
+// The penalty is an explicit fmaf and the file is built without fast-math, so
+// the fp32 ranking is reproducible from the fp32 logits bit for bit.
+#include "device_common.h"
+#include "moe_internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kRouteThreads = 256;
+constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kRouteLdsW = 64 * 1024;  // bytes of gate vectors staged per chunk
+
+template <typename TIn>
+struct ChunkDot;
+
+// 16-byte chunk = 8 bf16
+template <>
+struct ChunkDot<uint16_t> {
+    static constexpr int kVec = 8;
+    __device__ static __forceinline__ float dot(uint4 a, uint4 b, float acc) {
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x), __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y), __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z), __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+        acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+        return acc;
+    }
+};
+
+// 16-byte chunk = 4 fp32
+template <>
+struct ChunkDot<float> {
+    static constexpr int kVec = 4;
+    __device__ static __forceinline__ float dot(uint4 a, uint4 b, float acc) {
+        acc = __builtin_fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
+        acc = __builtin_fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
+        acc = __builtin_fmaf(__uint_as_float(a.z), __uint_as_float(b.z), acc);
+        acc = __builtin_fmaf(__uint_as_float(a.w), __uint_as_float(b.w), acc);
+        return acc;
+    }
+};
+
+// One butterfly reduce-scatter step: the lane keeps half of its V values
+// (the upper half when its STEP bit is set) and adds the partner's copy.
+template <int STEP, int V>
+__device__ __forceinline__ void rs_step(float (&v)[32], int lane) {
+    const bool upper = (lane & STEP) != 0;
+#pragma unroll
+    for (int i = 0; i < V / 2; i++) {
+        float send = upper ? v[i] : v[i + V / 2];
+        float keep = upper ? v[i + V / 2] : v[i];
+        v[i] = keep + exch_f32<STEP>(send);
+    }
+}
+
+// better(a, b): larger score, ties to the lower index
+__device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
+    return sa > sb || (sa == sb && ia < ib);
+}
+
+template <int STEP>
+__device__ __forceinline__ void argmax_step(float &s, int &i) {
+    float so = exch_f32<STEP>(s);
+    int io = exch_i32<STEP>(i);
+    if (better(so, io, s, i)) {
+        s = so;
+        i = io;
+    }
+}
+
+// NX: 16-byte chunks of one x row per lane; TPW: tokens per wave.
+template <typename TIn, int NX, int TPW>
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(
+    const TIn *__restrict__ x, const TIn *__restrict__ wr, const float *__restrict__ bias,
+    const float *__restrict__ load, float neg_lambda, int T, int d, int E, int K1, int EC,
+    float *__restrict__ logits, int32_t *__restrict__ cand, float *__restrict__ cand_score) {
+    constexpr int EA = 32 / TPW;  // experts accumulated together
+    constexpr int kVec = ChunkDot<TIn>::kVec;
+    extern __shared__ uint4 lds[];
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int nchunk = d / kVec;
+    const int t0 = (blockIdx.x * kRouteWaves + wave) * TPW;
+
+    uint4 *w_lds = lds;                                            // [EC][nchunk]
+    float *lg = reinterpret_cast<float *>(lds + (size_t)EC * nchunk) + wave * TPW * E;  // [TPW][E]
+
+    uint4 xr[TPW][NX];
+#pragma unroll
+    for (int j = 0; j < TPW; j++) {
+        const int t = t0 + j;
+#pragma unroll
+        for (int c = 0; c < NX; c++) {
+            const int ci = lane + 64 * c;
+            if (t < T && ci < nchunk)
+                xr[j][c] = reinterpret_cast<const uint4 *>(x + (size_t)t * d)[ci];
+            else
+                xr[j][c] = make_uint4(0, 0, 0, 0);
+        }
+    }
+
+    for (int e0 = 0; e0 < E; e0 += EC) {
+        const int ec = min(EC, E - e0);
+        __syncthreads();
+        const uint4 *src = reinterpret_cast<const uint4 *>(wr) + (size_t)e0 * nchunk;
+        for (int i = threadIdx.x; i < ec * nchunk; i += kRouteThreads) w_lds[i] = src[i];
+        __syncthreads();
+
+        for (int ea = 0; ea < ec; ea += EA) {
+            float v[32];
+#pragma unroll
+            for (int i = 0; i < 32; i++) v[i] = 0.0f;
+#pragma unroll
+            for (int q = 0; q < EA; q++) {
+                if (ea + q < ec) {
+                    const uint4 *wrow = w_lds + (size_t)(ea + q) * nchunk;
+#pragma unroll
+                    for (int c = 0; c < NX; c++) {
+                        const int ci = lane + 64 * c;
+                        if (ci < nchunk) {
+                            const uint4 w = wrow[ci];
+#pragma unroll
+                            for (int j = 0; j < TPW; j++) v[j * EA + q] = ChunkDot<TIn>::dot(xr[j][c], w, v[j * EA + q]);
+                        }
+                    }
+                }
+            }
+            // reduce-scatter: lane keeps value index (lane >> 1) & 31
+            rs_step<32, 32>(v, lane);
+            rs_step<16, 16>(v, lane);
+            rs_step<8, 8>(v, lane);
+            rs_step<4, 4>(v, lane);
+            rs_step<2, 2>(v, lane);
+            v[0] += exch_f32<1>(v[0]);
+            const int idx = (lane >> 1) & 31;
+            const int j = idx / EA, q = idx % EA;
+            const int e = e0 + ea + q;
+            if ((lane & 1) == 0 && ea + q < ec) {
+                float r = v[0];
+                if (bias) r = r + bias[e];
+                lg[j * E + e] = r;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ranking: lanes hold experts e = lane + 64 * i
+    constexpr int kMaxPerLane = kMaxExperts / 64;
+    for (int j = 0; j < TPW; j++) {
+        const int t = t0 + j;
+        if (t >= T) break;  // wave-uniform
+        float sc[kMaxPerLane];
+        uint32_t avail = 0;
+#pragma unroll
+        for (int i = 0; i < kMaxPerLane; i++) {
+            const int e = lane + 64 * i;
+            sc[i] = -INFINITY;
+            if (e < E) {
+                const float raw = lg[j * E + e];
+                logits[(size_t)t * E + e] = raw;
+                sc[i] = load ? __builtin_fmaf(neg_lambda, load[e], raw) : raw;
+                avail |= 1u << i;
+            }
+        }
+        for (int r = 0; r < K1; r++) {
+            float bs = -INFINITY;
+            int bi = 0x7fffffff;
+#pragma unroll
+            for (int i = 0; i < kMaxPerLane; i++) {
+                const int e = lane + 64 * i;
+                if ((avail >> i) & 1) {
+                    if (better(sc[i], e, bs, bi)) {
+                        bs = sc[i];
+                        bi = e;
+                    }
+                }
+            }
+            argmax_step<1>(bs, bi);
+            argmax_step<2>(bs, bi);
+            argmax_step<4>(bs, bi);
+            argmax_step<8>(bs, bi);
+            argmax_step<16>(bs, bi);
+            argmax_step<32>(bs, bi);
+            const bool none = bi == 0x7fffffff;
+            if (lane == 0) {
+                cand[(size_t)t * K1 + r] = none ? -1 : bi;
+                cand_score[(size_t)t * K1 + r] = none ? -INFINITY : bs;
+            }
+            if (!none && (bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+        }
+    }
+}
+
+template <typename TIn, int NX, int TPW>
+hipError_t launch_t(const moe_params &p, const void *x, const void *wr, const float *bias,
+                    const float *load, float *logits, int32_t *cand, float *cand_score,
+                    hipStream_t st) {
+    const int esz = sizeof(TIn);
+    const int row_bytes = p.d * esz;
+    int ec = kRouteLdsW / row_bytes;  // experts staged per LDS chunk
+    if (ec < 1) ec = 1;
+    if (ec > p.E) ec = p.E;
+    const size_t lds = (size_t)ec * row_bytes + sizeof(float) * kRouteWaves * TPW * p.E;
+    // dynamic LDS above the default limit must be allowed per kernel
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&route_kernel<TIn, NX, TPW>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int tokens_per_block = kRouteWaves * TPW;
+    const int grid = (int)ceil_div(p.T, tokens_per_block);
+    hipLaunchKernelGGL((route_kernel<TIn, NX, TPW>), dim3(grid), dim3(kRouteThreads), lds, st,
+                       static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load,
+                       -p.lambda, p.T, p.d, p.E, p.k + 1, ec, logits, cand, cand_score);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t launch_dtype(const moe_params &p, const void *x, const void *wr, const float *bias,
+                        const float *load, float *logits, int32_t *cand, float *cand_score,
+                        hipStream_t st) {
+    constexpr int kVec = ChunkDot<TIn>::kVec;
+    const int nx = (int)ceil_div(p.d / kVec, 64);
+    if (nx <= 1) return launch_t<TIn, 1, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 2) return launch_t<TIn, 2, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 4) return launch_t<TIn, 4, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 8) return launch_t<TIn, 8, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 16) return launch_t<TIn, 16, 2>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 32) return launch_t<TIn, 32, 1>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_route(const moe_params &p, const void *x, const void *wr, const float *bias,
+                        const float *load, float *logits, int32_t *cand, float *cand_score,
+                        hipStream_t st) {
+    if (p.T == 0) return hipSuccess;
+    if (p.dtype == MOE_BF16)
+        return launch_dtype<uint16_t>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    return launch_dtype<float>(p, x, wr, bias, load, logits, cand, cand_score, st);
+}
+
+}  // namespace moe

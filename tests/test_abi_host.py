@@ -1,0 +1,107 @@
+"""Host-side checks of the C ABI library: it loads, exports what include/moe.h
+declares, and its pure host functions and argument checks behave (no GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_mixture_experts_gemm_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(ROOT, "include", "moe.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(moe_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_forward"} <= set(names)
+    L = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in include/moe.h but not exported"
+
+
+def P(**kw):
+    base = dict(T=64, d=128, E=8, k=2, d_ff=256, capacity_factor=1.0, reroute=1, lam=0.0,
+                aux_coef=0.01, dtype=moe.MOE_F32)
+    base.update(kw)
+    return moe.Params(**base)
+
+
+def test_capacity_matches_oracle(oracle_mod):
+    cases = [(64, 2, 8, 1.0), (4096, 2, 8, 1.25), (8192, 2, 64, 1.0), (2048, 2, 16, 1.0),
+             (64, 2, 8, 1.25), (32, 2, 64, 1.3), (1000, 3, 7, 1.1), (5, 1, 8, 0.0), (7, 2, 3, 50.0),
+             (0, 2, 8, 1.0), (1, 1, 1, 1.0)]
+    for T, k, E, cf in cases:
+        p = P(T=T, k=k, E=E, capacity_factor=cf)
+        assert moe.capacity(p) == oracle_mod.capacity(T, k, E, cf), (T, k, E, cf)
+        C = oracle_mod.capacity(T, k, E, cf)
+        assert moe.max_rows(p) == min(T * k, E * C)
+
+
+def test_workspace_sizes_cover_buffers():
+    p = P(T=4096, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
+    R = moe.max_rows(p)
+    assert R == 8192
+    ws = moe.workspace_bytes(p)
+    assert ws >= R * (4096 + 14336 + 4096) * 2
+    assert moe.dispatch_workspace_bytes(p) > 0
+
+
+@pytest.mark.parametrize("bad", [dict(E=0), dict(E=257), dict(k=0), dict(k=9, E=16), dict(k=3, E=2),
+                                 dict(T=-1), dict(T=(1 << 20) + 1), dict(d=0)])
+def test_invalid_sizes_rejected(bad):
+    p = P(**bad)
+    assert moe.capacity(p) == -1
+    assert moe.workspace_bytes(p) == 0
+    r = moe.MoeRouting()
+    rc = moe.lib().moe_route(ctypes.byref(p.c()), None, None, None, None, None, ctypes.byref(r), None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("bad", [dict(d=100), dict(d_ff=96), dict(dtype=7), dict(d=16384 + 64)])
+def test_unsupported_shapes_rejected(bad):
+    p = P(**bad)
+    r = moe.MoeRouting()
+    rc = moe.lib().moe_forward(ctypes.byref(p.c()), None, None, None, None, None, None, None, None,
+                               None, ctypes.byref(r), None, 0, None)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_null_pointers_rejected():
+    p = P()
+    r = moe.MoeRouting()  # all members NULL
+    assert moe.lib().moe_route(ctypes.byref(p.c()), 16, 16, None, None, 16, ctypes.byref(r), None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_dispatch(ctypes.byref(p.c()), 16, ctypes.byref(r), 16, 16, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_expert_ffn(ctypes.byref(p.c()), 16, None, 16, 16, 16, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_combine(ctypes.byref(p.c()), 16, None, None, 16, None) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_workspace_too_small_rejected():
+    p = P()
+    names = moe.Routing.NAMES
+    r = moe.MoeRouting(*[256] * len(names))  # non-null fake addresses; never dereferenced
+    need = moe.workspace_bytes(p)
+    rc = moe.lib().moe_forward(ctypes.byref(p.c()), 256, 256, None, None, 256, 256, 256, 256, 256,
+                               ctypes.byref(r), 256, need - 1, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    rc = moe.lib().moe_dispatch(ctypes.byref(p.c()), 256, ctypes.byref(r), 256, 256,
+                                moe.dispatch_workspace_bytes(p) - 1, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+
+
+def test_misaligned_pointer_rejected():
+    p = P()
+    r = moe.MoeRouting(*[256] * len(moe.Routing.NAMES))
+    rc = moe.lib().moe_route(ctypes.byref(p.c()), 258, 256, None, None, 256, ctypes.byref(r), None)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_strerror():
+    assert moe.strerror(0) == "ok"
+    for c in (-1, -2, -3, 5):
+        assert isinstance(moe.strerror(c), str) and moe.strerror(c)

@@ -1,0 +1,333 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Routing arrays must be bit-exact with the oracle run on the GPU's fp32 router
+logits.  Layer outputs (and y_perm) must satisfy max|err| <= 2e-2 * RMS(ref)
+for bf16 (fp32 accumulation) and <= 1e-4 * RMS(ref) for fp32; edge cases in
+which whole tokens are dropped take the RMS over the tokens that kept a slot.
+Intermediates rounded once (h, the combine's store) are held to one ulp of
+their storage type per element.  Router logits are compared with the
+oracle's own double-accumulated logits at 1e-3 * RMS.
+
+The five workloads run at their full sizes; where the oracle would take too
+long on every row, sampled rows and tokens (tile boundaries, ragged tails,
+re-routed and dropped tokens, random picks) are computed one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_synth
+import oracle
+import sparse_mixture_experts_gemm_amd as moe
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+TOL = {moe.MOE_BF16: 2e-2, moe.MOE_F32: 1e-4}
+ROUTING_EXACT = ("cand", "cand_score", "eid", "pos", "row", "flag", "offsets", "token_of_row",
+                 "demand", "kept", "totals")
+
+
+def say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    moe.lib()
+    oracle.lib()
+
+
+def np_of(t):
+    return oracle._np(t)
+
+
+def rms(a):
+    return float(np.sqrt(np.mean(np.asarray(a, np.float64) ** 2)))
+
+
+def assert_close(got, ref, dtype, what, rms_rows=None):
+    """max|err| <= tol * RMS(ref); rms_rows selects the rows the RMS is taken
+    over (edge cases with many fully dropped tokens use the kept rows)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    r = rms(ref if rms_rows is None else ref[rms_rows])
+    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    assert err <= TOL[dtype] * r + 1e-30, f"{what}: max|err| {err:.3e} > {TOL[dtype]} * RMS {r:.3e}"
+    return err / r if r > 0 else 0.0
+
+
+def assert_close_elementwise(got, ref, rel, floor, what):
+    """Each element is one fp32 result rounded once to its storage type, so
+    |err| <= rel * |ref| + floor * RMS(ref), rel one ulp of the storage type
+    (2^-10 for fp16, 2^-8 for bf16) and the floor covering fp32 accumulation
+    where the exact value cancels to near zero."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bound = rel * np.abs(ref) + floor * rms(ref)
+    bad = np.abs(got - ref) > bound
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond rounding bound, first {np.argwhere(bad)[:3]}"
+
+
+def params(cfg, T=None, **over):
+    kw = dict(T=cfg.T if T is None else T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff,
+              capacity_factor=cfg.cf, reroute=cfg.reroute, lam=cfg.lam, aux_coef=cfg.aux_coef,
+              dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32)
+    kw.update(over)
+    return moe.Params(**kw)
+
+
+def load_for(cfg, L, T):
+    """Previous batch's kept fraction per expert, routed by the oracle without a penalty."""
+    if not cfg.load_from_prev:
+        return None
+    xp = L["x_prev"]
+    raw = oracle.router_logits(xp, L["w_router"], L["bias"])
+    c, cs = oracle.route(raw, cfg.k)
+    dp = oracle.dispatch(c, cs, cfg.E, cfg.k, oracle.capacity(T, cfg.k, cfg.E, cfg.cf), cfg.reroute)
+    return (dp["kept"].astype(np.float32) / np.float32(T * cfg.k)).astype(np.float32)
+
+
+def routing_vs_oracle(p, rc, logits_np, load_np, lam):
+    """Oracle routing from the GPU's logits; every array bit-exact."""
+    cand, cs = oracle.route(logits_np, p.k, load_np, lam)
+    C = oracle.capacity(p.T, p.k, p.E, p.capacity_factor)
+    ref = oracle.dispatch(cand, cs, p.E, p.k, C, p.reroute, p.aux_coef)
+    ref["cand"], ref["cand_score"] = cand, cs
+    for n in ROUTING_EXACT:
+        a = rc[n].numpy()
+        b = ref[n]
+        assert a.shape == b.shape, (n, a.shape, b.shape)
+        if n == "cand_score":
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), f"{n} not bit-exact"
+        else:
+            assert np.array_equal(a, b), f"routing array {n} differs: first at {np.argwhere(a != b)[:3]}"
+    g = rc["gate"].numpy().astype(np.float64)
+    assert np.allclose(g, ref["gate64"], rtol=1e-6, atol=1e-7), "gates"
+    assert math.isclose(float(rc["aux_loss"][0]), float(ref["aux_loss"][0]), rel_tol=1e-6, abs_tol=1e-12)
+    return ref
+
+
+class Layer:
+    """Inputs of one workload, drawn once on the GPU; CPU copies for the oracle."""
+
+    def __init__(self, cfg, T=None):
+        self.cfg = cfg
+        self.T = cfg.T if T is None else T
+        say(f"[gen] {cfg.name} T={self.T}")
+        self.g = moe_synth.make_layer(cfg, DEV, T=self.T)
+        torch.cuda.synchronize()
+        self.c = {n: (np_of(v) if v is not None else None) for n, v in self.g.items()}
+        self.load = load_for(cfg, self.c, self.T)
+        self.load_g = torch.from_numpy(self.load).to(DEV) if self.load is not None else None
+
+
+def sample_tokens(ref, T, n_rand, rng):
+    picks = {0, T - 1}
+    flags = ref["flag"]
+    for code in (1, 2):
+        hit = np.nonzero((flags == code).any(axis=1))[0]
+        picks.update(hit[:2].tolist())
+    picks.update(rng.choice(T, size=min(n_rand, T), replace=False).tolist())
+    return np.array(sorted(picks), np.int32)
+
+
+def sample_rows(offsets, n_per, rng, cap=48):
+    rows = set()
+    E = len(offsets) - 1
+    experts = [e for e in range(E) if offsets[e + 1] > offsets[e]]
+    if len(experts) * n_per > cap:
+        experts = sorted(rng.choice(experts, size=max(1, cap // n_per), replace=False).tolist())
+    for e in experts:
+        b, en = int(offsets[e]), int(offsets[e + 1])
+        for r in (b, en - 1, b + 255, b + 256, (b + en) // 2):
+            if b <= r < en:
+                rows.add(r)
+    return np.array(sorted(rows), np.int32)
+
+
+def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
+    """Run the four stage entry points, check each against the oracle, then
+    moe_forward end to end."""
+    cfg = L.cfg
+    g = L.g
+    dt = p.torch_dtype
+    T, E, k, d, dff = p.T, p.E, p.k, p.d, p.d_ff
+    R = moe.max_rows(p)
+    rng = np.random.default_rng(123)
+
+    # ---- route
+    say(f"[route] {cfg.name} T={T}")
+    r = moe.Routing(p, DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe.route(p, g["x"], g["w_router"], g["bias"], L.load_g, logits, r)
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy()
+    tok = np.arange(T) if T <= 512 else np.unique(np.r_[0, T - 1, rng.choice(T, 256, replace=False)])
+    own = oracle.router_logits(L.c["x"][tok], L.c["w_router"], L.c["bias"])
+    assert np.abs(own - gl[tok]).max() <= 1e-3 * rms(own), "router logits"
+    rc = r.cpu()
+    cand, cs = oracle.route(gl, k, L.load, p.lam)
+    assert np.array_equal(rc["cand"].numpy(), cand), "cand"
+    assert np.array_equal(rc["cand_score"].numpy().view(np.uint32), cs.view(np.uint32)), "cand_score"
+
+    # ---- dispatch
+    say(f"[dispatch] {cfg.name}")
+    x_perm = torch.empty((max(R, 1), d), dtype=dt, device=DEV)
+    ws = moe.alloc_workspace(p, DEV, dispatch_only=True)
+    moe.dispatch(p, g["x"], r, x_perm, ws)
+    torch.cuda.synchronize()
+    rc = r.cpu()
+    ref = routing_vs_oracle(p, rc, gl, L.load, p.lam)
+    rows = int(ref["totals"][0])
+    tor = ref["token_of_row"][:rows]
+    assert torch.equal(x_perm[:rows].cpu(), g["x"].cpu()[torch.from_numpy(tor.astype(np.int64))]), "x_perm"
+
+    # ---- expert FFN
+    say(f"[expert_ffn] {cfg.name} rows={rows}")
+    h = torch.empty((max(R, 1), dff), dtype=torch.float16 if p.dtype == moe.MOE_BF16 else dt, device=DEV)
+    y_perm = torch.empty((max(R, 1), d), dtype=torch.float32, device=DEV)
+    moe.expert_ffn(p, x_perm, r.offsets, g["w1"], g["w3"], g["w2"], h, y_perm)
+    torch.cuda.synchronize()
+    offs = ref["offsets"]
+    srows = np.arange(rows, dtype=np.int32) if full_rows else sample_rows(offs, 5, rng)
+    if len(srows):
+        expert_of = np.searchsorted(offs, srows, side="right").astype(np.int32) - 1
+        xp = np_of(x_perm[:rows].cpu())
+        yo, ho = oracle.ffn_rows(expert_of, srows, xp, L.c["w1"], L.c["w3"], L.c["w2"], want_h=True)
+        if p.dtype == moe.MOE_BF16:
+            assert_close_elementwise(h.float().cpu().numpy()[srows], ho, 2.0 ** -10, 1e-4, "h")
+        else:
+            assert_close_elementwise(h.cpu().numpy()[srows], ho, 1e-5, 1e-5, "h")
+        assert_close(y_perm.cpu().numpy()[srows], yo, p.dtype, "y_perm")
+
+    # ---- combine
+    say(f"[combine] {cfg.name}")
+    y = torch.empty((T, d), dtype=dt, device=DEV)
+    moe.combine(p, y_perm, r.row, r.gate, y)
+    torch.cuda.synchronize()
+    yc = oracle.combine(rc["row"].numpy(), rc["gate"].numpy(), np_of(y_perm[:max(rows, 1)].cpu()))
+    # combine's only rounding is the final store
+    assert_close_elementwise(y.float().cpu().numpy(), yc, 2.0 ** -8 if p.dtype == moe.MOE_BF16 else 1e-6,
+                             1e-6, "combine")
+
+    # ---- forward, end to end
+    say(f"[forward] {cfg.name}")
+    r2 = moe.Routing(p, DEV)
+    y2 = torch.empty((T, d), dtype=dt, device=DEV)
+    logits2 = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    wsf = moe.alloc_workspace(p, DEV)
+    moe.forward(p, g["x"], g["w_router"], g["bias"], L.load_g, g["w1"], g["w3"], g["w2"], y2, logits2, r2, wsf)
+    torch.cuda.synchronize()
+    gl2 = logits2.cpu().numpy()
+    assert np.array_equal(gl2.view(np.uint32), gl.view(np.uint32)), "forward logits differ from moe_route"
+    rc2 = r2.cpu()
+    ref2 = routing_vs_oracle(p, rc2, gl2, L.load, p.lam)
+    toks = np.arange(T, dtype=np.int32) if (full_rows or T <= 64) else sample_tokens(ref2, T, n_tok, rng)
+    yref = oracle.layer_tokens(toks, L.c["x"], L.c["w1"], L.c["w3"], L.c["w2"], ref2["eid"], ref2["gate64"])
+    kept_rows = (ref2["flag"][toks] != 2).any(axis=1) if rms_kept_rows else None
+    rel = assert_close(y2.float().cpu().numpy()[toks], yref, p.dtype, "layer output", kept_rows)
+    # informational: routing under the oracle's own logits
+    say(f"[ok] {cfg.name}: rows={rows} dropped={int(ref2['totals'][1])} rerouted={int(ref2['totals'][2])} "
+        f"max|err|/RMS={rel:.2e}")
+    return dict(ref=ref2, y=y2, rc=rc2)
+
+
+@pytest.mark.parametrize("name", ["tiny", "skew", "decode", "fine64", "mixtral"])
+def test_workload_parity(name):
+    cfg = moe_synth.CONFIGS[name]
+    L = Layer(cfg)
+    p = params(cfg)
+    run_stages(L, p, full_rows=(name == "tiny"))
+
+
+def small_cfg(**kw):
+    base = dict(name="small", T=700, d=256, E=4, k=2, d_ff=384, cf=1.0, dtype="bf16")
+    base.update(kw)
+    return moe_synth.MoEConfig(**base)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_tiles_and_ragged_tails_full(dtype):
+    """Several GEMM tiles per expert and ragged tails, every row and token checked."""
+    cfg = small_cfg(dtype=dtype)
+    L = Layer(cfg)
+    run_stages(L, params(cfg), full_rows=True)
+
+
+EDGE = {
+    "one_token": dict(T=1),
+    "ragged_T": dict(T=1003, E=5, d=128, d_ff=192),
+    "k_equals_E": dict(E=2, k=2, T=300, cf=0.6),
+    "capacity_one": dict(T=200, cf=1e-6),
+    "uncapped": dict(T=300, cf=0.0),
+    "no_reroute": dict(T=400, cf=0.5, reroute=0),
+    "dense_E1": dict(E=1, k=1, T=100, cf=0.0),
+    "many_experts_top8": dict(E=256, k=8, T=512, d=64, d_ff=64, cf=1.0),
+    "min_dims_f32": dict(T=77, d=64, d_ff=64, dtype="f32", E=3, k=1),
+    "bias_penalty": dict(T=500, E=16, bias="hot0", bias_hot=3.0, lam=0.3, load_from_prev=True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(EDGE))
+def test_edge_cases(case):
+    cfg = small_cfg(**EDGE[case])
+    L = Layer(cfg)
+    run_stages(L, params(cfg), full_rows=True, rms_kept_rows=True)
+
+
+def test_empty_batch():
+    cfg = small_cfg(T=0)
+    p = params(cfg)
+    g = moe_synth.make_layer(cfg, DEV, T=0)
+    r = moe.Routing(p, DEV)
+    # poison the outputs that must be written
+    for n in ("offsets", "demand", "kept", "totals"):
+        getattr(r, n).fill_(-7)
+    r.aux_loss.fill_(5.0)
+    y = torch.empty((0, cfg.d), dtype=torch.bfloat16, device=DEV)
+    logits = torch.empty((0, cfg.E), dtype=torch.float32, device=DEV)
+    ws = moe.alloc_workspace(p, DEV)
+    moe.forward(p, g["x"], g["w_router"], None, None, g["w1"], g["w3"], g["w2"], y, logits, r, ws)
+    torch.cuda.synchronize()
+    rc = r.cpu()
+    assert (rc["offsets"] == 0).all() and (rc["demand"] == 0).all() and (rc["kept"] == 0).all()
+    assert (rc["totals"] == 0).all() and float(rc["aux_loss"][0]) == 0.0
+
+
+def test_identical_tokens_tied_logits():
+    """All tokens equal: every logit row is the same, so ties and capacity
+    decide everything; routing must still match bit for bit."""
+    cfg = small_cfg(T=600, E=8, cf=1.0)
+    L = Layer(cfg)
+    L.g["x"][:] = L.g["x"][0:1]
+    L.c["x"] = np_of(L.g["x"].cpu())
+    # tie two experts exactly: identical gate vectors
+    L.g["w_router"][3] = L.g["w_router"][1]
+    L.c["w_router"] = np_of(L.g["w_router"].cpu())
+    out = run_stages(L, params(cfg), full_rows=True, rms_kept_rows=True)
+    assert out["ref"]["totals"][1] > 0  # capacity exhausted
+
+
+def test_deterministic_rerun():
+    cfg = moe_synth.CONFIGS["skew"]
+    L = Layer(cfg, T=1024)
+    p = params(cfg, T=1024)
+    outs = []
+    for _ in range(2):
+        r = moe.Routing(p, DEV)
+        y = torch.empty((p.T, p.d), dtype=torch.bfloat16, device=DEV)
+        logits = torch.empty((p.T, p.E), dtype=torch.float32, device=DEV)
+        ws = moe.alloc_workspace(p, DEV)
+        moe.forward(p, L.g["x"], L.g["w_router"], L.g["bias"], L.load_g, L.g["w1"], L.g["w3"], L.g["w2"],
+                    y, logits, r, ws)
+        torch.cuda.synchronize()
+        outs.append((y.cpu(), r.cpu()))
+    assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
+    for n in moe.Routing.NAMES:
+        assert torch.equal(outs[0][1][n], outs[1][1][n]), n
