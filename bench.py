@@ -1,0 +1,222 @@
+"""Benchmark: sparse MoE FFN layer forward (moe_forward) on one MI355X.
+
+One step = one moe_forward over one batch of seeded synthetic tokens (route,
+dispatch, expert SwiGLU grouped GEMM, combine), inputs and weights resident in
+HBM.  Prints one JSON line with tokens/s, the expert GEMM's roofline figures
+and the CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral]
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec + expert-GEMM MFMA util %, Mixtral-shape E=8 top-2 bf16"
+PEAK_MFMA_TFLOPS = 2516.6   # bf16 / fp16 dense matrix peak, MI355X
+PEAK_HBM_GBS = 8000.0       # HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="mixtral",
+                    choices=["tiny", "mixtral", "fine64", "skew", "decode"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    return ap.parse_args()
+
+
+def stage_bytes_flops(cfg, rows, active_experts):
+    """Algorithmic work per stage (what the method must touch)."""
+    T, d, E, dff = cfg.T, cfg.d, cfg.E, cfg.d_ff
+    es = 2 if cfg.dtype == "bf16" else 4
+    k1 = cfg.k + 1
+    route_bytes = T * d * es + E * d * es + T * E * 4 + T * k1 * 8
+    # dispatch: candidates in, routing arrays out, x rows read once, x_perm written
+    dispatch_bytes = T * k1 * 8 + T * cfg.k * 17 + T * d * es + rows * d * es
+    gemm_flops = rows * 6.0 * d * dff
+    gemm_weight_bytes = active_experts * 3 * d * dff * es
+    combine_bytes = rows * d * 4 + T * d * es + T * cfg.k * 8
+    return dict(route_bytes=route_bytes, dispatch_bytes=dispatch_bytes, gemm_flops=gemm_flops,
+                gemm_weight_bytes=gemm_weight_bytes, combine_bytes=combine_bytes,
+                route_flops=2.0 * T * d * E)
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs the MoE layer on one GPU (all experts resident in its HBM); "
+              "multi-GPU runs are not implemented. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_synth
+    import sparse_mixture_experts_gemm_amd as moe
+
+    dev = "cuda:0"
+    cfg = moe_synth.CONFIGS[args.workload]
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    L = moe_synth.make_layer(cfg, dev)
+    p = moe.Params(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff, capacity_factor=cfg.cf,
+                   reroute=cfg.reroute, lam=cfg.lam, aux_coef=cfg.aux_coef,
+                   dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32)
+    dt = p.torch_dtype
+    T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    R = moe.max_rows(p)
+
+    load = None
+    if cfg.load_from_prev:
+        # previous batch's per-expert kept fraction, routed without a penalty on the GPU path
+        pp = moe.Params(**{**p.__dict__, "lam": 0.0})
+        rp = moe.Routing(pp, dev)
+        lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+        moe.route(pp, L["x_prev"], L["w_router"], L["bias"], None, lg, rp)
+        xp = torch.empty((R, d), dtype=dt, device=dev)
+        moe.dispatch(pp, L["x_prev"], rp, xp, moe.alloc_workspace(pp, dev, dispatch_only=True))
+        load = rp.kept.float() / float(T * k)
+        del xp
+
+    y = torch.empty((T, d), dtype=dt, device=dev)
+    logits = torch.empty((T, E), dtype=torch.float32, device=dev)
+    r = moe.Routing(p, dev)
+    ws = moe.alloc_workspace(p, dev)
+
+    def step():
+        moe.forward(p, L["x"], L["w_router"], L["bias"], load, L["w1"], L["w3"], L["w2"], y, logits, r, ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done, timing {args.steps} steps", file=sys.stderr, flush=True)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for _ in range(args.steps):
+        step()
+    t1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_per_step = t0.elapsed_time(t1) / args.steps
+
+    totals = r.totals.cpu().tolist()
+    kept = r.kept.cpu()
+    rows = int(totals[0])
+    active = int((kept > 0).sum())
+
+    # per-stage times: each entry point bracketed by events on the launch stream
+    x_perm = torch.empty((max(R, 1), d), dtype=dt, device=dev)
+    h = torch.empty((max(R, 1), cfg.d_ff), dtype=torch.float16 if dt == torch.bfloat16 else dt, device=dev)
+    y_perm = torch.empty((max(R, 1), d), dtype=torch.float32, device=dev)
+    wsd = moe.alloc_workspace(p, dev, dispatch_only=True)
+    n_st = max(5, min(args.steps, 30))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_st)]
+    for i in range(n_st + 3):
+        e = ev[i - 3] if i >= 3 else None
+        if e: e[0].record()
+        moe.route(p, L["x"], L["w_router"], L["bias"], load, logits, r)
+        if e: e[1].record()
+        moe.dispatch(p, L["x"], r, x_perm, wsd)
+        if e: e[2].record()
+        moe.expert_ffn(p, x_perm, r.offsets, L["w1"], L["w3"], L["w2"], h, y_perm)
+        if e: e[3].record()
+        moe.combine(p, y_perm, r.row, r.gate, y)
+        if e: e[4].record()
+    torch.cuda.synchronize()
+    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])  # ms
+    st_ms = st.mean(axis=0)
+    work = stage_bytes_flops(cfg, rows, active)
+    t_route, t_disp, t_ffn, t_comb = (float(v) for v in st_ms)
+    gemm_tflops = work["gemm_flops"] / (t_ffn * 1e-3) / 1e12
+    stages = {
+        "route": {"us": t_route * 1e3, "GB/s": work["route_bytes"] / (t_route * 1e-3) / 1e9,
+                  "hbm_frac": work["route_bytes"] / (t_route * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "dispatch": {"us": t_disp * 1e3, "GB/s": work["dispatch_bytes"] / (t_disp * 1e-3) / 1e9,
+                     "hbm_frac": work["dispatch_bytes"] / (t_disp * 1e-3) / 1e9 / PEAK_HBM_GBS},
+        "expert_ffn": {"us": t_ffn * 1e3, "TFLOP/s": gemm_tflops, "mfma_frac": gemm_tflops / PEAK_MFMA_TFLOPS,
+                       "weight_GB/s": work["gemm_weight_bytes"] / (t_ffn * 1e-3) / 1e9},
+        "combine": {"us": t_comb * 1e3, "GB/s": work["combine_bytes"] / (t_comb * 1e-3) / 1e9,
+                    "hbm_frac": work["combine_bytes"] / (t_comb * 1e-3) / 1e9 / PEAK_HBM_GBS},
+    }
+    layer_flops = work["route_flops"] + work["gemm_flops"]
+
+    roofline = {"kernel": "expert grouped GEMM (moe_expert_ffn: gate-up + down launches)",
+                "bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": gemm_tflops / PEAK_MFMA_TFLOPS, "traffic": None}
+    if args.workload == "decode":
+        gbs = work["gemm_weight_bytes"] / (t_ffn * 1e-3) / 1e9
+        roofline = {"kernel": "expert grouped GEMM (weight streaming)", "bound": "hbm", "achieved": gbs,
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, L, load, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": cfg.dtype,
+        "data": "synthetic (seeded SplitMix64/Box-Muller inputs and random-init weights of the workload's shape)",
+        "config": {"workload": f"{cfg.name}: T={T} d={d} E={E} top-{k} d_ff={cfg.d_ff} cf={cfg.cf}"
+                               + (f" bias={cfg.bias} lambda={cfg.lam}" if cfg.bias != "none" else ""),
+                   "T": T, "d": d, "E": E, "k": k, "d_ff": cfg.d_ff, "capacity_factor": cfg.cf,
+                   "rows": rows, "dropped": int(totals[1]), "rerouted": int(totals[2]),
+                   "parallelism": "single GPU, all experts resident"},
+        "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
+        "mfma_util_pct": 100.0 * gemm_tflops / PEAK_MFMA_TFLOPS,
+        "stages": stages,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": wall,
+    }
+    print(json.dumps(out))
+
+
+def cpu_baseline(cfg, L, load, target_s):
+    """The oracle as it stands, on the host cores, on a bounded sample: router
+    logits, ranking and dispatch for every token (the capacity couples them),
+    expert FFN + combine for a sample of tokens; reported per token."""
+    import numpy as np
+    import oracle
+
+    oracle.lib()
+    print("[bench] cpu baseline: copying inputs to host", file=sys.stderr, flush=True)
+    c = {n: (oracle._np(v) if v is not None else None) for n, v in L.items()}
+    ld = None if load is None else load.cpu().numpy().astype(np.float32)
+    T = cfg.T
+    t0 = time.perf_counter()
+    raw = oracle.router_logits(c["x"], c["w_router"], c["bias"])
+    cand, cs = oracle.route(raw, cfg.k, ld, cfg.lam)
+    disp = oracle.dispatch(cand, cs, cfg.E, cfg.k, oracle.capacity(T, cfg.k, cfg.E, cfg.cf), cfg.reroute,
+                           cfg.aux_coef)
+    t_route = time.perf_counter() - t0
+    # calibrate on one token per oracle thread, then size the sample for about
+    # target_s seconds of expert work
+    n = max(2, oracle.num_threads())
+    t1 = time.perf_counter()
+    oracle.layer_tokens(np.arange(n, dtype=np.int32), c["x"], c["w1"], c["w3"], c["w2"], disp["eid"], disp["gate64"])
+    per_tok = (time.perf_counter() - t1) / n
+    n2 = int(max(2, min(T - n, target_s / max(per_tok, 1e-6))))
+    toks = np.arange(n, n + n2, dtype=np.int32)
+    t2 = time.perf_counter()
+    oracle.layer_tokens(toks, c["x"], c["w1"], c["w3"], c["w2"], disp["eid"], disp["gate64"])
+    t_ffn = time.perf_counter() - t2
+    per_token_s = t_ffn / n2 + t_route / T
+    return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"router logits + ranking + dispatch for all {T} tokens ({t_route:.2f} s), "
+                      f"expert FFN + combine for {n2} tokens ({t_ffn:.2f} s); rate per token"}
+
+
+if __name__ == "__main__":
+    main()
