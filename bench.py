@@ -31,6 +31,8 @@ def parse():
                     choices=["tiny", "mixtral", "fine64", "skew", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="first run one plain 1 GiB device copy (reference for byte counters)")
     return ap.parse_args()
 
 
@@ -64,6 +66,13 @@ def main():
     import sparse_mixture_experts_gemm_amd as moe
 
     dev = "cuda:0"
+    if args.calibrate_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
     cfg = moe_synth.CONFIGS[args.workload]
     print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
     L = moe_synth.make_layer(cfg, dev)

@@ -32,6 +32,8 @@
 //   * 32-row MFMA blocks that lie wholly past an expert's last row are
 //     skipped, so ragged tails and small groups cost little matrix-core time.
 // fp32 path (the tiny fp32 layer): a plain LDS-tiled VALU GEMM.
+#include <type_traits>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -42,7 +44,6 @@ constexpr int kGemmThreads = 256;
 constexpr int kBM = 256;   // rows per tile
 constexpr int kBN = 256;   // weight rows per tile (gate-up: 128 of W1 + 128 of W3)
 constexpr int kBK = 64;    // K per stage
-constexpr int kChunksPerRow = kBK / 8;  // 16-byte chunks per tile row
 constexpr int kTileBytes = kBM * kBK * 2;  // one operand tile, bf16
 constexpr int kStageBytes = 2 * kTileBytes;
 constexpr int kLdsBytes = 2 * kStageBytes;  // double-buffered
@@ -121,68 +122,207 @@ __device__ __forceinline__ f32x16_t mfma32(uint4 a, uint4 b, f32x16_t c) {
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
 }
 
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef const __attribute__((address_space(1))) char gbl_char_t;
+
+// 16 bytes per lane straight from global memory into LDS: the 64 lanes of
+// the wave fill the 1 KiB starting at the wave-uniform address `dst`.
+__device__ __forceinline__ void g2lds16(const char *src, char *dst) {
+    __builtin_amdgcn_global_load_lds((gbl_char_t *)src, (lds_char_t *)dst, 16, 0, 0);
+}
+
+__device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
+
+// Scheduling hints: interleave one group of `n` instructions of a class.
+#define SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, n, 0)
+#define SCHED_DSR(n) __builtin_amdgcn_sched_group_barrier(0x100, n, 0)
+#define SCHED_VMEM(n) __builtin_amdgcn_sched_group_barrier(0x020, n, 0)
+
+// Per-thread state of the MFMA grouped GEMM.
+struct GemmThread {
+    uint32_t a_off[8], b_off[8];  // global byte offsets of this lane's 16-byte chunks
+    const char *b_src[8];         // uniform base per B row group (W1 / W3 / W2)
+    const char *a_base;
+    uint32_t fa[2][4], fb[2][4];  // LDS byte offsets of fragments [parity][sub-step]
+    int wave, nact;
+};
+
+template <int MODE>
+__device__ __forceinline__ int b_imm(int jn) {
+    if (MODE == kGateUp) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * (kBK * 2);
+    return jn * 32 * (kBK * 2);
+}
+
+// Issue the 8 global -> LDS loads of one half (A or B) of K step kt into
+// the LDS stage at sbase.
+template <int HALF>
+__device__ __forceinline__ void issue_half(const GemmThread &g, char *sbase, uint32_t kb) {
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+        if (HALF == 0)
+            g2lds16(g.a_base + g.a_off[j] + kb, sbase + (g.wave * 8 + j) * 1024);
+        else
+            g2lds16(g.b_src[j] + g.b_off[j] + kb, sbase + kTileBytes + (g.wave * 8 + j) * 1024);
+    }
+}
+
+template <int MODE>
+__device__ __forceinline__ void load_frags(const GemmThread &g, const char *sb, int ss, uint4 (&af)[4],
+                                           uint4 (&bf)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) af[i] = lds_read16(sb + g.fa[i & 1][ss] + i * 32 * (kBK * 2));
+#pragma unroll
+    for (int jn = 0; jn < 4; jn++) bf[jn] = lds_read16(sb + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
+}
+
+// MFMAs of one 16-wide K sub-step.  In a partial tile, 32-row blocks at or
+// past nact are skipped (a wave-uniform branch) so ragged tails cost little
+// matrix-core time; full tiles run straight-line code.
+template <int MODE, bool FULL>
+__device__ __forceinline__ void mfma_substep(const uint4 (&af)[4], const uint4 (&bf)[4], int nact,
+                                             f32x16_t (&acc)[4][4]) {
+    constexpr bool kF16 = MODE == kDown;
+    uint4 bw[4];
+#pragma unroll
+    for (int jn = 0; jn < 4; jn++) bw[jn] = kF16 ? bf16x8_to_f16x8(bf[jn]) : bf[jn];
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        if (FULL || i < nact) {
+#pragma unroll
+            for (int jn = 0; jn < 4; jn++) acc[i][jn] = mfma32<kF16>(af[i], bw[jn], acc[i][jn]);
+        }
+    }
+}
+
+// One K step from stage `sb` while the next step's tile streams into `sn`.
+// Sub-step ss runs its 16 independent MFMAs while the fragments of sub-step
+// ss+1 are read from LDS (double-buffered registers) and, in sub-steps 0 and
+// 1, the 16 global->LDS loads of the next step are issued.  A scheduling
+// fence between sub-steps keeps the compiler from merging them (which would
+// chain dependent MFMAs on one accumulator).
+template <int MODE, bool FULL>
+__device__ __forceinline__ void kstep(const GemmThread &g, const char *sb, char *sn, uint32_t kb_next,
+                                      int nact, f32x16_t (&acc)[4][4]) {
+    uint4 af0[4], bf0[4], af1[4], bf1[4];
+    load_frags<MODE>(g, sb, 0, af0, bf0);
+#pragma unroll
+    for (int ss = 0; ss < 4; ss++) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (ss < 3) {
+            if (ss & 1)
+                load_frags<MODE>(g, sb, ss + 1, af0, bf0);
+            else
+                load_frags<MODE>(g, sb, ss + 1, af1, bf1);
+        }
+        if (ss == 0) issue_half<0>(g, sn, kb_next);
+        if (ss == 1) issue_half<1>(g, sn, kb_next);
+        if (ss & 1)
+            mfma_substep<MODE, FULL>(af1, bf1, nact, acc);
+        else
+            mfma_substep<MODE, FULL>(af0, bf0, nact, acc);
+        if (FULL) {
+            // next fragments early (first half), global loads in the second
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                SCHED_MFMA(1);
+                if (ss < 3) SCHED_DSR(1);
+            }
+#pragma unroll
+            for (int q = 0; q < 8; q++) {
+                SCHED_MFMA(1);
+                if (ss < 2) SCHED_VMEM(1);
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The K loop over pairs of steps: stage 0 computes while stage 1 fills, then
+// the reverse.  The two stages are distinct LDS objects so the compiler can
+// see that reading one never waits on the loads into the other.  An odd step
+// count runs one extra step with no MFMAs; loads past the end re-read the
+// last tile.
+template <int MODE, bool FULL>
+__device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s1, int nk,
+                                          f32x16_t (&acc)[4][4]) {
+    issue_half<0>(g, s0, 0);
+    issue_half<1>(g, s0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int kt = 0; kt < nk; kt += 2) {
+        const uint32_t kb1 = (uint32_t)min(kt + 1, nk - 1) * kBK * 2;
+        const uint32_t kb2 = (uint32_t)min(kt + 2, nk - 1) * kBK * 2;
+        kstep<MODE, FULL>(g, s0, s1, kb1, g.nact, acc);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (kt + 1 < nk) {
+            kstep<MODE, FULL>(g, s1, s0, kb2, g.nact, acc);
+        } else {
+            kstep<MODE, false>(g, s1, s0, kb2, 0, acc);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
+}
+
 // MODE kGateUp: A = x_perm (bf16), B = W1/W3 (bf16), writes h (fp16).
-// MODE kDown:   A = h (fp16), B = W2 (bf16, widened to fp16 into LDS),
-//               writes y_perm (fp32).
+// MODE kDown:   A = h (fp16), B = W2 (bf16, widened to fp16 after the LDS
+//               read), writes y_perm (fp32).
+//
+// LDS: two stages of [A tile 256 x 64 | B tile 256 x 64], 16-byte chunks of
+// each row XOR-swizzled by swz(row).  Global -> LDS with global_load_lds:
+// wave w loads row groups 8*(8w+j) .. +7 (j = 0..7) of A and of B; lane l
+// takes row 8g + l/8 and the logical chunk that lands at physical position
+// l%8.  Fragments: lane l reads row base + l%32, logical chunk 2s + l/32 of
+// sub-step s; the swizzle of such a row is sw0(l) ^ (4 * parity of base/32).
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
     const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
     void *__restrict__ out_v) {
-    extern __shared__ __attribute__((aligned(16))) char lds[];
+    __shared__ __attribute__((aligned(1024))) char lds_s0[kStageBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_s1[kStageBytes];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
 
     TileInfo ti;
     if (!find_tile(offsets, E, ntiles_n, kBM, xcd_remap(blockIdx.x, gridDim.x), ti)) return;
-
-    // n0: first output column of the tile; weight rows of the tile
     const int n0 = MODE == kGateUp ? ti.nt * (kBN / 2) : ti.nt * kBN;
     const size_t wexp = (size_t)ti.e * N * K;
 
-    // global source of the chunks this thread loads: 8 A chunks and 8 B chunks
-    const int lrow = tid >> 3;  // 0..31, + 32*j
-    const int lc = tid & 7;
-    const uint16_t *a_src[8];
-    const uint16_t *b_src[8];
+    GemmThread g;
+    g.wave = wave;
+    g.a_base = reinterpret_cast<const char *>(A);
+    const char *b_base0 = reinterpret_cast<const char *>(B0 + wexp);
+    const char *b_base1 = reinterpret_cast<const char *>((MODE == kGateUp ? B1 : B0) + wexp);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-        const int r = lrow + 32 * j;
-        int gm = ti.m0 + r;
-        if (gm >= ti.mend) gm = ti.mend - 1;
-        a_src[j] = A + (size_t)gm * K + lc * 8;
-        int gn;
-        const uint16_t *B;
-        if (MODE == kGateUp) {
-            B = r < kBN / 2 ? B0 : B1;
-            gn = n0 + (r & (kBN / 2 - 1));
-        } else {
-            B = B0;
-            gn = n0 + r;
+        const int row = (wave * 8 + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        const int gm = min(ti.m0 + row, ti.mend - 1);
+        g.a_off[j] = ((uint32_t)gm * K + c * 8) * 2;
+        int gn = MODE == kGateUp ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
+        gn = min(gn, N - 1);
+        g.b_off[j] = ((uint32_t)gn * K + c * 8) * 2;
+        // B row groups 0..15 come from B0, 16..31 from B1 (gate-up: W1 then W3)
+        g.b_src[j] = (MODE == kGateUp && wave * 8 + j >= 16) ? b_base1 : b_base0;
+    }
+    const int l5 = lane & 31, hi = lane >> 5;
+    const int sw0 = (l5 ^ (l5 >> 3)) & 7;
+    const int b_rbase = MODE == kGateUp ? wn * 64 : wn * 128;
+#pragma unroll
+    for (int pp = 0; pp < 2; pp++)
+#pragma unroll
+        for (int ss = 0; ss < 4; ss++) {
+            const uint32_t sw = (uint32_t)(((2 * ss + hi) ^ sw0 ^ (4 * pp)) << 4);
+            g.fa[pp][ss] = (uint32_t)(wm * 128 + l5) * (kBK * 2) + sw;
+            g.fb[pp][ss] = kTileBytes + (uint32_t)(b_rbase + l5) * (kBK * 2) + sw;
         }
-        if (gn >= N) gn = N - 1;
-        b_src[j] = B + wexp + (size_t)gn * K + lc * 8;
-    }
-    int st_off[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) st_off[j] = tile_off(lrow + 32 * j, lc);
-
-    // MFMA blocks of this wave: rows wm*128 + i*32, weight rows per jn
-    bool act[4];
-#pragma unroll
-    for (int i = 0; i < 4; i++) act[i] = ti.m0 + wm * 128 + i * 32 < ti.mend;
-    int brow[4];
-#pragma unroll
-    for (int jn = 0; jn < 4; jn++) {
-        if (MODE == kGateUp)
-            brow[jn] = (jn < 2 ? 0 : kBN / 2) + wn * 64 + (jn & 1) * 32;
-        else
-            brow[jn] = wn * 128 + jn * 32;
-    }
-    const int fr = lane & 31;   // fragment row within a 32-row block
-    const int fk = lane >> 5;   // which 8-element half of a 16-wide K slice
+    // active 32-row blocks of this wave (uniform)
+    const int nact_raw = (ti.mend - (ti.m0 + wm * 128) + 31) / 32;
+    g.nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -192,90 +332,39 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
 #pragma unroll
             for (int q = 0; q < 16; q++) acc[i][jn][q] = 0.0f;
 
-    const int nk = K / kBK;
-    uint4 ra[8], rb[8];
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        ra[j] = *reinterpret_cast<const uint4 *>(a_src[j]);
-        rb[j] = *reinterpret_cast<const uint4 *>(b_src[j]);
-    }
-    constexpr bool kF16 = MODE == kDown;
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        *reinterpret_cast<uint4 *>(lds + st_off[j]) = ra[j];
-        *reinterpret_cast<uint4 *>(lds + kTileBytes + st_off[j]) = kF16 ? bf16x8_to_f16x8(rb[j]) : rb[j];
-    }
-    __syncthreads();
+    if (g.nact == 4)
+        main_loop<MODE, true>(g, lds_s0, lds_s1, K / kBK, acc);
+    else
+        main_loop<MODE, false>(g, lds_s0, lds_s1, K / kBK, acc);
 
-    for (int kt = 0; kt < nk; kt++) {
-        const int cur = kt & 1;
-        if (kt + 1 < nk) {
-            const size_t ko = (size_t)(kt + 1) * kBK;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                ra[j] = *reinterpret_cast<const uint4 *>(a_src[j] + ko);
-                rb[j] = *reinterpret_cast<const uint4 *>(b_src[j] + ko);
-            }
-        }
-        const char *sa = lds + cur * kStageBytes;
-        const char *sb = sa + kTileBytes;
-#pragma unroll
-        for (int s = 0; s < kBK / 16; s++) {
-            const int c = s * 2 + fk;
-            uint4 af[4], bfr[4];
-#pragma unroll
-            for (int i = 0; i < 4; i++)
-                af[i] = *reinterpret_cast<const uint4 *>(sa + tile_off(wm * 128 + i * 32 + fr, c));
-#pragma unroll
-            for (int jn = 0; jn < 4; jn++)
-                bfr[jn] = *reinterpret_cast<const uint4 *>(sb + tile_off(brow[jn] + fr, c));
-#pragma unroll
-            for (int i = 0; i < 4; i++) {
-                if (!act[i]) continue;
-#pragma unroll
-                for (int jn = 0; jn < 4; jn++) acc[i][jn] = mfma32<kF16>(af[i], bfr[jn], acc[i][jn]);
-            }
-        }
-        if (kt + 1 < nk) {
-            char *da = lds + (cur ^ 1) * kStageBytes;
-#pragma unroll
-            for (int j = 0; j < 8; j++) {
-                *reinterpret_cast<uint4 *>(da + st_off[j]) = ra[j];
-                *reinterpret_cast<uint4 *>(da + kTileBytes + st_off[j]) = kF16 ? bf16x8_to_f16x8(rb[j]) : rb[j];
-            }
-        }
-        __syncthreads();
-    }
-
-    // epilogue: lane holds column fr of each 32x32 block, rows 8*(q/4) + 4*fk + q%4
-    const int ldo = N;
+    // epilogue: lane holds column l5 of each 32x32 block, rows 8*(q/4) + 4*hi + q%4
     uint16_t *out_h = static_cast<uint16_t *>(out_v);
     float *out_y = static_cast<float *>(out_v);
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        if (!act[i]) continue;
-        const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * fk;
+        if (i >= g.nact) continue;
+        const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * hi;
         if (MODE == kGateUp) {
 #pragma unroll
             for (int jn = 0; jn < 2; jn++) {
-                const int col = n0 + wn * 64 + jn * 32 + fr;
+                const int col = n0 + wn * 64 + jn * 32 + l5;
                 if (col >= N) continue;
 #pragma unroll
                 for (int q = 0; q < 16; q++) {
                     const int m = rbase + 8 * (q >> 2) + (q & 3);
                     if (m < ti.mend)
-                        out_h[(size_t)m * ldo + col] = f32_to_f16_sat(silu_mul(acc[i][jn][q], acc[i][jn + 2][q]));
+                        out_h[(size_t)m * N + col] = f32_to_f16_sat(silu_mul(acc[i][jn][q], acc[i][jn + 2][q]));
                 }
             }
         } else {
 #pragma unroll
             for (int jn = 0; jn < 4; jn++) {
-                const int col = n0 + wn * 128 + jn * 32 + fr;
+                const int col = n0 + wn * 128 + jn * 32 + l5;
                 if (col >= N) continue;
 #pragma unroll
                 for (int q = 0; q < 16; q++) {
                     const int m = rbase + 8 * (q >> 2) + (q & 3);
-                    if (m < ti.mend) out_y[(size_t)m * ldo + col] = acc[i][jn][q];
+                    if (m < ti.mend) out_y[(size_t)m * N + col] = acc[i][jn][q];
                 }
             }
         }
@@ -355,16 +444,12 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *
         const int64_t mt = max_rows / kBM + E;  // bound on sum_e ceil(rows_e / kBM)
         const int nt_up = (int)ceil_div(dff, kBN / 2);
         const int nt_dn = (int)ceil_div(d, kBN);
-        hipError_t e = allow_lds(reinterpret_cast<const void *>(&grouped_gemm_bf16<kGateUp>), kLdsBytes);
-        if (e != hipSuccess) return e;
-        e = allow_lds(reinterpret_cast<const void *>(&grouped_gemm_bf16<kDown>), kLdsBytes);
-        if (e != hipSuccess) return e;
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
-                           kLdsBytes, st, static_cast<const uint16_t *>(x_perm),
+                           0, st, static_cast<const uint16_t *>(x_perm),
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
                            offsets, E, dff, d, nt_up, h);
         hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(kGemmThreads),
-                           kLdsBytes, st, static_cast<const uint16_t *>(h),
+                           0, st, static_cast<const uint16_t *>(h),
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
                            offsets, E, d, dff, nt_dn, y_perm);
     } else {
