@@ -36,7 +36,7 @@ def parse():
     return ap.parse_args()
 
 
-def stage_bytes_flops(cfg, rows, active_experts):
+def stage_bytes_flops(cfg, rows, active_experts, splits=1):
     """Algorithmic work per stage (what the method must touch)."""
     T, d, E, dff = cfg.T, cfg.d, cfg.E, cfg.d_ff
     es = 2 if cfg.dtype == "bf16" else 4
@@ -46,7 +46,7 @@ def stage_bytes_flops(cfg, rows, active_experts):
     dispatch_bytes = T * k1 * 8 + T * cfg.k * 17 + T * d * es + rows * d * es
     gemm_flops = rows * 6.0 * d * dff
     gemm_weight_bytes = active_experts * 3 * d * dff * es
-    combine_bytes = rows * d * 4 + T * d * es + T * cfg.k * 8
+    combine_bytes = rows * d * 4 * splits + T * d * es + T * cfg.k * 8
     return dict(route_bytes=route_bytes, dispatch_bytes=dispatch_bytes, gemm_flops=gemm_flops,
                 gemm_weight_bytes=gemm_weight_bytes, combine_bytes=combine_bytes,
                 route_flops=2.0 * T * d * E)
@@ -127,7 +127,7 @@ def main():
     # per-stage times: each entry point bracketed by events on the launch stream
     x_perm = torch.empty((max(R, 1), d), dtype=dt, device=dev)
     h = torch.empty((max(R, 1), cfg.d_ff), dtype=torch.float16 if dt == torch.bfloat16 else dt, device=dev)
-    y_perm = torch.empty((max(R, 1), d), dtype=torch.float32, device=dev)
+    y_perm = moe.alloc_y_perm(p, dev)
     wsd = moe.alloc_workspace(p, dev, dispatch_only=True)
     n_st = max(5, min(args.steps, 30))
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_st)]
@@ -145,7 +145,7 @@ def main():
     torch.cuda.synchronize()
     st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])  # ms
     st_ms = st.mean(axis=0)
-    work = stage_bytes_flops(cfg, rows, active)
+    work = stage_bytes_flops(cfg, rows, active, moe.ffn_splits(p))
     t_route, t_disp, t_ffn, t_comb = (float(v) for v in st_ms)
     gemm_tflops = work["gemm_flops"] / (t_ffn * 1e-3) / 1e12
     stages = {

@@ -30,6 +30,10 @@
  *     output is rounded to the element type once).  The SwiGLU activations h
  *     are fp16 in a bf16 layer (saturated at +-65504) and fp32 in an fp32
  *     layer.
+ *   - y_perm is [S][R][d] with S = moe_ffn_splits(p): the down projection's
+ *     reduction over d_ff may be split into S slices, each stored as an fp32
+ *     partial product; the value of a row is the sum of its S slices, which
+ *     moe_combine adds in slice order (deterministic, no atomics).
  *   - Every output element listed for an entry point is written on every call.
  *   - NaN or Inf inputs are outside the contract.
  *   - Calls on different streams that share no output buffer may run
@@ -115,11 +119,15 @@ int64_t moe_capacity(const moe_params *p);
  * -1 if p is invalid. */
 int64_t moe_max_rows(const moe_params *p);
 
+/* Host-side, pure: S, the number of fp32 partial products y_perm holds
+ * (1 for fp32 layers); -1 if p is invalid. */
+int moe_ffn_splits(const moe_params *p);
+
 /* Host-side, pure: bytes of scratch moe_dispatch needs. */
 size_t moe_dispatch_workspace_bytes(const moe_params *p);
 
 /* Host-side, pure: bytes of workspace moe_forward needs: the dispatch scratch
- * plus x_perm [R][d], h [R][d_ff] and y_perm [R][d] (fp32), each 256-byte
+ * plus x_perm [R][d], h [R][d_ff] and y_perm [S][R][d] (fp32), each 256-byte
  * aligned. */
 size_t moe_workspace_bytes(const moe_params *p);
 
@@ -153,10 +161,10 @@ int moe_dispatch(const moe_params *p, const void *x, moe_routing *r, void *x_per
  * ("GPT-4稀疏激活真相" §3.1: Linear -> SwiGLU -> Linear per expert):
  *   for rows i in [offsets[e], offsets[e+1]):
  *     h[i]      = silu(x_perm[i] . W1[e]^T) * (x_perm[i] . W3[e]^T)
- *     y_perm[i] = h[i] . W2[e]^T
+ *     y_perm[i] = h[i] . W2[e]^T   (as S partial sums over slices of d_ff)
  *   x_perm [R][d]; w1, w3 [E][d_ff][d]; w2 [E][d][d_ff]; h [R][d_ff] (fp16
  *   for bf16, fp32 for fp32);
- *   y_perm [R][d] fp32.  offsets [E+1] is read on the device.  Rows past
+ *   y_perm [S][R][d] fp32.  offsets [E+1] is read on the device.  Rows past
  *   offsets[E] of h and y_perm are left untouched.
  */
 int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offsets,
@@ -167,8 +175,9 @@ int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offse
  * Stage 4, combine ("企业官网建设流程全解析" page §3, step 5: results are put
  * back in token order; "GPT-4稀疏激活真相" §4.3: weighted fusion):
  *   y[t] = sum over slots j with row[t][j] >= 0 of gate[t][j] * y_perm[row[t][j]]
+ *   where a y_perm row is the sum of its S slices (added in slice order)
  * accumulated in fp32 and rounded once; a token with no kept slot gets zeros.
- *   y_perm [R][d] fp32; row, gate [T][k]; y [T][d].
+ *   y_perm [S][R][d] fp32; row, gate [T][k]; y [T][d].
  */
 int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
                 void *y, void *stream);

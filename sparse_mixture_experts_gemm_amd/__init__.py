@@ -59,6 +59,8 @@ def lib():
         L.moe_capacity.restype = ctypes.c_int64
         L.moe_max_rows.argtypes = [PP]
         L.moe_max_rows.restype = ctypes.c_int64
+        L.moe_ffn_splits.argtypes = [PP]
+        L.moe_ffn_splits.restype = ctypes.c_int
         L.moe_dispatch_workspace_bytes.argtypes = [PP]
         L.moe_dispatch_workspace_bytes.restype = ctypes.c_size_t
         L.moe_workspace_bytes.argtypes = [PP]
@@ -108,6 +110,16 @@ def capacity(p: Params) -> int:
 
 def max_rows(p: Params) -> int:
     return int(lib().moe_max_rows(ctypes.byref(p.c())))
+
+
+def ffn_splits(p: Params) -> int:
+    """S: y_perm holds S fp32 partial products of the down projection."""
+    return int(lib().moe_ffn_splits(ctypes.byref(p.c())))
+
+
+def alloc_y_perm(p: Params, device="cuda"):
+    """y_perm [S, R, d] fp32 for moe_expert_ffn / moe_combine."""
+    return torch.empty((ffn_splits(p), max(max_rows(p), 1), p.d), dtype=torch.float32, device=device)
 
 
 def dispatch_workspace_bytes(p: Params) -> int:

@@ -6,8 +6,10 @@
 // weighted fusion).  A token with no kept slot gets zeros.
 //
 // y_perm is fp32 (the down GEMM's accumulator precision), so the bf16 output
-// is rounded exactly once.  HBM-bound gather: 16-byte loads and stores, the k
-// source rows read once each.
+// is rounded exactly once.  It may hold S partial products (slices of the
+// d_ff reduction, split_stride apart), which are added in slice order.
+// HBM-bound gather: 16-byte loads and stores, the k source rows read once
+// each.
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -40,7 +42,8 @@ template <typename TE>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ y_perm,
                                                            const int32_t *__restrict__ row,
                                                            const float *__restrict__ gate, int T,
-                                                           int k, int d, int tpb,
+                                                           int k, int d, int tpb, int splits,
+                                                           size_t split_stride,
                                                            TE *__restrict__ y) {
     const int per_tok = kThreads / tpb;  // threads per token
     if (threadIdx.x / per_tok >= tpb) return;
@@ -59,7 +62,14 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
         for (int r = 0; r < k; r++) {
             if (rws[r] < 0) continue;
             const float4 *src = reinterpret_cast<const float4 *>(y_perm + (size_t)rws[r] * d) + 2 * c;
-            const float4 u = src[0], v = src[1];
+            float4 u = src[0], v = src[1];
+            // the down projection's d_ff slices, added in slice order
+            for (int sl = 1; sl < splits; sl++) {
+                const float4 *ps = reinterpret_cast<const float4 *>(y_perm + sl * split_stride + (size_t)rws[r] * d) + 2 * c;
+                const float4 pu = ps[0], pv = ps[1];
+                u.x += pu.x; u.y += pu.y; u.z += pu.z; u.w += pu.w;
+                v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+            }
             const float g = gs[r];
             a[0] += g * u.x;
             a[1] += g * u.y;
@@ -76,8 +86,8 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
 
 }  // namespace
 
-hipError_t launch_combine(const moe_params &p, const void *y_perm, const int32_t *row,
-                          const float *gate, void *y, hipStream_t st) {
+hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
+                          const int32_t *row, const float *gate, void *y, hipStream_t st) {
     if (p.T == 0) return hipSuccess;
     const int groups = p.d / 8;
     // tokens per block: enough threads per token to cover its row in one pass
@@ -88,11 +98,11 @@ hipError_t launch_combine(const moe_params &p, const void *y_perm, const int32_t
     if (p.dtype == MOE_BF16)
         hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, st,
                            static_cast<const float *>(y_perm), row, gate, p.T, p.k, p.d, tpb,
-                           static_cast<uint16_t *>(y));
+                           splits, split_stride, static_cast<uint16_t *>(y));
     else
         hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(kThreads), 0, st,
                            static_cast<const float *>(y_perm), row, gate, p.T, p.k, p.d, tpb,
-                           static_cast<float *>(y));
+                           splits, split_stride, static_cast<float *>(y));
     return hipGetLastError();
 }
 

@@ -43,35 +43,43 @@ namespace {
 constexpr int kGemmThreads = 256;
 constexpr int kBM = 256;   // rows per tile
 constexpr int kBN = 256;   // weight rows per tile (gate-up: 128 of W1 + 128 of W3)
-constexpr int kBK = 64;    // K per stage
-constexpr int kTileBytes = kBM * kBK * 2;  // one operand tile, bf16
-constexpr int kStageBytes = 2 * kTileBytes;
-constexpr int kLdsBytes = 2 * kStageBytes;  // double-buffered
+constexpr int kBK = 64;    // K per pipeline step: 128-byte row segments (one cache line)
+constexpr int kRowBytes = kBK * 2;           // one tile row in LDS
+constexpr int kTileBytes = kBM * kRowBytes;  // one operand tile (32 KiB)
+constexpr int kStageBytes = 2 * kTileBytes;  // A tile + B tile (64 KiB)
+constexpr int kLoadsPerOperand = kTileBytes / 1024 / 4;  // 1 KiB wave loads per wave (8)
+constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (8)
 
 enum { kGateUp = 0, kDown = 1 };
 
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row.  Fragment
+// reads touch one chunk of 16 (or 8) consecutive rows per LDS cycle; with
+// this swizzle those rows hit distinct banks whether the LDS serves 16 lanes
+// over 64 banks or 8 lanes over 32 banks per cycle.
 __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
-// byte offset of chunk c of row r in a swizzled tile
-__device__ __forceinline__ int tile_off(int r, int c) { return r * (kBK * 2) + ((c ^ swz(r)) << 4); }
-
-// Flat tile index -> (expert, m range, n tile).  Returns false past the end.
+// Flat work index -> (expert, m range, n tile, K split).  Work items are
+// ordered expert, split, n tile, m tile (m fastest), so the m tiles that
+// share a weight tile are adjacent.  Returns false past the end.
 struct TileInfo {
-    int e, m0, mend, nt;
+    int e, m0, mend, nt, split;
 };
 
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int ntiles_n,
-                                          int bm, int L, TileInfo &ti) {
+                                          int bm, int splits, int L, TileInfo &ti) {
     int base = 0;
     for (int e = 0; e < E; e++) {
         const int beg = offsets[e], end = offsets[e + 1];
         const int mt = (end - beg + bm - 1) / bm;
-        const int cnt = mt * ntiles_n;
+        const int per_split = mt * ntiles_n;
+        const int cnt = per_split * splits;
         if (L < base + cnt) {
             const int local = L - base;
             ti.e = e;
-            ti.nt = local / mt;
-            ti.m0 = beg + (local % mt) * bm;
+            ti.split = local / per_split;
+            const int rem = local % per_split;
+            ti.nt = rem / mt;
+            ti.m0 = beg + (rem % mt) * bm;
             ti.mend = end;
             return true;
         }
@@ -140,39 +148,39 @@ __device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret
 
 // Per-thread state of the MFMA grouped GEMM.
 struct GemmThread {
-    uint32_t a_off[8], b_off[8];  // global byte offsets of this lane's 16-byte chunks
-    const char *b_src[8];         // uniform base per B row group (W1 / W3 / W2)
+    uint32_t a_off[kLoadsPerOperand], b_off[kLoadsPerOperand];  // global byte offsets (16 B per lane)
+    const char *b_src[kLoadsPerOperand];  // uniform base per B row group (W1 / W3 / W2)
     const char *a_base;
-    uint32_t fa[2][4], fb[2][4];  // LDS byte offsets of fragments [parity][sub-step]
-    int wave, nact;
+    uint32_t fa[2][4], fb[2][4];  // LDS byte offsets of fragments [block parity][sub-step]
+    int wave;
 };
 
 template <int MODE>
 __device__ __forceinline__ int b_imm(int jn) {
-    if (MODE == kGateUp) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * (kBK * 2);
-    return jn * 32 * (kBK * 2);
+    if (MODE == kGateUp) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * kRowBytes;
+    return jn * 32 * kRowBytes;
 }
 
-// Issue the 8 global -> LDS loads of one half (A or B) of K step kt into
-// the LDS stage at sbase.
+// Issue this wave's global -> LDS loads of one operand of one K step.
 template <int HALF>
-__device__ __forceinline__ void issue_half(const GemmThread &g, char *sbase, uint32_t kb) {
+__device__ __forceinline__ void issue_loads(const GemmThread &g, char *stage, uint32_t kb) {
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
+    for (int j = 0; j < kLoadsPerOperand; j++) {
+        const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group
         if (HALF == 0)
-            g2lds16(g.a_base + g.a_off[j] + kb, sbase + (g.wave * 8 + j) * 1024);
+            g2lds16(g.a_base + g.a_off[j] + kb, stage + grp * 1024);
         else
-            g2lds16(g.b_src[j] + g.b_off[j] + kb, sbase + kTileBytes + (g.wave * 8 + j) * 1024);
+            g2lds16(g.b_src[j] + g.b_off[j] + kb, stage + kTileBytes + grp * 1024);
     }
 }
 
 template <int MODE>
-__device__ __forceinline__ void load_frags(const GemmThread &g, const char *sb, int ss, uint4 (&af)[4],
+__device__ __forceinline__ void load_frags(const GemmThread &g, const char *stage, int ss, uint4 (&af)[4],
                                            uint4 (&bf)[4]) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) af[i] = lds_read16(sb + g.fa[i & 1][ss] + i * 32 * (kBK * 2));
+    for (int i = 0; i < 4; i++) af[i] = lds_read16(stage + g.fa[i & 1][ss] + i * 32 * kRowBytes);
 #pragma unroll
-    for (int jn = 0; jn < 4; jn++) bf[jn] = lds_read16(sb + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
+    for (int jn = 0; jn < 4; jn++) bf[jn] = lds_read16(stage + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
 }
 
 // MFMAs of one 16-wide K sub-step.  In a partial tile, 32-row blocks at or
@@ -194,92 +202,108 @@ __device__ __forceinline__ void mfma_substep(const uint4 (&af)[4], const uint4 (
     }
 }
 
-// One K step from stage `sb` while the next step's tile streams into `sn`.
-// Sub-step ss runs its 16 independent MFMAs while the fragments of sub-step
-// ss+1 are read from LDS (double-buffered registers) and, in sub-steps 0 and
-// 1, the 16 global->LDS loads of the next step are issued.  A scheduling
-// fence between sub-steps keeps the compiler from merging them (which would
-// chain dependent MFMAs on one accumulator).
-template <int MODE, bool FULL>
-__device__ __forceinline__ void kstep(const GemmThread &g, const char *sb, char *sn, uint32_t kb_next,
-                                      int nact, f32x16_t (&acc)[4][4]) {
-    uint4 af0[4], bf0[4], af1[4], bf1[4];
-    load_frags<MODE>(g, sb, 0, af0, bf0);
+// s_waitcnt with only the vector-memory counter: at most n loads in flight.
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
+// Workgroup barrier without an implied wait on every outstanding memory
+// operation (the waits the pipeline needs are explicit); the memory clobber
+// keeps the compiler from moving LDS accesses across it.
+__device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "memory"); }
+
+template <bool FULL, int SS>
+__device__ __forceinline__ void sched_substep() {
+    if (FULL) {
+        // next fragments in the first half, global loads in the second
 #pragma unroll
-    for (int ss = 0; ss < 4; ss++) {
-        __builtin_amdgcn_sched_barrier(0);
-        if (ss < 3) {
-            if (ss & 1)
-                load_frags<MODE>(g, sb, ss + 1, af0, bf0);
-            else
-                load_frags<MODE>(g, sb, ss + 1, af1, bf1);
+        for (int q = 0; q < 8; q++) {
+            SCHED_MFMA(1);
+            if (SS < 3) SCHED_DSR(1);
         }
-        if (ss == 0) issue_half<0>(g, sn, kb_next);
-        if (ss == 1) issue_half<1>(g, sn, kb_next);
-        if (ss & 1)
-            mfma_substep<MODE, FULL>(af1, bf1, nact, acc);
-        else
-            mfma_substep<MODE, FULL>(af0, bf0, nact, acc);
-        if (FULL) {
-            // next fragments early (first half), global loads in the second
 #pragma unroll
-            for (int q = 0; q < 8; q++) {
-                SCHED_MFMA(1);
-                if (ss < 3) SCHED_DSR(1);
-            }
-#pragma unroll
-            for (int q = 0; q < 8; q++) {
-                SCHED_MFMA(1);
-                if (ss < 2) SCHED_VMEM(1);
-            }
+        for (int q = 0; q < 8; q++) {
+            SCHED_MFMA(1);
+            if (SS < 2) SCHED_VMEM(1);
         }
-        __builtin_amdgcn_sched_barrier(0);
     }
 }
 
-// The K loop over pairs of steps: stage 0 computes while stage 1 fills, then
-// the reverse.  The two stages are distinct LDS objects so the compiler can
-// see that reading one never waits on the loads into the other.  An odd step
-// count runs one extra step with no MFMAs; loads past the end re-read the
-// last tile.
+// One K step (4 sub-steps of 16) on stage `cur` while the next step's tile
+// streams into `nxt`.  Entry: sub-step 0's fragments are in (af0, bf0).
+// Sub-step s reads the fragments of s+1 and (s = 0, 1) issues the A / B
+// loads of the next step.  Exit: all of this wave's loads landed, barrier,
+// then the next step's sub-step-0 fragments are read from `nxt`.  Fences
+// between sub-steps keep the compiler from chaining dependent MFMAs on one
+// accumulator.
 template <int MODE, bool FULL>
-__device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s1, int nk,
+__device__ __forceinline__ void kstep(const GemmThread &g, const char *cur, char *nxt, uint32_t kb_next,
+                                      int nact, uint4 (&af0)[4], uint4 (&bf0)[4],
+                                      f32x16_t (&acc)[4][4]) {
+    uint4 af1[4], bf1[4];
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<MODE>(g, cur, 1, af1, bf1);
+    issue_loads<0>(g, nxt, kb_next);
+    mfma_substep<MODE, FULL>(af0, bf0, nact, acc);
+    sched_substep<FULL, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<MODE>(g, cur, 2, af0, bf0);
+    issue_loads<1>(g, nxt, kb_next);
+    mfma_substep<MODE, FULL>(af1, bf1, nact, acc);
+    sched_substep<FULL, 1>();
+    __builtin_amdgcn_sched_barrier(0);
+    load_frags<MODE>(g, cur, 3, af1, bf1);
+    mfma_substep<MODE, FULL>(af0, bf0, nact, acc);
+    sched_substep<FULL, 2>();
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_substep<MODE, FULL>(af1, bf1, nact, acc);
+    sched_substep<FULL, 3>();
+    __builtin_amdgcn_sched_barrier(0);
+    WAIT_VMCNT(0);
+    block_sync();
+    load_frags<MODE>(g, nxt, 0, af0, bf0);
+}
+
+// The K loop over pairs of steps: stage 0 computes while stage 1 fills,
+// then the reverse.  The two stages are distinct LDS objects so the compiler
+// can see that reading one never waits on the loads into the other.  FULL
+// requires an even step count; otherwise the extra step runs no MFMAs.
+// Loads past the last step re-read the last tile.
+template <int MODE, bool FULL>
+__device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s1, int nk, int nact,
                                           f32x16_t (&acc)[4][4]) {
-    issue_half<0>(g, s0, 0);
-    issue_half<1>(g, s0, 0);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int kt = 0; kt < nk; kt += 2) {
-        const uint32_t kb1 = (uint32_t)min(kt + 1, nk - 1) * kBK * 2;
-        const uint32_t kb2 = (uint32_t)min(kt + 2, nk - 1) * kBK * 2;
-        kstep<MODE, FULL>(g, s0, s1, kb1, g.nact, acc);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (kt + 1 < nk) {
-            kstep<MODE, FULL>(g, s1, s0, kb2, g.nact, acc);
-        } else {
-            kstep<MODE, false>(g, s1, s0, kb2, 0, acc);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    auto kb = [nk](int k) -> uint32_t { return (uint32_t)min(k, nk - 1) * kRowBytes; };
+    issue_loads<0>(g, s0, kb(0));
+    issue_loads<1>(g, s0, kb(0));
+    WAIT_VMCNT(0);
+    block_sync();
+    uint4 af0[4], bf0[4];
+    load_frags<MODE>(g, s0, 0, af0, bf0);
+    for (int k = 0; k < nk; k += 2) {
+        const int n1 = FULL || k + 1 < nk ? nact : 0;
+        kstep<MODE, FULL>(g, s0, s1, kb(k + 1), nact, af0, bf0, acc);
+        kstep<MODE, FULL>(g, s1, s0, kb(k + 2), n1, af0, bf0, acc);
     }
 }
 
 // MODE kGateUp: A = x_perm (bf16), B = W1/W3 (bf16), writes h (fp16).
 // MODE kDown:   A = h (fp16), B = W2 (bf16, widened to fp16 after the LDS
-//               read), writes y_perm (fp32).
+//               read), writes y_perm (fp32).  The d_ff reduction is split
+//               into `splits` slices (work items of their own, for enough
+//               work to fill the chip); slice s writes its partial product to
+//               y_perm + s * split_stride and the combine adds the slices in
+//               order, so the result is deterministic.
 //
-// LDS: two stages of [A tile 256 x 64 | B tile 256 x 64], 16-byte chunks of
-// each row XOR-swizzled by swz(row).  Global -> LDS with global_load_lds:
-// wave w loads row groups 8*(8w+j) .. +7 (j = 0..7) of A and of B; lane l
-// takes row 8g + l/8 and the logical chunk that lands at physical position
-// l%8.  Fragments: lane l reads row base + l%32, logical chunk 2s + l/32 of
-// sub-step s; the swizzle of such a row is sw0(l) ^ (4 * parity of base/32).
+// LDS: two stages of [A tile 256 x 64 | B tile 256 x 64], the eight 16-byte
+// chunks of each row XOR-swizzled by swz(row).  Global -> LDS with
+// global_load_lds: wave w loads 8-row groups 8w .. 8w+7 of A and of B; lane
+// l takes row 8g + l/8 and the logical chunk that lands at physical position
+// l%8, so every wave load reads whole 128-byte lines.  Fragments: lane l
+// reads row base + l%32 (base a multiple of 32), logical chunk 2s + l/32 of
+// sub-step s; the swizzle of such a row is swz(l%32) ^ 4 * parity(base/32).
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
-    const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
-    void *__restrict__ out_v) {
+    const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n, int splits,
+    size_t split_stride, void *__restrict__ out_v) {
     __shared__ __attribute__((aligned(1024))) char lds_s0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds_s1[kStageBytes];
     const int tid = threadIdx.x;
@@ -288,9 +312,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const int wm = wave >> 1, wn = wave & 1;
 
     TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kBM, xcd_remap(blockIdx.x, gridDim.x), ti)) return;
+    if (!find_tile(offsets, E, ntiles_n, kBM, splits, xcd_remap(blockIdx.x, gridDim.x), ti)) return;
     const int n0 = MODE == kGateUp ? ti.nt * (kBN / 2) : ti.nt * kBN;
     const size_t wexp = (size_t)ti.e * N * K;
+    const int ks = K / splits;              // K elements of this split
+    const int k_first = ti.split * ks;      // first K element of this split
 
     GemmThread g;
     g.wave = wave;
@@ -298,31 +324,32 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const char *b_base0 = reinterpret_cast<const char *>(B0 + wexp);
     const char *b_base1 = reinterpret_cast<const char *>((MODE == kGateUp ? B1 : B0) + wexp);
 #pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const int row = (wave * 8 + j) * 8 + (lane >> 3);
+    for (int j = 0; j < kLoadsPerOperand; j++) {
+        const int grp = wave * kLoadsPerOperand + j;
+        const int row = grp * kRowsPerLoad + (lane >> 3);
         const int c = (lane & 7) ^ swz(row);
         const int gm = min(ti.m0 + row, ti.mend - 1);
-        g.a_off[j] = ((uint32_t)gm * K + c * 8) * 2;
+        g.a_off[j] = ((uint32_t)gm * K + k_first + c * 8) * 2;
         int gn = MODE == kGateUp ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
         gn = min(gn, N - 1);
-        g.b_off[j] = ((uint32_t)gn * K + c * 8) * 2;
-        // B row groups 0..15 come from B0, 16..31 from B1 (gate-up: W1 then W3)
-        g.b_src[j] = (MODE == kGateUp && wave * 8 + j >= 16) ? b_base1 : b_base0;
+        g.b_off[j] = ((uint32_t)gn * K + k_first + c * 8) * 2;
+        // B rows 0..127 come from B0, 128..255 from B1 (gate-up: W1 then W3)
+        g.b_src[j] = (MODE == kGateUp && grp * kRowsPerLoad >= kBN / 2) ? b_base1 : b_base0;
     }
     const int l5 = lane & 31, hi = lane >> 5;
-    const int sw0 = (l5 ^ (l5 >> 3)) & 7;
+    const int sw0 = swz(l5);  // swizzle of row base + l5 is sw0 ^ 4 * parity(base / 32)
     const int b_rbase = MODE == kGateUp ? wn * 64 : wn * 128;
 #pragma unroll
     for (int pp = 0; pp < 2; pp++)
 #pragma unroll
         for (int ss = 0; ss < 4; ss++) {
             const uint32_t sw = (uint32_t)(((2 * ss + hi) ^ sw0 ^ (4 * pp)) << 4);
-            g.fa[pp][ss] = (uint32_t)(wm * 128 + l5) * (kBK * 2) + sw;
-            g.fb[pp][ss] = kTileBytes + (uint32_t)(b_rbase + l5) * (kBK * 2) + sw;
+            g.fa[pp][ss] = (uint32_t)(wm * 128 + l5) * kRowBytes + sw;
+            g.fb[pp][ss] = kTileBytes + (uint32_t)(b_rbase + l5) * kRowBytes + sw;
         }
     // active 32-row blocks of this wave (uniform)
     const int nact_raw = (ti.mend - (ti.m0 + wm * 128) + 31) / 32;
-    g.nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
+    const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
 
     f32x16_t acc[4][4];
 #pragma unroll
@@ -332,17 +359,18 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
 #pragma unroll
             for (int q = 0; q < 16; q++) acc[i][jn][q] = 0.0f;
 
-    if (g.nact == 4)
-        main_loop<MODE, true>(g, lds_s0, lds_s1, K / kBK, acc);
+    const int nk = ks / kBK;
+    if (nact == 4 && nk % 2 == 0)
+        main_loop<MODE, true>(g, lds_s0, lds_s1, nk, nact, acc);
     else
-        main_loop<MODE, false>(g, lds_s0, lds_s1, K / kBK, acc);
+        main_loop<MODE, false>(g, lds_s0, lds_s1, nk, nact, acc);
 
     // epilogue: lane holds column l5 of each 32x32 block, rows 8*(q/4) + 4*hi + q%4
     uint16_t *out_h = static_cast<uint16_t *>(out_v);
-    float *out_y = static_cast<float *>(out_v);
+    float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-        if (i >= g.nact) continue;
+        if (i >= nact) continue;
         const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * hi;
         if (MODE == kGateUp) {
 #pragma unroll
@@ -385,7 +413,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict_
     __shared__ float sb0[kF32BK][kF32BN + 1];
     __shared__ float sb1[kF32BK][kF32BN + 1];
     TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kF32BM, blockIdx.x, ti)) return;
+    if (!find_tile(offsets, E, ntiles_n, kF32BM, 1, blockIdx.x, ti)) return;
     const int n0 = ti.nt * kF32BN;
     const size_t wexp = (size_t)ti.e * N * K;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // 4x4 outputs each
@@ -428,12 +456,18 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict_
     }
 }
 
-// Dynamic LDS above the default limit must be allowed per kernel.
-hipError_t allow_lds(const void *kernel, int bytes) {
-    return hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-}
-
 }  // namespace
+
+int ffn_splits(const moe_params &p, int64_t max_rows) {
+    if (p.dtype != MOE_BF16 || max_rows <= 0) return 1;
+    // down GEMM work items before splitting (upper bound); aim for at least
+    // three per compute unit
+    const int64_t tiles = (max_rows / kBM + p.E) * ceil_div(p.d, kBN);
+    const int64_t steps = p.d_ff / kBK;
+    int s = 1;
+    while (s < 8 && tiles * s < 3 * 256 && steps % (4 * s) == 0) s *= 2;
+    return s;
+}
 
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *x_perm,
                              const int32_t *offsets, const void *w1, const void *w3,
@@ -444,14 +478,16 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *
         const int64_t mt = max_rows / kBM + E;  // bound on sum_e ceil(rows_e / kBM)
         const int nt_up = (int)ceil_div(dff, kBN / 2);
         const int nt_dn = (int)ceil_div(d, kBN);
+        const int S = ffn_splits(p, max_rows);
+        const size_t split_stride = (size_t)max_rows * d;
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(x_perm),
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
-                           offsets, E, dff, d, nt_up, h);
-        hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(kGemmThreads),
+                           offsets, E, dff, d, nt_up, 1, (size_t)0, h);
+        hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(h),
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
-                           offsets, E, d, dff, nt_dn, y_perm);
+                           offsets, E, d, dff, nt_dn, S, split_stride, y_perm);
     } else {
         const int64_t mt = max_rows / kF32BM + E;
         const int nt_up = (int)ceil_div(dff, kF32BN);

@@ -59,10 +59,15 @@ struct ForwardWs {
     void *dispatch, *x_perm, *h, *y_perm;
 };
 
+size_t y_perm_bytes(const moe_params &p) {
+    const size_t R = (size_t)max_rows_of(p);
+    return (size_t)ffn_splits(p, (int64_t)R) * R * p.d * sizeof(float);
+}
+
 size_t forward_ws_bytes(const moe_params &p) {
     const size_t R = (size_t)max_rows_of(p);
     return align256(dispatch_scratch_bytes(p.T, p.E, p.k)) + align256(R * p.d * esize(p)) +
-           align256(R * p.d_ff * esize(p)) + align256(R * p.d * sizeof(float));
+           align256(R * p.d_ff * esize(p)) + align256(y_perm_bytes(p));
 }
 
 ForwardWs carve_forward(void *ws, const moe_params &p) {
@@ -96,6 +101,11 @@ int64_t moe_max_rows(const moe_params *p) {
 size_t moe_dispatch_workspace_bytes(const moe_params *p) {
     if (check_params(p) != MOE_OK) return 0;
     return dispatch_scratch_bytes(p->T, p->E, p->k);
+}
+
+int moe_ffn_splits(const moe_params *p) {
+    if (check_params(p) != MOE_OK) return -1;
+    return ffn_splits(*p, max_rows_of(*p));
 }
 
 size_t moe_workspace_bytes(const moe_params *p) {
@@ -146,7 +156,9 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
     if (rc != MOE_OK) return rc;
     if (p->T > 0 && (!row || !gate || !y || (max_rows_of(*p) > 0 && !y_perm))) return MOE_ERR_INVALID_ARG;
     if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
-    return hip_status(launch_combine(*p, y_perm, row, gate, y, static_cast<hipStream_t>(stream)));
+    const int64_t R = max_rows_of(*p);
+    return hip_status(launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, y_perm, row, gate, y,
+                                     static_cast<hipStream_t>(stream)));
 }
 
 int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
@@ -171,7 +183,7 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_expert_ffn(*p, R, f.x_perm, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    e = launch_combine(*p, f.y_perm, r->row, r->gate, y, st);
+    e = launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, f.y_perm, r->row, r->gate, y, st);
     return hip_status(e);
 }
 

@@ -48,11 +48,15 @@ hipError_t launch_route(const moe_params &p, const void *x, const void *wr, cons
 hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
                            void *x_perm, const DispatchScratch &ws, hipStream_t st);
 
+// Number of d_ff slices the down projection is split into (y_perm holds one
+// fp32 partial per slice; the combine adds them).  1 for fp32 layers.
+int ffn_splits(const moe_params &p, int64_t max_rows);
+
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *x_perm,
                              const int32_t *offsets, const void *w1, const void *w3,
                              const void *w2, void *h, void *y_perm, hipStream_t st);
 
-hipError_t launch_combine(const moe_params &p, const void *y_perm, const int32_t *row,
-                          const float *gate, void *y, hipStream_t st);
+hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
+                          const int32_t *row, const float *gate, void *y, hipStream_t st);
 
 }  // namespace moe

@@ -191,7 +191,7 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
     # ---- expert FFN
     say(f"[expert_ffn] {cfg.name} rows={rows}")
     h = torch.empty((max(R, 1), dff), dtype=torch.float16 if p.dtype == moe.MOE_BF16 else dt, device=DEV)
-    y_perm = torch.empty((max(R, 1), d), dtype=torch.float32, device=DEV)
+    y_perm = moe.alloc_y_perm(p, DEV)
     moe.expert_ffn(p, x_perm, r.offsets, g["w1"], g["w3"], g["w2"], h, y_perm)
     torch.cuda.synchronize()
     offs = ref["offsets"]
@@ -204,14 +204,20 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
             assert_close_elementwise(h.float().cpu().numpy()[srows], ho, 2.0 ** -10, 1e-4, "h")
         else:
             assert_close_elementwise(h.cpu().numpy()[srows], ho, 1e-5, 1e-5, "h")
-        assert_close(y_perm.cpu().numpy()[srows], yo, p.dtype, "y_perm")
+        yp_sum = y_perm.double().sum(dim=0).cpu().numpy()  # the S slices of the d_ff reduction
+        assert_close(yp_sum[srows], yo, p.dtype, "y_perm")
 
     # ---- combine
     say(f"[combine] {cfg.name}")
     y = torch.empty((T, d), dtype=dt, device=DEV)
     moe.combine(p, y_perm, r.row, r.gate, y)
     torch.cuda.synchronize()
-    yc = oracle.combine(rc["row"].numpy(), rc["gate"].numpy(), np_of(y_perm[:max(rows, 1)].cpu()))
+    # the oracle combines full y_perm rows: the sum of the device's S slices, formed in fp32 in
+    # slice order as the combine forms it
+    yp_rows = y_perm[0].clone()
+    for sl in range(1, y_perm.shape[0]):
+        yp_rows += y_perm[sl]
+    yc = oracle.combine(rc["row"].numpy(), rc["gate"].numpy(), np_of(yp_rows[:max(rows, 1)].cpu()))
     # combine's only rounding is the final store
     assert_close_elementwise(y.float().cpu().numpy(), yc, 2.0 ** -8 if p.dtype == moe.MOE_BF16 else 1e-6,
                              1e-6, "combine")
