@@ -167,6 +167,8 @@ __device__ __forceinline__ void issue_loads(const GemmThread &g, char *stage, ui
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; j++) {
         const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group
+        // rows past the tile's last valid row re-read that row (clamped
+        // addresses), which the L1 serves; they feed only discarded outputs
         if (HALF == 0)
             g2lds16(g.a_base + g.a_off[j] + kb, stage + grp * 1024);
         else
@@ -183,22 +185,21 @@ __device__ __forceinline__ void load_frags(const GemmThread &g, const char *stag
     for (int jn = 0; jn < 4; jn++) bf[jn] = lds_read16(stage + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
 }
 
-// MFMAs of one 16-wide K sub-step.  In a partial tile, 32-row blocks at or
-// past nact are skipped (a wave-uniform branch) so ragged tails cost little
-// matrix-core time; full tiles run straight-line code.
-template <int MODE, bool FULL>
-__device__ __forceinline__ void mfma_substep(const uint4 (&af)[4], const uint4 (&bf)[4], int nact,
+// MFMAs of one 16-wide K sub-step on the first NACT 32-row blocks of the
+// wave (a partial tile's blocks past the expert's last row do no matrix-core
+// work).  NACT is a template parameter so every variant is straight-line.
+template <int MODE, int NACT>
+__device__ __forceinline__ void mfma_substep(const uint4 (&af)[4], const uint4 (&bf)[4],
                                              f32x16_t (&acc)[4][4]) {
     constexpr bool kF16 = MODE == kDown;
+    if (NACT == 0) return;
     uint4 bw[4];
 #pragma unroll
     for (int jn = 0; jn < 4; jn++) bw[jn] = kF16 ? bf16x8_to_f16x8(bf[jn]) : bf[jn];
 #pragma unroll
-    for (int i = 0; i < 4; i++) {
-        if (FULL || i < nact) {
+    for (int i = 0; i < NACT; i++) {
 #pragma unroll
-            for (int jn = 0; jn < 4; jn++) acc[i][jn] = mfma32<kF16>(af[i], bw[jn], acc[i][jn]);
-        }
+        for (int jn = 0; jn < 4; jn++) acc[i][jn] = mfma32<kF16>(af[i], bw[jn], acc[i][jn]);
     }
 }
 
@@ -210,18 +211,20 @@ __device__ __forceinline__ void mfma_substep(const uint4 (&af)[4], const uint4 (
 // keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "memory"); }
 
-template <bool FULL, int SS>
+template <int NACT, int SS>
 __device__ __forceinline__ void sched_substep() {
-    if (FULL) {
-        // next fragments in the first half, global loads in the second
+    // interleave: the next fragments' LDS reads among the first MFMAs, the
+    // next step's global loads among the rest
+    constexpr int kM = 4 * NACT;  // MFMAs in this sub-step
+    if (kM >= 8) {
 #pragma unroll
         for (int q = 0; q < 8; q++) {
-            SCHED_MFMA(1);
+            SCHED_MFMA(kM / 16 > 0 ? kM / 16 : 1);
             if (SS < 3) SCHED_DSR(1);
         }
 #pragma unroll
         for (int q = 0; q < 8; q++) {
-            SCHED_MFMA(1);
+            SCHED_MFMA(kM / 16 > 0 ? kM / 16 : 1);
             if (SS < 2) SCHED_VMEM(1);
         }
     }
@@ -234,28 +237,45 @@ __device__ __forceinline__ void sched_substep() {
 // then the next step's sub-step-0 fragments are read from `nxt`.  Fences
 // between sub-steps keep the compiler from chaining dependent MFMAs on one
 // accumulator.
-template <int MODE, bool FULL>
+template <int MODE, int NACT, bool MAYBE_PAD>
 __device__ __forceinline__ void kstep(const GemmThread &g, const char *cur, char *nxt, uint32_t kb_next,
-                                      int nact, uint4 (&af0)[4], uint4 (&bf0)[4],
-                                      f32x16_t (&acc)[4][4]) {
+                                      bool pad, uint4 (&af0)[4], uint4 (&bf0)[4], f32x16_t (&acc)[4][4]) {
     uint4 af1[4], bf1[4];
+    if (MAYBE_PAD) {
+        // a padding step (past an odd step count) adds zero: its A fragments
+        // are replaced by zeros with selects, not branches
+#pragma unroll
+        for (int i = 0; i < 4; i++) af0[i] = pad ? make_uint4(0, 0, 0, 0) : af0[i];
+    }
     __builtin_amdgcn_sched_barrier(0);
     load_frags<MODE>(g, cur, 1, af1, bf1);
+    if (MAYBE_PAD) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) af1[i] = pad ? make_uint4(0, 0, 0, 0) : af1[i];
+    }
     issue_loads<0>(g, nxt, kb_next);
-    mfma_substep<MODE, FULL>(af0, bf0, nact, acc);
-    sched_substep<FULL, 0>();
+    mfma_substep<MODE, NACT>(af0, bf0, acc);
+    sched_substep<NACT, 0>();
     __builtin_amdgcn_sched_barrier(0);
     load_frags<MODE>(g, cur, 2, af0, bf0);
+    if (MAYBE_PAD) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) af0[i] = pad ? make_uint4(0, 0, 0, 0) : af0[i];
+    }
     issue_loads<1>(g, nxt, kb_next);
-    mfma_substep<MODE, FULL>(af1, bf1, nact, acc);
-    sched_substep<FULL, 1>();
+    mfma_substep<MODE, NACT>(af1, bf1, acc);
+    sched_substep<NACT, 1>();
     __builtin_amdgcn_sched_barrier(0);
     load_frags<MODE>(g, cur, 3, af1, bf1);
-    mfma_substep<MODE, FULL>(af0, bf0, nact, acc);
-    sched_substep<FULL, 2>();
+    if (MAYBE_PAD) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) af1[i] = pad ? make_uint4(0, 0, 0, 0) : af1[i];
+    }
+    mfma_substep<MODE, NACT>(af0, bf0, acc);
+    sched_substep<NACT, 2>();
     __builtin_amdgcn_sched_barrier(0);
-    mfma_substep<MODE, FULL>(af1, bf1, nact, acc);
-    sched_substep<FULL, 3>();
+    mfma_substep<MODE, NACT>(af1, bf1, acc);
+    sched_substep<NACT, 3>();
     __builtin_amdgcn_sched_barrier(0);
     WAIT_VMCNT(0);
     block_sync();
@@ -264,11 +284,11 @@ __device__ __forceinline__ void kstep(const GemmThread &g, const char *cur, char
 
 // The K loop over pairs of steps: stage 0 computes while stage 1 fills,
 // then the reverse.  The two stages are distinct LDS objects so the compiler
-// can see that reading one never waits on the loads into the other.  FULL
-// requires an even step count; otherwise the extra step runs no MFMAs.
-// Loads past the last step re-read the last tile.
-template <int MODE, bool FULL>
-__device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s1, int nk, int nact,
+// can see that reading one never waits on the loads into the other.  With an
+// odd step count (ODD) the last pair's second step is padding that adds
+// zero; loads past the last step re-read the last tile.
+template <int MODE, int NACT, bool ODD>
+__device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s1, int nk,
                                           f32x16_t (&acc)[4][4]) {
     auto kb = [nk](int k) -> uint32_t { return (uint32_t)min(k, nk - 1) * kRowBytes; };
     issue_loads<0>(g, s0, kb(0));
@@ -278,10 +298,63 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s
     uint4 af0[4], bf0[4];
     load_frags<MODE>(g, s0, 0, af0, bf0);
     for (int k = 0; k < nk; k += 2) {
-        const int n1 = FULL || k + 1 < nk ? nact : 0;
-        kstep<MODE, FULL>(g, s0, s1, kb(k + 1), nact, af0, bf0, acc);
-        kstep<MODE, FULL>(g, s1, s0, kb(k + 2), n1, af0, bf0, acc);
+        kstep<MODE, NACT, false>(g, s0, s1, kb(k + 1), false, af0, bf0, acc);
+        kstep<MODE, NACT, ODD>(g, s1, s0, kb(k + 2), k + 1 >= nk, af0, bf0, acc);
     }
+}
+
+// Epilogue: lane holds column l5 of each 32x32 block, rows 8*(q/4) + 4*hi + q%4.
+template <int MODE, int NACT>
+__device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, int wm, int wn, int lane,
+                                           size_t split_stride, const f32x16_t (&acc)[4][4], void *out_v) {
+    const int l5 = lane & 31, hi = lane >> 5;
+    uint16_t *out_h = static_cast<uint16_t *>(out_v);
+    float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
+#pragma unroll
+    for (int i = 0; i < NACT; i++) {
+        const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * hi;
+        if (MODE == kGateUp) {
+#pragma unroll
+            for (int jn = 0; jn < 2; jn++) {
+                const int col = n0 + wn * 64 + jn * 32 + l5;
+                if (col >= N) continue;
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    const int m = rbase + 8 * (q >> 2) + (q & 3);
+                    if (m < ti.mend)
+                        out_h[(size_t)m * N + col] = f32_to_f16_sat(silu_mul(acc[i][jn][q], acc[i][jn + 2][q]));
+                }
+            }
+        } else {
+#pragma unroll
+            for (int jn = 0; jn < 4; jn++) {
+                const int col = n0 + wn * 128 + jn * 32 + l5;
+                if (col >= N) continue;
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    const int m = rbase + 8 * (q >> 2) + (q & 3);
+                    if (m < ti.mend) out_y[(size_t)m * N + col] = acc[i][jn][q];
+                }
+            }
+        }
+    }
+}
+
+// A whole tile for one (active blocks, odd step count) variant: the
+// accumulators live only inside this function, so the variants never merge.
+template <int MODE, int NACT, bool ODD>
+__device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti, char *s0, char *s1,
+                                         int nk, int n0, int N, int wm, int wn, int lane,
+                                         size_t split_stride, void *out_v) {
+    f32x16_t acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+#pragma unroll
+        for (int jn = 0; jn < 4; jn++)
+#pragma unroll
+            for (int q = 0; q < 16; q++) acc[i][jn][q] = 0.0f;
+    main_loop<MODE, NACT, ODD>(g, s0, s1, nk, acc);
+    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v);
 }
 
 // MODE kGateUp: A = x_perm (bf16), B = W1/W3 (bf16), writes h (fp16).
@@ -351,52 +424,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const int nact_raw = (ti.mend - (ti.m0 + wm * 128) + 31) / 32;
     const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
 
-    f32x16_t acc[4][4];
-#pragma unroll
-    for (int i = 0; i < 4; i++)
-#pragma unroll
-        for (int jn = 0; jn < 4; jn++)
-#pragma unroll
-            for (int q = 0; q < 16; q++) acc[i][jn][q] = 0.0f;
-
     const int nk = ks / kBK;
-    if (nact == 4 && nk % 2 == 0)
-        main_loop<MODE, true>(g, lds_s0, lds_s1, nk, nact, acc);
-    else
-        main_loop<MODE, false>(g, lds_s0, lds_s1, nk, nact, acc);
-
-    // epilogue: lane holds column l5 of each 32x32 block, rows 8*(q/4) + 4*hi + q%4
-    uint16_t *out_h = static_cast<uint16_t *>(out_v);
-    float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
-#pragma unroll
-    for (int i = 0; i < 4; i++) {
-        if (i >= nact) continue;
-        const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * hi;
-        if (MODE == kGateUp) {
-#pragma unroll
-            for (int jn = 0; jn < 2; jn++) {
-                const int col = n0 + wn * 64 + jn * 32 + l5;
-                if (col >= N) continue;
-#pragma unroll
-                for (int q = 0; q < 16; q++) {
-                    const int m = rbase + 8 * (q >> 2) + (q & 3);
-                    if (m < ti.mend)
-                        out_h[(size_t)m * N + col] = f32_to_f16_sat(silu_mul(acc[i][jn][q], acc[i][jn + 2][q]));
-                }
-            }
-        } else {
-#pragma unroll
-            for (int jn = 0; jn < 4; jn++) {
-                const int col = n0 + wn * 128 + jn * 32 + l5;
-                if (col >= N) continue;
-#pragma unroll
-                for (int q = 0; q < 16; q++) {
-                    const int m = rbase + 8 * (q >> 2) + (q & 3);
-                    if (m < ti.mend) out_y[(size_t)m * N + col] = acc[i][jn][q];
-                }
-            }
-        }
+#define MOE_TILE(n)                                                                                  \
+    do {                                                                                             \
+        if (nk & 1)                                                                                  \
+            run_tile<MODE, n, true>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v);  \
+        else                                                                                         \
+            run_tile<MODE, n, false>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v); \
+    } while (0)
+    switch (nact) {
+        case 4: MOE_TILE(4); break;
+        case 3: MOE_TILE(3); break;
+        case 2: MOE_TILE(2); break;
+        case 1: MOE_TILE(1); break;
+        default: MOE_TILE(0); break;
     }
+#undef MOE_TILE
 }
 
 // ---------------------------------------------------------------- fp32 ----
