@@ -36,6 +36,29 @@ def parse():
     return ap.parse_args()
 
 
+def gemm_traffic(workload):
+    """HBM-side bytes (fetched + written) of one moe_expert_ffn call (both
+    grouped-GEMM launches), from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary of this workload, scaled by its copy calibration.
+    None when there is no summary or the GEMM source changed since."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
+    if not m:
+        return None
+    blob = json.loads(m.group(1))
+    src = os.path.join(ROOT, "sparse_mixture_experts_gemm_amd", "csrc", "expert_gemm.hip")
+    if hashlib.sha256(open(src, "rb").read()).hexdigest() != blob.get("expert_gemm_hip_sha256"):
+        return None
+    ks = [v for k, v in blob["kernels"].items() if k.startswith("grouped_gemm")]
+    if not ks:
+        return None
+    return sum(v["fetch_bytes"] + v["write_bytes"] for v in ks)
+
+
 def stage_bytes_flops(cfg, rows, active_experts, splits=1):
     """Algorithmic work per stage (what the method must touch)."""
     T, d, E, dff = cfg.T, cfg.d, cfg.E, cfg.d_ff
@@ -167,6 +190,8 @@ def main():
         gbs = work["gemm_weight_bytes"] / (t_ffn * 1e-3) / 1e9
         roofline = {"kernel": "expert grouped GEMM (weight streaming)", "bound": "hbm", "achieved": gbs,
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+
+    roofline["traffic"] = gemm_traffic(args.workload)
 
     cpu = None
     if not args.no_cpu_baseline:

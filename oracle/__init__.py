@@ -36,7 +36,7 @@ def build(force: bool = True) -> str:
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
+        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         L = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
