@@ -60,45 +60,76 @@ __device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Flat work index -> (expert, m range, n tile, K split).  Work items are
 // ordered expert, split, n tile, m tile (m fastest), so the m tiles that
-// share a weight tile are adjacent.  Returns false past the end.
+// share a weight tile are adjacent.
 struct TileInfo {
     int e, m0, mend, nt, split;
 };
 
+// Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).
+// The grid is sized by a bound on the work count; the real count comes from
+// the device-side offsets.  Each XCD is given an equal, contiguous range of
+// the real work items, so its L2 serves tiles that share operands and no
+// XCD is left with the empty tail of the grid.  Wave-parallel: lane l owns
+// experts 4l .. 4l+3 (E <= 256).  Returns false for blocks with no work.
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int ntiles_n,
-                                          int bm, int splits, int L, TileInfo &ti) {
-    int base = 0;
-    for (int e = 0; e < E; e++) {
-        const int beg = offsets[e], end = offsets[e + 1];
-        const int mt = (end - beg + bm - 1) / bm;
-        const int per_split = mt * ntiles_n;
-        const int cnt = per_split * splits;
-        if (L < base + cnt) {
-            const int local = L - base;
-            ti.e = e;
-            ti.split = local / per_split;
-            const int rem = local % per_split;
-            ti.nt = rem / mt;
-            ti.m0 = beg + (rem % mt) * bm;
-            ti.mend = end;
-            return true;
-        }
-        base += cnt;
+                                          int bm, int splits, int blk, TileInfo &ti) {
+    const int lane = lane_id();
+    const int e0 = lane * 4;
+    int mts[4], c = 0;
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int e = e0 + j;
+        mts[j] = e < E ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+        c += mts[j];
     }
-    return false;
+    int incl = c;  // inclusive prefix of m tiles over lanes
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += v;
+    }
+    const int per = ntiles_n * splits;  // work items per m tile
+    const int total = __builtin_amdgcn_readlane(incl, 63) * per;
+    const int xcd = blk & 7, local = blk >> 3;
+    const int q = total >> 3, r = total & 7;
+    if (local >= q + (xcd < r ? 1 : 0)) return false;
+    const int L = xcd * q + min(xcd, r) + local;
+    const int lo = (incl - c) * per, hi = incl * per;
+    const bool mine = L >= lo && L < hi;
+    int e_sel = 0, base_sel = 0;
+    if (mine) {
+        int b = lo;
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            const int cnt = mts[j] * per;
+            if (L >= b && L < b + cnt) {
+                e_sel = e0 + j;
+                base_sel = b;
+            }
+            b += cnt;
+        }
+    }
+    const int owner = __builtin_ctzll(ballot64(mine));
+    const int e = __builtin_amdgcn_readlane(e_sel, owner);
+    const int base = __builtin_amdgcn_readlane(base_sel, owner);
+    const int beg = offsets[e], end = offsets[e + 1];
+    const int mt = (end - beg + bm - 1) / bm;
+    const int local_e = L - base;
+    const int per_split = mt * ntiles_n;
+    ti.e = e;
+    ti.split = local_e / per_split;
+    const int rem = local_e % per_split;
+    ti.nt = rem / mt;
+    ti.m0 = beg + (rem % mt) * bm;
+    ti.mend = end;
+    return true;
 }
 
-// Round-robin XCD placement: block b runs on XCD b % 8.  Give each XCD a
-// contiguous range of logical tiles.
-__device__ __forceinline__ int xcd_remap(int b, int nblk) {
-    const int q = nblk / 8, rem = nblk % 8;
-    const int xcd = b % 8, local = b / 8;
-    const int start = xcd * q + min(xcd, rem);
-    return start + local;
-}
-
+// silu(a) * b with the hardware exp and reciprocal (about 1 ulp each in
+// fp32, far below the fp16 / fp32 rounding of the stored result).  Large
+// negative a gives exp -> inf, rcp -> 0, so silu -> -0.
 __device__ __forceinline__ float silu_mul(float a, float b) {
-    return a / (1.0f + __expf(-a)) * b;
+    return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)) * b;
 }
 
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -303,29 +334,53 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s
     }
 }
 
-// Epilogue: lane holds column l5 of each 32x32 block, rows 8*(q/4) + 4*hi + q%4.
+// Epilogue.  MFMA output layout: the lane holds column l5 of each 32x32
+// block, rows 8*(q/4) + 4*hi + q%4.
+// Gate-up: h = silu(W1 part) * (W3 part) in fp16.  Two-byte stores straight
+// from that layout would take 128 store instructions per wave, so each wave
+// stages its 128 x 64 block of h in LDS (row stride 128 B, the 16-byte
+// chunks of a row XOR-swizzled by row % 8 so the two half-waves write
+// disjoint banks) and writes it back with 16-byte stores, eight lanes per
+// 128-byte row segment.  Only the wave's own LDS region is touched, so no
+// barrier is needed between the LDS writes and reads.
+// Down: fp32 partial products, 32 lanes store one 128-byte row segment.
 template <int MODE, int NACT>
 __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, int wm, int wn, int lane,
-                                           size_t split_stride, const f32x16_t (&acc)[4][4], void *out_v) {
+                                           size_t split_stride, const f32x16_t (&acc)[4][4], void *out_v,
+                                           char *stage, int wave) {
     const int l5 = lane & 31, hi = lane >> 5;
-    uint16_t *out_h = static_cast<uint16_t *>(out_v);
-    float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
+    if (MODE == kGateUp) {
+        uint16_t *out_h = static_cast<uint16_t *>(out_v);
+        char *w = stage + wave * (128 * kRowBytes);
 #pragma unroll
-    for (int i = 0; i < NACT; i++) {
-        const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * hi;
-        if (MODE == kGateUp) {
+        for (int i = 0; i < NACT; i++)
 #pragma unroll
-            for (int jn = 0; jn < 2; jn++) {
-                const int col = n0 + wn * 64 + jn * 32 + l5;
-                if (col >= N) continue;
+            for (int jn = 0; jn < 2; jn++)
 #pragma unroll
                 for (int q = 0; q < 16; q++) {
-                    const int m = rbase + 8 * (q >> 2) + (q & 3);
-                    if (m < ti.mend)
-                        out_h[(size_t)m * N + col] = f32_to_f16_sat(silu_mul(acc[i][jn][q], acc[i][jn + 2][q]));
+                    const int row = i * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
+                    const int col = jn * 32 + l5;
+                    const int chunk = (col >> 3) ^ (row & 7);
+                    *reinterpret_cast<uint16_t *>(w + row * kRowBytes + chunk * 16 + (col & 7) * 2) =
+                        f32_to_f16_sat(silu_mul(acc[i][jn][q], acc[i][jn + 2][q]));
+                    // one 16-value block at a time keeps the live register set small
+                    if (q == 15) __builtin_amdgcn_sched_barrier(0);
                 }
-            }
-        } else {
+        const int cb = n0 + wn * 64;  // first column of this wave's block (N is a multiple of 64)
+        if (cb >= N) return;
+#pragma unroll
+        for (int rd = 0; rd < NACT * 4; rd++) {
+            const int row = rd * 8 + (lane >> 3), pc = lane & 7;
+            const uint4 v = lds_read16(w + row * kRowBytes + pc * 16);
+            const int m = ti.m0 + wm * 128 + row;
+            if (m < ti.mend)
+                *reinterpret_cast<uint4 *>(out_h + (size_t)m * N + cb + ((pc ^ (row & 7)) << 3)) = v;
+        }
+    } else {
+        float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
+#pragma unroll
+        for (int i = 0; i < NACT; i++) {
+            const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * hi;
 #pragma unroll
             for (int jn = 0; jn < 4; jn++) {
                 const int col = n0 + wn * 128 + jn * 32 + l5;
@@ -354,7 +409,10 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
 #pragma unroll
             for (int q = 0; q < 16; q++) acc[i][jn][q] = 0.0f;
     main_loop<MODE, NACT, ODD>(g, s0, s1, nk, acc);
-    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v);
+    // every wave's fragment reads are done before the stage is reused
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    block_sync();
+    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v, s0, g.wave);
 }
 
 // MODE kGateUp: A = x_perm (bf16), B = W1/W3 (bf16), writes h (fp16).
@@ -385,7 +443,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const int wm = wave >> 1, wn = wave & 1;
 
     TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kBM, splits, xcd_remap(blockIdx.x, gridDim.x), ti)) return;
+    if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, ti)) return;
     const int n0 = MODE == kGateUp ? ti.nt * (kBN / 2) : ti.nt * kBN;
     const size_t wexp = (size_t)ti.e * N * K;
     const int ks = K / splits;              // K elements of this split
