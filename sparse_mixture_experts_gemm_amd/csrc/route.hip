@@ -24,7 +24,7 @@
 namespace moe {
 namespace {
 
-constexpr int kRouteThreads = 256;
+constexpr int kRouteThreads = 512;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kRouteLdsW = 64 * 1024;  // bytes of gate vectors staged per chunk
 
@@ -85,23 +85,89 @@ __device__ __forceinline__ void argmax_step(float &s, int &i) {
     }
 }
 
-// NX: 16-byte chunks of one x row per lane; TPW: tokens per wave.
+typedef __attribute__((address_space(3))) char lds_char_t;
+typedef const __attribute__((address_space(1))) char gbl_char_t;
+
+// Stage `bytes` of gate vectors (a contiguous range of W rows) into `dst`
+// with direct global -> LDS loads: wave w moves the 1 KiB pieces w, w+8, ...
+// (lanes past the end re-read the last 16 bytes; `dst` has room for whole
+// pieces).  No registers are involved and nothing waits here.
+__device__ __forceinline__ void stage_w(const char *src, int bytes, char *dst, int wave, int lane) {
+    const int pieces = (bytes + 1023) >> 10;
+    for (int i = wave; i < pieces; i += kRouteWaves) {
+        const int off = min(i * 1024 + lane * 16, bytes - 16);
+        __builtin_amdgcn_global_load_lds((gbl_char_t *)(src + off), (lds_char_t *)(dst + i * 1024), 16, 0, 0);
+    }
+}
+
+// Logits of experts [e0, e0 + ec) for this wave's TPW tokens from the gate
+// vectors staged at w_lds, written to lg[token][expert].  Per group of EA
+// experts: all NX gate-vector chunks of one expert are read from LDS first,
+// then used for the TPW tokens held in registers (no lane-dependent
+// branches: x chunks past the row end are zero, so the gate-vector read is
+// simply clamped).  EA x TPW partial sums per lane then go through one
+// butterfly reduce-scatter.
 template <typename TIn, int NX, int TPW>
+__device__ __forceinline__ void route_chunk(const uint4 *w_lds, const uint4 (&xr)[TPW][NX], int nchunk, int e0,
+                                            int ec, const float *__restrict__ bias, float *lg, int E, int lane) {
+    constexpr int EA = 32 / TPW;  // experts accumulated together
+    for (int ea = 0; ea < ec; ea += EA) {
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 32; i++) v[i] = 0.0f;
+#pragma unroll
+        for (int q = 0; q < EA; q++) {
+            if (ea + q < ec) {  // wave-uniform
+                const uint4 *wrow = w_lds + (size_t)(ea + q) * nchunk;
+                uint4 w[NX];
+#pragma unroll
+                for (int c = 0; c < NX; c++) w[c] = wrow[min(lane + 64 * c, nchunk - 1)];
+#pragma unroll
+                for (int c = 0; c < NX; c++)
+#pragma unroll
+                    for (int j = 0; j < TPW; j++) v[j * EA + q] = ChunkDot<TIn>::dot(xr[j][c], w[c], v[j * EA + q]);
+            }
+        }
+        // reduce-scatter: lane keeps value index (lane >> 1) & 31
+        rs_step<32, 32>(v, lane);
+        rs_step<16, 16>(v, lane);
+        rs_step<8, 8>(v, lane);
+        rs_step<4, 4>(v, lane);
+        rs_step<2, 2>(v, lane);
+        v[0] += exch_f32<1>(v[0]);
+        const int idx = (lane >> 1) & 31;
+        const int j = idx / EA, q = idx % EA;
+        const int e = e0 + ea + q;
+        if ((lane & 1) == 0 && ea + q < ec) {
+            float r = v[0];
+            if (bias) r = r + bias[e];
+            lg[j * E + e] = r;
+        }
+    }
+}
+
+// NX: 16-byte chunks of one x row per lane; TPW: tokens per wave; NB: W
+// buffers (1 when all E gate vectors fit one chunk, else 2: the next chunk
+// streams in while the current one is used).
+template <typename TIn, int NX, int TPW, int NB>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wr, const float *__restrict__ bias,
     const float *__restrict__ load, float neg_lambda, int T, int d, int E, int K1, int EC,
     float *__restrict__ logits, int32_t *__restrict__ cand, float *__restrict__ cand_score) {
-    constexpr int EA = 32 / TPW;  // experts accumulated together
     constexpr int kVec = ChunkDot<TIn>::kVec;
-    extern __shared__ uint4 lds[];
+    // two distinct objects, so the compiler sees that the loads into one
+    // buffer never alias the reads of the other
+    __shared__ __attribute__((aligned(1024))) char w_buf0[kRouteLdsW];
+    __shared__ __attribute__((aligned(1024))) char w_buf1[NB == 2 ? kRouteLdsW : 1024];
+    __shared__ float lg_all[kRouteWaves * TPW * kMaxExperts];
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunk = d / kVec;
+    const int row_bytes = d * (int)sizeof(TIn);
     const int t0 = (blockIdx.x * kRouteWaves + wave) * TPW;
+    float *lg = lg_all + wave * TPW * E;  // [TPW][E]
 
-    uint4 *w_lds = lds;                                            // [EC][nchunk]
-    float *lg = reinterpret_cast<float *>(lds + (size_t)EC * nchunk) + wave * TPW * E;  // [TPW][E]
-
+    // this wave's x rows, 16-byte chunks lane + 64 c (zero past the row end)
     uint4 xr[TPW][NX];
 #pragma unroll
     for (int j = 0; j < TPW; j++) {
@@ -116,50 +182,28 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         }
     }
 
-    for (int e0 = 0; e0 < E; e0 += EC) {
-        const int ec = min(EC, E - e0);
-        __syncthreads();
-        const uint4 *src = reinterpret_cast<const uint4 *>(wr) + (size_t)e0 * nchunk;
-        for (int i = threadIdx.x; i < ec * nchunk; i += kRouteThreads) w_lds[i] = src[i];
-        __syncthreads();
-
-        for (int ea = 0; ea < ec; ea += EA) {
-            float v[32];
-#pragma unroll
-            for (int i = 0; i < 32; i++) v[i] = 0.0f;
-#pragma unroll
-            for (int q = 0; q < EA; q++) {
-                if (ea + q < ec) {
-                    const uint4 *wrow = w_lds + (size_t)(ea + q) * nchunk;
-#pragma unroll
-                    for (int c = 0; c < NX; c++) {
-                        const int ci = lane + 64 * c;
-                        if (ci < nchunk) {
-                            const uint4 w = wrow[ci];
-#pragma unroll
-                            for (int j = 0; j < TPW; j++) v[j * EA + q] = ChunkDot<TIn>::dot(xr[j][c], w, v[j * EA + q]);
-                        }
-                    }
-                }
-            }
-            // reduce-scatter: lane keeps value index (lane >> 1) & 31
-            rs_step<32, 32>(v, lane);
-            rs_step<16, 16>(v, lane);
-            rs_step<8, 8>(v, lane);
-            rs_step<4, 4>(v, lane);
-            rs_step<2, 2>(v, lane);
-            v[0] += exch_f32<1>(v[0]);
-            const int idx = (lane >> 1) & 31;
-            const int j = idx / EA, q = idx % EA;
-            const int e = e0 + ea + q;
-            if ((lane & 1) == 0 && ea + q < ec) {
-                float r = v[0];
-                if (bias) r = r + bias[e];
-                lg[j * E + e] = r;
-            }
-        }
-    }
+    const char *wsrc = reinterpret_cast<const char *>(wr);
+    stage_w(wsrc, min(EC, E) * row_bytes, w_buf0, wave, lane);
+    __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
+    // chunks of EC experts, alternating buffers (unrolled by two so each
+    // use names a fixed buffer); the next chunk streams in during the use
+    for (int e0 = 0; e0 < E; e0 += 2 * EC) {
+        if (NB == 2 && e0 + EC < E)
+            stage_w(wsrc + (size_t)(e0 + EC) * row_bytes, min(EC, E - e0 - EC) * row_bytes, w_buf1, wave, lane);
+        route_chunk<TIn, NX, TPW>(reinterpret_cast<const uint4 *>(w_buf0), xr, nchunk, e0, min(EC, E - e0), bias,
+                                  lg, E, lane);
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __syncthreads();
+        if (NB == 1 || e0 + EC >= E) break;
+        if (e0 + 2 * EC < E)
+            stage_w(wsrc + (size_t)(e0 + 2 * EC) * row_bytes, min(EC, E - e0 - 2 * EC) * row_bytes, w_buf0,
+                    wave, lane);
+        route_chunk<TIn, NX, TPW>(reinterpret_cast<const uint4 *>(w_buf1), xr, nchunk, e0 + EC,
+                                  min(EC, E - e0 - EC), bias, lg, E, lane);
+        __builtin_amdgcn_s_waitcnt(0x0070);
+        __syncthreads();
+    }
 
     // ranking: lanes hold experts e = lane + 64 * i
     constexpr int kMaxPerLane = kMaxExperts / 64;
@@ -212,22 +256,34 @@ template <typename TIn, int NX, int TPW>
 hipError_t launch_t(const moe_params &p, const void *x, const void *wr, const float *bias,
                     const float *load, float *logits, int32_t *cand, float *cand_score,
                     hipStream_t st) {
-    const int esz = sizeof(TIn);
-    const int row_bytes = p.d * esz;
+    const int row_bytes = p.d * (int)sizeof(TIn);
     int ec = kRouteLdsW / row_bytes;  // experts staged per LDS chunk
     if (ec < 1) ec = 1;
     if (ec > p.E) ec = p.E;
-    const size_t lds = (size_t)ec * row_bytes + sizeof(float) * kRouteWaves * TPW * p.E;
-    // dynamic LDS above the default limit must be allowed per kernel
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&route_kernel<TIn, NX, TPW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
     const int tokens_per_block = kRouteWaves * TPW;
     const int grid = (int)ceil_div(p.T, tokens_per_block);
-    hipLaunchKernelGGL((route_kernel<TIn, NX, TPW>), dim3(grid), dim3(kRouteThreads), lds, st,
-                       static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load,
-                       -p.lambda, p.T, p.d, p.E, p.k + 1, ec, logits, cand, cand_score);
+    if (ec >= p.E)
+        hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, 1>), dim3(grid), dim3(kRouteThreads), 0, st,
+                           static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load,
+                           -p.lambda, p.T, p.d, p.E, p.k + 1, ec, logits, cand, cand_score);
+    else
+        hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, 2>), dim3(grid), dim3(kRouteThreads), 0, st,
+                           static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load,
+                           -p.lambda, p.T, p.d, p.E, p.k + 1, ec, logits, cand, cand_score);
     return hipGetLastError();
+}
+
+// Tokens per wave: up to 4 (more tokens share each gate-vector read from
+// LDS), fewer when that would leave compute units without a block.
+template <typename TIn, int NX>
+hipError_t launch_nx(const moe_params &p, const void *x, const void *wr, const float *bias,
+                     const float *load, float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
+    constexpr int kCUs = 256;
+    if (p.T >= kCUs * kRouteWaves * 4)
+        return launch_t<TIn, NX, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (p.T >= kCUs * kRouteWaves * 2)
+        return launch_t<TIn, NX, 2>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    return launch_t<TIn, NX, 1>(p, x, wr, bias, load, logits, cand, cand_score, st);
 }
 
 template <typename TIn>
@@ -236,10 +292,10 @@ hipError_t launch_dtype(const moe_params &p, const void *x, const void *wr, cons
                         hipStream_t st) {
     constexpr int kVec = ChunkDot<TIn>::kVec;
     const int nx = (int)ceil_div(p.d / kVec, 64);
-    if (nx <= 1) return launch_t<TIn, 1, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
-    if (nx <= 2) return launch_t<TIn, 2, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
-    if (nx <= 4) return launch_t<TIn, 4, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
-    if (nx <= 8) return launch_t<TIn, 8, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 1) return launch_nx<TIn, 1>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 2) return launch_nx<TIn, 2>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 4) return launch_nx<TIn, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 8) return launch_nx<TIn, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (nx <= 16) return launch_t<TIn, 16, 2>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (nx <= 32) return launch_t<TIn, 32, 1>(p, x, wr, bias, load, logits, cand, cand_score, st);
     return hipErrorInvalidValue;
