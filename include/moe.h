@@ -67,8 +67,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *
  * Limits: 0 <= T <= 2^20 (T = 0 is an empty batch); 1 <= E <= 256;
  * 1 <= k <= min(E, 8); d and d_ff positive multiples of 64; d <= 16384 for
- * bf16 and d <= 8192 for fp32.  Other values return MOE_ERR_INVALID_ARG (sizes)
- * or MOE_ERR_UNSUPPORTED (dtype, multiples, d too large).
+ * bf16 and d <= 8192 for fp32; one expert matrix (d * d_ff elements) below
+ * 4 GiB.  Other values return MOE_ERR_INVALID_ARG (sizes) or
+ * MOE_ERR_UNSUPPORTED (dtype, multiples, d or d * d_ff too large).
  */
 typedef struct moe_params {
     int32_t T, d, E, k, d_ff;
@@ -127,8 +128,8 @@ int moe_ffn_splits(const moe_params *p);
 size_t moe_dispatch_workspace_bytes(const moe_params *p);
 
 /* Host-side, pure: bytes of workspace moe_forward needs: the dispatch scratch
- * plus x_perm [R][d], h [R][d_ff] and y_perm [S][R][d] (fp32), each 256-byte
- * aligned. */
+ * plus h [R][d_ff] and y_perm [S][R][d] (fp32), and x_perm [R][d] only when
+ * x spans 4 GiB or more (see moe_forward), each 256-byte aligned. */
 size_t moe_workspace_bytes(const moe_params *p);
 
 /*
@@ -185,7 +186,10 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
 /*
  * Stages 1-4 on one stream with no host synchronisation.  workspace holds at
  * least moe_workspace_bytes(p) bytes (256-B aligned) and is carved into the
- * dispatch scratch, x_perm, h and y_perm.
+ * dispatch scratch, h and y_perm.  When x spans less than 4 GiB the dispatch
+ * copy of the token rows is not made: the gate-up GEMM reads its rows from x
+ * through token_of_row (same values, one pass over x fewer); otherwise
+ * x_perm is materialised in the workspace as moe_dispatch does.
  */
 int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
                 const float *load, const void *w1, const void *w3, const void *w2, void *y,

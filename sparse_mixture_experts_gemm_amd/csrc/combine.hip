@@ -36,8 +36,9 @@ __device__ __forceinline__ void store8<float>(float *y, const float (&a)[8]) {
     reinterpret_cast<float4 *>(y)[1] = make_float4(a[4], a[5], a[6], a[7]);
 }
 
-// grid.x = blocks of tpb tokens; each token's row is spread over the
-// block's threads in groups of 8 elements.
+// Sum of gate * (slices of row) for 8 consecutive elements.  Generic path
+// (any k <= 8 and any slice count): the loads of one row's slices are
+// issued together, rows one after another.
 template <typename TE>
 __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ y_perm,
                                                            const int32_t *__restrict__ row,
@@ -84,11 +85,107 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
     }
 }
 
+// The common shapes (k and the slice count known at compile time): each
+// thread owns G groups of 8 outputs of one token and issues every load it
+// needs (K rows x S slices x G groups x 32 bytes) before the first add, so
+// a wave keeps a whole token row's worth of reads in flight.  A dropped
+// slot reads row 0 and is discarded by a select, so no branch splits the
+// batch and an uninitialised row can never leak a NaN into the sum.
+template <typename TE, int K, int S, int G>
+__global__ __launch_bounds__(kThreads) void combine_fixed(const float *__restrict__ y_perm,
+                                                          const int32_t *__restrict__ row,
+                                                          const float *__restrict__ gate, int T, int d,
+                                                          size_t split_stride, TE *__restrict__ y) {
+    const int per_tok = d / (8 * G);  // threads per token (divides kThreads)
+    const int t = blockIdx.x * (kThreads / per_tok) + threadIdx.x / per_tok;
+    const int lt = threadIdx.x % per_tok;
+    if (t >= T) return;
+    int rws[K];
+    float gs[K];
+#pragma unroll
+    for (int r = 0; r < K; r++) {
+        rws[r] = row[(size_t)t * K + r];
+        gs[r] = gate[(size_t)t * K + r];
+    }
+    float4 u[G][K][S][2];
+#pragma unroll
+    for (int gi = 0; gi < G; gi++)
+#pragma unroll
+        for (int r = 0; r < K; r++)
+#pragma unroll
+            for (int sl = 0; sl < S; sl++) {
+                const float4 *src = reinterpret_cast<const float4 *>(
+                                        y_perm + sl * split_stride + (size_t)max(rws[r], 0) * d) +
+                                    2 * (lt + gi * per_tok);
+                u[gi][r][sl][0] = src[0];
+                u[gi][r][sl][1] = src[1];
+            }
+#pragma unroll
+    for (int gi = 0; gi < G; gi++) {
+        float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < K; r++) {
+            float4 p = u[gi][r][0][0], q = u[gi][r][0][1];
+#pragma unroll
+            for (int sl = 1; sl < S; sl++) {
+                p.x += u[gi][r][sl][0].x; p.y += u[gi][r][sl][0].y; p.z += u[gi][r][sl][0].z; p.w += u[gi][r][sl][0].w;
+                q.x += u[gi][r][sl][1].x; q.y += u[gi][r][sl][1].y; q.z += u[gi][r][sl][1].z; q.w += u[gi][r][sl][1].w;
+            }
+            const bool kept = rws[r] >= 0;
+            const float g = gs[r];
+            a[0] += kept ? g * p.x : 0.0f;
+            a[1] += kept ? g * p.y : 0.0f;
+            a[2] += kept ? g * p.z : 0.0f;
+            a[3] += kept ? g * p.w : 0.0f;
+            a[4] += kept ? g * q.x : 0.0f;
+            a[5] += kept ? g * q.y : 0.0f;
+            a[6] += kept ? g * q.z : 0.0f;
+            a[7] += kept ? g * q.w : 0.0f;
+        }
+        store8<TE>(y + (size_t)t * d + 8 * (lt + gi * per_tok), a);
+    }
+}
+
+template <typename TE, int K, int S>
+bool launch_fixed(const moe_params &p, size_t split_stride, const void *y_perm, const int32_t *row,
+                  const float *gate, void *y, hipStream_t st) {
+    // G = 2 groups per thread when a token row has at least 512 groups
+    const int groups = p.d / 8;
+    const int G = groups >= 2 * kThreads ? 2 : 1;
+    const int per_tok = groups / G;
+    if (per_tok > kThreads || kThreads % per_tok != 0) return false;
+    const int tpb = kThreads / per_tok;
+    const int grid = (int)ceil_div(p.T, tpb);
+    if (G == 2)
+        hipLaunchKernelGGL((combine_fixed<TE, K, S, 2>), dim3(grid), dim3(kThreads), 0, st,
+                           static_cast<const float *>(y_perm), row, gate, p.T, p.d, split_stride,
+                           static_cast<TE *>(y));
+    else
+        hipLaunchKernelGGL((combine_fixed<TE, K, S, 1>), dim3(grid), dim3(kThreads), 0, st,
+                           static_cast<const float *>(y_perm), row, gate, p.T, p.d, split_stride,
+                           static_cast<TE *>(y));
+    return true;
+}
+
+template <typename TE>
+bool launch_fixed_any(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
+                      const int32_t *row, const float *gate, void *y, hipStream_t st) {
+    if (p.k == 2 && splits == 1) return launch_fixed<TE, 2, 1>(p, split_stride, y_perm, row, gate, y, st);
+    if (p.k == 2 && splits == 2) return launch_fixed<TE, 2, 2>(p, split_stride, y_perm, row, gate, y, st);
+    if (p.k == 2 && splits == 4) return launch_fixed<TE, 2, 4>(p, split_stride, y_perm, row, gate, y, st);
+    if (p.k == 1 && splits == 1) return launch_fixed<TE, 1, 1>(p, split_stride, y_perm, row, gate, y, st);
+    return false;
+}
+
 }  // namespace
 
 hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
                           const int32_t *row, const float *gate, void *y, hipStream_t st) {
     if (p.T == 0) return hipSuccess;
+    const bool fixed = p.dtype == MOE_BF16
+                           ? launch_fixed_any<uint16_t>(p, splits, split_stride, y_perm, row, gate, y, st)
+                           : launch_fixed_any<float>(p, splits, split_stride, y_perm, row, gate, y, st);
+    if (fixed) return hipGetLastError();
     const int groups = p.d / 8;
     // tokens per block: enough threads per token to cover its row in one pass
     const int per_tok = groups < kThreads ? groups : kThreads;

@@ -307,7 +307,7 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
                        E, k, (int)C, nb, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim,
                        ws.fb_hist, r.eid, r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row,
                        r.demand, r.kept, r.totals, r.aux_loss);
-    if (T > 0) {
+    if (T > 0 && x_perm) {
         const int esz = p.dtype == MOE_BF16 ? 2 : 4;
         const int chunks = p.d * esz / 16;
         hipLaunchKernelGGL(dispatch_gather, dim3(T), dim3(256), 0, st,

@@ -179,9 +179,9 @@ __device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret
 
 // Per-thread state of the MFMA grouped GEMM.
 struct GemmThread {
-    uint32_t a_off[kLoadsPerOperand], b_off[kLoadsPerOperand];  // global byte offsets (16 B per lane)
+    uint32_t a_off[kLoadsPerOperand], b_off[kLoadsPerOperand];  // byte offsets from the bases (16 B per lane)
     const char *b_src[kLoadsPerOperand];  // uniform base per B row group (W1 / W3 / W2)
-    const char *a_base;
+    const char *a_base;                   // A rows: the tile's first row, or the unpermuted x
     uint32_t fa[2][4], fb[2][4];  // LDS byte offsets of fragments [block parity][sub-step]
     int wave;
 };
@@ -415,7 +415,10 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
     store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v, s0, g.wave);
 }
 
-// MODE kGateUp: A = x_perm (bf16), B = W1/W3 (bf16), writes h (fp16).
+// MODE kGateUp: A = x_perm (bf16), B = W1/W3 (bf16), writes h (fp16).  With
+//               a_rows, A is the unpermuted x and row m of the expert range
+//               is x row a_rows[m] (the dispatch gather folded into the A
+//               loads; x must then span less than 4 GiB).
 // MODE kDown:   A = h (fp16), B = W2 (bf16, widened to fp16 after the LDS
 //               read), writes y_perm (fp32).  The d_ff reduction is split
 //               into `splits` slices (work items of their own, for enough
@@ -432,9 +435,9 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
 // sub-step s; the swizzle of such a row is swz(l%32) ^ 4 * parity(base/32).
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
-    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B0, const uint16_t *__restrict__ B1,
-    const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n, int splits,
-    size_t split_stride, void *__restrict__ out_v) {
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
+    const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
+    int splits, size_t split_stride, void *__restrict__ out_v) {
     __shared__ __attribute__((aligned(1024))) char lds_s0[kStageBytes];
     __shared__ __attribute__((aligned(1024))) char lds_s1[kStageBytes];
     const int tid = threadIdx.x;
@@ -451,7 +454,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
 
     GemmThread g;
     g.wave = wave;
-    g.a_base = reinterpret_cast<const char *>(A);
+    // A offsets stay below 4 GiB: relative to the tile's first row, or into
+    // x (whose size the host checks) when rows are gathered
+    g.a_base = reinterpret_cast<const char *>(a_rows ? A : A + (size_t)ti.m0 * K);
     const char *b_base0 = reinterpret_cast<const char *>(B0 + wexp);
     const char *b_base1 = reinterpret_cast<const char *>((MODE == kGateUp ? B1 : B0) + wexp);
 #pragma unroll
@@ -460,7 +465,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         const int row = grp * kRowsPerLoad + (lane >> 3);
         const int c = (lane & 7) ^ swz(row);
         const int gm = min(ti.m0 + row, ti.mend - 1);
-        g.a_off[j] = ((uint32_t)gm * K + k_first + c * 8) * 2;
+        const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
+        g.a_off[j] = ((uint32_t)ar * K + k_first + c * 8) * 2;
         int gn = MODE == kGateUp ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
         gn = min(gn, N - 1);
         g.b_off[j] = ((uint32_t)gn * K + k_first + c * 8) * 2;
@@ -505,6 +511,7 @@ constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
 template <int MODE>
 __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict__ A,
+                                                        const int32_t *__restrict__ a_rows,
                                                         const float *__restrict__ B0,
                                                         const float *__restrict__ B1,
                                                         const int32_t *__restrict__ offsets, int E,
@@ -524,7 +531,8 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict_
             const int r = i / kF32BK, kk = i % kF32BK;
             int gm = ti.m0 + r;
             if (gm >= ti.mend) gm = ti.mend - 1;
-            sa[kk][r] = A[(size_t)gm * K + k0 + kk];
+            const size_t ar = a_rows ? (size_t)a_rows[gm] : (size_t)gm;
+            sa[kk][r] = A[ar * K + k0 + kk];
             int gn = n0 + r;
             if (gn >= N) gn = N - 1;
             sb0[kk][r] = B0[wexp + (size_t)gn * K + k0 + kk];
@@ -571,8 +579,8 @@ int ffn_splits(const moe_params &p, int64_t max_rows) {
 }
 
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *x_perm,
-                             const int32_t *offsets, const void *w1, const void *w3,
-                             const void *w2, void *h, void *y_perm, hipStream_t st) {
+                             const int32_t *a_rows, const int32_t *offsets, const void *w1,
+                             const void *w3, const void *w2, void *h, void *y_perm, hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
     const int E = p.E, d = p.d, dff = p.d_ff;
     if (p.dtype == MOE_BF16) {
@@ -582,11 +590,11 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *
         const int S = ffn_splits(p, max_rows);
         const size_t split_stride = (size_t)max_rows * d;
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
-                           0, st, static_cast<const uint16_t *>(x_perm),
+                           0, st, static_cast<const uint16_t *>(x_perm), a_rows,
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
                            offsets, E, dff, d, nt_up, 1, (size_t)0, h);
         hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
-                           0, st, static_cast<const uint16_t *>(h),
+                           0, st, static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
                            offsets, E, d, dff, nt_dn, S, split_stride, y_perm);
     } else {
@@ -594,11 +602,11 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *
         const int nt_up = (int)ceil_div(dff, kF32BN);
         const int nt_dn = (int)ceil_div(d, kF32BN);
         hipLaunchKernelGGL(grouped_gemm_f32<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(256), 0, st,
-                           static_cast<const float *>(x_perm), static_cast<const float *>(w1),
+                           static_cast<const float *>(x_perm), a_rows, static_cast<const float *>(w1),
                            static_cast<const float *>(w3), offsets, E, dff, d, nt_up,
                            static_cast<float *>(h));
         hipLaunchKernelGGL(grouped_gemm_f32<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(256), 0, st,
-                           static_cast<const float *>(h), static_cast<const float *>(w2),
+                           static_cast<const float *>(h), (const int32_t *)nullptr, static_cast<const float *>(w2),
                            static_cast<const float *>(w2), offsets, E, d, dff, nt_dn,
                            static_cast<float *>(y_perm));
     }

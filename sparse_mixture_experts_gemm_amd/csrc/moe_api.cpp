@@ -21,6 +21,8 @@ int check_params(const moe_params *p) {
     if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_ERR_UNSUPPORTED;
     if (p->d % 64 != 0 || p->d_ff % 64 != 0) return MOE_ERR_UNSUPPORTED;
     if (p->d > (p->dtype == MOE_BF16 ? 16384 : 8192)) return MOE_ERR_UNSUPPORTED;
+    // one expert's weight matrix is addressed with 32-bit byte offsets
+    if ((int64_t)p->d * p->d_ff * (p->dtype == MOE_BF16 ? 2 : 4) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
     if (!(p->lambda == p->lambda) || !(p->capacity_factor == p->capacity_factor)) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
@@ -54,9 +56,14 @@ int routing_ok(const moe_routing *r, const moe_params &p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// moe_forward folds the dispatch gather into the gate-up GEMM (A rows read
+// from x through token_of_row) whenever x spans less than 4 GiB, the reach
+// of the GEMM's 32-bit load offsets; x_perm is then never materialised.
+bool gather_in_gemm(const moe_params &p) { return (int64_t)p.T * p.d * (int64_t)esize(p) < ((int64_t)1 << 32); }
+
 // Workspace layout of moe_forward.
 struct ForwardWs {
-    void *dispatch, *x_perm, *h, *y_perm;
+    void *dispatch, *x_perm, *h, *y_perm;  // x_perm null when the GEMM gathers
 };
 
 size_t y_perm_bytes(const moe_params &p) {
@@ -66,8 +73,9 @@ size_t y_perm_bytes(const moe_params &p) {
 
 size_t forward_ws_bytes(const moe_params &p) {
     const size_t R = (size_t)max_rows_of(p);
-    return align256(dispatch_scratch_bytes(p.T, p.E, p.k)) + align256(R * p.d * esize(p)) +
-           align256(R * p.d_ff * esize(p)) + align256(y_perm_bytes(p));
+    const size_t xp = gather_in_gemm(p) ? 0 : align256(R * p.d * esize(p));
+    return align256(dispatch_scratch_bytes(p.T, p.E, p.k)) + xp + align256(R * p.d_ff * esize(p)) +
+           align256(y_perm_bytes(p));
 }
 
 ForwardWs carve_forward(void *ws, const moe_params &p) {
@@ -76,8 +84,11 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
     ForwardWs f;
     f.dispatch = c;
     c += align256(dispatch_scratch_bytes(p.T, p.E, p.k));
-    f.x_perm = c;
-    c += align256(R * p.d * esize(p));
+    f.x_perm = nullptr;
+    if (!gather_in_gemm(p)) {
+        f.x_perm = c;
+        c += align256(R * p.d * esize(p));
+    }
     f.h = c;
     c += align256(R * p.d_ff * esize(p));
     f.y_perm = c;
@@ -146,7 +157,7 @@ int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offse
     if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(h) ||
         !aligned16(y_perm))
         return MOE_ERR_UNSUPPORTED;
-    return hip_status(launch_expert_ffn(*p, R, x_perm, offsets, w1, w3, w2, h, y_perm,
+    return hip_status(launch_expert_ffn(*p, R, x_perm, nullptr, offsets, w1, w3, w2, h, y_perm,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -181,7 +192,10 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_dispatch(*p, C, x, *r, f.x_perm, carve_dispatch(f.dispatch, p->T, p->E, p->k), st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    e = launch_expert_ffn(*p, R, f.x_perm, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
+    if (f.x_perm)
+        e = launch_expert_ffn(*p, R, f.x_perm, nullptr, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
+    else
+        e = launch_expert_ffn(*p, R, x, r->token_of_row, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, f.y_perm, r->row, r->gate, y, st);
     return hip_status(e);

@@ -45,6 +45,7 @@ hipError_t launch_route(const moe_params &p, const void *x, const void *wr, cons
                         const float *load, float *logits, int32_t *cand, float *cand_score,
                         hipStream_t st);
 
+// x_perm == nullptr: routing only, no copy of the token rows.
 hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
                            void *x_perm, const DispatchScratch &ws, hipStream_t st);
 
@@ -52,9 +53,11 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
 // fp32 partial per slice; the combine adds them).  1 for fp32 layers.
 int ffn_splits(const moe_params &p, int64_t max_rows);
 
+// a_rows == nullptr: A is x_perm.  Otherwise A is the unpermuted x and packed
+// row m is x row a_rows[m] (token_of_row); x must span less than 4 GiB.
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *x_perm,
-                             const int32_t *offsets, const void *w1, const void *w3,
-                             const void *w2, void *h, void *y_perm, hipStream_t st);
+                             const int32_t *a_rows, const int32_t *offsets, const void *w1,
+                             const void *w3, const void *w2, void *h, void *y_perm, hipStream_t st);
 
 hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
                           const int32_t *row, const float *gate, void *y, hipStream_t st);
