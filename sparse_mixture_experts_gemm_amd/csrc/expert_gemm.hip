@@ -176,12 +176,14 @@ __device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret
 #define SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, n, 0)
 #define SCHED_DSR(n) __builtin_amdgcn_sched_group_barrier(0x100, n, 0)
 #define SCHED_VMEM(n) __builtin_amdgcn_sched_group_barrier(0x020, n, 0)
+#define SCHED_VALU(n) __builtin_amdgcn_sched_group_barrier(0x002, n, 0)
 
 // Per-thread state of the MFMA grouped GEMM.
 struct GemmThread {
     uint32_t a_off[kLoadsPerOperand], b_off[kLoadsPerOperand];  // byte offsets from the bases (16 B per lane)
     const char *b_src[kLoadsPerOperand];  // uniform base per B row group (W1 / W3 / W2)
     const char *a_base;                   // A rows: the tile's first row, or the unpermuted x
+    int a_valid;                          // valid rows of the tile (uniform)
     uint32_t fa[2][4], fb[2][4];  // LDS byte offsets of fragments [block parity][sub-step]
     int wave;
 };
@@ -193,124 +195,141 @@ __device__ __forceinline__ int b_imm(int jn) {
 }
 
 // Issue this wave's global -> LDS loads of one operand of one K step.
-template <int HALF>
+template <int HALF, bool SKIPA>
 __device__ __forceinline__ void issue_loads(const GemmThread &g, char *stage, uint32_t kb) {
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; j++) {
         const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group
-        // rows past the tile's last valid row re-read that row (clamped
-        // addresses), which the L1 serves; they feed only discarded outputs
-        if (HALF == 0)
-            g2lds16(g.a_base + g.a_off[j] + kb, stage + grp * 1024);
+        // rows past the tile's last valid row in a partly valid group re-read
+        // that row (clamped addresses)
+        // A row groups wholly past the tile's valid rows are not loaded: their
+        // LDS rows feed only discarded outputs (a block with no valid row
+        // does no MFMA at all)
+        if (HALF == 0) {
+            if (!SKIPA || grp * kRowsPerLoad < g.a_valid) g2lds16(g.a_base + g.a_off[j] + kb, stage + grp * 1024);
+        }
         else
             g2lds16(g.b_src[j] + g.b_off[j] + kb, stage + kTileBytes + grp * 1024);
     }
 }
 
+// Fragments of one 16-wide K sub-step: A of the wave's four 32-row blocks,
+// B of its four 32-column blocks.
+struct Frags {
+    uint4 a[4], b[4];
+};
+
 template <int MODE>
-__device__ __forceinline__ void load_frags(const GemmThread &g, const char *stage, int ss, uint4 (&af)[4],
-                                           uint4 (&bf)[4]) {
+__device__ __forceinline__ void load_frags(const GemmThread &g, const char *stage, int ss, Frags &f) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) af[i] = lds_read16(stage + g.fa[i & 1][ss] + i * 32 * kRowBytes);
+    for (int i = 0; i < 4; i++) f.a[i] = lds_read16(stage + g.fa[i & 1][ss] + i * 32 * kRowBytes);
 #pragma unroll
-    for (int jn = 0; jn < 4; jn++) bf[jn] = lds_read16(stage + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
+    for (int jn = 0; jn < 4; jn++) f.b[jn] = lds_read16(stage + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
 }
 
-// MFMAs of one 16-wide K sub-step on the first NACT 32-row blocks of the
-// wave (a partial tile's blocks past the expert's last row do no matrix-core
-// work).  NACT is a template parameter so every variant is straight-line.
-template <int MODE, int NACT>
-__device__ __forceinline__ void mfma_substep(const uint4 (&af)[4], const uint4 (&bf)[4],
-                                             f32x16_t (&acc)[4][4]) {
+// Down GEMM: W2 fragments (bf16) widened to fp16 for the fp16 MFMA.
+template <int MODE>
+__device__ __forceinline__ void widen_b(Frags &f) {
+    if (MODE == kDown) {
+#pragma unroll
+        for (int jn = 0; jn < 4; jn++) f.b[jn] = bf16x8_to_f16x8(f.b[jn]);
+    }
+}
+
+// A padding step (past an odd step count) must add zero: its A fragments
+// are replaced by zeros with selects, not branches.
+__device__ __forceinline__ void zero_a_if(bool pad, Frags &f) {
+#pragma unroll
+    for (int i = 0; i < 4; i++) f.a[i] = pad ? make_uint4(0, 0, 0, 0) : f.a[i];
+}
+
+// MFMAs of one 16-wide K sub-step on 32-row blocks [I0, min(I1, NACT)) of
+// the wave (a partial tile's blocks past the expert's last row do no
+// matrix-core work).  NACT is a template parameter so every variant is
+// straight-line.
+template <int MODE, int NACT, int I0, int I1>
+__device__ __forceinline__ void mfma_blocks(const Frags &f, f32x16_t (&acc)[4][4]) {
     constexpr bool kF16 = MODE == kDown;
-    if (NACT == 0) return;
-    uint4 bw[4];
 #pragma unroll
-    for (int jn = 0; jn < 4; jn++) bw[jn] = kF16 ? bf16x8_to_f16x8(bf[jn]) : bf[jn];
+    for (int i = I0; i < (I1 < NACT ? I1 : NACT); i++) {
 #pragma unroll
-    for (int i = 0; i < NACT; i++) {
-#pragma unroll
-        for (int jn = 0; jn < 4; jn++) acc[i][jn] = mfma32<kF16>(af[i], bw[jn], acc[i][jn]);
+        for (int jn = 0; jn < 4; jn++) acc[i][jn] = mfma32<kF16>(f.a[i], f.b[jn], acc[i][jn]);
     }
 }
 
 // s_waitcnt with only the vector-memory counter: at most n loads in flight.
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+// s_waitcnt vmcnt(0) lgkmcnt(0)
+#define WAIT_VM_LGKM0() __builtin_amdgcn_s_waitcnt(0x0070)
 
 // Workgroup barrier without an implied wait on every outstanding memory
 // operation (the waits the pipeline needs are explicit); the memory clobber
 // keeps the compiler from moving LDS accesses across it.
 __device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "memory"); }
 
-template <int NACT, int SS>
-__device__ __forceinline__ void sched_substep() {
-    // interleave: the next fragments' LDS reads among the first MFMAs, the
-    // next step's global loads among the rest
-    constexpr int kM = 4 * NACT;  // MFMAs in this sub-step
-    if (kM >= 8) {
+// One sub-step in two scheduling regions.  First half: the MFMAs of blocks
+// 0-1 with the LDS reads of the next fragments between them.  Second half:
+// the MFMAs of blocks 2-3 with the global loads (if any) and, for the down
+// GEMM, the fp16 widening of the fragments just read (by then the reads
+// have landed, so the widening does not wait on the LDS latency).
+template <int MODE, int NACT, int HALF, bool LOADS>
+__device__ __forceinline__ void sched_half() {
+    constexpr int kLo = NACT < 2 ? NACT : 2;
+    constexpr int kM = 4 * (HALF == 0 ? kLo : NACT - kLo);  // MFMAs in this half
+    if (kM >= 4) {
 #pragma unroll
         for (int q = 0; q < 8; q++) {
-            SCHED_MFMA(kM / 16 > 0 ? kM / 16 : 1);
-            if (SS < 3) SCHED_DSR(1);
-        }
-#pragma unroll
-        for (int q = 0; q < 8; q++) {
-            SCHED_MFMA(kM / 16 > 0 ? kM / 16 : 1);
-            if (SS < 2) SCHED_VMEM(1);
+            if (q < kM) SCHED_MFMA(1);
+            if (HALF == 0) SCHED_DSR(1);
+            if (HALF == 1 && LOADS) SCHED_VMEM(1);
+            if (HALF == 1 && MODE == kDown) SCHED_VALU(6);
         }
     }
 }
 
-// One K step (4 sub-steps of 16) on stage `cur` while the next step's tile
-// streams into `nxt`.  Entry: sub-step 0's fragments are in (af0, bf0).
-// Sub-step s reads the fragments of s+1 and (s = 0, 1) issues the A / B
-// loads of the next step.  Exit: all of this wave's loads landed, barrier,
-// then the next step's sub-step-0 fragments are read from `nxt`.  Fences
-// between sub-steps keep the compiler from chaining dependent MFMAs on one
-// accumulator.
-template <int MODE, int NACT, bool MAYBE_PAD>
-__device__ __forceinline__ void kstep(const GemmThread &g, const char *cur, char *nxt, uint32_t kb_next,
-                                      bool pad, uint4 (&af0)[4], uint4 (&bf0)[4], f32x16_t (&acc)[4][4]) {
-    uint4 af1[4], bf1[4];
-    if (MAYBE_PAD) {
-        // a padding step (past an odd step count) adds zero: its A fragments
-        // are replaced by zeros with selects, not branches
-#pragma unroll
-        for (int i = 0; i < 4; i++) af0[i] = pad ? make_uint4(0, 0, 0, 0) : af0[i];
+template <int MODE, int NACT, bool LOADS_HALF1, bool SKIPA>
+__device__ __forceinline__ void substep(const GemmThread &g, const char *rd_stage, int rd_ss, Frags &nextf,
+                                        const Frags &f, char *ld_stage, uint32_t kb, int ld_operand,
+                                        f32x16_t (&acc)[4][4]) {
+    load_frags<MODE>(g, rd_stage, rd_ss, nextf);
+    mfma_blocks<MODE, NACT, 0, 2>(f, acc);
+    sched_half<MODE, NACT, 0, false>();
+    __builtin_amdgcn_sched_barrier(0);
+    if (LOADS_HALF1) {
+        if (ld_operand == 0) issue_loads<0, SKIPA>(g, ld_stage, kb);
+        else issue_loads<1, SKIPA>(g, ld_stage, kb);
     }
+    widen_b<MODE>(nextf);
+    mfma_blocks<MODE, NACT, 2, 4>(f, acc);
+    sched_half<MODE, NACT, 1, LOADS_HALF1>();
     __builtin_amdgcn_sched_barrier(0);
-    load_frags<MODE>(g, cur, 1, af1, bf1);
-    if (MAYBE_PAD) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) af1[i] = pad ? make_uint4(0, 0, 0, 0) : af1[i];
-    }
-    issue_loads<0>(g, nxt, kb_next);
-    mfma_substep<MODE, NACT>(af0, bf0, acc);
-    sched_substep<NACT, 0>();
+}
+
+// One K step (4 sub-steps of 16) on stage `cur`.  Entry: sub-step 0's
+// fragments are in f0; the A tile of the next step is already streaming
+// into `nxt`.  Sub-step 0 starts the B tile of the next step.  After
+// sub-step 2 every wave waits for its loads and for its LDS reads and meets
+// the others at a barrier: the next stage is then complete and no wave
+// reads `cur` any more, so sub-step 3 (whose fragments are already in
+// registers) overlaps the first LDS reads of `nxt` and the A loads of the
+// step after next into `cur`.  Fences between the halves of the sub-steps
+// keep the compiler from chaining dependent MFMAs on one accumulator.
+template <int MODE, int NACT, bool MAYBE_PAD, bool SKIPA>
+__device__ __forceinline__ void kstep(const GemmThread &g, char *cur, char *nxt, uint32_t kb_next,
+                                      uint32_t kb_next2, bool pad, Frags &f0, f32x16_t (&acc)[4][4]) {
+    Frags f1;
+    if (MAYBE_PAD) zero_a_if(pad, f0);
     __builtin_amdgcn_sched_barrier(0);
-    load_frags<MODE>(g, cur, 2, af0, bf0);
-    if (MAYBE_PAD) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) af0[i] = pad ? make_uint4(0, 0, 0, 0) : af0[i];
-    }
-    issue_loads<1>(g, nxt, kb_next);
-    mfma_substep<MODE, NACT>(af1, bf1, acc);
-    sched_substep<NACT, 1>();
-    __builtin_amdgcn_sched_barrier(0);
-    load_frags<MODE>(g, cur, 3, af1, bf1);
-    if (MAYBE_PAD) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) af1[i] = pad ? make_uint4(0, 0, 0, 0) : af1[i];
-    }
-    mfma_substep<MODE, NACT>(af0, bf0, acc);
-    sched_substep<NACT, 2>();
-    __builtin_amdgcn_sched_barrier(0);
-    mfma_substep<MODE, NACT>(af1, bf1, acc);
-    sched_substep<NACT, 3>();
-    __builtin_amdgcn_sched_barrier(0);
-    WAIT_VMCNT(0);
+    substep<MODE, NACT, true, SKIPA>(g, cur, 1, f1, f0, nxt, kb_next, 1, acc);
+    if (MAYBE_PAD) zero_a_if(pad, f1);
+    substep<MODE, NACT, false, SKIPA>(g, cur, 2, f0, f1, nxt, 0, 0, acc);
+    if (MAYBE_PAD) zero_a_if(pad, f0);
+    substep<MODE, NACT, false, SKIPA>(g, cur, 3, f1, f0, nxt, 0, 0, acc);
+    WAIT_VM_LGKM0();
     block_sync();
-    load_frags<MODE>(g, nxt, 0, af0, bf0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (MAYBE_PAD) zero_a_if(pad, f1);
+    substep<MODE, NACT, true, SKIPA>(g, nxt, 0, f0, f1, cur, kb_next2, 0, acc);
 }
 
 // The K loop over pairs of steps: stage 0 computes while stage 1 fills,
@@ -318,19 +337,21 @@ __device__ __forceinline__ void kstep(const GemmThread &g, const char *cur, char
 // can see that reading one never waits on the loads into the other.  With an
 // odd step count (ODD) the last pair's second step is padding that adds
 // zero; loads past the last step re-read the last tile.
-template <int MODE, int NACT, bool ODD>
+template <int MODE, int NACT, bool ODD, bool SKIPA>
 __device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s1, int nk,
                                           f32x16_t (&acc)[4][4]) {
     auto kb = [nk](int k) -> uint32_t { return (uint32_t)min(k, nk - 1) * kRowBytes; };
-    issue_loads<0>(g, s0, kb(0));
-    issue_loads<1>(g, s0, kb(0));
+    issue_loads<0, SKIPA>(g, s0, kb(0));
+    issue_loads<1, SKIPA>(g, s0, kb(0));
     WAIT_VMCNT(0);
     block_sync();
-    uint4 af0[4], bf0[4];
-    load_frags<MODE>(g, s0, 0, af0, bf0);
+    Frags f0;
+    load_frags<MODE>(g, s0, 0, f0);
+    widen_b<MODE>(f0);
+    issue_loads<0, SKIPA>(g, s1, kb(1));
     for (int k = 0; k < nk; k += 2) {
-        kstep<MODE, NACT, false>(g, s0, s1, kb(k + 1), false, af0, bf0, acc);
-        kstep<MODE, NACT, ODD>(g, s1, s0, kb(k + 2), k + 1 >= nk, af0, bf0, acc);
+        kstep<MODE, NACT, false, SKIPA>(g, s0, s1, kb(k + 1), kb(k + 2), false, f0, acc);
+        kstep<MODE, NACT, ODD, SKIPA>(g, s1, s0, kb(k + 2), kb(k + 3), k + 1 >= nk, f0, acc);
     }
 }
 
@@ -397,7 +418,7 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
 
 // A whole tile for one (active blocks, odd step count) variant: the
 // accumulators live only inside this function, so the variants never merge.
-template <int MODE, int NACT, bool ODD>
+template <int MODE, int NACT, bool ODD, bool SKIPA>
 __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti, char *s0, char *s1,
                                          int nk, int n0, int N, int wm, int wn, int lane,
                                          size_t split_stride, void *out_v) {
@@ -408,9 +429,10 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
         for (int jn = 0; jn < 4; jn++)
 #pragma unroll
             for (int q = 0; q < 16; q++) acc[i][jn][q] = 0.0f;
-    main_loop<MODE, NACT, ODD>(g, s0, s1, nk, acc);
-    // every wave's fragment reads are done before the stage is reused
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    main_loop<MODE, NACT, ODD, SKIPA>(g, s0, s1, nk, acc);
+    // the last (discarded) loads and fragment reads have landed in every
+    // wave before the epilogue reuses the stage
+    WAIT_VM_LGKM0();
     block_sync();
     store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v, s0, g.wave);
 }
@@ -454,6 +476,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
 
     GemmThread g;
     g.wave = wave;
+    g.a_valid = ti.mend - ti.m0;
     // A offsets stay below 4 GiB: relative to the tile's first row, or into
     // x (whose size the host checks) when rows are gathered
     g.a_base = reinterpret_cast<const char *>(a_rows ? A : A + (size_t)ti.m0 * K);
@@ -489,19 +512,24 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
 
     const int nk = ks / kBK;
-#define MOE_TILE(n)                                                                                  \
-    do {                                                                                             \
-        if (nk & 1)                                                                                  \
-            run_tile<MODE, n, true>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v);  \
-        else                                                                                         \
-            run_tile<MODE, n, false>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v); \
+#define MOE_TILE(n, skip)                                                                                 \
+    do {                                                                                                  \
+        if (nk & 1)                                                                                       \
+            run_tile<MODE, n, true, skip>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v);  \
+        else                                                                                              \
+            run_tile<MODE, n, false, skip>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v); \
     } while (0)
-    switch (nact) {
-        case 4: MOE_TILE(4); break;
-        case 3: MOE_TILE(3); break;
-        case 2: MOE_TILE(2); break;
-        case 1: MOE_TILE(1); break;
-        default: MOE_TILE(0); break;
+    // a full tile loads every A row group: no per-load branch in its loop
+    if (g.a_valid >= kBM) {
+        MOE_TILE(4, false);
+    } else {
+        switch (nact) {
+            case 4: MOE_TILE(4, true); break;
+            case 3: MOE_TILE(3, true); break;
+            case 2: MOE_TILE(2, true); break;
+            case 1: MOE_TILE(1, true); break;
+            default: MOE_TILE(0, true); break;
+        }
     }
 #undef MOE_TILE
 }
