@@ -48,7 +48,11 @@ def test_workspace_sizes_cover_buffers():
     R = moe.max_rows(p)
     assert R == 8192
     ws = moe.workspace_bytes(p)
-    assert ws >= R * (4096 + 14336 + 4096) * 2
+    S = moe.ffn_splits(p)
+    # h [R][d_ff] (fp16) and y_perm [S][R][d] (fp32); x spans less than 4 GiB, so
+    # moe_forward reads the gate-up rows from x and needs no x_perm
+    assert ws >= R * 14336 * 2 + S * R * 4096 * 4 + moe.dispatch_workspace_bytes(p)
+    assert ws < R * 14336 * 2 + S * R * 4096 * 4 + R * 4096 * 2
     assert moe.dispatch_workspace_bytes(p) > 0
 
 
@@ -63,7 +67,9 @@ def test_invalid_sizes_rejected(bad):
     assert rc == moe.MOE_ERR_INVALID_ARG
 
 
-@pytest.mark.parametrize("bad", [dict(d=100), dict(d_ff=96), dict(dtype=7), dict(d=16384 + 64)])
+@pytest.mark.parametrize("bad", [dict(d=100), dict(d_ff=96), dict(dtype=7), dict(d=16384 + 64),
+                                 dict(d=16384, d_ff=131072, dtype=moe.MOE_BF16),  # one expert matrix of 4 GiB
+                                 dict(d=8192, d_ff=131072, dtype=moe.MOE_F32)])
 def test_unsupported_shapes_rejected(bad):
     p = P(**bad)
     r = moe.MoeRouting()

@@ -232,6 +232,11 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
     torch.cuda.synchronize()
     gl2 = logits2.cpu().numpy()
     assert np.array_equal(gl2.view(np.uint32), gl.view(np.uint32)), "forward logits differ from moe_route"
+    # moe_forward reads the gate-up rows from x through token_of_row instead of
+    # a materialised x_perm: same values in the same order, so the output is
+    # bit-identical to the stage-by-stage path
+    iv = torch.int16 if p.dtype == moe.MOE_BF16 else torch.int32
+    assert torch.equal(y2.view(iv), y.view(iv)), "moe_forward differs from the staged path"
     rc2 = r2.cpu()
     ref2 = routing_vs_oracle(p, rc2, gl2, L.load, p.lam)
     toks = np.arange(T, dtype=np.int32) if (full_rows or T <= 64) else sample_tokens(ref2, T, n_tok, rng)
