@@ -398,19 +398,31 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
                 *reinterpret_cast<uint4 *>(out_h + (size_t)m * N + cb + ((pc ^ (row & 7)) << 3)) = v;
         }
     } else {
+        // one 32 x 128 fp32 block per pass through the wave's 16 KiB of LDS
+        // (512-byte rows; the 16-byte chunks of rows 4..7 mod 8 XOR-swizzled by
+        // 8 so the two half-waves, four rows apart, write disjoint banks), then
+        // 16-byte stores: 32 lanes per 512-byte row segment
         float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
+        char *w = stage + wave * (32 * 512);
+        const int cb = n0 + wn * 128;  // first column of this wave's block (N is a multiple of 64)
 #pragma unroll
         for (int i = 0; i < NACT; i++) {
-            const int rbase = ti.m0 + wm * 128 + i * 32 + 4 * hi;
 #pragma unroll
-            for (int jn = 0; jn < 4; jn++) {
-                const int col = n0 + wn * 128 + jn * 32 + l5;
-                if (col >= N) continue;
+            for (int jn = 0; jn < 4; jn++)
 #pragma unroll
                 for (int q = 0; q < 16; q++) {
-                    const int m = rbase + 8 * (q >> 2) + (q & 3);
-                    if (m < ti.mend) out_y[(size_t)m * N + col] = acc[i][jn][q];
+                    const int row = 8 * (q >> 2) + 4 * hi + (q & 3);
+                    const int col = jn * 32 + l5;
+                    const int chunk = (col >> 2) ^ (((row >> 2) & 1) << 3);
+                    *reinterpret_cast<float *>(w + row * 512 + chunk * 16 + (col & 3) * 4) = acc[i][jn][q];
                 }
+#pragma unroll
+            for (int rd = 0; rd < 16; rd++) {
+                const int row = rd * 2 + (lane >> 5), pc = lane & 31;
+                const uint4 v = lds_read16(w + row * 512 + pc * 16);
+                const int m = ti.m0 + wm * 128 + i * 32 + row;
+                const int col = cb + ((pc ^ (((row >> 2) & 1) << 3)) << 2);
+                if (m < ti.mend && col < N) *reinterpret_cast<uint4 *>(out_y + (size_t)m * N + col) = v;
             }
         }
     }
