@@ -546,6 +546,199 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
 #undef MOE_TILE
 }
 
+// ------------------------------------------------------------- skinny ----
+// Small groups (every expert at most 32 rows, e.g. a decode batch): the GEMM
+// is a weight stream, so the tile is one 32-row block by 128 weight rows
+// (gate-up: 64 columns of h, i.e. 64 rows of W1 and the same 64 rows of W3;
+// down: 128 output columns), and six LDS stages keep five K steps (80 KiB of
+// weights) in flight per CU.  MFMA 16x16x32 (bf16, or fp16 for the down GEMM
+// with W2 widened after the LDS read); 4 waves, each with both 16-row halves
+// of the tile and 32 of its weight rows (gate-up: 16 of W1 and the same 16
+// of W3).  The down projection is not split (one d_ff slice).
+constexpr int kSkThreads = 256;
+constexpr int kSkBM = 32;                       // rows per tile
+constexpr int kSkBN = 64;                       // h columns per gate-up tile (128 weight rows)
+constexpr int kSkBNd = 128;                     // output columns per down tile
+constexpr int kSkA = kSkBM * kRowBytes;         // A part of a stage (4 KiB)
+constexpr int kSkStage = kSkA + 2 * kSkBN * kRowBytes;  // + B part, 128 weight rows (16 KiB)
+constexpr int kSkStages = 6;
+
+template <bool F16>
+__device__ __forceinline__ f32x4_t mfma16(uint4 a, uint4 b, f32x4_t c) {
+    if constexpr (F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+struct SkThread {
+    const char *a_base;  // the tile's first row (or x when rows are gathered)
+    const char *b_base[2];
+    uint32_t a_off;      // this lane's A load row (wave w loads rows 8w .. 8w+7)
+    uint32_t b_off[4];   // this lane's B load rows (gate-up: 4 groups of 8, down: 2)
+    int wave;
+};
+
+// B rows per tile: 128 (gate-up: W1 rows n0.., then the same rows of W3;
+// down: W2 rows n0..); loads per wave per stage: 1 A + 4 B.
+template <int MODE>
+__device__ __forceinline__ constexpr int sk_lb() { return 4; }
+
+template <int MODE>
+__device__ __forceinline__ void sk_issue(const SkThread &g, char *stage, uint32_t kb) {
+    g2lds16(g.a_base + g.a_off + kb, stage + g.wave * 1024);
+#pragma unroll
+    for (int j = 0; j < sk_lb<MODE>(); j++) {
+        const int grp = g.wave * sk_lb<MODE>() + j;  // 8-row group of the B part
+        const int src = MODE == kGateUp ? grp >> 3 : 0;  // gate-up: groups 8.. are W3
+        g2lds16(g.b_base[src] + g.b_off[j] + kb, stage + kSkA + grp * 1024);
+    }
+}
+
+// Fragment of tile row `row` (16-row block base + lane % 16), logical chunk
+// c = 4 * sub-step + lane / 16, through the stage's XOR swizzle.
+__device__ __forceinline__ uint4 sk_frag(const char *part, int row, int c) {
+    return lds_read16(part + row * kRowBytes + ((c ^ swz(row)) << 4));
+}
+
+template <int MODE, int NB>
+__device__ __forceinline__ void sk_compute(const char *stage, int wave, int lane, f32x4_t (&acc)[2][2]) {
+    constexpr bool kF16 = MODE == kDown;
+    const int r16 = lane & 15, kq = lane >> 4;
+#pragma unroll
+    for (int ss = 0; ss < 2; ss++) {
+        const int c = 4 * ss + kq;
+        uint4 a[2], b[2];
+#pragma unroll
+        for (int ib = 0; ib < NB; ib++) a[ib] = sk_frag(stage, ib * 16 + r16, c);
+        // gate-up: W1 rows 16w.. and the same W3 rows (64 further); down:
+        // W2 rows 32w.. and 32w+16..
+        b[0] = sk_frag(stage + kSkA, (MODE == kGateUp ? 16 : 32) * wave + r16, c);
+        b[1] = sk_frag(stage + kSkA, (MODE == kGateUp ? kSkBN + 16 * wave : 32 * wave + 16) + r16, c);
+        if (kF16) {
+            b[0] = bf16x8_to_f16x8(b[0]);
+            b[1] = bf16x8_to_f16x8(b[1]);
+        }
+#pragma unroll
+        for (int ib = 0; ib < NB; ib++) {
+            acc[ib][0] = mfma16<kF16>(a[ib], b[0], acc[ib][0]);
+            acc[ib][1] = mfma16<kF16>(a[ib], b[1], acc[ib][1]);
+        }
+    }
+}
+
+#define SK_STEP(I, cur, nxt)                                                             \
+    do {                                                                                 \
+        if (k0 + (I) >= nk) goto done;                                                   \
+        WAIT_VMCNT((1 + sk_lb<MODE>()) * (kSkStages - 2));                               \
+        block_sync();                                                                    \
+        sk_issue<MODE>(g, nxt, kb(k0 + (I) + kSkStages - 1));                            \
+        sk_compute<MODE, NB>(cur, g.wave, lane, acc);                                    \
+    } while (0)
+
+// The K loop: stage k lives in buffer k % 6 (six distinct LDS objects, the
+// loop unrolled by six so every access names a fixed one); when step k is
+// computed, steps k+1 .. k+4 are in flight and step k+5 is issued into the
+// buffer step k-1 used (free: every wave passed the barrier after it).
+// Loads past the last step re-read the last K slice.
+template <int MODE, int NB>
+__device__ __forceinline__ void sk_main(const SkThread &g, int nk, int lane, char *b0, char *b1, char *b2,
+                                        char *b3, char *b4, char *b5, f32x4_t (&acc)[2][2]) {
+    auto kb = [nk](int k) -> uint32_t { return (uint32_t)min(k, nk - 1) * kRowBytes; };
+    sk_issue<MODE>(g, b0, kb(0));
+    sk_issue<MODE>(g, b1, kb(1));
+    sk_issue<MODE>(g, b2, kb(2));
+    sk_issue<MODE>(g, b3, kb(3));
+    sk_issue<MODE>(g, b4, kb(4));
+    for (int k0 = 0;; k0 += kSkStages) {
+        SK_STEP(0, b0, b5);
+        SK_STEP(1, b1, b0);
+        SK_STEP(2, b2, b1);
+        SK_STEP(3, b3, b2);
+        SK_STEP(4, b4, b3);
+        SK_STEP(5, b5, b4);
+    }
+done:
+    WAIT_VMCNT(0);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
+    const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
+    int splits, size_t split_stride, void *__restrict__ out_v) {
+    __shared__ __attribute__((aligned(1024))) char sb0[kSkStage];
+    __shared__ __attribute__((aligned(1024))) char sb1[kSkStage];
+    __shared__ __attribute__((aligned(1024))) char sb2[kSkStage];
+    __shared__ __attribute__((aligned(1024))) char sb3[kSkStage];
+    __shared__ __attribute__((aligned(1024))) char sb4[kSkStage];
+    __shared__ __attribute__((aligned(1024))) char sb5[kSkStage];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    TileInfo ti;
+    if (!find_tile(offsets, E, ntiles_n, kSkBM, splits, blockIdx.x, ti)) return;
+    const int n0 = ti.nt * (MODE == kGateUp ? kSkBN : kSkBNd);
+    const size_t wexp = (size_t)ti.e * N * K;
+    const int ks = K / splits;
+    const int k_first = ti.split * ks;
+
+    SkThread g;
+    g.wave = wave;
+    g.a_base = reinterpret_cast<const char *>(a_rows ? A : A + (size_t)ti.m0 * K);
+    {
+        const int row = wave * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        const int gm = min(ti.m0 + row, ti.mend - 1);
+        const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
+        g.a_off = ((uint32_t)ar * K + k_first + c * 8) * 2;
+    }
+    g.b_base[0] = reinterpret_cast<const char *>(B0 + wexp);
+    g.b_base[1] = reinterpret_cast<const char *>((MODE == kGateUp ? B1 : B0) + wexp);
+#pragma unroll
+    for (int j = 0; j < sk_lb<MODE>(); j++) {
+        const int grp = wave * sk_lb<MODE>() + j;
+        const int row = grp * 8 + (lane >> 3);  // row of the B part
+        const int c = (lane & 7) ^ swz(row);
+        const int gn = min(n0 + (MODE == kGateUp ? (row & (kSkBN - 1)) : row), N - 1);
+        g.b_off[j] = ((uint32_t)gn * K + k_first + c * 8) * 2;
+    }
+    const int nk = ks / kBK;
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++) acc[ib][jb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int nb = ti.mend - ti.m0 > 16 ? 2 : 1;  // active 16-row blocks (uniform)
+    if (nb == 2)
+        sk_main<MODE, 2>(g, nk, lane, sb0, sb1, sb2, sb3, sb4, sb5, acc);
+    else
+        sk_main<MODE, 1>(g, nk, lane, sb0, sb1, sb2, sb3, sb4, sb5, acc);
+
+    // epilogue: the lane holds column lane % 16, rows 4 * (lane / 16) + q
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int m = ti.m0 + ib * 16 + 4 * (lane >> 4) + q;
+            if (m >= ti.mend) continue;
+            if (MODE == kGateUp) {
+                const int col = n0 + wave * 16 + (lane & 15);
+                if (col < N)
+                    static_cast<uint16_t *>(out_v)[(size_t)m * N + col] =
+                        f32_to_f16_sat(silu_mul(acc[ib][0][q], acc[ib][1][q]));
+            } else {
+#pragma unroll
+                for (int jb = 0; jb < 2; jb++) {
+                    const int col = n0 + wave * 32 + jb * 16 + (lane & 15);
+                    if (col < N) (static_cast<float *>(out_v) + ti.split * split_stride)[(size_t)m * N + col] = acc[ib][jb][q];
+                }
+            }
+        }
+}
+#undef SK_STEP
+
 // ---------------------------------------------------------------- fp32 ----
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
@@ -609,6 +802,10 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict_
 
 int ffn_splits(const moe_params &p, int64_t max_rows) {
     if (p.dtype != MOE_BF16 || max_rows <= 0) return 1;
+    // small groups run the weight-streaming kernel, whose down projection is
+    // one slice (a CU per 128 output columns of an expert already fills the
+    // chip, and longer tiles stream better)
+    if (capacity_rows(p) <= kSkBM) return 1;
     // down GEMM work items before splitting (upper bound); aim for at least
     // three per compute unit
     const int64_t tiles = (max_rows / kBM + p.E) * ceil_div(p.d, kBN);
@@ -618,11 +815,27 @@ int ffn_splits(const moe_params &p, int64_t max_rows) {
     return s;
 }
 
-hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *x_perm,
+hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
                              const void *w3, const void *w2, void *h, void *y_perm, hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
     const int E = p.E, d = p.d, dff = p.d_ff;
+    if (p.dtype == MOE_BF16 && cap <= kSkBM) {
+        // every expert holds at most 32 rows: the weight-streaming kernel
+        const int64_t mt = max_rows / kSkBM + E;  // bound on sum_e ceil(rows_e / 32)
+        const int nt_up = (int)ceil_div(dff, kSkBN);
+        const int nt_dn = (int)ceil_div(d, kSkBNd);
+        const int S = ffn_splits(p, max_rows);
+        const size_t split_stride = (size_t)max_rows * d;
+        hipLaunchKernelGGL(grouped_gemm_skinny<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
+                           static_cast<const uint16_t *>(x_perm), a_rows, static_cast<const uint16_t *>(w1),
+                           static_cast<const uint16_t *>(w3), offsets, E, dff, d, nt_up, 1, (size_t)0, h);
+        hipLaunchKernelGGL(grouped_gemm_skinny<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kSkThreads), 0, st,
+                           static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
+                           static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2), offsets, E, d,
+                           dff, nt_dn, S, split_stride, y_perm);
+        return hipGetLastError();
+    }
     if (p.dtype == MOE_BF16) {
         const int64_t mt = max_rows / kBM + E;  // bound on sum_e ceil(rows_e / kBM)
         const int nt_up = (int)ceil_div(dff, kBN / 2);

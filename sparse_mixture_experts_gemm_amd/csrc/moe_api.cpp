@@ -27,14 +27,7 @@ int check_params(const moe_params *p) {
     return MOE_OK;
 }
 
-int64_t capacity_of(const moe_params &p) {
-    if (p.capacity_factor <= 0.0f) return p.T;
-    const double c = ceil((double)p.T * (double)p.k / (double)p.E * (double)p.capacity_factor);
-    int64_t C = (int64_t)c;
-    if (C > p.T) C = p.T;
-    if (C < 0) C = 0;
-    return C;
-}
+int64_t capacity_of(const moe_params &p) { return capacity_rows(p); }
 
 int64_t max_rows_of(const moe_params &p) {
     const int64_t C = capacity_of(p);
@@ -157,7 +150,7 @@ int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offse
     if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(h) ||
         !aligned16(y_perm))
         return MOE_ERR_UNSUPPORTED;
-    return hip_status(launch_expert_ffn(*p, R, x_perm, nullptr, offsets, w1, w3, w2, h, y_perm,
+    return hip_status(launch_expert_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w1, w3, w2, h, y_perm,
                                         static_cast<hipStream_t>(stream)));
 }
 
@@ -193,9 +186,9 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
     e = launch_dispatch(*p, C, x, *r, f.x_perm, carve_dispatch(f.dispatch, p->T, p->E, p->k), st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (f.x_perm)
-        e = launch_expert_ffn(*p, R, f.x_perm, nullptr, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
+        e = launch_expert_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
     else
-        e = launch_expert_ffn(*p, R, x, r->token_of_row, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
+        e = launch_expert_ffn(*p, R, C, x, r->token_of_row, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, f.y_perm, r->row, r->gate, y, st);
     return hip_status(e);

@@ -1,6 +1,8 @@
 // Internal interface between the C ABI (moe_api.cpp) and the HIP kernels.
 #pragma once
 
+#include <math.h>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -49,13 +51,25 @@ hipError_t launch_route(const moe_params &p, const void *x, const void *wr, cons
 hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
                            void *x_perm, const DispatchScratch &ws, hipStream_t st);
 
+// Capacity C = min(T, ceil(T*k/E * capacity_factor)) evaluated in double;
+// capacity_factor <= 0 means uncapped (C = T).
+inline int64_t capacity_rows(const moe_params &p) {
+    if (p.capacity_factor <= 0.0f) return p.T;
+    const double c = ceil((double)p.T * (double)p.k / (double)p.E * (double)p.capacity_factor);
+    int64_t C = (int64_t)c;
+    if (C > p.T) C = p.T;
+    if (C < 0) C = 0;
+    return C;
+}
+
 // Number of d_ff slices the down projection is split into (y_perm holds one
 // fp32 partial per slice; the combine adds them).  1 for fp32 layers.
 int ffn_splits(const moe_params &p, int64_t max_rows);
 
 // a_rows == nullptr: A is x_perm.  Otherwise A is the unpermuted x and packed
 // row m is x row a_rows[m] (token_of_row); x must span less than 4 GiB.
-hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, const void *x_perm,
+// cap bounds the rows of any one expert (the capacity C).
+hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
                              const void *w3, const void *w2, void *h, void *y_perm, hipStream_t st);
 
