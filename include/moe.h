@@ -97,7 +97,8 @@ typedef struct moe_params {
  * offsets, demand, kept, totals and aux_loss are always required.
  */
 typedef struct moe_routing {
-    int32_t *cand;       /* [T][K1] experts by (score desc, index asc); -1 past E   */
+    int32_t *cand;       /* [T][K1] experts by (score desc, index asc), NaN scores
+                          *         after every number; -1 past E               */
     float *cand_score;   /* [T][K1] penalised fp32 scores; -inf past E              */
     int32_t *eid;        /* [T][k]  final expert of slot j, -1 when dropped         */
     int32_t *pos;        /* [T][k]  position in that expert's queue, -1 if dropped  */
@@ -151,7 +152,8 @@ int moe_route(const moe_params *p, const void *x, const void *w_router, const fl
  * ..., then one fallback round in token order); a slot is kept while its
  * expert holds fewer than C rows ("GPT-4稀疏激活真相" §2.3; "MoE架构揭秘"
  * §3.3).  Gates are the softmax of the kept slots' scores renormalised over
- * the kept slots.  Deterministic: no atomics.
+ * the kept slots.  Deterministic: no atomics.  A candidate outside [0, E)
+ * (a caller's own r->cand) names no expert: such a slot is never kept.
  *   workspace: at least moe_dispatch_workspace_bytes(p) bytes, 256-B aligned.
  */
 int moe_dispatch(const moe_params *p, const void *x, moe_routing *r, void *x_perm,

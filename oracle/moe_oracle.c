@@ -108,10 +108,21 @@ void oracle_scores(int T, int E, const float *raw, const float *load, float lamb
 /*
  * Ranked candidates (P2 §3.1: softmax, then the top-2 indices).  Softmax is
  * monotone, so ranking by the fp32 score s is the same order without the
- * rounding of exp; ties go to the lower expert index.  K columns are produced
+ * rounding of exp; ties go to the lower expert index, and NaN scores come
+ * after every number (lower index first among them).  K columns are produced
  * (k chosen experts plus the fallback candidate); ranks >= E are -1 with score
  * -inf.
  */
+/* a ranks above b: the larger score; a NaN ranks below every number.  The
+ * pages never meet a NaN score; this reading keeps the order total, so every
+ * rank below E names an expert. */
+static int ranks_above(float a, float b)
+{
+    if (isnan(b))
+        return !isnan(a);
+    return a > b;
+}
+
 void oracle_topk(int T, int E, int K, const float *s, int32_t *cand, float *cand_score)
 {
     unsigned char *taken = (unsigned char *)malloc((size_t)E);
@@ -123,7 +134,7 @@ void oracle_topk(int T, int E, int K, const float *s, int32_t *cand, float *cand
             for (int e = 0; e < E; e++) {
                 if (taken[e])
                     continue;
-                if (best < 0 || st[e] > st[best])
+                if (best < 0 || ranks_above(st[e], st[best]))
                     best = e;
             }
             cand[(size_t)t * K + r] = best;

@@ -50,21 +50,24 @@ __device__ __forceinline__ int wave_rank_count(int key, int *wave_cnt) {
     return rank;
 }
 
+// A candidate id outside [0, E) (moe_route writes -1 for ranks past E; a
+// caller's own routing may hold anything) is read as "no expert", so it is
+// never used as an index.
+__device__ __forceinline__ int valid_expert(int c, int E) { return (unsigned)c < (unsigned)E ? c : -1; }
+
 __device__ __forceinline__ void zero_lds(int *a, int n) {
     for (int i = threadIdx.x; i < n; i += kThreads) a[i] = 0;
 }
 
-__global__ __launch_bounds__(kThreads) void dispatch_hist(const int32_t *__restrict__ cand, int T,
-                                                          int E, int k, int32_t *__restrict__ hist) {
-    __shared__ int wcnt[kWaves][kMaxExperts];
+__device__ __forceinline__ void hist_body(int b, const int32_t *__restrict__ cand, int T, int E, int k,
+                                          int32_t *__restrict__ hist, int (&wcnt)[kWaves][kMaxExperts]) {
     const int K1 = k + 1;
-    const int b = blockIdx.x;
     const int t = b * kThreads + threadIdx.x;
     const int wave = threadIdx.x >> 6;
     for (int r = 0; r < k; r++) {
         zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
         __syncthreads();
-        const int key = t < T ? cand[(size_t)t * K1 + r] : -1;
+        const int key = t < T ? valid_expert(cand[(size_t)t * K1 + r], E) : -1;
         wave_rank_count(key, wcnt[wave]);
         __syncthreads();
         for (int e = threadIdx.x; e < E; e += kThreads) {
@@ -76,15 +79,27 @@ __global__ __launch_bounds__(kThreads) void dispatch_hist(const int32_t *__restr
     }
 }
 
-__global__ __launch_bounds__(kThreads) void dispatch_primary(
-    const int32_t *__restrict__ cand, int T, int E, int k, int C, int nb, int use_fallback,
-    const int32_t *__restrict__ hist, int32_t *__restrict__ fill_prim, int32_t *__restrict__ eid,
-    int32_t *__restrict__ pos, uint8_t *__restrict__ flag, int32_t *__restrict__ fb_hist) {
-    __shared__ int base[kMaxTopK][kMaxExperts];
-    __shared__ int tot[kMaxTopK][kMaxExperts];
+__global__ __launch_bounds__(kThreads) void dispatch_hist(const int32_t *__restrict__ cand, int T,
+                                                          int E, int k, int32_t *__restrict__ hist) {
     __shared__ int wcnt[kWaves][kMaxExperts];
+    hist_body(blockIdx.x, cand, T, E, k, hist, wcnt);
+}
+
+struct PrimaryLds {
+    int base[kMaxTopK][kMaxExperts];
+    int tot[kMaxTopK][kMaxExperts];
+    int wcnt[kWaves][kMaxExperts];
+};
+
+__device__ __forceinline__ void primary_body(int b, const int32_t *__restrict__ cand, int T, int E, int k, int C,
+                                             int nb, int use_fallback, const int32_t *__restrict__ hist,
+                                             int32_t *__restrict__ fill_prim, int32_t *__restrict__ eid,
+                                             int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
+                                             int32_t *__restrict__ fb_hist, PrimaryLds &sm) {
+    auto &base = sm.base;
+    auto &tot = sm.tot;
+    auto &wcnt = sm.wcnt;
     const int K1 = k + 1;
-    const int b = blockIdx.x;
     const int t = b * kThreads + threadIdx.x;
     const int wave = threadIdx.x >> 6;
 
@@ -115,12 +130,15 @@ __global__ __launch_bounds__(kThreads) void dispatch_primary(
     for (int r = 0; r < k; r++) {
         zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
         __syncthreads();
-        const int key = t < T ? cand[(size_t)t * K1 + r] : -1;
+        const int key = t < T ? valid_expert(cand[(size_t)t * K1 + r], E) : -1;
         const int rank = wave_rank_count(key, wcnt[wave]);
         __syncthreads();
         if (t < T) {
-            int p = base[r][key] + rank;
-            for (int w = 0; w < wave; w++) p += wcnt[w][key];
+            int p = C;  // a candidate that names no expert is never kept
+            if (key >= 0) {
+                p = base[r][key] + rank;
+                for (int w = 0; w < wave; w++) p += wcnt[w][key];
+            }
             const size_t j = (size_t)t * k + r;
             if (p < C) {
                 eid[j] = key;
@@ -139,7 +157,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_primary(
     // fallback requests of this block, per expert
     zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
     __syncthreads();
-    const int fkey = (t < T && use_fallback && first_over >= 0) ? cand[(size_t)t * K1 + k] : -1;
+    const int fkey = (t < T && use_fallback && first_over >= 0) ? valid_expert(cand[(size_t)t * K1 + k], E) : -1;
     wave_rank_count(fkey, wcnt[wave]);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) {
@@ -149,21 +167,36 @@ __global__ __launch_bounds__(kThreads) void dispatch_primary(
     }
 }
 
-__global__ __launch_bounds__(kThreads) void dispatch_finalize(
-    const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k,
+__global__ __launch_bounds__(kThreads) void dispatch_primary(
+    const int32_t *__restrict__ cand, int T, int E, int k, int C, int nb, int use_fallback,
+    const int32_t *__restrict__ hist, int32_t *__restrict__ fill_prim, int32_t *__restrict__ eid,
+    int32_t *__restrict__ pos, uint8_t *__restrict__ flag, int32_t *__restrict__ fb_hist) {
+    __shared__ PrimaryLds sm;
+    primary_body(blockIdx.x, cand, T, E, k, C, nb, use_fallback, hist, fill_prim, eid, pos, flag, fb_hist, sm);
+}
+
+struct FinalizeLds {
+    int fbase[kMaxExperts];
+    int kcnt[kMaxExperts];
+    int offs[kMaxExperts + 1];
+    int scan_tmp[2][kMaxExperts];
+    int wcnt[kWaves][kMaxExperts];
+};
+
+__device__ __forceinline__ void finalize_body(
+    int b, const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k,
     int C, int nb, int use_fallback, float aux_coef, int cap_rows, const int32_t *__restrict__ hist,
     const int32_t *__restrict__ fill_prim, const int32_t *__restrict__ fb_hist,
     int32_t *__restrict__ eid, int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
     int32_t *__restrict__ row, float *__restrict__ gate, int32_t *__restrict__ offsets,
     int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand, int32_t *__restrict__ kept,
-    int32_t *__restrict__ totals, float *__restrict__ aux_loss) {
-    __shared__ int fbase[kMaxExperts];
-    __shared__ int kcnt[kMaxExperts];
-    __shared__ int offs[kMaxExperts + 1];
-    __shared__ int scan_tmp[2][kMaxExperts];
-    __shared__ int wcnt[kWaves][kMaxExperts];
+    int32_t *__restrict__ totals, float *__restrict__ aux_loss, FinalizeLds &sm) {
+    auto &fbase = sm.fbase;
+    auto &kcnt = sm.kcnt;
+    auto &offs = sm.offs;
+    auto &scan_tmp = sm.scan_tmp;
+    auto &wcnt = sm.wcnt;
     const int K1 = k + 1;
-    const int b = blockIdx.x;
     const int t = b * kThreads + threadIdx.x;
     const int wave = threadIdx.x >> 6;
 
@@ -202,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_finalize(
                 first_over = r;
                 break;
             }
-    const int fkey = (t < T && use_fallback && first_over >= 0) ? cand[(size_t)t * K1 + k] : -1;
+    const int fkey = (t < T && use_fallback && first_over >= 0) ? valid_expert(cand[(size_t)t * K1 + k], E) : -1;
     const int rank = wave_rank_count(fkey, wcnt[wave]);
     __syncthreads();
     if (fkey >= 0) {
@@ -277,6 +310,45 @@ __global__ __launch_bounds__(kThreads) void dispatch_finalize(
     }
 }
 
+__global__ __launch_bounds__(kThreads) void dispatch_finalize(
+    const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k,
+    int C, int nb, int use_fallback, float aux_coef, int cap_rows, const int32_t *__restrict__ hist,
+    const int32_t *__restrict__ fill_prim, const int32_t *__restrict__ fb_hist,
+    int32_t *__restrict__ eid, int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
+    int32_t *__restrict__ row, float *__restrict__ gate, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand, int32_t *__restrict__ kept,
+    int32_t *__restrict__ totals, float *__restrict__ aux_loss) {
+    __shared__ FinalizeLds sm;
+    finalize_body(blockIdx.x, cand, cand_score, T, E, k, C, nb, use_fallback, aux_coef, cap_rows, hist, fill_prim,
+                  fb_hist, eid, pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm);
+}
+
+// T <= kThreads: one block runs the three phases back to back (the
+// histograms, fills and fallback counts pass through global memory exactly
+// as between the three kernels; the block's barriers order them), saving two
+// launches and their latency.
+__global__ __launch_bounds__(kThreads) void dispatch_single(
+    const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k, int C,
+    int use_fallback, float aux_coef, int cap_rows, int32_t *__restrict__ hist, int32_t *__restrict__ fill_prim,
+    int32_t *__restrict__ fb_hist, int32_t *__restrict__ eid, int32_t *__restrict__ pos,
+    uint8_t *__restrict__ flag, int32_t *__restrict__ row, float *__restrict__ gate,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand,
+    int32_t *__restrict__ kept, int32_t *__restrict__ totals, float *__restrict__ aux_loss) {
+    __shared__ union {
+        int wcnt[kWaves][kMaxExperts];
+        PrimaryLds p;
+        FinalizeLds f;
+    } sm;
+    hist_body(0, cand, T, E, k, hist, sm.wcnt);
+    __threadfence_block();
+    __syncthreads();
+    primary_body(0, cand, T, E, k, C, 1, use_fallback, hist, fill_prim, eid, pos, flag, fb_hist, sm.p);
+    __threadfence_block();
+    __syncthreads();
+    finalize_body(0, cand, cand_score, T, E, k, C, 1, use_fallback, aux_coef, cap_rows, hist, fill_prim, fb_hist,
+                  eid, pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm.f);
+}
+
 // x_perm[row[t][j]] = x[t] for every kept slot: the token row is read once.
 __global__ __launch_bounds__(256) void dispatch_gather(const uint4 *__restrict__ x,
                                                        const int32_t *__restrict__ row, int k,
@@ -300,13 +372,20 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
     const int use_fb = (p.reroute && k < E) ? 1 : 0;
     int64_t cap_rows = (int64_t)T * k;
     if ((int64_t)E * C < cap_rows) cap_rows = (int64_t)E * C;
-    hipLaunchKernelGGL(dispatch_hist, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, ws.hist);
-    hipLaunchKernelGGL(dispatch_primary, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, (int)C,
-                       nb, use_fb, ws.hist, ws.fill_prim, r.eid, r.pos, r.flag, ws.fb_hist);
-    hipLaunchKernelGGL(dispatch_finalize, dim3(nb), dim3(kThreads), 0, st, r.cand, r.cand_score, T,
-                       E, k, (int)C, nb, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim,
-                       ws.fb_hist, r.eid, r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row,
-                       r.demand, r.kept, r.totals, r.aux_loss);
+    if (nb == 1) {
+        hipLaunchKernelGGL(dispatch_single, dim3(1), dim3(kThreads), 0, st, r.cand, r.cand_score, T, E, k,
+                           (int)C, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim, ws.fb_hist, r.eid,
+                           r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row, r.demand, r.kept, r.totals,
+                           r.aux_loss);
+    } else {
+        hipLaunchKernelGGL(dispatch_hist, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, ws.hist);
+        hipLaunchKernelGGL(dispatch_primary, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, (int)C,
+                           nb, use_fb, ws.hist, ws.fill_prim, r.eid, r.pos, r.flag, ws.fb_hist);
+        hipLaunchKernelGGL(dispatch_finalize, dim3(nb), dim3(kThreads), 0, st, r.cand, r.cand_score, T,
+                           E, k, (int)C, nb, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim,
+                           ws.fb_hist, r.eid, r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row,
+                           r.demand, r.kept, r.totals, r.aux_loss);
+    }
     if (T > 0 && x_perm) {
         const int esz = p.dtype == MOE_BF16 ? 2 : 4;
         const int chunks = p.d * esz / 16;

@@ -13,8 +13,9 @@
 // v_dot2_f32_bf16.  Each lane ends with 32 partial sums (TPW tokens x EA
 // experts); a butterfly reduce-scatter over the 64 lanes (DPP inside rows of
 // 16, ds_bpermute across rows) leaves one full sum per lane pair, so the
-// cross-lane cost is one shuffle per logit.  Ranking is k+1 wave argmax
-// reductions on (score, index), also DPP/bpermute butterflies.
+// cross-lane cost is one shuffle per logit.  Ranking is k+1 wave max
+// reductions of a 64-bit key (order-preserving score bits with NaN lowest,
+// then the inverted expert index), also DPP/bpermute butterflies.
 //
 // The penalty is an explicit fmaf and the file is built without fast-math, so
 // the fp32 ranking is reproducible from the fp32 logits bit for bit.
@@ -70,19 +71,26 @@ __device__ __forceinline__ void rs_step(float (&v)[32], int lane) {
     }
 }
 
-// better(a, b): larger score, ties to the lower index
-__device__ __forceinline__ bool better(float sa, int ia, float sb, int ib) {
-    return sa > sb || (sa == sb && ia < ib);
+// Ranking key of (score, expert): a larger key ranks higher.  The high word
+// is an order-preserving map of the fp32 score onto uint32, with -0 and +0
+// merged (equal scores) and every NaN placed below -inf, so the order is total
+// and every rank below E names an expert even when a row's logits are NaN.
+// The low word is the inverted expert index, so among equal scores the lower
+// index has the larger key.  Key 0 means "no expert".
+__device__ __forceinline__ uint64_t rank_key(float s, int e) {
+    const uint32_t u = s == 0.0f ? 0u : __float_as_uint(s);
+    uint32_t k = (u >> 31) ? ~u : (u | 0x80000000u);
+    k = s != s ? 0u : k;
+    return ((uint64_t)k << 32) | (uint32_t)~e;
 }
 
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
 template <int STEP>
-__device__ __forceinline__ void argmax_step(float &s, int &i) {
-    float so = exch_f32<STEP>(s);
-    int io = exch_i32<STEP>(i);
-    if (better(so, io, s, i)) {
-        s = so;
-        i = io;
-    }
+__device__ __forceinline__ uint64_t max_step(uint64_t v) {
+    const uint32_t lo = (uint32_t)exch_i32<STEP>((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)exch_i32<STEP>((int)(uint32_t)(v >> 32));
+    return max_u64(v, ((uint64_t)hi << 32) | lo);
 }
 
 typedef __attribute__((address_space(3))) char lds_char_t;
@@ -148,8 +156,9 @@ __device__ __forceinline__ void route_chunk(const uint4 *w_lds, const uint4 (&xr
 
 // NX: 16-byte chunks of one x row per lane; TPW: tokens per wave; NB: W
 // buffers (1 when all E gate vectors fit one chunk, else 2: the next chunk
-// streams in while the current one is used).
-template <typename TIn, int NX, int TPW, int NB>
+// streams in while the current one is used); PL: experts per lane in the
+// ranking (1 for E <= 64, else 4).
+template <typename TIn, int NX, int TPW, int NB, int PL>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wr, const float *__restrict__ bias,
     const float *__restrict__ load, float neg_lambda, int T, int d, int E, int K1, int EC,
@@ -205,49 +214,49 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         __syncthreads();
     }
 
-    // ranking: lanes hold experts e = lane + 64 * i
-    constexpr int kMaxPerLane = kMaxExperts / 64;
+    // ranking: lanes hold experts e = lane + 64 * i; each round is one wave
+    // max of the ranking keys, and the winner's key is cleared
     for (int j = 0; j < TPW; j++) {
         const int t = t0 + j;
         if (t >= T) break;  // wave-uniform
-        float sc[kMaxPerLane];
-        uint32_t avail = 0;
+        float sc[PL];
+        uint64_t key[PL];
 #pragma unroll
-        for (int i = 0; i < kMaxPerLane; i++) {
+        for (int i = 0; i < PL; i++) {
             const int e = lane + 64 * i;
-            sc[i] = -INFINITY;
+            sc[i] = 0.0f;
+            key[i] = 0;
             if (e < E) {
                 const float raw = lg[j * E + e];
                 logits[(size_t)t * E + e] = raw;
                 sc[i] = load ? __builtin_fmaf(neg_lambda, load[e], raw) : raw;
-                avail |= 1u << i;
+                key[i] = rank_key(sc[i], e);
             }
         }
         for (int r = 0; r < K1; r++) {
-            float bs = -INFINITY;
-            int bi = 0x7fffffff;
+            uint64_t m = key[0];
 #pragma unroll
-            for (int i = 0; i < kMaxPerLane; i++) {
-                const int e = lane + 64 * i;
-                if ((avail >> i) & 1) {
-                    if (better(sc[i], e, bs, bi)) {
-                        bs = sc[i];
-                        bi = e;
-                    }
-                }
-            }
-            argmax_step<1>(bs, bi);
-            argmax_step<2>(bs, bi);
-            argmax_step<4>(bs, bi);
-            argmax_step<8>(bs, bi);
-            argmax_step<16>(bs, bi);
-            argmax_step<32>(bs, bi);
-            const bool none = bi == 0x7fffffff;
+            for (int i = 1; i < PL; i++) m = max_u64(m, key[i]);
+            m = max_step<1>(m);
+            m = max_step<2>(m);
+            m = max_step<4>(m);
+            m = max_step<8>(m);
+            m = max_step<16>(m);
+            m = max_step<32>(m);
+            const bool none = m == 0;
+            const int e = __builtin_amdgcn_readfirstlane((int)~(uint32_t)m);
+            // the winner's own score (its sign of zero and NaN bits), from its lane
+            float s = sc[0];
+#pragma unroll
+            for (int i = 1; i < PL; i++) s = (e >> 6) == i ? sc[i] : s;
+            s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), e & 63));
             if (lane == 0) {
-                cand[(size_t)t * K1 + r] = none ? -1 : bi;
-                cand_score[(size_t)t * K1 + r] = none ? -INFINITY : bs;
+                cand[(size_t)t * K1 + r] = none ? -1 : e;
+                cand_score[(size_t)t * K1 + r] = none ? -INFINITY : s;
             }
-            if (!none && (bi & 63) == lane) avail &= ~(1u << (bi >> 6));
+#pragma unroll
+            for (int i = 0; i < PL; i++)
+                if (!none && (e & 63) == lane && (e >> 6) == i) key[i] = 0;
         }
     }
 }
@@ -262,14 +271,18 @@ hipError_t launch_t(const moe_params &p, const void *x, const void *wr, const fl
     if (ec > p.E) ec = p.E;
     const int tokens_per_block = kRouteWaves * TPW;
     const int grid = (int)ceil_div(p.T, tokens_per_block);
-    if (ec >= p.E)
-        hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, 1>), dim3(grid), dim3(kRouteThreads), 0, st,
-                           static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load,
-                           -p.lambda, p.T, p.d, p.E, p.k + 1, ec, logits, cand, cand_score);
-    else
-        hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, 2>), dim3(grid), dim3(kRouteThreads), 0, st,
-                           static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load,
-                           -p.lambda, p.T, p.d, p.E, p.k + 1, ec, logits, cand, cand_score);
+#define MOE_ROUTE_LAUNCH(NB, PL)                                                                           \
+    hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, NB, PL>), dim3(grid), dim3(kRouteThreads), 0, st,          \
+                       static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load, -p.lambda, p.T, \
+                       p.d, p.E, p.k + 1, ec, logits, cand, cand_score)
+    if (ec >= p.E) {
+        if (p.E <= 64) MOE_ROUTE_LAUNCH(1, 1);
+        else MOE_ROUTE_LAUNCH(1, kMaxExperts / 64);
+    } else {
+        if (p.E <= 64) MOE_ROUTE_LAUNCH(2, 1);
+        else MOE_ROUTE_LAUNCH(2, kMaxExperts / 64);
+    }
+#undef MOE_ROUTE_LAUNCH
     return hipGetLastError();
 }
 

@@ -93,7 +93,7 @@ def load_for(cfg, L, T):
     return (dp["kept"].astype(np.float32) / np.float32(T * cfg.k)).astype(np.float32)
 
 
-def routing_vs_oracle(p, rc, logits_np, load_np, lam):
+def routing_vs_oracle(p, rc, logits_np, load_np, lam, nan_gates=False):
     """Oracle routing from the GPU's logits; every array bit-exact."""
     cand, cs = oracle.route(logits_np, p.k, load_np, lam)
     C = oracle.capacity(p.T, p.k, p.E, p.capacity_factor)
@@ -108,7 +108,7 @@ def routing_vs_oracle(p, rc, logits_np, load_np, lam):
         else:
             assert np.array_equal(a, b), f"routing array {n} differs: first at {np.argwhere(a != b)[:3]}"
     g = rc["gate"].numpy().astype(np.float64)
-    assert np.allclose(g, ref["gate64"], rtol=1e-6, atol=1e-7), "gates"
+    assert np.allclose(g, ref["gate64"], rtol=1e-6, atol=1e-7, equal_nan=nan_gates), "gates"
     assert math.isclose(float(rc["aux_loss"][0]), float(ref["aux_loss"][0]), rel_tol=1e-6, abs_tol=1e-12)
     return ref
 
@@ -323,6 +323,37 @@ def test_identical_tokens_tied_logits():
     L.c["w_router"] = np_of(L.g["w_router"].cpu())
     out = run_stages(L, params(cfg), full_rows=True, rms_kept_rows=True)
     assert out["ref"]["totals"][1] > 0  # capacity exhausted
+
+
+def test_nan_rows_route_and_dispatch():
+    """A token row holding a NaN (or both infinities) makes its logits NaN.
+    NaN scores rank after every number, so the token still names k+1 experts
+    (the lowest indices) and its slots queue like any other; routing must
+    match the oracle bit for bit and the NaN gates stay on their tokens."""
+    cfg = small_cfg(T=600, E=8, cf=1.0)
+    L = Layer(cfg)
+    L.g["x"][5] = float("nan")
+    L.g["x"][17, 3] = float("nan")
+    L.g["x"][40] = float("inf")
+    L.g["x"][40, ::2] = -float("inf")
+    p = params(cfg)
+    say(f"[case] nan rows T={p.T} E={p.E} k={p.k}")
+    r = moe.Routing(p, DEV)
+    logits = torch.empty((p.T, p.E), dtype=torch.float32, device=DEV)
+    moe.route(p, L.g["x"], L.g["w_router"], L.g["bias"], None, logits, r)
+    R = moe.max_rows(p)
+    xp = torch.empty((max(R, 1), p.d), dtype=torch.bfloat16, device=DEV)
+    moe.dispatch(p, L.g["x"], r, xp, moe.alloc_workspace(p, DEV, dispatch_only=True))
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert np.isnan(lg[[5, 17, 40]]).all() and np.isfinite(np.delete(lg, [5, 17, 40], axis=0)).all()
+    rc = r.cpu()
+    routing_vs_oracle(p, rc, lg, None, 0.0, nan_gates=True)
+    for t in (5, 17, 40):
+        assert list(rc["cand"][t].numpy()) == [0, 1, 2]
+    g = rc["gate"].numpy()
+    assert np.isnan(g[[5, 17, 40]][rc["flag"].numpy()[[5, 17, 40]] != 2]).all()
+    assert np.isfinite(np.delete(g, [5, 17, 40], axis=0)).all()
 
 
 def test_deterministic_rerun():

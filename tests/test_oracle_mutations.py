@@ -17,7 +17,8 @@ import oracle
 from tests import test_oracle_pins as pins
 
 MUTATIONS = {
-    "ties_to_higher_index": ("st[e] > st[best]", "st[e] >= st[best]"),
+    "ties_to_higher_index": ("    return a > b;\n}", "    return a >= b;\n}"),
+    "nan_ranked_by_position": ("        return !isnan(a);", "        return 0;"),
     "penalty_two_roundings": ("fmaf(-lambda, load[e], raw[i])", "raw[i] - lambda * load[e]"),
     "capacity_floor": ("ceil((double)T", "floor((double)T"),
     "queue_limit_off_by_one": ("if (fill[e] < C) {", "if (fill[e] <= C) {"),

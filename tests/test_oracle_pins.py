@@ -162,6 +162,18 @@ def check_topk(o):
     assert list(o.topk(s, 2)[0][0]) == [0, 1]
     s = np.array([[0.0, -0.0, -1.0]], np.float32)
     assert list(o.topk(s, 2)[0][0]) == [0, 1]
+    # NaN scores come after every number (-inf included), NaNs by index; a row
+    # of NaNs still names E experts
+    s = r.integers(0, 3, (60, 6)).astype(np.float32)
+    s[r.random(s.shape) < 0.3] = np.nan
+    s[::7, 5] = -np.inf
+    s[5] = np.nan
+    cand, cs = o.topk(s, 7)
+    for t in range(s.shape[0]):
+        order = sorted(range(6), key=lambda e: (bool(np.isnan(s[t, e])),
+                                                0.0 if np.isnan(s[t, e]) else -float(s[t, e]), e))
+        assert list(cand[t]) == order + [-1], t
+        assert np.array_equal(cs[t, :6], s[t, order], equal_nan=True)
 
 
 def test_topk_pins(oracle_mod):
