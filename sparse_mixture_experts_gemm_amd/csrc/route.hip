@@ -19,6 +19,8 @@
 //
 // The penalty is an explicit fmaf and the file is built without fast-math, so
 // the fp32 ranking is reproducible from the fp32 logits bit for bit.
+#include <type_traits>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -60,8 +62,8 @@ struct ChunkDot<float> {
 
 // One butterfly reduce-scatter step: the lane keeps half of its V values
 // (the upper half when its STEP bit is set) and adds the partner's copy.
-template <int STEP, int V>
-__device__ __forceinline__ void rs_step(float (&v)[32], int lane) {
+template <int STEP, int V, int N>
+__device__ __forceinline__ void rs_step(float (&v)[N], int lane) {
     const bool upper = (lane & STEP) != 0;
 #pragma unroll
     for (int i = 0; i < V / 2; i++) {
@@ -108,21 +110,40 @@ __device__ __forceinline__ void stage_w(const char *src, int bytes, char *dst, i
     }
 }
 
+// Butterfly reduce-scatter of V partial sums per lane over the 64 lanes: the
+// value set halves at steps 32, 16, ... until one value is left, then plain
+// butterfly adds finish the sum.  Lane l ends with the full sum of value
+// (l >> (6 - log2 V)) & (V - 1).
+template <int V>
+__device__ __forceinline__ float reduce_scatter(float (&v)[V], int lane) {
+    static_assert(V == 8 || V == 16 || V == 32, "8, 16 or 32 values per lane");
+    rs_step<32, V>(v, lane);
+    rs_step<16, V / 2>(v, lane);
+    rs_step<8, V / 4>(v, lane);
+    if constexpr (V >= 16) rs_step<4, V / 8>(v, lane);
+    else v[0] += exch_f32<4>(v[0]);
+    if constexpr (V >= 32) rs_step<2, 2>(v, lane);
+    else v[0] += exch_f32<2>(v[0]);
+    return v[0] + exch_f32<1>(v[0]);
+}
+
 // Logits of experts [e0, e0 + ec) for this wave's TPW tokens from the gate
 // vectors staged at w_lds, written to lg[token][expert].  Per group of EA
 // experts: all NX gate-vector chunks of one expert are read from LDS first,
 // then used for the TPW tokens held in registers (no lane-dependent
 // branches: x chunks past the row end are zero, so the gate-vector read is
-// simply clamped).  EA x TPW partial sums per lane then go through one
-// butterfly reduce-scatter.
-template <typename TIn, int NX, int TPW>
+// simply clamped).  The TPW x EA partial sums per lane then go through one
+// butterfly reduce-scatter (EA is the smallest power of two that holds the
+// experts, up to 32 / TPW, so no shuffle carries an empty slot).
+template <typename TIn, int NX, int TPW, int EA>
 __device__ __forceinline__ void route_chunk(const uint4 *w_lds, const uint4 (&xr)[TPW][NX], int nchunk, int e0,
                                             int ec, const float *__restrict__ bias, float *lg, int E, int lane) {
-    constexpr int EA = 32 / TPW;  // experts accumulated together
+    constexpr int V = TPW * EA;
+    constexpr int kShift = V == 32 ? 1 : V == 16 ? 2 : 3;
     for (int ea = 0; ea < ec; ea += EA) {
-        float v[32];
+        float v[V];
 #pragma unroll
-        for (int i = 0; i < 32; i++) v[i] = 0.0f;
+        for (int i = 0; i < V; i++) v[i] = 0.0f;
 #pragma unroll
         for (int q = 0; q < EA; q++) {
             if (ea + q < ec) {  // wave-uniform
@@ -136,18 +157,12 @@ __device__ __forceinline__ void route_chunk(const uint4 *w_lds, const uint4 (&xr
                     for (int j = 0; j < TPW; j++) v[j * EA + q] = ChunkDot<TIn>::dot(xr[j][c], w[c], v[j * EA + q]);
             }
         }
-        // reduce-scatter: lane keeps value index (lane >> 1) & 31
-        rs_step<32, 32>(v, lane);
-        rs_step<16, 16>(v, lane);
-        rs_step<8, 8>(v, lane);
-        rs_step<4, 4>(v, lane);
-        rs_step<2, 2>(v, lane);
-        v[0] += exch_f32<1>(v[0]);
-        const int idx = (lane >> 1) & 31;
+        const float sum = reduce_scatter<V>(v, lane);
+        const int idx = (lane >> kShift) & (V - 1);
         const int j = idx / EA, q = idx % EA;
         const int e = e0 + ea + q;
-        if ((lane & 1) == 0 && ea + q < ec) {
-            float r = v[0];
+        if ((lane & ((1 << kShift) - 1)) == 0 && ea + q < ec) {
+            float r = sum;
             if (bias) r = r + bias[e];
             lg[j * E + e] = r;
         }
@@ -156,9 +171,10 @@ __device__ __forceinline__ void route_chunk(const uint4 *w_lds, const uint4 (&xr
 
 // NX: 16-byte chunks of one x row per lane; TPW: tokens per wave; NB: W
 // buffers (1 when all E gate vectors fit one chunk, else 2: the next chunk
-// streams in while the current one is used); PL: experts per lane in the
-// ranking (1 for E <= 64, else 4).
-template <typename TIn, int NX, int TPW, int NB, int PL>
+// streams in while the current one is used); EA: experts per reduce-scatter
+// group; EMAX: bound on E that sizes the logit buffer (a small one leaves
+// room for two blocks per CU) and the experts per lane of the ranking.
+template <typename TIn, int NX, int TPW, int NB, int EA, int EMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wr, const float *__restrict__ bias,
     const float *__restrict__ load, float neg_lambda, int T, int d, int E, int K1, int EC,
@@ -168,7 +184,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     // buffer never alias the reads of the other
     __shared__ __attribute__((aligned(1024))) char w_buf0[kRouteLdsW];
     __shared__ __attribute__((aligned(1024))) char w_buf1[NB == 2 ? kRouteLdsW : 1024];
-    __shared__ float lg_all[kRouteWaves * TPW * kMaxExperts];
+    __shared__ float lg_all[kRouteWaves * TPW * EMAX];
+    constexpr int PL = (EMAX + 63) / 64;  // experts per lane in the ranking
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int nchunk = d / kVec;
@@ -200,7 +217,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     for (int e0 = 0; e0 < E; e0 += 2 * EC) {
         if (NB == 2 && e0 + EC < E)
             stage_w(wsrc + (size_t)(e0 + EC) * row_bytes, min(EC, E - e0 - EC) * row_bytes, w_buf1, wave, lane);
-        route_chunk<TIn, NX, TPW>(reinterpret_cast<const uint4 *>(w_buf0), xr, nchunk, e0, min(EC, E - e0), bias,
+        route_chunk<TIn, NX, TPW, EA>(reinterpret_cast<const uint4 *>(w_buf0), xr, nchunk, e0, min(EC, E - e0), bias,
                                   lg, E, lane);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
@@ -208,7 +225,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
         if (e0 + 2 * EC < E)
             stage_w(wsrc + (size_t)(e0 + 2 * EC) * row_bytes, min(EC, E - e0 - 2 * EC) * row_bytes, w_buf0,
                     wave, lane);
-        route_chunk<TIn, NX, TPW>(reinterpret_cast<const uint4 *>(w_buf1), xr, nchunk, e0 + EC,
+        route_chunk<TIn, NX, TPW, EA>(reinterpret_cast<const uint4 *>(w_buf1), xr, nchunk, e0 + EC,
                                   min(EC, E - e0 - EC), bias, lg, E, lane);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
@@ -261,42 +278,59 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 }
 
-template <typename TIn, int NX, int TPW>
-hipError_t launch_t(const moe_params &p, const void *x, const void *wr, const float *bias,
-                    const float *load, float *logits, int32_t *cand, float *cand_score,
-                    hipStream_t st) {
+template <typename TIn, int NX, int TPW, int EA, int EMAX>
+hipError_t launch_k(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
+                    float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
     const int row_bytes = p.d * (int)sizeof(TIn);
     int ec = kRouteLdsW / row_bytes;  // experts staged per LDS chunk
     if (ec < 1) ec = 1;
     if (ec > p.E) ec = p.E;
     const int tokens_per_block = kRouteWaves * TPW;
     const int grid = (int)ceil_div(p.T, tokens_per_block);
-#define MOE_ROUTE_LAUNCH(NB, PL)                                                                           \
-    hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, NB, PL>), dim3(grid), dim3(kRouteThreads), 0, st,          \
+#define MOE_ROUTE_LAUNCH(NB)                                                                                  \
+    hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, NB, EA, EMAX>), dim3(grid), dim3(kRouteThreads), 0, st,    \
                        static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load, -p.lambda, p.T, \
                        p.d, p.E, p.k + 1, ec, logits, cand, cand_score)
-    if (ec >= p.E) {
-        if (p.E <= 64) MOE_ROUTE_LAUNCH(1, 1);
-        else MOE_ROUTE_LAUNCH(1, kMaxExperts / 64);
-    } else {
-        if (p.E <= 64) MOE_ROUTE_LAUNCH(2, 1);
-        else MOE_ROUTE_LAUNCH(2, kMaxExperts / 64);
-    }
+    if (ec >= p.E) MOE_ROUTE_LAUNCH(1);
+    else MOE_ROUTE_LAUNCH(2);
 #undef MOE_ROUTE_LAUNCH
     return hipGetLastError();
 }
 
-// Tokens per wave: up to 4 (more tokens share each gate-vector read from
-// LDS), fewer when that would leave compute units without a block.
+// SPEC: instantiate the expert-count classes (E <= 8, 16, 32 with one token
+// per wave; E <= 64); otherwise one variant that serves every E <= 256.
+template <typename TIn, int NX, int TPW, bool SPEC>
+hipError_t launch_t(const moe_params &p, const void *x, const void *wr, const float *bias,
+                    const float *load, float *logits, int32_t *cand, float *cand_score,
+                    hipStream_t st) {
+    constexpr int kEA = 32 / TPW;
+    if constexpr (SPEC) {
+        if constexpr (TPW == 1) {  // the only tokens-per-wave count used for E <= 32
+            if (p.E <= 8) return launch_k<TIn, NX, 1, 8, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
+            if (p.E <= 16) return launch_k<TIn, NX, 1, 16, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
+            if (p.E <= 32) return launch_k<TIn, NX, 1, 32, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
+        }
+        if (p.E <= 64) return launch_k<TIn, NX, TPW, kEA, 64>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    }
+    return launch_k<TIn, NX, TPW, kEA, kMaxExperts>(p, x, wr, bias, load, logits, cand, cand_score, st);
+}
+
+// Tokens per wave.  Up to 32 experts, one: the logit buffer is then small,
+// two blocks share a CU, and one block's loads overlap the other's dot
+// products (measured faster at every T).  With more experts the dot loop is
+// bound by the VALU and the LDS reads of the gate vectors, which TPW tokens
+// share: up to 4, fewer when that would leave compute units without a block.
 template <typename TIn, int NX>
 hipError_t launch_nx(const moe_params &p, const void *x, const void *wr, const float *bias,
                      const float *load, float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
     constexpr int kCUs = 256;
+    constexpr bool kSpec = std::is_same<TIn, uint16_t>::value && (NX == 4 || NX == 8);
+    if (kSpec && p.E <= 32) return launch_t<TIn, NX, 1, kSpec>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (p.T >= kCUs * kRouteWaves * 4)
-        return launch_t<TIn, NX, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
+        return launch_t<TIn, NX, 4, kSpec>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (p.T >= kCUs * kRouteWaves * 2)
-        return launch_t<TIn, NX, 2>(p, x, wr, bias, load, logits, cand, cand_score, st);
-    return launch_t<TIn, NX, 1>(p, x, wr, bias, load, logits, cand, cand_score, st);
+        return launch_t<TIn, NX, 2, kSpec>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    return launch_t<TIn, NX, 1, kSpec>(p, x, wr, bias, load, logits, cand, cand_score, st);
 }
 
 template <typename TIn>
@@ -309,8 +343,8 @@ hipError_t launch_dtype(const moe_params &p, const void *x, const void *wr, cons
     if (nx <= 2) return launch_nx<TIn, 2>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (nx <= 4) return launch_nx<TIn, 4>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (nx <= 8) return launch_nx<TIn, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
-    if (nx <= 16) return launch_t<TIn, 16, 2>(p, x, wr, bias, load, logits, cand, cand_score, st);
-    if (nx <= 32) return launch_t<TIn, 32, 1>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 16) return launch_t<TIn, 16, 2, false>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (nx <= 32) return launch_t<TIn, 32, 1, false>(p, x, wr, bias, load, logits, cand, cand_score, st);
     return hipErrorInvalidValue;
 }
 
