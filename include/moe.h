@@ -130,7 +130,7 @@ size_t moe_dispatch_workspace_bytes(const moe_params *p);
 
 /* Host-side, pure: bytes of workspace moe_forward needs: the dispatch scratch
  * plus h [R][d_ff] and y_perm [S][R][d] (fp32), and x_perm [R][d] only when
- * x spans 4 GiB or more (see moe_forward), each 256-byte aligned. */
+ * x spans 2 GiB or more (see moe_forward), each 256-byte aligned. */
 size_t moe_workspace_bytes(const moe_params *p);
 
 /*
@@ -188,7 +188,7 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
 /*
  * Stages 1-4 on one stream with no host synchronisation.  workspace holds at
  * least moe_workspace_bytes(p) bytes (256-B aligned) and is carved into the
- * dispatch scratch, h and y_perm.  When x spans less than 4 GiB the dispatch
+ * dispatch scratch, h and y_perm.  When x spans less than 2 GiB the dispatch
  * copy of the token rows is not made: the gate-up GEMM reads its rows from x
  * through token_of_row (same values, one pass over x fewer); otherwise
  * x_perm is materialised in the workspace as moe_dispatch does.

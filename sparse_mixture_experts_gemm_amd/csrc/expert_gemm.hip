@@ -46,7 +46,6 @@ constexpr int kBN = 256;   // weight rows per tile (gate-up: 128 of W1 + 128 of 
 constexpr int kBK = 64;    // K per pipeline step: 128-byte row segments (one cache line)
 constexpr int kRowBytes = kBK * 2;           // one tile row in LDS
 constexpr int kTileBytes = kBM * kRowBytes;  // one operand tile (32 KiB)
-constexpr int kStageBytes = 2 * kTileBytes;  // A tile + B tile (64 KiB)
 constexpr int kLoadsPerOperand = kTileBytes / 1024 / 4;  // 1 KiB wave loads per wave (8)
 constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (8)
 
@@ -170,6 +169,27 @@ __device__ __forceinline__ void g2lds16(const char *src, char *dst) {
     __builtin_amdgcn_global_load_lds((gbl_char_t *)src, (lds_char_t *)dst, 16, 0, 0);
 }
 
+// The same through a buffer resource: the base and extent are in scalar
+// registers, the lane's byte offset in `voff` and a wave-uniform offset (the
+// K step) in `soff`, so no 64-bit address is kept per load; reads at or past
+// the extent return zeros.
+// (base and extent are made wave-uniform explicitly, so the descriptor is
+// built in scalar registers and every load takes it from there)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((hi << 32) | lo), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+// A byte offset past every A extent (each is below 2 GiB): such a load
+// fetches nothing.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
+__device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char_t *)dst, 16, voff, soff, 0, 0);
+}
+
 __device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
 
 // Scheduling hints: interleave one group of `n` instructions of a class.
@@ -181,8 +201,8 @@ __device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret
 // Per-thread state of the MFMA grouped GEMM.
 struct GemmThread {
     uint32_t a_off[kLoadsPerOperand], b_off[kLoadsPerOperand];  // byte offsets from the bases (16 B per lane)
-    const char *b_src[kLoadsPerOperand];  // uniform base per B row group (W1 / W3 / W2)
-    const char *a_base;                   // A rows: the tile's first row, or the unpermuted x
+    __amdgpu_buffer_rsrc_t a_rsrc;  // A rows: the tile's first row, or the unpermuted x
+    __amdgpu_buffer_rsrc_t b_rsrc;  // this wave's weight rows: W1 / W3 (gate-up) or W2
     int a_valid;                          // valid rows of the tile (uniform)
     uint32_t fa[2][4], fb[2][4];  // LDS byte offsets of fragments [block parity][sub-step]
     int wave;
@@ -194,22 +214,19 @@ __device__ __forceinline__ int b_imm(int jn) {
     return jn * 32 * kRowBytes;
 }
 
-// Issue this wave's global -> LDS loads of one operand of one K step.
-template <int HALF, bool SKIPA>
-__device__ __forceinline__ void issue_loads(const GemmThread &g, char *stage, uint32_t kb) {
+// Issue this wave's global -> LDS loads of one operand (HALF 0: A, 1: B) of
+// one K step into that operand's LDS buffer `buf`.  Rows past the tile's last
+// valid row in a partly valid 8-row group re-read that row (clamped offsets);
+// groups wholly past it carry an offset beyond the buffer extent, so their
+// loads fetch nothing and write zeros (those LDS rows feed only discarded
+// outputs), with no branch in the loop.
+template <int HALF>
+__device__ __forceinline__ void issue_loads(const GemmThread &g, char *buf, uint32_t kb) {
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; j++) {
         const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group
-        // rows past the tile's last valid row in a partly valid group re-read
-        // that row (clamped addresses)
-        // A row groups wholly past the tile's valid rows are not loaded: their
-        // LDS rows feed only discarded outputs (a block with no valid row
-        // does no MFMA at all)
-        if (HALF == 0) {
-            if (!SKIPA || grp * kRowsPerLoad < g.a_valid) g2lds16(g.a_base + g.a_off[j] + kb, stage + grp * 1024);
-        }
-        else
-            g2lds16(g.b_src[j] + g.b_off[j] + kb, stage + kTileBytes + grp * 1024);
+        if (HALF == 0) buf2lds16(g.a_rsrc, g.a_off[j], kb, buf + grp * 1024);
+        else buf2lds16(g.b_rsrc, g.b_off[j], kb, buf + grp * 1024);
     }
 }
 
@@ -220,11 +237,12 @@ struct Frags {
 };
 
 template <int MODE>
-__device__ __forceinline__ void load_frags(const GemmThread &g, const char *stage, int ss, Frags &f) {
+__device__ __forceinline__ void load_frags(const GemmThread &g, const char *abuf, const char *bbuf, int ss,
+                                           Frags &f) {
 #pragma unroll
-    for (int i = 0; i < 4; i++) f.a[i] = lds_read16(stage + g.fa[i & 1][ss] + i * 32 * kRowBytes);
+    for (int i = 0; i < 4; i++) f.a[i] = lds_read16(abuf + g.fa[i & 1][ss] + i * 32 * kRowBytes);
 #pragma unroll
-    for (int jn = 0; jn < 4; jn++) f.b[jn] = lds_read16(stage + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
+    for (int jn = 0; jn < 4; jn++) f.b[jn] = lds_read16(bbuf + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
 }
 
 // Down GEMM: W2 fragments (bf16) widened to fp16 for the fp16 MFMA.
@@ -259,6 +277,8 @@ __device__ __forceinline__ void mfma_blocks(const Frags &f, f32x16_t (&acc)[4][4
 
 // s_waitcnt with only the vector-memory counter: at most n loads in flight.
 #define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+// s_waitcnt vmcnt(n) lgkmcnt(0): at most n loads in flight, no LDS access
+#define WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4))
 // s_waitcnt vmcnt(0) lgkmcnt(0)
 #define WAIT_VM_LGKM0() __builtin_amdgcn_s_waitcnt(0x0070)
 
@@ -287,17 +307,17 @@ __device__ __forceinline__ void sched_half() {
     }
 }
 
-template <int MODE, int NACT, bool LOADS_HALF1, bool SKIPA>
-__device__ __forceinline__ void substep(const GemmThread &g, const char *rd_stage, int rd_ss, Frags &nextf,
-                                        const Frags &f, char *ld_stage, uint32_t kb, int ld_operand,
+template <int MODE, int NACT, bool LOADS_HALF1>
+__device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, const char *rd_b, int rd_ss,
+                                        Frags &nextf, const Frags &f, char *ld_buf, uint32_t kb, int ld_operand,
                                         f32x16_t (&acc)[4][4]) {
-    load_frags<MODE>(g, rd_stage, rd_ss, nextf);
+    load_frags<MODE>(g, rd_a, rd_b, rd_ss, nextf);
     mfma_blocks<MODE, NACT, 0, 2>(f, acc);
     sched_half<MODE, NACT, 0, false>();
     __builtin_amdgcn_sched_barrier(0);
     if (LOADS_HALF1) {
-        if (ld_operand == 0) issue_loads<0, SKIPA>(g, ld_stage, kb);
-        else issue_loads<1, SKIPA>(g, ld_stage, kb);
+        if (ld_operand == 0) issue_loads<0>(g, ld_buf, kb);
+        else issue_loads<1>(g, ld_buf, kb);
     }
     widen_b<MODE>(nextf);
     mfma_blocks<MODE, NACT, 2, 4>(f, acc);
@@ -305,54 +325,116 @@ __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_stag
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// One K step (4 sub-steps of 16) on stage `cur`.  Entry: sub-step 0's
-// fragments are in f0; the A tile of the next step is already streaming
-// into `nxt`.  Sub-step 0 starts the B tile of the next step.  After
-// sub-step 2 every wave waits for its loads and for its LDS reads and meets
-// the others at a barrier: the next stage is then complete and no wave
-// reads `cur` any more, so sub-step 3 (whose fragments are already in
-// registers) overlaps the first LDS reads of `nxt` and the A loads of the
-// step after next into `cur`.  Fences between the halves of the sub-steps
-// keep the compiler from chaining dependent MFMAs on one accumulator.
-template <int MODE, int NACT, bool MAYBE_PAD, bool SKIPA>
-__device__ __forceinline__ void kstep(const GemmThread &g, char *cur, char *nxt, uint32_t kb_next,
-                                      uint32_t kb_next2, bool pad, Frags &f0, f32x16_t (&acc)[4][4]) {
+// B buffers of each GEMM: three for the gate-up GEMM, whose weight tiles
+// arrive from HBM (the third buffer lets a tile start almost two K steps
+// before its use); two for the down GEMM, which has no registers to spare
+// for the addresses of a third.
+template <int MODE>
+__device__ __forceinline__ constexpr int b_buffers() { return MODE == kGateUp ? 3 : 2; }
+
+// One K step (4 sub-steps of 16) on the A buffer `ca` and B buffer `cb`.
+// LDS holds two A buffers and NB B buffers (distinct objects, so the compiler
+// can see that reading one never waits on loads into another).  Entry:
+// sub-step 0's fragments are in f0; the A tile of the next step (into `na`)
+// is already streaming, and with NB = 3 its B tile (into `nb`) too.
+// Sub-step 0 starts a B tile: with NB = 3 that of the step after next, into
+// the free third buffer `fb`; with NB = 2 that of the next step, into `nb`.
+// After sub-step 2 every wave waits for its loads (but the eight just
+// issued, with NB = 3) and its LDS reads and meets the others at a barrier:
+// the next step's tiles are then complete and no wave reads `ca` or `cb` any
+// more, so sub-step 3 (whose fragments are already in registers) overlaps
+// the first LDS reads of the next step and the A loads of the step after
+// next into `ca`.  Fences between the halves of the sub-steps keep the
+// compiler from chaining dependent MFMAs on one accumulator.
+// MAYBE_PAD: the step may be the padding step past an odd step count
+// (two B buffers only), which must add zero.
+template <int MODE, int NACT, bool MAYBE_PAD>
+__device__ __forceinline__ void kstep(const GemmThread &g, char *ca, char *cb, char *na, char *nb, char *fb,
+                                      uint32_t kb1, uint32_t kb2, bool pad, Frags &f0, f32x16_t (&acc)[4][4]) {
+    constexpr bool kRing = b_buffers<MODE>() == 3;
     Frags f1;
     if (MAYBE_PAD) zero_a_if(pad, f0);
     __builtin_amdgcn_sched_barrier(0);
-    substep<MODE, NACT, true, SKIPA>(g, cur, 1, f1, f0, nxt, kb_next, 1, acc);
+    substep<MODE, NACT, true>(g, ca, cb, 1, f1, f0, kRing ? fb : nb, kRing ? kb2 : kb1, 1, acc);
     if (MAYBE_PAD) zero_a_if(pad, f1);
-    substep<MODE, NACT, false, SKIPA>(g, cur, 2, f0, f1, nxt, 0, 0, acc);
+    substep<MODE, NACT, false>(g, ca, cb, 2, f0, f1, nullptr, 0, 0, acc);
     if (MAYBE_PAD) zero_a_if(pad, f0);
-    substep<MODE, NACT, false, SKIPA>(g, cur, 3, f1, f0, nxt, 0, 0, acc);
-    WAIT_VM_LGKM0();
+    substep<MODE, NACT, false>(g, ca, cb, 3, f1, f0, nullptr, 0, 0, acc);
+    WAIT_VMCNT_LGKM0(kRing ? kLoadsPerOperand : 0);
     block_sync();
     __builtin_amdgcn_sched_barrier(0);
     if (MAYBE_PAD) zero_a_if(pad, f1);
-    substep<MODE, NACT, true, SKIPA>(g, nxt, 0, f0, f1, cur, kb_next2, 0, acc);
+    substep<MODE, NACT, true>(g, na, nb, 0, f0, f1, ca, kb2, 0, acc);
 }
 
-// The K loop over pairs of steps: stage 0 computes while stage 1 fills,
-// then the reverse.  The two stages are distinct LDS objects so the compiler
-// can see that reading one never waits on the loads into the other.  With an
-// odd step count (ODD) the last pair's second step is padding that adds
-// zero; loads past the last step re-read the last tile.
-template <int MODE, int NACT, bool ODD, bool SKIPA>
-__device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s1, int nk,
-                                          f32x16_t (&acc)[4][4]) {
+// Step I of a buffer rotation: A alternates over two buffers, B rotates over
+// NB.  The indices are constants, so every step names fixed buffers.
+template <int MODE, int NACT, int I, bool MAYBE_PAD = false>
+__device__ __forceinline__ void kstep_at(const GemmThread &g, char *a0, char *a1, char *b0, char *b1, char *b2,
+                                         uint32_t kb1, uint32_t kb2, bool pad, Frags &f0,
+                                         f32x16_t (&acc)[4][4]) {
+    constexpr int NB = b_buffers<MODE>();
+    char *const A[2] = {a0, a1};
+    char *const B[3] = {b0, b1, b2};
+    kstep<MODE, NACT, MAYBE_PAD>(g, A[I % 2], B[I % NB], A[(I + 1) % 2], B[(I + 1) % NB], B[(I + 2) % NB], kb1,
+                                 kb2, pad, f0, acc);
+}
+
+// The K loop, unrolled over one period of the buffer rotation.  Three B
+// buffers: 6 steps, then the remaining steps.  Two: pairs of steps, and with
+// an odd step count (ODD) the last pair's second step is padding that adds
+// zero (a separate last step would cost the down GEMM registers it does not
+// have).  Loads past the last step re-read the last tile.
+template <int MODE, int NACT, bool ODD>
+__device__ __forceinline__ void main_loop(const GemmThread &g, char *a0, char *a1, char *b0, char *b1, char *b2,
+                                          int nk, f32x16_t (&acc)[4][4]) {
+    constexpr int NB = b_buffers<MODE>();
     auto kb = [nk](int k) -> uint32_t { return (uint32_t)min(k, nk - 1) * kRowBytes; };
-    issue_loads<0, SKIPA>(g, s0, kb(0));
-    issue_loads<1, SKIPA>(g, s0, kb(0));
-    WAIT_VMCNT(0);
+    issue_loads<0>(g, a0, kb(0));
+    issue_loads<1>(g, b0, kb(0));
+    if (NB == 3) issue_loads<1>(g, b1, kb(1));
+    WAIT_VMCNT(NB == 3 ? kLoadsPerOperand : 0);
     block_sync();
     Frags f0;
-    load_frags<MODE>(g, s0, 0, f0);
+    load_frags<MODE>(g, a0, b0, 0, f0);
     widen_b<MODE>(f0);
-    issue_loads<0, SKIPA>(g, s1, kb(1));
-    for (int k = 0; k < nk; k += 2) {
-        kstep<MODE, NACT, false, SKIPA>(g, s0, s1, kb(k + 1), kb(k + 2), false, f0, acc);
-        kstep<MODE, NACT, ODD, SKIPA>(g, s1, s0, kb(k + 2), kb(k + 3), k + 1 >= nk, f0, acc);
+    issue_loads<0>(g, a1, kb(1));
+#define MOE_KSTEP(I, K) kstep_at<MODE, NACT, I>(g, a0, a1, b0, b1, b2, kb((K) + 1), kb((K) + 2), false, f0, acc)
+    if constexpr (NB == 3) {
+        const int nk6 = nk - nk % 6;
+        for (int k = 0; k < nk6; k += 6) {
+            MOE_KSTEP(0, k);
+            MOE_KSTEP(1, k + 1);
+            MOE_KSTEP(2, k + 2);
+            MOE_KSTEP(3, k + 3);
+            MOE_KSTEP(4, k + 4);
+            MOE_KSTEP(5, k + 5);
+        }
+        // the last nk % 6 steps, in the same rotation.  Nested, so that each
+        // step is reached from the previous one only: the compiler then still
+        // tells the LDS buffers apart when it places its waits (a join of
+        // paths with different loads in flight would make it wait for all).
+        const int r = nk - nk6;
+        if (r > 0) {
+            MOE_KSTEP(0, nk6);
+            if (r > 1) {
+                MOE_KSTEP(1, nk6 + 1);
+                if (r > 2) {
+                    MOE_KSTEP(2, nk6 + 2);
+                    if (r > 3) {
+                        MOE_KSTEP(3, nk6 + 3);
+                        if (r > 4) MOE_KSTEP(4, nk6 + 4);
+                    }
+                }
+            }
+        }
+    } else {
+        for (int k = 0; k < nk; k += 2) {
+            MOE_KSTEP(0, k);
+            kstep_at<MODE, NACT, 1, ODD>(g, a0, a1, b0, b1, b2, kb(k + 2), kb(k + 3), k + 1 >= nk, f0, acc);
+        }
     }
+#undef MOE_KSTEP
 }
 
 // Epilogue.  MFMA output layout: the lane holds column l5 of each 32x32
@@ -368,11 +450,10 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *s0, char *s
 template <int MODE, int NACT>
 __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, int wm, int wn, int lane,
                                            size_t split_stride, const f32x16_t (&acc)[4][4], void *out_v,
-                                           char *stage, int wave) {
+                                           char *w) {
     const int l5 = lane & 31, hi = lane >> 5;
     if (MODE == kGateUp) {
         uint16_t *out_h = static_cast<uint16_t *>(out_v);
-        char *w = stage + wave * (128 * kRowBytes);
 #pragma unroll
         for (int i = 0; i < NACT; i++)
 #pragma unroll
@@ -403,7 +484,6 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
         // 8 so the two half-waves, four rows apart, write disjoint banks), then
         // 16-byte stores: 32 lanes per 512-byte row segment
         float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
-        char *w = stage + wave * (32 * 512);
         const int cb = n0 + wn * 128;  // first column of this wave's block (N is a multiple of 64)
 #pragma unroll
         for (int i = 0; i < NACT; i++) {
@@ -428,11 +508,11 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
     }
 }
 
-// A whole tile for one (active blocks, odd step count) variant: the
-// accumulators live only inside this function, so the variants never merge.
-template <int MODE, int NACT, bool ODD, bool SKIPA>
-__device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti, char *s0, char *s1,
-                                         int nk, int n0, int N, int wm, int wn, int lane,
+// A whole tile for one active-block count: the accumulators live only
+// inside this function, so the variants never merge.
+template <int MODE, int NACT, bool ODD>
+__device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti, char *a0, char *a1, char *b0,
+                                         char *b1, char *b2, int nk, int n0, int N, int wm, int wn, int lane,
                                          size_t split_stride, void *out_v) {
     f32x16_t acc[4][4];
 #pragma unroll
@@ -441,18 +521,19 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
         for (int jn = 0; jn < 4; jn++)
 #pragma unroll
             for (int q = 0; q < 16; q++) acc[i][jn][q] = 0.0f;
-    main_loop<MODE, NACT, ODD, SKIPA>(g, s0, s1, nk, acc);
+    main_loop<MODE, NACT, ODD>(g, a0, a1, b0, b1, b2, nk, acc);
     // the last (discarded) loads and fragment reads have landed in every
-    // wave before the epilogue reuses the stage
+    // wave before the epilogue reuses the A buffers (16 KiB per wave)
     WAIT_VM_LGKM0();
     block_sync();
-    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v, s0, g.wave);
+    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v,
+                           (g.wave < 2 ? a0 : a1) + (g.wave & 1) * (kTileBytes / 2));
 }
 
 // MODE kGateUp: A = x_perm (bf16), B = W1/W3 (bf16), writes h (fp16).  With
 //               a_rows, A is the unpermuted x and row m of the expert range
 //               is x row a_rows[m] (the dispatch gather folded into the A
-//               loads; x must then span less than 4 GiB).
+//               loads; x must then span less than 2 GiB).
 // MODE kDown:   A = h (fp16), B = W2 (bf16, widened to fp16 after the LDS
 //               read), writes y_perm (fp32).  The d_ff reduction is split
 //               into `splits` slices (work items of their own, for enough
@@ -460,8 +541,9 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
 //               y_perm + s * split_stride and the combine adds the slices in
 //               order, so the result is deterministic.
 //
-// LDS: two stages of [A tile 256 x 64 | B tile 256 x 64], the eight 16-byte
-// chunks of each row XOR-swizzled by swz(row).  Global -> LDS with
+// LDS: two A buffers and three (gate-up) or two (down) B buffers of 256 rows
+// x 64 K (32 KiB each), the eight 16-byte chunks of each row XOR-swizzled by
+// swz(row).  Global -> LDS with
 // global_load_lds: wave w loads 8-row groups 8w .. 8w+7 of A and of B; lane
 // l takes row 8g + l/8 and the logical chunk that lands at physical position
 // l%8, so every wave load reads whole 128-byte lines.  Fragments: lane l
@@ -471,9 +553,12 @@ template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
-    int splits, size_t split_stride, void *__restrict__ out_v) {
-    __shared__ __attribute__((aligned(1024))) char lds_s0[kStageBytes];
-    __shared__ __attribute__((aligned(1024))) char lds_s1[kStageBytes];
+    int splits, size_t split_stride, uint32_t a_bytes, void *__restrict__ out_v) {
+    __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_b1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_b2[b_buffers<MODE>() == 3 ? kTileBytes : 1024];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -489,11 +574,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     GemmThread g;
     g.wave = wave;
     g.a_valid = ti.mend - ti.m0;
-    // A offsets stay below 4 GiB: relative to the tile's first row, or into
-    // x (whose size the host checks) when rows are gathered
-    g.a_base = reinterpret_cast<const char *>(a_rows ? A : A + (size_t)ti.m0 * K);
-    const char *b_base0 = reinterpret_cast<const char *>(B0 + wexp);
-    const char *b_base1 = reinterpret_cast<const char *>((MODE == kGateUp ? B1 : B0) + wexp);
+    // Buffer extents (all below 2 GiB for A, checked on the host, so an
+    // offset of 2 GiB is past the end): A is x (a_bytes) when rows are
+    // gathered, else the tile's valid rows; B is the expert's weight matrix
+    // (below 4 GiB, also checked).
+    g.a_rsrc = a_rows ? make_rsrc(A, a_bytes)
+                      : make_rsrc(A + (size_t)ti.m0 * K, (uint32_t)(g.a_valid < kBM ? g.a_valid : kBM) * K * 2);
+    const uint32_t w_bytes = (uint32_t)((size_t)N * K * 2);
+    // gate-up: waves 0-1 load B rows 0..127 (W1), waves 2-3 rows 128..255 (W3)
+    g.b_rsrc = make_rsrc((MODE == kGateUp && wave >= 2 ? B1 : B0) + wexp, w_bytes);
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; j++) {
         const int grp = wave * kLoadsPerOperand + j;
@@ -501,12 +590,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         const int c = (lane & 7) ^ swz(row);
         const int gm = min(ti.m0 + row, ti.mend - 1);
         const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
-        g.a_off[j] = ((uint32_t)ar * K + k_first + c * 8) * 2;
+        g.a_off[j] = grp * kRowsPerLoad < g.a_valid ? ((uint32_t)ar * K + k_first + c * 8) * 2 : kPastEnd;
         int gn = MODE == kGateUp ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
         gn = min(gn, N - 1);
         g.b_off[j] = ((uint32_t)gn * K + k_first + c * 8) * 2;
-        // B rows 0..127 come from B0, 128..255 from B1 (gate-up: W1 then W3)
-        g.b_src[j] = (MODE == kGateUp && grp * kRowsPerLoad >= kBN / 2) ? b_base1 : b_base0;
     }
     const int l5 = lane & 31, hi = lane >> 5;
     const int sw0 = swz(l5);  // swizzle of row base + l5 is sw0 ^ 4 * parity(base / 32)
@@ -517,31 +604,28 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         for (int ss = 0; ss < 4; ss++) {
             const uint32_t sw = (uint32_t)(((2 * ss + hi) ^ sw0 ^ (4 * pp)) << 4);
             g.fa[pp][ss] = (uint32_t)(wm * 128 + l5) * kRowBytes + sw;
-            g.fb[pp][ss] = kTileBytes + (uint32_t)(b_rbase + l5) * kRowBytes + sw;
+            g.fb[pp][ss] = (uint32_t)(b_rbase + l5) * kRowBytes + sw;
         }
     // active 32-row blocks of this wave (uniform)
     const int nact_raw = (ti.mend - (ti.m0 + wm * 128) + 31) / 32;
     const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
 
     const int nk = ks / kBK;
-#define MOE_TILE(n, skip)                                                                                 \
-    do {                                                                                                  \
-        if (nk & 1)                                                                                       \
-            run_tile<MODE, n, true, skip>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v);  \
-        else                                                                                              \
-            run_tile<MODE, n, false, skip>(g, ti, lds_s0, lds_s1, nk, n0, N, wm, wn, lane, split_stride, out_v); \
+#define MOE_TILE(n)                                                                                              \
+    do {                                                                                                         \
+        if (b_buffers<MODE>() == 2 && (nk & 1))                                                                  \
+            run_tile<MODE, n, b_buffers<MODE>() == 2>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N,  \
+                                                      wm, wn, lane, split_stride, out_v);                        \
+        else                                                                                                     \
+            run_tile<MODE, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane,     \
+                                     split_stride, out_v);                                                       \
     } while (0)
-    // a full tile loads every A row group: no per-load branch in its loop
-    if (g.a_valid >= kBM) {
-        MOE_TILE(4, false);
-    } else {
-        switch (nact) {
-            case 4: MOE_TILE(4, true); break;
-            case 3: MOE_TILE(3, true); break;
-            case 2: MOE_TILE(2, true); break;
-            case 1: MOE_TILE(1, true); break;
-            default: MOE_TILE(0, true); break;
-        }
+    switch (nact) {
+        case 4: MOE_TILE(4); break;
+        case 3: MOE_TILE(3); break;
+        case 2: MOE_TILE(2); break;
+        case 1: MOE_TILE(1); break;
+        default: MOE_TILE(0); break;
     }
 #undef MOE_TILE
 }
@@ -837,6 +921,9 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         return hipGetLastError();
     }
     if (p.dtype == MOE_BF16) {
+        // gathered A rows are read from x through a buffer extent below 2 GiB
+        const int64_t a_bytes = a_rows ? (int64_t)p.T * d * 2 : 0;
+        if (a_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
         const int64_t mt = max_rows / kBM + E;  // bound on sum_e ceil(rows_e / kBM)
         const int nt_up = (int)ceil_div(dff, kBN / 2);
         const int nt_dn = (int)ceil_div(d, kBN);
@@ -845,11 +932,11 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(x_perm), a_rows,
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
-                           offsets, E, dff, d, nt_up, 1, (size_t)0, h);
+                           offsets, E, dff, d, nt_up, 1, (size_t)0, (uint32_t)a_bytes, h);
         hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
-                           offsets, E, d, dff, nt_dn, S, split_stride, y_perm);
+                           offsets, E, d, dff, nt_dn, S, split_stride, (uint32_t)0, y_perm);
     } else {
         const int64_t mt = max_rows / kF32BM + E;
         const int nt_up = (int)ceil_div(dff, kF32BN);

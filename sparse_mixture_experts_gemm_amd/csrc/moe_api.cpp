@@ -50,9 +50,10 @@ int routing_ok(const moe_routing *r, const moe_params &p) {
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // moe_forward folds the dispatch gather into the gate-up GEMM (A rows read
-// from x through token_of_row) whenever x spans less than 4 GiB, the reach
-// of the GEMM's 32-bit load offsets; x_perm is then never materialised.
-bool gather_in_gemm(const moe_params &p) { return (int64_t)p.T * p.d * (int64_t)esize(p) < ((int64_t)1 << 32); }
+// from x through token_of_row) whenever x spans less than 2 GiB (the GEMM
+// reads A through a buffer extent kept below 2 GiB, so that an offset of
+// 2 GiB marks a load that fetches nothing); x_perm is then never materialised.
+bool gather_in_gemm(const moe_params &p) { return (int64_t)p.T * p.d * (int64_t)esize(p) < ((int64_t)1 << 31); }
 
 // Workspace layout of moe_forward.
 struct ForwardWs {

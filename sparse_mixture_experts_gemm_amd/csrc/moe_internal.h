@@ -67,7 +67,7 @@ inline int64_t capacity_rows(const moe_params &p) {
 int ffn_splits(const moe_params &p, int64_t max_rows);
 
 // a_rows == nullptr: A is x_perm.  Otherwise A is the unpermuted x and packed
-// row m is x row a_rows[m] (token_of_row); x must span less than 4 GiB.
+// row m is x row a_rows[m] (token_of_row); x must span less than 2 GiB.
 // cap bounds the rows of any one expert (the capacity C).
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,

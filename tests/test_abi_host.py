@@ -49,11 +49,18 @@ def test_workspace_sizes_cover_buffers():
     assert R == 8192
     ws = moe.workspace_bytes(p)
     S = moe.ffn_splits(p)
-    # h [R][d_ff] (fp16) and y_perm [S][R][d] (fp32); x spans less than 4 GiB, so
+    # h [R][d_ff] (fp16) and y_perm [S][R][d] (fp32); x spans less than 2 GiB, so
     # moe_forward reads the gate-up rows from x and needs no x_perm
     assert ws >= R * 14336 * 2 + S * R * 4096 * 4 + moe.dispatch_workspace_bytes(p)
     assert ws < R * 14336 * 2 + S * R * 4096 * 4 + R * 4096 * 2
     assert moe.dispatch_workspace_bytes(p) > 0
+    # x of 2 GiB and more: moe_forward writes x_perm [R][d] into its workspace
+    for T, has_xp in (((1 << 18) - 1, False), (1 << 18, True)):
+        q = P(T=T, d=4096, E=8, k=2, d_ff=1024, capacity_factor=1.0, dtype=moe.MOE_BF16)
+        Rq, Sq = moe.max_rows(q), moe.ffn_splits(q)
+        base = Rq * 1024 * 2 + Sq * Rq * 4096 * 4 + moe.dispatch_workspace_bytes(q)
+        wq = moe.workspace_bytes(q)
+        assert (wq >= base + Rq * 4096 * 2) == has_xp and wq >= base, (T, wq, base)
 
 
 @pytest.mark.parametrize("bad", [dict(E=0), dict(E=257), dict(k=0), dict(k=9, E=16), dict(k=3, E=2),
