@@ -323,10 +323,10 @@ __global__ __launch_bounds__(kThreads) void dispatch_finalize(
                   fb_hist, eid, pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm);
 }
 
-// T <= kThreads: one block runs the three phases back to back (the
-// histograms, fills and fallback counts pass through global memory exactly
-// as between the three kernels; the block's barriers order them), saving two
-// launches and their latency.
+// T <= kThreads: one block runs the three phases back to back, saving two
+// launches and their latency.  The histograms, fills and fallback counts
+// pass through LDS; the slot arrays (eid, pos, flag) through global memory,
+// as between the three kernels.  The block's barriers order the phases.
 __global__ __launch_bounds__(kThreads) void dispatch_single(
     const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k, int C,
     int use_fallback, float aux_coef, int cap_rows, int32_t *__restrict__ hist, int32_t *__restrict__ fill_prim,
@@ -339,14 +339,20 @@ __global__ __launch_bounds__(kThreads) void dispatch_single(
         PrimaryLds p;
         FinalizeLds f;
     } sm;
-    hist_body(0, cand, T, E, k, hist, sm.wcnt);
+    // the histograms and fills stay in LDS (the kernel arguments of the same
+    // names are unused here)
+    __shared__ int32_t hist_l[kMaxTopK * kMaxExperts], fill_l[kMaxExperts], fb_l[kMaxExperts];
+    (void)hist;
+    (void)fill_prim;
+    (void)fb_hist;
+    hist_body(0, cand, T, E, k, hist_l, sm.wcnt);
     __threadfence_block();
     __syncthreads();
-    primary_body(0, cand, T, E, k, C, 1, use_fallback, hist, fill_prim, eid, pos, flag, fb_hist, sm.p);
+    primary_body(0, cand, T, E, k, C, 1, use_fallback, hist_l, fill_l, eid, pos, flag, fb_l, sm.p);
     __threadfence_block();
     __syncthreads();
-    finalize_body(0, cand, cand_score, T, E, k, C, 1, use_fallback, aux_coef, cap_rows, hist, fill_prim, fb_hist,
-                  eid, pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm.f);
+    finalize_body(0, cand, cand_score, T, E, k, C, 1, use_fallback, aux_coef, cap_rows, hist_l, fill_l, fb_l, eid,
+                  pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm.f);
 }
 
 // x_perm[row[t][j]] = x[t] for every kept slot: the token row is read once.
