@@ -167,8 +167,11 @@ int moe_dispatch(const moe_params *p, const void *x, moe_routing *r, void *x_per
  *     y_perm[i] = h[i] . W2[e]^T   (as S partial sums over slices of d_ff)
  *   x_perm [R][d]; w1, w3 [E][d_ff][d]; w2 [E][d][d_ff]; h [R][d_ff] (fp16
  *   for bf16, fp32 for fp32);
- *   y_perm [S][R][d] fp32.  offsets [E+1] is read on the device.  Rows past
- *   offsets[E] of h and y_perm are left untouched.
+ *   y_perm [S][R][d] fp32.  offsets [E+1] is read on the device and must
+ *   be as moe_dispatch writes them: non-decreasing, offsets[0] = 0,
+ *   offsets[E] <= R and at most C rows per expert (the launch is sized by
+ *   these bounds; rows beyond them are not computed).  Rows past offsets[E]
+ *   of h and y_perm are left untouched.
  */
 int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offsets,
                    const void *w1, const void *w3, const void *w2, void *h, void *y_perm,

@@ -79,9 +79,17 @@ __device__ __forceinline__ void hist_body(int b, const int32_t *__restrict__ can
     }
 }
 
+// claim (null or kClaimCounters ints): the expert GEMM's work-claim counters,
+// zeroed here for the launch that follows the dispatch.
+__device__ __forceinline__ void zero_claim(int32_t *claim) {
+    if (claim && blockIdx.x == 0 && threadIdx.x < kClaimCounters) claim[threadIdx.x] = 0;
+}
+
 __global__ __launch_bounds__(kThreads) void dispatch_hist(const int32_t *__restrict__ cand, int T,
-                                                          int E, int k, int32_t *__restrict__ hist) {
+                                                          int E, int k, int32_t *__restrict__ hist,
+                                                          int32_t *__restrict__ claim) {
     __shared__ int wcnt[kWaves][kMaxExperts];
+    zero_claim(claim);
     hist_body(blockIdx.x, cand, T, E, k, hist, wcnt);
 }
 
@@ -333,12 +341,14 @@ __global__ __launch_bounds__(kThreads) void dispatch_single(
     int32_t *__restrict__ fb_hist, int32_t *__restrict__ eid, int32_t *__restrict__ pos,
     uint8_t *__restrict__ flag, int32_t *__restrict__ row, float *__restrict__ gate,
     int32_t *__restrict__ offsets, int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand,
-    int32_t *__restrict__ kept, int32_t *__restrict__ totals, float *__restrict__ aux_loss) {
+    int32_t *__restrict__ kept, int32_t *__restrict__ totals, float *__restrict__ aux_loss,
+    int32_t *__restrict__ claim) {
     __shared__ union {
         int wcnt[kWaves][kMaxExperts];
         PrimaryLds p;
         FinalizeLds f;
     } sm;
+    zero_claim(claim);
     // the histograms and fills stay in LDS (the kernel arguments of the same
     // names are unused here)
     __shared__ int32_t hist_l[kMaxTopK * kMaxExperts], fill_l[kMaxExperts], fb_l[kMaxExperts];
@@ -382,9 +392,9 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
         hipLaunchKernelGGL(dispatch_single, dim3(1), dim3(kThreads), 0, st, r.cand, r.cand_score, T, E, k,
                            (int)C, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim, ws.fb_hist, r.eid,
                            r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row, r.demand, r.kept, r.totals,
-                           r.aux_loss);
+                           r.aux_loss, ws.claim);
     } else {
-        hipLaunchKernelGGL(dispatch_hist, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, ws.hist);
+        hipLaunchKernelGGL(dispatch_hist, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, ws.hist, ws.claim);
         hipLaunchKernelGGL(dispatch_primary, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, (int)C,
                            nb, use_fb, ws.hist, ws.fill_prim, r.eid, r.pos, r.flag, ws.fb_hist);
         hipLaunchKernelGGL(dispatch_finalize, dim3(nb), dim3(kThreads), 0, st, r.cand, r.cand_score, T,

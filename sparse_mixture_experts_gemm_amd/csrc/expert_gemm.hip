@@ -32,6 +32,7 @@
 //   * 32-row MFMA blocks that lie wholly past an expert's last row are
 //     skipped, so ragged tails and small groups cost little matrix-core time.
 // fp32 path (the tiny fp32 layer): a plain LDS-tiled VALU GEMM.
+#include <algorithm>
 #include <type_traits>
 
 #include "device_common.h"
@@ -68,10 +69,21 @@ struct TileInfo {
 // The grid is sized by a bound on the work count; the real count comes from
 // the device-side offsets.  Each XCD is given an equal, contiguous range of
 // the real work items, so its L2 serves tiles that share operands and no
-// XCD is left with the empty tail of the grid.  Wave-parallel: lane l owns
-// experts 4l .. 4l+3 (E <= 256).  Returns false for blocks with no work.
+// XCD is left with the empty tail of the grid.  Without claim counters the
+// block takes item (XCD b % 8, position b / 8).  With them (8 zeroed ints)
+// thread 0 claims the next item of its XCD's range with an atomic add, and
+// once that range is used up, the next item of another XCD's range: the
+// XCDs run at different speeds, and the ones that finish early take over
+// the others' last items.  Each item is claimed exactly once (the adds
+// return distinct values), and a block that finds every range used up has
+// nothing to do; the grid (at least the item count) always suffices.  The
+// claimed index passes through `slot` (one int of LDS that nothing else uses
+// until the second barrier).  Wave-parallel: lane l owns experts
+// 4l .. 4l+3 (E <= 256).  Returns false for blocks with no work (uniformly
+// over the block).
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int ntiles_n,
-                                          int bm, int splits, int blk, TileInfo &ti) {
+                                          int bm, int splits, int blk, int32_t *claim, int *slot,
+                                          TileInfo &ti) {
     const int lane = lane_id();
     const int e0 = lane * 4;
     int mts[4], c = 0;
@@ -91,8 +103,28 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
     const int total = __builtin_amdgcn_readlane(incl, 63) * per;
     const int xcd = blk & 7, local = blk >> 3;
     const int q = total >> 3, r = total & 7;
-    if (local >= q + (xcd < r ? 1 : 0)) return false;
-    const int L = xcd * q + min(xcd, r) + local;
+    int L;
+    if (claim) {
+        if (threadIdx.x == 0) {
+            int item = -1;
+            for (int s = 0; s < 8; s++) {
+                const int y = (xcd + s) & 7;
+                const int i = atomicAdd(&claim[y], 1);
+                if (i < q + (y < r ? 1 : 0)) {
+                    item = y * q + min(y, r) + i;
+                    break;
+                }
+            }
+            *slot = item;
+        }
+        __syncthreads();
+        L = __builtin_amdgcn_readfirstlane(*slot);
+        __syncthreads();  // every wave has read the slot before its LDS is reused
+        if (L < 0) return false;
+    } else {
+        if (local >= q + (xcd < r ? 1 : 0)) return false;
+        L = xcd * q + min(xcd, r) + local;
+    }
     const int lo = (incl - c) * per, hi = incl * per;
     const bool mine = L >= lo && L < hi;
     int e_sel = 0, base_sel = 0;
@@ -553,7 +585,7 @@ template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
-    int splits, size_t split_stride, uint32_t a_bytes, void *__restrict__ out_v) {
+    int splits, size_t split_stride, uint32_t a_bytes, int32_t *claim, void *__restrict__ out_v) {
     __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
@@ -565,7 +597,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const int wm = wave >> 1, wn = wave & 1;
 
     TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, ti)) return;
+    if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti))
+        return;
     const int n0 = MODE == kGateUp ? ti.nt * (kBN / 2) : ti.nt * kBN;
     const size_t wexp = (size_t)ti.e * N * K;
     const int ks = K / splits;              // K elements of this split
@@ -762,7 +795,7 @@ __global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny(
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kSkBM, splits, blockIdx.x, ti)) return;
+    if (!find_tile(offsets, E, ntiles_n, kSkBM, splits, blockIdx.x, nullptr, nullptr, ti)) return;
     const int n0 = ti.nt * (MODE == kGateUp ? kSkBN : kSkBNd);
     const size_t wexp = (size_t)ti.e * N * K;
     const int ks = K / splits;
@@ -838,7 +871,7 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict_
     __shared__ float sb0[kF32BK][kF32BN + 1];
     __shared__ float sb1[kF32BK][kF32BN + 1];
     TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kF32BM, 1, blockIdx.x, ti)) return;
+    if (!find_tile(offsets, E, ntiles_n, kF32BM, 1, blockIdx.x, nullptr, nullptr, ti)) return;
     const int n0 = ti.nt * kF32BN;
     const size_t wexp = (size_t)ti.e * N * K;
     const int tx = threadIdx.x & 15, ty = threadIdx.x >> 4;  // 4x4 outputs each
@@ -899,14 +932,22 @@ int ffn_splits(const moe_params &p, int64_t max_rows) {
     return s;
 }
 
+// Bound on sum_e ceil(rows_e / bm), the m tiles of all experts: every
+// expert holds at most cap rows, and all of them at most max_rows.  The grid
+// is sized by it, so a tight bound leaves few blocks without work.
+static int64_t mtile_bound(int64_t max_rows, int64_t cap, int E, int bm) {
+    return std::min<int64_t>(max_rows / bm + E, (int64_t)E * ((cap + bm - 1) / bm));
+}
+
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
-                             const void *w3, const void *w2, void *h, void *y_perm, hipStream_t st) {
+                             const void *w3, const void *w2, void *h, void *y_perm, int32_t *claim,
+                             hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
     const int E = p.E, d = p.d, dff = p.d_ff;
     if (p.dtype == MOE_BF16 && cap <= kSkBM) {
         // every expert holds at most 32 rows: the weight-streaming kernel
-        const int64_t mt = max_rows / kSkBM + E;  // bound on sum_e ceil(rows_e / 32)
+        const int64_t mt = mtile_bound(max_rows, cap, E, kSkBM);
         const int nt_up = (int)ceil_div(dff, kSkBN);
         const int nt_dn = (int)ceil_div(d, kSkBNd);
         const int S = ffn_splits(p, max_rows);
@@ -924,7 +965,7 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         // gathered A rows are read from x through a buffer extent below 2 GiB
         const int64_t a_bytes = a_rows ? (int64_t)p.T * d * 2 : 0;
         if (a_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
-        const int64_t mt = max_rows / kBM + E;  // bound on sum_e ceil(rows_e / kBM)
+        const int64_t mt = mtile_bound(max_rows, cap, E, kBM);
         const int nt_up = (int)ceil_div(dff, kBN / 2);
         const int nt_dn = (int)ceil_div(d, kBN);
         const int S = ffn_splits(p, max_rows);
@@ -932,11 +973,12 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(x_perm), a_rows,
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
-                           offsets, E, dff, d, nt_up, 1, (size_t)0, (uint32_t)a_bytes, h);
+                           offsets, E, dff, d, nt_up, 1, (size_t)0, (uint32_t)a_bytes, claim, h);
         hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
-                           offsets, E, d, dff, nt_dn, S, split_stride, (uint32_t)0, y_perm);
+                           offsets, E, d, dff, nt_dn, S, split_stride, (uint32_t)0,
+                           claim ? claim + 8 : nullptr, y_perm);
     } else {
         const int64_t mt = max_rows / kF32BM + E;
         const int nt_up = (int)ceil_div(dff, kF32BN);

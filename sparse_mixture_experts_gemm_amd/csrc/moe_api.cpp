@@ -58,6 +58,7 @@ bool gather_in_gemm(const moe_params &p) { return (int64_t)p.T * p.d * (int64_t)
 // Workspace layout of moe_forward.
 struct ForwardWs {
     void *dispatch, *x_perm, *h, *y_perm;  // x_perm null when the GEMM gathers
+    int32_t *claim;                        // the expert GEMM's work-claim counters
 };
 
 size_t y_perm_bytes(const moe_params &p) {
@@ -69,7 +70,7 @@ size_t forward_ws_bytes(const moe_params &p) {
     const size_t R = (size_t)max_rows_of(p);
     const size_t xp = gather_in_gemm(p) ? 0 : align256(R * p.d * esize(p));
     return align256(dispatch_scratch_bytes(p.T, p.E, p.k)) + xp + align256(R * p.d_ff * esize(p)) +
-           align256(y_perm_bytes(p));
+           align256(y_perm_bytes(p)) + align256(sizeof(int32_t) * kClaimCounters);
 }
 
 ForwardWs carve_forward(void *ws, const moe_params &p) {
@@ -86,6 +87,8 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
     f.h = c;
     c += align256(R * p.d_ff * esize(p));
     f.y_perm = c;
+    c += align256(y_perm_bytes(p));
+    f.claim = reinterpret_cast<int32_t *>(c);
     return f;
 }
 
@@ -152,7 +155,7 @@ int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offse
         !aligned16(y_perm))
         return MOE_ERR_UNSUPPORTED;
     return hip_status(launch_expert_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w1, w3, w2, h, y_perm,
-                                        static_cast<hipStream_t>(stream)));
+                                        nullptr, static_cast<hipStream_t>(stream)));
 }
 
 int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
@@ -184,12 +187,15 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
     const int64_t R = max_rows_of(*p);
     hipError_t e = launch_route(*p, x, w_router, bias, load, logits, r->cand, r->cand_score, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    e = launch_dispatch(*p, C, x, *r, f.x_perm, carve_dispatch(f.dispatch, p->T, p->E, p->k), st);
+    DispatchScratch ds = carve_dispatch(f.dispatch, p->T, p->E, p->k);
+    ds.claim = f.claim;  // zeroed by the dispatch, used by the expert GEMM
+    e = launch_dispatch(*p, C, x, *r, f.x_perm, ds, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (f.x_perm)
-        e = launch_expert_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
+        e = launch_expert_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w1, w3, w2, f.h, f.y_perm, f.claim, st);
     else
-        e = launch_expert_ffn(*p, R, C, x, r->token_of_row, r->offsets, w1, w3, w2, f.h, f.y_perm, st);
+        e = launch_expert_ffn(*p, R, C, x, r->token_of_row, r->offsets, w1, w3, w2, f.h, f.y_perm, f.claim,
+                              st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, f.y_perm, r->row, r->gate, y, st);
     return hip_status(e);

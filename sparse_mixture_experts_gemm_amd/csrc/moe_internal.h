@@ -23,7 +23,11 @@ struct DispatchScratch {
     int32_t *hist;       // [NB][k][E]
     int32_t *fb_hist;    // [NB][E]
     int32_t *fill_prim;  // [E]
+    int32_t *claim = nullptr;  // [kClaimCounters] zeroed by the dispatch for the GEMM's work claims, or null
 };
+
+// Work-claim counters of the expert GEMM (one per XCD, gate-up then down).
+constexpr int kClaimCounters = 16;
 
 inline size_t dispatch_scratch_bytes(int T, int E, int k) {
     int64_t nb = ceil_div(T > 0 ? T : 1, kDispatchBlock);
@@ -68,10 +72,13 @@ int ffn_splits(const moe_params &p, int64_t max_rows);
 
 // a_rows == nullptr: A is x_perm.  Otherwise A is the unpermuted x and packed
 // row m is x row a_rows[m] (token_of_row); x must span less than 2 GiB.
-// cap bounds the rows of any one expert (the capacity C).
+// cap bounds the rows of any one expert (the capacity C).  claim: null, or
+// kClaimCounters zeroed ints through which the 256-row GEMM's blocks claim
+// their work items (an XCD whose range is done takes items of another).
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
-                             const void *w3, const void *w2, void *h, void *y_perm, hipStream_t st);
+                             const void *w3, const void *w2, void *h, void *y_perm, int32_t *claim,
+                             hipStream_t st);
 
 hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
                           const int32_t *row, const float *gate, void *y, hipStream_t st);
