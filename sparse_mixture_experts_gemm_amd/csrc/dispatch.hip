@@ -55,6 +55,26 @@ __device__ __forceinline__ int wave_rank_count(int key, int *wave_cnt) {
 // never used as an index.
 __device__ __forceinline__ int valid_expert(int c, int E) { return (unsigned)c < (unsigned)E ? c : -1; }
 
+// Sum of p[j * stride] over j < n (all) and over j < lim (below), read in
+// batches of eight independent loads (clamped indices, no branch) so that
+// their latencies overlap instead of adding up.  n >= 1.
+__device__ __forceinline__ void strided_sums(const int32_t *p, size_t stride, int n, int lim, int &below,
+                                             int &all) {
+    below = 0;
+    all = 0;
+    for (int j0 = 0; j0 < n; j0 += 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; u++) v[u] = p[(size_t)min(j0 + u, n - 1) * stride];
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int x = j0 + u < n ? v[u] : 0;
+            all += x;
+            below += j0 + u < lim ? x : 0;
+        }
+    }
+}
+
 __device__ __forceinline__ void zero_lds(int *a, int n) {
     for (int i = threadIdx.x; i < n; i += kThreads) a[i] = 0;
 }
@@ -114,12 +134,8 @@ __device__ __forceinline__ void primary_body(int b, const int32_t *__restrict__ 
     // requests before this block, and in total, per (round, expert)
     for (int i = threadIdx.x; i < k * E; i += kThreads) {
         const int r = i / E, e = i % E;
-        int pre = 0, all = 0;
-        for (int bb = 0; bb < nb; bb++) {
-            const int v = hist[((size_t)bb * k + r) * E + e];
-            all += v;
-            pre += bb < b ? v : 0;
-        }
+        int pre, all;
+        strided_sums(hist + (size_t)r * E + e, (size_t)k * E, nb, b, pre, all);
         base[r][e] = pre;
         tot[r][e] = all;
     }
@@ -209,12 +225,8 @@ __device__ __forceinline__ void finalize_body(
     const int wave = threadIdx.x >> 6;
 
     for (int e = threadIdx.x; e < E; e += kThreads) {
-        int pre = 0, all = 0;
-        for (int bb = 0; bb < nb; bb++) {
-            const int v = fb_hist[(size_t)bb * E + e];
-            all += v;
-            pre += bb < b ? v : 0;
-        }
+        int pre, all;
+        strided_sums(fb_hist + e, (size_t)E, nb, b, pre, all);
         const int fp = fill_prim[e];
         fbase[e] = fp + pre;
         const int kc = min(C, fp + all);
@@ -294,9 +306,8 @@ __device__ __forceinline__ void finalize_body(
     if (b == 0) {
         for (int e = threadIdx.x; e <= E; e += kThreads) offsets[e] = offs[e];
         for (int e = threadIdx.x; e < E; e += kThreads) {
-            int dem = 0;
-            for (int bb = 0; bb < nb; bb++)
-                for (int r = 0; r < k; r++) dem += hist[((size_t)bb * k + r) * E + e];
+            int dem, unused;
+            strided_sums(hist + e, (size_t)E, nb * k, 0, unused, dem);  // rows (block, round) of hist
             demand[e] = dem;
             kept[e] = kcnt[e];
             scan_tmp[0][e] = dem;  // reuse for the loss below
