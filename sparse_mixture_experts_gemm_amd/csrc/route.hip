@@ -12,10 +12,10 @@
 // lanes read consecutive 16-byte chunks).  bf16 products are accumulated with
 // v_dot2_f32_bf16.  Each lane ends with 32 partial sums (TPW tokens x EA
 // experts); a butterfly reduce-scatter over the 64 lanes (DPP inside rows of
-// 16, ds_bpermute across rows) leaves one full sum per lane pair, so the
+// 16, the gfx950 lane swaps across rows) leaves one full sum per lane pair, so the
 // cross-lane cost is one shuffle per logit.  Ranking is k+1 wave max
 // reductions of a 64-bit key (order-preserving score bits with NaN lowest,
-// then the inverted expert index), also DPP/bpermute butterflies.
+// then the inverted expert index), also DPP / lane-swap butterflies.
 //
 // The penalty is an explicit fmaf and the file is built without fast-math, so
 // the fp32 ranking is reproducible from the fp32 logits bit for bit.
@@ -60,16 +60,44 @@ struct ChunkDot<float> {
     }
 };
 
+// Exchange across 32 or 16 lanes with the gfx950 lane-swap instructions:
+// for a pair (a, b) they leave a' = a and b' = b of the partner half, so
+// that a' + b' is a reduce-scatter step (a lane whose STEP bit is clear
+// gets a[l] + a[l ^ STEP], a lane whose bit is set b[l ^ STEP] + b[l]).
+// VALU only, no LDS round trip.
+template <int STEP>
+__device__ __forceinline__ void swap_halves(uint32_t &a, uint32_t &b) {
+    static_assert(STEP == 16 || STEP == 32, "lane-swap steps");
+    if constexpr (STEP == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    } else {
+        const auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+        a = r[0];
+        b = r[1];
+    }
+}
+
 // One butterfly reduce-scatter step: the lane keeps half of its V values
 // (the upper half when its STEP bit is set) and adds the partner's copy.
 template <int STEP, int V, int N>
 __device__ __forceinline__ void rs_step(float (&v)[N], int lane) {
-    const bool upper = (lane & STEP) != 0;
+    if constexpr (STEP >= 16) {
 #pragma unroll
-    for (int i = 0; i < V / 2; i++) {
-        float send = upper ? v[i] : v[i + V / 2];
-        float keep = upper ? v[i + V / 2] : v[i];
-        v[i] = keep + exch_f32<STEP>(send);
+        for (int i = 0; i < V / 2; i++) {
+            uint32_t a = __float_as_uint(v[i]), b = __float_as_uint(v[i + V / 2]);
+            swap_halves<STEP>(a, b);
+            v[i] = __uint_as_float(a) + __uint_as_float(b);
+        }
+    } else {
+        const bool upper = (lane & STEP) != 0;
+#pragma unroll
+        for (int i = 0; i < V / 2; i++) {
+            float send = upper ? v[i] : v[i + V / 2];
+            float keep = upper ? v[i + V / 2] : v[i];
+            v[i] = keep + exch_f32<STEP>(send);
+        }
     }
 }
 
@@ -90,9 +118,16 @@ __device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a >
 
 template <int STEP>
 __device__ __forceinline__ uint64_t max_step(uint64_t v) {
-    const uint32_t lo = (uint32_t)exch_i32<STEP>((int)(uint32_t)v);
-    const uint32_t hi = (uint32_t)exch_i32<STEP>((int)(uint32_t)(v >> 32));
-    return max_u64(v, ((uint64_t)hi << 32) | lo);
+    if constexpr (STEP >= 16) {
+        uint32_t lo0 = (uint32_t)v, lo1 = lo0, hi0 = (uint32_t)(v >> 32), hi1 = hi0;
+        swap_halves<STEP>(lo0, lo1);  // (own half, partner half) in some order
+        swap_halves<STEP>(hi0, hi1);
+        return max_u64(((uint64_t)hi0 << 32) | lo0, ((uint64_t)hi1 << 32) | lo1);
+    } else {
+        const uint32_t lo = (uint32_t)exch_i32<STEP>((int)(uint32_t)v);
+        const uint32_t hi = (uint32_t)exch_i32<STEP>((int)(uint32_t)(v >> 32));
+        return max_u64(v, ((uint64_t)hi << 32) | lo);
+    }
 }
 
 typedef __attribute__((address_space(3))) char lds_char_t;
