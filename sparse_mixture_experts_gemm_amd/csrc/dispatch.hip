@@ -13,8 +13,9 @@
 // Because a primary request's queue position depends only on how many earlier
 // requests chose the same expert, positions are counting problems: per-block
 // expert histograms, an exclusive prefix over blocks, and an in-block rank from
-// wave ballots (mbcnt over the lanes holding the same expert).  The fallback
-// round depends on the primary overflow, so it takes a second histogram pass.
+// wave ballots (one ballot per bit of the expert index, then mbcnt over the
+// lanes holding the same expert).  The fallback round depends on the primary
+// overflow, so it takes a second histogram pass.
 // Kernels (one token per thread, 1024 tokens per block):
 //   hist      per-block counts of each primary round
 //   primary   queue positions of the primary rounds, fallback histograms
@@ -34,19 +35,20 @@ static_assert(kThreads == kDispatchBlock, "one token per thread");
 
 // Rank of this lane among the lanes of its wave holding the same key (keys
 // < 0 are ignored), and the per-key lane counts of the wave, written to
-// wave_cnt[key].  One ballot per distinct key in the wave.
-__device__ __forceinline__ int wave_rank_count(int key, int *wave_cnt) {
-    const int lane = threadIdx.x & 63;
-    uint64_t active = ballot64(key >= 0);
-    int rank = 0;
-    while (active) {
-        const int leader = __builtin_ctzll(active);
-        const int lk = __builtin_amdgcn_readlane(key, leader);
-        const uint64_t m = ballot64(key == lk);
-        if (key == lk) rank = rank_below(m);
-        if (lane == leader) wave_cnt[lk] = __popcll(m);
-        active &= ~m;
+// wave_cnt[key].  The lanes holding this lane's key are found bit by bit:
+// one ballot per key bit (nbits = ceil(log2 E)), each narrowing the set to
+// the lanes that agree on that bit, so the cost does not grow with the
+// number of distinct keys in the wave.  The lowest lane of each key writes
+// the count.
+__device__ __forceinline__ int wave_rank_count(int key, int nbits, int *wave_cnt) {
+    uint64_t same = ballot64(key >= 0);
+    for (int b = 0; b < nbits; b++) {  // nbits is uniform
+        const bool bit = (key >> b) & 1;
+        const uint64_t m = ballot64(bit);
+        same &= bit ? m : ~m;
     }
+    const int rank = rank_below(same);
+    if (key >= 0 && rank == 0) wave_cnt[key] = __popcll(same);
     return rank;
 }
 
@@ -54,6 +56,9 @@ __device__ __forceinline__ int wave_rank_count(int key, int *wave_cnt) {
 // caller's own routing may hold anything) is read as "no expert", so it is
 // never used as an index.
 __device__ __forceinline__ int valid_expert(int c, int E) { return (unsigned)c < (unsigned)E ? c : -1; }
+
+// Bits of an expert index: ceil(log2 E), at least 1.
+__device__ __forceinline__ int key_bits(int E) { return E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 1; }
 
 // Sum of p[j * stride] over j < n (all) and over j < lim (below), read in
 // batches of eight independent loads (clamped indices, no branch) so that
@@ -88,7 +93,7 @@ __device__ __forceinline__ void hist_body(int b, const int32_t *__restrict__ can
         zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
         __syncthreads();
         const int key = t < T ? valid_expert(cand[(size_t)t * K1 + r], E) : -1;
-        wave_rank_count(key, wcnt[wave]);
+        wave_rank_count(key, key_bits(E), wcnt[wave]);
         __syncthreads();
         for (int e = threadIdx.x; e < E; e += kThreads) {
             int s = 0;
@@ -155,7 +160,7 @@ __device__ __forceinline__ void primary_body(int b, const int32_t *__restrict__ 
         zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
         __syncthreads();
         const int key = t < T ? valid_expert(cand[(size_t)t * K1 + r], E) : -1;
-        const int rank = wave_rank_count(key, wcnt[wave]);
+        const int rank = wave_rank_count(key, key_bits(E), wcnt[wave]);
         __syncthreads();
         if (t < T) {
             int p = C;  // a candidate that names no expert is never kept
@@ -182,7 +187,7 @@ __device__ __forceinline__ void primary_body(int b, const int32_t *__restrict__ 
     zero_lds(&wcnt[0][0], kWaves * kMaxExperts);
     __syncthreads();
     const int fkey = (t < T && use_fallback && first_over >= 0) ? valid_expert(cand[(size_t)t * K1 + k], E) : -1;
-    wave_rank_count(fkey, wcnt[wave]);
+    wave_rank_count(fkey, key_bits(E), wcnt[wave]);
     __syncthreads();
     for (int e = threadIdx.x; e < E; e += kThreads) {
         int s = 0;
@@ -256,7 +261,7 @@ __device__ __forceinline__ void finalize_body(
                 break;
             }
     const int fkey = (t < T && use_fallback && first_over >= 0) ? valid_expert(cand[(size_t)t * K1 + k], E) : -1;
-    const int rank = wave_rank_count(fkey, wcnt[wave]);
+    const int rank = wave_rank_count(fkey, key_bits(E), wcnt[wave]);
     __syncthreads();
     if (fkey >= 0) {
         int p = fbase[fkey] + rank;
