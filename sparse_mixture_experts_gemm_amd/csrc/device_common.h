@@ -70,4 +70,28 @@ __device__ __forceinline__ int rank_below(uint64_t m) {
 
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0)); }
 
+// Buffer resource over [base, base + bytes): base and extent are made
+// wave-uniform explicitly, so the descriptor is built in scalar registers and
+// every load takes it from there.  A load whose lane offset is at or past the
+// extent reads nothing and returns zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t b = reinterpret_cast<uint64_t>(base);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((hi << 32) | lo), (short)0,
+                                             __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
+}
+// A lane offset past every extent used with it (each is below 2 GiB): such a
+// load fetches nothing.
+constexpr uint32_t kPastEnd = 0x80000000u;
+
+// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row.  Fragment
+// reads touch one chunk of 16 (or 8) consecutive rows per LDS cycle; with
+// this swizzle those rows hit distinct banks whether the LDS serves 16 lanes
+// over 64 banks or 8 lanes over 32 banks per cycle.
+__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+
+// s_waitcnt with only the vector-memory counter: at most n loads in flight.
+#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
+
 }  // namespace moe

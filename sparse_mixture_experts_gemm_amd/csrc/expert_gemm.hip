@@ -52,11 +52,6 @@ constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (
 
 enum { kGateUp = 0, kDown = 1 };
 
-// XOR swizzle of the eight 16-byte chunks of a 128-byte LDS row.  Fragment
-// reads touch one chunk of 16 (or 8) consecutive rows per LDS cycle; with
-// this swizzle those rows hit distinct banks whether the LDS serves 16 lanes
-// over 64 banks or 8 lanes over 32 banks per cycle.
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
 
 // Flat work index -> (expert, m range, n tile, K split).  Work items are
 // ordered expert, split, n tile, m tile (m fastest), so the m tiles that
@@ -201,23 +196,10 @@ __device__ __forceinline__ void g2lds16(const char *src, char *dst) {
     __builtin_amdgcn_global_load_lds((gbl_char_t *)src, (lds_char_t *)dst, 16, 0, 0);
 }
 
-// The same through a buffer resource: the base and extent are in scalar
-// registers, the lane's byte offset in `voff` and a wave-uniform offset (the
-// K step) in `soff`, so no 64-bit address is kept per load; reads at or past
-// the extent return zeros.
-// (base and extent are made wave-uniform explicitly, so the descriptor is
-// built in scalar registers and every load takes it from there)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    const uint64_t b = reinterpret_cast<uint64_t>(base);
-    const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void *>((hi << 32) | lo), (short)0,
-                                             __builtin_amdgcn_readfirstlane((int)bytes), 0x00020000);
-}
-// A byte offset past every A extent (each is below 2 GiB): such a load
-// fetches nothing.
-constexpr uint32_t kPastEnd = 0x80000000u;
-
+// Loads through a buffer resource (make_rsrc, kPastEnd): the base and extent
+// are in scalar registers, the lane's byte offset in `voff` and a
+// wave-uniform offset (the K step) in `soff`, so no 64-bit address is kept
+// per load; reads at or past the extent return zeros.
 __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char *dst) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char_t *)dst, 16, voff, soff, 0, 0);
 }
@@ -307,8 +289,6 @@ __device__ __forceinline__ void mfma_blocks(const Frags &f, f32x16_t (&acc)[4][4
     }
 }
 
-// s_waitcnt with only the vector-memory counter: at most n loads in flight.
-#define WAIT_VMCNT(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4) | (15 << 8))
 // s_waitcnt vmcnt(n) lgkmcnt(0): at most n loads in flight, no LDS access
 #define WAIT_VMCNT_LGKM0(n) __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | (7 << 4))
 // s_waitcnt vmcnt(0) lgkmcnt(0)

@@ -5,8 +5,10 @@
 //   s[t][e]   = fmaf(-lambda, load[e], raw[t][e])      (raw when load == NULL)
 //   cand[t]   = the k+1 experts with the largest s, ties to the lower index.
 //
-// Mapping on CDNA4.  The router is a skinny GEMM (N = E is 8..256), so it runs
-// on the vector ALU, not MFMA: a wave owns TPW tokens and holds their x rows
+// Mapping on CDNA4.  The router is a skinny GEMM (N = E is 1..256) and one
+// pass over x.  bf16 layers with E <= 64 run it on the matrix cores
+// (route_mfma, below).  Otherwise (fp32 layers, more experts) it runs on the
+// vector ALU: a wave owns TPW tokens and holds their x rows
 // in registers, 16-byte chunks strided over the 64 lanes.  The gate vectors
 // are staged in LDS in chunks of experts and read conflict-free (consecutive
 // lanes read consecutive 16-byte chunks).  bf16 products are accumulated with
@@ -368,6 +370,210 @@ hipError_t launch_nx(const moe_params &p, const void *x, const void *wr, const f
     return launch_t<TIn, NX, 1, kSpec>(p, x, wr, bias, load, logits, cand, cand_score, st);
 }
 
+// ------------------------------------------------------------ MFMA router --
+// bf16 layers with E <= 64 run the router GEMM on the matrix cores.  A block
+// owns BT = 16 NT tokens and every expert; its 4 waves split the hidden
+// dimension into 64-element slabs (one 128-byte line of a row), wave w taking
+// slabs w, w + 4, ... in an order rotated per block (so that the blocks
+// resident at one time read different columns of x and W, not all the same
+// HBM channels and L2 lines).  Each wave streams its slabs through a private
+// ring of P LDS slots with direct global -> LDS loads: one load moves eight
+// whole 128-byte lines (x rows of the block, then W rows; rows past the block's
+// tokens or past E read nothing and write zeros), so the accesses coalesce,
+// which loads straight into the MFMA register layout (16 rows per load) do
+// not.  No barrier is needed in the loop: a wave reads only what it loaded.
+// MFMA 16x16x32 bf16 on fragments read from the slot through the XOR
+// swizzle; in k step i of a slab, lane l takes row l % 16 and 16-byte chunk
+// 4 i + l / 16 (x and W alike).  The four waves' fp32 partials are added in
+// LDS in wave order, then the bias, the penalty and the top-(k+1) ranking,
+// with 64 / G tokens ranked at once in groups of G lanes.
+constexpr int kRmThreads = 256;
+constexpr int kRmWaves = kRmThreads / 64;
+constexpr int kSlabBytes = 128;
+
+
+__device__ __forceinline__ void rt_buf2lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, char *dst) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_char_t *)dst, 16, voff, soff, 0, 0);
+}
+
+template <int NT, int NE, int P, int G>
+__global__ __launch_bounds__(kRmThreads) void route_mfma(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, const float *__restrict__ bias,
+    const float *__restrict__ load, float neg_lambda, int T, int d, int E, int K1, float *__restrict__ logits,
+    int32_t *__restrict__ cand, float *__restrict__ cand_score) {
+    constexpr int BT = 16 * NT, EP = 16 * NE, TPP = 64 / G;
+    constexpr int kXG = BT / 8, kWG = EP / 8, L = kXG + kWG;  // 1 KiB loads per slab
+    constexpr int kSlot = L * 1024;                           // one wave's slab
+    static_assert(G == 8 || G == 16 || G == 32 || G == 64, "ranking group");
+    static_assert(P >= 2 && P <= 8 && (P - 1) * L <= 63, "ring depth");
+    static_assert(kRmWaves * BT * EP * 4 <= kRmWaves * kSlot, "partials fit the first slot");
+    __shared__ __attribute__((aligned(1024))) char s0[kRmWaves * kSlot];
+    __shared__ __attribute__((aligned(1024))) char s1[kRmWaves * kSlot];
+    __shared__ __attribute__((aligned(1024))) char s2[P > 2 ? kRmWaves * kSlot : 16];
+    __shared__ __attribute__((aligned(1024))) char s3[P > 3 ? kRmWaves * kSlot : 16];
+    __shared__ __attribute__((aligned(1024))) char s4[P > 4 ? kRmWaves * kSlot : 16];
+    __shared__ __attribute__((aligned(1024))) char s5[P > 5 ? kRmWaves * kSlot : 16];
+    __shared__ __attribute__((aligned(1024))) char s6[P > 6 ? kRmWaves * kSlot : 16];
+    __shared__ __attribute__((aligned(1024))) char s7[P > 7 ? kRmWaves * kSlot : 16];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    auto slot = [&](int sl) -> char * {
+        char *b = sl == 0 ? s0 : sl == 1 ? s1 : sl == 2 ? s2 : sl == 3 ? s3 : sl == 4 ? s4 : sl == 5 ? s5 : sl == 6 ? s6 : s7;
+        return b + wave * kSlot;
+    };
+    const int t0 = blockIdx.x * BT;
+    const int nt = min(BT, T - t0);
+    const uint32_t row_bytes = (uint32_t)d * 2;
+    const auto xs = make_rsrc(x + (size_t)t0 * d, (uint32_t)nt * row_bytes);
+    const auto ws = make_rsrc(wr, (uint32_t)E * row_bytes);
+    // load group gi moves rows 8 gi .. 8 gi + 7 of the slot (x rows, then W
+    // rows); lane l fetches chunk (l % 8) ^ swz(row) of row 8 gi + l / 8, so
+    // LDS chunk c of a row holds the row's chunk c ^ swz(row)
+    uint32_t voff[L];
+#pragma unroll
+    for (int gi = 0; gi < L; gi++) {
+        const int row = 8 * (gi < kXG ? gi : gi - kXG) + (lane >> 3);
+        const int lim = gi < kXG ? nt : E;
+        voff[gi] = row < lim ? row * row_bytes + (((lane & 7) ^ swz(8 * gi + (lane >> 3))) << 4) : kPastEnd;
+    }
+
+    const int nslab = d / 64;
+    const int mine = (nslab - wave + kRmWaves - 1) / kRmWaves;  // slabs of this wave
+    const int rot = mine > 0 ? (int)(((blockIdx.x >> 3) + (blockIdx.x & 7) * 2) % (unsigned)mine) : 0;
+    // slab j of this wave (past its last slab every load is out of range and
+    // writes zeros, so the compute needs no branch)
+    auto issue = [&](int j, char *dst) {
+        const bool v = j < mine;
+        int jj = j + rot;
+        jj = jj >= mine ? jj - mine : jj;
+        const uint32_t so = v ? (uint32_t)(wave + kRmWaves * jj) * kSlabBytes : 0u;
+#pragma unroll
+        for (int gi = 0; gi < L; gi++)
+            rt_buf2lds(gi < kXG ? xs : ws, v ? voff[gi] : kPastEnd, so, dst + gi * 1024);
+    };
+    const int r16 = lane & 15, q = lane >> 4;
+    f32x4_t acc[NT][NE];
+#pragma unroll
+    for (int f = 0; f < NT; f++)
+#pragma unroll
+        for (int g = 0; g < NE; g++) acc[f][g] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    auto compute = [&](const char *src) {
+#pragma unroll
+        for (int i = 0; i < 2; i++) {
+            uint4 a[NT], b[NE];
+#pragma unroll
+            for (int f = 0; f < NT; f++) {
+                const int row = 16 * f + r16;
+                a[f] = *reinterpret_cast<const uint4 *>(src + row * kSlabBytes + (((4 * i + q) ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int g = 0; g < NE; g++) {
+                const int row = BT + 16 * g + r16;
+                b[g] = *reinterpret_cast<const uint4 *>(src + row * kSlabBytes + (((4 * i + q) ^ swz(row)) << 4));
+            }
+#pragma unroll
+            for (int f = 0; f < NT; f++)
+#pragma unroll
+                for (int g = 0; g < NE; g++)
+                    acc[f][g] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[f]),
+                                                                       __builtin_bit_cast(bf16x8_t, b[g]), acc[f][g],
+                                                                       0, 0, 0);
+        }
+    };
+#pragma unroll
+    for (int sl = 0; sl < P; sl++) issue(sl, slot(sl));
+    // P slabs per loop iteration (slab j sits in slot j % P; when it is
+    // used, the P - 1 later slabs may still be in flight); slabs past the
+    // wave's last one, at most P - 1, are zeros
+    for (int j0 = 0; j0 < mine; j0 += P) {
+#pragma unroll
+        for (int u = 0; u < P; u++) {
+            WAIT_VMCNT((P - 1) * L);
+            compute(slot(u));
+            __builtin_amdgcn_sched_barrier(0);
+            issue(j0 + u + P, slot(u));
+        }
+    }
+    WAIT_VMCNT(0);  // the ring is reused below; no load may still write it
+    __syncthreads();
+
+    // the lane holds expert 16 g + lane % 16 of tokens 16 f + 4 (lane / 16) + c
+    float(*part)[BT][EP] = reinterpret_cast<float(*)[BT][EP]>(s0);
+#pragma unroll
+    for (int f = 0; f < NT; f++)
+#pragma unroll
+        for (int g = 0; g < NE; g++)
+#pragma unroll
+            for (int c = 0; c < 4; c++) part[wave][16 * f + 4 * q + c][16 * g + r16] = acc[f][g][c];
+    __syncthreads();
+    for (int i = threadIdx.x; i < nt * E; i += kRmThreads) {
+        const int t = i / E, e = i - t * E;
+        float raw = ((part[0][t][e] + part[1][t][e]) + part[2][t][e]) + part[3][t][e];
+        if (bias) raw = raw + bias[e];
+        logits[(size_t)(t0 + t) * E + e] = raw;
+        part[0][t][e] = load ? __builtin_fmaf(neg_lambda, load[e], raw) : raw;
+    }
+    __syncthreads();
+
+    // ranking: groups of G lanes, one token each; lane e of a group holds
+    // expert e; each round is a group max of the ranking keys, and the
+    // winner's key is cleared
+    const int e = lane & (G - 1);
+    for (int base = wave * TPP; base < nt; base += kRmWaves * TPP) {
+        const int t = base + lane / G;  // < BT
+        const bool ok = t < nt && e < E;
+        uint64_t key = ok ? rank_key(part[0][t][e], e) : 0;
+        for (int r = 0; r < K1; r++) {
+            uint64_t m = max_step<1>(key);
+            m = max_step<2>(m);
+            m = max_step<4>(m);
+            if constexpr (G >= 16) m = max_step<8>(m);
+            if constexpr (G >= 32) m = max_step<16>(m);
+            if constexpr (G >= 64) m = max_step<32>(m);
+            const bool none = m == 0;
+            const int we = none ? 0 : (int)~(uint32_t)m;  // the group's winner
+            const float sw = part[0][t][we];               // its own score bits
+            if (e == 0 && t < nt) {
+                cand[(size_t)(t0 + t) * K1 + r] = none ? -1 : we;
+                cand_score[(size_t)(t0 + t) * K1 + r] = none ? -INFINITY : sw;
+            }
+            if (!none && e == we) key = 0;
+        }
+    }
+}
+
+template <int NT, int NE, int G>
+hipError_t launch_mfma_g(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
+                         float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
+    // ring depth: as many slots as 144 KiB of LDS holds (4 waves, one slab
+    // of BT x rows and 16 NE W rows each), at most 8
+    constexpr int kSlotBlock = 4 * (2 * NT + 2 * NE) * 1024;
+    constexpr int P = 144 * 1024 / kSlotBlock > 8 ? 8 : 144 * 1024 / kSlotBlock;
+    const int grid = (int)ceil_div(p.T, 16 * NT);
+    hipLaunchKernelGGL((route_mfma<NT, NE, P, G>), dim3(grid), dim3(kRmThreads), 0, st,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wr), bias, load, -p.lambda,
+                       p.T, p.d, p.E, p.k + 1, logits, cand, cand_score);
+    return hipGetLastError();
+}
+
+template <int NT>
+hipError_t launch_mfma_nt(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
+                          float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
+    if (p.E <= 8) return launch_mfma_g<NT, 1, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (p.E <= 16) return launch_mfma_g<NT, 1, 16>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (p.E <= 32) return launch_mfma_g<NT, 2, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (p.E <= 48) return launch_mfma_g<NT, 3, 64>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    return launch_mfma_g<NT, 4, 64>(p, x, wr, bias, load, logits, cand, cand_score, st);
+}
+
+// 32 tokens per block once that still gives every compute unit a block
+// (half the gate-vector reads per token), else 16.
+hipError_t launch_mfma(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
+                       float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
+    if (p.T >= 256 * 32) return launch_mfma_nt<2>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    return launch_mfma_nt<1>(p, x, wr, bias, load, logits, cand, cand_score, st);
+}
+
 template <typename TIn>
 hipError_t launch_dtype(const moe_params &p, const void *x, const void *wr, const float *bias,
                         const float *load, float *logits, int32_t *cand, float *cand_score,
@@ -389,6 +595,8 @@ hipError_t launch_route(const moe_params &p, const void *x, const void *wr, cons
                         const float *load, float *logits, int32_t *cand, float *cand_score,
                         hipStream_t st) {
     if (p.T == 0) return hipSuccess;
+    if (p.dtype == MOE_BF16 && p.E <= 64)
+        return launch_mfma(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (p.dtype == MOE_BF16)
         return launch_dtype<uint16_t>(p, x, wr, bias, load, logits, cand, cand_score, st);
     return launch_dtype<float>(p, x, wr, bias, load, logits, cand, cand_score, st);

@@ -2,8 +2,10 @@
 
 Routing arrays must be bit-exact with the oracle run on the GPU's fp32 router
 logits.  Layer outputs (and y_perm) must satisfy max|err| <= 2e-2 * RMS(ref)
-for bf16 (fp32 accumulation) and <= 1e-4 * RMS(ref) for fp32; edge cases in
-which whole tokens are dropped take the RMS over the tokens that kept a slot.
+for bf16 (fp32 accumulation) and <= 1e-4 * RMS(ref) for fp32, the layer
+output beyond the rounding of each element to its storage type (one unit
+roundoff of |ref|); edge cases in which whole tokens are dropped take the RMS
+over the tokens that kept a slot.
 Intermediates rounded once (h, the combine's store) are held to one ulp of
 their storage type per element.  Router logits are compared with the
 oracle's own double-accumulated logits at 1e-3 * RMS.
@@ -51,13 +53,23 @@ def rms(a):
     return float(np.sqrt(np.mean(np.asarray(a, np.float64) ** 2)))
 
 
-def assert_close(got, ref, dtype, what, rms_rows=None):
+def assert_close(got, ref, dtype, what, rms_rows=None, stored=False):
     """max|err| <= tol * RMS(ref); rms_rows selects the rows the RMS is taken
-    over (edge cases with many fully dropped tokens use the kept rows)."""
+    over (edge cases with many fully dropped tokens use the kept rows).
+    stored: `got` is the layer output in its element type, so each element
+    may also carry that type's own rounding of the exact value, up to one
+    unit roundoff of |ref| (2^-8 for bf16, 2^-24 for fp32); at small hidden
+    sizes the output has elements of 7-9 RMS, where the bf16 rounding alone
+    reaches 2-3% of RMS."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     r = rms(ref if rms_rows is None else ref[rms_rows])
-    err = float(np.abs(got - ref).max()) if ref.size else 0.0
+    if not ref.size:
+        return 0.0
+    dev = np.abs(got - ref)
+    if stored:
+        dev = dev - (2.0 ** -8 if dtype == moe.MOE_BF16 else 2.0 ** -24) * np.abs(ref)
+    err = float(dev.max())
     assert err <= TOL[dtype] * r + 1e-30, f"{what}: max|err| {err:.3e} > {TOL[dtype]} * RMS {r:.3e}"
     return err / r if r > 0 else 0.0
 
@@ -242,7 +254,7 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
     toks = np.arange(T, dtype=np.int32) if (full_rows or T <= 64) else sample_tokens(ref2, T, n_tok, rng)
     yref = oracle.layer_tokens(toks, L.c["x"], L.c["w1"], L.c["w3"], L.c["w2"], ref2["eid"], ref2["gate64"])
     kept_rows = (ref2["flag"][toks] != 2).any(axis=1) if rms_kept_rows else None
-    rel = assert_close(y2.float().cpu().numpy()[toks], yref, p.dtype, "layer output", kept_rows)
+    rel = assert_close(y2.float().cpu().numpy()[toks], yref, p.dtype, "layer output", kept_rows, stored=True)
     # informational: routing under the oracle's own logits
     say(f"[ok] {cfg.name}: rows={rows} dropped={int(ref2['totals'][1])} rerouted={int(ref2['totals'][2])} "
         f"max|err|/RMS={rel:.2e}")
@@ -282,6 +294,11 @@ EDGE = {
     "many_experts_top8": dict(E=256, k=8, T=512, d=64, d_ff=64, cf=1.0),
     "min_dims_f32": dict(T=77, d=64, d_ff=64, dtype="f32", E=3, k=1),
     "bias_penalty": dict(T=500, E=16, bias="hot0", bias_hot=3.0, lam=0.3, load_from_prev=True),
+    # router classes: 32 tokens per block and two expert fragments; three
+    # expert fragments with a hidden size of 5 slabs over 4 waves; one slab
+    "experts_32_blocks_of_32": dict(T=8200, E=32, k=4, d=128, d_ff=64),
+    "experts_40_odd_slabs": dict(T=650, E=40, k=3, d=320, d_ff=128),
+    "min_dims_bf16": dict(T=77, d=64, d_ff=64, E=3, k=1),
 }
 
 
