@@ -142,6 +142,15 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
+    # distribution of single-step times (events around each step, no sync in
+    # between), then cold-cache steps: a 1 GiB fill before each one evicts
+    # x, the weights and the workspace from L2 and the 256 MiB last-level cache
+    step_ms = step_times(step, max(20, args.steps), torch)
+    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    cold_ms = step_times(step, 10, torch, before=lambda i: scratch.fill_(float(i)))
+    del scratch
+    gpu_state = smi_under_load(step, torch)
+
     totals = r.totals.cpu().tolist()
     kept = r.kept.cpu()
     rows = int(totals[0])
@@ -213,8 +222,55 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
+        "step_ms": step_ms,
+        "cold_step_ms": cold_ms,
+        "gpu_state": gpu_state,
     }
     print(json.dumps(out))
+
+
+def step_times(step, n, torch, before=None):
+    """Median, p10 and p90 (ms) of n single steps, each bracketed by events
+    on the launch stream; `before(i)` runs outside the bracket."""
+    import numpy as np
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    for i, (a, b) in enumerate(ev):
+        if before is not None:
+            before(i)
+        a.record()
+        step()
+        b.record()
+    torch.cuda.synchronize()
+    t = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median": float(np.median(t)), "p10": float(np.percentile(t, 10)),
+            "p90": float(np.percentile(t, 90)), "n": n}
+
+
+def smi_under_load(step, torch, cap_s=8.0):
+    """Socket power and per-XCD shader clocks from `amd-smi metric`, sampled
+    in a child process while steps run back to back; None if unavailable."""
+    import subprocess
+    try:
+        proc = subprocess.Popen(["amd-smi", "metric", "--clock", "--power", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        return None
+    t_end = time.perf_counter() + cap_s
+    while proc.poll() is None and time.perf_counter() < t_end:
+        for _ in range(20):
+            step()
+        torch.cuda.synchronize()
+    try:
+        out, _ = proc.communicate(timeout=max(1.0, t_end - time.perf_counter()))
+        g = json.loads(out)["gpu_data"][0]
+        clk = g["clock"]
+        xcd = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
+        return {"socket_power_w": g["power"]["socket_power"]["value"], "gfx_clk_mhz": xcd,
+                "source": "amd-smi metric --clock --power, sampled while steps ran"}
+    except Exception:
+        proc.kill()
+        return None
 
 
 def cpu_baseline(cfg, L, load, target_s):
