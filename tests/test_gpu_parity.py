@@ -342,6 +342,30 @@ def test_identical_tokens_tied_logits():
     assert out["ref"]["totals"][1] > 0  # capacity exhausted
 
 
+@pytest.mark.parametrize("T", [700, 8192 + 17])
+@pytest.mark.parametrize("E", [8, 16, 32, 48, 64])
+def test_router_classes(T, E):
+    """Every router instantiation (16 or 32 tokens per block, 1-4 expert
+    fragments, ranking groups of 8-64 lanes), with a hidden size of 5 slabs
+    over the 4 waves: logits against the oracle's own, then routing and
+    dispatch bit-exact from the GPU's logits."""
+    cfg = small_cfg(T=T, E=E, k=2, d=320, d_ff=64, cf=1.0)
+    L = Layer(cfg)
+    p = params(cfg)
+    say(f"[case] router class T={T} E={E}")
+    r = moe.Routing(p, DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe.route(p, L.g["x"], L.g["w_router"], L.g["bias"], None, logits, r)
+    R = moe.max_rows(p)
+    xp = torch.empty((max(R, 1), p.d), dtype=torch.bfloat16, device=DEV)
+    moe.dispatch(p, L.g["x"], r, xp, moe.alloc_workspace(p, DEV, dispatch_only=True))
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    own = oracle.router_logits(L.c["x"], L.c["w_router"], L.c["bias"])
+    assert np.abs(own - lg).max() <= 1e-3 * rms(own), "router logits"
+    routing_vs_oracle(p, r.cpu(), lg, None, 0.0)
+
+
 def test_nan_rows_route_and_dispatch():
     """A token row holding a NaN (or both infinities) makes its logits NaN.
     NaN scores rank after every number, so the token still names k+1 experts
