@@ -30,6 +30,9 @@ def parse():
     ap.add_argument("--workload", default="mixtral",
                     choices=["tiny", "mixtral", "fine64", "skew", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the step-time distribution, cold-cache steps and amd-smi sampling "
+                         "(for runs under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for byte counters)")
@@ -145,11 +148,13 @@ def main():
     # distribution of single-step times (events around each step, no sync in
     # between), then cold-cache steps: a 1 GiB fill before each one evicts
     # x, the weights and the workspace from L2 and the 256 MiB last-level cache
-    step_ms = step_times(step, max(20, args.steps), torch)
-    scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
-    cold_ms = step_times(step, 10, torch, before=lambda i: scratch.fill_(float(i)))
-    del scratch
-    gpu_state = smi_under_load(step, torch)
+    step_ms = cold_ms = gpu_state = None
+    if not args.no_extras:
+        step_ms = step_times(step, max(20, args.steps), torch)
+        scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+        cold_ms = step_times(step, 10, torch, before=lambda i: scratch.fill_(float(i)))
+        del scratch
+        gpu_state = smi_under_load(step, torch)
 
     totals = r.totals.cpu().tolist()
     kept = r.kept.cpu()
