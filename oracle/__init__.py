@@ -47,7 +47,7 @@ def lib():
         L.oracle_router_logits.argtypes = [i32, i32, i32, i32, P, P, P, P]
         L.oracle_scores.argtypes = [i32, i32, P, P, f32, P]
         L.oracle_topk.argtypes = [i32, i32, i32, P, P, P]
-        L.oracle_dispatch.argtypes = [i32, i32, i32, i64, i32, f32, P, P] + [P] * 12
+        L.oracle_dispatch.argtypes = [i32, i32, i32, i64, i32, f32, ctypes.c_double, P, P] + [P] * 12
         L.oracle_ffn_rows.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_layer_tokens.argtypes = [i32, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
@@ -128,7 +128,9 @@ def route(raw, k: int, load=None, lam: float = 0.0):
     return topk(s, k + 1)
 
 
-def dispatch(cand, cand_score, E: int, k: int, C: int, reroute: int = 1, aux_coef: float = 0.01) -> dict:
+def dispatch(cand, cand_score, E: int, k: int, C: int, reroute: int = 1, aux_coef: float = 0.01,
+             tau: float = 1.0) -> dict:
+    """Capacity-capped dispatch; gates are the softmax of score / tau over the kept slots."""
     cand = _np(cand).astype(np.int32)
     cs = _np(cand_score).astype(np.float32)
     T = cand.shape[0]
@@ -142,7 +144,7 @@ def dispatch(cand, cand_score, E: int, k: int, C: int, reroute: int = 1, aux_coe
         demand=np.empty(E, np.int32), kept=np.empty(E, np.int32),
         totals=np.empty(3, np.int32), aux_loss=np.empty(1, np.float32),
     )
-    lib().oracle_dispatch(T, E, k, C, int(reroute), float(np.float32(aux_coef)), _p(cand), _p(cs),
+    lib().oracle_dispatch(T, E, k, C, int(reroute), float(np.float32(aux_coef)), float(tau), _p(cand), _p(cs),
                           _p(o["eid"]), _p(o["pos"]), _p(o["flag"]), _p(o["row"]), _p(o["gate"]),
                           _p(o["gate64"]), _p(o["offsets"]), _p(o["token_of_row"]),
                           _p(o["demand"]), _p(o["kept"]), _p(o["totals"]), _p(o["aux_loss"]))

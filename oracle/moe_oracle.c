@@ -161,7 +161,10 @@ void oracle_topk(int T, int E, int K, const float *s, int32_t *cand, float *cand
  *   - rows are packed per expert in arrival order; offsets is the exclusive
  *     scan of the kept counts.
  * Gates: the softmax of the chosen scores renormalised over the kept slots
- * (P2 §3.1 uses softmax probabilities p1, p2); a dropped slot gets 0.
+ * (P2 §3.1 uses softmax probabilities p1, p2); a dropped slot gets 0.  With a
+ * temperature tau > 0 the softmax is taken of score / tau (P3 §3.1, third
+ * step: dividing the scores by a temperature sharpens or flattens the
+ * distribution; the ranking is unchanged, so only the gates depend on it).
  * Load-balancing loss: aux_coef * sum_e (demand[e] / T)^2 with demand the
  * pre-cap rank < k selections (the balance loss of the MoELayer example in P3
  * §4.2, whose usage is normalised by the token count).
@@ -171,7 +174,7 @@ void oracle_topk(int T, int E, int K, const float *s, int32_t *cand, float *cand
  * (double, may be NULL); offsets [E+1]; token_of_row [min(T*k, E*C)] (-1 past
  * the last row); demand, kept [E]; totals = {rows, dropped, rerouted}.
  */
-void oracle_dispatch(int T, int E, int k, int64_t C, int reroute, float aux_coef,
+void oracle_dispatch(int T, int E, int k, int64_t C, int reroute, float aux_coef, double tau,
                      const int32_t *cand, const float *cand_score,
                      int32_t *eid, int32_t *pos, uint8_t *flag, int32_t *row, float *gate,
                      double *gate64, int32_t *offsets, int32_t *token_of_row,
@@ -267,13 +270,13 @@ void oracle_dispatch(int T, int E, int k, int64_t C, int reroute, float aux_coef
         for (int r = 0; r < k; r++) {
             size_t j = (size_t)t * k + r;
             if (flag[j] != 2)
-                z += exp((double)cand_score[(size_t)t * K + src_rank[j]] - m);
+                z += exp(((double)cand_score[(size_t)t * K + src_rank[j]] - m) / tau);
         }
         for (int r = 0; r < k; r++) {
             size_t j = (size_t)t * k + r;
             double g = 0.0;
             if (flag[j] != 2)
-                g = exp((double)cand_score[(size_t)t * K + src_rank[j]] - m) / z;
+                g = exp(((double)cand_score[(size_t)t * K + src_rank[j]] - m) / tau) / z;
             gate[j] = (float)g;
             if (gate64)
                 gate64[j] = g;

@@ -317,6 +317,45 @@ def check_dispatch_invariants(o, T=300, E=6, k=2, C=90, reroute=1, seed=4):
     return d
 
 
+def check_gate_temperature(o):
+    """Gates at temperature tau are the softmax of score / tau over the kept
+    slots ("MoE稀疏激活原理与工程实践" §3.1, third step): the routing does not
+    change with tau, two kept slots have the gate ratio exp((s_a - s_b) / tau),
+    a tiny tau puts the whole gate on the best kept slot and a huge one
+    spreads it evenly."""
+    T, E, k, C = 300, 6, 2, 90
+    r = rng(4)
+    s = (r.standard_normal((T, E)) + np.array([1.5] + [0.0] * (E - 1))).astype(np.float32)
+    cand, cs = o.topk(s, k + 1)
+    base = o.dispatch(cand, cs, E, k, C, 1, 0.01)
+    for tau in (0.5, 4.0, 1e-3, 1e3):
+        d = o.dispatch(cand, cs, E, k, C, 1, 0.01, tau)
+        for n in ("eid", "pos", "flag", "row", "offsets", "token_of_row", "kept", "totals"):
+            assert np.array_equal(d[n], base[n]), (tau, n)
+        for t in range(T):
+            m = d["flag"][t] != 2
+            idx = np.nonzero(m)[0]
+            src = [r_ if d["flag"][t, r_] == 0 else k for r_ in range(k)]
+            sc = np.array([cs[t, src[r_]] for r_ in range(k)], np.float64)
+            if len(idx) == 2:
+                a, b = idx
+                x = (sc[a] - sc[b]) / tau
+                if abs(x) < 500:
+                    assert math.isclose(d["gate64"][t, a] / d["gate64"][t, b], math.exp(x), rel_tol=1e-12)
+            if len(idx):
+                assert abs(d["gate64"][t][m].sum() - 1.0) < 1e-12
+                if tau == 1e3:
+                    assert np.allclose(d["gate64"][t][m], 1.0 / len(idx), atol=2e-3)
+                if tau == 1e-3 and len(idx) == 2 and abs(sc[idx[0]] - sc[idx[1]]) > 0.05:
+                    best = idx[np.argmax(sc[idx])]
+                    assert d["gate64"][t, best] > 1.0 - 1e-12
+    return base
+
+
+def test_gate_temperature(oracle_mod):
+    check_gate_temperature(oracle_mod)
+
+
 def test_dispatch_invariants(oracle_mod):
     d = check_dispatch_invariants(oracle_mod)
     assert d["totals"][2] > 0 and d["totals"][1] > 0  # both re-routes and drops exercised
