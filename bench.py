@@ -104,7 +104,7 @@ def main():
     L = moe_synth.make_layer(cfg, dev)
     p = moe.Params(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff, capacity_factor=cfg.cf,
                    reroute=cfg.reroute, lam=cfg.lam, aux_coef=cfg.aux_coef,
-                   dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32)
+                   dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32, gate_temperature=cfg.tau)
     dt = p.torch_dtype
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     R = moe.max_rows(p)
@@ -294,7 +294,7 @@ def cpu_baseline(cfg, L, load, target_s):
     raw = oracle.router_logits(c["x"], c["w_router"], c["bias"])
     cand, cs = oracle.route(raw, cfg.k, ld, cfg.lam)
     disp = oracle.dispatch(cand, cs, cfg.E, cfg.k, oracle.capacity(T, cfg.k, cfg.E, cfg.cf), cfg.reroute,
-                           cfg.aux_coef)
+                           cfg.aux_coef, cfg.tau if cfg.tau > 0 else 1.0)
     t_route = time.perf_counter() - t0
     # calibrate on one token per oracle thread, then size the sample for about
     # target_s seconds of expert work

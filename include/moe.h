@@ -88,6 +88,12 @@ typedef struct moe_params {
      * (demand[e]/T)^2 ("MoE稀疏激活原理与工程实践" §4.2, coefficient 0.01). */
     float aux_coef;
     int32_t dtype; /* moe_dtype */
+    /* gate temperature tau: the gates are the softmax of score / tau over the
+     * kept slots ("MoE稀疏激活原理与工程实践" §3.1, third step: a smaller tau
+     * sharpens the distribution, a larger one flattens it).  The ranking and
+     * every routing decision are independent of tau.  0 means 1 (the plain
+     * softmax); a negative, NaN or infinite value is MOE_ERR_INVALID_ARG. */
+    float gate_temperature;
 } moe_params;
 
 /*

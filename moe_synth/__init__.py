@@ -119,6 +119,7 @@ class MoEConfig:
     load_from_prev: bool = False    # load vector = previous batch's kept fraction
     reroute: int = 1
     aux_coef: float = 0.01
+    tau: float = 0.0                # gate temperature (0: plain softmax)
     note: str = ""
     extra: dict = field(default_factory=dict)
 

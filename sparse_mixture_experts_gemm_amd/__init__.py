@@ -33,7 +33,8 @@ class MoeParams(ctypes.Structure):
     _fields_ = [("T", ctypes.c_int32), ("d", ctypes.c_int32), ("E", ctypes.c_int32),
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_float), ("reroute", ctypes.c_int32),
-                ("lam", ctypes.c_float), ("aux_coef", ctypes.c_float), ("dtype", ctypes.c_int32)]
+                ("lam", ctypes.c_float), ("aux_coef", ctypes.c_float), ("dtype", ctypes.c_int32),
+                ("gate_temperature", ctypes.c_float)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -94,10 +95,11 @@ class Params:
     lam: float = 0.0
     aux_coef: float = 0.01
     dtype: int = MOE_BF16
+    gate_temperature: float = 0.0  # 0: plain softmax gates
 
     def c(self) -> MoeParams:
         return MoeParams(self.T, self.d, self.E, self.k, self.d_ff, self.capacity_factor,
-                         self.reroute, self.lam, self.aux_coef, self.dtype)
+                         self.reroute, self.lam, self.aux_coef, self.dtype, self.gate_temperature)
 
     @property
     def torch_dtype(self):

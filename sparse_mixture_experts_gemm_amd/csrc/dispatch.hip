@@ -8,7 +8,9 @@
 //   1, ..., then one fallback round in token order.  A request is kept while
 //   its expert holds fewer than C rows.  A token with an overflowed slot sends
 //   its lowest overflowed slot to its rank-k candidate; further overflowed
-//   slots are dropped.  Gates are the softmax of the kept slots' scores.
+//   slots are dropped.  Gates are the softmax of the kept slots' scores,
+//   divided by the gate temperature ("MoE稀疏激活原理与工程实践" §3.1,
+//   third step; 1 when the parameter is 0).
 //
 // Because a primary request's queue position depends only on how many earlier
 // requests chose the same expert, positions are counting problems: per-block
@@ -214,7 +216,7 @@ struct FinalizeLds {
 
 __device__ __forceinline__ void finalize_body(
     int b, const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k,
-    int C, int nb, int use_fallback, float aux_coef, int cap_rows, const int32_t *__restrict__ hist,
+    int C, int nb, int use_fallback, float aux_coef, float tau, int cap_rows, const int32_t *__restrict__ hist,
     const int32_t *__restrict__ fill_prim, const int32_t *__restrict__ fb_hist,
     int32_t *__restrict__ eid, int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
     int32_t *__restrict__ row, float *__restrict__ gate, int32_t *__restrict__ offsets,
@@ -289,7 +291,7 @@ __device__ __forceinline__ void finalize_body(
         }
         float z = 0.0f;
         for (int r = 0; r < k; r++)
-            if (f_s[r] != 2) z += expf(sc[r] - m);
+            if (f_s[r] != 2) z += expf((sc[r] - m) / tau);
         for (int r = 0; r < k; r++) {
             const size_t j = (size_t)t * k + r;
             if (f_s[r] == 2) {
@@ -299,7 +301,7 @@ __device__ __forceinline__ void finalize_body(
                 const int rw = offs[e_s[r]] + p_s[r];
                 row[j] = rw;
                 token_of_row[rw] = t;
-                gate[j] = expf(sc[r] - m) / z;
+                gate[j] = expf((sc[r] - m) / tau) / z;
             }
         }
     }
@@ -336,14 +338,14 @@ __device__ __forceinline__ void finalize_body(
 
 __global__ __launch_bounds__(kThreads) void dispatch_finalize(
     const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k,
-    int C, int nb, int use_fallback, float aux_coef, int cap_rows, const int32_t *__restrict__ hist,
+    int C, int nb, int use_fallback, float aux_coef, float tau, int cap_rows, const int32_t *__restrict__ hist,
     const int32_t *__restrict__ fill_prim, const int32_t *__restrict__ fb_hist,
     int32_t *__restrict__ eid, int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
     int32_t *__restrict__ row, float *__restrict__ gate, int32_t *__restrict__ offsets,
     int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand, int32_t *__restrict__ kept,
     int32_t *__restrict__ totals, float *__restrict__ aux_loss) {
     __shared__ FinalizeLds sm;
-    finalize_body(blockIdx.x, cand, cand_score, T, E, k, C, nb, use_fallback, aux_coef, cap_rows, hist, fill_prim,
+    finalize_body(blockIdx.x, cand, cand_score, T, E, k, C, nb, use_fallback, aux_coef, tau, cap_rows, hist, fill_prim,
                   fb_hist, eid, pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm);
 }
 
@@ -353,7 +355,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_finalize(
 // as between the three kernels.  The block's barriers order the phases.
 __global__ __launch_bounds__(kThreads) void dispatch_single(
     const int32_t *__restrict__ cand, const float *__restrict__ cand_score, int T, int E, int k, int C,
-    int use_fallback, float aux_coef, int cap_rows, int32_t *__restrict__ hist, int32_t *__restrict__ fill_prim,
+    int use_fallback, float aux_coef, float tau, int cap_rows, int32_t *__restrict__ hist, int32_t *__restrict__ fill_prim,
     int32_t *__restrict__ fb_hist, int32_t *__restrict__ eid, int32_t *__restrict__ pos,
     uint8_t *__restrict__ flag, int32_t *__restrict__ row, float *__restrict__ gate,
     int32_t *__restrict__ offsets, int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand,
@@ -377,7 +379,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_single(
     primary_body(0, cand, T, E, k, C, 1, use_fallback, hist_l, fill_l, eid, pos, flag, fb_l, sm.p);
     __threadfence_block();
     __syncthreads();
-    finalize_body(0, cand, cand_score, T, E, k, C, 1, use_fallback, aux_coef, cap_rows, hist_l, fill_l, fb_l, eid,
+    finalize_body(0, cand, cand_score, T, E, k, C, 1, use_fallback, aux_coef, tau, cap_rows, hist_l, fill_l, fb_l, eid,
                   pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm.f);
 }
 
@@ -402,11 +404,12 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
     const int T = p.T, E = p.E, k = p.k;
     const int nb = (int)ceil_div(T > 0 ? T : 1, kThreads);
     const int use_fb = (p.reroute && k < E) ? 1 : 0;
+    const float tau = p.gate_temperature > 0.0f ? p.gate_temperature : 1.0f;  // 0: plain softmax
     int64_t cap_rows = (int64_t)T * k;
     if ((int64_t)E * C < cap_rows) cap_rows = (int64_t)E * C;
     if (nb == 1) {
         hipLaunchKernelGGL(dispatch_single, dim3(1), dim3(kThreads), 0, st, r.cand, r.cand_score, T, E, k,
-                           (int)C, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim, ws.fb_hist, r.eid,
+                           (int)C, use_fb, p.aux_coef, tau, (int)cap_rows, ws.hist, ws.fill_prim, ws.fb_hist, r.eid,
                            r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row, r.demand, r.kept, r.totals,
                            r.aux_loss, ws.claim);
     } else {
@@ -414,7 +417,7 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
         hipLaunchKernelGGL(dispatch_primary, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, (int)C,
                            nb, use_fb, ws.hist, ws.fill_prim, r.eid, r.pos, r.flag, ws.fb_hist);
         hipLaunchKernelGGL(dispatch_finalize, dim3(nb), dim3(kThreads), 0, st, r.cand, r.cand_score, T,
-                           E, k, (int)C, nb, use_fb, p.aux_coef, (int)cap_rows, ws.hist, ws.fill_prim,
+                           E, k, (int)C, nb, use_fb, p.aux_coef, tau, (int)cap_rows, ws.hist, ws.fill_prim,
                            ws.fb_hist, r.eid, r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row,
                            r.demand, r.kept, r.totals, r.aux_loss);
     }

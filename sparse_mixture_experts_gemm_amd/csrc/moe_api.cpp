@@ -24,6 +24,7 @@ int check_params(const moe_params *p) {
     // one expert's weight matrix is addressed with 32-bit byte offsets
     if ((int64_t)p->d * p->d_ff * (p->dtype == MOE_BF16 ? 2 : 4) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
     if (!(p->lambda == p->lambda) || !(p->capacity_factor == p->capacity_factor)) return MOE_ERR_INVALID_ARG;
+    if (!(p->gate_temperature >= 0.0f) || isinf(p->gate_temperature)) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 

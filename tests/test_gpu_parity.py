@@ -89,7 +89,7 @@ def assert_close_elementwise(got, ref, rel, floor, what):
 def params(cfg, T=None, **over):
     kw = dict(T=cfg.T if T is None else T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff,
               capacity_factor=cfg.cf, reroute=cfg.reroute, lam=cfg.lam, aux_coef=cfg.aux_coef,
-              dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32)
+              dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32, gate_temperature=cfg.tau)
     kw.update(over)
     return moe.Params(**kw)
 
@@ -109,7 +109,8 @@ def routing_vs_oracle(p, rc, logits_np, load_np, lam, nan_gates=False):
     """Oracle routing from the GPU's logits; every array bit-exact."""
     cand, cs = oracle.route(logits_np, p.k, load_np, lam)
     C = oracle.capacity(p.T, p.k, p.E, p.capacity_factor)
-    ref = oracle.dispatch(cand, cs, p.E, p.k, C, p.reroute, p.aux_coef)
+    ref = oracle.dispatch(cand, cs, p.E, p.k, C, p.reroute, p.aux_coef,
+                          p.gate_temperature if p.gate_temperature > 0 else 1.0)
     ref["cand"], ref["cand_score"] = cand, cs
     for n in ROUTING_EXACT:
         a = rc[n].numpy()
@@ -299,6 +300,9 @@ EDGE = {
     "experts_32_blocks_of_32": dict(T=8200, E=32, k=4, d=128, d_ff=64),
     "experts_40_odd_slabs": dict(T=650, E=40, k=3, d=320, d_ff=128),
     "min_dims_bf16": dict(T=77, d=64, d_ff=64, E=3, k=1),
+    # gate temperature: sharper and flatter gates, routing unchanged
+    "gate_temperature_sharp": dict(T=600, E=8, k=2, cf=0.8, tau=0.25),
+    "gate_temperature_flat": dict(T=600, E=8, k=3, cf=0.8, tau=3.0),
 }
 
 
