@@ -81,11 +81,29 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
                                           TileInfo &ti) {
     const int lane = lane_id();
     const int e0 = lane * 4;
+    const int xcd = blk & 7, local = blk >> 3;
+    // The claim of this XCD's next item is issued first, so that its round
+    // trip overlaps the reads of the offsets (whether it is in range is
+    // known only once the item count is).  The counter's address goes
+    // through an opaque zero held in a VGPR: for an address it knows to be
+    // uniform the compiler combines the lanes' adds and waits for the result
+    // on the spot, which would serialise the two round trips again.
+    int first = 0;
+    if (claim && threadIdx.x == 0) {
+        int vzero;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
+        first = atomicAdd(claim + xcd + vzero, 1);
+    }
+    // offsets[e0 .. e0 + 4], clamped to offsets[E]: five independent loads
+    // in flight together (a load per expert under a branch each would wait
+    // for each one in turn)
+    int ofs[5];
+#pragma unroll
+    for (int j = 0; j < 5; j++) ofs[j] = offsets[min(e0 + j, E)];
     int mts[4], c = 0;
 #pragma unroll
     for (int j = 0; j < 4; j++) {
-        const int e = e0 + j;
-        mts[j] = e < E ? (offsets[e + 1] - offsets[e] + bm - 1) / bm : 0;
+        mts[j] = (ofs[j + 1] - ofs[j] + bm - 1) / bm;  // 0 past E (both ends clamp to E)
         c += mts[j];
     }
     int incl = c;  // inclusive prefix of m tiles over lanes
@@ -96,7 +114,6 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
     }
     const int per = ntiles_n * splits;  // work items per m tile
     const int total = __builtin_amdgcn_readlane(incl, 63) * per;
-    const int xcd = blk & 7, local = blk >> 3;
     const int q = total >> 3, r = total & 7;
     int L;
     if (claim) {
@@ -104,7 +121,7 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
             int item = -1;
             for (int s = 0; s < 8; s++) {
                 const int y = (xcd + s) & 7;
-                const int i = atomicAdd(&claim[y], 1);
+                const int i = s == 0 ? first : atomicAdd(&claim[y], 1);
                 if (i < q + (y < r ? 1 : 0)) {
                     item = y * q + min(y, r) + i;
                     break;
