@@ -308,7 +308,16 @@ def cpu_baseline(cfg, L, load, target_s):
     oracle.layer_tokens(toks, c["x"], c["w1"], c["w3"], c["w2"], disp["eid"], disp["gate64"])
     t_ffn = time.perf_counter() - t2
     per_token_s = t_ffn / n2 + t_route / T
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "cpu_model": cpu_model,
             "sample": f"router logits + ranking + dispatch for all {T} tokens ({t_route:.2f} s), "
                       f"expert FFN + combine for {n2} tokens ({t_ffn:.2f} s); rate per token"}
 
