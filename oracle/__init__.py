@@ -47,11 +47,12 @@ def lib():
         L.oracle_router_logits.argtypes = [i32, i32, i32, i32, P, P, P, P]
         L.oracle_scores.argtypes = [i32, i32, P, P, f32, P]
         L.oracle_topk.argtypes = [i32, i32, i32, P, P, P]
+        L.oracle_gap_swap.argtypes = [i32, i32, f32, P, P]
         L.oracle_dispatch.argtypes = [i32, i32, i32, i64, i32, f32, ctypes.c_double, P, P] + [P] * 12
         L.oracle_ffn_rows.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_layer_tokens.argtypes = [i32, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
-        for f in (L.oracle_router_logits, L.oracle_scores, L.oracle_topk, L.oracle_dispatch,
+        for f in (L.oracle_router_logits, L.oracle_scores, L.oracle_topk, L.oracle_gap_swap, L.oracle_dispatch,
                   L.oracle_ffn_rows, L.oracle_layer_tokens, L.oracle_combine):
             f.restype = None
         _lib = L
@@ -122,10 +123,23 @@ def topk(s, K: int):
     return cand, cs
 
 
-def route(raw, k: int, load=None, lam: float = 0.0):
-    """Scores and top-(k+1) candidates from fp32 router logits."""
+def gap_swap(cand, cand_score, delta: float):
+    """Top-2 gap threshold: ranks 1 and 2 swapped where s[0] - s[1] < delta (fp32)."""
+    cand = np.ascontiguousarray(_np(cand).astype(np.int32))
+    cs = np.ascontiguousarray(_np(cand_score).astype(np.float32))
+    T, K = cand.shape
+    lib().oracle_gap_swap(T, K, float(np.float32(delta)), _p(cand), _p(cs))
+    return cand, cs
+
+
+def route(raw, k: int, load=None, lam: float = 0.0, gap: float = 0.0):
+    """Scores and top-(k+1) candidates from fp32 router logits, then the
+    top-2 gap threshold when gap > 0."""
     s = scores(raw, load, lam)
-    return topk(s, k + 1)
+    cand, cs = topk(s, k + 1)
+    if gap > 0:
+        cand, cs = gap_swap(cand, cs, gap)
+    return cand, cs
 
 
 def dispatch(cand, cand_score, E: int, k: int, C: int, reroute: int = 1, aux_coef: float = 0.01,

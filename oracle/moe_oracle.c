@@ -147,6 +147,36 @@ void oracle_topk(int T, int E, int K, const float *s, int32_t *cand, float *cand
 }
 
 /*
+ * Top-2 gap threshold (the adg.csdn.net page, §3.1: when the best and the
+ * second-best score differ by less than a threshold, the second choice is
+ * replaced by the third-ranked expert, so that the two experts are clearly
+ * distinct).  Readings: the gap is taken on the ranking scores s (the fp32
+ * difference s[rank 0] - s[rank 1], compared in fp32); the replacement swaps
+ * ranks 1 and 2, so the displaced expert becomes the fallback candidate and
+ * the list stays a permutation of the top K.  It applies only with a third
+ * candidate that names an expert (K >= 3, cand[2] >= 0), and delta <= 0 turns
+ * it off.  A NaN gap is not below delta.
+ */
+void oracle_gap_swap(int T, int K, float delta, int32_t *cand, float *cand_score)
+{
+    if (!(delta > 0.0f) || K < 3)
+        return;
+    for (int t = 0; t < T; t++) {
+        int32_t *c = cand + (size_t)t * K;
+        float *cs = cand_score + (size_t)t * K;
+        const float gap = cs[0] - cs[1];
+        if (c[2] >= 0 && gap < delta) {
+            const int32_t ce = c[1];
+            const float sc = cs[1];
+            c[1] = c[2];
+            cs[1] = cs[2];
+            c[2] = ce;
+            cs[2] = sc;
+        }
+    }
+}
+
+/*
  * Capacity-capped dispatch.
  *
  * Queue semantics (P1 §2.3: an expert whose queue has reached the limit sends

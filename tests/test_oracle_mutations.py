@@ -32,13 +32,15 @@ MUTATIONS = {
     "bias_dropped": ("r = r + bias[e];", "r = r;"),
     "gate_uses_primary_score": ("                src_rank[j] = k;\n", ""),
     "temperature_left_out_of_numerator": ("- m) / tau) / z;", "- m)) / z;"),
+    "gap_taken_below_second": ("const float gap = cs[0] - cs[1];", "const float gap = cs[1] - cs[2];"),
+    "gap_swap_drops_displaced": ("            c[2] = ce;\n", ""),
     "router_weight_transposed": ("elem(wr, (size_t)e * d + i, dt)", "elem(wr, (size_t)i * E + e, dt)"),
 }
 
 CHECKS = [
     pins.check_capacity, pins.check_router_logits, pins.check_scores, pins.check_topk,
     pins.check_dispatch_exhaustive, pins.check_dispatch_invariants, pins.check_aux_loss,
-    pins.check_gate_temperature,
+    pins.check_gate_temperature, pins.check_gap_swap,
     lambda o: pins.check_dense_equivalence(o, "f32"), pins.check_identical_experts,
     pins.check_expert_relabel,
 ]

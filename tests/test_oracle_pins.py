@@ -352,6 +352,45 @@ def check_gate_temperature(o):
     return base
 
 
+def check_gap_swap(o):
+    """Top-2 gap threshold (the adg.csdn.net page, §3.1): where the best two
+    scores differ by less than delta, ranks 1 and 2 trade places (the second
+    choice becomes the third-ranked expert); elsewhere the list is the plain
+    ranking.  A printed-style example, then random rows checked one by one
+    against the definition written out in fp32."""
+    # best two within the threshold: 0.49 vs 0.48 (gap 0.01 < 0.05)
+    s = np.array([[0.48, 0.10, 0.49, 0.30], [0.90, 0.48, 0.20, 0.10]], np.float32)
+    cand, cs = o.topk(s, 3)
+    c2, cs2 = o.gap_swap(cand, cs, 0.05)
+    assert c2[0].tolist() == [2, 3, 0] and np.array_equal(cs2[0], np.float32([0.49, 0.30, 0.48]))
+    assert c2[1].tolist() == cand[1].tolist()  # gap 0.42: unchanged
+    assert np.array_equal(o.gap_swap(cand, cs, 0.0)[0], cand)  # off
+    r = rng(9)
+    T, E, K = 2000, 6, 3
+    s = (r.standard_normal((T, E)) * 0.1).astype(np.float32)
+    cand, cs = o.topk(s, K)
+    delta = np.float32(0.05)
+    c2, cs2 = o.gap_swap(cand, cs, delta)
+    n_swapped = 0
+    for t in range(T):
+        if np.float32(cs[t, 0] - cs[t, 1]) < delta:
+            n_swapped += 1
+            assert c2[t].tolist() == [cand[t, 0], cand[t, 2], cand[t, 1]]
+            assert np.array_equal(cs2[t], cs[t][[0, 2, 1]])
+        else:
+            assert np.array_equal(c2[t], cand[t]) and np.array_equal(cs2[t], cs[t])
+    assert 0 < n_swapped < T
+    # k = 1 (two columns) and a missing third candidate (E = 2): never swapped
+    c1, s1 = o.topk(s[:, :2], 2)
+    assert np.array_equal(o.gap_swap(c1, s1, 10.0)[0], c1)
+    c3, s3 = o.topk(s[:, :2], 3)
+    assert np.array_equal(o.gap_swap(c3, s3, 10.0)[0], c3)
+
+
+def test_gap_swap(oracle_mod):
+    check_gap_swap(oracle_mod)
+
+
 def test_gate_temperature(oracle_mod):
     check_gate_temperature(oracle_mod)
 
