@@ -104,7 +104,8 @@ def main():
     L = moe_synth.make_layer(cfg, dev)
     p = moe.Params(T=cfg.T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff, capacity_factor=cfg.cf,
                    reroute=cfg.reroute, lam=cfg.lam, aux_coef=cfg.aux_coef,
-                   dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32, gate_temperature=cfg.tau)
+                   dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32, gate_temperature=cfg.tau,
+                   top2_gap=cfg.gap)
     dt = p.torch_dtype
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     R = moe.max_rows(p)
@@ -292,7 +293,7 @@ def cpu_baseline(cfg, L, load, target_s):
     T = cfg.T
     t0 = time.perf_counter()
     raw = oracle.router_logits(c["x"], c["w_router"], c["bias"])
-    cand, cs = oracle.route(raw, cfg.k, ld, cfg.lam)
+    cand, cs = oracle.route(raw, cfg.k, ld, cfg.lam, cfg.gap)
     disp = oracle.dispatch(cand, cs, cfg.E, cfg.k, oracle.capacity(T, cfg.k, cfg.E, cfg.cf), cfg.reroute,
                            cfg.aux_coef, cfg.tau if cfg.tau > 0 else 1.0)
     t_route = time.perf_counter() - t0

@@ -94,6 +94,14 @@ typedef struct moe_params {
      * every routing decision are independent of tau.  0 means 1 (the plain
      * softmax); a negative, NaN or infinite value is MOE_ERR_INVALID_ARG. */
     float gate_temperature;
+    /* top-2 gap threshold delta: where the best two ranking scores differ by
+     * less than delta (their fp32 difference), the second choice is replaced
+     * by the third-ranked expert (the adg.csdn.net page, §3.1): ranks 1 and 2
+     * of cand / cand_score trade places, the displaced expert becoming the
+     * fallback candidate.  Applies when k + 1 >= 3 and the third candidate
+     * names an expert.  0 turns it off; a negative, NaN or infinite value is
+     * MOE_ERR_INVALID_ARG. */
+    float top2_gap;
 } moe_params;
 
 /*
@@ -104,7 +112,8 @@ typedef struct moe_params {
  */
 typedef struct moe_routing {
     int32_t *cand;       /* [T][K1] experts by (score desc, index asc), NaN scores
-                          *         after every number; -1 past E               */
+                          *         after every number (ranks 1-2 swapped under
+                          *         the top-2 gap threshold); -1 past E         */
     float *cand_score;   /* [T][K1] penalised fp32 scores; -inf past E              */
     int32_t *eid;        /* [T][k]  final expert of slot j, -1 when dropped         */
     int32_t *pos;        /* [T][k]  position in that expert's queue, -1 if dropped  */

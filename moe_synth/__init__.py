@@ -120,6 +120,7 @@ class MoEConfig:
     reroute: int = 1
     aux_coef: float = 0.01
     tau: float = 0.0                # gate temperature (0: plain softmax)
+    gap: float = 0.0                # top-2 gap threshold (0: off)
     note: str = ""
     extra: dict = field(default_factory=dict)
 

@@ -34,7 +34,7 @@ class MoeParams(ctypes.Structure):
                 ("k", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("capacity_factor", ctypes.c_float), ("reroute", ctypes.c_int32),
                 ("lam", ctypes.c_float), ("aux_coef", ctypes.c_float), ("dtype", ctypes.c_int32),
-                ("gate_temperature", ctypes.c_float)]
+                ("gate_temperature", ctypes.c_float), ("top2_gap", ctypes.c_float)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -96,10 +96,12 @@ class Params:
     aux_coef: float = 0.01
     dtype: int = MOE_BF16
     gate_temperature: float = 0.0  # 0: plain softmax gates
+    top2_gap: float = 0.0          # 0: no top-2 gap threshold
 
     def c(self) -> MoeParams:
         return MoeParams(self.T, self.d, self.E, self.k, self.d_ff, self.capacity_factor,
-                         self.reroute, self.lam, self.aux_coef, self.dtype, self.gate_temperature)
+                         self.reroute, self.lam, self.aux_coef, self.dtype, self.gate_temperature,
+                         self.top2_gap)
 
     @property
     def torch_dtype(self):

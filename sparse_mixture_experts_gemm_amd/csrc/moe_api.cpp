@@ -25,6 +25,7 @@ int check_params(const moe_params *p) {
     if ((int64_t)p->d * p->d_ff * (p->dtype == MOE_BF16 ? 2 : 4) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
     if (!(p->lambda == p->lambda) || !(p->capacity_factor == p->capacity_factor)) return MOE_ERR_INVALID_ARG;
     if (!(p->gate_temperature >= 0.0f) || isinf(p->gate_temperature)) return MOE_ERR_INVALID_ARG;
+    if (!(p->top2_gap >= 0.0f) || isinf(p->top2_gap)) return MOE_ERR_INVALID_ARG;
     return MOE_OK;
 }
 

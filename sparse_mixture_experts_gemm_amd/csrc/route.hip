@@ -3,7 +3,9 @@
 // What it computes ("MoE架构揭秘" §3.1; "GPT-4稀疏激活真相" §2.3):
 //   raw[t][e] = sum_i x[t][i] * Wr[e][i] + bias[e]
 //   s[t][e]   = fmaf(-lambda, load[e], raw[t][e])      (raw when load == NULL)
-//   cand[t]   = the k+1 experts with the largest s, ties to the lower index.
+//   cand[t]   = the k+1 experts with the largest s, ties to the lower index;
+//               with the top-2 gap threshold, ranks 1 and 2 swapped where
+//               s[rank 0] - s[rank 1] < gap (the adg.csdn.net page, §3.1).
 //
 // Mapping on CDNA4.  The router is a skinny GEMM (N = E is 1..256) and one
 // pass over x.  bf16 layers with E <= 64 run it on the matrix cores
@@ -132,6 +134,53 @@ __device__ __forceinline__ uint64_t max_step(uint64_t v) {
     }
 }
 
+// Write-out of one token's ranked candidates with the top-2 gap threshold
+// (the adg.csdn.net page, §3.1): ranks 0-2 are held until the third is known;
+// where the best two scores differ by less than `gap` (their fp32
+// difference) and the third candidate names an expert, ranks 1 and 2 trade
+// places, so the second choice is the third-ranked expert and the displaced
+// one becomes the fallback.  gap <= 0 leaves the ranking as it is.  All lanes
+// hold the same values; only `writer` stores.
+struct RankOut {
+    int c0 = -1, c1 = -1, c2 = -1;
+    float s0 = -INFINITY, s1 = -INFINITY, s2 = -INFINITY;
+    __device__ __forceinline__ void put(int r, int c, float sc, int32_t *cand_t, float *cs_t, bool writer) {
+        if (r == 0) {
+            c0 = c;
+            s0 = sc;
+        } else if (r == 1) {
+            c1 = c;
+            s1 = sc;
+        } else if (r == 2) {
+            c2 = c;
+            s2 = sc;
+        } else if (writer) {
+            cand_t[r] = c;
+            cs_t[r] = sc;
+        }
+    }
+    __device__ __forceinline__ void flush(int K1, float gap, int32_t *cand_t, float *cs_t, bool writer) {
+        if (gap > 0.0f && K1 >= 3 && c2 >= 0 && s0 - s1 < gap) {
+            const int c = c1;
+            const float sc = s1;
+            c1 = c2;
+            s1 = s2;
+            c2 = c;
+            s2 = sc;
+        }
+        if (writer) {
+            cand_t[0] = c0;
+            cs_t[0] = s0;
+            cand_t[1] = c1;  // K1 >= 2 (k >= 1)
+            cs_t[1] = s1;
+            if (K1 >= 3) {
+                cand_t[2] = c2;
+                cs_t[2] = s2;
+            }
+        }
+    }
+};
+
 typedef __attribute__((address_space(3))) char lds_char_t;
 typedef const __attribute__((address_space(1))) char gbl_char_t;
 
@@ -214,7 +263,7 @@ __device__ __forceinline__ void route_chunk(const uint4 *w_lds, const uint4 (&xr
 template <typename TIn, int NX, int TPW, int NB, int EA, int EMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wr, const float *__restrict__ bias,
-    const float *__restrict__ load, float neg_lambda, int T, int d, int E, int K1, int EC,
+    const float *__restrict__ load, float neg_lambda, float gap, int T, int d, int E, int K1, int EC,
     float *__restrict__ logits, int32_t *__restrict__ cand, float *__restrict__ cand_score) {
     constexpr int kVec = ChunkDot<TIn>::kVec;
     // two distinct objects, so the compiler sees that the loads into one
@@ -287,6 +336,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
                 key[i] = rank_key(sc[i], e);
             }
         }
+        RankOut ro;
         for (int r = 0; r < K1; r++) {
             uint64_t m = key[0];
 #pragma unroll
@@ -304,14 +354,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
 #pragma unroll
             for (int i = 1; i < PL; i++) s = (e >> 6) == i ? sc[i] : s;
             s = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(s), e & 63));
-            if (lane == 0) {
-                cand[(size_t)t * K1 + r] = none ? -1 : e;
-                cand_score[(size_t)t * K1 + r] = none ? -INFINITY : s;
-            }
+            ro.put(r, none ? -1 : e, none ? -INFINITY : s, cand + (size_t)t * K1, cand_score + (size_t)t * K1,
+                   lane == 0);
 #pragma unroll
             for (int i = 0; i < PL; i++)
                 if (!none && (e & 63) == lane && (e >> 6) == i) key[i] = 0;
         }
+        ro.flush(K1, gap, cand + (size_t)t * K1, cand_score + (size_t)t * K1, lane == 0);
     }
 }
 
@@ -326,7 +375,8 @@ hipError_t launch_k(const moe_params &p, const void *x, const void *wr, const fl
     const int grid = (int)ceil_div(p.T, tokens_per_block);
 #define MOE_ROUTE_LAUNCH(NB)                                                                                  \
     hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, NB, EA, EMAX>), dim3(grid), dim3(kRouteThreads), 0, st,    \
-                       static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load, -p.lambda, p.T, \
+                       static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load, -p.lambda,    \
+                       p.top2_gap, p.T,                                                                      \
                        p.d, p.E, p.k + 1, ec, logits, cand, cand_score)
     if (ec >= p.E) MOE_ROUTE_LAUNCH(1);
     else MOE_ROUTE_LAUNCH(2);
@@ -399,8 +449,8 @@ __device__ __forceinline__ void rt_buf2lds(__amdgpu_buffer_rsrc_t r, uint32_t vo
 template <int NT, int NE, int P, int G>
 __global__ __launch_bounds__(kRmThreads) void route_mfma(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, const float *__restrict__ bias,
-    const float *__restrict__ load, float neg_lambda, int T, int d, int E, int K1, float *__restrict__ logits,
-    int32_t *__restrict__ cand, float *__restrict__ cand_score) {
+    const float *__restrict__ load, float neg_lambda, float gap, int T, int d, int E, int K1,
+    float *__restrict__ logits, int32_t *__restrict__ cand, float *__restrict__ cand_score) {
     constexpr int BT = 16 * NT, EP = 16 * NE, TPP = 64 / G;
     constexpr int kXG = BT / 8, kWG = EP / 8, L = kXG + kWG;  // 1 KiB loads per slab
     constexpr int kSlot = L * 1024;                           // one wave's slab
@@ -523,6 +573,9 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
         const int t = base + lane / G;  // < BT
         const bool ok = t < nt && e < E;
         uint64_t key = ok ? rank_key(part[0][t][e], e) : 0;
+        const size_t to = (size_t)(t0 + min(t, nt - 1)) * K1;  // this group's token's candidate row
+        const bool writer = e == 0 && t < nt;
+        RankOut ro;
         for (int r = 0; r < K1; r++) {
             uint64_t m = max_step<1>(key);
             m = max_step<2>(m);
@@ -533,12 +586,10 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
             const bool none = m == 0;
             const int we = none ? 0 : (int)~(uint32_t)m;  // the group's winner
             const float sw = part[0][t][we];               // its own score bits
-            if (e == 0 && t < nt) {
-                cand[(size_t)(t0 + t) * K1 + r] = none ? -1 : we;
-                cand_score[(size_t)(t0 + t) * K1 + r] = none ? -INFINITY : sw;
-            }
+            ro.put(r, none ? -1 : we, none ? -INFINITY : sw, cand + to, cand_score + to, writer);
             if (!none && e == we) key = 0;
         }
+        ro.flush(K1, gap, cand + to, cand_score + to, writer);
     }
 }
 
@@ -552,7 +603,7 @@ hipError_t launch_mfma_g(const moe_params &p, const void *x, const void *wr, con
     const int grid = (int)ceil_div(p.T, 16 * NT);
     hipLaunchKernelGGL((route_mfma<NT, NE, P, G>), dim3(grid), dim3(kRmThreads), 0, st,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wr), bias, load, -p.lambda,
-                       p.T, p.d, p.E, p.k + 1, logits, cand, cand_score);
+                       p.top2_gap, p.T, p.d, p.E, p.k + 1, logits, cand, cand_score);
     return hipGetLastError();
 }
 

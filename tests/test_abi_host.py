@@ -65,7 +65,8 @@ def test_workspace_sizes_cover_buffers():
 
 @pytest.mark.parametrize("bad", [dict(E=0), dict(E=257), dict(k=0), dict(k=9, E=16), dict(k=3, E=2),
                                  dict(T=-1), dict(T=(1 << 20) + 1), dict(d=0), dict(gate_temperature=-0.5),
-                                 dict(gate_temperature=float("nan")), dict(gate_temperature=float("inf"))])
+                                 dict(gate_temperature=float("nan")), dict(gate_temperature=float("inf")),
+                                 dict(top2_gap=-0.1), dict(top2_gap=float("nan")), dict(top2_gap=float("inf"))])
 def test_invalid_sizes_rejected(bad):
     p = P(**bad)
     assert moe.capacity(p) == -1

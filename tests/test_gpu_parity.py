@@ -89,7 +89,8 @@ def assert_close_elementwise(got, ref, rel, floor, what):
 def params(cfg, T=None, **over):
     kw = dict(T=cfg.T if T is None else T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff,
               capacity_factor=cfg.cf, reroute=cfg.reroute, lam=cfg.lam, aux_coef=cfg.aux_coef,
-              dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32, gate_temperature=cfg.tau)
+              dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32, gate_temperature=cfg.tau,
+              top2_gap=cfg.gap)
     kw.update(over)
     return moe.Params(**kw)
 
@@ -107,7 +108,7 @@ def load_for(cfg, L, T):
 
 def routing_vs_oracle(p, rc, logits_np, load_np, lam, nan_gates=False):
     """Oracle routing from the GPU's logits; every array bit-exact."""
-    cand, cs = oracle.route(logits_np, p.k, load_np, lam)
+    cand, cs = oracle.route(logits_np, p.k, load_np, lam, p.top2_gap)
     C = oracle.capacity(p.T, p.k, p.E, p.capacity_factor)
     ref = oracle.dispatch(cand, cs, p.E, p.k, C, p.reroute, p.aux_coef,
                           p.gate_temperature if p.gate_temperature > 0 else 1.0)
@@ -185,7 +186,7 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
     own = oracle.router_logits(L.c["x"][tok], L.c["w_router"], L.c["bias"])
     assert np.abs(own - gl[tok]).max() <= 1e-3 * rms(own), "router logits"
     rc = r.cpu()
-    cand, cs = oracle.route(gl, k, L.load, p.lam)
+    cand, cs = oracle.route(gl, k, L.load, p.lam, p.top2_gap)
     assert np.array_equal(rc["cand"].numpy(), cand), "cand"
     assert np.array_equal(rc["cand_score"].numpy().view(np.uint32), cs.view(np.uint32)), "cand_score"
 
@@ -303,6 +304,11 @@ EDGE = {
     # gate temperature: sharper and flatter gates, routing unchanged
     "gate_temperature_sharp": dict(T=600, E=8, k=2, cf=0.8, tau=0.25),
     "gate_temperature_flat": dict(T=600, E=8, k=3, cf=0.8, tau=3.0),
+    # top-2 gap threshold: MFMA router (E 8, E 64), VALU router (fp32; E 100)
+    "top2_gap_mfma_e8": dict(T=900, E=8, k=2, cf=1.0, gap=0.1),
+    "top2_gap_mfma_e64_k3": dict(T=700, E=64, k=3, cf=1.5, gap=0.05),
+    "top2_gap_valu_f32": dict(T=300, E=6, k=2, d=128, d_ff=128, dtype="f32", gap=0.2),
+    "top2_gap_valu_e100": dict(T=400, E=100, k=2, d=128, d_ff=64, gap=0.05),
 }
 
 
