@@ -48,11 +48,12 @@ def lib():
         L.oracle_scores.argtypes = [i32, i32, P, P, f32, P]
         L.oracle_topk.argtypes = [i32, i32, i32, P, P, P]
         L.oracle_gap_swap.argtypes = [i32, i32, f32, P, P]
+        L.oracle_router_logits_glu.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
         L.oracle_dispatch.argtypes = [i32, i32, i32, i64, i32, f32, ctypes.c_double, P, P] + [P] * 12
         L.oracle_ffn_rows.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_layer_tokens.argtypes = [i32, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
-        for f in (L.oracle_router_logits, L.oracle_scores, L.oracle_topk, L.oracle_gap_swap, L.oracle_dispatch,
+        for f in (L.oracle_router_logits, L.oracle_router_logits_glu, L.oracle_scores, L.oracle_topk, L.oracle_gap_swap, L.oracle_dispatch,
                   L.oracle_ffn_rows, L.oracle_layer_tokens, L.oracle_combine):
             f.restype = None
         _lib = L
@@ -102,6 +103,19 @@ def router_logits(x, wr, bias=None) -> np.ndarray:
     assert wr.shape == (E, d) and x.dtype == wr.dtype
     raw = np.empty((T, E), np.float32)
     lib().oracle_router_logits(T, d, E, _dt(x), _p(x), _p(wr), _p(bias), _p(raw))
+    return raw
+
+
+def router_logits_glu(x, w1, w2, bias=None) -> np.ndarray:
+    """Two-layer router: raw = silu(x W1^T) W2^T + bias, W1 [H][d], W2 [E][H]."""
+    x, w1, w2 = _np(x), _np(w1), _np(w2)
+    bias = None if bias is None else _np(bias).astype(np.float32)
+    T, d = x.shape
+    H = w1.shape[0]
+    E = w2.shape[0]
+    assert w1.shape == (H, d) and w2.shape == (E, H) and x.dtype == w1.dtype == w2.dtype
+    raw = np.empty((T, E), np.float32)
+    lib().oracle_router_logits_glu(T, d, E, H, _dt(x), _p(x), _p(w1), _p(w2), _p(bias), _p(raw))
     return raw
 
 

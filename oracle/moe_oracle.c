@@ -92,6 +92,39 @@ void oracle_router_logits(int T, int d, int E, int dt, const void *x, const void
 }
 
 /*
+ * Two-layer router ("MoE稀疏激活原理与工程实践" §3.1, second step: a gated
+ * linear unit W1 x -> silu -> W2 instead of one linear map; W1 is
+ * d x (2E), W2 (2E) x E, and W2's outputs are the expert scores):
+ *   a[t][j]   = silu(sum_i x[t][i] * W1[j][i]),  j < H,  silu(v) = v / (1 + e^-v)
+ *   raw[t][e] = fp32(sum_j a[t][j] * W2[e][j]) + bias[e]
+ * in double up to the one fp32 rounding.  W1 is stored [H][d], W2 [E][H],
+ * both of element type dt (H is the hidden width, 2E on the page).
+ */
+void oracle_router_logits_glu(int T, int d, int E, int H, int dt, const void *x, const void *w1,
+                              const void *w2, const float *bias, float *raw)
+{
+    double *a = (double *)malloc((size_t)H * sizeof(double));
+    for (int t = 0; t < T; t++) {
+        for (int j = 0; j < H; j++) {
+            double acc = 0.0;
+            for (int i = 0; i < d; i++)
+                acc += elem(x, (size_t)t * d + i, dt) * elem(w1, (size_t)j * d + i, dt);
+            a[j] = acc / (1.0 + exp(-acc));
+        }
+        for (int e = 0; e < E; e++) {
+            double acc = 0.0;
+            for (int j = 0; j < H; j++)
+                acc += a[j] * elem(w2, (size_t)e * H + j, dt);
+            float r = (float)acc;
+            if (bias)
+                r = r + bias[e];
+            raw[(size_t)t * E + e] = r;
+        }
+    }
+    free(a);
+}
+
+/*
  * Load-aware penalty (P1 §2.3: score_i = raw_i - lambda * load_i).  Taken as
  * one fused multiply-add in fp32, fmaf(-lambda, load, raw), so that both sides
  * round once.  load == NULL means no penalty (s = raw).

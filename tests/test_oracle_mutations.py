@@ -34,15 +34,21 @@ MUTATIONS = {
     "temperature_left_out_of_numerator": ("- m) / tau) / z;", "- m)) / z;"),
     "gap_taken_below_second": ("const float gap = cs[0] - cs[1];", "const float gap = cs[1] - cs[2];"),
     "gap_swap_drops_displaced": ("            c[2] = ce;\n", ""),
+    "glu_w2_transposed": ("acc += a[j] * elem(w2, (size_t)e * H + j, dt);", "acc += a[j] * elem(w2, (size_t)j * E + e, dt);"),
+    "glu_silu_missing": ("a[j] = acc / (1.0 + exp(-acc));", "a[j] = acc;"),
     "router_weight_transposed": ("elem(wr, (size_t)e * d + i, dt)", "elem(wr, (size_t)i * E + e, dt)"),
 }
 
+# (name, check) pairs, run in this order by the child process below
 CHECKS = [
-    pins.check_capacity, pins.check_router_logits, pins.check_scores, pins.check_topk,
-    pins.check_dispatch_exhaustive, pins.check_dispatch_invariants, pins.check_aux_loss,
-    pins.check_gate_temperature, pins.check_gap_swap,
-    lambda o: pins.check_dense_equivalence(o, "f32"), pins.check_identical_experts,
-    pins.check_expert_relabel,
+    ("capacity", pins.check_capacity), ("router_logits", pins.check_router_logits),
+    ("scores", pins.check_scores), ("topk", pins.check_topk),
+    ("dispatch_exhaustive", pins.check_dispatch_exhaustive),
+    ("dispatch_invariants", pins.check_dispatch_invariants), ("aux_loss", pins.check_aux_loss),
+    ("dense_equivalence", lambda o: pins.check_dense_equivalence(o, "f32")),
+    ("identical_experts", pins.check_identical_experts), ("expert_relabel", pins.check_expert_relabel),
+    ("gate_temperature", pins.check_gate_temperature), ("gap_swap", pins.check_gap_swap),
+    ("router_glu", pins.check_router_glu),
 ]
 
 
@@ -64,10 +70,7 @@ for name, chk in m.named_checks():
 
 
 def named_checks():
-    names = ["capacity", "router_logits", "scores", "topk", "dispatch_exhaustive",
-             "dispatch_invariants", "aux_loss", "dense_equivalence", "identical_experts",
-             "expert_relabel"]
-    return list(zip(names, CHECKS))
+    return list(CHECKS)
 
 
 @pytest.fixture(scope="module")

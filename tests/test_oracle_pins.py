@@ -16,6 +16,7 @@ from fractions import Fraction
 
 import numpy as np
 import pytest
+import torch
 
 GOLD = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "page_values.json")))
 
@@ -350,6 +351,50 @@ def check_gate_temperature(o):
                     best = idx[np.argmax(sc[idx])]
                     assert d["gate64"][t, best] > 1.0 - 1e-12
     return base
+
+
+def check_router_glu(o):
+    """Two-layer router ("MoE稀疏激活原理与工程实践" §3.1, second step), pinned
+    through the linear router (itself pinned above): with W2 = I (H = E) the
+    logits are silu of the linear router's; far in silu's linear regime they
+    are the linear router of the product W2 W1; relabelling the hidden units
+    (rows of W1 with the columns of W2) changes nothing; W2 = 0 leaves the
+    bias."""
+    r = rng(11)
+    T, d, E = 40, 24, 6
+    H = 2 * E
+    x = r.standard_normal((T, d)).astype(np.float32)
+    w1 = (r.standard_normal((H, d)) / np.sqrt(d)).astype(np.float32)
+    w2 = (r.standard_normal((E, H)) / np.sqrt(H)).astype(np.float32)
+    b = r.standard_normal(E).astype(np.float32)
+    # W2 = I: silu of the linear logits (no bias, H = E)
+    w1e = w1[:E].copy()
+    lin = o.router_logits(x, w1e).astype(np.float64)
+    glu_i = o.router_logits_glu(x, w1e, np.eye(E, dtype=np.float32))
+    assert np.allclose(glu_i, lin / (1.0 + np.exp(-lin)), rtol=1e-6, atol=1e-6)
+    # silu's linear regime: pre-activations near 40 (silu(v) = v to 1e-17)
+    w1p = np.abs(w1) + 0.05
+    xp = (np.abs(x) * 40.0 / (np.abs(x) @ w1p.T).mean()).astype(np.float32)
+    glu_l = o.router_logits_glu(xp, w1p, w2).astype(np.float64)
+    lin2 = o.router_logits(xp, (w2.astype(np.float64) @ w1p.astype(np.float64)).astype(np.float32))
+    assert (xp.astype(np.float64) @ w1p.T.astype(np.float64)).min() > 20.0
+    assert np.allclose(glu_l, lin2, rtol=1e-5, atol=1e-4)
+    # hidden relabelling
+    perm = r.permutation(H)
+    g0 = o.router_logits_glu(x, w1, w2, b)
+    gp = o.router_logits_glu(x, np.ascontiguousarray(w1[perm]), np.ascontiguousarray(w2[:, perm]), b)
+    assert np.allclose(g0, gp, rtol=1e-6, atol=1e-6)
+    # W2 = 0: the bias
+    assert np.array_equal(o.router_logits_glu(x, w1, np.zeros((E, H), np.float32), b), np.tile(b, (T, 1)))
+    # bf16 operands are read exactly (the same values in fp32 give the same logits)
+    xb, w1b, w2b = (torch.from_numpy(a).to(torch.bfloat16) for a in (x, w1, w2))
+    gb = o.router_logits_glu(xb, w1b, w2b, b)
+    gf = o.router_logits_glu(xb.float().numpy(), w1b.float().numpy(), w2b.float().numpy(), b)
+    assert np.array_equal(gb, gf)
+
+
+def test_router_glu(oracle_mod):
+    check_router_glu(oracle_mod)
 
 
 def check_gap_swap(o):
