@@ -102,6 +102,13 @@ typedef struct moe_params {
      * names an expert.  0 turns it off; a negative, NaN or infinite value is
      * MOE_ERR_INVALID_ARG. */
     float top2_gap;
+    /* router network: 0 is the linear router (w_router [E][d]); H > 0 is the
+     * two-layer router of "MoE稀疏激活原理与工程实践" §3.1, second step,
+     * raw = silu(x . W1^T) . W2^T + bias with H hidden units (2E on the page),
+     * w_router then holding W1 [H][d] followed by W2 [E][H].  Supported for
+     * bf16 with E <= 64 and H <= 64 (MOE_ERR_UNSUPPORTED otherwise); a
+     * negative value is MOE_ERR_INVALID_ARG. */
+    int32_t router_hidden;
 } moe_params;
 
 /*
@@ -150,7 +157,8 @@ size_t moe_workspace_bytes(const moe_params *p);
 
 /*
  * Stage 1, route.  raw[t][e] = sum_i x[t][i] * w_router[e][i] + bias[e]
- * ("MoE架构揭秘" §3.1: z = h . W_router), s = fmaf(-lambda, load[e], raw)
+ * ("MoE架构揭秘" §3.1: z = h . W_router; with p->router_hidden > 0 the
+ * two-layer router described there), s = fmaf(-lambda, load[e], raw)
  * (or raw when load is NULL), then the K1 best experts by (s desc, e asc)
  * ("MoE架构揭秘" §3.1: softmax then top-k; softmax is monotone, so the ranking
  * is taken on s).

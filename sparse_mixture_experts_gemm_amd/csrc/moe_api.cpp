@@ -26,6 +26,9 @@ int check_params(const moe_params *p) {
     if (!(p->lambda == p->lambda) || !(p->capacity_factor == p->capacity_factor)) return MOE_ERR_INVALID_ARG;
     if (!(p->gate_temperature >= 0.0f) || isinf(p->gate_temperature)) return MOE_ERR_INVALID_ARG;
     if (!(p->top2_gap >= 0.0f) || isinf(p->top2_gap)) return MOE_ERR_INVALID_ARG;
+    if (p->router_hidden < 0) return MOE_ERR_INVALID_ARG;
+    if (p->router_hidden > 0 && (p->dtype != MOE_BF16 || p->E > 64 || p->router_hidden > 64))
+        return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 

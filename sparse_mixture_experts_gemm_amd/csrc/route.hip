@@ -421,7 +421,8 @@ hipError_t launch_nx(const moe_params &p, const void *x, const void *wr, const f
 }
 
 // ------------------------------------------------------------ MFMA router --
-// bf16 layers with E <= 64 run the router GEMM on the matrix cores.  A block
+// bf16 layers with E <= 64 run the router GEMM on the matrix cores (and so
+// does the two-layer router, whose first layer has at most 64 outputs).  A block
 // owns BT = 16 NT tokens and every expert; its 4 waves split the hidden
 // dimension into 64-element slabs (one 128-byte line of a row), wave w taking
 // slabs w, w + 4, ... in an order rotated per block (so that the blocks
@@ -449,8 +450,10 @@ __device__ __forceinline__ void rt_buf2lds(__amdgpu_buffer_rsrc_t r, uint32_t vo
 template <int NT, int NE, int P, int G>
 __global__ __launch_bounds__(kRmThreads) void route_mfma(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ wr, const float *__restrict__ bias,
-    const float *__restrict__ load, float neg_lambda, float gap, int T, int d, int E, int K1,
+    const float *__restrict__ load, float neg_lambda, float gap, int T, int d, int E, int K1, int H,
     float *__restrict__ logits, int32_t *__restrict__ cand, float *__restrict__ cand_score) {
+    // H > 0: two-layer router; wr holds W1 [H][d] followed by W2 [E][H], the
+    // MFMA GEMM computes the H hidden pre-activations, the epilogue the rest
     constexpr int BT = 16 * NT, EP = 16 * NE, TPP = 64 / G;
     constexpr int kXG = BT / 8, kWG = EP / 8, L = kXG + kWG;  // 1 KiB loads per slab
     constexpr int kSlot = L * 1024;                           // one wave's slab
@@ -475,7 +478,8 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
     const int nt = min(BT, T - t0);
     const uint32_t row_bytes = (uint32_t)d * 2;
     const auto xs = make_rsrc(x + (size_t)t0 * d, (uint32_t)nt * row_bytes);
-    const auto ws = make_rsrc(wr, (uint32_t)E * row_bytes);
+    const int NO = H > 0 ? H : E;  // rows of the matrix the MFMAs multiply by
+    const auto ws = make_rsrc(wr, (uint32_t)NO * row_bytes);
     // load group gi moves rows 8 gi .. 8 gi + 7 of the slot (x rows, then W
     // rows); lane l fetches chunk (l % 8) ^ swz(row) of row 8 gi + l / 8, so
     // LDS chunk c of a row holds the row's chunk c ^ swz(row)
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
 #pragma unroll
     for (int gi = 0; gi < L; gi++) {
         const int row = 8 * (gi < kXG ? gi : gi - kXG) + (lane >> 3);
-        const int lim = gi < kXG ? nt : E;
+        const int lim = gi < kXG ? nt : NO;
         voff[gi] = row < lim ? row * row_bytes + (((lane & 7) ^ swz(8 * gi + (lane >> 3))) << 4) : kPastEnd;
     }
 
@@ -556,12 +560,37 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
 #pragma unroll
             for (int c = 0; c < 4; c++) part[wave][16 * f + 4 * q + c][16 * g + r16] = acc[f][g][c];
     __syncthreads();
-    for (int i = threadIdx.x; i < nt * E; i += kRmThreads) {
-        const int t = i / E, e = i - t * E;
-        float raw = ((part[0][t][e] + part[1][t][e]) + part[2][t][e]) + part[3][t][e];
-        if (bias) raw = raw + bias[e];
-        logits[(size_t)(t0 + t) * E + e] = raw;
-        part[0][t][e] = load ? __builtin_fmaf(neg_lambda, load[e], raw) : raw;
+    float(*sc)[EP] = part[0];  // the scores the ranking reads
+    if (H == 0) {
+        for (int i = threadIdx.x; i < nt * E; i += kRmThreads) {
+            const int t = i / E, e = i - t * E;
+            float raw = ((part[0][t][e] + part[1][t][e]) + part[2][t][e]) + part[3][t][e];
+            if (bias) raw = raw + bias[e];
+            logits[(size_t)(t0 + t) * E + e] = raw;
+            part[0][t][e] = load ? __builtin_fmaf(neg_lambda, load[e], raw) : raw;
+        }
+    } else {
+        // hidden activations silu(sum of the partials) into part[0]; W2 as
+        // fp32 into the (now idle) second ring slot
+        for (int i = threadIdx.x; i < nt * H; i += kRmThreads) {
+            const int t = i / H, j = i - t * H;
+            const float v = ((part[0][t][j] + part[1][t][j]) + part[2][t][j]) + part[3][t][j];
+            part[0][t][j] = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+        }
+        float *w2l = reinterpret_cast<float *>(s1);
+        const uint16_t *w2 = wr + (size_t)H * d;
+        for (int i = threadIdx.x; i < E * H; i += kRmThreads) w2l[i] = __uint_as_float((uint32_t)w2[i] << 16);
+        __syncthreads();
+        // raw = a . W2^T + bias, j ascending in fp32, into part[1]
+        for (int i = threadIdx.x; i < nt * E; i += kRmThreads) {
+            const int t = i / E, e = i - t * E;
+            float acc = 0.0f;
+            for (int j = 0; j < H; j++) acc = __builtin_fmaf(part[0][t][j], w2l[e * H + j], acc);
+            if (bias) acc = acc + bias[e];
+            logits[(size_t)(t0 + t) * E + e] = acc;
+            part[1][t][e] = load ? __builtin_fmaf(neg_lambda, load[e], acc) : acc;
+        }
+        sc = part[1];
     }
     __syncthreads();
 
@@ -572,7 +601,7 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
     for (int base = wave * TPP; base < nt; base += kRmWaves * TPP) {
         const int t = base + lane / G;  // < BT
         const bool ok = t < nt && e < E;
-        uint64_t key = ok ? rank_key(part[0][t][e], e) : 0;
+        uint64_t key = ok ? rank_key(sc[t][e], e) : 0;
         const size_t to = (size_t)(t0 + min(t, nt - 1)) * K1;  // this group's token's candidate row
         const bool writer = e == 0 && t < nt;
         RankOut ro;
@@ -585,7 +614,7 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
             if constexpr (G >= 64) m = max_step<32>(m);
             const bool none = m == 0;
             const int we = none ? 0 : (int)~(uint32_t)m;  // the group's winner
-            const float sw = part[0][t][we];               // its own score bits
+            const float sw = sc[t][we];                    // its own score bits
             ro.put(r, none ? -1 : we, none ? -INFINITY : sw, cand + to, cand_score + to, writer);
             if (!none && e == we) key = 0;
         }
@@ -603,13 +632,21 @@ hipError_t launch_mfma_g(const moe_params &p, const void *x, const void *wr, con
     const int grid = (int)ceil_div(p.T, 16 * NT);
     hipLaunchKernelGGL((route_mfma<NT, NE, P, G>), dim3(grid), dim3(kRmThreads), 0, st,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(wr), bias, load, -p.lambda,
-                       p.top2_gap, p.T, p.d, p.E, p.k + 1, logits, cand, cand_score);
+                       p.top2_gap, p.T, p.d, p.E, p.k + 1, p.router_hidden, logits, cand, cand_score);
     return hipGetLastError();
 }
 
 template <int NT>
 hipError_t launch_mfma_nt(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
                           float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
+    if constexpr (NT == 1) {
+        if (p.router_hidden > 0) {  // two-layer router: up to 64 hidden units, 4 fragments
+            if (p.E <= 8) return launch_mfma_g<1, 4, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
+            if (p.E <= 16) return launch_mfma_g<1, 4, 16>(p, x, wr, bias, load, logits, cand, cand_score, st);
+            if (p.E <= 32) return launch_mfma_g<1, 4, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
+            return launch_mfma_g<1, 4, 64>(p, x, wr, bias, load, logits, cand, cand_score, st);
+        }
+    }
     if (p.E <= 8) return launch_mfma_g<NT, 1, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (p.E <= 16) return launch_mfma_g<NT, 1, 16>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (p.E <= 32) return launch_mfma_g<NT, 2, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
@@ -621,7 +658,8 @@ hipError_t launch_mfma_nt(const moe_params &p, const void *x, const void *wr, co
 // (half the gate-vector reads per token), else 16.
 hipError_t launch_mfma(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
                        float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
-    if (p.T >= 256 * 32) return launch_mfma_nt<2>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (p.T >= 256 * 32 && p.router_hidden == 0)
+        return launch_mfma_nt<2>(p, x, wr, bias, load, logits, cand, cand_score, st);
     return launch_mfma_nt<1>(p, x, wr, bias, load, logits, cand, cand_score, st);
 }
 

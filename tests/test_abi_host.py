@@ -66,7 +66,8 @@ def test_workspace_sizes_cover_buffers():
 @pytest.mark.parametrize("bad", [dict(E=0), dict(E=257), dict(k=0), dict(k=9, E=16), dict(k=3, E=2),
                                  dict(T=-1), dict(T=(1 << 20) + 1), dict(d=0), dict(gate_temperature=-0.5),
                                  dict(gate_temperature=float("nan")), dict(gate_temperature=float("inf")),
-                                 dict(top2_gap=-0.1), dict(top2_gap=float("nan")), dict(top2_gap=float("inf"))])
+                                 dict(top2_gap=-0.1), dict(top2_gap=float("nan")), dict(top2_gap=float("inf")),
+                                 dict(router_hidden=-1)])
 def test_invalid_sizes_rejected(bad):
     p = P(**bad)
     assert moe.capacity(p) == -1
@@ -78,7 +79,10 @@ def test_invalid_sizes_rejected(bad):
 
 @pytest.mark.parametrize("bad", [dict(d=100), dict(d_ff=96), dict(dtype=7), dict(d=16384 + 64),
                                  dict(d=16384, d_ff=131072, dtype=moe.MOE_BF16),  # one expert matrix of 4 GiB
-                                 dict(d=8192, d_ff=131072, dtype=moe.MOE_F32)])
+                                 dict(d=8192, d_ff=131072, dtype=moe.MOE_F32),
+                                 dict(router_hidden=16),  # two-layer router: bf16 only
+                                 dict(router_hidden=65, dtype=moe.MOE_BF16),
+                                 dict(router_hidden=16, E=65, k=2, dtype=moe.MOE_BF16)])
 def test_unsupported_shapes_rejected(bad):
     p = P(**bad)
     r = moe.MoeRouting()

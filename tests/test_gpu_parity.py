@@ -376,6 +376,40 @@ def test_router_classes(T, E):
     routing_vs_oracle(p, r.cpu(), lg, None, 0.0)
 
 
+@pytest.mark.parametrize("T,E,H", [(700, 8, 16), (500, 32, 64), (300, 64, 64), (40, 5, 10)])
+def test_router_glu(T, E, H):
+    """Two-layer router ("MoE稀疏激活原理与工程实践" §3.1, second step): logits
+    against the oracle's, routing and dispatch bit-exact from the GPU's
+    logits, and moe_forward's logits identical to moe_route's."""
+    cfg = small_cfg(T=T, E=E, k=2, d=256, d_ff=64, cf=1.0)
+    L = Layer(cfg)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(7 * H + E)
+    w1 = (torch.randn((H, cfg.d), device=DEV, generator=g) / cfg.d ** 0.5).to(torch.bfloat16)
+    w2 = (torch.randn((E, H), device=DEV, generator=g) / H ** 0.5).to(torch.bfloat16)
+    wr = torch.cat([w1.flatten(), w2.flatten()])
+    p = params(cfg, router_hidden=H)
+    say(f"[case] glu router T={T} E={E} H={H}")
+    r = moe.Routing(p, DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe.route(p, L.g["x"], wr, L.g["bias"], None, logits, r)
+    R = moe.max_rows(p)
+    xp = torch.empty((max(R, 1), p.d), dtype=torch.bfloat16, device=DEV)
+    moe.dispatch(p, L.g["x"], r, xp, moe.alloc_workspace(p, DEV, dispatch_only=True))
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    own = oracle.router_logits_glu(L.c["x"], np_of(w1.cpu()), np_of(w2.cpu()), L.c["bias"])
+    assert np.abs(own - lg).max() <= 1e-3 * rms(own), "router logits"
+    routing_vs_oracle(p, r.cpu(), lg, None, 0.0)
+    # the forward pass routes with the same kernel
+    y = torch.empty((T, p.d), dtype=torch.bfloat16, device=DEV)
+    lg2 = torch.empty_like(logits)
+    moe.forward(p, L.g["x"], wr, L.g["bias"], None, L.g["w1"], L.g["w3"], L.g["w2"], y, lg2, moe.Routing(p, DEV),
+                moe.alloc_workspace(p, DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(lg2.cpu().numpy().view(np.uint32), lg.view(np.uint32))
+
+
 def test_nan_rows_route_and_dispatch():
     """A token row holding a NaN (or both infinities) makes its logits NaN.
     NaN scores rank after every number, so the token still names k+1 experts
