@@ -577,15 +577,20 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
             const float v = ((part[0][t][j] + part[1][t][j]) + part[2][t][j]) + part[3][t][j];
             part[0][t][j] = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
         }
+        // (stored transposed, [H][E]: the lanes of a wave take consecutive
+        // experts, so they read consecutive words, not one bank H apart)
         float *w2l = reinterpret_cast<float *>(s1);
         const uint16_t *w2 = wr + (size_t)H * d;
-        for (int i = threadIdx.x; i < E * H; i += kRmThreads) w2l[i] = __uint_as_float((uint32_t)w2[i] << 16);
+        for (int i = threadIdx.x; i < E * H; i += kRmThreads) {
+            const int j = i / E, e = i - j * E;
+            w2l[i] = __uint_as_float((uint32_t)w2[(size_t)e * H + j] << 16);
+        }
         __syncthreads();
         // raw = a . W2^T + bias, j ascending in fp32, into part[1]
         for (int i = threadIdx.x; i < nt * E; i += kRmThreads) {
             const int t = i / E, e = i - t * E;
             float acc = 0.0f;
-            for (int j = 0; j < H; j++) acc = __builtin_fmaf(part[0][t][j], w2l[e * H + j], acc);
+            for (int j = 0; j < H; j++) acc = __builtin_fmaf(part[0][t][j], w2l[j * E + e], acc);
             if (bias) acc = acc + bias[e];
             logits[(size_t)(t0 + t) * E + e] = acc;
             part[1][t][e] = load ? __builtin_fmaf(neg_lambda, load[e], acc) : acc;
@@ -639,13 +644,11 @@ hipError_t launch_mfma_g(const moe_params &p, const void *x, const void *wr, con
 template <int NT>
 hipError_t launch_mfma_nt(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
                           float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
-    if constexpr (NT == 1) {
-        if (p.router_hidden > 0) {  // two-layer router: up to 64 hidden units, 4 fragments
-            if (p.E <= 8) return launch_mfma_g<1, 4, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
-            if (p.E <= 16) return launch_mfma_g<1, 4, 16>(p, x, wr, bias, load, logits, cand, cand_score, st);
-            if (p.E <= 32) return launch_mfma_g<1, 4, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
-            return launch_mfma_g<1, 4, 64>(p, x, wr, bias, load, logits, cand, cand_score, st);
-        }
+    if (p.router_hidden > 0) {  // two-layer router: up to 64 hidden units, 4 fragments
+        if (p.E <= 8) return launch_mfma_g<NT, 4, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
+        if (p.E <= 16) return launch_mfma_g<NT, 4, 16>(p, x, wr, bias, load, logits, cand, cand_score, st);
+        if (p.E <= 32) return launch_mfma_g<NT, 4, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
+        return launch_mfma_g<NT, 4, 64>(p, x, wr, bias, load, logits, cand, cand_score, st);
     }
     if (p.E <= 8) return launch_mfma_g<NT, 1, 8>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (p.E <= 16) return launch_mfma_g<NT, 1, 16>(p, x, wr, bias, load, logits, cand, cand_score, st);
@@ -658,8 +661,7 @@ hipError_t launch_mfma_nt(const moe_params &p, const void *x, const void *wr, co
 // (half the gate-vector reads per token), else 16.
 hipError_t launch_mfma(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
                        float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
-    if (p.T >= 256 * 32 && p.router_hidden == 0)
-        return launch_mfma_nt<2>(p, x, wr, bias, load, logits, cand, cand_score, st);
+    if (p.T >= 256 * 32) return launch_mfma_nt<2>(p, x, wr, bias, load, logits, cand, cand_score, st);
     return launch_mfma_nt<1>(p, x, wr, bias, load, logits, cand, cand_score, st);
 }
 

@@ -376,7 +376,7 @@ def test_router_classes(T, E):
     routing_vs_oracle(p, r.cpu(), lg, None, 0.0)
 
 
-@pytest.mark.parametrize("T,E,H", [(700, 8, 16), (500, 32, 64), (300, 64, 64), (40, 5, 10)])
+@pytest.mark.parametrize("T,E,H", [(700, 8, 16), (500, 32, 64), (300, 64, 64), (40, 5, 10), (8192 + 17, 16, 32)])
 def test_router_glu(T, E, H):
     """Two-layer router ("MoE稀疏激活原理与工程实践" §3.1, second step): logits
     against the oracle's, routing and dispatch bit-exact from the GPU's
