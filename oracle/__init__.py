@@ -53,8 +53,13 @@ def lib():
         L.oracle_ffn_rows.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_layer_tokens.argtypes = [i32, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        L.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
+        L.oracle_fp8_e4m3_value.restype = f64
+        L.oracle_fp8_e4m3_decode.argtypes = [i64, P, P]
+        L.oracle_dequant_rows.argtypes = [i64, i64, P, P, P]
         for f in (L.oracle_router_logits, L.oracle_router_logits_glu, L.oracle_scores, L.oracle_topk, L.oracle_gap_swap, L.oracle_dispatch,
-                  L.oracle_ffn_rows, L.oracle_layer_tokens, L.oracle_combine):
+                  L.oracle_ffn_rows, L.oracle_layer_tokens, L.oracle_combine, L.oracle_fp8_e4m3_decode,
+                  L.oracle_dequant_rows):
             f.restype = None
         _lib = L
     return _lib
@@ -80,7 +85,9 @@ def _dt(a: np.ndarray) -> int:
         return 0
     if a.dtype == np.uint16:
         return 1
-    raise TypeError(f"oracle element type must be float32 or bf16 bits, got {a.dtype}")
+    if a.dtype == np.float64:
+        return 2
+    raise TypeError(f"oracle element type must be float32, bf16 bits or float64, got {a.dtype}")
 
 
 def _p(a):
@@ -177,6 +184,29 @@ def dispatch(cand, cand_score, E: int, k: int, C: int, reroute: int = 1, aux_coe
                           _p(o["gate64"]), _p(o["offsets"]), _p(o["token_of_row"]),
                           _p(o["demand"]), _p(o["kept"]), _p(o["totals"]), _p(o["aux_loss"]))
     return o
+
+
+def fp8_e4m3_value(byte: int) -> float:
+    """Value of one OCP E4M3 byte."""
+    return float(lib().oracle_fp8_e4m3_value(int(byte)))
+
+
+def fp8_e4m3_decode(q) -> np.ndarray:
+    """Values (double) of an array of E4M3 bytes, same shape."""
+    q = np.ascontiguousarray(_np(q), dtype=np.uint8)
+    out = np.empty(q.shape, np.float64)
+    lib().oracle_fp8_e4m3_decode(q.size, _p(q), _p(out))
+    return out
+
+
+def dequant_rows(q, scale) -> np.ndarray:
+    """w[..., r, c] = scale[..., r] * value(q[..., r, c]) in double."""
+    q = np.ascontiguousarray(_np(q), dtype=np.uint8)
+    scale = np.ascontiguousarray(_np(scale), dtype=np.float32)
+    assert scale.shape == q.shape[:-1]
+    w = np.empty(q.shape, np.float64)
+    lib().oracle_dequant_rows(scale.size, q.shape[-1], _p(q), _p(scale), _p(w))
+    return w
 
 
 def ffn_rows(expert, src, x, w1, w3, w2, want_h: bool = False):

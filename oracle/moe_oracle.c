@@ -18,7 +18,8 @@
  * Where the pages leave a step open, the reading taken is stated at the step.
  *
  * Element types: dt = 0 means fp32 elements, dt = 1 means bfloat16 bit
- * patterns (uint16), widened exactly to float.
+ * patterns (uint16), widened exactly to float, dt = 2 means double elements
+ * (used for dequantised one-byte expert weights, which are exact in double).
  *
  * Parity status: every function below is pinned by a CPU test (worked values
  * printed on the pages, closed forms, brute force, or special cases that reduce
@@ -36,6 +37,8 @@ static double elem(const void *p, size_t i, int dt)
 {
     if (dt == 0)
         return (double)((const float *)p)[i];
+    if (dt == 2)
+        return ((const double *)p)[i];
     uint32_t u = (uint32_t)((const uint16_t *)p)[i] << 16;
     float f;
     memcpy(&f, &u, sizeof f);
@@ -49,6 +52,47 @@ int oracle_num_threads(void)
 #else
     return 1;
 #endif
+}
+
+/*
+ * One-byte expert weights (P5 §5.1, expert-kernel quantisation; P3 §3.2 on
+ * INT8 expert weights; P1 §2.1 counts FP8 at one byte per parameter).  Reading: the byte format is OCP 8-bit
+ * floating point E4M3 ("FN": no infinities): bit 7 sign, bits 6..3 a biased
+ * exponent (bias 7), bits 2..0 the fraction.  Exponent field 0 encodes the
+ * subnormals f/8 * 2^-6; exponent 15 with fraction 7 is NaN; every other code
+ * is (1 + f/8) * 2^(e - 7).  Largest finite value 448.
+ */
+double oracle_fp8_e4m3_value(uint8_t b)
+{
+    int sgn = b >> 7, e = (b >> 3) & 15, f = b & 7;
+    double v;
+    if (e == 15 && f == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)f / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)f / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+void oracle_fp8_e4m3_decode(int64_t n, const uint8_t *q, double *out)
+{
+    for (int64_t i = 0; i < n; i++)
+        out[i] = oracle_fp8_e4m3_value(q[i]);
+}
+
+/*
+ * Dequantised weight rows: w[r][c] = scale[r] * value(q[r][c]), one fp32 scale
+ * per output row (per output channel) of a weight matrix.  Reading: the pages
+ * give no scale granularity; a per-row scale keeps every dot product of the
+ * layer a plain scaled sum.  The product of an fp32 scale and an E4M3 value is
+ * exact in double.
+ */
+void oracle_dequant_rows(int64_t rows, int64_t cols, const uint8_t *q, const float *scale, double *w)
+{
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            w[r * cols + c] = (double)scale[r] * oracle_fp8_e4m3_value(q[r * cols + c]);
 }
 
 /*

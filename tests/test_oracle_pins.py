@@ -532,6 +532,77 @@ def check_dense_equivalence(o, dtype="f32"):
     assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
 
 
+# ------------------------------------------------- one-byte expert weights --
+
+# Values fixed by the OCP 8-bit floating point specification for E4M3 (code:
+# value); the largest finite value, the smallest normal and subnormal, one,
+# a fraction step and the signed zero.
+E4M3_SPEC = {0x00: 0.0, 0x01: 2.0 ** -9, 0x07: 7 * 2.0 ** -9, 0x08: 2.0 ** -6, 0x38: 1.0,
+             0x39: 1.125, 0x40: 2.0, 0x7E: 448.0, 0xB8: -1.0, 0xFE: -448.0, 0x81: -(2.0 ** -9)}
+
+
+def check_fp8_decode(o):
+    """E4M3 decode against the specification's values, torch's float8_e4m3fn
+    on all 256 codes (an independent implementation), the NaN codes and the
+    strict order of the positive codes."""
+    for code, v in E4M3_SPEC.items():
+        assert o.fp8_e4m3_value(code) == v, hex(code)
+    assert math.copysign(1.0, o.fp8_e4m3_value(0x80)) == -1.0 and o.fp8_e4m3_value(0x80) == 0.0
+    codes = np.arange(256, dtype=np.uint8)
+    got = o.fp8_e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan) and nan.sum() == 2 and nan[0x7F] and nan[0xFF]
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert (np.diff(got[:0x7F]) > 0).all()
+    assert np.array_equal(got[0x80:0xFF], -got[:0x7F])
+
+
+def e4m3_bytes(r, shape):
+    """Random E4M3 codes without the two NaN codes."""
+    q = r.integers(0, 256, size=shape, dtype=np.uint8)
+    return np.where((q & 0x7F) == 0x7F, q ^ 1, q).astype(np.uint8)
+
+
+def check_dequant_rows(o):
+    """w[r][c] = scale[r] * value(q[r][c]): against torch's float8 widening
+    times the scale in float64 (exact), with rows != columns and distinct
+    scales so that a transposed scale or operand fails."""
+    r = rng(21)
+    q = e4m3_bytes(r, (3, 5, 7))
+    s = (r.random((3, 5)) * 4 + 0.01).astype(np.float32)
+    w = o.dequant_rows(q, s)
+    ref = torch.from_numpy(q).view(torch.float8_e4m3fn).to(torch.float64) * torch.from_numpy(s).double()[..., None]
+    assert np.array_equal(w, ref.numpy())
+
+
+def check_ffn_double_elements(o):
+    """The expert FFN over double elements (dequantised weights, bf16 inputs
+    widened) equals the dense textbook SwiGLU in float64."""
+    r = rng(22)
+    T, d, d_ff = 7, 24, 40
+    x = bits_to_f32(bf16_bits(r.standard_normal((T, d)).astype(np.float32))).astype(np.float64)
+    w1 = o.dequant_rows(e4m3_bytes(r, (1, d_ff, d)), np.full((1, d_ff), 1 / 64, np.float32))
+    w3 = o.dequant_rows(e4m3_bytes(r, (1, d_ff, d)), np.full((1, d_ff), 1 / 32, np.float32))
+    w2 = o.dequant_rows(e4m3_bytes(r, (1, d, d_ff)), (r.random((1, d)) / 50).astype(np.float32))
+    y, h = o.ffn_rows(np.zeros(T, np.int32), np.arange(T, dtype=np.int32), x, w1, w3, w2, want_h=True)
+    ref, href = textbook_swiglu(x, w1[0], w3[0], w2[0])
+    assert np.allclose(h, href, rtol=1e-12, atol=1e-12)
+    assert np.allclose(y, ref, rtol=1e-12, atol=1e-12)
+
+
+def test_fp8_decode(oracle_mod):
+    check_fp8_decode(oracle_mod)
+
+
+def test_dequant_rows(oracle_mod):
+    check_dequant_rows(oracle_mod)
+
+
+def test_ffn_double_elements(oracle_mod):
+    check_ffn_double_elements(oracle_mod)
+
+
 def test_dense_equivalence_f32(oracle_mod):
     check_dense_equivalence(oracle_mod, "f32")
 
