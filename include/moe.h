@@ -223,6 +223,33 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
                 const float *load, const void *w1, const void *w3, const void *w2, void *y,
                 float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * One-byte expert weights ("企业官网建设流程全解析" page §5.1: the experts'
+ * W1/W2/W3 kernels quantised; "GPT-4稀疏激活真相" §2.1 counts FP8 at one byte
+ * per parameter).  Each weight matrix is held as OCP FP8 E4M3 codes (no
+ * infinities; 0x7F and 0xFF are NaN) with one fp32 scale per output row:
+ *   W1[e][j][i] = s1[e][j] * q1[e][j][i], W3 likewise with s3,
+ *   W2[e][c][j] = s2[e][c] * q2[e][c][j].
+ *   q1, q3 [E][d_ff][d] bytes, s1, s3 [E][d_ff] fp32; q2 [E][d][d_ff] bytes,
+ *   s2 [E][d] fp32; q pointers 16-byte aligned, scales 4-byte aligned.
+ * The activations are as for the bf16 layer (x_perm bf16, h fp16, y_perm
+ * fp32 with a single slice).  Built for the weight-streaming (decode) regime:
+ * dtype MOE_BF16, capacity C = moe_capacity(p) <= 32, d and d_ff multiples
+ * of 128; other layers get MOE_ERR_UNSUPPORTED.  Otherwise as moe_expert_ffn.
+ */
+int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                       const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
+                       const uint8_t *w2, const float *s2, void *h, void *y_perm, void *stream);
+
+/*
+ * moe_forward with one-byte expert weights (as moe_expert_ffn_fp8; same
+ * workspace size, same limits).  The router weights stay bf16.
+ */
+int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                    const float *load, const uint8_t *w1, const float *s1, const uint8_t *w3,
+                    const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
+                    moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
+
 /* Static description of a return code. */
 const char *moe_strerror(int code);
 

@@ -181,3 +181,16 @@ def make_layer(cfg: MoEConfig, device="cpu", seed: int = 0, T: Optional[int] = N
     if "w2" in want:
         out["w2"] = normal_tensor(seed, "w2", (cfg.E, cfg.d, cfg.d_ff), sf, dt, device)
     return out
+
+
+def quantize_rows_e4m3(w: torch.Tensor):
+    """Synthetic one-byte weights from a weight tensor [..., rows, cols]: an
+    fp32 scale per row, amax / 448 (448 is the largest E4M3 value; 1 for an
+    all-zero row), and the E4M3 codes of w / scale by torch's round-to-nearest
+    conversion.  Returns (codes uint8 [..., rows, cols], scales fp32 [..., rows]).
+    """
+    wf = w.float()
+    amax = wf.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    q = (wf / s[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
+    return q.contiguous(), s.contiguous()

@@ -853,6 +853,197 @@ __global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny(
 }
 #undef SK_STEP
 
+// ------------------------------------------------------ skinny, FP8 W ----
+// FP8 (OCP E4M3) expert weights with one fp32 scale per weight row,
+// W[n][k] = s[n] * q[n][k], in the weight-streaming regime (every expert at
+// most 32 rows).  The tile is that of the bf16 skinny kernel, but a stage
+// spans 128 K elements (weight rows of 128 bytes, x or h rows of 256 bytes),
+// so as many weight bytes are in flight per CU as there, covering twice the
+// K depth.  The q fragments are converted in registers, exactly, to bf16
+// (gate-up) or fp16 (down) with the gfx950 scaled conversion at scale 1; the
+// row scales multiply the fp32 accumulators in the epilogue (a row's scale
+// factors out of its dot products).
+constexpr int kSk8A = kSkBM * 256;                   // A part: 32 rows x 128 elements (8 KiB)
+constexpr int kSk8Stage = kSk8A + 2 * kSkBN * 128;  // + 128 weight rows x 128 bytes (16 KiB)
+constexpr int kSk8K = 128;                           // K elements per stage
+
+struct Sk8Thread {
+    const char *a_base;
+    const char *b_base[2];
+    uint32_t a_off[2];  // wave w loads A rows 8w .. 8w+7, four per load
+    uint32_t b_off[4];
+    int wave;
+};
+
+// Chunk swizzle of a 256-byte A row (16 chunks of 16 bytes): a fragment read
+// touches one chunk of 16 consecutive rows, which the XOR spreads over all
+// the banks.
+__device__ __forceinline__ int swz16(int row) { return row & 15; }
+
+template <int MODE>
+__device__ __forceinline__ void sk8_issue(const Sk8Thread &g, char *stage, int k) {
+    const uint32_t ka = (uint32_t)k * kSk8K * 2, kq = (uint32_t)k * kSk8K;
+    g2lds16(g.a_base + g.a_off[0] + ka, stage + (2 * g.wave) * 1024);
+    g2lds16(g.a_base + g.a_off[1] + ka, stage + (2 * g.wave + 1) * 1024);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int grp = g.wave * 4 + j;                  // 8-row group of the B part
+        const int src = MODE == kGateUp ? grp >> 3 : 0;  // gate-up: groups 8.. are W3
+        g2lds16(g.b_base[src] + g.b_off[j] + kq, stage + kSk8A + grp * 1024);
+    }
+}
+
+// eight E4M3 values -> eight bf16 (gate-up) or fp16 (down), element i from
+// byte i
+template <bool F16>
+__device__ __forceinline__ uint4 fp8x8_widen(uint2 q) {
+    if constexpr (F16) {
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.y, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.y, 1.0f, true)));
+    } else {
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true)));
+    }
+}
+
+template <int MODE, int NB>
+__device__ __forceinline__ void sk8_compute(const char *stage, int wave, int lane, f32x4_t (&acc)[2][2]) {
+    constexpr bool kF16 = MODE == kDown;
+    const int r16 = lane & 15, kq = lane >> 4;
+    const int rb0 = (MODE == kGateUp ? 16 : 32) * wave + r16;
+    const int rb1 = (MODE == kGateUp ? kSkBN + 16 * wave : 32 * wave + 16) + r16;
+#pragma unroll
+    for (int ss = 0; ss < 4; ss++) {
+        // A: 8 elements at k = 32 ss + 8 kq, chunk 4 ss + kq of the row;
+        // B: 8 bytes at the same k, half kq & 1 of chunk 2 ss + kq / 2
+        const int c = 4 * ss + kq, cb = 2 * ss + (kq >> 1), hb = (kq & 1) * 8;
+        uint4 a[2];
+#pragma unroll
+        for (int ib = 0; ib < NB; ib++) {
+            const int row = ib * 16 + r16;
+            a[ib] = lds_read16(stage + row * 256 + ((c ^ swz16(row)) << 4));
+        }
+        const uint2 q0 = *reinterpret_cast<const uint2 *>(stage + kSk8A + rb0 * 128 + ((cb ^ swz(rb0)) << 4) + hb);
+        const uint2 q1 = *reinterpret_cast<const uint2 *>(stage + kSk8A + rb1 * 128 + ((cb ^ swz(rb1)) << 4) + hb);
+        const uint4 b0 = fp8x8_widen<kF16>(q0), b1 = fp8x8_widen<kF16>(q1);
+#pragma unroll
+        for (int ib = 0; ib < NB; ib++) {
+            acc[ib][0] = mfma16<kF16>(a[ib], b0, acc[ib][0]);
+            acc[ib][1] = mfma16<kF16>(a[ib], b1, acc[ib][1]);
+        }
+    }
+}
+
+#define SK8_STEP(I, cur, nxt)                                                            \
+    do {                                                                                 \
+        if (k0 + (I) >= nk) goto done;                                                   \
+        WAIT_VMCNT(6 * (kSkStages - 2));                                                 \
+        block_sync();                                                                    \
+        sk8_issue<MODE>(g, nxt, min(k0 + (I) + kSkStages - 1, nk - 1));                  \
+        sk8_compute<MODE, NB>(cur, g.wave, lane, acc);                                   \
+    } while (0)
+
+// The K loop of the bf16 skinny kernel, over stages of 128 K elements.
+template <int MODE, int NB>
+__device__ __forceinline__ void sk8_main(const Sk8Thread &g, int nk, int lane, char *b0, char *b1, char *b2,
+                                         char *b3, char *b4, char *b5, f32x4_t (&acc)[2][2]) {
+    sk8_issue<MODE>(g, b0, 0);
+    sk8_issue<MODE>(g, b1, min(1, nk - 1));
+    sk8_issue<MODE>(g, b2, min(2, nk - 1));
+    sk8_issue<MODE>(g, b3, min(3, nk - 1));
+    sk8_issue<MODE>(g, b4, min(4, nk - 1));
+    for (int k0 = 0;; k0 += kSkStages) {
+        SK8_STEP(0, b0, b5);
+        SK8_STEP(1, b1, b0);
+        SK8_STEP(2, b2, b1);
+        SK8_STEP(3, b3, b2);
+        SK8_STEP(4, b4, b3);
+        SK8_STEP(5, b5, b4);
+    }
+done:
+    WAIT_VMCNT(0);
+}
+#undef SK8_STEP
+
+template <int MODE>
+__global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny_fp8(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ B0,
+    const uint8_t *__restrict__ B1, const float *__restrict__ S0, const float *__restrict__ S1,
+    const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n, void *__restrict__ out_v) {
+    __shared__ __attribute__((aligned(1024))) char sb0[kSk8Stage];
+    __shared__ __attribute__((aligned(1024))) char sb1[kSk8Stage];
+    __shared__ __attribute__((aligned(1024))) char sb2[kSk8Stage];
+    __shared__ __attribute__((aligned(1024))) char sb3[kSk8Stage];
+    __shared__ __attribute__((aligned(1024))) char sb4[kSk8Stage];
+    __shared__ __attribute__((aligned(1024))) char sb5[kSk8Stage];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    TileInfo ti;
+    if (!find_tile(offsets, E, ntiles_n, kSkBM, 1, blockIdx.x, nullptr, nullptr, ti)) return;
+    const int n0 = ti.nt * (MODE == kGateUp ? kSkBN : kSkBNd);
+    const size_t wexp = (size_t)ti.e * N * K;  // bytes: one fp8 per element
+
+    Sk8Thread g;
+    g.wave = wave;
+    g.a_base = reinterpret_cast<const char *>(a_rows ? A : A + (size_t)ti.m0 * K);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int row = (2 * wave + j) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ swz16(row);
+        const int gm = min(ti.m0 + row, ti.mend - 1);
+        const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
+        g.a_off[j] = ((uint32_t)ar * K + c * 8) * 2;
+    }
+    g.b_base[0] = reinterpret_cast<const char *>(B0 + wexp);
+    g.b_base[1] = reinterpret_cast<const char *>((MODE == kGateUp ? B1 : B0) + wexp);
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+        const int grp = wave * 4 + j;
+        const int row = grp * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        const int gn = min(n0 + (MODE == kGateUp ? (row & (kSkBN - 1)) : row), N - 1);
+        g.b_off[j] = (uint32_t)gn * K + c * 16;
+    }
+    const int nk = K / kSk8K;
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++) acc[ib][jb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int nb = ti.mend - ti.m0 > 16 ? 2 : 1;  // active 16-row blocks (uniform)
+    if (nb == 2)
+        sk8_main<MODE, 2>(g, nk, lane, sb0, sb1, sb2, sb3, sb4, sb5, acc);
+    else
+        sk8_main<MODE, 1>(g, nk, lane, sb0, sb1, sb2, sb3, sb4, sb5, acc);
+
+    // epilogue: the lane holds column lane % 16, rows 4 * (lane / 16) + q;
+    // the weight rows' scales multiply the accumulators first
+    const float *s0e = S0 + (size_t)ti.e * N, *s1e = (MODE == kGateUp ? S1 : S0) + (size_t)ti.e * N;
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int m = ti.m0 + ib * 16 + 4 * (lane >> 4) + q;
+            if (m >= ti.mend) continue;
+            if (MODE == kGateUp) {
+                const int col = n0 + wave * 16 + (lane & 15);
+                if (col < N)
+                    static_cast<uint16_t *>(out_v)[(size_t)m * N + col] =
+                        f32_to_f16_sat(silu_mul(acc[ib][0][q] * s0e[col], acc[ib][1][q] * s1e[col]));
+            } else {
+#pragma unroll
+                for (int jb = 0; jb < 2; jb++) {
+                    const int col = n0 + wave * 32 + jb * 16 + (lane & 15);
+                    if (col < N) static_cast<float *>(out_v)[(size_t)m * N + col] = acc[ib][jb][q] * s0e[col];
+                }
+            }
+        }
+}
+
 // ---------------------------------------------------------------- fp32 ----
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
@@ -934,6 +1125,28 @@ int ffn_splits(const moe_params &p, int64_t max_rows) {
 // is sized by it, so a tight bound leaves few blocks without work.
 static int64_t mtile_bound(int64_t max_rows, int64_t cap, int E, int bm) {
     return std::min<int64_t>(max_rows / bm + E, (int64_t)E * ((cap + bm - 1) / bm));
+}
+
+bool fp8_ffn_supported(const moe_params &p) {
+    return p.dtype == MOE_BF16 && capacity_rows(p) <= kSkBM && p.d % kSk8K == 0 && p.d_ff % kSk8K == 0;
+}
+
+hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
+                                 const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
+                                 const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
+                                 void *y_perm, hipStream_t st) {
+    if (max_rows <= 0) return hipSuccess;
+    const int E = p.E, d = p.d, dff = p.d_ff;
+    if (p.dtype != MOE_BF16 || cap > kSkBM || d % kSk8K != 0 || dff % kSk8K != 0) return hipErrorInvalidValue;
+    const int64_t mt = mtile_bound(max_rows, cap, E, kSkBM);
+    const int nt_up = (int)ceil_div(dff, kSkBN);
+    const int nt_dn = (int)ceil_div(d, kSkBNd);
+    hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
+                       static_cast<const uint16_t *>(x_perm), a_rows, w1, w3, s1, s3, offsets, E, dff, d, nt_up, h);
+    hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(kSkThreads), 0, st,
+                       static_cast<const uint16_t *>(h), (const int32_t *)nullptr, w2, w2, s2, s2, offsets, E, d,
+                       dff, nt_dn, y_perm);
+    return hipGetLastError();
 }
 
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,

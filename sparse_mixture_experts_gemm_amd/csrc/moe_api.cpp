@@ -54,6 +54,34 @@ int routing_ok(const moe_routing *r, const moe_params &p) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
+
+// Expert weights of a forward pass: matrices of the layer's dtype, or E4M3
+// codes with fp32 row scales (s1 non-null).
+struct FfnWeights {
+    const void *w1, *w3, *w2;
+    const float *s1, *s3, *s2;
+};
+
+int fp8_weights_ok(const moe_params &p, const FfnWeights &w) {
+    if (!w.w1 || !w.w3 || !w.w2 || !w.s1 || !w.s3 || !w.s2) return MOE_ERR_INVALID_ARG;
+    if (!fp8_ffn_supported(p)) return MOE_ERR_UNSUPPORTED;
+    if (!aligned16(w.w1) || !aligned16(w.w3) || !aligned16(w.w2) || !aligned4(w.s1) || !aligned4(w.s3) ||
+        !aligned4(w.s2))
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+hipError_t launch_ffn(const moe_params &p, int64_t R, int64_t C, const void *a, const int32_t *a_rows,
+                      const int32_t *offsets, const FfnWeights &w, void *h, void *y_perm, int32_t *claim,
+                      hipStream_t st) {
+    if (w.s1)
+        return launch_expert_ffn_fp8(p, R, C, a, a_rows, offsets, static_cast<const uint8_t *>(w.w1), w.s1,
+                                     static_cast<const uint8_t *>(w.w3), w.s3,
+                                     static_cast<const uint8_t *>(w.w2), w.s2, h, y_perm, st);
+    return launch_expert_ffn(p, R, C, a, a_rows, offsets, w.w1, w.w3, w.w2, h, y_perm, claim, st);
+}
+
 // moe_forward folds the dispatch gather into the gate-up GEMM (A rows read
 // from x through token_of_row) whenever x spans less than 2 GiB (the GEMM
 // reads A through a buffer extent kept below 2 GiB, so that an offset of
@@ -163,6 +191,21 @@ int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offse
                                         nullptr, static_cast<hipStream_t>(stream)));
 }
 
+int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                       const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
+                       const uint8_t *w2, const float *s2, void *h, void *y_perm, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    const FfnWeights w{w1, w3, w2, s1, s3, s2};
+    const int64_t R = max_rows_of(*p);
+    if (!offsets) return MOE_ERR_INVALID_ARG;
+    if ((rc = fp8_weights_ok(*p, w)) != MOE_OK) return rc;
+    if (R > 0 && (!x_perm || !h || !y_perm)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x_perm) || !aligned16(h) || !aligned16(y_perm)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w, h, y_perm, nullptr,
+                                 static_cast<hipStream_t>(stream)));
+}
+
 int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
                 void *y, void *stream) {
     int rc = check_params(p);
@@ -174,17 +217,22 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
                                      static_cast<hipStream_t>(stream)));
 }
 
-int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
-                const float *load, const void *w1, const void *w3, const void *w2, void *y,
-                float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int forward_impl(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                 const float *load, const FfnWeights &w, void *y, float *logits, moe_routing *r,
+                 void *workspace, size_t ws_bytes, void *stream) {
     int rc = check_params(p);
     if (rc != MOE_OK) return rc;
-    if (!routing_ok(r, *p) || !w_router || !w1 || !w3 || !w2 || !workspace ||
+    if (!routing_ok(r, *p) || !w_router || !w.w1 || !w.w3 || !w.w2 || !workspace ||
         (p->T > 0 && (!x || !y || !logits)))
         return MOE_ERR_INVALID_ARG;
+    if (w.s1 && (rc = fp8_weights_ok(*p, w)) != MOE_OK) return rc;
     if (ws_bytes < forward_ws_bytes(*p)) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w3) ||
-        !aligned16(w2) || !aligned16(y) || !aligned16(workspace))
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w.w1) || !aligned16(w.w3) ||
+        !aligned16(w.w2) || !aligned16(y) || !aligned16(workspace))
         return MOE_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     const ForwardWs f = carve_forward(workspace, *p);
@@ -197,13 +245,32 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
     e = launch_dispatch(*p, C, x, *r, f.x_perm, ds, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (f.x_perm)
-        e = launch_expert_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w1, w3, w2, f.h, f.y_perm, f.claim, st);
+        e = launch_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w, f.h, f.y_perm, f.claim, st);
     else
-        e = launch_expert_ffn(*p, R, C, x, r->token_of_row, r->offsets, w1, w3, w2, f.h, f.y_perm, f.claim,
-                              st);
+        e = launch_ffn(*p, R, C, x, r->token_of_row, r->offsets, w, f.h, f.y_perm, f.claim, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
     e = launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, f.y_perm, r->row, r->gate, y, st);
     return hip_status(e);
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                const float *load, const void *w1, const void *w3, const void *w2, void *y,
+                float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
+    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, nullptr, nullptr, nullptr}, y,
+                        logits, r, workspace, ws_bytes, stream);
+}
+
+int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                    const float *load, const uint8_t *w1, const float *s1, const uint8_t *w3,
+                    const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
+                    moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
+    if (!s1 || !s3 || !s2) return MOE_ERR_INVALID_ARG;
+    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, s1, s3, s2}, y, logits, r,
+                        workspace, ws_bytes, stream);
 }
 
 const char *moe_strerror(int code) {

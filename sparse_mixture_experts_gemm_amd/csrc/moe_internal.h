@@ -80,6 +80,15 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
                              const void *w3, const void *w2, void *h, void *y_perm, int32_t *claim,
                              hipStream_t st);
 
+// One-byte (E4M3) expert weights with fp32 row scales: the weight-streaming
+// kernel only (bf16 layer, cap <= 32 rows per expert, d and d_ff multiples of
+// 128).  fp8_ffn_supported tells whether a layer qualifies.
+bool fp8_ffn_supported(const moe_params &p);
+hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
+                                 const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
+                                 const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
+                                 void *y_perm, hipStream_t st);
+
 hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
                           const int32_t *row, const float *gate, void *y, hipStream_t st);
 
