@@ -30,6 +30,9 @@ def parse():
     ap.add_argument("--workload", default="mixtral",
                     choices=["tiny", "mixtral", "fine64", "skew", "decode"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--fp8-weights", action="store_true",
+                    help="expert weights as E4M3 codes with fp32 row scales (weight-streaming layers: "
+                         "capacity <= 32 rows per expert)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the step-time distribution, cold-cache steps and amd-smi sampling "
                          "(for runs under a profiler)")
@@ -39,14 +42,14 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_traffic(workload):
+def gemm_traffic(workload, fp8=False):
     """HBM-side bytes (fetched + written) of one moe_expert_ffn call (both
     grouped-GEMM launches), from the committed rocprofv3 FETCH_SIZE /
     WRITE_SIZE summary of this workload, scaled by its copy calibration.
     None when there is no summary or the GEMM source changed since."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}_traffic.md")
+    path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}{'_fp8' if fp8 else ''}_traffic.md")
     if not os.path.exists(path):
         return None
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
@@ -62,8 +65,9 @@ def gemm_traffic(workload):
     return sum(v["fetch_bytes"] + v["write_bytes"] for v in ks)
 
 
-def stage_bytes_flops(cfg, rows, active_experts, splits=1):
-    """Algorithmic work per stage (what the method must touch)."""
+def stage_bytes_flops(cfg, rows, active_experts, splits=1, fp8=False):
+    """Algorithmic work per stage (what the method must touch).  fp8: expert
+    weights of one byte plus an fp32 scale per weight row."""
     T, d, E, dff = cfg.T, cfg.d, cfg.E, cfg.d_ff
     es = 2 if cfg.dtype == "bf16" else 4
     k1 = cfg.k + 1
@@ -71,7 +75,7 @@ def stage_bytes_flops(cfg, rows, active_experts, splits=1):
     # dispatch: candidates in, routing arrays out, x rows read once, x_perm written
     dispatch_bytes = T * k1 * 8 + T * cfg.k * 17 + T * d * es + rows * d * es
     gemm_flops = rows * 6.0 * d * dff
-    gemm_weight_bytes = active_experts * 3 * d * dff * es
+    gemm_weight_bytes = active_experts * (3 * d * dff + (2 * dff + d) * 4 if fp8 else 3 * d * dff * es)
     combine_bytes = rows * d * 4 * splits + T * d * es + T * cfg.k * 8
     return dict(route_bytes=route_bytes, dispatch_bytes=dispatch_bytes, gemm_flops=gemm_flops,
                 gemm_weight_bytes=gemm_weight_bytes, combine_bytes=combine_bytes,
@@ -108,6 +112,17 @@ def main():
                    top2_gap=cfg.gap)
     dt = p.torch_dtype
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
+    fp8 = None
+    if args.fp8_weights:
+        if not (p.dtype == moe.MOE_BF16 and moe.capacity(p) <= 32 and d % 128 == 0 and cfg.d_ff % 128 == 0):
+            print(f"bench.py: --fp8-weights needs a bf16 layer with capacity <= 32 and d, d_ff multiples of 128; "
+                  f"{cfg.name} has capacity {moe.capacity(p)}", file=sys.stderr)
+            sys.exit(2)
+        fp8 = {}
+        for n in ("w1", "w3", "w2"):
+            fp8["q" + n[1]], fp8["s" + n[1]] = moe_synth.quantize_rows_e4m3(L[n])
+            L[n] = None
+        torch.cuda.empty_cache()
     R = moe.max_rows(p)
 
     load = None
@@ -128,7 +143,11 @@ def main():
     ws = moe.alloc_workspace(p, dev)
 
     def step():
-        moe.forward(p, L["x"], L["w_router"], L["bias"], load, L["w1"], L["w3"], L["w2"], y, logits, r, ws)
+        if fp8:
+            moe.forward_fp8(p, L["x"], L["w_router"], L["bias"], load, fp8["q1"], fp8["s1"], fp8["q3"], fp8["s3"],
+                            fp8["q2"], fp8["s2"], y, logits, r, ws)
+        else:
+            moe.forward(p, L["x"], L["w_router"], L["bias"], load, L["w1"], L["w3"], L["w2"], y, logits, r, ws)
 
     for _ in range(args.warmup):
         step()
@@ -176,14 +195,18 @@ def main():
         if e: e[1].record()
         moe.dispatch(p, L["x"], r, x_perm, wsd)
         if e: e[2].record()
-        moe.expert_ffn(p, x_perm, r.offsets, L["w1"], L["w3"], L["w2"], h, y_perm)
+        if fp8:
+            moe.expert_ffn_fp8(p, x_perm, r.offsets, fp8["q1"], fp8["s1"], fp8["q3"], fp8["s3"], fp8["q2"],
+                               fp8["s2"], h, y_perm)
+        else:
+            moe.expert_ffn(p, x_perm, r.offsets, L["w1"], L["w3"], L["w2"], h, y_perm)
         if e: e[3].record()
         moe.combine(p, y_perm, r.row, r.gate, y)
         if e: e[4].record()
     torch.cuda.synchronize()
     st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])  # ms
     st_ms = st.mean(axis=0)
-    work = stage_bytes_flops(cfg, rows, active, moe.ffn_splits(p))
+    work = stage_bytes_flops(cfg, rows, active, moe.ffn_splits(p), fp8=bool(fp8))
     t_route, t_disp, t_ffn, t_comb = (float(v) for v in st_ms)
     gemm_tflops = work["gemm_flops"] / (t_ffn * 1e-3) / 1e12
     stages = {
@@ -203,14 +226,15 @@ def main():
                 "frac": gemm_tflops / PEAK_MFMA_TFLOPS, "traffic": None}
     if args.workload == "decode":
         gbs = work["gemm_weight_bytes"] / (t_ffn * 1e-3) / 1e9
-        roofline = {"kernel": "expert grouped GEMM (weight streaming)", "bound": "hbm", "achieved": gbs,
+        roofline = {"kernel": "expert grouped GEMM (weight streaming" + (", E4M3 weights)" if fp8 else ")"),
+                    "bound": "hbm", "achieved": gbs,
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}
 
-    roofline["traffic"] = gemm_traffic(args.workload)
+    roofline["traffic"] = gemm_traffic(args.workload, fp8=bool(fp8))
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(cfg, L, load, args.cpu_seconds)
+        cpu = cpu_baseline(cfg, L, load, args.cpu_seconds, fp8)
 
     out = {
         "metric": METRIC, "value": T / (ms_per_step * 1e-3), "unit": "tokens/s", "n_gpus": 1,
@@ -221,7 +245,8 @@ def main():
                                + (f" bias={cfg.bias} lambda={cfg.lam}" if cfg.bias != "none" else ""),
                    "T": T, "d": d, "E": E, "k": k, "d_ff": cfg.d_ff, "capacity_factor": cfg.cf,
                    "rows": rows, "dropped": int(totals[1]), "rerouted": int(totals[2]),
-                   "parallelism": "single GPU, all experts resident"},
+                   "parallelism": "single GPU, all experts resident",
+                   "expert_weights": "fp8 e4m3 codes + fp32 row scales" if fp8 else cfg.dtype},
         "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
         "mfma_util_pct": 100.0 * gemm_tflops / PEAK_MFMA_TFLOPS,
         "stages": stages,
@@ -279,16 +304,22 @@ def smi_under_load(step, torch, cap_s=8.0):
         return None
 
 
-def cpu_baseline(cfg, L, load, target_s):
+def cpu_baseline(cfg, L, load, target_s, fp8=None):
     """The oracle as it stands, on the host cores, on a bounded sample: router
     logits, ranking and dispatch for every token (the capacity couples them),
-    expert FFN + combine for a sample of tokens; reported per token."""
+    expert FFN + combine for a sample of tokens; reported per token.  fp8: the
+    expert FFN runs on the oracle's dequantised weights (double)."""
     import numpy as np
     import oracle
 
     oracle.lib()
     print("[bench] cpu baseline: copying inputs to host", file=sys.stderr, flush=True)
     c = {n: (oracle._np(v) if v is not None else None) for n, v in L.items()}
+    xe = c["x"]
+    if fp8:
+        for j in ("1", "3", "2"):
+            c["w" + j] = oracle.dequant_rows(fp8["q" + j].cpu().numpy(), fp8["s" + j].cpu().numpy())
+        xe = L["x"].float().cpu().numpy().astype(np.float64)
     ld = None if load is None else load.cpu().numpy().astype(np.float32)
     T = cfg.T
     t0 = time.perf_counter()
@@ -301,12 +332,12 @@ def cpu_baseline(cfg, L, load, target_s):
     # target_s seconds of expert work
     n = max(2, oracle.num_threads())
     t1 = time.perf_counter()
-    oracle.layer_tokens(np.arange(n, dtype=np.int32), c["x"], c["w1"], c["w3"], c["w2"], disp["eid"], disp["gate64"])
+    oracle.layer_tokens(np.arange(n, dtype=np.int32), xe, c["w1"], c["w3"], c["w2"], disp["eid"], disp["gate64"])
     per_tok = (time.perf_counter() - t1) / n
     n2 = int(max(2, min(T - n, target_s / max(per_tok, 1e-6))))
     toks = np.arange(n, n + n2, dtype=np.int32)
     t2 = time.perf_counter()
-    oracle.layer_tokens(toks, c["x"], c["w1"], c["w3"], c["w2"], disp["eid"], disp["gate64"])
+    oracle.layer_tokens(toks, xe, c["w1"], c["w3"], c["w2"], disp["eid"], disp["gate64"])
     t_ffn = time.perf_counter() - t2
     per_token_s = t_ffn / n2 + t_route / T
     cpu_model = None

@@ -223,6 +223,19 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 __device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// LDS read issued as inline assembly, for the weight-streaming kernels: the
+// compiler's wait-count pass then does not take it for a read of a buffer
+// that a stage load in flight may still write, and adds no wait for all loads
+// at the head of the K loop (the explicit vmcnt wait and the barrier before
+// the read order the stage being read).  Ready only after the lgkmcnt wait
+// that names it.
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t lds_read16_async(const char *p) {
+    u32x4_t v;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"((uint32_t)(uintptr_t)(const lds_char_t *)p) : "memory");
+    return v;
+}
+
 // Scheduling hints: interleave one group of `n` instructions of a class.
 #define SCHED_MFMA(n) __builtin_amdgcn_sched_group_barrier(0x008, n, 0)
 #define SCHED_DSR(n) __builtin_amdgcn_sched_group_barrier(0x100, n, 0)
@@ -707,38 +720,49 @@ __device__ __forceinline__ void sk_issue(const SkThread &g, char *stage, uint32_
     for (int j = 0; j < sk_lb<MODE>(); j++) {
         const int grp = g.wave * sk_lb<MODE>() + j;  // 8-row group of the B part
         const int src = MODE == kGateUp ? grp >> 3 : 0;  // gate-up: groups 8.. are W3
-        g2lds16(g.b_base[src] + g.b_off[j] + kb, stage + kSkA + grp * 1024);
+        g2lds16((src ? g.b_base[1] : g.b_base[0]) + g.b_off[j] + kb, stage + kSkA + grp * 1024);
     }
-}
-
-// Fragment of tile row `row` (16-row block base + lane % 16), logical chunk
-// c = 4 * sub-step + lane / 16, through the stage's XOR swizzle.
-__device__ __forceinline__ uint4 sk_frag(const char *part, int row, int c) {
-    return lds_read16(part + row * kRowBytes + ((c ^ swz(row)) << 4));
 }
 
 template <int MODE, int NB>
 __device__ __forceinline__ void sk_compute(const char *stage, int wave, int lane, f32x4_t (&acc)[2][2]) {
     constexpr bool kF16 = MODE == kDown;
     const int r16 = lane & 15, kq = lane >> 4;
+    // tile row r (16-row block base + lane % 16), chunk c = 4 * sub-step +
+    // lane / 16, through the stage's XOR swizzle; gate-up: W1 rows 16w.. and
+    // the same W3 rows (64 further); down: W2 rows 32w.. and 32w+16..  Every
+    // fragment of the stage is read, then one wait.
+    const int rb0 = (MODE == kGateUp ? 16 : 32) * wave + r16;
+    const int rb1 = (MODE == kGateUp ? kSkBN + 16 * wave : 32 * wave + 16) + r16;
+    u32x4_t a[2][2], b[2][2];  // [sub-step][16-row block or weight fragment]
 #pragma unroll
     for (int ss = 0; ss < 2; ss++) {
         const int c = 4 * ss + kq;
-        uint4 a[2], b[2];
 #pragma unroll
-        for (int ib = 0; ib < NB; ib++) a[ib] = sk_frag(stage, ib * 16 + r16, c);
-        // gate-up: W1 rows 16w.. and the same W3 rows (64 further); down:
-        // W2 rows 32w.. and 32w+16..
-        b[0] = sk_frag(stage + kSkA, (MODE == kGateUp ? 16 : 32) * wave + r16, c);
-        b[1] = sk_frag(stage + kSkA, (MODE == kGateUp ? kSkBN + 16 * wave : 32 * wave + 16) + r16, c);
+        for (int ib = 0; ib < 2; ib++) {
+            const int row = ib * 16 + r16;
+            a[ss][ib] = lds_read16_async(stage + row * kRowBytes + ((c ^ swz(row)) << 4));
+        }
+        b[ss][0] = lds_read16_async(stage + kSkA + rb0 * kRowBytes + ((c ^ swz(rb0)) << 4));
+        b[ss][1] = lds_read16_async(stage + kSkA + rb1 * kRowBytes + ((c ^ swz(rb1)) << 4));
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]), "+v"(b[0][0]), "+v"(b[0][1]),
+                   "+v"(b[1][0]), "+v"(b[1][1])
+                 :
+                 : "memory");
+#pragma unroll
+    for (int ss = 0; ss < 2; ss++) {
+        uint4 b0 = __builtin_bit_cast(uint4, b[ss][0]), b1 = __builtin_bit_cast(uint4, b[ss][1]);
         if (kF16) {
-            b[0] = bf16x8_to_f16x8(b[0]);
-            b[1] = bf16x8_to_f16x8(b[1]);
+            b0 = bf16x8_to_f16x8(b0);
+            b1 = bf16x8_to_f16x8(b1);
         }
 #pragma unroll
         for (int ib = 0; ib < NB; ib++) {
-            acc[ib][0] = mfma16<kF16>(a[ib], b[0], acc[ib][0]);
-            acc[ib][1] = mfma16<kF16>(a[ib], b[1], acc[ib][1]);
+            const uint4 av = __builtin_bit_cast(uint4, a[ss][ib]);
+            acc[ib][0] = mfma16<kF16>(av, b0, acc[ib][0]);
+            acc[ib][1] = mfma16<kF16>(av, b1, acc[ib][1]);
         }
     }
 }
@@ -889,7 +913,7 @@ __device__ __forceinline__ void sk8_issue(const Sk8Thread &g, char *stage, int k
     for (int j = 0; j < 4; j++) {
         const int grp = g.wave * 4 + j;                  // 8-row group of the B part
         const int src = MODE == kGateUp ? grp >> 3 : 0;  // gate-up: groups 8.. are W3
-        g2lds16(g.b_base[src] + g.b_off[j] + kq, stage + kSk8A + grp * 1024);
+        g2lds16((src ? g.b_base[1] : g.b_base[0]) + g.b_off[j] + kq, stage + kSk8A + grp * 1024);
     }
 }
 
@@ -916,26 +940,49 @@ __device__ __forceinline__ void sk8_compute(const char *stage, int wave, int lan
     const int r16 = lane & 15, kq = lane >> 4;
     const int rb0 = (MODE == kGateUp ? 16 : 32) * wave + r16;
     const int rb1 = (MODE == kGateUp ? kSkBN + 16 * wave : 32 * wave + 16) + r16;
+    // The stage's 128 K elements are taken in an order of their own (a dot
+    // product does not depend on the order of its terms, as long as both
+    // operands follow it): for sub-step pair pr, lane quarter kq reads one
+    // 16-byte chunk 4 pr + kq of a weight row (16 K elements) and spends its
+    // halves on sub-steps 2 pr and 2 pr + 1; the x fragments are the 8
+    // elements at the same K, chunk 8 pr + 2 kq + half of the 256-byte row.
+    // Every fragment of the stage is read, then one wait.
+    u32x4_t q[2][2], a[2][2][2];  // [pair][weight fragment], [pair][half][16-row block]
 #pragma unroll
-    for (int ss = 0; ss < 4; ss++) {
-        // A: 8 elements at k = 32 ss + 8 kq, chunk 4 ss + kq of the row;
-        // B: 8 bytes at the same k, half kq & 1 of chunk 2 ss + kq / 2
-        const int c = 4 * ss + kq, cb = 2 * ss + (kq >> 1), hb = (kq & 1) * 8;
-        uint4 a[2];
+    for (int pr = 0; pr < 2; pr++) {
+        const int cb = 4 * pr + kq;
+        q[pr][0] = lds_read16_async(stage + kSk8A + rb0 * 128 + ((cb ^ swz(rb0)) << 4));
+        q[pr][1] = lds_read16_async(stage + kSk8A + rb1 * 128 + ((cb ^ swz(rb1)) << 4));
 #pragma unroll
-        for (int ib = 0; ib < NB; ib++) {
-            const int row = ib * 16 + r16;
-            a[ib] = lds_read16(stage + row * 256 + ((c ^ swz16(row)) << 4));
-        }
-        const uint2 q0 = *reinterpret_cast<const uint2 *>(stage + kSk8A + rb0 * 128 + ((cb ^ swz(rb0)) << 4) + hb);
-        const uint2 q1 = *reinterpret_cast<const uint2 *>(stage + kSk8A + rb1 * 128 + ((cb ^ swz(rb1)) << 4) + hb);
-        const uint4 b0 = fp8x8_widen<kF16>(q0), b1 = fp8x8_widen<kF16>(q1);
+        for (int hf = 0; hf < 2; hf++) {
+            const int c = 8 * pr + 2 * kq + hf;
 #pragma unroll
-        for (int ib = 0; ib < NB; ib++) {
-            acc[ib][0] = mfma16<kF16>(a[ib], b0, acc[ib][0]);
-            acc[ib][1] = mfma16<kF16>(a[ib], b1, acc[ib][1]);
+            for (int ib = 0; ib < 2; ib++) {
+                const int row = ib * 16 + r16;
+                a[pr][hf][ib] = lds_read16_async(stage + row * 256 + ((c ^ swz16(row)) << 4));
+            }
         }
     }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(q[0][0]), "+v"(q[0][1]), "+v"(q[1][0]), "+v"(q[1][1]), "+v"(a[0][0][0]), "+v"(a[0][0][1]),
+                   "+v"(a[0][1][0]), "+v"(a[0][1][1]), "+v"(a[1][0][0]), "+v"(a[1][0][1]), "+v"(a[1][1][0]),
+                   "+v"(a[1][1][1])
+                 :
+                 : "memory");
+#pragma unroll
+    for (int pr = 0; pr < 2; pr++)
+#pragma unroll
+        for (int hf = 0; hf < 2; hf++) {
+            const u32x4_t w0 = q[pr][0], w1 = q[pr][1];
+            const uint4 b0 = fp8x8_widen<kF16>(hf ? make_uint2(w0.z, w0.w) : make_uint2(w0.x, w0.y));
+            const uint4 b1 = fp8x8_widen<kF16>(hf ? make_uint2(w1.z, w1.w) : make_uint2(w1.x, w1.y));
+#pragma unroll
+            for (int ib = 0; ib < NB; ib++) {
+                const uint4 av = __builtin_bit_cast(uint4, a[pr][hf][ib]);
+                acc[ib][0] = mfma16<kF16>(av, b0, acc[ib][0]);
+                acc[ib][1] = mfma16<kF16>(av, b1, acc[ib][1]);
+            }
+        }
 }
 
 #define SK8_STEP(I, cur, nxt)                                                            \
@@ -1008,6 +1055,15 @@ __global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny_fp8(
         const int gn = min(n0 + (MODE == kGateUp ? (row & (kSkBN - 1)) : row), N - 1);
         g.b_off[j] = (uint32_t)gn * K + c * 16;
     }
+    // the row scales of the lane's output columns, fetched before the K loop
+    // (they are the oldest loads, so the loop's first wait covers them)
+    const float *s0e = S0 + (size_t)ti.e * N, *s1e = (MODE == kGateUp ? S1 : S0) + (size_t)ti.e * N;
+    float sc[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++) {
+        const int col = MODE == kGateUp ? n0 + wave * 16 + (lane & 15) : n0 + wave * 32 + jb * 16 + (lane & 15);
+        sc[jb] = (MODE == kGateUp && jb == 1 ? s1e : s0e)[min(col, N - 1)];
+    }
     const int nk = K / kSk8K;
     f32x4_t acc[2][2];
 #pragma unroll
@@ -1022,7 +1078,6 @@ __global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny_fp8(
 
     // epilogue: the lane holds column lane % 16, rows 4 * (lane / 16) + q;
     // the weight rows' scales multiply the accumulators first
-    const float *s0e = S0 + (size_t)ti.e * N, *s1e = (MODE == kGateUp ? S1 : S0) + (size_t)ti.e * N;
 #pragma unroll
     for (int ib = 0; ib < 2; ib++)
 #pragma unroll
@@ -1033,12 +1088,12 @@ __global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny_fp8(
                 const int col = n0 + wave * 16 + (lane & 15);
                 if (col < N)
                     static_cast<uint16_t *>(out_v)[(size_t)m * N + col] =
-                        f32_to_f16_sat(silu_mul(acc[ib][0][q] * s0e[col], acc[ib][1][q] * s1e[col]));
+                        f32_to_f16_sat(silu_mul(acc[ib][0][q] * sc[0], acc[ib][1][q] * sc[1]));
             } else {
 #pragma unroll
                 for (int jb = 0; jb < 2; jb++) {
                     const int col = n0 + wave * 32 + jb * 16 + (lane & 15);
-                    if (col < N) static_cast<float *>(out_v)[(size_t)m * N + col] = acc[ib][jb][q] * s0e[col];
+                    if (col < N) static_cast<float *>(out_v)[(size_t)m * N + col] = acc[ib][jb][q] * sc[jb];
                 }
             }
         }
