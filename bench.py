@@ -288,10 +288,16 @@ def smi_under_load(step, torch, cap_s=8.0):
     except OSError:
         return None
     t_end = time.perf_counter() + cap_s
+    pending = []  # keep three batches queued so that the GPU never idles between them
     while proc.poll() is None and time.perf_counter() < t_end:
         for _ in range(20):
             step()
-        torch.cuda.synchronize()
+        ev = torch.cuda.Event()
+        ev.record()
+        pending.append(ev)
+        if len(pending) > 3:
+            pending.pop(0).synchronize()
+    torch.cuda.synchronize()
     try:
         out, _ = proc.communicate(timeout=max(1.0, t_end - time.perf_counter()))
         g = json.loads(out)["gpu_data"][0]
