@@ -53,6 +53,8 @@ def lib():
         L.oracle_ffn_rows.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_layer_tokens.argtypes = [i32, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
         L.oracle_combine.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        L.oracle_dynamic_capacity_factor.argtypes = [i64]
+        L.oracle_dynamic_capacity_factor.restype = f64
         L.oracle_fp8_e4m3_value.argtypes = [ctypes.c_uint8]
         L.oracle_fp8_e4m3_value.restype = f64
         L.oracle_fp8_e4m3_decode.argtypes = [i64, P, P]
@@ -100,6 +102,15 @@ def num_threads() -> int:
 
 def capacity(T: int, k: int, E: int, cf: float) -> int:
     return int(lib().oracle_capacity(T, k, E, float(np.float32(cf))))
+
+
+def dynamic_capacity_factor(T: int) -> float:
+    return float(lib().oracle_dynamic_capacity_factor(T))
+
+
+def capacity_dynamic(T: int, k: int, E: int) -> int:
+    """Capacity under the dynamic factor (double throughout)."""
+    return int(lib().oracle_capacity(T, k, E, dynamic_capacity_factor(T)))
 
 
 def router_logits(x, wr, bias=None) -> np.ndarray:

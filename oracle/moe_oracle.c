@@ -96,6 +96,18 @@ void oracle_dequant_rows(int64_t rows, int64_t cols, const uint8_t *q, const flo
 }
 
 /*
+ * Dynamic capacity factor (P1 §5.4: the factor grows with the batch as
+ * 1 + 0.01 * log2(batch size), 1.05 at 32).  Reading: the batch size is the
+ * number of tokens T routed together; evaluated in double; T < 1 gives 1.
+ */
+double oracle_dynamic_capacity_factor(int64_t T)
+{
+    if (T < 1)
+        return 1.0;
+    return 1.0 + 0.01 * log2((double)T);
+}
+
+/*
  * Expert capacity.  Reading: C = ceil(T*k/E * cf) evaluated in double in that
  * order (the expert_capacity formula of P2 §5.2, which gives 2 for 64 experts,
  * top-2, batch 32 and factor 1.3).  cf <= 0 means uncapped.  C never exceeds T:

@@ -37,6 +37,8 @@ MUTATIONS = {
     "glu_w2_transposed": ("acc += a[j] * elem(w2, (size_t)e * H + j, dt);", "acc += a[j] * elem(w2, (size_t)j * E + e, dt);"),
     "glu_silu_missing": ("a[j] = acc / (1.0 + exp(-acc));", "a[j] = acc;"),
     "router_weight_transposed": ("elem(wr, (size_t)e * d + i, dt)", "elem(wr, (size_t)i * E + e, dt)"),
+    "dynamic_cf_natural_log": ("return 1.0 + 0.01 * log2((double)T);", "return 1.0 + 0.01 * log((double)T);"),
+    "dynamic_cf_slope": ("return 1.0 + 0.01 * log2((double)T);", "return 1.0 + 0.1 * log2((double)T);"),
     "e4m3_bias_8": ("e - 7);", "e - 8);"),
     "e4m3_subnormal_scale": ("(double)f / 8.0, -6);", "(double)f / 8.0, -7);"),
     "e4m3_no_nan": ("if (e == 15 && f == 7)\n        return NAN;", "if (0)\n        return NAN;"),
@@ -54,6 +56,7 @@ CHECKS = [
     ("identical_experts", pins.check_identical_experts), ("expert_relabel", pins.check_expert_relabel),
     ("gate_temperature", pins.check_gate_temperature), ("gap_swap", pins.check_gap_swap),
     ("router_glu", pins.check_router_glu), ("fp8_decode", pins.check_fp8_decode),
+    ("dynamic_capacity", pins.check_dynamic_capacity),
     ("dequant_rows", pins.check_dequant_rows), ("ffn_double_elements", pins.check_ffn_double_elements),
 ]
 

@@ -57,6 +57,28 @@ def test_capacity_pins(oracle_mod):
     check_capacity(oracle_mod)
 
 
+def check_dynamic_capacity(o):
+    """The dynamic factor against the page's worked value (1.05 at a batch of
+    32), its exact values at powers of two, its floor at one token, and the
+    capacity it gives (ceil(T*k/E*cf) with cf in double)."""
+    g = GOLD["dynamic_capacity_factor_worked"]
+    assert abs(o.dynamic_capacity_factor(g["T"]) - g["cf"]) < 1e-15
+    for e in range(0, 21):
+        assert o.dynamic_capacity_factor(2 ** e) == 1.0 + 0.01 * e
+    assert o.dynamic_capacity_factor(0) == 1.0
+    assert 1.0 + 0.01 * math.log2(1000) - 1e-15 < o.dynamic_capacity_factor(1000) < 1.0 + 0.01 * math.log2(1000) + 1e-15
+    # T 4096, top-2, 8 experts: cf 1.12 -> ceil(1024 * 1.12) = 1147
+    assert o.capacity_dynamic(4096, 2, 8) == math.ceil(4096 * 2 / 8 * (1.0 + 0.01 * 12))
+    assert o.capacity_dynamic(4096, 2, 8) == 1147
+    # 32 tokens, top-2, 64 experts: ceil(1 * 1.05) = 2
+    assert o.capacity_dynamic(32, 2, 64) == 2
+    assert o.capacity_dynamic(1, 1, 1) == 1
+
+
+def test_dynamic_capacity(oracle_mod):
+    check_dynamic_capacity(oracle_mod)
+
+
 # ----------------------------------------------------------- router logits --
 
 def check_router_logits(o):
