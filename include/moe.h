@@ -109,6 +109,11 @@ typedef struct moe_params {
      * bf16 with E <= 64 and H <= 64 (MOE_ERR_UNSUPPORTED otherwise); a
      * negative value is MOE_ERR_INVALID_ARG. */
     int32_t router_hidden;
+    /* 1: the capacity factor grows with the batch, cf = 1 + 0.01 * log2(T)
+     * in double ("GPT-4稀疏激活真相" §5.4; 1.05 at 32 tokens), and
+     * capacity_factor is ignored; 0: capacity_factor as given.  Any other
+     * value is MOE_ERR_INVALID_ARG. */
+    int32_t dynamic_capacity;
 } moe_params;
 
 /*

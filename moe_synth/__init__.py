@@ -121,6 +121,7 @@ class MoEConfig:
     aux_coef: float = 0.01
     tau: float = 0.0                # gate temperature (0: plain softmax)
     gap: float = 0.0                # top-2 gap threshold (0: off)
+    dyn_cap: int = 0                # 1: capacity factor 1 + 0.01 log2(T) (cf ignored)
     note: str = ""
     extra: dict = field(default_factory=dict)
 

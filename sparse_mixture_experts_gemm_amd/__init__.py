@@ -35,7 +35,7 @@ class MoeParams(ctypes.Structure):
                 ("capacity_factor", ctypes.c_float), ("reroute", ctypes.c_int32),
                 ("lam", ctypes.c_float), ("aux_coef", ctypes.c_float), ("dtype", ctypes.c_int32),
                 ("gate_temperature", ctypes.c_float), ("top2_gap", ctypes.c_float),
-                ("router_hidden", ctypes.c_int32)]
+                ("router_hidden", ctypes.c_int32), ("dynamic_capacity", ctypes.c_int32)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -102,11 +102,12 @@ class Params:
     gate_temperature: float = 0.0  # 0: plain softmax gates
     top2_gap: float = 0.0          # 0: no top-2 gap threshold
     router_hidden: int = 0         # 0: linear router; H: two-layer router (w_router = W1 [H][d] then W2 [E][H])
+    dynamic_capacity: int = 0      # 1: capacity factor 1 + 0.01 log2(T), capacity_factor ignored
 
     def c(self) -> MoeParams:
         return MoeParams(self.T, self.d, self.E, self.k, self.d_ff, self.capacity_factor,
                          self.reroute, self.lam, self.aux_coef, self.dtype, self.gate_temperature,
-                         self.top2_gap, self.router_hidden)
+                         self.top2_gap, self.router_hidden, self.dynamic_capacity)
 
     @property
     def torch_dtype(self):

@@ -27,6 +27,7 @@ int check_params(const moe_params *p) {
     if (!(p->gate_temperature >= 0.0f) || isinf(p->gate_temperature)) return MOE_ERR_INVALID_ARG;
     if (!(p->top2_gap >= 0.0f) || isinf(p->top2_gap)) return MOE_ERR_INVALID_ARG;
     if (p->router_hidden < 0) return MOE_ERR_INVALID_ARG;
+    if (p->dynamic_capacity != 0 && p->dynamic_capacity != 1) return MOE_ERR_INVALID_ARG;
     if (p->router_hidden > 0 && (p->dtype != MOE_BF16 || p->E > 64 || p->router_hidden > 64))
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;

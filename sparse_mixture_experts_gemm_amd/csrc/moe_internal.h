@@ -55,11 +55,14 @@ hipError_t launch_route(const moe_params &p, const void *x, const void *wr, cons
 hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
                            void *x_perm, const DispatchScratch &ws, hipStream_t st);
 
-// Capacity C = min(T, ceil(T*k/E * capacity_factor)) evaluated in double;
-// capacity_factor <= 0 means uncapped (C = T).
+// Capacity C = min(T, ceil(T*k/E * cf)) evaluated in double, cf the
+// capacity_factor, or 1 + 0.01 * log2(T) with dynamic_capacity; a
+// capacity_factor <= 0 (without dynamic_capacity) means uncapped (C = T).
 inline int64_t capacity_rows(const moe_params &p) {
-    if (p.capacity_factor <= 0.0f) return p.T;
-    const double c = ceil((double)p.T * (double)p.k / (double)p.E * (double)p.capacity_factor);
+    if (!p.dynamic_capacity && p.capacity_factor <= 0.0f) return p.T;
+    const double cf = p.dynamic_capacity ? (p.T >= 1 ? 1.0 + 0.01 * log2((double)p.T) : 1.0)
+                                         : (double)p.capacity_factor;
+    const double c = ceil((double)p.T * (double)p.k / (double)p.E * cf);
     int64_t C = (int64_t)c;
     if (C > p.T) C = p.T;
     if (C < 0) C = 0;

@@ -126,6 +126,17 @@ def test_strerror():
         assert isinstance(moe.strerror(c), str) and moe.strerror(c)
 
 
+def test_dynamic_capacity_matches_oracle(oracle_mod):
+    for T, k, E in ((32, 2, 64), (1000, 2, 12), (4096, 2, 8), (1, 1, 1), (0, 2, 8), (8191, 4, 16), (3, 2, 2)):
+        p = P(T=T, k=k, E=E, capacity_factor=-1.0, dynamic_capacity=1)
+        assert moe.capacity(p) == oracle_mod.capacity_dynamic(T, k, E), (T, k, E)
+    bad = P(dynamic_capacity=2)
+    r = moe.MoeRouting()
+    rc = moe.lib().moe_forward(ctypes.byref(bad.c()), None, None, None, None, None, None, None, None,
+                               None, ctypes.byref(r), None, 0, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+
+
 def fp8_ffn_rc(p, s_ptr=256):
     return moe.lib().moe_expert_ffn_fp8(ctypes.byref(p.c()), 256, 256, 256, s_ptr, 256, s_ptr, 256, s_ptr,
                                         256, 256, None)

@@ -90,7 +90,7 @@ def params(cfg, T=None, **over):
     kw = dict(T=cfg.T if T is None else T, d=cfg.d, E=cfg.E, k=cfg.k, d_ff=cfg.d_ff,
               capacity_factor=cfg.cf, reroute=cfg.reroute, lam=cfg.lam, aux_coef=cfg.aux_coef,
               dtype=moe.MOE_BF16 if cfg.dtype == "bf16" else moe.MOE_F32, gate_temperature=cfg.tau,
-              top2_gap=cfg.gap)
+              top2_gap=cfg.gap, dynamic_capacity=cfg.dyn_cap)
     kw.update(over)
     return moe.Params(**kw)
 
@@ -109,7 +109,8 @@ def load_for(cfg, L, T):
 def routing_vs_oracle(p, rc, logits_np, load_np, lam, nan_gates=False):
     """Oracle routing from the GPU's logits; every array bit-exact."""
     cand, cs = oracle.route(logits_np, p.k, load_np, lam, p.top2_gap)
-    C = oracle.capacity(p.T, p.k, p.E, p.capacity_factor)
+    C = (oracle.capacity_dynamic(p.T, p.k, p.E) if p.dynamic_capacity
+         else oracle.capacity(p.T, p.k, p.E, p.capacity_factor))
     ref = oracle.dispatch(cand, cs, p.E, p.k, C, p.reroute, p.aux_coef,
                           p.gate_temperature if p.gate_temperature > 0 else 1.0)
     ref["cand"], ref["cand_score"] = cand, cs
@@ -309,6 +310,8 @@ EDGE = {
     "top2_gap_mfma_e64_k3": dict(T=700, E=64, k=3, cf=1.5, gap=0.05),
     "top2_gap_valu_f32": dict(T=300, E=6, k=2, d=128, d_ff=128, dtype="f32", gap=0.2),
     "top2_gap_valu_e100": dict(T=400, E=100, k=2, d=128, d_ff=64, gap=0.05),
+    # dynamic capacity factor 1 + 0.01 log2(T): 1.0997 at T 1000, C 184 (cf 0.25 ignored)
+    "dynamic_capacity": dict(T=1000, E=12, k=2, cf=0.25, dyn_cap=1),
 }
 
 
