@@ -278,18 +278,16 @@ def step_times(step, n, torch, before=None):
             "p90": float(np.percentile(t, 90)), "n": n}
 
 
-def smi_under_load(step, torch, cap_s=8.0):
-    """Socket power and per-XCD shader clocks from `amd-smi metric`, sampled
-    in a child process while steps run back to back; None if unavailable."""
+def smi_under_load(step, torch, ramp_s=2.0, cap_s=30.0):
+    """Socket power and per-XCD shader clocks from `amd-smi metric` under
+    sustained load: steps run back to back for ramp_s first (power and clock
+    settle within about a second; a sample taken at once reads the idle
+    state), then the tool runs in a child process while the steps go on until
+    it has exited.  None if unavailable or slower than cap_s."""
     import subprocess
-    try:
-        proc = subprocess.Popen(["amd-smi", "metric", "--clock", "--power", "--json"],
-                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
-    except OSError:
-        return None
-    t_end = time.perf_counter() + cap_s
     pending = []  # keep three batches queued so that the GPU never idles between them
-    while proc.poll() is None and time.perf_counter() < t_end:
+
+    def batch():
         for _ in range(20):
             step()
         ev = torch.cuda.Event()
@@ -297,16 +295,32 @@ def smi_under_load(step, torch, cap_s=8.0):
         pending.append(ev)
         if len(pending) > 3:
             pending.pop(0).synchronize()
-    torch.cuda.synchronize()
+
+    t_ramp = time.perf_counter() + ramp_s
+    while time.perf_counter() < t_ramp:
+        batch()
     try:
-        out, _ = proc.communicate(timeout=max(1.0, t_end - time.perf_counter()))
+        proc = subprocess.Popen(["amd-smi", "metric", "--clock", "--power", "--json"],
+                                stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+    except OSError:
+        torch.cuda.synchronize()
+        return None
+    t_end = time.perf_counter() + cap_s
+    while proc.poll() is None and time.perf_counter() < t_end:
+        batch()
+    torch.cuda.synchronize()
+    if proc.poll() is None:
+        proc.kill()
+        proc.communicate()
+        return None
+    try:
+        out, _ = proc.communicate()
         g = json.loads(out)["gpu_data"][0]
         clk = g["clock"]
         xcd = [clk[k]["clk"]["value"] for k in sorted(clk) if k.startswith("gfx_")]
         return {"socket_power_w": g["power"]["socket_power"]["value"], "gfx_clk_mhz": xcd,
-                "source": "amd-smi metric --clock --power, sampled while steps ran"}
+                "source": f"amd-smi metric --clock --power, sampled after {ramp_s:.0f} s of back-to-back steps"}
     except Exception:
-        proc.kill()
         return None
 
 
