@@ -85,7 +85,7 @@ def stage_bytes_flops(cfg, rows, active_experts, splits=1, fp8=False):
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs the MoE layer on one GPU (all experts resident in its HBM); "
+        print("bench.py: the MoE layer runs on one GPU here (all experts resident in its HBM); "
               "multi-GPU runs are not implemented. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
 
