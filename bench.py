@@ -42,41 +42,58 @@ def parse():
     return ap.parse_args()
 
 
-def gemm_traffic(workload, fp8=False):
-    """HBM-side bytes (fetched + written) of one moe_expert_ffn call (both
-    grouped-GEMM launches), from the committed rocprofv3 FETCH_SIZE /
-    WRITE_SIZE summary of this workload, scaled by its copy calibration.
-    None when there is no summary or the GEMM source changed since."""
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_gemm_amd", "csrc")
+# the source file of each stage's kernels: a committed counter summary is used
+# for a stage only while that file still has the hash recorded with it
+STAGE_SOURCE = {"route": "route.hip", "dispatch": "dispatch.hip", "expert_ffn": "expert_gemm.hip",
+                "combine": "combine.hip"}
+STAGE_KERNELS = {"route": ("route_",), "dispatch": ("dispatch_",), "expert_ffn": ("grouped_gemm",),
+                 "combine": ("combine_", "zero_fill")}
+
+
+def counter_traffic(workload, fp8=False):
+    """HBM-side bytes (fetched + written) per forward pass of each stage's
+    kernels, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of
+    this workload, scaled by its copy calibration.  A stage is left out when
+    its kernel source changed since the counters were taken."""
     import hashlib
     import re
     path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}{'_fp8' if fp8 else ''}_traffic.md")
     if not os.path.exists(path):
-        return None
+        return {}
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
     if not m:
-        return None
+        return {}
     blob = json.loads(m.group(1))
-    src = os.path.join(ROOT, "sparse_mixture_experts_gemm_amd", "csrc", "expert_gemm.hip")
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != blob.get("expert_gemm_hip_sha256"):
-        return None
-    ks = [v for k, v in blob["kernels"].items() if k.startswith("grouped_gemm")]
-    if not ks:
-        return None
-    return sum(v["fetch_bytes"] + v["write_bytes"] for v in ks)
+    out = {}
+    for stage, src in STAGE_SOURCE.items():
+        sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+        if blob.get("sources", {}).get(src) != sha:
+            continue
+        ks = [v for k, v in blob["kernels"].items() if k.startswith(STAGE_KERNELS[stage])]
+        if ks:
+            out[stage] = sum(v["fetch_bytes"] + v["write_bytes"] for v in ks)
+    return out
 
 
-def stage_bytes_flops(cfg, rows, active_experts, splits=1, fp8=False):
-    """Algorithmic work per stage (what the method must touch).  fp8: expert
-    weights of one byte plus an fp32 scale per weight row."""
-    T, d, E, dff = cfg.T, cfg.d, cfg.E, cfg.d_ff
+def stage_work(cfg, rows, active_experts, fp8=False):
+    """Algorithmic work per stage of one forward pass: what the method must
+    touch (kept rows, active experts, one read of x, one write of y), not
+    what this implementation moves.  fp8: expert weights of one byte plus an
+    fp32 scale per weight row."""
+    T, d, E, dff, k = cfg.T, cfg.d, cfg.E, cfg.d_ff, cfg.k
     es = 2 if cfg.dtype == "bf16" else 4
-    k1 = cfg.k + 1
+    k1 = k + 1
+    # route: x and the router weights read, logits and ranked candidates written
     route_bytes = T * d * es + E * d * es + T * E * 4 + T * k1 * 8
-    # dispatch: candidates in, routing arrays out, x rows read once, x_perm written
-    dispatch_bytes = T * k1 * 8 + T * cfg.k * 17 + T * d * es + rows * d * es
+    # dispatch: candidates read, the slot arrays (eid, pos, row, flag, gate) and
+    # token_of_row written (moe_forward gathers x inside the GEMM, so no copy)
+    dispatch_bytes = T * k1 * 8 + T * k * 17 + rows * 4
     gemm_flops = rows * 6.0 * d * dff
     gemm_weight_bytes = active_experts * (3 * d * dff + (2 * dff + d) * 4 if fp8 else 3 * d * dff * es)
-    combine_bytes = rows * d * 4 * splits + T * d * es + T * cfg.k * 8
+    # combine: each kept row's expert output (layer dtype) read once, y written,
+    # the slot arrays read
+    combine_bytes = rows * d * es + T * d * es + T * k * 8
     return dict(route_bytes=route_bytes, dispatch_bytes=dispatch_bytes, gemm_flops=gemm_flops,
                 gemm_weight_bytes=gemm_weight_bytes, combine_bytes=combine_bytes,
                 route_flops=2.0 * T * d * E)
@@ -142,10 +159,13 @@ def main():
     r = moe.Routing(p, dev)
     ws = moe.alloc_workspace(p, dev)
 
-    def step():
+    def step(events=None):
         if fp8:
             moe.forward_fp8(p, L["x"], L["w_router"], L["bias"], load, fp8["q1"], fp8["s1"], fp8["q3"], fp8["s3"],
                             fp8["q2"], fp8["s2"], y, logits, r, ws)
+        elif events is not None:
+            moe.forward_events(p, L["x"], L["w_router"], L["bias"], load, L["w1"], L["w3"], L["w2"], y, logits, r,
+                               ws, events)
         else:
             moe.forward(p, L["x"], L["w_router"], L["bias"], load, L["w1"], L["w3"], L["w2"], y, logits, r, ws)
 
@@ -165,6 +185,22 @@ def main():
     wall = time.perf_counter() - wall0
     ms_per_step = t0.elapsed_time(t1) / args.steps
 
+    # per-stage times of the forward pass itself: moe_forward_events enqueues
+    # the same launches as moe_forward with six events between its stages (on
+    # the launch stream); averaged over as many steps as were timed
+    stage_names = ("route", "dispatch", "gate_up", "down", "combine")
+    st_ms = None
+    if not fp8:
+        n_ev = args.steps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_ev)]
+        torch.cuda.synchronize()
+        for e in evs:
+            step(e)
+        torch.cuda.synchronize()
+        st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(5)] for e in evs])  # ms
+        st_ms = dict(zip(stage_names, (float(v) for v in st.mean(axis=0))))
+        st_ms["events_step"] = float(np.mean([e[0].elapsed_time(e[5]) for e in evs]))
+
     # distribution of single-step times (events around each step, no sync in
     # between), then cold-cache steps: a 1 GiB fill before each one evicts
     # x, the weights and the workspace from L2 and the 256 MiB last-level cache
@@ -180,57 +216,60 @@ def main():
     kept = r.kept.cpu()
     rows = int(totals[0])
     active = int((kept > 0).sum())
-
-    # per-stage times: each entry point bracketed by events on the launch stream
-    x_perm = torch.empty((max(R, 1), d), dtype=dt, device=dev)
-    h = torch.empty((max(R, 1), cfg.d_ff), dtype=torch.float16 if dt == torch.bfloat16 else dt, device=dev)
-    y_perm = moe.alloc_y_perm(p, dev)
-    wsd = moe.alloc_workspace(p, dev, dispatch_only=True)
-    n_st = max(5, min(args.steps, 30))
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(n_st)]
-    for i in range(n_st + 3):
-        e = ev[i - 3] if i >= 3 else None
-        if e: e[0].record()
-        moe.route(p, L["x"], L["w_router"], L["bias"], load, logits, r)
-        if e: e[1].record()
-        moe.dispatch(p, L["x"], r, x_perm, wsd)
-        if e: e[2].record()
-        if fp8:
-            moe.expert_ffn_fp8(p, x_perm, r.offsets, fp8["q1"], fp8["s1"], fp8["q3"], fp8["s3"], fp8["q2"],
-                               fp8["s2"], h, y_perm)
-        else:
-            moe.expert_ffn(p, x_perm, r.offsets, L["w1"], L["w3"], L["w2"], h, y_perm)
-        if e: e[3].record()
-        moe.combine(p, y_perm, r.row, r.gate, y)
-        if e: e[4].record()
-    torch.cuda.synchronize()
-    st = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(4)] for e in ev])  # ms
-    st_ms = st.mean(axis=0)
-    work = stage_bytes_flops(cfg, rows, active, moe.ffn_splits(p), fp8=bool(fp8))
-    t_route, t_disp, t_ffn, t_comb = (float(v) for v in st_ms)
-    gemm_tflops = work["gemm_flops"] / (t_ffn * 1e-3) / 1e12
-    stages = {
-        "route": {"us": t_route * 1e3, "GB/s": work["route_bytes"] / (t_route * 1e-3) / 1e9,
-                  "hbm_frac": work["route_bytes"] / (t_route * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "dispatch": {"us": t_disp * 1e3, "GB/s": work["dispatch_bytes"] / (t_disp * 1e-3) / 1e9,
-                     "hbm_frac": work["dispatch_bytes"] / (t_disp * 1e-3) / 1e9 / PEAK_HBM_GBS},
-        "expert_ffn": {"us": t_ffn * 1e3, "TFLOP/s": gemm_tflops, "mfma_frac": gemm_tflops / PEAK_MFMA_TFLOPS,
-                       "weight_GB/s": work["gemm_weight_bytes"] / (t_ffn * 1e-3) / 1e9},
-        "combine": {"us": t_comb * 1e3, "GB/s": work["combine_bytes"] / (t_comb * 1e-3) / 1e9,
-                    "hbm_frac": work["combine_bytes"] / (t_comb * 1e-3) / 1e9 / PEAK_HBM_GBS},
-    }
+    work = stage_work(cfg, rows, active, fp8=bool(fp8))
+    traffic = counter_traffic(args.workload, fp8=bool(fp8))
     layer_flops = work["route_flops"] + work["gemm_flops"]
 
-    roofline = {"kernel": "expert grouped GEMM (moe_expert_ffn: gate-up + down launches)",
-                "bound": "mfma", "achieved": gemm_tflops, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": gemm_tflops / PEAK_MFMA_TFLOPS, "traffic": None}
-    if args.workload == "decode":
-        gbs = work["gemm_weight_bytes"] / (t_ffn * 1e-3) / 1e9
-        roofline = {"kernel": "expert grouped GEMM (weight streaming" + (", E4M3 weights)" if fp8 else ")"),
-                    "bound": "hbm", "achieved": gbs,
-                    "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS, "traffic": None}
+    def hbm(nbytes, ms, stage):
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        out = {"us": ms * 1e3, "algorithmic_bytes": nbytes, "GB/s": gbs, "hbm_frac": gbs / PEAK_HBM_GBS}
+        if stage in traffic:
+            out["traffic_bytes"] = traffic[stage]
+            out["traffic_over_algorithmic"] = traffic[stage] / nbytes
+        return out
 
-    roofline["traffic"] = gemm_traffic(args.workload, fp8=bool(fp8))
+    stages = None
+    if st_ms is not None:
+        t_ffn = st_ms["gate_up"] + st_ms["down"]
+        gemm_tflops = work["gemm_flops"] / (t_ffn * 1e-3) / 1e12
+        stages = {
+            "route": hbm(work["route_bytes"], st_ms["route"], "route"),
+            "dispatch": hbm(work["dispatch_bytes"], st_ms["dispatch"], "dispatch"),
+            "expert_ffn": {"us": t_ffn * 1e3, "gate_up_us": st_ms["gate_up"] * 1e3, "down_us": st_ms["down"] * 1e3,
+                           "TFLOP/s": gemm_tflops, "mfma_frac": gemm_tflops / PEAK_MFMA_TFLOPS,
+                           "gate_up_TFLOP/s": work["gemm_flops"] * 2 / 3 / (st_ms["gate_up"] * 1e-3) / 1e12,
+                           "down_TFLOP/s": work["gemm_flops"] / 3 / (st_ms["down"] * 1e-3) / 1e12,
+                           "weight_bytes": work["gemm_weight_bytes"],
+                           "weight_GB/s": work["gemm_weight_bytes"] / (t_ffn * 1e-3) / 1e9},
+            "combine": hbm(work["combine_bytes"], st_ms["combine"], "combine"),
+            "sum_of_stages_ms": sum(st_ms[n] for n in stage_names),
+            "events_step_ms": st_ms["events_step"],
+            "source": "moe_forward_events: HIP events between the forward's own launches on its stream, "
+                      f"mean of {args.steps} steps",
+        }
+        if "expert_ffn" in traffic:
+            stages["expert_ffn"]["traffic_bytes"] = traffic["expert_ffn"]
+            stages["expert_ffn"]["traffic_over_weight_bytes"] = traffic["expert_ffn"] / work["gemm_weight_bytes"]
+        achieved_ms = t_ffn
+    else:
+        achieved_ms = None
+
+    if args.workload == "decode" or fp8:
+        # weight streaming: the expert weights' bytes against HBM bandwidth.  With
+        # one-byte weights there is no events variant; the whole step bounds it.
+        t = achieved_ms if achieved_ms is not None else ms_per_step
+        gbs = work["gemm_weight_bytes"] / (t * 1e-3) / 1e9
+        roofline = {"kernel": "expert grouped GEMM, gate-up + down launches (weight streaming"
+                              + (", E4M3 weights; timed over the whole step)" if fp8 else ")"),
+                    "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                    "traffic": traffic.get("expert_ffn"),
+                    "per_launch_work": f"{work['gemm_weight_bytes']} weight bytes ({active} active experts x 3 x d x d_ff)"}
+    else:
+        tf = work["gemm_flops"] / (achieved_ms * 1e-3) / 1e12
+        roofline = {"kernel": "expert grouped GEMM, gate-up + down launches of moe_forward",
+                    "bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
+                    "frac": tf / PEAK_MFMA_TFLOPS, "traffic": traffic.get("expert_ffn"),
+                    "per_launch_work": f"{work['gemm_flops']:.4g} flop ({rows} kept rows x 6 x d x d_ff)"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -248,7 +287,7 @@ def main():
                    "parallelism": "single GPU, all experts resident",
                    "expert_weights": "fp8 e4m3 codes + fp32 row scales" if fp8 else cfg.dtype},
         "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
-        "mfma_util_pct": 100.0 * gemm_tflops / PEAK_MFMA_TFLOPS,
+        "mfma_util_pct": (100.0 * roofline["frac"]) if roofline["bound"] == "mfma" else None,
         "stages": stages,
         "roofline": roofline,
         "cpu_baseline": cpu,
@@ -368,10 +407,36 @@ def cpu_baseline(cfg, L, load, target_s, fp8=None):
                 break
     except OSError:
         pass
+    # the tiny fp32 layer in full on one thread: route, dispatch, expert FFN
+    # and combine for all of its tokens
+    tiny = tiny_single_thread(oracle)
     return {"value": 1.0 / per_token_s, "unit": "tokens/s", "cores": oracle.num_threads(), "kind": "oracle",
             "cpu_model": cpu_model,
             "sample": f"router logits + ranking + dispatch for all {T} tokens ({t_route:.2f} s), "
-                      f"expert FFN + combine for {n2} tokens ({t_ffn:.2f} s); rate per token"}
+                      f"expert FFN + combine for {n2} tokens ({t_ffn:.2f} s); rate per token",
+            "tiny_layer_single_thread": tiny}
+
+
+def tiny_single_thread(oracle, reps=20):
+    """The oracle's whole forward pass of the tiny fp32 layer (T 64, d 128,
+    E 8, top-2, d_ff 256, capacity factor 1.0) on one thread, best of reps."""
+    import moe_synth
+    cfg = moe_synth.CONFIGS["tiny"]
+    L = moe_synth.make_layer(cfg, "cpu")
+    c = {n: (oracle._np(v) if v is not None else None) for n, v in L.items()}
+    n0 = oracle.num_threads()
+    oracle.set_num_threads(1)
+    try:
+        best = float("inf")
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.forward(c["x"], c["w_router"], c["bias"], c["w1"], c["w3"], c["w2"], E=cfg.E, k=cfg.k, cf=cfg.cf)
+            best = min(best, time.perf_counter() - t0)
+    finally:
+        oracle.set_num_threads(n0)
+    return {"value": cfg.T / best, "unit": "tokens/s", "cores": 1, "ms_per_layer": best * 1e3,
+            "sample": f"tiny fp32 layer T={cfg.T} d={cfg.d} E={cfg.E} top-{cfg.k} d_ff={cfg.d_ff}, whole forward, "
+                      f"best of {reps}"}
 
 
 if __name__ == "__main__":

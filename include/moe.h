@@ -26,14 +26,18 @@
  *     conversions from fp32 round to nearest even.  Accumulation is fp32.
  *   - Elements of x, w_router, w1, w3, w2, x_perm and y have the element type
  *     p->dtype.  logits, bias, load, cand_score, gate and y_perm are fp32
- *     (y_perm holds the down-projection at accumulator precision, so the layer
- *     output is rounded to the element type once).  The SwiGLU activations h
- *     are fp16 in a bf16 layer (saturated at +-65504) and fp32 in an fp32
- *     layer.
- *   - y_perm is [S][R][d] with S = moe_ffn_splits(p): the down projection's
- *     reduction over d_ff may be split into S slices, each stored as an fp32
- *     partial product; the value of a row is the sum of its S slices, which
- *     moe_combine adds in slice order (deterministic, no atomics).
+ *     (y_perm [R][d] holds the down projection at accumulator precision, so
+ *     the staged layer output is rounded to the element type once).
+ *   - Intermediate precision of a bf16 layer: the SwiGLU activations h are
+ *     fp16 (saturated at +-65504); the down projection multiplies h by W2 in
+ *     fp16, W2 being narrowed from bf16 with round-toward-zero (exact for
+ *     magnitudes 2^-14 .. 65504; above 65504 a weight clamps to +-65504,
+ *     below 2^-14 it keeps fewer bits as an fp16 subnormal, below 2^-24 it
+ *     becomes 0).  moe_forward also keeps each kept row's gate-weighted
+ *     down projection in fp16 (saturated at +-65504) before the combine.
+ *     Layers whose weights or activations reach these limits are outside
+ *     the contract of a bf16 layer.  An fp32 layer keeps h and y_perm in
+ *     fp32 throughout.
  *   - Every output element listed for an entry point is written on every call.
  *   - NaN or Inf inputs are outside the contract.
  *   - Calls on different streams that share no output buffer may run
@@ -67,9 +71,9 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
  *
  * Limits: 0 <= T <= 2^20 (T = 0 is an empty batch); 1 <= E <= 256;
  * 1 <= k <= min(E, 8); d and d_ff positive multiples of 64; d <= 16384 for
- * bf16 and d <= 8192 for fp32; one expert matrix (d * d_ff elements) below
- * 4 GiB.  Other values return MOE_ERR_INVALID_ARG (sizes) or
- * MOE_ERR_UNSUPPORTED (dtype, multiples, d or d * d_ff too large).
+ * bf16 and d <= 8192 for fp32; d_ff < 2^22; one expert matrix (d * d_ff
+ * elements) below 4 GiB.  Other values return MOE_ERR_INVALID_ARG (sizes) or
+ * MOE_ERR_UNSUPPORTED (dtype, multiples, d, d_ff or d * d_ff too large).
  */
 typedef struct moe_params {
     int32_t T, d, E, k, d_ff;
@@ -148,16 +152,19 @@ int64_t moe_capacity(const moe_params *p);
  * -1 if p is invalid. */
 int64_t moe_max_rows(const moe_params *p);
 
-/* Host-side, pure: S, the number of fp32 partial products y_perm holds
- * (1 for fp32 layers); -1 if p is invalid. */
-int moe_ffn_splits(const moe_params *p);
+/* Host-side, pure: bytes of scratch moe_expert_ffn needs (the partial
+ * products of a down projection split over slices of d_ff); 0 when it needs
+ * none, or if p is invalid. */
+size_t moe_ffn_workspace_bytes(const moe_params *p);
 
 /* Host-side, pure: bytes of scratch moe_dispatch needs. */
 size_t moe_dispatch_workspace_bytes(const moe_params *p);
 
-/* Host-side, pure: bytes of workspace moe_forward needs: the dispatch scratch
- * plus h [R][d_ff] and y_perm [S][R][d] (fp32), and x_perm [R][d] only when
- * x spans 2 GiB or more (see moe_forward), each 256-byte aligned. */
+/* Host-side, pure: bytes of workspace moe_forward needs: the dispatch scratch,
+ * h [R][d_ff], the down projection's output rows (bf16: fp16 gated partial
+ * products of each d_ff slice, and each row's gate; fp32: y_perm [R][d]),
+ * and x_perm [R][d] only when x spans 2 GiB or more (see moe_forward), each
+ * 256-byte aligned. */
 size_t moe_workspace_bytes(const moe_params *p);
 
 /*
@@ -192,26 +199,29 @@ int moe_dispatch(const moe_params *p, const void *x, moe_routing *r, void *x_per
  * ("GPT-4稀疏激活真相" §3.1: Linear -> SwiGLU -> Linear per expert):
  *   for rows i in [offsets[e], offsets[e+1]):
  *     h[i]      = silu(x_perm[i] . W1[e]^T) * (x_perm[i] . W3[e]^T)
- *     y_perm[i] = h[i] . W2[e]^T   (as S partial sums over slices of d_ff)
+ *     y_perm[i] = h[i] . W2[e]^T
  *   x_perm [R][d]; w1, w3 [E][d_ff][d]; w2 [E][d][d_ff]; h [R][d_ff] (fp16
- *   for bf16, fp32 for fp32);
- *   y_perm [S][R][d] fp32.  offsets [E+1] is read on the device and must
- *   be as moe_dispatch writes them: non-decreasing, offsets[0] = 0,
- *   offsets[E] <= R and at most C rows per expert (the launch is sized by
- *   these bounds; rows beyond them are not computed).  Rows past offsets[E]
- *   of h and y_perm are left untouched.
+ *   for bf16, fp32 for fp32); y_perm [R][d] fp32.  offsets [E+1] is read on
+ *   the device and must be as moe_dispatch writes them: non-decreasing,
+ *   offsets[0] = 0, offsets[E] <= R and at most C rows per expert (the launch
+ *   is sized by these bounds; rows beyond them are not computed).  Rows past
+ *   offsets[E] of h and y_perm are left untouched.
+ *   workspace: at least moe_ffn_workspace_bytes(p) bytes, 256-B aligned (may
+ *   be NULL when that is 0).  Where the down projection is split over slices
+ *   of d_ff to fill the chip, the partial products of slices 1.. are kept
+ *   there and added to slice 0 in slice order (deterministic, no atomics).
  */
 int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offsets,
                    const void *w1, const void *w3, const void *w2, void *h, void *y_perm,
-                   void *stream);
+                   void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Stage 4, combine ("企业官网建设流程全解析" page §3, step 5: results are put
  * back in token order; "GPT-4稀疏激活真相" §4.3: weighted fusion):
  *   y[t] = sum over slots j with row[t][j] >= 0 of gate[t][j] * y_perm[row[t][j]]
- *   where a y_perm row is the sum of its S slices (added in slice order)
- * accumulated in fp32 and rounded once; a token with no kept slot gets zeros.
- *   y_perm [S][R][d] fp32; row, gate [T][k]; y [T][d].
+ * accumulated in fp32 (slot order) and rounded once; a token with no kept
+ * slot gets zeros.  y_perm [R][d] fp32 (not read when R = 0); row, gate
+ * [T][k]; y [T][d].
  */
 int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
                 void *y, void *stream);
@@ -219,14 +229,33 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
 /*
  * Stages 1-4 on one stream with no host synchronisation.  workspace holds at
  * least moe_workspace_bytes(p) bytes (256-B aligned) and is carved into the
- * dispatch scratch, h and y_perm.  When x spans less than 2 GiB the dispatch
- * copy of the token rows is not made: the gate-up GEMM reads its rows from x
- * through token_of_row (same values, one pass over x fewer); otherwise
- * x_perm is materialised in the workspace as moe_dispatch does.
+ * dispatch scratch, h and the down projection's output rows.  When x spans
+ * less than 2 GiB the dispatch copy of the token rows is not made: the
+ * gate-up GEMM reads its rows from x through token_of_row (same values, one
+ * pass over x fewer); otherwise x_perm is materialised in the workspace as
+ * moe_dispatch does.  In a bf16 layer the gates are folded into the down
+ * projection ("企业官网建设流程全解析" page §5.2: one fused forward;
+ * "MoE稀疏激活原理与工程实践" §3.2: the MoE layer's time goes to moving
+ * data): each kept row's gate multiplies its fp32 down projection (per d_ff
+ * slice) before it is stored in fp16, and the combine adds the k rows of a
+ * token (slot order, then slice order) in fp32 and rounds once.  The routing
+ * arrays and logits are those of moe_route + moe_dispatch; y agrees with the
+ * stage-by-stage result to within the fp16 rounding of the gated rows.
  */
 int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
                 const float *load, const void *w1, const void *w3, const void *w2, void *y,
                 float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * moe_forward with per-stage timing marks: events is NULL or an array of six
+ * hipEvent_t (NULL entries are skipped), recorded on `stream` before the
+ * route, the dispatch, the gate-up GEMM, the down GEMM and the combine, and
+ * after the combine.  The work enqueued is exactly that of moe_forward.
+ */
+int moe_forward_events(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                       const float *load, const void *w1, const void *w3, const void *w2, void *y,
+                       float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream,
+                       void *const *events);
 
 /*
  * One-byte expert weights ("企业官网建设流程全解析" page §5.1: the experts'
@@ -238,9 +267,11 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
  *   q1, q3 [E][d_ff][d] bytes, s1, s3 [E][d_ff] fp32; q2 [E][d][d_ff] bytes,
  *   s2 [E][d] fp32; q pointers 16-byte aligned, scales 4-byte aligned.
  * The activations are as for the bf16 layer (x_perm bf16, h fp16, y_perm
- * fp32 with a single slice).  Built for the weight-streaming (decode) regime:
+ * [R][d] fp32; the scaled weights are not narrowed).  Built for the
+ * weight-streaming (decode) regime:
  * dtype MOE_BF16, capacity C = moe_capacity(p) <= 32, d and d_ff multiples
- * of 128; other layers get MOE_ERR_UNSUPPORTED.  Otherwise as moe_expert_ffn.
+ * of 128; other layers get MOE_ERR_UNSUPPORTED.  Otherwise as moe_expert_ffn
+ * (the down projection is never split, so no workspace is needed).
  */
 int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *offsets,
                        const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,

@@ -42,6 +42,8 @@ def lib():
         P = ctypes.c_void_p
         i32, i64, f32, f64 = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_double
         L.oracle_num_threads.restype = i32
+        L.oracle_set_num_threads.argtypes = [i32]
+        L.oracle_set_num_threads.restype = None
         L.oracle_capacity.argtypes = [i64, i64, i64, f64]
         L.oracle_capacity.restype = i64
         L.oracle_router_logits.argtypes = [i32, i32, i32, i32, P, P, P, P]
@@ -98,6 +100,10 @@ def _p(a):
 
 def num_threads() -> int:
     return lib().oracle_num_threads()
+
+
+def set_num_threads(n: int) -> None:
+    lib().oracle_set_num_threads(int(n))
 
 
 def capacity(T: int, k: int, E: int, cf: float) -> int:

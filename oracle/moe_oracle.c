@@ -54,6 +54,18 @@ int oracle_num_threads(void)
 #endif
 }
 
+/* Threads of the OpenMP loops that follow (n >= 1); used to time the oracle
+ * single-threaded.  No effect on any result. */
+void oracle_set_num_threads(int n)
+{
+#ifdef _OPENMP
+    if (n >= 1)
+        omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /*
  * One-byte expert weights (P5 §5.1, expert-kernel quantisation; P3 §3.2 on
  * INT8 expert weights; P1 §2.1 counts FP8 at one byte per parameter).  Reading: the byte format is OCP 8-bit
@@ -118,9 +130,11 @@ int64_t oracle_capacity(int64_t T, int64_t k, int64_t E, double cf)
     if (cf <= 0.0)
         return T;
     double c = ceil((double)T * (double)k / (double)E * cf);
+    /* the clamp to T comes before the conversion: a factor so large (or
+     * infinite) that c does not fit an int64_t still gives C = T */
+    if (!(c < (double)T))
+        return T;
     int64_t C = (int64_t)c;
-    if (C > T)
-        C = T;
     if (C < 0)
         C = 0;
     return C;

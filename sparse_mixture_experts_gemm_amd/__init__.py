@@ -5,7 +5,8 @@ torch provides device memory and streams.  The binding refuses to run when
 the library is missing; there is no fallback.
 
 Entry points mirror the C ABI in include/moe.h: route, dispatch, expert_ffn,
-combine, forward, plus capacity / max_rows / workspace sizing.
+combine, forward (and forward_events), the one-byte-weight variants, plus
+capacity / max_rows / workspace sizing.
 """
 from __future__ import annotations
 
@@ -61,21 +62,23 @@ def lib():
         L.moe_capacity.restype = ctypes.c_int64
         L.moe_max_rows.argtypes = [PP]
         L.moe_max_rows.restype = ctypes.c_int64
-        L.moe_ffn_splits.argtypes = [PP]
-        L.moe_ffn_splits.restype = ctypes.c_int
+        L.moe_ffn_workspace_bytes.argtypes = [PP]
+        L.moe_ffn_workspace_bytes.restype = ctypes.c_size_t
         L.moe_dispatch_workspace_bytes.argtypes = [PP]
         L.moe_dispatch_workspace_bytes.restype = ctypes.c_size_t
         L.moe_workspace_bytes.argtypes = [PP]
         L.moe_workspace_bytes.restype = ctypes.c_size_t
         L.moe_route.argtypes = [PP, P, P, P, P, P, PR, P]
         L.moe_dispatch.argtypes = [PP, P, PR, P, P, ctypes.c_size_t, P]
-        L.moe_expert_ffn.argtypes = [PP, P, P, P, P, P, P, P, P]
+        L.moe_expert_ffn.argtypes = [PP, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_combine.argtypes = [PP, P, P, P, P, P]
         L.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P]
+        L.moe_forward_events.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P,
+                                         ctypes.POINTER(ctypes.c_void_p)]
         L.moe_expert_ffn_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P]
         L.moe_forward_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P]
         for f in (L.moe_route, L.moe_dispatch, L.moe_expert_ffn, L.moe_combine, L.moe_forward,
-                  L.moe_expert_ffn_fp8, L.moe_forward_fp8):
+                  L.moe_forward_events, L.moe_expert_ffn_fp8, L.moe_forward_fp8):
             f.restype = ctypes.c_int
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -122,14 +125,14 @@ def max_rows(p: Params) -> int:
     return int(lib().moe_max_rows(ctypes.byref(p.c())))
 
 
-def ffn_splits(p: Params) -> int:
-    """S: y_perm holds S fp32 partial products of the down projection."""
-    return int(lib().moe_ffn_splits(ctypes.byref(p.c())))
+def ffn_workspace_bytes(p: Params) -> int:
+    """Scratch bytes moe_expert_ffn needs (0: none)."""
+    return int(lib().moe_ffn_workspace_bytes(ctypes.byref(p.c())))
 
 
 def alloc_y_perm(p: Params, device="cuda"):
-    """y_perm [S, R, d] fp32 for moe_expert_ffn / moe_combine."""
-    return torch.empty((ffn_splits(p), max(max_rows(p), 1), p.d), dtype=torch.float32, device=device)
+    """y_perm [R, d] fp32 for moe_expert_ffn / moe_combine."""
+    return torch.empty((max(max_rows(p), 1), p.d), dtype=torch.float32, device=device)
 
 
 def dispatch_workspace_bytes(p: Params) -> int:
@@ -201,9 +204,12 @@ def dispatch(p: Params, x, r: Routing, x_perm, workspace, stream=None):
     _check(rc, "moe_dispatch")
 
 
-def expert_ffn(p: Params, x_perm, offsets, w1, w3, w2, h, y_perm, stream=None):
+def expert_ffn(p: Params, x_perm, offsets, w1, w3, w2, h, y_perm, workspace=None, stream=None):
+    """Stage 3.  workspace: a uint8 tensor of at least ffn_workspace_bytes(p)
+    bytes (None when that is 0)."""
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     rc = lib().moe_expert_ffn(ctypes.byref(p.c()), _ptr(x_perm), _ptr(offsets), _ptr(w1), _ptr(w3),
-                              _ptr(w2), _ptr(h), _ptr(y_perm), _stream(stream))
+                              _ptr(w2), _ptr(h), _ptr(y_perm), _ptr(workspace), nbytes, _stream(stream))
     _check(rc, "moe_expert_ffn")
 
 
@@ -220,6 +226,21 @@ def forward(p: Params, x, w_router, bias, load, w1, w3, w2, y, logits, r: Routin
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                            _stream(stream))
     _check(rc, "moe_forward")
+
+
+def forward_events(p: Params, x, w_router, bias, load, w1, w3, w2, y, logits, r: Routing, workspace, events,
+                   stream=None):
+    """moe_forward with six timing events (torch.cuda.Event, enable_timing) recorded before the route,
+    dispatch, gate-up GEMM, down GEMM and combine, and after the combine."""
+    for e in events:
+        if e is not None and not e.cuda_event:
+            e.record()  # torch creates the HIP event on its first record
+    ev = (ctypes.c_void_p * 6)(*[e.cuda_event if e is not None else None for e in events])
+    rc = lib().moe_forward_events(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(load),
+                                  _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y), _ptr(logits), ctypes.byref(r.c()),
+                                  _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _stream(stream), ev)
+    _check(rc, "moe_forward_events")
 
 
 def expert_ffn_fp8(p: Params, x_perm, offsets, q1, s1, q3, s3, q2, s2, h, y_perm, stream=None):
@@ -240,6 +261,7 @@ def forward_fp8(p: Params, x, w_router, bias, load, q1, s1, q3, s3, q2, s2, y, l
     _check(rc, "moe_forward_fp8")
 
 
-def alloc_workspace(p: Params, device="cuda", dispatch_only: bool = False) -> torch.Tensor:
-    n = dispatch_workspace_bytes(p) if dispatch_only else workspace_bytes(p)
+def alloc_workspace(p: Params, device="cuda", dispatch_only: bool = False, ffn_only: bool = False) -> torch.Tensor:
+    """Workspace of moe_forward, or of moe_dispatch / moe_expert_ffn alone."""
+    n = dispatch_workspace_bytes(p) if dispatch_only else ffn_workspace_bytes(p) if ffn_only else workspace_bytes(p)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)

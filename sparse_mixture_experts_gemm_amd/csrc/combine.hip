@@ -5,11 +5,16 @@
 // experts' results are put back in token order; "GPT-4稀疏激活真相" §4.3:
 // weighted fusion).  A token with no kept slot gets zeros.
 //
-// y_perm is fp32 (the down GEMM's accumulator precision), so the bf16 output
-// is rounded exactly once.  It may hold S partial products (slices of the
-// d_ff reduction, split_stride apart), which are added in slice order.
-// HBM-bound gather: 16-byte loads and stores, the k source rows read once
-// each.
+// Two sources:
+//   * y_perm [R][d] fp32 with the gates applied here (moe_combine, and the
+//     fp32 layer's forward pass);
+//   * gated rows: S fp16 slices [S][R][d] holding gate * (partial product of
+//     d_ff slice s), written by the down projection's epilogue in a bf16
+//     layer's forward pass.  The combine is then a plain sum of the k rows'
+//     slices (slot order, then slice order), read at half the bytes of fp32.
+// HBM-bound gather: 16-byte loads and stores, each source row read once.
+#include <algorithm>
+
 #include "device_common.h"
 #include "moe_internal.h"
 
@@ -18,9 +23,8 @@ namespace {
 
 constexpr int kThreads = 256;
 
-// Each thread produces 8 consecutive outputs: it reads two 16-byte fp32
-// chunks from each kept y_perm row and writes 8 bf16 (16 bytes) or 8 fp32
-// (32 bytes).
+// Each thread produces 8 consecutive outputs and writes 8 bf16 (16 bytes)
+// or 8 fp32 (32 bytes).
 template <typename TE>
 __device__ __forceinline__ void store8(TE *y, const float (&a)[8]);
 
@@ -36,15 +40,54 @@ __device__ __forceinline__ void store8<float>(float *y, const float (&a)[8]) {
     reinterpret_cast<float4 *>(y)[1] = make_float4(a[4], a[5], a[6], a[7]);
 }
 
-// Sum of gate * (slices of row) for 8 consecutive elements.  Generic path
-// (any k <= 8 and any slice count): the loads of one row's slices are
-// issued together, rows one after another.
-template <typename TE>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restrict__ y_perm,
-                                                           const int32_t *__restrict__ row,
-                                                           const float *__restrict__ gate, int T,
-                                                           int k, int d, int tpb, int splits,
-                                                           size_t split_stride,
+// 8 consecutive source elements of one row: fp32 (two 16-byte loads) or
+// fp16 (one).
+struct Src8f {
+    float4 u, v;
+};
+struct Src8h {
+    uint4 u;
+};
+
+__device__ __forceinline__ Src8f load8(const float *row, int c) {
+    const float4 *p = reinterpret_cast<const float4 *>(row) + 2 * c;
+    return Src8f{p[0], p[1]};
+}
+__device__ __forceinline__ Src8h load8(const uint16_t *row, int c) {
+    return Src8h{reinterpret_cast<const uint4 *>(row)[c]};
+}
+
+__device__ __forceinline__ void widen8(const Src8f &s, float (&o)[8]) {
+    o[0] = s.u.x; o[1] = s.u.y; o[2] = s.u.z; o[3] = s.u.w;
+    o[4] = s.v.x; o[5] = s.v.y; o[6] = s.v.z; o[7] = s.v.w;
+}
+__device__ __forceinline__ void widen8(const Src8h &s, float (&o)[8]) {
+    const uint32_t w[4] = {s.u.x, s.u.y, s.u.z, s.u.w};
+#pragma unroll
+    for (int i = 0; i < 4; i++) {
+        o[2 * i] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFF));
+        o[2 * i + 1] = (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16));
+    }
+}
+
+template <typename TY>
+struct SrcOf;
+template <>
+struct SrcOf<float> {
+    typedef Src8f type;
+};
+template <>
+struct SrcOf<uint16_t> {
+    typedef Src8h type;
+};
+
+// Generic path (any k <= 8, any slice count): one token row per group of
+// threads, the loads of one slot's slices issued together.  GATED: the
+// sources are gated fp16 slices and no gate is applied here.
+template <typename TE, typename TY, bool GATED>
+__global__ __launch_bounds__(kThreads) void combine_kernel(const TY *__restrict__ src, const int32_t *__restrict__ row,
+                                                           const float *__restrict__ gate, int T, int k, int d,
+                                                           int tpb, int splits, size_t stride,
                                                            TE *__restrict__ y) {
     const int per_tok = kThreads / tpb;  // threads per token
     if (threadIdx.x / per_tok >= tpb) return;
@@ -55,31 +98,23 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
     float gs[kMaxTopK];
     for (int r = 0; r < k; r++) {
         rws[r] = row[(size_t)t * k + r];
-        gs[r] = gate[(size_t)t * k + r];
+        gs[r] = GATED ? 1.0f : gate[(size_t)t * k + r];
     }
     const int groups = d / 8;
     for (int c = lt; c < groups; c += per_tok) {
         float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
         for (int r = 0; r < k; r++) {
             if (rws[r] < 0) continue;
-            const float4 *src = reinterpret_cast<const float4 *>(y_perm + (size_t)rws[r] * d) + 2 * c;
-            float4 u = src[0], v = src[1];
-            // the down projection's d_ff slices, added in slice order
+            float u[8];
+            widen8(load8(src + (size_t)rws[r] * d, c), u);
             for (int sl = 1; sl < splits; sl++) {
-                const float4 *ps = reinterpret_cast<const float4 *>(y_perm + sl * split_stride + (size_t)rws[r] * d) + 2 * c;
-                const float4 pu = ps[0], pv = ps[1];
-                u.x += pu.x; u.y += pu.y; u.z += pu.z; u.w += pu.w;
-                v.x += pv.x; v.y += pv.y; v.z += pv.z; v.w += pv.w;
+                float v[8];
+                widen8(load8(src + sl * stride + (size_t)rws[r] * d, c), v);
+#pragma unroll
+                for (int i = 0; i < 8; i++) u[i] += v[i];
             }
-            const float g = gs[r];
-            a[0] += g * u.x;
-            a[1] += g * u.y;
-            a[2] += g * u.z;
-            a[3] += g * u.w;
-            a[4] += g * v.x;
-            a[5] += g * v.y;
-            a[6] += g * v.z;
-            a[7] += g * v.w;
+#pragma unroll
+            for (int i = 0; i < 8; i++) a[i] += GATED ? u[i] : gs[r] * u[i];
         }
         store8<TE>(y + (size_t)t * d + 8 * c, a);
     }
@@ -87,15 +122,15 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const float *__restri
 
 // The common shapes (k and the slice count known at compile time): each
 // thread owns G groups of 8 outputs of one token and issues every load it
-// needs (K rows x S slices x G groups x 32 bytes) before the first add, so
-// a wave keeps a whole token row's worth of reads in flight.  A dropped
-// slot reads row 0 and is discarded by a select, so no branch splits the
-// batch and an uninitialised row can never leak a NaN into the sum.
-template <typename TE, int K, int S, int G>
-__global__ __launch_bounds__(kThreads) void combine_fixed(const float *__restrict__ y_perm,
-                                                          const int32_t *__restrict__ row,
-                                                          const float *__restrict__ gate, int T, int d,
-                                                          size_t split_stride, TE *__restrict__ y) {
+// needs (K rows x S slices x G groups) before the first add, so a wave keeps
+// a whole token row's worth of reads in flight.  A dropped slot reads row 0
+// and is discarded by a select, so no branch splits the batch and an
+// uninitialised row can never leak a NaN into the sum (R >= 1 here).
+template <typename TE, typename TY, bool GATED, int K, int S, int G>
+__global__ __launch_bounds__(kThreads) void combine_fixed(const TY *__restrict__ src, const int32_t *__restrict__ row,
+                                                          const float *__restrict__ gate, int T, int d, size_t stride,
+                                                          TE *__restrict__ y) {
+    typedef typename SrcOf<TY>::type Src;
     const int per_tok = d / (8 * G);  // threads per token (divides kThreads)
     const int t = blockIdx.x * (kThreads / per_tok) + threadIdx.x / per_tok;
     const int lt = threadIdx.x % per_tok;
@@ -105,50 +140,47 @@ __global__ __launch_bounds__(kThreads) void combine_fixed(const float *__restric
 #pragma unroll
     for (int r = 0; r < K; r++) {
         rws[r] = row[(size_t)t * K + r];
-        gs[r] = gate[(size_t)t * K + r];
+        gs[r] = GATED ? 1.0f : gate[(size_t)t * K + r];
     }
-    float4 u[G][K][S][2];
+    Src u[G][K][S];
 #pragma unroll
     for (int gi = 0; gi < G; gi++)
 #pragma unroll
         for (int r = 0; r < K; r++)
 #pragma unroll
-            for (int sl = 0; sl < S; sl++) {
-                const float4 *src = reinterpret_cast<const float4 *>(
-                                        y_perm + sl * split_stride + (size_t)max(rws[r], 0) * d) +
-                                    2 * (lt + gi * per_tok);
-                u[gi][r][sl][0] = src[0];
-                u[gi][r][sl][1] = src[1];
-            }
+            for (int sl = 0; sl < S; sl++)
+                u[gi][r][sl] = load8(src + sl * stride + (size_t)max(rws[r], 0) * d, lt + gi * per_tok);
 #pragma unroll
     for (int gi = 0; gi < G; gi++) {
         float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int r = 0; r < K; r++) {
-            float4 p = u[gi][r][0][0], q = u[gi][r][0][1];
+            float p[8];
+            widen8(u[gi][r][0], p);
 #pragma unroll
             for (int sl = 1; sl < S; sl++) {
-                p.x += u[gi][r][sl][0].x; p.y += u[gi][r][sl][0].y; p.z += u[gi][r][sl][0].z; p.w += u[gi][r][sl][0].w;
-                q.x += u[gi][r][sl][1].x; q.y += u[gi][r][sl][1].y; q.z += u[gi][r][sl][1].z; q.w += u[gi][r][sl][1].w;
+                float q[8];
+                widen8(u[gi][r][sl], q);
+#pragma unroll
+                for (int i = 0; i < 8; i++) p[i] += q[i];
             }
             const bool kept = rws[r] >= 0;
-            const float g = gs[r];
-            a[0] += kept ? g * p.x : 0.0f;
-            a[1] += kept ? g * p.y : 0.0f;
-            a[2] += kept ? g * p.z : 0.0f;
-            a[3] += kept ? g * p.w : 0.0f;
-            a[4] += kept ? g * q.x : 0.0f;
-            a[5] += kept ? g * q.y : 0.0f;
-            a[6] += kept ? g * q.z : 0.0f;
-            a[7] += kept ? g * q.w : 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i++) a[i] += kept ? (GATED ? p[i] : gs[r] * p[i]) : 0.0f;
         }
         store8<TE>(y + (size_t)t * d + 8 * (lt + gi * per_tok), a);
     }
 }
 
-template <typename TE, int K, int S>
-bool launch_fixed(const moe_params &p, size_t split_stride, const void *y_perm, const int32_t *row,
-                  const float *gate, void *y, hipStream_t st) {
+// Every output element zero (no permuted rows at all: nothing to read).
+__global__ __launch_bounds__(kThreads) void zero_fill(uint4 *__restrict__ y, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x; i < n16; i += (size_t)gridDim.x * kThreads)
+        y[i] = make_uint4(0, 0, 0, 0);
+}
+
+template <typename TE, typename TY, bool GATED, int K, int S>
+bool launch_fixed(const moe_params &p, size_t stride, const TY *src, const int32_t *row, const float *gate, void *y,
+                  hipStream_t st) {
     // G = 2 groups per thread when a token row has at least 512 groups
     const int groups = p.d / 8;
     const int G = groups >= 2 * kThreads ? 2 : 1;
@@ -157,34 +189,22 @@ bool launch_fixed(const moe_params &p, size_t split_stride, const void *y_perm, 
     const int tpb = kThreads / per_tok;
     const int grid = (int)ceil_div(p.T, tpb);
     if (G == 2)
-        hipLaunchKernelGGL((combine_fixed<TE, K, S, 2>), dim3(grid), dim3(kThreads), 0, st,
-                           static_cast<const float *>(y_perm), row, gate, p.T, p.d, split_stride,
-                           static_cast<TE *>(y));
+        hipLaunchKernelGGL((combine_fixed<TE, TY, GATED, K, S, 2>), dim3(grid), dim3(kThreads), 0, st, src, row, gate,
+                           p.T, p.d, stride, static_cast<TE *>(y));
     else
-        hipLaunchKernelGGL((combine_fixed<TE, K, S, 1>), dim3(grid), dim3(kThreads), 0, st,
-                           static_cast<const float *>(y_perm), row, gate, p.T, p.d, split_stride,
-                           static_cast<TE *>(y));
+        hipLaunchKernelGGL((combine_fixed<TE, TY, GATED, K, S, 1>), dim3(grid), dim3(kThreads), 0, st, src, row, gate,
+                           p.T, p.d, stride, static_cast<TE *>(y));
     return true;
 }
 
-template <typename TE>
-bool launch_fixed_any(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
-                      const int32_t *row, const float *gate, void *y, hipStream_t st) {
-    if (p.k == 2 && splits == 1) return launch_fixed<TE, 2, 1>(p, split_stride, y_perm, row, gate, y, st);
-    if (p.k == 2 && splits == 2) return launch_fixed<TE, 2, 2>(p, split_stride, y_perm, row, gate, y, st);
-    if (p.k == 2 && splits == 4) return launch_fixed<TE, 2, 4>(p, split_stride, y_perm, row, gate, y, st);
-    if (p.k == 1 && splits == 1) return launch_fixed<TE, 1, 1>(p, split_stride, y_perm, row, gate, y, st);
-    return false;
-}
-
-}  // namespace
-
-hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
-                          const int32_t *row, const float *gate, void *y, hipStream_t st) {
-    if (p.T == 0) return hipSuccess;
-    const bool fixed = p.dtype == MOE_BF16
-                           ? launch_fixed_any<uint16_t>(p, splits, split_stride, y_perm, row, gate, y, st)
-                           : launch_fixed_any<float>(p, splits, split_stride, y_perm, row, gate, y, st);
+template <typename TE, typename TY, bool GATED>
+hipError_t launch_any(const moe_params &p, int splits, size_t stride, const TY *src, const int32_t *row,
+                      const float *gate, void *y, hipStream_t st) {
+    bool fixed = false;
+    if (p.k == 2 && splits == 1) fixed = launch_fixed<TE, TY, GATED, 2, 1>(p, stride, src, row, gate, y, st);
+    else if (p.k == 2 && splits == 2) fixed = launch_fixed<TE, TY, GATED, 2, 2>(p, stride, src, row, gate, y, st);
+    else if (p.k == 2 && splits == 4) fixed = launch_fixed<TE, TY, GATED, 2, 4>(p, stride, src, row, gate, y, st);
+    else if (p.k == 1 && splits == 1) fixed = launch_fixed<TE, TY, GATED, 1, 1>(p, stride, src, row, gate, y, st);
     if (fixed) return hipGetLastError();
     const int groups = p.d / 8;
     // tokens per block: enough threads per token to cover its row in one pass
@@ -192,15 +212,34 @@ hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, 
     int tpb = kThreads / per_tok;
     if (tpb < 1) tpb = 1;
     const int grid = (int)ceil_div(p.T, tpb);
-    if (p.dtype == MOE_BF16)
-        hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, st,
-                           static_cast<const float *>(y_perm), row, gate, p.T, p.k, p.d, tpb,
-                           splits, split_stride, static_cast<uint16_t *>(y));
-    else
-        hipLaunchKernelGGL(combine_kernel<float>, dim3(grid), dim3(kThreads), 0, st,
-                           static_cast<const float *>(y_perm), row, gate, p.T, p.k, p.d, tpb,
-                           splits, split_stride, static_cast<float *>(y));
+    hipLaunchKernelGGL((combine_kernel<TE, TY, GATED>), dim3(grid), dim3(kThreads), 0, st, src, row, gate, p.T, p.k,
+                       p.d, tpb, splits, stride, static_cast<TE *>(y));
     return hipGetLastError();
+}
+
+hipError_t launch_zero(const moe_params &p, void *y, hipStream_t st) {
+    const size_t n16 = (size_t)p.T * p.d * (p.dtype == MOE_BF16 ? 2 : 4) / 16;
+    const int grid = (int)std::min<size_t>((n16 + kThreads - 1) / kThreads, 4096);
+    hipLaunchKernelGGL(zero_fill, dim3(grid), dim3(kThreads), 0, st, static_cast<uint4 *>(y), n16);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_params &p, int64_t max_rows, const float *y_perm, const int32_t *row,
+                          const float *gate, void *y, hipStream_t st) {
+    if (p.T == 0) return hipSuccess;
+    if (max_rows <= 0) return launch_zero(p, y, st);
+    if (p.dtype == MOE_BF16) return launch_any<uint16_t, float, false>(p, 1, 0, y_perm, row, gate, y, st);
+    return launch_any<float, float, false>(p, 1, 0, y_perm, row, gate, y, st);
+}
+
+hipError_t launch_combine_gated(const moe_params &p, int64_t max_rows, int splits, const uint16_t *yg,
+                                const int32_t *row, void *y, hipStream_t st) {
+    if (p.T == 0) return hipSuccess;
+    if (max_rows <= 0) return launch_zero(p, y, st);
+    const size_t stride = (size_t)max_rows * p.d;
+    return launch_any<uint16_t, uint16_t, true>(p, splits, stride, yg, row, nullptr, y, st);
 }
 
 }  // namespace moe

@@ -221,7 +221,7 @@ __device__ __forceinline__ void finalize_body(
     int32_t *__restrict__ eid, int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
     int32_t *__restrict__ row, float *__restrict__ gate, int32_t *__restrict__ offsets,
     int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand, int32_t *__restrict__ kept,
-    int32_t *__restrict__ totals, float *__restrict__ aux_loss, FinalizeLds &sm) {
+    int32_t *__restrict__ totals, float *__restrict__ aux_loss, float *__restrict__ gate_of_row, FinalizeLds &sm) {
     auto &fbase = sm.fbase;
     auto &kcnt = sm.kcnt;
     auto &offs = sm.offs;
@@ -299,9 +299,11 @@ __device__ __forceinline__ void finalize_body(
                 gate[j] = 0.0f;
             } else {
                 const int rw = offs[e_s[r]] + p_s[r];
+                const float gv = expf((sc[r] - m) / tau) / z;
                 row[j] = rw;
                 token_of_row[rw] = t;
-                gate[j] = expf((sc[r] - m) / tau) / z;
+                gate[j] = gv;
+                if (gate_of_row) gate_of_row[rw] = gv;  // the row's combine weight, for the down epilogue
             }
         }
     }
@@ -343,10 +345,11 @@ __global__ __launch_bounds__(kThreads) void dispatch_finalize(
     int32_t *__restrict__ eid, int32_t *__restrict__ pos, uint8_t *__restrict__ flag,
     int32_t *__restrict__ row, float *__restrict__ gate, int32_t *__restrict__ offsets,
     int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand, int32_t *__restrict__ kept,
-    int32_t *__restrict__ totals, float *__restrict__ aux_loss) {
+    int32_t *__restrict__ totals, float *__restrict__ aux_loss, float *__restrict__ gate_of_row) {
     __shared__ FinalizeLds sm;
     finalize_body(blockIdx.x, cand, cand_score, T, E, k, C, nb, use_fallback, aux_coef, tau, cap_rows, hist, fill_prim,
-                  fb_hist, eid, pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm);
+                  fb_hist, eid, pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss,
+                  gate_of_row, sm);
 }
 
 // T <= kThreads: one block runs the three phases back to back, saving two
@@ -360,7 +363,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_single(
     uint8_t *__restrict__ flag, int32_t *__restrict__ row, float *__restrict__ gate,
     int32_t *__restrict__ offsets, int32_t *__restrict__ token_of_row, int32_t *__restrict__ demand,
     int32_t *__restrict__ kept, int32_t *__restrict__ totals, float *__restrict__ aux_loss,
-    int32_t *__restrict__ claim) {
+    float *__restrict__ gate_of_row, int32_t *__restrict__ claim) {
     __shared__ union {
         int wcnt[kWaves][kMaxExperts];
         PrimaryLds p;
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(kThreads) void dispatch_single(
     __threadfence_block();
     __syncthreads();
     finalize_body(0, cand, cand_score, T, E, k, C, 1, use_fallback, aux_coef, tau, cap_rows, hist_l, fill_l, fb_l, eid,
-                  pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, sm.f);
+                  pos, flag, row, gate, offsets, token_of_row, demand, kept, totals, aux_loss, gate_of_row, sm.f);
 }
 
 // x_perm[row[t][j]] = x[t] for every kept slot: the token row is read once.
@@ -411,7 +414,7 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
         hipLaunchKernelGGL(dispatch_single, dim3(1), dim3(kThreads), 0, st, r.cand, r.cand_score, T, E, k,
                            (int)C, use_fb, p.aux_coef, tau, (int)cap_rows, ws.hist, ws.fill_prim, ws.fb_hist, r.eid,
                            r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row, r.demand, r.kept, r.totals,
-                           r.aux_loss, ws.claim);
+                           r.aux_loss, ws.gate_of_row, ws.claim);
     } else {
         hipLaunchKernelGGL(dispatch_hist, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, ws.hist, ws.claim);
         hipLaunchKernelGGL(dispatch_primary, dim3(nb), dim3(kThreads), 0, st, r.cand, T, E, k, (int)C,
@@ -419,7 +422,7 @@ hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const 
         hipLaunchKernelGGL(dispatch_finalize, dim3(nb), dim3(kThreads), 0, st, r.cand, r.cand_score, T,
                            E, k, (int)C, nb, use_fb, p.aux_coef, tau, (int)cap_rows, ws.hist, ws.fill_prim,
                            ws.fb_hist, r.eid, r.pos, r.flag, r.row, r.gate, r.offsets, r.token_of_row,
-                           r.demand, r.kept, r.totals, r.aux_loss);
+                           r.demand, r.kept, r.totals, r.aux_loss, ws.gate_of_row);
     }
     if (T > 0 && x_perm) {
         const int esz = p.dtype == MOE_BF16 ? 2 : 4;

@@ -60,6 +60,11 @@ struct TileInfo {
     int e, m0, mend, nt, split;
 };
 
+template <typename T>
+__device__ __forceinline__ T *slice_ptr(const GemmOut &o, int split) {
+    return split == 0 ? static_cast<T *>(o.y0) : static_cast<T *>(o.y_rest) + (size_t)(split - 1) * o.stride;
+}
+
 // Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).
 // The grid is sized by a bound on the work count; the real count comes from
 // the device-side offsets.  Each XCD is given an equal, contiguous range of
@@ -491,11 +496,10 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *a0, char *a
 // Down: fp32 partial products, 32 lanes store one 128-byte row segment.
 template <int MODE, int NACT>
 __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, int wm, int wn, int lane,
-                                           size_t split_stride, const f32x16_t (&acc)[4][4], void *out_v,
-                                           char *w) {
+                                           const GemmOut &out, const f32x16_t (&acc)[4][4], char *w) {
     const int l5 = lane & 31, hi = lane >> 5;
     if (MODE == kGateUp) {
-        uint16_t *out_h = static_cast<uint16_t *>(out_v);
+        uint16_t *out_h = static_cast<uint16_t *>(out.y0);
 #pragma unroll
         for (int i = 0; i < NACT; i++)
 #pragma unroll
@@ -524,9 +528,18 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
         // one 32 x 128 fp32 block per pass through the wave's 16 KiB of LDS
         // (512-byte rows; the 16-byte chunks of rows 4..7 mod 8 XOR-swizzled by
         // 8 so the two half-waves, four rows apart, write disjoint banks), then
-        // 16-byte stores: 32 lanes per 512-byte row segment
-        float *out_y = static_cast<float *>(out_v) + ti.split * split_stride;  // this split's partial
+        // 32 lanes per 512-byte row segment: 16-byte stores of fp32, or, with
+        // row gates, 8-byte stores of the fp16 gated values
         const int cb = n0 + wn * 128;  // first column of this wave's block (N is a multiple of 64)
+        const bool gated = out.row_gate != nullptr;
+        // gates of the wave's 128 rows: row l of the wave in g_lo of lane l,
+        // row 64 + l in g_hi (rows past the expert's end read its last row)
+        float g_lo = 0.0f, g_hi = 0.0f;
+        if (gated) {
+            const int r0 = ti.m0 + wm * 128;
+            g_lo = out.row_gate[min(r0 + lane, ti.mend - 1)];
+            g_hi = out.row_gate[min(r0 + 64 + lane, ti.mend - 1)];
+        }
 #pragma unroll
         for (int i = 0; i < NACT; i++) {
 #pragma unroll
@@ -544,7 +557,19 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
                 const uint4 v = lds_read16(w + row * 512 + pc * 16);
                 const int m = ti.m0 + wm * 128 + i * 32 + row;
                 const int col = cb + ((pc ^ (((row >> 2) & 1) << 3)) << 2);
-                if (m < ti.mend && col < N) *reinterpret_cast<uint4 *>(out_y + (size_t)m * N + col) = v;
+                if (gated) {
+                    // row i * 32 + row of the wave: lane (i & 1) * 32 + row of g_lo (i < 2) or g_hi
+                    const float g = __shfl(i < 2 ? g_lo : g_hi, (i & 1) * 32 + row, 64);
+                    const uint32_t lo = (uint32_t)f32_to_f16_sat(g * __uint_as_float(v.x)) |
+                                        ((uint32_t)f32_to_f16_sat(g * __uint_as_float(v.y)) << 16);
+                    const uint32_t hi2 = (uint32_t)f32_to_f16_sat(g * __uint_as_float(v.z)) |
+                                         ((uint32_t)f32_to_f16_sat(g * __uint_as_float(v.w)) << 16);
+                    if (m < ti.mend && col < N)
+                        *reinterpret_cast<uint2 *>(slice_ptr<uint16_t>(out, ti.split) + (size_t)m * N + col) =
+                            make_uint2(lo, hi2);
+                } else if (m < ti.mend && col < N) {
+                    *reinterpret_cast<uint4 *>(slice_ptr<float>(out, ti.split) + (size_t)m * N + col) = v;
+                }
             }
         }
     }
@@ -555,7 +580,7 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
 template <int MODE, int NACT, bool ODD>
 __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti, char *a0, char *a1, char *b0,
                                          char *b1, char *b2, int nk, int n0, int N, int wm, int wn, int lane,
-                                         size_t split_stride, void *out_v) {
+                                         const GemmOut &out) {
     f32x16_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -568,7 +593,7 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
     // wave before the epilogue reuses the A buffers (16 KiB per wave)
     WAIT_VM_LGKM0();
     block_sync();
-    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, split_stride, acc, out_v,
+    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, out, acc,
                            (g.wave < 2 ? a0 : a1) + (g.wave & 1) * (kTileBytes / 2));
 }
 
@@ -577,11 +602,13 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
 //               is x row a_rows[m] (the dispatch gather folded into the A
 //               loads; x must then span less than 2 GiB).
 // MODE kDown:   A = h (fp16), B = W2 (bf16, widened to fp16 after the LDS
-//               read), writes y_perm (fp32).  The d_ff reduction is split
-//               into `splits` slices (work items of their own, for enough
-//               work to fill the chip); slice s writes its partial product to
-//               y_perm + s * split_stride and the combine adds the slices in
-//               order, so the result is deterministic.
+//               read), writes the down projection (see GemmOut: fp32, or
+//               fp16 with the row's combine weight folded in).  The d_ff
+//               reduction is split into `splits` slices (work items of their
+//               own, for enough work to fill the chip); each slice stores
+//               its partial product and a later pass (the fix-up or the
+//               combine) adds the slices in order, so the result is
+//               deterministic.
 //
 // LDS: two A buffers and three (gate-up) or two (down) B buffers of 256 rows
 // x 64 K (32 KiB each), the eight 16-byte chunks of each row XOR-swizzled by
@@ -595,7 +622,7 @@ template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
-    int splits, size_t split_stride, uint32_t a_bytes, int32_t *claim, void *__restrict__ out_v) {
+    int splits, uint32_t a_bytes, int32_t *claim, GemmOut out) {
     __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
@@ -658,10 +685,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     do {                                                                                                         \
         if (b_buffers<MODE>() == 2 && (nk & 1))                                                                  \
             run_tile<MODE, n, b_buffers<MODE>() == 2>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N,  \
-                                                      wm, wn, lane, split_stride, out_v);                        \
+                                                      wm, wn, lane, out);                                        \
         else                                                                                                     \
             run_tile<MODE, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane,     \
-                                     split_stride, out_v);                                                       \
+                                     out);                                                                       \
     } while (0)
     switch (nact) {
         case 4: MOE_TILE(4); break;
@@ -806,7 +833,7 @@ template <int MODE>
 __global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
-    int splits, size_t split_stride, void *__restrict__ out_v) {
+    int splits, GemmOut out) {
     __shared__ __attribute__((aligned(1024))) char sb0[kSkStage];
     __shared__ __attribute__((aligned(1024))) char sb1[kSkStage];
     __shared__ __attribute__((aligned(1024))) char sb2[kSkStage];
@@ -864,13 +891,20 @@ __global__ __launch_bounds__(kSkThreads) void grouped_gemm_skinny(
             if (MODE == kGateUp) {
                 const int col = n0 + wave * 16 + (lane & 15);
                 if (col < N)
-                    static_cast<uint16_t *>(out_v)[(size_t)m * N + col] =
+                    static_cast<uint16_t *>(out.y0)[(size_t)m * N + col] =
                         f32_to_f16_sat(silu_mul(acc[ib][0][q], acc[ib][1][q]));
+            } else if (out.row_gate) {
+                const float gt = out.row_gate[m];
+#pragma unroll
+                for (int jb = 0; jb < 2; jb++) {
+                    const int col = n0 + wave * 32 + jb * 16 + (lane & 15);
+                    if (col < N) slice_ptr<uint16_t>(out, ti.split)[(size_t)m * N + col] = f32_to_f16_sat(gt * acc[ib][jb][q]);
+                }
             } else {
 #pragma unroll
                 for (int jb = 0; jb < 2; jb++) {
                     const int col = n0 + wave * 32 + jb * 16 + (lane & 15);
-                    if (col < N) (static_cast<float *>(out_v) + ti.split * split_stride)[(size_t)m * N + col] = acc[ib][jb][q];
+                    if (col < N) slice_ptr<float>(out, ti.split)[(size_t)m * N + col] = acc[ib][jb][q];
                 }
             }
         }
@@ -1018,7 +1052,7 @@ template <int MODE>
 __global__ __launch_bounds__(kSkThreads, 2) void grouped_gemm_skinny_fp8(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ B0,
     const uint8_t *__restrict__ B1, const float *__restrict__ S0, const float *__restrict__ S1,
-    const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n, void *__restrict__ out_v) {
+    const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n, GemmOut out) {
     __shared__ __attribute__((aligned(1024))) char sb0[kSk8Stage];
     __shared__ __attribute__((aligned(1024))) char sb1[kSk8Stage];
     __shared__ __attribute__((aligned(1024))) char sb2[kSk8Stage];
@@ -1082,13 +1116,21 @@ __global__ __launch_bounds__(kSkThreads, 2) void grouped_gemm_skinny_fp8(
             if (MODE == kGateUp) {
                 const int col = n0 + wave * 16 + (lane & 15);
                 if (col < N)
-                    static_cast<uint16_t *>(out_v)[(size_t)m * N + col] =
+                    static_cast<uint16_t *>(out.y0)[(size_t)m * N + col] =
                         f32_to_f16_sat(silu_mul(acc[ib][0][q] * sc[0], acc[ib][1][q] * sc[1]));
+            } else if (out.row_gate) {
+                const float gt = out.row_gate[m];
+#pragma unroll
+                for (int jb = 0; jb < 2; jb++) {
+                    const int col = n0 + wave * 32 + jb * 16 + (lane & 15);
+                    if (col < N)
+                        static_cast<uint16_t *>(out.y0)[(size_t)m * N + col] = f32_to_f16_sat(gt * (acc[ib][jb][q] * sc[jb]));
+                }
             } else {
 #pragma unroll
                 for (int jb = 0; jb < 2; jb++) {
                     const int col = n0 + wave * 32 + jb * 16 + (lane & 15);
-                    if (col < N) static_cast<float *>(out_v)[(size_t)m * N + col] = acc[ib][jb][q] * sc[jb];
+                    if (col < N) static_cast<float *>(out.y0)[(size_t)m * N + col] = acc[ib][jb][q] * sc[jb];
                 }
             }
         }
@@ -1181,10 +1223,34 @@ bool fp8_ffn_supported(const moe_params &p) {
     return p.dtype == MOE_BF16 && capacity_rows(p) <= kSkBM && p.d % kSk8K == 0 && p.d_ff % kSk8K == 0;
 }
 
+namespace {
+
+// y[r] += rest[0][r] + rest[1][r] + ... (slice order) for the rows below
+// offsets[E]: the split down projection's partial products reduced into
+// slice 0, deterministically.
+__global__ __launch_bounds__(256) void ffn_fixup(float *__restrict__ y, const float *__restrict__ rest, int nrest,
+                                                 size_t stride, const int32_t *__restrict__ offsets, int E, int d) {
+    const size_t n = (size_t)offsets[E] * (d / 4);
+    float4 *y4 = reinterpret_cast<float4 *>(y);
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) {
+        float4 a = y4[i];
+        for (int sl = 0; sl < nrest; sl++) {
+            const float4 b = reinterpret_cast<const float4 *>(rest + (size_t)sl * stride)[i];
+            a.x += b.x;
+            a.y += b.y;
+            a.z += b.z;
+            a.w += b.w;
+        }
+        y4[i] = a;
+    }
+}
+
+}  // namespace
+
 hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                                  const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
                                  const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
-                                 void *y_perm, hipStream_t st) {
+                                 const GemmOut &down, hipEvent_t mid, hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
     const int E = p.E, d = p.d, dff = p.d_ff;
     if (p.dtype != MOE_BF16 || cap > kSkBM || d % kSk8K != 0 || dff % kSk8K != 0) return hipErrorInvalidValue;
@@ -1192,33 +1258,36 @@ hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t 
     const int nt_up = (int)ceil_div(dff, kSkBN);
     const int nt_dn = (int)ceil_div(d, kSkBNd);
     hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
-                       static_cast<const uint16_t *>(x_perm), a_rows, w1, w3, s1, s3, offsets, E, dff, d, nt_up, h);
+                       static_cast<const uint16_t *>(x_perm), a_rows, w1, w3, s1, s3, offsets, E, dff, d, nt_up,
+                       GemmOut{h, nullptr, 0, nullptr});
+    if (mid) hipEventRecord(mid, st);
     hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(kSkThreads), 0, st,
                        static_cast<const uint16_t *>(h), (const int32_t *)nullptr, w2, w2, s2, s2, offsets, E, d,
-                       dff, nt_dn, y_perm);
+                       dff, nt_dn, down);
     return hipGetLastError();
 }
 
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
-                             const void *w3, const void *w2, void *h, void *y_perm, int32_t *claim,
-                             hipStream_t st) {
+                             const void *w3, const void *w2, void *h, const GemmOut &down, int32_t *claim,
+                             hipEvent_t mid, hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
     const int E = p.E, d = p.d, dff = p.d_ff;
+    const GemmOut up{h, nullptr, 0, nullptr};
     if (p.dtype == MOE_BF16 && cap <= kSkBM) {
         // every expert holds at most 32 rows: the weight-streaming kernel
         const int64_t mt = mtile_bound(max_rows, cap, E, kSkBM);
         const int nt_up = (int)ceil_div(dff, kSkBN);
         const int nt_dn = (int)ceil_div(d, kSkBNd);
         const int S = ffn_splits(p, max_rows);
-        const size_t split_stride = (size_t)max_rows * d;
         hipLaunchKernelGGL(grouped_gemm_skinny<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
                            static_cast<const uint16_t *>(x_perm), a_rows, static_cast<const uint16_t *>(w1),
-                           static_cast<const uint16_t *>(w3), offsets, E, dff, d, nt_up, 1, (size_t)0, h);
+                           static_cast<const uint16_t *>(w3), offsets, E, dff, d, nt_up, 1, up);
+        if (mid) hipEventRecord(mid, st);
         hipLaunchKernelGGL(grouped_gemm_skinny<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kSkThreads), 0, st,
                            static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2), offsets, E, d,
-                           dff, nt_dn, S, split_stride, y_perm);
+                           dff, nt_dn, S, down);
         return hipGetLastError();
     }
     if (p.dtype == MOE_BF16) {
@@ -1229,16 +1298,16 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         const int nt_up = (int)ceil_div(dff, kBN / 2);
         const int nt_dn = (int)ceil_div(d, kBN);
         const int S = ffn_splits(p, max_rows);
-        const size_t split_stride = (size_t)max_rows * d;
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(x_perm), a_rows,
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
-                           offsets, E, dff, d, nt_up, 1, (size_t)0, (uint32_t)a_bytes, claim, h);
+                           offsets, E, dff, d, nt_up, 1, (uint32_t)a_bytes, claim, up);
+        if (mid) hipEventRecord(mid, st);
         hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
-                           offsets, E, d, dff, nt_dn, S, split_stride, (uint32_t)0,
-                           claim ? claim + 8 : nullptr, y_perm);
+                           offsets, E, d, dff, nt_dn, S, (uint32_t)0,
+                           claim ? claim + 8 : nullptr, down);
     } else {
         const int64_t mt = max_rows / kF32BM + E;
         const int nt_up = (int)ceil_div(dff, kF32BN);
@@ -1247,11 +1316,22 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
                            static_cast<const float *>(x_perm), a_rows, static_cast<const float *>(w1),
                            static_cast<const float *>(w3), offsets, E, dff, d, nt_up,
                            static_cast<float *>(h));
+        if (mid) hipEventRecord(mid, st);
         hipLaunchKernelGGL(grouped_gemm_f32<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(256), 0, st,
                            static_cast<const float *>(h), (const int32_t *)nullptr, static_cast<const float *>(w2),
                            static_cast<const float *>(w2), offsets, E, d, dff, nt_dn,
-                           static_cast<float *>(y_perm));
+                           static_cast<float *>(down.y0));
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_ffn_fixup(const moe_params &p, int64_t max_rows, const int32_t *offsets, float *y_perm,
+                            const float *rest, int nrest, hipStream_t st) {
+    if (max_rows <= 0 || nrest <= 0) return hipSuccess;
+    const int64_t n4 = max_rows * (p.d / 4);
+    const int grid = (int)std::min<int64_t>(ceil_div(n4, 256), 4096);
+    hipLaunchKernelGGL(ffn_fixup, dim3(grid), dim3(256), 0, st, y_perm, rest, nrest, (size_t)max_rows * p.d,
+                       offsets, p.E, p.d);
     return hipGetLastError();
 }
 

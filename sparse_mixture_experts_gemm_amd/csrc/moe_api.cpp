@@ -23,6 +23,9 @@ int check_params(const moe_params *p) {
     if (p->d > (p->dtype == MOE_BF16 ? 16384 : 8192)) return MOE_ERR_UNSUPPORTED;
     // one expert's weight matrix is addressed with 32-bit byte offsets
     if ((int64_t)p->d * p->d_ff * (p->dtype == MOE_BF16 ? 2 : 4) >= ((int64_t)1 << 32)) return MOE_ERR_UNSUPPORTED;
+    // a 256-row tile of h (the down projection's A operand) is addressed with
+    // byte offsets below 2 GiB (an offset of 2 GiB marks a load past the end)
+    if ((int64_t)256 * p->d_ff * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (!(p->lambda == p->lambda) || !(p->capacity_factor == p->capacity_factor)) return MOE_ERR_INVALID_ARG;
     if (!(p->gate_temperature >= 0.0f) || isinf(p->gate_temperature)) return MOE_ERR_INVALID_ARG;
     if (!(p->top2_gap >= 0.0f) || isinf(p->top2_gap)) return MOE_ERR_INVALID_ARG;
@@ -74,13 +77,13 @@ int fp8_weights_ok(const moe_params &p, const FfnWeights &w) {
 }
 
 hipError_t launch_ffn(const moe_params &p, int64_t R, int64_t C, const void *a, const int32_t *a_rows,
-                      const int32_t *offsets, const FfnWeights &w, void *h, void *y_perm, int32_t *claim,
-                      hipStream_t st) {
+                      const int32_t *offsets, const FfnWeights &w, void *h, const GemmOut &down, int32_t *claim,
+                      hipEvent_t mid, hipStream_t st) {
     if (w.s1)
         return launch_expert_ffn_fp8(p, R, C, a, a_rows, offsets, static_cast<const uint8_t *>(w.w1), w.s1,
                                      static_cast<const uint8_t *>(w.w3), w.s3,
-                                     static_cast<const uint8_t *>(w.w2), w.s2, h, y_perm, st);
-    return launch_expert_ffn(p, R, C, a, a_rows, offsets, w.w1, w.w3, w.w2, h, y_perm, claim, st);
+                                     static_cast<const uint8_t *>(w.w2), w.s2, h, down, mid, st);
+    return launch_expert_ffn(p, R, C, a, a_rows, offsets, w.w1, w.w3, w.w2, h, down, claim, mid, st);
 }
 
 // moe_forward folds the dispatch gather into the gate-up GEMM (A rows read
@@ -89,22 +92,35 @@ hipError_t launch_ffn(const moe_params &p, int64_t R, int64_t C, const void *a, 
 // 2 GiB marks a load that fetches nothing); x_perm is then never materialised.
 bool gather_in_gemm(const moe_params &p) { return (int64_t)p.T * p.d * (int64_t)esize(p) < ((int64_t)1 << 31); }
 
+int splits_of(const moe_params &p) { return ffn_splits(p, max_rows_of(p)); }
+
+// moe_expert_ffn's scratch: the partial products of d_ff slices 1..S-1
+// (slice 0 goes straight to y_perm; the fix-up adds the others).
+size_t ffn_ws_bytes(const moe_params &p) {
+    const size_t R = (size_t)max_rows_of(p);
+    const int S = splits_of(p);
+    return S > 1 ? align256((size_t)(S - 1) * R * p.d * sizeof(float)) : 0;
+}
+
 // Workspace layout of moe_forward.
 struct ForwardWs {
-    void *dispatch, *x_perm, *h, *y_perm;  // x_perm null when the GEMM gathers
-    int32_t *claim;                        // the expert GEMM's work-claim counters
+    void *dispatch, *x_perm, *h;  // x_perm null when the GEMM gathers
+    void *y;                      // bf16: gated fp16 slices [S][R][d]; fp32: y_perm [R][d]
+    float *gate_of_row;           // bf16: [R] each row's gate, for the down epilogue; fp32: null
+    int32_t *claim;               // the expert GEMM's work-claim counters
 };
 
-size_t y_perm_bytes(const moe_params &p) {
+size_t forward_y_bytes(const moe_params &p) {
     const size_t R = (size_t)max_rows_of(p);
-    return (size_t)ffn_splits(p, (int64_t)R) * R * p.d * sizeof(float);
+    return p.dtype == MOE_BF16 ? (size_t)splits_of(p) * R * p.d * 2 : R * p.d * sizeof(float);
 }
 
 size_t forward_ws_bytes(const moe_params &p) {
     const size_t R = (size_t)max_rows_of(p);
     const size_t xp = gather_in_gemm(p) ? 0 : align256(R * p.d * esize(p));
+    const size_t gr = p.dtype == MOE_BF16 ? align256(R * sizeof(float)) : 0;
     return align256(dispatch_scratch_bytes(p.T, p.E, p.k)) + xp + align256(R * p.d_ff * esize(p)) +
-           align256(y_perm_bytes(p)) + align256(sizeof(int32_t) * kClaimCounters);
+           align256(forward_y_bytes(p)) + gr + align256(sizeof(int32_t) * kClaimCounters);
 }
 
 ForwardWs carve_forward(void *ws, const moe_params &p) {
@@ -120,8 +136,13 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
     }
     f.h = c;
     c += align256(R * p.d_ff * esize(p));
-    f.y_perm = c;
-    c += align256(y_perm_bytes(p));
+    f.y = c;
+    c += align256(forward_y_bytes(p));
+    f.gate_of_row = nullptr;
+    if (p.dtype == MOE_BF16) {
+        f.gate_of_row = reinterpret_cast<float *>(c);
+        c += align256(R * sizeof(float));
+    }
     f.claim = reinterpret_cast<int32_t *>(c);
     return f;
 }
@@ -145,9 +166,9 @@ size_t moe_dispatch_workspace_bytes(const moe_params *p) {
     return dispatch_scratch_bytes(p->T, p->E, p->k);
 }
 
-int moe_ffn_splits(const moe_params *p) {
-    if (check_params(p) != MOE_OK) return -1;
-    return ffn_splits(*p, max_rows_of(*p));
+size_t moe_ffn_workspace_bytes(const moe_params *p) {
+    if (check_params(p) != MOE_OK) return 0;
+    return ffn_ws_bytes(*p);
 }
 
 size_t moe_workspace_bytes(const moe_params *p) {
@@ -179,17 +200,25 @@ int moe_dispatch(const moe_params *p, const void *x, moe_routing *r, void *x_per
 
 int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offsets,
                    const void *w1, const void *w3, const void *w2, void *h, void *y_perm,
-                   void *stream) {
+                   void *workspace, size_t ws_bytes, void *stream) {
     int rc = check_params(p);
     if (rc != MOE_OK) return rc;
     const int64_t R = max_rows_of(*p);
+    const size_t need = ffn_ws_bytes(*p);
     if (!offsets || !w1 || !w3 || !w2) return MOE_ERR_INVALID_ARG;
     if (R > 0 && (!x_perm || !h || !y_perm)) return MOE_ERR_INVALID_ARG;
+    if (need > 0 && (!workspace || ws_bytes < need)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x_perm) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) || !aligned16(h) ||
-        !aligned16(y_perm))
+        !aligned16(y_perm) || !aligned16(workspace))
         return MOE_ERR_UNSUPPORTED;
-    return hip_status(launch_expert_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w1, w3, w2, h, y_perm,
-                                        nullptr, static_cast<hipStream_t>(stream)));
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const int S = splits_of(*p);
+    const GemmOut down{y_perm, workspace, (size_t)R * p->d, nullptr};
+    hipError_t e = launch_expert_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w1, w3, w2, h, down,
+                                     nullptr, nullptr, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    return hip_status(launch_ffn_fixup(*p, R, offsets, static_cast<float *>(y_perm),
+                                       static_cast<const float *>(workspace), S - 1, st));
 }
 
 int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *offsets,
@@ -203,7 +232,8 @@ int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *o
     if ((rc = fp8_weights_ok(*p, w)) != MOE_OK) return rc;
     if (R > 0 && (!x_perm || !h || !y_perm)) return MOE_ERR_INVALID_ARG;
     if (!aligned16(x_perm) || !aligned16(h) || !aligned16(y_perm)) return MOE_ERR_UNSUPPORTED;
-    return hip_status(launch_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w, h, y_perm, nullptr,
+    const GemmOut down{y_perm, nullptr, 0, nullptr};
+    return hip_status(launch_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w, h, down, nullptr, nullptr,
                                  static_cast<hipStream_t>(stream)));
 }
 
@@ -211,10 +241,10 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
                 void *y, void *stream) {
     int rc = check_params(p);
     if (rc != MOE_OK) return rc;
-    if (p->T > 0 && (!row || !gate || !y || (max_rows_of(*p) > 0 && !y_perm))) return MOE_ERR_INVALID_ARG;
-    if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
     const int64_t R = max_rows_of(*p);
-    return hip_status(launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, y_perm, row, gate, y,
+    if (p->T > 0 && (!row || !gate || !y || (R > 0 && !y_perm))) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(y_perm) || !aligned16(y)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_combine(*p, R, static_cast<const float *>(y_perm), row, gate, y,
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -222,9 +252,12 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
 
 namespace {
 
+// events: null, or 6 hipEvent_t (null entries skipped) recorded before route,
+// dispatch, the gate-up GEMM, the down GEMM and the combine, and after the
+// combine.
 int forward_impl(const moe_params *p, const void *x, const void *w_router, const float *bias,
                  const float *load, const FfnWeights &w, void *y, float *logits, moe_routing *r,
-                 void *workspace, size_t ws_bytes, void *stream) {
+                 void *workspace, size_t ws_bytes, void *stream, void *const *events) {
     int rc = check_params(p);
     if (rc != MOE_OK) return rc;
     if (!routing_ok(r, *p) || !w_router || !w.w1 || !w.w3 || !w.w2 || !workspace ||
@@ -236,22 +269,43 @@ int forward_impl(const moe_params *p, const void *x, const void *w_router, const
         !aligned16(w.w2) || !aligned16(y) || !aligned16(workspace))
         return MOE_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    auto mark = [&](int i) {
+        if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+    };
     const ForwardWs f = carve_forward(workspace, *p);
     const int64_t C = capacity_of(*p);
     const int64_t R = max_rows_of(*p);
+    const int S = splits_of(*p);
+    mark(0);
     hipError_t e = launch_route(*p, x, w_router, bias, load, logits, r->cand, r->cand_score, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(1);
     DispatchScratch ds = carve_dispatch(f.dispatch, p->T, p->E, p->k);
     ds.claim = f.claim;  // zeroed by the dispatch, used by the expert GEMM
+    ds.gate_of_row = f.gate_of_row;
     e = launch_dispatch(*p, C, x, *r, f.x_perm, ds, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(2);
+    // bf16: the down projection folds each row's gate in and stores fp16
+    // slices; fp32: y_perm [R][d] in fp32, gates applied by the combine
+    const size_t stride = (size_t)R * p->d;
+    const GemmOut down = p->dtype == MOE_BF16
+                             ? GemmOut{f.y, static_cast<uint16_t *>(f.y) + stride, stride, f.gate_of_row}
+                             : GemmOut{f.y, nullptr, stride, nullptr};
+    hipEvent_t mid = events ? static_cast<hipEvent_t>(events[3]) : nullptr;
     if (f.x_perm)
-        e = launch_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w, f.h, f.y_perm, f.claim, st);
+        e = launch_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w, f.h, down, f.claim, mid, st);
     else
-        e = launch_ffn(*p, R, C, x, r->token_of_row, r->offsets, w, f.h, f.y_perm, f.claim, st);
+        e = launch_ffn(*p, R, C, x, r->token_of_row, r->offsets, w, f.h, down, f.claim, mid, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    e = launch_combine(*p, ffn_splits(*p, R), (size_t)R * p->d, f.y_perm, r->row, r->gate, y, st);
-    return hip_status(e);
+    mark(4);
+    if (p->dtype == MOE_BF16)
+        e = launch_combine_gated(*p, R, S, static_cast<const uint16_t *>(f.y), r->row, y, st);
+    else
+        e = launch_combine(*p, R, static_cast<const float *>(f.y), r->row, r->gate, y, st);
+    if (e != hipSuccess) return MOE_ERR_HIP;
+    mark(5);
+    return MOE_OK;
 }
 
 }  // namespace
@@ -262,7 +316,15 @@ int moe_forward(const moe_params *p, const void *x, const void *w_router, const 
                 const float *load, const void *w1, const void *w3, const void *w2, void *y,
                 float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
     return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, nullptr, nullptr, nullptr}, y,
-                        logits, r, workspace, ws_bytes, stream);
+                        logits, r, workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_forward_events(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                       const float *load, const void *w1, const void *w3, const void *w2, void *y,
+                       float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream,
+                       void *const *events) {
+    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, nullptr, nullptr, nullptr}, y,
+                        logits, r, workspace, ws_bytes, stream, events);
 }
 
 int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, const float *bias,
@@ -271,7 +333,7 @@ int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, co
                     moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
     if (!s1 || !s3 || !s2) return MOE_ERR_INVALID_ARG;
     return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, s1, s3, s2}, y, logits, r,
-                        workspace, ws_bytes, stream);
+                        workspace, ws_bytes, stream, nullptr);
 }
 
 const char *moe_strerror(int code) {

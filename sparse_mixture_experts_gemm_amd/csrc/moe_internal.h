@@ -24,6 +24,7 @@ struct DispatchScratch {
     int32_t *fb_hist;    // [NB][E]
     int32_t *fill_prim;  // [E]
     int32_t *claim = nullptr;  // [kClaimCounters] zeroed by the dispatch for the GEMM's work claims, or null
+    float *gate_of_row = nullptr;  // [R] each kept row's gate (the down projection folds it in), or null
 };
 
 // Work-claim counters of the expert GEMM (one per XCD, gate-up then down).
@@ -63,25 +64,47 @@ inline int64_t capacity_rows(const moe_params &p) {
     const double cf = p.dynamic_capacity ? (p.T >= 1 ? 1.0 + 0.01 * log2((double)p.T) : 1.0)
                                          : (double)p.capacity_factor;
     const double c = ceil((double)p.T * (double)p.k / (double)p.E * cf);
+    // clamp before the conversion: an infinite or huge factor gives C = T
+    // (converting a double beyond the int64_t range is undefined)
+    if (!(c < (double)p.T)) return p.T;
     int64_t C = (int64_t)c;
-    if (C > p.T) C = p.T;
     if (C < 0) C = 0;
     return C;
 }
 
-// Number of d_ff slices the down projection is split into (y_perm holds one
-// fp32 partial per slice; the combine adds them).  1 for fp32 layers.
+// Number of d_ff slices the down projection is split into (each slice
+// stores its partial product; the fix-up or the combine adds them in slice
+// order).  1 for fp32 layers.
 int ffn_splits(const moe_params &p, int64_t max_rows);
+
+// Where the expert GEMM writes.  Gate-up: h at y0.  Down: the partial
+// product of d_ff slice s goes to y0 (s = 0) or to y_rest + (s - 1) * stride
+// elements; with row_gate null each partial is stored in fp32 (the layer's
+// element type for fp32 layers), otherwise as the fp16 of row_gate[row] *
+// partial (the combine weight folded in, saturated at +-65504; bf16 layers).
+struct GemmOut {
+    void *y0;
+    void *y_rest;
+    size_t stride;
+    const float *row_gate;
+};
 
 // a_rows == nullptr: A is x_perm.  Otherwise A is the unpermuted x and packed
 // row m is x row a_rows[m] (token_of_row); x must span less than 2 GiB.
 // cap bounds the rows of any one expert (the capacity C).  claim: null, or
 // kClaimCounters zeroed ints through which the 256-row GEMM's blocks claim
 // their work items (an XCD whose range is done takes items of another).
+// mid: null, or an event recorded between the gate-up and down launches.
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
-                             const void *w3, const void *w2, void *h, void *y_perm, int32_t *claim,
-                             hipStream_t st);
+                             const void *w3, const void *w2, void *h, const GemmOut &down, int32_t *claim,
+                             hipEvent_t mid, hipStream_t st);
+
+// y_perm[r] += rest[0][r] + ... + rest[nrest-1][r] (slices max_rows * d
+// apart) for the rows below offsets[E]: a split down projection reduced in
+// slice order.
+hipError_t launch_ffn_fixup(const moe_params &p, int64_t max_rows, const int32_t *offsets, float *y_perm,
+                            const float *rest, int nrest, hipStream_t st);
 
 // One-byte (E4M3) expert weights with fp32 row scales: the weight-streaming
 // kernel only (bf16 layer, cap <= 32 rows per expert, d and d_ff multiples of
@@ -90,9 +113,16 @@ bool fp8_ffn_supported(const moe_params &p);
 hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                                  const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
                                  const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
-                                 void *y_perm, hipStream_t st);
+                                 const GemmOut &down, hipEvent_t mid, hipStream_t st);
 
-hipError_t launch_combine(const moe_params &p, int splits, size_t split_stride, const void *y_perm,
-                          const int32_t *row, const float *gate, void *y, hipStream_t st);
+// y[t] = sum over kept slots j of gate[t][j] * y_perm[row[t][j]], y_perm
+// [R][d] fp32; zeros everywhere when max_rows is 0 (y_perm is then not read).
+hipError_t launch_combine(const moe_params &p, int64_t max_rows, const float *y_perm, const int32_t *row,
+                          const float *gate, void *y, hipStream_t st);
+
+// bf16 layers: y[t] = sum over kept slots j and slices s of yg[s][row[t][j]],
+// yg the down projection's gated fp16 slices [splits][max_rows][d].
+hipError_t launch_combine_gated(const moe_params &p, int64_t max_rows, int splits, const uint16_t *yg,
+                                const int32_t *row, void *y, hipStream_t st);
 
 }  // namespace moe

@@ -43,24 +43,72 @@ def test_capacity_matches_oracle(oracle_mod):
         assert moe.max_rows(p) == min(T * k, E * C)
 
 
+def splits_of(p):
+    """Slices of the down projection, read back from moe_expert_ffn's scratch
+    size: slices 1.. each take R x d fp32."""
+    R = moe.max_rows(p)
+    return 1 + moe.ffn_workspace_bytes(p) // (R * p.d * 4)
+
+
 def test_workspace_sizes_cover_buffers():
     p = P(T=4096, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
     R = moe.max_rows(p)
     assert R == 8192
     ws = moe.workspace_bytes(p)
-    S = moe.ffn_splits(p)
-    # h [R][d_ff] (fp16) and y_perm [S][R][d] (fp32); x spans less than 2 GiB, so
-    # moe_forward reads the gate-up rows from x and needs no x_perm
-    assert ws >= R * 14336 * 2 + S * R * 4096 * 4 + moe.dispatch_workspace_bytes(p)
-    assert ws < R * 14336 * 2 + S * R * 4096 * 4 + R * 4096 * 2
+    S = splits_of(p)
+    assert S == 2 and moe.ffn_workspace_bytes(p) == (S - 1) * R * 4096 * 4
+    # h [R][d_ff] (fp16), the gated rows [S][R][d] (fp16) and the row gates [R];
+    # x spans less than 2 GiB, so moe_forward reads the gate-up rows from x and
+    # needs no x_perm
+    base = R * 14336 * 2 + S * R * 4096 * 2 + R * 4 + moe.dispatch_workspace_bytes(p)
+    assert base <= ws < base + R * 4096 * 2
     assert moe.dispatch_workspace_bytes(p) > 0
+    # an fp32 layer keeps y_perm [R][d] in fp32 and needs no row gates
+    q = P(T=700, d=256, E=4, k=2, d_ff=384, capacity_factor=1.0, dtype=moe.MOE_F32)
+    Rq = moe.max_rows(q)
+    assert moe.ffn_workspace_bytes(q) == 0
+    base = Rq * 384 * 4 + Rq * 256 * 4 + moe.dispatch_workspace_bytes(q)
+    assert base <= moe.workspace_bytes(q) < base + 6 * 256
     # x of 2 GiB and more: moe_forward writes x_perm [R][d] into its workspace
     for T, has_xp in (((1 << 18) - 1, False), (1 << 18, True)):
         q = P(T=T, d=4096, E=8, k=2, d_ff=1024, capacity_factor=1.0, dtype=moe.MOE_BF16)
-        Rq, Sq = moe.max_rows(q), moe.ffn_splits(q)
-        base = Rq * 1024 * 2 + Sq * Rq * 4096 * 4 + moe.dispatch_workspace_bytes(q)
+        Rq, Sq = moe.max_rows(q), splits_of(q)
+        base = Rq * 1024 * 2 + Sq * Rq * 4096 * 2 + Rq * 4 + moe.dispatch_workspace_bytes(q)
         wq = moe.workspace_bytes(q)
         assert (wq >= base + Rq * 4096 * 2) == has_xp and wq >= base, (T, wq, base)
+
+
+def test_ffn_workspace_only_for_split_down_projections():
+    """The expert FFN needs scratch only where its down projection is split
+    (few row tiles for the chip): the Mixtral-shape layer (2 slices) and the
+    skewed layer (4), not the fine-grained layer, the decode shape or fp32."""
+    mix = P(T=4096, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
+    skew = P(T=2048, d=2048, E=16, k=2, d_ff=5632, capacity_factor=1.0, dtype=moe.MOE_BF16)
+    fine = P(T=8192, d=4096, E=64, k=2, d_ff=2048, capacity_factor=1.0, dtype=moe.MOE_BF16)
+    dec = P(T=64, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
+    assert (splits_of(mix), splits_of(skew), splits_of(fine), splits_of(dec)) == (2, 4, 1, 1)
+    assert moe.ffn_workspace_bytes(fine) == moe.ffn_workspace_bytes(dec) == 0
+
+
+@pytest.mark.parametrize("cf", [float("inf"), 1e30, 3.0e38, 1e19])
+def test_huge_capacity_factor_is_uncapped(cf, oracle_mod):
+    """A capacity factor so large that T*k/E*cf exceeds the int64 range (or
+    is infinite) still gives C = T: the clamp comes before the conversion."""
+    for T, k, E in ((64, 2, 8), (4096, 2, 8), (1, 1, 1), (1000, 8, 256)):
+        p = P(T=T, k=k, E=E, capacity_factor=cf)
+        assert moe.capacity(p) == T, (T, k, E, cf)
+        assert moe.max_rows(p) == T * k
+        assert oracle_mod.capacity(T, k, E, cf) == T
+
+
+def test_d_ff_bound_of_the_down_tile():
+    """A 256-row tile of h must span less than 2 GiB: d_ff < 2^22."""
+    assert moe.capacity(P(d=64, d_ff=(1 << 22) - 64)) == 16  # accepted: C = ceil(64 * 2 / 8)
+    r = moe.MoeRouting()
+    p = P(d=64, d_ff=1 << 22)
+    rc = moe.lib().moe_forward(ctypes.byref(p.c()), None, None, None, None, None, None, None, None,
+                               None, ctypes.byref(r), None, 0, None)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("bad", [dict(E=0), dict(E=257), dict(k=0), dict(k=9, E=16), dict(k=3, E=2),
@@ -96,7 +144,7 @@ def test_null_pointers_rejected():
     r = moe.MoeRouting()  # all members NULL
     assert moe.lib().moe_route(ctypes.byref(p.c()), 16, 16, None, None, 16, ctypes.byref(r), None) == moe.MOE_ERR_INVALID_ARG
     assert moe.lib().moe_dispatch(ctypes.byref(p.c()), 16, ctypes.byref(r), 16, 16, 1 << 20, None) == moe.MOE_ERR_INVALID_ARG
-    assert moe.lib().moe_expert_ffn(ctypes.byref(p.c()), 16, None, 16, 16, 16, 16, 16, None) == moe.MOE_ERR_INVALID_ARG
+    assert moe.lib().moe_expert_ffn(ctypes.byref(p.c()), 16, None, 16, 16, 16, 16, 16, None, 0, None) == moe.MOE_ERR_INVALID_ARG
     assert moe.lib().moe_combine(ctypes.byref(p.c()), 16, None, None, 16, None) == moe.MOE_ERR_INVALID_ARG
 
 
@@ -111,6 +159,13 @@ def test_workspace_too_small_rejected():
     rc = moe.lib().moe_dispatch(ctypes.byref(p.c()), 256, ctypes.byref(r), 256, 256,
                                 moe.dispatch_workspace_bytes(p) - 1, None)
     assert rc == moe.MOE_ERR_INVALID_ARG
+    # a split down projection needs its scratch
+    q = P(T=4096, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
+    need = moe.ffn_workspace_bytes(q)
+    assert need > 0
+    for ws, nb in ((None, 0), (256, need - 1)):
+        rc = moe.lib().moe_expert_ffn(ctypes.byref(q.c()), 256, 256, 256, 256, 256, 256, 256, ws, nb, None)
+        assert rc == moe.MOE_ERR_INVALID_ARG
 
 
 def test_misaligned_pointer_rejected():

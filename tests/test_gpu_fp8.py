@@ -4,7 +4,9 @@ the same codes and scales exactly (double) and runs its plain SwiGLU FFN.
 
 Tolerances as for the bf16 layer: h (rounded once to fp16) within one fp16
 ulp per element plus 1e-4 * RMS for fp32 accumulation; y_perm and the layer
-output within 2e-2 * RMS, the output beyond one bf16 unit roundoff of |ref|.
+output within 2e-2 * RMS (the output beyond one bf16 unit roundoff of |ref|
+only where the storage rounding of the largest element alone would take half
+of that budget).
 Routing arrays bit-exact with the oracle run on the GPU's fp32 logits.
 """
 import sys
@@ -86,7 +88,6 @@ def check_layer(L, full=True, rows_sample=None):
     moe.dispatch(p, L.x, r, x_perm, moe.alloc_workspace(p, DEV, dispatch_only=True))
     h = torch.empty((max(R, 1), dff), dtype=torch.float16, device=DEV)
     y_perm = moe.alloc_y_perm(p, DEV)
-    assert y_perm.shape[0] == 1
     say(f"[expert_ffn_fp8] T={T} R={R}")
     moe.expert_ffn_fp8(p, x_perm, r.offsets, *L.weights(), h, y_perm)
     torch.cuda.synchronize()
@@ -103,10 +104,12 @@ def check_layer(L, full=True, rows_sample=None):
         hg = h.float().cpu().numpy()[srows].astype(np.float64)
         bad = np.abs(hg - ho) > 2.0 ** -10 * np.abs(ho) + 1e-4 * rms(ho)
         assert not bad.any(), f"h: {bad.sum()} elements beyond rounding bound"
-        yg = y_perm[0].double().cpu().numpy()[srows]
+        yg = y_perm.double().cpu().numpy()[srows]
         err = np.abs(yg - yo).max()
         assert err <= 2e-2 * rms(yo), f"y_perm: {err:.3e} > 2e-2 * {rms(yo):.3e}"
-    # combine, then the whole layer through moe_forward_fp8: bit-identical
+    # combine, then the whole layer through moe_forward_fp8 (gates folded into
+    # the down projection, gated rows in fp16): within one bf16 ulp of the
+    # staged output plus the fp16 roundings
     y = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
     moe.combine(p, y_perm, r.row, r.gate, y)
     say(f"[forward_fp8] T={T}")
@@ -115,12 +118,18 @@ def check_layer(L, full=True, rows_sample=None):
     logits2 = torch.empty((T, p.E), dtype=torch.float32, device=DEV)
     moe.forward_fp8(p, L.x, L.wr, L.bias, None, *L.weights(), y2, logits2, r2, moe.alloc_workspace(p, DEV))
     torch.cuda.synchronize()
-    assert torch.equal(y2.view(torch.int16), y.view(torch.int16)), "moe_forward_fp8 differs from the staged path"
+    ys, y2f = y.float().cpu().numpy().astype(np.float64), y2.float().cpu().numpy().astype(np.float64)
+    bad = np.abs(y2f - ys) > 2.0 ** -7 * np.abs(ys) + 2.0 ** -7 * rms(ys)
+    assert not bad.any(), f"moe_forward_fp8 vs staged: {bad.sum()} elements beyond rounding bound"
     ref2 = routing_exact(p, r2.cpu(), logits2.cpu().numpy())
     toks = np.arange(T, dtype=np.int32) if full else np.unique(np.r_[0, T - 1, np.arange(0, T, 7)]).astype(np.int32)
     yref = oracle.layer_tokens(toks, L.xd, L.wd["w1"], L.wd["w3"], L.wd["w2"], ref2["eid"], ref2["gate64"])
     got = y2.float().cpu().numpy()[toks].astype(np.float64)
-    dev = np.abs(got - yref) - 2.0 ** -8 * np.abs(yref)
+    dev = np.abs(got - yref)
+    # the bf16 storage rounding of each element is allowed only where that of the
+    # largest one alone would take half the 2e-2 * RMS budget (as in the bf16 parity tests)
+    if dev.size and np.abs(yref).max() * 2.0 ** -9 >= 0.5 * 2e-2 * rms(yref):
+        dev = dev - 2.0 ** -8 * np.abs(yref)
     err = float(dev.max()) if dev.size else 0.0
     assert err <= 2e-2 * rms(yref) + 1e-30, f"layer output: {err:.3e} > 2e-2 * {rms(yref):.3e}"
     say(f"[ok] T={T} rows={rows} dropped={int(ref2['totals'][1])} max|err|/RMS={err / max(rms(yref), 1e-30):.2e}")

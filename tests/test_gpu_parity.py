@@ -2,10 +2,12 @@
 
 Routing arrays must be bit-exact with the oracle run on the GPU's fp32 router
 logits.  Layer outputs (and y_perm) must satisfy max|err| <= 2e-2 * RMS(ref)
-for bf16 (fp32 accumulation) and <= 1e-4 * RMS(ref) for fp32, the layer
-output beyond the rounding of each element to its storage type (one unit
-roundoff of |ref|); edge cases in which whole tokens are dropped take the RMS
-over the tokens that kept a slot.
+for bf16 (fp32 accumulation) and <= 1e-4 * RMS(ref) for fp32.  The five
+workloads are held to that plain bound.  Only where the storage rounding of
+the largest output element alone would take half the budget (small hidden
+sizes, whose outputs have elements of 7-9 RMS) may each element of the layer
+output also carry that rounding (one unit roundoff of |ref|).  Edge cases in
+which whole tokens are dropped take the RMS over the tokens that kept a slot.
 Intermediates rounded once (h, the combine's store) are held to one ulp of
 their storage type per element.  Router logits are compared with the
 oracle's own double-accumulated logits at 1e-3 * RMS.
@@ -56,19 +58,22 @@ def rms(a):
 def assert_close(got, ref, dtype, what, rms_rows=None, stored=False):
     """max|err| <= tol * RMS(ref); rms_rows selects the rows the RMS is taken
     over (edge cases with many fully dropped tokens use the kept rows).
-    stored: `got` is the layer output in its element type, so each element
-    may also carry that type's own rounding of the exact value, up to one
-    unit roundoff of |ref| (2^-8 for bf16, 2^-24 for fp32); at small hidden
-    sizes the output has elements of 7-9 RMS, where the bf16 rounding alone
-    reaches 2-3% of RMS."""
+    stored: `got` is the layer output in its element type.  Where the
+    rounding of the largest element to that type (half a unit roundoff,
+    2^-9 |ref| for bf16) alone reaches half the budget, each element may
+    also carry that rounding (one unit roundoff of |ref|): at small hidden
+    sizes the output has elements of 7-9 RMS, whose bf16 rounding alone is
+    2-3% of RMS.  Elsewhere (every full-size workload) the plain bound
+    applies."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     r = rms(ref if rms_rows is None else ref[rms_rows])
     if not ref.size:
         return 0.0
     dev = np.abs(got - ref)
-    if stored:
-        dev = dev - (2.0 ** -8 if dtype == moe.MOE_BF16 else 2.0 ** -24) * np.abs(ref)
+    u = 2.0 ** -8 if dtype == moe.MOE_BF16 else 2.0 ** -24
+    if stored and float(np.abs(ref).max()) * u / 2 >= 0.5 * TOL[dtype] * r:
+        dev = dev - u * np.abs(ref)
     err = float(dev.max())
     assert err <= TOL[dtype] * r + 1e-30, f"{what}: max|err| {err:.3e} > {TOL[dtype]} * RMS {r:.3e}"
     return err / r if r > 0 else 0.0
@@ -166,9 +171,9 @@ def sample_rows(offsets, n_per, rng, cap=48):
     return np.array(sorted(rows), np.int32)
 
 
-def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
+def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False, stored=False):
     """Run the four stage entry points, check each against the oracle, then
-    moe_forward end to end."""
+    moe_forward end to end (stored: see assert_close)."""
     cfg = L.cfg
     g = L.g
     dt = p.torch_dtype
@@ -207,7 +212,8 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
     say(f"[expert_ffn] {cfg.name} rows={rows}")
     h = torch.empty((max(R, 1), dff), dtype=torch.float16 if p.dtype == moe.MOE_BF16 else dt, device=DEV)
     y_perm = moe.alloc_y_perm(p, DEV)
-    moe.expert_ffn(p, x_perm, r.offsets, g["w1"], g["w3"], g["w2"], h, y_perm)
+    wsf_ffn = moe.alloc_workspace(p, DEV, ffn_only=True) if moe.ffn_workspace_bytes(p) else None
+    moe.expert_ffn(p, x_perm, r.offsets, g["w1"], g["w3"], g["w2"], h, y_perm, wsf_ffn)
     torch.cuda.synchronize()
     offs = ref["offsets"]
     srows = np.arange(rows, dtype=np.int32) if full_rows else sample_rows(offs, 5, rng)
@@ -219,20 +225,14 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
             assert_close_elementwise(h.float().cpu().numpy()[srows], ho, 2.0 ** -10, 1e-4, "h")
         else:
             assert_close_elementwise(h.cpu().numpy()[srows], ho, 1e-5, 1e-5, "h")
-        yp_sum = y_perm.double().sum(dim=0).cpu().numpy()  # the S slices of the d_ff reduction
-        assert_close(yp_sum[srows], yo, p.dtype, "y_perm")
+        assert_close(y_perm.double().cpu().numpy()[srows], yo, p.dtype, "y_perm")
 
     # ---- combine
     say(f"[combine] {cfg.name}")
     y = torch.empty((T, d), dtype=dt, device=DEV)
     moe.combine(p, y_perm, r.row, r.gate, y)
     torch.cuda.synchronize()
-    # the oracle combines full y_perm rows: the sum of the device's S slices, formed in fp32 in
-    # slice order as the combine forms it
-    yp_rows = y_perm[0].clone()
-    for sl in range(1, y_perm.shape[0]):
-        yp_rows += y_perm[sl]
-    yc = oracle.combine(rc["row"].numpy(), rc["gate"].numpy(), np_of(yp_rows[:max(rows, 1)].cpu()))
+    yc = oracle.combine(rc["row"].numpy(), rc["gate"].numpy(), np_of(y_perm[:max(rows, 1)].cpu()))
     # combine's only rounding is the final store
     assert_close_elementwise(y.float().cpu().numpy(), yc, 2.0 ** -8 if p.dtype == moe.MOE_BF16 else 1e-6,
                              1e-6, "combine")
@@ -247,20 +247,27 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False):
     torch.cuda.synchronize()
     gl2 = logits2.cpu().numpy()
     assert np.array_equal(gl2.view(np.uint32), gl.view(np.uint32)), "forward logits differ from moe_route"
-    # moe_forward reads the gate-up rows from x through token_of_row instead of
-    # a materialised x_perm: same values in the same order, so the output is
-    # bit-identical to the stage-by-stage path
-    iv = torch.int16 if p.dtype == moe.MOE_BF16 else torch.int32
-    assert torch.equal(y2.view(iv), y.view(iv)), "moe_forward differs from the staged path"
+    if p.dtype == moe.MOE_F32:
+        # fp32: the same kernels in the same order, the gate-up rows read from
+        # x through token_of_row instead of a materialised x_perm: bit-identical
+        assert torch.equal(y2.view(torch.int32), y.view(torch.int32)), "moe_forward differs from the staged path"
+    else:
+        # bf16: the gates folded into the down projection, whose gated rows are
+        # kept in fp16 (2^-11 relative each) before the same single rounding:
+        # within one bf16 ulp of the staged output, plus the fp16 roundings
+        assert_close_elementwise(y2.float().cpu().numpy(), y.float().cpu().numpy(), 2.0 ** -7, 2.0 ** -7,
+                                 "moe_forward vs staged")
     rc2 = r2.cpu()
     ref2 = routing_vs_oracle(p, rc2, gl2, L.load, p.lam)
     toks = np.arange(T, dtype=np.int32) if (full_rows or T <= 64) else sample_tokens(ref2, T, n_tok, rng)
     yref = oracle.layer_tokens(toks, L.c["x"], L.c["w1"], L.c["w3"], L.c["w2"], ref2["eid"], ref2["gate64"])
     kept_rows = (ref2["flag"][toks] != 2).any(axis=1) if rms_kept_rows else None
-    rel = assert_close(y2.float().cpu().numpy()[toks], yref, p.dtype, "layer output", kept_rows, stored=True)
+    rel = assert_close(y2.float().cpu().numpy()[toks], yref, p.dtype, "layer output", kept_rows, stored=stored)
+    rel_staged = assert_close(y.float().cpu().numpy()[toks], yref, p.dtype, "staged layer output", kept_rows,
+                              stored=stored)
     # informational: routing under the oracle's own logits
     say(f"[ok] {cfg.name}: rows={rows} dropped={int(ref2['totals'][1])} rerouted={int(ref2['totals'][2])} "
-        f"max|err|/RMS={rel:.2e}")
+        f"max|err|/RMS forward {rel:.2e}, staged {rel_staged:.2e}")
     return dict(ref=ref2, y=y2, rc=rc2)
 
 
@@ -283,7 +290,7 @@ def test_tiles_and_ragged_tails_full(dtype):
     """Several GEMM tiles per expert and ragged tails, every row and token checked."""
     cfg = small_cfg(dtype=dtype)
     L = Layer(cfg)
-    run_stages(L, params(cfg), full_rows=True)
+    run_stages(L, params(cfg), full_rows=True, stored=True)
 
 
 EDGE = {
@@ -319,7 +326,7 @@ EDGE = {
 def test_edge_cases(case):
     cfg = small_cfg(**EDGE[case])
     L = Layer(cfg)
-    run_stages(L, params(cfg), full_rows=True, rms_kept_rows=True)
+    run_stages(L, params(cfg), full_rows=True, rms_kept_rows=True, stored=True)
 
 
 def test_empty_batch():
@@ -351,7 +358,7 @@ def test_identical_tokens_tied_logits():
     # tie two experts exactly: identical gate vectors
     L.g["w_router"][3] = L.g["w_router"][1]
     L.c["w_router"] = np_of(L.g["w_router"].cpu())
-    out = run_stages(L, params(cfg), full_rows=True, rms_kept_rows=True)
+    out = run_stages(L, params(cfg), full_rows=True, rms_kept_rows=True, stored=True)
     assert out["ref"]["totals"][1] > 0  # capacity exhausted
 
 
