@@ -60,6 +60,11 @@ extern "C" {
 #define MOE_ERR_INVALID_ARG (-1) /* null pointer, size out of range, workspace too small */
 #define MOE_ERR_UNSUPPORTED (-2) /* dtype, alignment or a dimension the kernels do not take */
 #define MOE_ERR_HIP (-3)         /* a kernel launch failed */
+#define MOE_ERR_TOO_LARGE (-4)   /* moe_forward_noalloc: the layer's scratch exceeds the static array */
+
+/* Bytes of the static scratch array behind moe_forward_noalloc (32 MiB,
+ * one copy per GPU the library runs on, held until the process ends). */
+#define MOE_STATIC_SCRATCH_BYTES (32u << 20)
 
 typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
@@ -245,6 +250,24 @@ int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, con
 int moe_forward(const moe_params *p, const void *x, const void *w_router, const float *bias,
                 const float *load, const void *w1, const void *w3, const void *w2, void *y,
                 float *logits, moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  The
+ * caller passes inputs and outputs only; the workspace is a file-scope
+ * device array of MOE_STATIC_SCRATCH_BYTES in the library, one per GPU
+ * (its address looked up on the first call on each device).  No allocation
+ * of any kind happens in the call.  A layer whose workspace
+ * (moe_workspace_bytes(p)) exceeds the array returns MOE_ERR_TOO_LARGE
+ * (32 MiB holds, for example, a Mixtral-shape layer of d 4096, E 8, top-2,
+ * d_ff 14336, capacity factor 1.25, up to 178 tokens).  Every call on one GPU shares that
+ * GPU's array: calls that overlap on one GPU (different streams or host
+ * threads) race and must not be issued.  Results are identical to
+ * moe_forward's on the same inputs.
+ */
+int moe_forward_noalloc(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                        const float *load, const void *w1, const void *w3, const void *w2, void *y,
+                        float *logits, moe_routing *r, void *stream);
 
 /*
  * moe_forward with per-stage timing marks: events is NULL or an array of six

@@ -20,7 +20,8 @@ import torch  # load torch's HIP runtime before the library binds to it
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_hip.so")
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP = 0, -1, -2, -3
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_HIP, MOE_ERR_TOO_LARGE = 0, -1, -2, -3, -4
+STATIC_SCRATCH_BYTES = 32 << 20  # MOE_STATIC_SCRATCH_BYTES: the array behind forward_noalloc
 MOE_F32, MOE_BF16 = 0, 1
 
 
@@ -75,10 +76,11 @@ def lib():
         L.moe_forward.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P]
         L.moe_forward_events.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P,
                                          ctypes.POINTER(ctypes.c_void_p)]
+        L.moe_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P]
         L.moe_expert_ffn_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P]
         L.moe_forward_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P]
         for f in (L.moe_route, L.moe_dispatch, L.moe_expert_ffn, L.moe_combine, L.moe_forward,
-                  L.moe_forward_events, L.moe_expert_ffn_fp8, L.moe_forward_fp8):
+                  L.moe_forward_events, L.moe_forward_noalloc, L.moe_expert_ffn_fp8, L.moe_forward_fp8):
             f.restype = ctypes.c_int
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -226,6 +228,14 @@ def forward(p: Params, x, w_router, bias, load, w1, w3, w2, y, logits, r: Routin
                            _ptr(workspace), workspace.numel() * workspace.element_size(),
                            _stream(stream))
     _check(rc, "moe_forward")
+
+
+def forward_noalloc(p: Params, x, w_router, bias, load, w1, w3, w2, y, logits, r: Routing, stream=None):
+    """moe_forward on the library's static scratch array (no workspace, no allocation)."""
+    rc = lib().moe_forward_noalloc(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(load),
+                                   _ptr(w1), _ptr(w3), _ptr(w2), _ptr(y), _ptr(logits), ctypes.byref(r.c()),
+                                   _stream(stream))
+    _check(rc, "moe_forward_noalloc")
 
 
 def forward_events(p: Params, x, w_router, bias, load, w1, w3, w2, y, logits, r: Routing, workspace, events,

@@ -3,11 +3,39 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "moe_internal.h"
 
 using namespace moe;
 
+// Scratch of moe_forward_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends.  Host code never passes `scratch`
+// itself to a kernel (in host code the name is a host-side stand-in); it
+// uses the device address hipGetSymbolAddress returns for the current GPU.
+static __device__ __align__(256) char scratch[MOE_STATIC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr int kMaxDevices = 64;
+
+// The device address of `scratch` on the current GPU, looked up once per
+// device (with that device current) and kept; null if the lookup fails.
+void *scratch_ptr() {
+    static std::mutex mu;
+    static void *ptr[kMaxDevices] = {};
+    static bool done[kMaxDevices] = {};
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!done[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        ptr[dev] = p;
+        done[dev] = true;
+    }
+    return ptr[dev];
+}
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
 
@@ -327,6 +355,18 @@ int moe_forward_events(const moe_params *p, const void *x, const void *w_router,
                         logits, r, workspace, ws_bytes, stream, events);
 }
 
+int moe_forward_noalloc(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                        const float *load, const void *w1, const void *w3, const void *w2, void *y,
+                        float *logits, moe_routing *r, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    if (forward_ws_bytes(*p) > (size_t)MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_TOO_LARGE;
+    void *ws = scratch_ptr();
+    if (!ws) return MOE_ERR_HIP;
+    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, nullptr, nullptr, nullptr}, y,
+                        logits, r, ws, (size_t)MOE_STATIC_SCRATCH_BYTES, stream, nullptr);
+}
+
 int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, const float *bias,
                     const float *load, const uint8_t *w1, const float *s1, const uint8_t *w3,
                     const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
@@ -342,6 +382,7 @@ const char *moe_strerror(int code) {
         case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, size out of range or workspace too small)";
         case MOE_ERR_UNSUPPORTED: return "unsupported dtype, alignment or dimension";
         case MOE_ERR_HIP: return "HIP kernel launch failed";
+        case MOE_ERR_TOO_LARGE: return "layer needs more scratch than the static scratch array holds";
         default: return "unknown error code";
     }
 }
