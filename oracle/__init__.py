@@ -61,6 +61,11 @@ def lib():
         L.oracle_fp8_e4m3_value.restype = f64
         L.oracle_fp8_e4m3_decode.argtypes = [i64, P, P]
         L.oracle_dequant_rows.argtypes = [i64, i64, P, P, P]
+        L.oracle_backward_tokens.argtypes = [i32, P, i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, P, P, P, P]
+        L.oracle_backward_expert_units.argtypes = [i32, i32, P, i32, P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
+        L.oracle_router_wgrad.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        for f in (L.oracle_backward_tokens, L.oracle_backward_expert_units, L.oracle_router_wgrad):
+            f.restype = None
         for f in (L.oracle_router_logits, L.oracle_router_logits_glu, L.oracle_scores, L.oracle_topk, L.oracle_gap_swap, L.oracle_dispatch,
                   L.oracle_ffn_rows, L.oracle_layer_tokens, L.oracle_combine, L.oracle_fp8_e4m3_decode,
                   L.oracle_dequant_rows):
@@ -283,3 +288,81 @@ def forward(x, wr, bias, w1, w3, w2, E: int, k: int, cf: float, load=None, lam: 
     out = dict(raw=raw, cand=cand, cand_score=cs, C=C, y=y)
     out.update(disp)
     return out
+
+
+# ---------------------------------------------------------------- backward --
+def backward_tokens(tokens, x, wr, w1, w3, w2, eid, gate64, dy, tau: float = 1.0):
+    """Router-logit gradient dlogits [n, E] and input gradient dx [n, d]
+    (double) for the listed tokens, the routing held fixed."""
+    tokens = _np(tokens).astype(np.int32)
+    x, wr, w1, w3, w2 = _np(x), _np(wr), _np(w1), _np(w3), _np(w2)
+    assert x.dtype == wr.dtype == w1.dtype == w3.dtype == w2.dtype
+    eid = _np(eid).astype(np.int32)
+    gate64 = _np(gate64).astype(np.float64)
+    dy = np.ascontiguousarray(_np(dy), dtype=np.float64)
+    E, d_ff, d = w1.shape
+    k = eid.shape[1]
+    assert k <= 64 and dy.shape == (x.shape[0], d)
+    n = tokens.shape[0]
+    dl = np.empty((n, E), np.float64)
+    dx = np.empty((n, d), np.float64)
+    lib().oracle_backward_tokens(n, _p(tokens), d, E, k, d_ff, _dt(x), float(tau), _p(x), _p(wr), _p(w1),
+                                 _p(w3), _p(w2), _p(eid), _p(gate64), _p(dy), _p(dl), _p(dx))
+    return dl, dx
+
+
+def backward_expert_units(e: int, fs, tok, g, x, w1, w3, w2, dy):
+    """Weight gradients of expert e for the intermediate units fs: rows
+    dW1[e][f], dW3[e][f] ([nf, d] each) and columns dW2[e][:, f] ([d, nf]).
+    The expert's kept slots are (tok[r], g[r]) in row order."""
+    fs = _np(fs).astype(np.int32)
+    tok = _np(tok).astype(np.int32)
+    g = np.ascontiguousarray(_np(g), dtype=np.float64)
+    x, w1, w3, w2 = _np(x), _np(w1), _np(w3), _np(w2)
+    dy = np.ascontiguousarray(_np(dy), dtype=np.float64)
+    E, d_ff, d = w1.shape
+    nf = fs.shape[0]
+    dw1 = np.empty((nf, d), np.float64)
+    dw3 = np.empty((nf, d), np.float64)
+    dw2 = np.empty((d, nf), np.float64)
+    lib().oracle_backward_expert_units(e, nf, _p(fs), tok.shape[0], _p(tok), _p(g), d, d_ff, _dt(x), _p(x),
+                                       _p(w1), _p(w3), _p(w2), _p(dy), _p(dw1), _p(dw3), _p(dw2))
+    return dw1, dw3, dw2
+
+
+def router_wgrad(x, dlogits):
+    """dW_r [E, d] = dlogits^T x and dbias [E] = column sums of dlogits."""
+    x = _np(x)
+    dlogits = np.ascontiguousarray(_np(dlogits), dtype=np.float64)
+    T, d = x.shape
+    E = dlogits.shape[1]
+    dwr = np.empty((E, d), np.float64)
+    db = np.empty(E, np.float64)
+    lib().oracle_router_wgrad(T, d, E, _dt(x), _p(x), _p(dlogits), _p(dwr), _p(db))
+    return dwr, db
+
+
+def expert_slots(eid, row, gate64, e: int):
+    """The kept slots of expert e in row order: (tokens, gates)."""
+    eid, row = _np(eid), _np(row)
+    t, j = np.nonzero(eid == e)
+    order = np.argsort(row[t, j], kind="stable")
+    return t[order].astype(np.int32), np.asarray(gate64)[t[order], j[order]].astype(np.float64)
+
+
+def backward(x, wr, w1, w3, w2, eid, row, gate64, dy, tau: float = 1.0) -> dict:
+    """The whole backward pass (small layers): dlogits, dx, dW_r, dbias, dW1,
+    dW3, dW2 in double, the routing (eid, row, gate64 of the forward) fixed."""
+    x = _np(x)
+    T = x.shape[0]
+    E, d_ff, d = _np(w1).shape
+    dl, dx = backward_tokens(np.arange(T, dtype=np.int32), x, wr, w1, w3, w2, eid, gate64, dy, tau)
+    dwr, dbias = router_wgrad(x, dl)
+    dw1 = np.empty((E, d_ff, d))
+    dw3 = np.empty((E, d_ff, d))
+    dw2 = np.empty((E, d, d_ff))
+    fs = np.arange(d_ff, dtype=np.int32)
+    for e in range(E):
+        tok, g = expert_slots(eid, row, gate64, e)
+        dw1[e], dw3[e], dw2[e] = backward_expert_units(e, fs, tok, g, x, w1, w3, w2, dy)
+    return dict(dlogits=dl, dx=dx, dwr=dwr, dbias=dbias, dw1=dw1, dw3=dw3, dw2=dw2)

@@ -543,3 +543,193 @@ void oracle_combine(int T, int k, int d, int dt, const int32_t *row, const float
         }
     }
 }
+
+/*
+ * ------------------------------------------------------------------------
+ * Backward pass (training).  The pages train the router through the experts:
+ * its gradient is what flows back from the experts' outputs (P2 §3.3, "the
+ * router's gradient comes from the experts' gradients flowing back").
+ * Readings:
+ *   - the routing decisions (ranking, capacity, re-route, drop) are held
+ *     fixed, as the forward pass took them: they are piecewise constant in
+ *     the inputs, so the gradient flows through the gates of the kept slots
+ *     and through the experts only (inference-style deterministic top-k; the
+ *     Gumbel noise P2 §3.3 adds during training is not part of this layer);
+ *   - the load-balancing loss of P3 §4.2 counts top-k picks under no_grad,
+ *     so its gradient with respect to every input is zero and adds nothing;
+ *   - the penalty load vector is an input without a gradient.
+ * With do = g_j dy_t the upstream gradient of a kept slot's expert output
+ * o_j = FFN_e(x_t) (y_t = sum_j g_j o_j, P5 §3 step 5), the chain rule gives
+ *   u    = W2_e^T dy_t                    (d_ff)
+ *   dh   = g_j u                          (gradient of h = silu(a) * b)
+ *   da   = dh * b * silu'(a),  db = dh * silu(a),
+ *          silu'(a) = s(a) (1 + a (1 - s(a))), s the logistic function
+ *   dW2_e += do h^T,  dW1_e += da x_t^T,  dW3_e += db x_t^T
+ *   dx_t  += W1_e^T da + W3_e^T db
+ *   dg_j  = dy_t . o_j
+ * and through the gate softmax over the kept slots K_t (scores s divided by
+ * the temperature tau, P3 §3.1):
+ *   ds_j  = g_j (dg_j - sum_{l in K_t} g_l dg_l) / tau   for j in K_t,
+ * which is the gradient of the router logit raw[t][eid_j] (s = raw - lambda
+ * load, and raw = x W_r^T + bias), so
+ *   dlogits[t][eid_j] = ds_j (0 for every other expert),
+ *   dx_t += sum_e dlogits[t][e] W_r[e],  dW_r = dlogits^T x,  dbias = sum_t dlogits[t].
+ * dy is double; x and the weights have element type dt.
+ * ------------------------------------------------------------------------
+ */
+
+static double logistic(double a) { return 1.0 / (1.0 + exp(-a)); }
+
+/*
+ * Per-token part for a list of tokens: the router-logit gradient
+ * dlogits [n][E] and the input gradient dx [n][d] (expert and router terms).
+ */
+void oracle_backward_tokens(int n, const int32_t *tokens, int d, int E, int k, int d_ff, int dt, double tau,
+                            const void *x, const void *wr, const void *w1, const void *w3, const void *w2,
+                            const int32_t *eid, const double *gate64, const double *dy, double *dlogits,
+                            double *dx)
+{
+#pragma omp parallel
+    {
+        double *a = (double *)malloc((size_t)d_ff * sizeof(double));
+        double *b = (double *)malloc((size_t)d_ff * sizeof(double));
+        double *u = (double *)malloc((size_t)d_ff * sizeof(double));
+        double dg[64];
+#pragma omp for schedule(dynamic, 1)
+        for (int i = 0; i < n; i++) {
+            const int t = tokens[i];
+            const double *dyt = dy + (size_t)t * d;
+            double *dxt = dx + (size_t)i * d;
+            double *dlt = dlogits + (size_t)i * E;
+            for (int q = 0; q < d; q++)
+                dxt[q] = 0.0;
+            for (int e = 0; e < E; e++)
+                dlt[e] = 0.0;
+            for (int r = 0; r < k; r++) {
+                const int e = eid[(size_t)t * k + r];
+                dg[r] = 0.0;
+                if (e < 0)
+                    continue;
+                const double g = gate64[(size_t)t * k + r];
+                const size_t wo = (size_t)e * d_ff * d, w2o = (size_t)e * d * d_ff;
+                /* pre-activations a = W1 x, b = W3 x and u = W2^T dy */
+                for (int j = 0; j < d_ff; j++) {
+                    double sa = 0.0, sb = 0.0, su = 0.0;
+                    for (int q = 0; q < d; q++) {
+                        const double xv = elem(x, (size_t)t * d + q, dt);
+                        sa += xv * elem(w1, wo + (size_t)j * d + q, dt);
+                        sb += xv * elem(w3, wo + (size_t)j * d + q, dt);
+                        su += dyt[q] * elem(w2, w2o + (size_t)q * d_ff + j, dt);
+                    }
+                    a[j] = sa;
+                    b[j] = sb;
+                    u[j] = su;
+                }
+                /* dg = dy . o = dy . (W2 h) = u . h */
+                double s = 0.0;
+                for (int j = 0; j < d_ff; j++) {
+                    const double sg = logistic(a[j]);
+                    const double silu = a[j] * sg;
+                    s += u[j] * silu * b[j];
+                    /* input gradient through the expert: W1^T da + W3^T db */
+                    const double dh = g * u[j];
+                    const double da = dh * b[j] * sg * (1.0 + a[j] * (1.0 - sg));
+                    const double db = dh * silu;
+                    for (int q = 0; q < d; q++)
+                        dxt[q] += da * elem(w1, wo + (size_t)j * d + q, dt) + db * elem(w3, wo + (size_t)j * d + q, dt);
+                }
+                dg[r] = s;
+            }
+            /* softmax over the kept slots: ds_j = g_j (dg_j - sum_l g_l dg_l) / tau */
+            double mean = 0.0;
+            for (int r = 0; r < k; r++)
+                if (eid[(size_t)t * k + r] >= 0)
+                    mean += gate64[(size_t)t * k + r] * dg[r];
+            for (int r = 0; r < k; r++) {
+                const int e = eid[(size_t)t * k + r];
+                if (e >= 0)
+                    dlt[e] = gate64[(size_t)t * k + r] * (dg[r] - mean) / tau;
+            }
+            /* router term of the input gradient */
+            for (int e = 0; e < E; e++) {
+                if (dlt[e] == 0.0)
+                    continue;
+                for (int q = 0; q < d; q++)
+                    dxt[q] += dlt[e] * elem(wr, (size_t)e * d + q, dt);
+            }
+        }
+        free(a);
+        free(b);
+        free(u);
+    }
+}
+
+/*
+ * Weight gradients of one expert e for a list of its intermediate units
+ * fs[0..nf): rows dW1[e][f][:] and dW3[e][f][:] into dw1, dw3 [nf][d], and
+ * columns dW2[e][:][f] into dw2 [d][nf].  The expert's kept slots are given
+ * as (token, gate) pairs in row order: tok [nrows], g [nrows].
+ */
+void oracle_backward_expert_units(int e, int nf, const int32_t *fs, int nrows, const int32_t *tok,
+                                  const double *g, int d, int d_ff, int dt, const void *x, const void *w1,
+                                  const void *w3, const void *w2, const double *dy, double *dw1, double *dw3,
+                                  double *dw2)
+{
+    const size_t wo = (size_t)e * d_ff * d, w2o = (size_t)e * d * d_ff;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int i = 0; i < nf; i++) {
+        const int f = fs[i];
+        double *r1 = dw1 + (size_t)i * d, *r3 = dw3 + (size_t)i * d;
+        for (int q = 0; q < d; q++) {
+            r1[q] = 0.0;
+            r3[q] = 0.0;
+            dw2[(size_t)q * nf + i] = 0.0;
+        }
+        for (int rr = 0; rr < nrows; rr++) {
+            const int t = tok[rr];
+            const double *dyt = dy + (size_t)t * d;
+            double a = 0.0, b = 0.0, u = 0.0;
+            for (int q = 0; q < d; q++) {
+                const double xv = elem(x, (size_t)t * d + q, dt);
+                a += xv * elem(w1, wo + (size_t)f * d + q, dt);
+                b += xv * elem(w3, wo + (size_t)f * d + q, dt);
+                u += dyt[q] * elem(w2, w2o + (size_t)q * d_ff + f, dt);
+            }
+            const double sg = logistic(a), silu = a * sg;
+            const double h = silu * b, dh = g[rr] * u;
+            const double da = dh * b * sg * (1.0 + a * (1.0 - sg)), db = dh * silu;
+            for (int q = 0; q < d; q++) {
+                const double xv = elem(x, (size_t)t * d + q, dt);
+                r1[q] += da * xv;
+                r3[q] += db * xv;
+                dw2[(size_t)q * nf + i] += g[rr] * dyt[q] * h;
+            }
+        }
+    }
+}
+
+/*
+ * Router weight and bias gradients: dW_r[e][:] = sum_t dlogits[t][e] x_t,
+ * dbias[e] = sum_t dlogits[t][e] (raw = x W_r^T + bias).  dlogits [T][E]
+ * double; dwr [E][d], dbias [E].
+ */
+void oracle_router_wgrad(int T, int d, int E, int dt, const void *x, const double *dlogits, double *dwr,
+                         double *dbias)
+{
+#pragma omp parallel for schedule(static)
+    for (int e = 0; e < E; e++) {
+        double *we = dwr + (size_t)e * d;
+        double sb = 0.0;
+        for (int q = 0; q < d; q++)
+            we[q] = 0.0;
+        for (int t = 0; t < T; t++) {
+            const double gl = dlogits[(size_t)t * E + e];
+            if (gl == 0.0)
+                continue;
+            sb += gl;
+            for (int q = 0; q < d; q++)
+                we[q] += gl * elem(x, (size_t)t * d + q, dt);
+        }
+        dbias[e] = sb;
+    }
+}

@@ -14,6 +14,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_backward as bwd
 from tests import test_oracle_pins as pins
 
 MUTATIONS = {
@@ -44,6 +45,22 @@ MUTATIONS = {
     "e4m3_no_nan": ("if (e == 15 && f == 7)\n        return NAN;", "if (0)\n        return NAN;"),
     "dequant_scale_by_column": ("(double)scale[r] * oracle_fp8", "(double)scale[c % rows] * oracle_fp8"),
     "double_elements_as_float": ("        return ((const double *)p)[i];", "        return (double)((const float *)p)[i];"),
+    # backward pass
+    "bwd_silu_derivative_first_term_only": ("const double da = dh * b[j] * sg * (1.0 + a[j] * (1.0 - sg));",
+                                            "const double da = dh * b[j] * sg;"),
+    "bwd_units_silu_derivative_first_term_only": ("const double da = dh * b * sg * (1.0 + a * (1.0 - sg)), db",
+                                                  "const double da = dh * b * sg, db"),
+    "bwd_softmax_mean_left_out": ("(dg[r] - mean) / tau;", "dg[r] / tau;"),
+    "bwd_temperature_left_out": ("(dg[r] - mean) / tau;", "(dg[r] - mean);"),
+    "bwd_expert_grad_ungated": ("const double dh = g * u[j];", "const double dh = u[j];"),
+    "bwd_db_times_b": ("const double db = dh * silu;", "const double db = dh * silu * b[j];"),
+    "bwd_w2_grad_ungated": ("dw2[(size_t)q * nf + i] += g[rr] * dyt[q] * h;", "dw2[(size_t)q * nf + i] += dyt[q] * h;"),
+    "bwd_router_input_term_left_out": ("dxt[q] += dlt[e] * elem(wr,", "dxt[q] += 0.0 * elem(wr,"),
+    "bwd_w1_w3_swapped_in_dx": ("da * elem(w1, wo + (size_t)j * d + q, dt) + db * elem(w3, wo + (size_t)j * d + q, dt)",
+                                "da * elem(w3, wo + (size_t)j * d + q, dt) + db * elem(w1, wo + (size_t)j * d + q, dt)"),
+    "bwd_bias_grad_left_out": ("            sb += gl;\n", ""),
+    "bwd_w2_transposed_in_u": ("su += dyt[q] * elem(w2, w2o + (size_t)q * d_ff + j, dt);",
+                               "su += dyt[q] * elem(w2, w2o + (size_t)j * d + q, dt);"),
 }
 
 # (name, check) pairs, run in this order by the child process below
@@ -58,6 +75,10 @@ CHECKS = [
     ("router_glu", pins.check_router_glu), ("fp8_decode", pins.check_fp8_decode),
     ("dynamic_capacity", pins.check_dynamic_capacity),
     ("dequant_rows", pins.check_dequant_rows), ("ffn_double_elements", pins.check_ffn_double_elements),
+    ("backward_autograd", bwd.check_backward_autograd),
+    ("backward_finite_differences", bwd.check_backward_finite_differences),
+    ("backward_invariants", bwd.check_backward_invariants),
+    ("backward_sampled_units", bwd.check_backward_sampled_units),
 ]
 
 
@@ -73,7 +94,7 @@ for name, chk in m.named_checks():
     try:
         chk(oracle)
         print("PASS", name, flush=True)
-    except (AssertionError, IndexError, ValueError) as exc:
+    except (AssertionError, IndexError, ValueError, RuntimeError) as exc:
         print("FAIL", name, flush=True)
 """
 
