@@ -309,6 +309,38 @@ int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, co
                     const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
                     moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
 
+/* Host-side, pure: bytes of workspace moe_backward needs; 0 if p is invalid. */
+size_t moe_backward_workspace_bytes(const moe_params *p);
+
+/*
+ * Backward pass (training) of a bf16 layer with the linear router, the
+ * routing of the forward pass held fixed.  The router is trained through
+ * the experts: its gradient flows back from the experts' outputs through
+ * the gates of the kept slots ("MoE架构揭秘" §3.3); the ranking, capacity,
+ * re-route and drop decisions are piecewise constant and pass no gradient.
+ * The balance loss counts top-k picks without gradient
+ * ("MoE稀疏激活原理与工程实践" §4.2) and contributes none; the penalty's
+ * load vector is an input without gradient.
+ *   Inputs: x [T][d], w_router [E][d], w1, w3 [E][d_ff][d], w2 [E][d][d_ff]
+ *   (bf16, as given to the forward pass); r: the routing the forward pass
+ *   wrote for this x (eid, row, gate, offsets, token_of_row are read); dy
+ *   [T][d] bf16, the gradient of the loss with respect to the layer output.
+ *   Outputs (fp32, every element written): dx [T][d]; dlogits [T][E], the
+ *   gradient with respect to the router logits (nonzero only at a token's
+ *   kept experts; each row sums to 0); dw_router [E][d]; dbias [E] (the
+ *   gradient of a per-expert router bias); dw1, dw3 [E][d_ff][d]; dw2
+ *   [E][d][d_ff].  An expert without rows gets zero weight gradients.
+ *   workspace: at least moe_backward_workspace_bytes(p) bytes, 256-B aligned.
+ * The a = x W1^T, b = x W3^T products are recomputed; the GEMMs run on bf16
+ * matrix cores with fp32 accumulation, the SwiGLU gradients and g * h being
+ * rounded to bf16 as their operands.  Deterministic (no atomics).  An fp32
+ * layer, the two-layer router or x of 2 GiB and more: MOE_ERR_UNSUPPORTED.
+ */
+int moe_backward(const moe_params *p, const void *x, const void *w_router, const void *w1, const void *w3,
+                 const void *w2, const moe_routing *r, const void *dy, float *dx, float *dlogits,
+                 float *dw_router, float *dbias, float *dw1, float *dw3, float *dw2, void *workspace,
+                 size_t ws_bytes, void *stream);
+
 /* Static description of a return code. */
 const char *moe_strerror(int code);
 

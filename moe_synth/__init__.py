@@ -35,7 +35,7 @@ MIX1 = 0xBF58476D1CE4E5B9
 MIX2 = 0x94D049BB133111EB
 
 # one substream per tensor
-TAGS = {"x": 1, "x_prev": 2, "w_router": 3, "bias": 4, "w1": 5, "w3": 6, "w2": 7}
+TAGS = {"x": 1, "x_prev": 2, "w_router": 3, "bias": 4, "w1": 5, "w3": 6, "w2": 7, "dy": 8}
 
 
 def _s64(v: int) -> int:
@@ -195,3 +195,10 @@ def quantize_rows_e4m3(w: torch.Tensor):
     s = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
     q = (wf / s[..., None]).to(torch.float8_e4m3fn).view(torch.uint8)
     return q.contiguous(), s.contiguous()
+
+
+def upstream_grad(cfg: MoEConfig, device="cpu", seed: int = 0, T: Optional[int] = None) -> torch.Tensor:
+    """Upstream gradient dy [T, d] of the layer output for the backward pass:
+    N(0, 1) in the layer's dtype, substream "dy"."""
+    T = cfg.T if T is None else T
+    return normal_tensor(seed, "dy", (T, cfg.d), 1.0, cfg.torch_dtype, device)

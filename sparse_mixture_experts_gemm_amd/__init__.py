@@ -77,10 +77,14 @@ def lib():
         L.moe_forward_events.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P,
                                          ctypes.POINTER(ctypes.c_void_p)]
         L.moe_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P]
+        L.moe_backward_workspace_bytes.argtypes = [PP]
+        L.moe_backward_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_backward.argtypes = [PP, P, P, P, P, P, PR, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
         L.moe_expert_ffn_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P]
         L.moe_forward_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P]
         for f in (L.moe_route, L.moe_dispatch, L.moe_expert_ffn, L.moe_combine, L.moe_forward,
-                  L.moe_forward_events, L.moe_forward_noalloc, L.moe_expert_ffn_fp8, L.moe_forward_fp8):
+                  L.moe_forward_events, L.moe_forward_noalloc, L.moe_expert_ffn_fp8, L.moe_forward_fp8,
+                  L.moe_backward):
             f.restype = ctypes.c_int
         L.moe_strerror.argtypes = [ctypes.c_int]
         L.moe_strerror.restype = ctypes.c_char_p
@@ -275,3 +279,36 @@ def alloc_workspace(p: Params, device="cuda", dispatch_only: bool = False, ffn_o
     """Workspace of moe_forward, or of moe_dispatch / moe_expert_ffn alone."""
     n = dispatch_workspace_bytes(p) if dispatch_only else ffn_workspace_bytes(p) if ffn_only else workspace_bytes(p)
     return torch.empty(max(n, 256), dtype=torch.uint8, device=device)
+
+
+def backward_workspace_bytes(p: Params) -> int:
+    return int(lib().moe_backward_workspace_bytes(ctypes.byref(p.c())))
+
+
+class Grads:
+    """fp32 gradient tensors of the backward pass (layouts as in include/moe.h)."""
+
+    NAMES = ("dx", "dlogits", "dw_router", "dbias", "dw1", "dw3", "dw2")
+
+    def __init__(self, p: Params, device="cuda"):
+        f32 = torch.float32
+        self.dx = torch.empty((p.T, p.d), dtype=f32, device=device)
+        self.dlogits = torch.empty((p.T, p.E), dtype=f32, device=device)
+        self.dw_router = torch.empty((p.E, p.d), dtype=f32, device=device)
+        self.dbias = torch.empty(p.E, dtype=f32, device=device)
+        self.dw1 = torch.empty((p.E, p.d_ff, p.d), dtype=f32, device=device)
+        self.dw3 = torch.empty((p.E, p.d_ff, p.d), dtype=f32, device=device)
+        self.dw2 = torch.empty((p.E, p.d, p.d_ff), dtype=f32, device=device)
+
+
+def backward(p: Params, x, w_router, w1, w3, w2, r: Routing, dy, g: Grads, workspace, stream=None):
+    """Gradients of the layer with the forward routing r held fixed (bf16 layers)."""
+    rc = lib().moe_backward(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(w1), _ptr(w3), _ptr(w2),
+                            ctypes.byref(r.c()), _ptr(dy), _ptr(g.dx), _ptr(g.dlogits), _ptr(g.dw_router),
+                            _ptr(g.dbias), _ptr(g.dw1), _ptr(g.dw3), _ptr(g.dw2), _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "moe_backward")
+
+
+def alloc_backward_workspace(p: Params, device="cuda") -> torch.Tensor:
+    return torch.empty(max(backward_workspace_bytes(p), 256), dtype=torch.uint8, device=device)

@@ -7,7 +7,7 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libmoe_hip.so")
-SOURCES = ["route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "expert_gemm.hip", "combine.hip", "backward.hip", "moe_api.cpp"]
 ARCH = os.environ.get("MOE_OFFLOAD_ARCH", "gfx950")
 # Packed-fp32 instructions are kept out of every kernel: the compiler's own
 # v_pk_* fp32 forms are disabled for the device pass.

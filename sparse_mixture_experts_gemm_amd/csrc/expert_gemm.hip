@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "grouped_tiles.h"
 #include "moe_internal.h"
 
 namespace moe {
@@ -50,127 +51,14 @@ constexpr int kTileBytes = kBM * kRowBytes;  // one operand tile (32 KiB)
 constexpr int kLoadsPerOperand = kTileBytes / 1024 / 4;  // 1 KiB wave loads per wave (8)
 constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (8)
 
-enum { kGateUp = 0, kDown = 1 };
+// kGateUpRaw: the gate-up GEMM storing its two products a = x W1^T and
+// b = x W3^T in fp32 instead of silu(a) * b (the backward pass needs them).
+enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2 };
 
-
-// Flat work index -> (expert, m range, n tile, K split).  Work items are
-// ordered expert, split, n tile, m tile (m fastest), so the m tiles that
-// share a weight tile are adjacent.
-struct TileInfo {
-    int e, m0, mend, nt, split;
-};
 
 template <typename T>
 __device__ __forceinline__ T *slice_ptr(const GemmOut &o, int split) {
     return split == 0 ? static_cast<T *>(o.y0) : static_cast<T *>(o.y_rest) + (size_t)(split - 1) * o.stride;
-}
-
-// Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).
-// The grid is sized by a bound on the work count; the real count comes from
-// the device-side offsets.  Each XCD is given an equal, contiguous range of
-// the real work items, so its L2 serves tiles that share operands and no
-// XCD is left with the empty tail of the grid.  Without claim counters the
-// block takes item (XCD b % 8, position b / 8).  With them (8 zeroed ints)
-// thread 0 claims the next item of its XCD's range with an atomic add, and
-// once that range is used up, the next item of another XCD's range: the
-// XCDs run at different speeds, and the ones that finish early take over
-// the others' last items.  Each item is claimed exactly once (the adds
-// return distinct values), and a block that finds every range used up has
-// nothing to do; the grid (at least the item count) always suffices.  The
-// claimed index passes through `slot` (one int of LDS that nothing else uses
-// until the second barrier).  Wave-parallel: lane l owns experts
-// 4l .. 4l+3 (E <= 256).  Returns false for blocks with no work (uniformly
-// over the block).
-__device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int ntiles_n,
-                                          int bm, int splits, int blk, int32_t *claim, int *slot,
-                                          TileInfo &ti) {
-    const int lane = lane_id();
-    const int e0 = lane * 4;
-    const int xcd = blk & 7, local = blk >> 3;
-    // The claim of this XCD's next item is issued first, so that its round
-    // trip overlaps the reads of the offsets (whether it is in range is
-    // known only once the item count is).  The counter's address goes
-    // through an opaque zero held in a VGPR: for an address it knows to be
-    // uniform the compiler combines the lanes' adds and waits for the result
-    // on the spot, which would serialise the two round trips again.
-    int first = 0;
-    if (claim && threadIdx.x == 0) {
-        int vzero;
-        asm volatile("v_mov_b32 %0, 0" : "=v"(vzero));
-        first = atomicAdd(claim + xcd + vzero, 1);
-    }
-    // offsets[e0 .. e0 + 4], clamped to offsets[E]: five independent loads
-    // in flight together (a load per expert under a branch each would wait
-    // for each one in turn)
-    int ofs[5];
-#pragma unroll
-    for (int j = 0; j < 5; j++) ofs[j] = offsets[min(e0 + j, E)];
-    int mts[4], c = 0;
-#pragma unroll
-    for (int j = 0; j < 4; j++) {
-        mts[j] = (ofs[j + 1] - ofs[j] + bm - 1) / bm;  // 0 past E (both ends clamp to E)
-        c += mts[j];
-    }
-    int incl = c;  // inclusive prefix of m tiles over lanes
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int v = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += v;
-    }
-    const int per = ntiles_n * splits;  // work items per m tile
-    const int total = __builtin_amdgcn_readlane(incl, 63) * per;
-    const int q = total >> 3, r = total & 7;
-    int L;
-    if (claim) {
-        if (threadIdx.x == 0) {
-            int item = -1;
-            for (int s = 0; s < 8; s++) {
-                const int y = (xcd + s) & 7;
-                const int i = s == 0 ? first : atomicAdd(&claim[y], 1);
-                if (i < q + (y < r ? 1 : 0)) {
-                    item = y * q + min(y, r) + i;
-                    break;
-                }
-            }
-            *slot = item;
-        }
-        __syncthreads();
-        L = __builtin_amdgcn_readfirstlane(*slot);
-        __syncthreads();  // every wave has read the slot before its LDS is reused
-        if (L < 0) return false;
-    } else {
-        if (local >= q + (xcd < r ? 1 : 0)) return false;
-        L = xcd * q + min(xcd, r) + local;
-    }
-    const int lo = (incl - c) * per, hi = incl * per;
-    const bool mine = L >= lo && L < hi;
-    int e_sel = 0, base_sel = 0;
-    if (mine) {
-        int b = lo;
-#pragma unroll
-        for (int j = 0; j < 4; j++) {
-            const int cnt = mts[j] * per;
-            if (L >= b && L < b + cnt) {
-                e_sel = e0 + j;
-                base_sel = b;
-            }
-            b += cnt;
-        }
-    }
-    const int owner = __builtin_ctzll(ballot64(mine));
-    const int e = __builtin_amdgcn_readlane(e_sel, owner);
-    const int base = __builtin_amdgcn_readlane(base_sel, owner);
-    const int beg = offsets[e], end = offsets[e + 1];
-    const int mt = (end - beg + bm - 1) / bm;
-    const int local_e = L - base;
-    const int per_split = mt * ntiles_n;
-    ti.e = e;
-    ti.split = local_e / per_split;
-    const int rem = local_e % per_split;
-    ti.nt = rem / mt;
-    ti.m0 = beg + (rem % mt) * bm;
-    ti.mend = end;
-    return true;
 }
 
 // silu(a) * b with the hardware exp and reciprocal (about 1 ulp each in
@@ -259,7 +147,7 @@ struct GemmThread {
 
 template <int MODE>
 __device__ __forceinline__ int b_imm(int jn) {
-    if (MODE == kGateUp) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * kRowBytes;
+    if (MODE != kDown) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * kRowBytes;
     return jn * 32 * kRowBytes;
 }
 
@@ -377,7 +265,7 @@ __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, c
 // before its use); two for the down GEMM, which has no registers to spare
 // for the addresses of a third.
 template <int MODE>
-__device__ __forceinline__ constexpr int b_buffers() { return MODE == kGateUp ? 3 : 2; }
+__device__ __forceinline__ constexpr int b_buffers() { return MODE != kDown ? 3 : 2; }
 
 // One K step (4 sub-steps of 16) on the A buffer `ca` and B buffer `cb`.
 // LDS holds two A buffers and NB B buffers (distinct objects, so the compiler
@@ -524,6 +412,34 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
             if (m < ti.mend)
                 *reinterpret_cast<uint4 *>(out_h + (size_t)m * N + cb + ((pc ^ (row & 7)) << 3)) = v;
         }
+    } else if (MODE == kGateUpRaw) {
+        // a (W1 part, blocks jn 0-1) and b (W3 part, jn 2-3) of the wave's 64
+        // columns, staged per 32-row block as 128 fp32 columns (a, then b)
+        // like the down projection's partials, then 16-byte stores to y0 (a)
+        // and y_rest (b), both [rows][N]
+        const int cb = n0 + wn * 64;
+#pragma unroll
+        for (int i = 0; i < NACT; i++) {
+#pragma unroll
+            for (int jn = 0; jn < 4; jn++)
+#pragma unroll
+                for (int q = 0; q < 16; q++) {
+                    const int row = 8 * (q >> 2) + 4 * hi + (q & 3);
+                    const int col = jn * 32 + l5;
+                    const int chunk = (col >> 2) ^ (((row >> 2) & 1) << 3);
+                    *reinterpret_cast<float *>(w + row * 512 + chunk * 16 + (col & 3) * 4) = acc[i][jn][q];
+                }
+#pragma unroll
+            for (int rd = 0; rd < 16; rd++) {
+                const int row = rd * 2 + (lane >> 5), pc = lane & 31;
+                const uint4 v = lds_read16(w + row * 512 + pc * 16);
+                const int m = ti.m0 + wm * 128 + i * 32 + row;
+                const int lc = (pc ^ (((row >> 2) & 1) << 3)) << 2;  // logical column 0..127
+                const int col = cb + (lc & 63);
+                float *dst = static_cast<float *>(lc < 64 ? out.y0 : out.y_rest);
+                if (m < ti.mend && col < N) *reinterpret_cast<uint4 *>(dst + (size_t)m * N + col) = v;
+            }
+        }
     } else {
         // one 32 x 128 fp32 block per pass through the wave's 16 KiB of LDS
         // (512-byte rows; the 16-byte chunks of rows 4..7 mod 8 XOR-swizzled by
@@ -636,7 +552,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     TileInfo ti;
     if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti))
         return;
-    const int n0 = MODE == kGateUp ? ti.nt * (kBN / 2) : ti.nt * kBN;
+    const int n0 = MODE != kDown ? ti.nt * (kBN / 2) : ti.nt * kBN;
     const size_t wexp = (size_t)ti.e * N * K;
     const int ks = K / splits;              // K elements of this split
     const int k_first = ti.split * ks;      // first K element of this split
@@ -652,7 +568,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
                       : make_rsrc(A + (size_t)ti.m0 * K, (uint32_t)(g.a_valid < kBM ? g.a_valid : kBM) * K * 2);
     const uint32_t w_bytes = (uint32_t)((size_t)N * K * 2);
     // gate-up: waves 0-1 load B rows 0..127 (W1), waves 2-3 rows 128..255 (W3)
-    g.b_rsrc = make_rsrc((MODE == kGateUp && wave >= 2 ? B1 : B0) + wexp, w_bytes);
+    g.b_rsrc = make_rsrc((MODE != kDown && wave >= 2 ? B1 : B0) + wexp, w_bytes);
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; j++) {
         const int grp = wave * kLoadsPerOperand + j;
@@ -661,13 +577,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         const int gm = min(ti.m0 + row, ti.mend - 1);
         const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
         g.a_off[j] = grp * kRowsPerLoad < g.a_valid ? ((uint32_t)ar * K + k_first + c * 8) * 2 : kPastEnd;
-        int gn = MODE == kGateUp ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
+        int gn = MODE != kDown ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
         gn = min(gn, N - 1);
         g.b_off[j] = ((uint32_t)gn * K + k_first + c * 8) * 2;
     }
     const int l5 = lane & 31, hi = lane >> 5;
     const int sw0 = swz(l5);  // swizzle of row base + l5 is sw0 ^ 4 * parity(base / 32)
-    const int b_rbase = MODE == kGateUp ? wn * 64 : wn * 128;
+    const int b_rbase = MODE != kDown ? wn * 64 : wn * 128;
 #pragma unroll
     for (int pp = 0; pp < 2; pp++)
 #pragma unroll
@@ -1260,7 +1176,7 @@ hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t 
     hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
                        static_cast<const uint16_t *>(x_perm), a_rows, w1, w3, s1, s3, offsets, E, dff, d, nt_up,
                        GemmOut{h, nullptr, 0, nullptr});
-    if (mid) hipEventRecord(mid, st);
+    if (mid && hipEventRecord(mid, st) != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(kSkThreads), 0, st,
                        static_cast<const uint16_t *>(h), (const int32_t *)nullptr, w2, w2, s2, s2, offsets, E, d,
                        dff, nt_dn, down);
@@ -1283,7 +1199,7 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         hipLaunchKernelGGL(grouped_gemm_skinny<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
                            static_cast<const uint16_t *>(x_perm), a_rows, static_cast<const uint16_t *>(w1),
                            static_cast<const uint16_t *>(w3), offsets, E, dff, d, nt_up, 1, up);
-        if (mid) hipEventRecord(mid, st);
+        if (mid && hipEventRecord(mid, st) != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL(grouped_gemm_skinny<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kSkThreads), 0, st,
                            static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2), offsets, E, d,
@@ -1302,7 +1218,7 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
                            0, st, static_cast<const uint16_t *>(x_perm), a_rows,
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
                            offsets, E, dff, d, nt_up, 1, (uint32_t)a_bytes, claim, up);
-        if (mid) hipEventRecord(mid, st);
+        if (mid && hipEventRecord(mid, st) != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
@@ -1316,12 +1232,27 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
                            static_cast<const float *>(x_perm), a_rows, static_cast<const float *>(w1),
                            static_cast<const float *>(w3), offsets, E, dff, d, nt_up,
                            static_cast<float *>(h));
-        if (mid) hipEventRecord(mid, st);
+        if (mid && hipEventRecord(mid, st) != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL(grouped_gemm_f32<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(256), 0, st,
                            static_cast<const float *>(h), (const int32_t *)nullptr, static_cast<const float *>(w2),
                            static_cast<const float *>(w2), offsets, E, d, dff, nt_dn,
                            static_cast<float *>(down.y0));
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_gate_up_raw(const moe_params &p, int64_t max_rows, int64_t cap, const void *x,
+                              const int32_t *a_rows, const int32_t *offsets, const void *w1, const void *w3,
+                              float *a, float *b, hipStream_t st) {
+    if (max_rows <= 0) return hipSuccess;
+    const int64_t a_bytes = a_rows ? (int64_t)p.T * p.d * 2 : 0;
+    if (p.dtype != MOE_BF16 || a_bytes >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const int64_t mt = mtile_bound(max_rows, cap, p.E, kBM);
+    const int nt_up = (int)ceil_div(p.d_ff, kBN / 2);
+    hipLaunchKernelGGL(grouped_gemm_bf16<kGateUpRaw>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads), 0, st,
+                       static_cast<const uint16_t *>(x), a_rows, static_cast<const uint16_t *>(w1),
+                       static_cast<const uint16_t *>(w3), offsets, p.E, p.d_ff, p.d, nt_up, 1, (uint32_t)a_bytes,
+                       (int32_t *)nullptr, GemmOut{a, b, 0, nullptr});
     return hipGetLastError();
 }
 

@@ -175,9 +175,83 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
     return f;
 }
 
+// Workspace layout of moe_backward.
+size_t backward_ws_bytes(const moe_params &p) {
+    const size_t R = (size_t)max_rows_of(p), F = (size_t)p.d_ff;
+    // da, db, hg: bf16 hi and lo parts, [2][R][d_ff] each
+    return 3 * align256(R * sizeof(float)) + 3 * align256(R * F * sizeof(float)) + 3 * align256(2 * R * F * 2) +
+           align256(R * p.d * sizeof(float));
+}
+
+void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
+    const size_t R = (size_t)max_rows_of(p), F = (size_t)p.d_ff;
+    char *c = static_cast<char *>(ws);
+    auto take = [&c](size_t n) {
+        char *q = c;
+        c += align256(n);
+        return q;
+    };
+    a.gate_of_row = reinterpret_cast<float *>(take(R * sizeof(float)));
+    a.ds_of_row = reinterpret_cast<float *>(take(R * sizeof(float)));
+    a.dg = reinterpret_cast<float *>(take(R * sizeof(float)));
+    a.a = reinterpret_cast<float *>(take(R * F * sizeof(float)));
+    a.b = reinterpret_cast<float *>(take(R * F * sizeof(float)));
+    a.u = reinterpret_cast<float *>(take(R * F * sizeof(float)));
+    a.da = reinterpret_cast<uint16_t *>(take(2 * R * F * 2));
+    a.db = reinterpret_cast<uint16_t *>(take(2 * R * F * 2));
+    a.hg = reinterpret_cast<uint16_t *>(take(2 * R * F * 2));
+    a.dx_perm = reinterpret_cast<float *>(take(R * p.d * sizeof(float)));
+}
+
 }  // namespace
 
 extern "C" {
+
+size_t moe_backward_workspace_bytes(const moe_params *p) {
+    if (check_params(p) != MOE_OK) return 0;
+    return backward_ws_bytes(*p);
+}
+
+int moe_backward(const moe_params *p, const void *x, const void *w_router, const void *w1, const void *w3,
+                 const void *w2, const moe_routing *r, const void *dy, float *dx, float *dlogits,
+                 float *dw_router, float *dbias, float *dw1, float *dw3, float *dw2, void *workspace,
+                 size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    if (p->dtype != MOE_BF16 || p->router_hidden != 0 || (int64_t)p->T * p->d * 2 >= ((int64_t)1 << 31))
+        return MOE_ERR_UNSUPPORTED;
+    const int64_t R = max_rows_of(*p);
+    if (!r || !r->offsets || !w_router || !w1 || !w3 || !w2 || !dw_router || !dbias || !dw1 || !dw3 || !dw2 ||
+        !workspace)
+        return MOE_ERR_INVALID_ARG;
+    if (p->T > 0 && (!x || !dy || !dx || !dlogits || !r->eid || !r->row || !r->gate || !r->token_of_row))
+        return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < backward_ws_bytes(*p)) return MOE_ERR_INVALID_ARG;
+    if (!aligned16(x) || !aligned16(w_router) || !aligned16(w1) || !aligned16(w3) || !aligned16(w2) ||
+        !aligned16(dy) || !aligned16(dx) || !aligned16(workspace))
+        return MOE_ERR_UNSUPPORTED;
+    BackwardArgs a{};
+    a.x = x;
+    a.w_router = w_router;
+    a.w1 = w1;
+    a.w3 = w3;
+    a.w2 = w2;
+    a.dy = dy;
+    a.eid = r->eid;
+    a.row = r->row;
+    a.offsets = r->offsets;
+    a.token_of_row = r->token_of_row;
+    a.gate = r->gate;
+    a.dx = dx;
+    a.dlogits = dlogits;
+    a.dw_router = dw_router;
+    a.dbias = dbias;
+    a.dw1 = dw1;
+    a.dw3 = dw3;
+    a.dw2 = dw2;
+    carve_backward(workspace, *p, a);
+    return hip_status(launch_backward(*p, R, capacity_of(*p), a, static_cast<hipStream_t>(stream)));
+}
 
 int64_t moe_capacity(const moe_params *p) {
     if (check_params(p) != MOE_OK) return -1;
@@ -298,22 +372,22 @@ int forward_impl(const moe_params *p, const void *x, const void *w_router, const
         return MOE_ERR_UNSUPPORTED;
     hipStream_t st = static_cast<hipStream_t>(stream);
     auto mark = [&](int i) {
-        if (events && events[i]) hipEventRecord(static_cast<hipEvent_t>(events[i]), st);
+        return !(events && events[i]) || hipEventRecord(static_cast<hipEvent_t>(events[i]), st) == hipSuccess;
     };
     const ForwardWs f = carve_forward(workspace, *p);
     const int64_t C = capacity_of(*p);
     const int64_t R = max_rows_of(*p);
     const int S = splits_of(*p);
-    mark(0);
+    if (!mark(0)) return MOE_ERR_HIP;
     hipError_t e = launch_route(*p, x, w_router, bias, load, logits, r->cand, r->cand_score, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(1);
+    if (!mark(1)) return MOE_ERR_HIP;
     DispatchScratch ds = carve_dispatch(f.dispatch, p->T, p->E, p->k);
     ds.claim = f.claim;  // zeroed by the dispatch, used by the expert GEMM
     ds.gate_of_row = f.gate_of_row;
     e = launch_dispatch(*p, C, x, *r, f.x_perm, ds, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(2);
+    if (!mark(2)) return MOE_ERR_HIP;
     // bf16: the down projection folds each row's gate in and stores fp16
     // slices; fp32: y_perm [R][d] in fp32, gates applied by the combine
     const size_t stride = (size_t)R * p->d;
@@ -326,13 +400,13 @@ int forward_impl(const moe_params *p, const void *x, const void *w_router, const
     else
         e = launch_ffn(*p, R, C, x, r->token_of_row, r->offsets, w, f.h, down, f.claim, mid, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(4);
+    if (!mark(4)) return MOE_ERR_HIP;
     if (p->dtype == MOE_BF16)
         e = launch_combine_gated(*p, R, S, static_cast<const uint16_t *>(f.y), r->row, y, st);
     else
         e = launch_combine(*p, R, static_cast<const float *>(f.y), r->row, r->gate, y, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
-    mark(5);
+    if (!mark(5)) return MOE_ERR_HIP;
     return MOE_OK;
 }
 

@@ -115,6 +115,28 @@ hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t 
                                  const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
                                  const GemmOut &down, hipEvent_t mid, hipStream_t st);
 
+// The gate-up GEMM storing its two products a = x W1^T and b = x W3^T
+// (fp32 [R][d_ff] each) for the kept rows; rows read from x through a_rows
+// (token_of_row; x below 2 GiB).
+hipError_t launch_gate_up_raw(const moe_params &p, int64_t max_rows, int64_t cap, const void *x,
+                              const int32_t *a_rows, const int32_t *offsets, const void *w1, const void *w3,
+                              float *a, float *b, hipStream_t st);
+
+// Backward pass of a bf16 layer: inputs, the forward's routing, gradients
+// (fp32) and the workspace buffers.
+struct BackwardArgs {
+    const void *x, *w_router, *w1, *w3, *w2, *dy;
+    const int32_t *eid, *row, *offsets, *token_of_row;
+    const float *gate;
+    float *dx, *dlogits, *dw_router, *dbias, *dw1, *dw3, *dw2;
+    float *gate_of_row, *ds_of_row, *dg;  // [R]
+    float *a, *b, *u;                     // [R][d_ff]
+    uint16_t *da, *db, *hg;               // [2][R][d_ff] bf16: hi parts, then lo parts
+    float *dx_perm;                       // [R][d]
+};
+hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, const BackwardArgs &a,
+                           hipStream_t st);
+
 // y[t] = sum over kept slots j of gate[t][j] * y_perm[row[t][j]], y_perm
 // [R][d] fp32; zeros everywhere when max_rows is 0 (y_perm is then not read).
 hipError_t launch_combine(const moe_params &p, int64_t max_rows, const float *y_perm, const int32_t *row,
