@@ -37,6 +37,8 @@ def parse():
                     help="skip the step-time distribution, cold-cache steps and amd-smi sampling "
                          "(for runs under a profiler)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work of the oracle sample")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the timing of moe_backward (the training pass) after the forward pass")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="first run one plain 1 GiB device copy (reference for byte counters)")
     return ap.parse_args()
@@ -271,6 +273,10 @@ def main():
                     "frac": tf / PEAK_MFMA_TFLOPS, "traffic": traffic.get("expert_ffn"),
                     "per_launch_work": f"{work['gemm_flops']:.4g} flop ({rows} kept rows x 6 x d x d_ff)"}
 
+    backward = None
+    if not args.no_backward and not fp8 and p.dtype == moe.MOE_BF16:
+        backward = bench_backward(moe, moe_synth, torch, np, p, cfg, L, r, rows, dev, max(5, args.steps // 2))
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, L, load, args.cpu_seconds, fp8)
@@ -290,6 +296,7 @@ def main():
         "mfma_util_pct": (100.0 * roofline["frac"]) if roofline["bound"] == "mfma" else None,
         "stages": stages,
         "roofline": roofline,
+        "backward": backward,
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
         "step_ms": step_ms,
@@ -297,6 +304,40 @@ def main():
         "gpu_state": gpu_state,
     }
     print(json.dumps(out))
+
+
+def bench_backward(moe, moe_synth, torch, np, p, cfg, L, r, rows, dev, n):
+    """moe_backward on the forward's routing with a seeded upstream gradient:
+    mean time of n steps (events on the launch stream, after 2 warm-up steps).
+    Algorithmic work: the three expert gradients (u = W2^T dy, dx_perm, dW1,
+    dW3, dW2: 12 rows d d_ff flop); the recomputed gate-up products (4 rows
+    d d_ff) are reported apart."""
+    dy = moe_synth.upstream_grad(cfg, dev)
+    gr = moe.Grads(p, dev)
+    wsb = moe.alloc_backward_workspace(p, dev)
+
+    def bstep():
+        moe.backward(p, L["x"], L["w_router"], L["w1"], L["w3"], L["w2"], r, dy, gr, wsb)
+
+    for _ in range(2):
+        bstep()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(n):
+        bstep()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / n
+    flops = 12.0 * rows * cfg.d * cfg.d_ff
+    tf = flops / (ms * 1e-3) / 1e12
+    out = {"ms_per_step": ms, "steps": n, "algorithmic_flop": flops, "TFLOP/s": tf, "mfma_frac": tf / PEAK_MFMA_TFLOPS,
+           "recompute_flop": 4.0 * rows * cfg.d * cfg.d_ff,
+           "tokens_per_s": cfg.T / (ms * 1e-3),
+           "note": "moe_backward: fp32 gradients of x, router logits, W_r, bias, W1, W3, W2; routing held fixed"}
+    del gr, wsb
+    torch.cuda.empty_cache()
+    return out
 
 
 def step_times(step, n, torch, before=None):
