@@ -112,10 +112,12 @@ typedef struct moe_params {
      * MOE_ERR_INVALID_ARG. */
     float top2_gap;
     /* router network: 0 is the linear router (w_router [E][d]); H > 0 is the
-     * two-layer router of "MoE稀疏激活原理与工程实践" §3.1, second step,
-     * raw = silu(x . W1^T) . W2^T + bias with H hidden units (2E on the page),
-     * w_router then holding W1 [H][d] followed by W2 [E][H].  Supported for
-     * bf16 with E <= 64 and H <= 64 (MOE_ERR_UNSUPPORTED otherwise); a
+     * two-layer router of "MoE稀疏激活原理与工程实践" §3.1, second step, and
+     * of its §4.2 code (Linear(d, 2E) -> SiLU -> Linear(2E, E)),
+     * raw = silu(x . W1^T + b1) . W2^T + b2 with H hidden units (2E on the
+     * page): w_router then holds W1 [H][d] followed by W2 [E][H], and the
+     * bias argument of moe_route / moe_forward (when not NULL) holds b1 [H]
+     * followed by b2 [E].  1 <= H <= 256 (MOE_ERR_UNSUPPORTED above); a
      * negative value is MOE_ERR_INVALID_ARG. */
     int32_t router_hidden;
     /* 1: the capacity factor grows with the batch, cf = 1 + 0.01 * log2(T)
@@ -179,8 +181,9 @@ size_t moe_workspace_bytes(const moe_params *p);
  * (or raw when load is NULL), then the K1 best experts by (s desc, e asc)
  * ("MoE架构揭秘" §3.1: softmax then top-k; softmax is monotone, so the ranking
  * is taken on s).
- *   x [T][d], w_router [E][d] (dtype); bias [E] fp32 or NULL; load [E] fp32 or
- *   NULL.  Writes logits [T][E] (raw, fp32), r->cand and r->cand_score.
+ *   x [T][d], w_router [E][d] (dtype); bias [E] fp32 or NULL ([H + E] for
+ *   the two-layer router); load [E] fp32 or NULL.  Writes logits [T][E]
+ *   (raw, fp32), r->cand and r->cand_score.
  */
 int moe_route(const moe_params *p, const void *x, const void *w_router, const float *bias,
               const float *load, float *logits, moe_routing *r, void *stream);
@@ -308,6 +311,30 @@ int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, co
                     const float *load, const uint8_t *w1, const float *s1, const uint8_t *w3,
                     const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
                     moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
+
+/* Host-side, pure: bytes of workspace moe_load_window needs for a window
+ * of `window` tokens; 0 if p is invalid or window < 1. */
+size_t moe_load_window_workspace_bytes(const moe_params *p, int32_t window);
+
+/*
+ * Windowed load statistic ("企业官网建设流程全解析" page §2: an expert's load
+ * is its selection frequency over a sliding window of the most recent
+ * tokens, 1024 on the page, with a decay factor, 0.99 on the page, so that
+ * it follows the current load).  The T tokens of the batch fall, in token
+ * order, into consecutive windows of `window` tokens (the last may be
+ * shorter); each window updates the statistic once:
+ *   load[e] <- decay * load[e] + (1 - decay) * f[e],
+ *   f[e] = (selections of e in the window) / (k * tokens in the window),
+ * a selection being one of a token's ranks 0..k-1 in cand (the router's
+ * top-k choices before the capacity cap; an entry outside [0, E) selects
+ * nothing).  Computed in double, windows in order, load rounded to fp32
+ * once.  cand [T][k+1] as moe_route writes it; load [E] fp32 (device), read
+ * and overwritten, e.g. the `load` of the next batch's penalty.  decay in
+ * [0, 1]; window >= 1.  workspace: moe_load_window_workspace_bytes(p,
+ * window) bytes, 256-B aligned.  T = 0 leaves load unchanged.
+ */
+int moe_load_window(const moe_params *p, const int32_t *cand, int32_t window, float decay, float *load,
+                    void *workspace, size_t ws_bytes, void *stream);
 
 /* Host-side, pure: bytes of workspace moe_backward needs; 0 if p is invalid. */
 size_t moe_backward_workspace_bytes(const moe_params *p);

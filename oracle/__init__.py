@@ -50,7 +50,7 @@ def lib():
         L.oracle_scores.argtypes = [i32, i32, P, P, f32, P]
         L.oracle_topk.argtypes = [i32, i32, i32, P, P, P]
         L.oracle_gap_swap.argtypes = [i32, i32, f32, P, P]
-        L.oracle_router_logits_glu.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P]
+        L.oracle_router_logits_glu.argtypes = [i32, i32, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_dispatch.argtypes = [i32, i32, i32, i64, i32, f32, ctypes.c_double, P, P] + [P] * 12
         L.oracle_ffn_rows.argtypes = [i32, P, P, i32, i32, i32, P, P, P, P, P, P]
         L.oracle_layer_tokens.argtypes = [i32, P, i32, i32, i32, i32, P, P, P, P, P, P, P]
@@ -64,6 +64,8 @@ def lib():
         L.oracle_backward_tokens.argtypes = [i32, P, i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, P, P, P, P]
         L.oracle_backward_expert_units.argtypes = [i32, i32, P, i32, P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.oracle_router_wgrad.argtypes = [i32, i32, i32, i32, P, P, P, P]
+        L.oracle_load_window.argtypes = [i32, i32, i32, i32, P, i32, f64, P]
+        L.oracle_load_window.restype = None
         for f in (L.oracle_backward_tokens, L.oracle_backward_expert_units, L.oracle_router_wgrad):
             f.restype = None
         for f in (L.oracle_router_logits, L.oracle_router_logits_glu, L.oracle_scores, L.oracle_topk, L.oracle_gap_swap, L.oracle_dispatch,
@@ -135,16 +137,19 @@ def router_logits(x, wr, bias=None) -> np.ndarray:
     return raw
 
 
-def router_logits_glu(x, w1, w2, bias=None) -> np.ndarray:
-    """Two-layer router: raw = silu(x W1^T) W2^T + bias, W1 [H][d], W2 [E][H]."""
+def router_logits_glu(x, w1, w2, bias=None, bias1=None) -> np.ndarray:
+    """Two-layer router: raw = silu(x W1^T + bias1) W2^T + bias, W1 [H][d],
+    W2 [E][H], bias1 [H] and bias [E] (either may be None)."""
     x, w1, w2 = _np(x), _np(w1), _np(w2)
-    bias = None if bias is None else _np(bias).astype(np.float32)
+    bias = None if bias is None else np.ascontiguousarray(_np(bias), dtype=np.float32)
+    bias1 = None if bias1 is None else np.ascontiguousarray(_np(bias1), dtype=np.float32)
     T, d = x.shape
     H = w1.shape[0]
     E = w2.shape[0]
     assert w1.shape == (H, d) and w2.shape == (E, H) and x.dtype == w1.dtype == w2.dtype
+    assert bias1 is None or bias1.shape == (H,)
     raw = np.empty((T, E), np.float32)
-    lib().oracle_router_logits_glu(T, d, E, H, _dt(x), _p(x), _p(w1), _p(w2), _p(bias), _p(raw))
+    lib().oracle_router_logits_glu(T, d, E, H, _dt(x), _p(x), _p(w1), _p(w2), _p(bias1), _p(bias), _p(raw))
     return raw
 
 
@@ -366,3 +371,15 @@ def backward(x, wr, w1, w3, w2, eid, row, gate64, dy, tau: float = 1.0) -> dict:
         tok, g = expert_slots(eid, row, gate64, e)
         dw1[e], dw3[e], dw2[e] = backward_expert_units(e, fs, tok, g, x, w1, w3, w2, dy)
     return dict(dlogits=dl, dx=dx, dwr=dwr, dbias=dbias, dw1=dw1, dw3=dw3, dw2=dw2)
+
+
+def load_window(cand, E: int, k: int, load, window: int = 1024, alpha: float = 0.99) -> np.ndarray:
+    """Windowed load statistic: per window of `window` tokens (token order),
+    load = alpha * load + (1 - alpha) * (the window's top-k selection
+    frequency per expert).  Returns the updated fp32 [E] vector."""
+    cand = np.ascontiguousarray(_np(cand), dtype=np.int32)
+    T, K1 = cand.shape
+    out = np.array(_np(load), dtype=np.float32, copy=True)
+    assert out.shape == (E,) and k < K1 + 1
+    lib().oracle_load_window(T, E, k, K1, _p(cand), int(window), float(alpha), _p(out))
+    return out

@@ -164,14 +164,18 @@ void oracle_router_logits(int T, int d, int E, int dt, const void *x, const void
 /*
  * Two-layer router ("MoE稀疏激活原理与工程实践" §3.1, second step: a gated
  * linear unit W1 x -> silu -> W2 instead of one linear map; W1 is
- * d x (2E), W2 (2E) x E, and W2's outputs are the expert scores):
- *   a[t][j]   = silu(sum_i x[t][i] * W1[j][i]),  j < H,  silu(v) = v / (1 + e^-v)
+ * d x (2E), W2 (2E) x E, and W2's outputs are the expert scores; the
+ * router of the page's MoELayer code (§4.2) is Linear(d, 2E) -> SiLU ->
+ * Linear(2E, E), both linear maps with a bias):
+ *   a[t][j]   = silu(sum_i x[t][i] * W1[j][i] + bias1[j]),  j < H,
+ *               silu(v) = v / (1 + e^-v)
  *   raw[t][e] = fp32(sum_j a[t][j] * W2[e][j]) + bias[e]
  * in double up to the one fp32 rounding.  W1 is stored [H][d], W2 [E][H],
- * both of element type dt (H is the hidden width, 2E on the page).
+ * both of element type dt (H is the hidden width, 2E on the page); bias1
+ * [H] and bias [E] are fp32 or NULL.
  */
 void oracle_router_logits_glu(int T, int d, int E, int H, int dt, const void *x, const void *w1,
-                              const void *w2, const float *bias, float *raw)
+                              const void *w2, const float *bias1, const float *bias, float *raw)
 {
     double *a = (double *)malloc((size_t)H * sizeof(double));
     for (int t = 0; t < T; t++) {
@@ -179,6 +183,8 @@ void oracle_router_logits_glu(int T, int d, int E, int H, int dt, const void *x,
             double acc = 0.0;
             for (int i = 0; i < d; i++)
                 acc += elem(x, (size_t)t * d + i, dt) * elem(w1, (size_t)j * d + i, dt);
+            if (bias1)
+                acc += bias1[j];
             a[j] = acc / (1.0 + exp(-acc));
         }
         for (int e = 0; e < E; e++) {
@@ -732,4 +738,43 @@ void oracle_router_wgrad(int T, int d, int E, int dt, const void *x, const doubl
         }
         dbias[e] = sb;
     }
+}
+
+/*
+ * Windowed load statistic (P5 §2, first constraint: an expert's load is its
+ * selection frequency over a sliding window of the most recent tokens, for
+ * example 1024, with a decay factor alpha = 0.99 so that the statistic
+ * follows the current load).  Reading: the T tokens of a batch fall, in
+ * token order, into consecutive windows of W tokens (the last one may be
+ * shorter); each window updates the statistic once,
+ *   load[e] <- alpha * load[e] + (1 - alpha) * f[e],
+ *   f[e] = (selections of e in the window) / (k * tokens in the window),
+ * a selection being one of a token's ranks 0..k-1 in its candidate list
+ * (the router's top-k choices, before the capacity cap); entries outside
+ * [0, E) select nothing.  In double, windows in order; load is fp32 in and
+ * out, rounded once at the end.  cand is [T][K1].
+ */
+void oracle_load_window(int T, int E, int k, int K1, const int32_t *cand, int window, double alpha, float *load)
+{
+    double *l = (double *)malloc((size_t)E * sizeof(double));
+    long *cnt = (long *)malloc((size_t)E * sizeof(long));
+    for (int e = 0; e < E; e++)
+        l[e] = load[e];
+    for (int t0 = 0; t0 < T; t0 += window) {
+        const int n = T - t0 < window ? T - t0 : window;
+        for (int e = 0; e < E; e++)
+            cnt[e] = 0;
+        for (int t = t0; t < t0 + n; t++)
+            for (int r = 0; r < k; r++) {
+                const int c = cand[(size_t)t * K1 + r];
+                if (c >= 0 && c < E)
+                    cnt[c]++;
+            }
+        for (int e = 0; e < E; e++)
+            l[e] = alpha * l[e] + (1.0 - alpha) * ((double)cnt[e] / ((double)k * n));
+    }
+    for (int e = 0; e < E; e++)
+        load[e] = (float)l[e];
+    free(l);
+    free(cnt);
 }

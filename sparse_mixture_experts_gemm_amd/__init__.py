@@ -77,6 +77,10 @@ def lib():
         L.moe_forward_events.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P,
                                          ctypes.POINTER(ctypes.c_void_p)]
         L.moe_forward_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, PR, P]
+        L.moe_load_window_workspace_bytes.argtypes = [PP, ctypes.c_int32]
+        L.moe_load_window_workspace_bytes.restype = ctypes.c_size_t
+        L.moe_load_window.argtypes = [PP, P, ctypes.c_int32, ctypes.c_float, P, P, ctypes.c_size_t, P]
+        L.moe_load_window.restype = ctypes.c_int
         L.moe_backward_workspace_bytes.argtypes = [PP]
         L.moe_backward_workspace_bytes.restype = ctypes.c_size_t
         L.moe_backward.argtypes = [PP, P, P, P, P, P, PR, P, P, P, P, P, P, P, P, P, ctypes.c_size_t, P]
@@ -312,3 +316,17 @@ def backward(p: Params, x, w_router, w1, w3, w2, r: Routing, dy, g: Grads, works
 
 def alloc_backward_workspace(p: Params, device="cuda") -> torch.Tensor:
     return torch.empty(max(backward_workspace_bytes(p), 256), dtype=torch.uint8, device=device)
+
+
+def load_window_workspace_bytes(p: Params, window: int) -> int:
+    return int(lib().moe_load_window_workspace_bytes(ctypes.byref(p.c()), int(window)))
+
+
+def load_window(p: Params, cand, window: int, decay: float, load, workspace=None, stream=None):
+    """Windowed load statistic: updates the fp32 [E] tensor `load` in place from the router's cand."""
+    if workspace is None:
+        workspace = torch.empty(max(load_window_workspace_bytes(p, window), 256), dtype=torch.uint8,
+                                device=load.device)
+    rc = lib().moe_load_window(ctypes.byref(p.c()), _ptr(cand), int(window), float(decay), _ptr(load),
+                               _ptr(workspace), workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "moe_load_window")

@@ -400,7 +400,56 @@ __global__ __launch_bounds__(256) void dispatch_gather(const uint4 *__restrict__
     }
 }
 
+// Windowed load statistic ("企业官网建设流程全解析" page §2: an expert's
+// selection frequency over a sliding window of recent tokens, with a decay
+// factor).  Block w counts the top-k selections (ranks 0..k-1 of the
+// candidate lists; entries outside [0, E) select nothing) of tokens
+// [w W, min(T, (w+1) W)); integer LDS counts, so the result does not depend
+// on the order of the adds.
+__global__ __launch_bounds__(256) void load_window_counts(const int32_t *__restrict__ cand, int T, int E, int k,
+                                                          int K1, int window, int32_t *__restrict__ counts) {
+    __shared__ int c[kMaxExperts];
+    for (int e = threadIdx.x; e < E; e += 256) c[e] = 0;
+    __syncthreads();
+    const int64_t t0 = (int64_t)blockIdx.x * window, t1 = min((int64_t)T, t0 + window);
+    for (int64_t i = t0 * k + threadIdx.x; i < t1 * k; i += 256) {
+        const int64_t t = i / k;
+        const int ex = valid_expert(cand[t * K1 + (i - t * k)], E);
+        if (ex >= 0) atomicAdd(&c[ex], 1);
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += 256) counts[(size_t)blockIdx.x * E + e] = c[e];
+}
+
+// load[e] <- alpha load[e] + (1 - alpha) f_w[e] for the windows in order, in
+// double (f_w the window's selections over k x its tokens), one thread per
+// expert, rounded to fp32 once.  No contraction into fused multiply-adds:
+// each operation rounds as written.
+__global__ __launch_bounds__(256) void load_window_update(const int32_t *__restrict__ counts, int nw, int T, int E,
+                                                          int k, int window, double alpha, float *__restrict__ load) {
+#pragma clang fp contract(off)
+    const int e = blockIdx.x * 256 + threadIdx.x;
+    if (e >= E) return;
+    double l = load[e];
+    for (int w = 0; w < nw; w++) {
+        const int n = (int)min((int64_t)window, (int64_t)T - (int64_t)w * window);
+        const double f = (double)counts[(size_t)w * E + e] / ((double)k * (double)n);
+        l = alpha * l + (1.0 - alpha) * f;
+    }
+    load[e] = (float)l;
+}
+
 }  // namespace
+
+hipError_t launch_load_window(const moe_params &p, const int32_t *cand, int window, float decay, float *load,
+                              int32_t *counts, hipStream_t st) {
+    if (p.T == 0) return hipSuccess;
+    const int nw = (int)ceil_div(p.T, window);
+    hipLaunchKernelGGL(load_window_counts, dim3(nw), dim3(256), 0, st, cand, p.T, p.E, p.k, p.k + 1, window, counts);
+    hipLaunchKernelGGL(load_window_update, dim3((unsigned)ceil_div(p.E, 256)), dim3(256), 0, st, counts, nw, p.T,
+                       p.E, p.k, window, (double)decay, load);
+    return hipGetLastError();
+}
 
 hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
                            void *x_perm, const DispatchScratch &ws, hipStream_t st) {

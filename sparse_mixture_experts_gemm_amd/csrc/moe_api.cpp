@@ -59,8 +59,7 @@ int check_params(const moe_params *p) {
     if (!(p->top2_gap >= 0.0f) || isinf(p->top2_gap)) return MOE_ERR_INVALID_ARG;
     if (p->router_hidden < 0) return MOE_ERR_INVALID_ARG;
     if (p->dynamic_capacity != 0 && p->dynamic_capacity != 1) return MOE_ERR_INVALID_ARG;
-    if (p->router_hidden > 0 && (p->dtype != MOE_BF16 || p->E > 64 || p->router_hidden > 64))
-        return MOE_ERR_UNSUPPORTED;
+    if (p->router_hidden > kMaxExperts) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -206,6 +205,23 @@ void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
 }  // namespace
 
 extern "C" {
+
+size_t moe_load_window_workspace_bytes(const moe_params *p, int32_t window) {
+    if (check_params(p) != MOE_OK || window < 1) return 0;
+    return align256(sizeof(int32_t) * (size_t)ceil_div(p->T > 0 ? p->T : 1, window) * p->E);
+}
+
+int moe_load_window(const moe_params *p, const int32_t *cand, int32_t window, float decay, float *load,
+                    void *workspace, size_t ws_bytes, void *stream) {
+    int rc = check_params(p);
+    if (rc != MOE_OK) return rc;
+    if (window < 1 || !(decay >= 0.0f && decay <= 1.0f) || !load || !workspace || (p->T > 0 && !cand))
+        return MOE_ERR_INVALID_ARG;
+    if (ws_bytes < moe_load_window_workspace_bytes(p, window)) return MOE_ERR_INVALID_ARG;
+    if (!aligned4(load) || !aligned16(workspace)) return MOE_ERR_UNSUPPORTED;
+    return hip_status(launch_load_window(*p, cand, window, decay, load, static_cast<int32_t *>(workspace),
+                                         static_cast<hipStream_t>(stream)));
+}
 
 size_t moe_backward_workspace_bytes(const moe_params *p) {
     if (check_params(p) != MOE_OK) return 0;

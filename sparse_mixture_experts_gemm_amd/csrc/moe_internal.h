@@ -56,6 +56,10 @@ hipError_t launch_route(const moe_params &p, const void *x, const void *wr, cons
 hipError_t launch_dispatch(const moe_params &p, int64_t C, const void *x, const moe_routing &r,
                            void *x_perm, const DispatchScratch &ws, hipStream_t st);
 
+// Windowed load statistic: counts [ceil(T/window)][E] int32 scratch.
+hipError_t launch_load_window(const moe_params &p, const int32_t *cand, int window, float decay, float *load,
+                              int32_t *counts, hipStream_t st);
+
 // Capacity C = min(T, ceil(T*k/E * cf)) evaluated in double, cf the
 // capacity_factor, or 1 + 0.01 * log2(T) with dynamic_capacity; a
 // capacity_factor <= 0 (without dynamic_capacity) means uncapped (C = T).

@@ -49,12 +49,14 @@ struct ChunkDot<uint16_t> {
         acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w), __builtin_bit_cast(bf16x2_t, b.w), acc, false);
         return acc;
     }
+    __device__ static __forceinline__ float widen(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 };
 
 // 16-byte chunk = 4 fp32
 template <>
 struct ChunkDot<float> {
     static constexpr int kVec = 4;
+    __device__ static __forceinline__ float widen(float v) { return v; }
     __device__ static __forceinline__ float dot(uint4 a, uint4 b, float acc) {
         acc = __builtin_fmaf(__uint_as_float(a.x), __uint_as_float(b.x), acc);
         acc = __builtin_fmaf(__uint_as_float(a.y), __uint_as_float(b.y), acc);
@@ -260,10 +262,16 @@ __device__ __forceinline__ void route_chunk(const uint4 *w_lds, const uint4 (&xr
 // streams in while the current one is used); EA: experts per reduce-scatter
 // group; EMAX: bound on E that sizes the logit buffer (a small one leaves
 // room for two blocks per CU) and the experts per lane of the ranking.
+// H > 0: the two-layer router.  wr holds W1 [H][d] followed by W2 [E][H];
+// bias (or NULL) holds the H first-layer biases, then the E second-layer
+// ones.  The dot loop computes the H hidden pre-activations (as it computes
+// the E logits of the linear router); silu and the second layer follow,
+// with W2 staged transposed in LDS in chunks of hidden units (fp32, hidden
+// units in ascending order).  H <= EMAX.
 template <typename TIn, int NX, int TPW, int NB, int EA, int EMAX>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const TIn *__restrict__ x, const TIn *__restrict__ wr, const float *__restrict__ bias,
-    const float *__restrict__ load, float neg_lambda, float gap, int T, int d, int E, int K1, int EC,
+    const float *__restrict__ load, float neg_lambda, float gap, int T, int d, int E, int K1, int EC, int H,
     float *__restrict__ logits, int32_t *__restrict__ cand, float *__restrict__ cand_score) {
     constexpr int kVec = ChunkDot<TIn>::kVec;
     // two distinct objects, so the compiler sees that the loads into one
@@ -277,7 +285,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     const int nchunk = d / kVec;
     const int row_bytes = d * (int)sizeof(TIn);
     const int t0 = (blockIdx.x * kRouteWaves + wave) * TPW;
-    float *lg = lg_all + wave * TPW * E;  // [TPW][E]
+    const int NO = H > 0 ? H : E;         // outputs of the dot loop
+    float *lg = lg_all + wave * TPW * EMAX;  // [TPW][NO], then [TPW][E]
 
     // this wave's x rows, 16-byte chunks lane + 64 c (zero past the row end)
     uint4 xr[TPW][NX];
@@ -295,26 +304,75 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(
     }
 
     const char *wsrc = reinterpret_cast<const char *>(wr);
-    stage_w(wsrc, min(EC, E) * row_bytes, w_buf0, wave, lane);
+    stage_w(wsrc, min(EC, NO) * row_bytes, w_buf0, wave, lane);
     __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     __syncthreads();
-    // chunks of EC experts, alternating buffers (unrolled by two so each
-    // use names a fixed buffer); the next chunk streams in during the use
-    for (int e0 = 0; e0 < E; e0 += 2 * EC) {
-        if (NB == 2 && e0 + EC < E)
-            stage_w(wsrc + (size_t)(e0 + EC) * row_bytes, min(EC, E - e0 - EC) * row_bytes, w_buf1, wave, lane);
-        route_chunk<TIn, NX, TPW, EA>(reinterpret_cast<const uint4 *>(w_buf0), xr, nchunk, e0, min(EC, E - e0), bias,
-                                  lg, E, lane);
+    // chunks of EC experts (hidden units), alternating buffers (unrolled by
+    // two so each use names a fixed buffer); the next chunk streams in
+    // during the use
+    for (int e0 = 0; e0 < NO; e0 += 2 * EC) {
+        if (NB == 2 && e0 + EC < NO)
+            stage_w(wsrc + (size_t)(e0 + EC) * row_bytes, min(EC, NO - e0 - EC) * row_bytes, w_buf1, wave, lane);
+        route_chunk<TIn, NX, TPW, EA>(reinterpret_cast<const uint4 *>(w_buf0), xr, nchunk, e0, min(EC, NO - e0),
+                                  bias, lg, NO, lane);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
-        if (NB == 1 || e0 + EC >= E) break;
-        if (e0 + 2 * EC < E)
-            stage_w(wsrc + (size_t)(e0 + 2 * EC) * row_bytes, min(EC, E - e0 - 2 * EC) * row_bytes, w_buf0,
+        if (NB == 1 || e0 + EC >= NO) break;
+        if (e0 + 2 * EC < NO)
+            stage_w(wsrc + (size_t)(e0 + 2 * EC) * row_bytes, min(EC, NO - e0 - 2 * EC) * row_bytes, w_buf0,
                     wave, lane);
         route_chunk<TIn, NX, TPW, EA>(reinterpret_cast<const uint4 *>(w_buf1), xr, nchunk, e0 + EC,
-                                  min(EC, E - e0 - EC), bias, lg, E, lane);
+                                  min(EC, NO - e0 - EC), bias, lg, NO, lane);
         __builtin_amdgcn_s_waitcnt(0x0070);
         __syncthreads();
+    }
+
+    if (H > 0) {
+        // silu of this wave's hidden pre-activations, in place
+        for (int i = lane; i < TPW * H; i += 64) {
+            const float v = lg[i];
+            lg[i] = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
+        }
+        // second layer: lane e (+ 64 i) of every token; W2 chunks of HC hidden
+        // units staged transposed ([HC][E] fp32: the lanes read consecutive
+        // words) by the whole block
+        const TIn *w2 = wr + (size_t)H * d;
+        float *w2t = reinterpret_cast<float *>(w_buf0);
+        const int HC = kRouteLdsW / (E * (int)sizeof(float));  // >= 64 (E <= 256)
+        float acc2[TPW][PL];
+#pragma unroll
+        for (int j = 0; j < TPW; j++)
+#pragma unroll
+            for (int i = 0; i < PL; i++) acc2[j][i] = 0.0f;
+        for (int h0 = 0; h0 < H; h0 += HC) {
+            const int hn = min(HC, H - h0);
+            __syncthreads();  // the previous chunk has been read by every wave
+            for (int i = threadIdx.x; i < hn * E; i += kRouteThreads) {
+                const int hh = i / E, e = i - hh * E;
+                w2t[i] = ChunkDot<TIn>::widen(w2[(size_t)e * H + h0 + hh]);
+            }
+            __syncthreads();
+            for (int hh = 0; hh < hn; hh++) {
+                float hv[TPW];
+#pragma unroll
+                for (int j = 0; j < TPW; j++) hv[j] = lg[j * H + h0 + hh];
+#pragma unroll
+                for (int i = 0; i < PL; i++) {
+                    const int e = lane + 64 * i;
+                    const float w = e < E ? w2t[hh * E + e] : 0.0f;
+#pragma unroll
+                    for (int j = 0; j < TPW; j++) acc2[j][i] = __builtin_fmaf(hv[j], w, acc2[j][i]);
+                }
+            }
+        }
+        // the logits, [TPW][E], over the hidden values (every read of them is done)
+#pragma unroll
+        for (int j = 0; j < TPW; j++)
+#pragma unroll
+            for (int i = 0; i < PL; i++) {
+                const int e = lane + 64 * i;
+                if (e < E) lg[j * E + e] = bias ? acc2[j][i] + bias[H + e] : acc2[j][i];
+            }
     }
 
     // ranking: lanes hold experts e = lane + 64 * i; each round is one wave
@@ -368,17 +426,18 @@ template <typename TIn, int NX, int TPW, int EA, int EMAX>
 hipError_t launch_k(const moe_params &p, const void *x, const void *wr, const float *bias, const float *load,
                     float *logits, int32_t *cand, float *cand_score, hipStream_t st) {
     const int row_bytes = p.d * (int)sizeof(TIn);
-    int ec = kRouteLdsW / row_bytes;  // experts staged per LDS chunk
+    const int NO = p.router_hidden > 0 ? p.router_hidden : p.E;  // outputs of the dot loop
+    int ec = kRouteLdsW / row_bytes;  // experts (hidden units) staged per LDS chunk
     if (ec < 1) ec = 1;
-    if (ec > p.E) ec = p.E;
+    if (ec > NO) ec = NO;
     const int tokens_per_block = kRouteWaves * TPW;
     const int grid = (int)ceil_div(p.T, tokens_per_block);
 #define MOE_ROUTE_LAUNCH(NB)                                                                                  \
     hipLaunchKernelGGL((route_kernel<TIn, NX, TPW, NB, EA, EMAX>), dim3(grid), dim3(kRouteThreads), 0, st,    \
                        static_cast<const TIn *>(x), static_cast<const TIn *>(wr), bias, load, -p.lambda,    \
                        p.top2_gap, p.T,                                                                      \
-                       p.d, p.E, p.k + 1, ec, logits, cand, cand_score)
-    if (ec >= p.E) MOE_ROUTE_LAUNCH(1);
+                       p.d, p.E, p.k + 1, ec, p.router_hidden, logits, cand, cand_score)
+    if (ec >= NO) MOE_ROUTE_LAUNCH(1);
     else MOE_ROUTE_LAUNCH(2);
 #undef MOE_ROUTE_LAUNCH
     return hipGetLastError();
@@ -391,6 +450,9 @@ hipError_t launch_t(const moe_params &p, const void *x, const void *wr, const fl
                     const float *load, float *logits, int32_t *cand, float *cand_score,
                     hipStream_t st) {
     constexpr int kEA = 32 / TPW;
+    // the two-layer router: the hidden units and the experts both fit 256
+    if (p.router_hidden > 0)
+        return launch_k<TIn, NX, TPW, kEA, kMaxExperts>(p, x, wr, bias, load, logits, cand, cand_score, st);
     if constexpr (SPEC) {
         if constexpr (TPW == 1) {  // the only tokens-per-wave count used for E <= 32
             if (p.E <= 8) return launch_k<TIn, NX, 1, 8, 32>(p, x, wr, bias, load, logits, cand, cand_score, st);
@@ -570,11 +632,13 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
             part[0][t][e] = load ? __builtin_fmaf(neg_lambda, load[e], raw) : raw;
         }
     } else {
-        // hidden activations silu(sum of the partials) into part[0]; W2 as
-        // fp32 into the (now idle) second ring slot
+        // hidden activations silu(sum of the partials + first-layer bias)
+        // into part[0]; W2 as fp32 into the (now idle) second ring slot.
+        // bias holds the H first-layer biases, then the E second-layer ones.
         for (int i = threadIdx.x; i < nt * H; i += kRmThreads) {
             const int t = i / H, j = i - t * H;
-            const float v = ((part[0][t][j] + part[1][t][j]) + part[2][t][j]) + part[3][t][j];
+            float v = ((part[0][t][j] + part[1][t][j]) + part[2][t][j]) + part[3][t][j];
+            if (bias) v = v + bias[j];
             part[0][t][j] = v * __builtin_amdgcn_rcpf(1.0f + __expf(-v));
         }
         // (stored transposed, [H][E]: the lanes of a wave take consecutive
@@ -591,7 +655,7 @@ __global__ __launch_bounds__(kRmThreads) void route_mfma(
             const int t = i / E, e = i - t * E;
             float acc = 0.0f;
             for (int j = 0; j < H; j++) acc = __builtin_fmaf(part[0][t][j], w2l[j * E + e], acc);
-            if (bias) acc = acc + bias[e];
+            if (bias) acc = acc + bias[H + e];
             logits[(size_t)(t0 + t) * E + e] = acc;
             part[1][t][e] = load ? __builtin_fmaf(neg_lambda, load[e], acc) : acc;
         }
@@ -686,7 +750,10 @@ hipError_t launch_route(const moe_params &p, const void *x, const void *wr, cons
                         const float *load, float *logits, int32_t *cand, float *cand_score,
                         hipStream_t st) {
     if (p.T == 0) return hipSuccess;
-    if (p.dtype == MOE_BF16 && p.E <= 64)
+    // matrix cores for bf16 layers with at most 64 experts (and, for the
+    // two-layer router, at most 64 hidden units); the vector-ALU kernel
+    // otherwise
+    if (p.dtype == MOE_BF16 && p.E <= 64 && p.router_hidden <= 64)
         return launch_mfma(p, x, wr, bias, load, logits, cand, cand_score, st);
     if (p.dtype == MOE_BF16)
         return launch_dtype<uint16_t>(p, x, wr, bias, load, logits, cand, cand_score, st);

@@ -22,7 +22,7 @@ double oracle_dynamic_capacity_factor(int64_t T);
 int64_t oracle_capacity(int64_t T, int64_t k, int64_t E, double cf);
 void oracle_router_logits(int T, int d, int E, int dt, const void *x, const void *wr, const float *bias, float *raw);
 void oracle_router_logits_glu(int T, int d, int E, int H, int dt, const void *x, const void *w1, const void *w2,
-                              const float *bias, float *raw);
+                              const float *bias1, const float *bias, float *raw);
 void oracle_scores(int T, int E, const float *raw, const float *load, float lambda, float *s);
 void oracle_topk(int T, int E, int K, const float *s, int32_t *cand, float *cand_score);
 void oracle_gap_swap(int T, int K, float delta, int32_t *cand, float *cand_score);
@@ -43,6 +43,7 @@ void oracle_backward_expert_units(int e, int nf, const int32_t *fs, int nrows, c
                                   const void *w2, const double *dy, double *dw1, double *dw3, double *dw2);
 void oracle_router_wgrad(int T, int d, int E, int dt, const void *x, const double *dlogits, double *dwr,
                          double *dbias);
+void oracle_load_window(int T, int E, int k, int K1, const int32_t *cand, int window, double alpha, float *load);
 
 static uint64_t rng_state = 0x9E3779B97F4A7C15ull;
 static double urand(void) /* SplitMix64, uniform in [-1, 1) */
@@ -180,12 +181,23 @@ static void run_layer(int T, int d, int E, int k, int d_ff, double cf, int rerou
                 }
         oracle_backward_expert_units(e, d_ff, fs, n, tk, gk, d, d_ff, dt, x, w1, w3, w2, dy, dw1, dw3, dw2);
     }
+    /* windowed load statistic */
+    float *lw = (float *)xalloc((size_t)E * 4);
+    for (int e = 0; e < E; e++)
+        lw[e] = 1.0f / E;
+    oracle_load_window(T, E, k, K1, cand, 7, 0.99, lw);
+    oracle_load_window(T, E, k, K1, cand, 1, 0.5, lw);
+    free(lw);
     /* two-layer router */
     const int H = 2 * E;
     void *g1 = xalloc((size_t)H * d * es), *g2 = xalloc((size_t)E * H * es);
     memset(g1, 0, (size_t)H * d * es);
     memset(g2, 0, (size_t)E * H * es);
-    oracle_router_logits_glu(T, d, E, H, dt, x, g1, g2, bias, raw);
+    float *b1 = (float *)xalloc((size_t)H * sizeof(float));
+    for (int j = 0; j < H; j++)
+        b1[j] = (float)urand();
+    oracle_router_logits_glu(T, d, E, H, dt, x, g1, g2, b1, bias, raw);
+    free(b1);
     void *frees[] = {x, wr, w1, w3, w2, bias, load, raw, s, cand, cs, eid, pos, row, flag, gate, gate64, offsets,
                      tor, demand, kept, ex, yr, hr, yrf, y, y2, toks, dy, dl, dx, dwr, db, fs, dw1, dw3, dw2, tk, gk,
                      g1, g2};

@@ -128,9 +128,8 @@ def test_invalid_sizes_rejected(bad):
 @pytest.mark.parametrize("bad", [dict(d=100), dict(d_ff=96), dict(dtype=7), dict(d=16384 + 64),
                                  dict(d=16384, d_ff=131072, dtype=moe.MOE_BF16),  # one expert matrix of 4 GiB
                                  dict(d=8192, d_ff=131072, dtype=moe.MOE_F32),
-                                 dict(router_hidden=16),  # two-layer router: bf16 only
-                                 dict(router_hidden=65, dtype=moe.MOE_BF16),
-                                 dict(router_hidden=16, E=65, k=2, dtype=moe.MOE_BF16)])
+                                 dict(router_hidden=257),  # two-layer router: at most 256 hidden units
+                                 dict(router_hidden=257, dtype=moe.MOE_BF16)])
 def test_unsupported_shapes_rejected(bad):
     p = P(**bad)
     r = moe.MoeRouting()

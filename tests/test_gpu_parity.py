@@ -386,35 +386,53 @@ def test_router_classes(T, E):
     routing_vs_oracle(p, r.cpu(), lg, None, 0.0)
 
 
-@pytest.mark.parametrize("T,E,H", [(700, 8, 16), (500, 32, 64), (300, 64, 64), (40, 5, 10), (8192 + 17, 16, 32)])
-def test_router_glu(T, E, H):
-    """Two-layer router ("MoE稀疏激活原理与工程实践" §3.1, second step): logits
+GLU_CASES = [
+    # matrix-core router: bf16, E <= 64, H <= 64 (16 and 32 tokens per block)
+    (700, 8, 16, "bf16", True), (500, 32, 64, "bf16", False), (300, 64, 64, "bf16", True),
+    (40, 5, 10, "bf16", True), (8192 + 17, 16, 32, "bf16", True),
+    # vector-ALU router: the page's widths (E 128, H 2E = 256) at 1, 2 and 4
+    # tokens per wave, E = 256, a hidden width that is no multiple of 64, fp32
+    (1000, 128, 256, "bf16", True), (4100, 128, 256, "bf16", True), (8300, 96, 100, "bf16", True),
+    (300, 256, 256, "bf16", True), (300, 128, 256, "f32", True), (600, 8, 16, "f32", False),
+]
+
+
+@pytest.mark.parametrize("T,E,H,dtype,with_bias", GLU_CASES)
+def test_router_glu(T, E, H, dtype, with_bias):
+    """Two-layer router ("MoE稀疏激活原理与工程实践" §3.1, second step; its §4.2
+    code: Linear(d, 2E) -> SiLU -> Linear(2E, E), both with a bias): logits
     against the oracle's, routing and dispatch bit-exact from the GPU's
     logits, and moe_forward's logits identical to moe_route's."""
-    cfg = small_cfg(T=T, E=E, k=2, d=256, d_ff=64, cf=1.0)
+    cfg = small_cfg(T=T, E=E, k=2, d=256, d_ff=64, cf=1.0, dtype=dtype)
     L = Layer(cfg)
     g = torch.Generator(device=DEV)
     g.manual_seed(7 * H + E)
-    w1 = (torch.randn((H, cfg.d), device=DEV, generator=g) / cfg.d ** 0.5).to(torch.bfloat16)
-    w2 = (torch.randn((E, H), device=DEV, generator=g) / H ** 0.5).to(torch.bfloat16)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    w1 = (torch.randn((H, cfg.d), device=DEV, generator=g) / cfg.d ** 0.5).to(dt)
+    w2 = (torch.randn((E, H), device=DEV, generator=g) / H ** 0.5).to(dt)
+    b1 = torch.randn(H, device=DEV, generator=g) * 0.5 if with_bias else None
+    b2 = torch.randn(E, device=DEV, generator=g) * 0.5 if with_bias else None
+    bias = torch.cat([b1, b2]) if with_bias else None
     wr = torch.cat([w1.flatten(), w2.flatten()])
     p = params(cfg, router_hidden=H)
-    say(f"[case] glu router T={T} E={E} H={H}")
+    say(f"[case] glu router T={T} E={E} H={H} {dtype} bias={with_bias}")
     r = moe.Routing(p, DEV)
     logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
-    moe.route(p, L.g["x"], wr, L.g["bias"], None, logits, r)
+    moe.route(p, L.g["x"], wr, bias, None, logits, r)
     R = moe.max_rows(p)
-    xp = torch.empty((max(R, 1), p.d), dtype=torch.bfloat16, device=DEV)
+    xp = torch.empty((max(R, 1), p.d), dtype=dt, device=DEV)
     moe.dispatch(p, L.g["x"], r, xp, moe.alloc_workspace(p, DEV, dispatch_only=True))
     torch.cuda.synchronize()
     lg = logits.cpu().numpy()
-    own = oracle.router_logits_glu(L.c["x"], np_of(w1.cpu()), np_of(w2.cpu()), L.c["bias"])
-    assert np.abs(own - lg).max() <= 1e-3 * rms(own), "router logits"
+    tok = np.arange(T) if T <= 1000 else np.unique(np.r_[0, T - 1, np.random.default_rng(3).choice(T, 512, replace=False)])
+    own = oracle.router_logits_glu(L.c["x"][tok], np_of(w1.cpu()), np_of(w2.cpu()),
+                                   None if b2 is None else b2.cpu().numpy(), None if b1 is None else b1.cpu().numpy())
+    assert np.abs(own - lg[tok]).max() <= 1e-3 * rms(own), "router logits"
     routing_vs_oracle(p, r.cpu(), lg, None, 0.0)
     # the forward pass routes with the same kernel
-    y = torch.empty((T, p.d), dtype=torch.bfloat16, device=DEV)
+    y = torch.empty((T, p.d), dtype=dt, device=DEV)
     lg2 = torch.empty_like(logits)
-    moe.forward(p, L.g["x"], wr, L.g["bias"], None, L.g["w1"], L.g["w3"], L.g["w2"], y, lg2, moe.Routing(p, DEV),
+    moe.forward(p, L.g["x"], wr, bias, None, L.g["w1"], L.g["w3"], L.g["w2"], y, lg2, moe.Routing(p, DEV),
                 moe.alloc_workspace(p, DEV))
     torch.cuda.synchronize()
     assert np.array_equal(lg2.cpu().numpy().view(np.uint32), lg.view(np.uint32))
@@ -468,3 +486,31 @@ def test_deterministic_rerun():
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
     for n in moe.Routing.NAMES:
         assert torch.equal(outs[0][1][n], outs[1][1][n]), n
+
+
+@pytest.mark.parametrize("T,E,k,window,decay", [
+    (4096, 8, 2, 1024, 0.99),    # the page's window and decay, whole windows
+    (3000, 16, 2, 1024, 0.99),   # a shorter last window
+    (777, 64, 3, 100, 0.9),
+    (1000, 256, 8, 1, 0.5),      # one token per window
+    (500, 8, 2, 4096, 0.0),      # one window longer than the batch, no memory
+    ((1 << 20), 8, 2, 1024, 0.99),
+])
+def test_load_window(T, E, k, window, decay):
+    """Windowed load statistic ("企业官网建设流程全解析" page §2) from the GPU
+    router's candidates: bit-exact with the oracle on the same candidates."""
+    cfg = small_cfg(T=T, E=E, k=k, d=64, d_ff=64, cf=1.0)
+    p = params(cfg)
+    say(f"[case] load window T={T} E={E} k={k} window={window} decay={decay}")
+    g = moe_synth.make_layer(cfg, DEV, want=("x", "w_router", "bias"))
+    r = moe.Routing(p, DEV)
+    logits = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    moe.route(p, g["x"], g["w_router"], None, None, logits, r)
+    load0 = (torch.arange(E, dtype=torch.float32, device=DEV) + 1.0) / (E * (E + 1) / 2)
+    load = load0.clone()
+    moe.load_window(p, r.cand, window, decay, load)
+    torch.cuda.synchronize()
+    want = oracle.load_window(r.cand.cpu().numpy(), E, k, load0.cpu().numpy(), window, float(np.float32(decay)))
+    got = load.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), f"max diff {np.abs(got - want).max()}"
+    assert abs(float(got.astype(np.float64).sum()) - 1.0) < 1e-5

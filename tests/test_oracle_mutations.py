@@ -45,6 +45,14 @@ MUTATIONS = {
     "e4m3_no_nan": ("if (e == 15 && f == 7)\n        return NAN;", "if (0)\n        return NAN;"),
     "dequant_scale_by_column": ("(double)scale[r] * oracle_fp8", "(double)scale[c % rows] * oracle_fp8"),
     "double_elements_as_float": ("        return ((const double *)p)[i];", "        return (double)((const float *)p)[i];"),
+    "glu_bias1_after_silu": ("            if (bias1)\n                acc += bias1[j];\n            a[j] = acc / (1.0 + exp(-acc));",
+                             "            a[j] = acc / (1.0 + exp(-acc));\n            if (bias1)\n                a[j] += bias1[j];"),
+    "glu_bias1_dropped": ("                acc += bias1[j];", "                acc += 0.0;"),
+    "load_window_decay_swapped": ("l[e] = alpha * l[e] + (1.0 - alpha) *", "l[e] = (1.0 - alpha) * l[e] + alpha *"),
+    "load_window_counts_fallback": ("            for (int r = 0; r < k; r++) {\n                const int c = cand[(size_t)t * K1 + r];",
+                                    "            for (int r = 0; r < K1; r++) {\n                const int c = cand[(size_t)t * K1 + r];"),
+    "load_window_over_batch": ("((double)cnt[e] / ((double)k * n));", "((double)cnt[e] / ((double)k * T));"),
+    "load_window_full_last": ("const int n = T - t0 < window ? T - t0 : window;", "const int n = window;"),
     # backward pass
     "bwd_silu_derivative_first_term_only": ("const double da = dh * b[j] * sg * (1.0 + a[j] * (1.0 - sg));",
                                             "const double da = dh * b[j] * sg;"),
@@ -75,6 +83,7 @@ CHECKS = [
     ("router_glu", pins.check_router_glu), ("fp8_decode", pins.check_fp8_decode),
     ("dynamic_capacity", pins.check_dynamic_capacity),
     ("dequant_rows", pins.check_dequant_rows), ("ffn_double_elements", pins.check_ffn_double_elements),
+    ("load_window", pins.check_load_window),
     ("backward_autograd", bwd.check_backward_autograd),
     ("backward_finite_differences", bwd.check_backward_finite_differences),
     ("backward_invariants", bwd.check_backward_invariants),

@@ -413,6 +413,22 @@ def check_router_glu(o):
     gb = o.router_logits_glu(xb, w1b, w2b, b)
     gf = o.router_logits_glu(xb.float().numpy(), w1b.float().numpy(), w2b.float().numpy(), b)
     assert np.array_equal(gb, gf)
+    # the first layer's bias is one more input feature: a constant-1 column of
+    # x whose W1 column is the bias (added before the silu, in the same sum)
+    b1 = r.standard_normal(H).astype(np.float32)
+    xa = np.ascontiguousarray(np.concatenate([x, np.ones((T, 1), np.float32)], axis=1))
+    w1a = np.ascontiguousarray(np.concatenate([w1, b1[:, None]], axis=1))
+    assert np.array_equal(o.router_logits_glu(x, w1, w2, b, bias1=b1), o.router_logits_glu(xa, w1a, w2, b))
+    # the page's router code form, Linear(d, 2E) -> SiLU -> Linear(2E, E), by torch in float64
+    lin1, lin2 = torch.nn.Linear(d, H).double(), torch.nn.Linear(H, E).double()
+    with torch.no_grad():
+        lin1.weight.copy_(torch.from_numpy(w1.astype(np.float64)))
+        lin1.bias.copy_(torch.from_numpy(b1.astype(np.float64)))
+        lin2.weight.copy_(torch.from_numpy(w2.astype(np.float64)))
+        lin2.bias.zero_()
+        ref = torch.nn.Sequential(lin1, torch.nn.SiLU(), lin2)(torch.from_numpy(x.astype(np.float64))).numpy()
+    got = o.router_logits_glu(x, w1, w2, None, bias1=b1).astype(np.float64)
+    assert np.allclose(got, ref.astype(np.float32), rtol=1e-6, atol=1e-6)
 
 
 def test_router_glu(oracle_mod):
@@ -716,3 +732,48 @@ def test_example_shape(oracle_mod):
     w2 = r.standard_normal((8, d, 16)).astype(np.float32) / 4
     out = o.forward(x, wr, None, w1, w1, w2, E=8, k=2, cf=1.25)
     assert out["y"].reshape(g["B"], g["S"], d).shape == (g["B"], g["S"], d)
+
+
+def check_load_window(o):
+    """Windowed load statistic ("企业官网建设流程全解析" page §2: selection
+    frequency over a sliding window of recent tokens, 1024 on the page, with
+    a decay factor 0.99), pinned by closed forms of the iterated update:
+      * n windows that all repeat one selection pattern of frequency f give
+        alpha^n load0 + (1 - alpha^n) f (geometric series);
+      * decay 1 leaves the statistic as it was; decay 0 gives the last
+        window's frequency, its selections over k x its own token count
+        (a last window shorter than the others included);
+      * a statistic that sums to 1 still sums to 1 (each window's
+        frequencies do);
+      * the page's parameters: 100 windows of 1024 tokens that all pick
+        expert 0 (top-1) take a zero statistic to 1 - 0.99^100."""
+    r = rng(21)
+    E, k, W = 6, 2, 16
+    pat = np.stack([r.permutation(E)[:k + 1] for _ in range(W)]).astype(np.int32)
+    f = np.bincount(pat[:, :k].ravel(), minlength=E) / (k * W)
+    load0 = (r.random(E) / E).astype(np.float32)
+    for n, alpha in ((1, 0.99), (7, 0.9), (50, 0.5)):
+        cand = np.tile(pat, (n, 1))
+        got = o.load_window(cand, E, k, load0, W, alpha).astype(np.float64)
+        want = alpha ** n * load0.astype(np.float64) + (1 - alpha ** n) * f
+        assert np.allclose(got, want, rtol=1e-6, atol=1e-7), (n, alpha, got, want)
+    cand = np.concatenate([np.tile(pat, (3, 1)), pat[:5]])  # three full windows and one of 5 tokens
+    assert np.array_equal(o.load_window(cand, E, k, load0, W, 1.0), load0)
+    last = np.bincount(pat[:5, :k].ravel(), minlength=E) / (k * 5)
+    assert np.allclose(o.load_window(cand, E, k, load0, W, 0.0), last, rtol=1e-7, atol=0)
+    u = np.full(E, 1.0 / E, np.float32)
+    cand = np.stack([r.permutation(E)[:k + 1] for _ in range(203)]).astype(np.int32)
+    assert abs(float(o.load_window(cand, E, k, u, 17, 0.8).astype(np.float64).sum()) - 1.0) < 1e-6
+    # the page's window and decay: top-1, every token picks expert 0
+    cand = np.zeros((100 * 1024, 2), np.int32)
+    cand[:, 1] = 1
+    got = o.load_window(cand, 4, 1, np.zeros(4, np.float32), 1024, 0.99)
+    assert abs(float(got[0]) - (1.0 - 0.99 ** 100)) < 1e-6 and np.all(got[1:] == 0)
+    # candidates that name no expert select nothing; the fallback rank is not a selection
+    cand = np.array([[-1, 2, 0], [1, 7, 0]], np.int32)
+    got = o.load_window(cand, 3, 2, np.zeros(3, np.float32), 8, 0.0)
+    assert np.allclose(got, [0.0, 0.25, 0.25])
+
+
+def test_load_window(oracle_mod):
+    check_load_window(oracle_mod)
