@@ -33,6 +33,9 @@ def parse():
     ap.add_argument("--fp8-weights", action="store_true",
                     help="expert weights as E4M3 codes with fp32 row scales (weight-streaming layers: "
                          "capacity <= 32 rows per expert)")
+    ap.add_argument("--int8-weights", action="store_true",
+                    help="expert weights as INT8 codes with fp32 row scales (weight-streaming layers: "
+                         "capacity <= 32 rows per expert)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the step-time distribution, cold-cache steps and amd-smi sampling "
                          "(for runs under a profiler)")
@@ -132,14 +135,16 @@ def main():
     dt = p.torch_dtype
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     fp8 = None
-    if args.fp8_weights:
+    qfmt = "int8" if args.int8_weights else "e4m3" if args.fp8_weights else None
+    if qfmt:
         if not (p.dtype == moe.MOE_BF16 and moe.capacity(p) <= 32 and d % 128 == 0 and cfg.d_ff % 128 == 0):
-            print(f"bench.py: --fp8-weights needs a bf16 layer with capacity <= 32 and d, d_ff multiples of 128; "
+            print(f"bench.py: one-byte weights need a bf16 layer with capacity <= 32 and d, d_ff multiples of 128; "
                   f"{cfg.name} has capacity {moe.capacity(p)}", file=sys.stderr)
             sys.exit(2)
-        fp8 = {}
+        fp8 = {"fmt": qfmt}
+        quant = moe_synth.quantize_rows_int8 if qfmt == "int8" else moe_synth.quantize_rows_e4m3
         for n in ("w1", "w3", "w2"):
-            fp8["q" + n[1]], fp8["s" + n[1]] = moe_synth.quantize_rows_e4m3(L[n])
+            fp8["q" + n[1]], fp8["s" + n[1]] = quant(L[n])
             L[n] = None
         torch.cuda.empty_cache()
     R = moe.max_rows(p)
@@ -163,8 +168,9 @@ def main():
 
     def step(events=None):
         if fp8:
-            moe.forward_fp8(p, L["x"], L["w_router"], L["bias"], load, fp8["q1"], fp8["s1"], fp8["q3"], fp8["s3"],
-                            fp8["q2"], fp8["s2"], y, logits, r, ws)
+            (moe.forward_i8 if fp8["fmt"] == "int8" else moe.forward_fp8)(
+                p, L["x"], L["w_router"], L["bias"], load, fp8["q1"], fp8["s1"], fp8["q3"], fp8["s3"], fp8["q2"],
+                fp8["s2"], y, logits, r, ws)
         elif events is not None:
             moe.forward_events(p, L["x"], L["w_router"], L["bias"], load, L["w1"], L["w3"], L["w2"], y, logits, r,
                                ws, events)
@@ -262,7 +268,7 @@ def main():
         t = achieved_ms if achieved_ms is not None else ms_per_step
         gbs = work["gemm_weight_bytes"] / (t * 1e-3) / 1e9
         roofline = {"kernel": "expert grouped GEMM, gate-up + down launches (weight streaming"
-                              + (", E4M3 weights; timed over the whole step)" if fp8 else ")"),
+                              + (f", {fp8['fmt']} weights; timed over the whole step)" if fp8 else ")"),
                     "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
                     "traffic": traffic.get("expert_ffn"),
                     "per_launch_work": f"{work['gemm_weight_bytes']} weight bytes ({active} active experts x 3 x d x d_ff)"}
@@ -291,7 +297,7 @@ def main():
                    "T": T, "d": d, "E": E, "k": k, "d_ff": cfg.d_ff, "capacity_factor": cfg.cf,
                    "rows": rows, "dropped": int(totals[1]), "rerouted": int(totals[2]),
                    "parallelism": "single GPU, all experts resident",
-                   "expert_weights": "fp8 e4m3 codes + fp32 row scales" if fp8 else cfg.dtype},
+                   "expert_weights": f"{fp8['fmt']} codes + fp32 row scales" if fp8 else cfg.dtype},
         "layer_tflops": layer_flops / (ms_per_step * 1e-3) / 1e12,
         "mfma_util_pct": (100.0 * roofline["frac"]) if roofline["bound"] == "mfma" else None,
         "stages": stages,
@@ -417,8 +423,9 @@ def cpu_baseline(cfg, L, load, target_s, fp8=None):
     c = {n: (oracle._np(v) if v is not None else None) for n, v in L.items()}
     xe = c["x"]
     if fp8:
+        deq = oracle.dequant_rows_i8 if fp8["fmt"] == "int8" else oracle.dequant_rows
         for j in ("1", "3", "2"):
-            c["w" + j] = oracle.dequant_rows(fp8["q" + j].cpu().numpy(), fp8["s" + j].cpu().numpy())
+            c["w" + j] = deq(fp8["q" + j].cpu().numpy(), fp8["s" + j].cpu().numpy())
         xe = L["x"].float().cpu().numpy().astype(np.float64)
     ld = None if load is None else load.cpu().numpy().astype(np.float32)
     T = cfg.T

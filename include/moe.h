@@ -368,6 +368,23 @@ int moe_backward(const moe_params *p, const void *x, const void *w_router, const
                  float *dw_router, float *dbias, float *dw1, float *dw3, float *dw2, void *workspace,
                  size_t ws_bytes, void *stream);
 
+/*
+ * One-byte expert weights as INT8 codes (two's complement, -128..127) with
+ * one fp32 scale per output row: W[e][j][i] = s[e][j] * q[e][j][i]
+ * ("MoE稀疏激活原理与工程实践" §3.2 quantises the experts to INT8;
+ * "企业官网建设流程全解析" page §5.1 to integer formats).  The codes are
+ * widened exactly to bf16 (gate-up) and fp16 (down) in registers and the
+ * scales multiply the fp32 accumulators.  Layouts, limits, activations and
+ * workspace as for moe_expert_ffn_fp8 / moe_forward_fp8.
+ */
+int moe_expert_ffn_i8(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                      const int8_t *w1, const float *s1, const int8_t *w3, const float *s3,
+                      const int8_t *w2, const float *s2, void *h, void *y_perm, void *stream);
+int moe_forward_i8(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                   const float *load, const int8_t *w1, const float *s1, const int8_t *w3,
+                   const float *s3, const int8_t *w2, const float *s2, void *y, float *logits,
+                   moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
+
 /* Static description of a return code. */
 const char *moe_strerror(int code);
 

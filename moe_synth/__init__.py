@@ -197,6 +197,18 @@ def quantize_rows_e4m3(w: torch.Tensor):
     return q.contiguous(), s.contiguous()
 
 
+def quantize_rows_int8(w: torch.Tensor):
+    """Synthetic INT8 weights from a weight tensor [..., rows, cols]: an fp32
+    scale per row, amax / 127 (1 for an all-zero row), and the codes
+    round-half-even(w / scale) in [-127, 127].  Returns (codes int8
+    [..., rows, cols], scales fp32 [..., rows])."""
+    wf = w.float()
+    amax = wf.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / 127.0, torch.ones_like(amax))
+    q = torch.round(wf / s[..., None]).clamp_(-127, 127).to(torch.int8)
+    return q.contiguous(), s.contiguous()
+
+
 def upstream_grad(cfg: MoEConfig, device="cpu", seed: int = 0, T: Optional[int] = None) -> torch.Tensor:
     """Upstream gradient dy [T, d] of the layer output for the backward pass:
     N(0, 1) in the layer's dtype, substream "dy"."""

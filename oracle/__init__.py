@@ -61,6 +61,8 @@ def lib():
         L.oracle_fp8_e4m3_value.restype = f64
         L.oracle_fp8_e4m3_decode.argtypes = [i64, P, P]
         L.oracle_dequant_rows.argtypes = [i64, i64, P, P, P]
+        L.oracle_dequant_rows_i8.argtypes = [i64, i64, P, P, P]
+        L.oracle_dequant_rows_i8.restype = None
         L.oracle_backward_tokens.argtypes = [i32, P, i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, P, P, P, P]
         L.oracle_backward_expert_units.argtypes = [i32, i32, P, i32, P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.oracle_router_wgrad.argtypes = [i32, i32, i32, i32, P, P, P, P]
@@ -233,6 +235,16 @@ def dequant_rows(q, scale) -> np.ndarray:
     assert scale.shape == q.shape[:-1]
     w = np.empty(q.shape, np.float64)
     lib().oracle_dequant_rows(scale.size, q.shape[-1], _p(q), _p(scale), _p(w))
+    return w
+
+
+def dequant_rows_i8(q, scale) -> np.ndarray:
+    """w[..., r, c] = scale[..., r] * q[..., r, c] in double, q INT8 codes."""
+    q = np.ascontiguousarray(_np(q), dtype=np.int8)
+    scale = np.ascontiguousarray(_np(scale), dtype=np.float32)
+    assert scale.shape == q.shape[:-1]
+    w = np.empty(q.shape, np.float64)
+    lib().oracle_dequant_rows_i8(scale.size, q.shape[-1], _p(q), _p(scale), _p(w))
     return w
 
 

@@ -112,6 +112,19 @@ void oracle_dequant_rows(int64_t rows, int64_t cols, const uint8_t *q, const flo
  * 1 + 0.01 * log2(batch size), 1.05 at 32).  Reading: the batch size is the
  * number of tokens T routed together; evaluated in double; T < 1 gives 1.
  */
+/*
+ * INT8 expert weights (P3 §3.2 quantises the experts' weights to INT8; P5
+ * §5.1 to integer formats).  Reading: a code is a two's complement byte,
+ * value -128..127, and w[r][c] = scale[r] * q[r][c] with one fp32 scale per
+ * output row, as for the E4M3 codes above; exact in double.
+ */
+void oracle_dequant_rows_i8(int64_t rows, int64_t cols, const int8_t *q, const float *scale, double *w)
+{
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            w[r * cols + c] = (double)scale[r] * (double)q[r * cols + c];
+}
+
 double oracle_dynamic_capacity_factor(int64_t T)
 {
     if (T < 1)

@@ -871,11 +871,29 @@ __device__ __forceinline__ void sk8_issue(const Sk8Thread &g, char *stage, int k
     }
 }
 
-// eight E4M3 values -> eight bf16 (gate-up) or fp16 (down), element i from
-// byte i
+// eight INT8 values (two's complement) -> eight bf16 (gate-up) or fp16
+// (down), element i from byte i: sign-extended, converted to fp32 and packed.
+// Every value in [-128, 127] is exact in both types; for bf16 the fp32 bits
+// of such an integer end in 16 zero bits, so the upper halves are packed.
 template <bool F16>
+__device__ __forceinline__ uint32_t i8x2_widen(uint32_t w, int byte0) {
+    const float a = (float)(int32_t)__builtin_amdgcn_sbfe(w, 8 * byte0, 8),
+                b = (float)(int32_t)__builtin_amdgcn_sbfe(w, 8 * byte0 + 8, 8);
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    else return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// one-byte weight codes: OCP E4M3 or INT8
+enum { kQE4M3 = 0, kQInt8 = 1 };
+
+// eight one-byte codes -> eight bf16 (gate-up) or fp16 (down), element i
+// from byte i
+template <bool F16, int FMT = kQE4M3>
 __device__ __forceinline__ uint4 fp8x8_widen(uint2 q) {
-    if constexpr (F16) {
+    if constexpr (FMT == kQInt8) {
+        return make_uint4(i8x2_widen<F16>(q.x, 0), i8x2_widen<F16>(q.x, 2), i8x2_widen<F16>(q.y, 0),
+                          i8x2_widen<F16>(q.y, 2));
+    } else if constexpr (F16) {
         return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, false)),
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, true)),
                           __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.y, 1.0f, false)),
@@ -888,7 +906,7 @@ __device__ __forceinline__ uint4 fp8x8_widen(uint2 q) {
     }
 }
 
-template <int MODE, int NB>
+template <int MODE, int NB, int FMT>
 __device__ __forceinline__ void sk8_compute(const char *stage, int wave, int lane, f32x4_t (&acc)[2][2]) {
     constexpr bool kF16 = MODE == kDown;
     const int r16 = lane & 15, kq = lane >> 4;
@@ -928,8 +946,8 @@ __device__ __forceinline__ void sk8_compute(const char *stage, int wave, int lan
 #pragma unroll
         for (int hf = 0; hf < 2; hf++) {
             const u32x4_t w0 = q[pr][0], w1 = q[pr][1];
-            const uint4 b0 = fp8x8_widen<kF16>(hf ? make_uint2(w0.z, w0.w) : make_uint2(w0.x, w0.y));
-            const uint4 b1 = fp8x8_widen<kF16>(hf ? make_uint2(w1.z, w1.w) : make_uint2(w1.x, w1.y));
+            const uint4 b0 = fp8x8_widen<kF16, FMT>(hf ? make_uint2(w0.z, w0.w) : make_uint2(w0.x, w0.y));
+            const uint4 b1 = fp8x8_widen<kF16, FMT>(hf ? make_uint2(w1.z, w1.w) : make_uint2(w1.x, w1.y));
 #pragma unroll
             for (int ib = 0; ib < NB; ib++) {
                 const uint4 av = __builtin_bit_cast(uint4, a[pr][hf][ib]);
@@ -945,11 +963,11 @@ __device__ __forceinline__ void sk8_compute(const char *stage, int wave, int lan
         WAIT_VMCNT(6 * (kSk8Stages - 2));                                                \
         block_sync();                                                                    \
         sk8_issue<MODE>(g, nxt, min(k0 + (I) + kSk8Stages - 1, nk - 1));                 \
-        sk8_compute<MODE, NB>(cur, g.wave, lane, acc);                                   \
+        sk8_compute<MODE, NB, FMT>(cur, g.wave, lane, acc);                              \
     } while (0)
 
 // The K loop of the bf16 skinny kernel, over three stages of 128 K elements.
-template <int MODE, int NB>
+template <int MODE, int NB, int FMT>
 __device__ __forceinline__ void sk8_main(const Sk8Thread &g, int nk, int lane, char *b0, char *b1, char *b2,
                                          f32x4_t (&acc)[2][2]) {
     sk8_issue<MODE>(g, b0, 0);
@@ -964,7 +982,7 @@ done:
 }
 #undef SK8_STEP
 
-template <int MODE>
+template <int MODE, int FMT>
 __global__ __launch_bounds__(kSkThreads, 2) void grouped_gemm_skinny_fp8(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ B0,
     const uint8_t *__restrict__ B1, const float *__restrict__ S0, const float *__restrict__ S1,
@@ -1017,9 +1035,9 @@ __global__ __launch_bounds__(kSkThreads, 2) void grouped_gemm_skinny_fp8(
         for (int jb = 0; jb < 2; jb++) acc[ib][jb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
     const int nb = ti.mend - ti.m0 > 16 ? 2 : 1;  // active 16-row blocks (uniform)
     if (nb == 2)
-        sk8_main<MODE, 2>(g, nk, lane, sb0, sb1, sb2, acc);
+        sk8_main<MODE, 2, FMT>(g, nk, lane, sb0, sb1, sb2, acc);
     else
-        sk8_main<MODE, 1>(g, nk, lane, sb0, sb1, sb2, acc);
+        sk8_main<MODE, 1, FMT>(g, nk, lane, sb0, sb1, sb2, acc);
 
     // epilogue: the lane holds column lane % 16, rows 4 * (lane / 16) + q;
     // the weight rows' scales multiply the accumulators first
@@ -1163,23 +1181,36 @@ __global__ __launch_bounds__(256) void ffn_fixup(float *__restrict__ y, const fl
 
 }  // namespace
 
+template <int FMT>
+static void launch_q8(const moe_params &p, int64_t mt, const void *x_perm, const int32_t *a_rows,
+                      const int32_t *offsets, const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
+                      const uint8_t *w2, const float *s2, void *h, const GemmOut &down, hipEvent_t mid,
+                      hipError_t &ev, hipStream_t st) {
+    const int E = p.E, d = p.d, dff = p.d_ff;
+    const int nt_up = (int)ceil_div(dff, kSkBN);
+    const int nt_dn = (int)ceil_div(d, kSkBNd);
+    hipLaunchKernelGGL((grouped_gemm_skinny_fp8<kGateUp, FMT>), dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0,
+                       st, static_cast<const uint16_t *>(x_perm), a_rows, w1, w3, s1, s3, offsets, E, dff, d, nt_up,
+                       GemmOut{h, nullptr, 0, nullptr});
+    if (mid) ev = hipEventRecord(mid, st);
+    hipLaunchKernelGGL((grouped_gemm_skinny_fp8<kDown, FMT>), dim3((unsigned)(mt * nt_dn)), dim3(kSkThreads), 0, st,
+                       static_cast<const uint16_t *>(h), (const int32_t *)nullptr, w2, w2, s2, s2, offsets, E, d,
+                       dff, nt_dn, down);
+}
+
 hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                                  const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
                                  const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
-                                 const GemmOut &down, hipEvent_t mid, hipStream_t st) {
+                                 const GemmOut &down, hipEvent_t mid, int qfmt, hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
-    const int E = p.E, d = p.d, dff = p.d_ff;
-    if (p.dtype != MOE_BF16 || cap > kSkBM || d % kSk8K != 0 || dff % kSk8K != 0) return hipErrorInvalidValue;
-    const int64_t mt = mtile_bound(max_rows, cap, E, kSkBM);
-    const int nt_up = (int)ceil_div(dff, kSkBN);
-    const int nt_dn = (int)ceil_div(d, kSkBNd);
-    hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
-                       static_cast<const uint16_t *>(x_perm), a_rows, w1, w3, s1, s3, offsets, E, dff, d, nt_up,
-                       GemmOut{h, nullptr, 0, nullptr});
-    if (mid && hipEventRecord(mid, st) != hipSuccess) return hipErrorLaunchFailure;
-    hipLaunchKernelGGL(grouped_gemm_skinny_fp8<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(kSkThreads), 0, st,
-                       static_cast<const uint16_t *>(h), (const int32_t *)nullptr, w2, w2, s2, s2, offsets, E, d,
-                       dff, nt_dn, down);
+    if (p.dtype != MOE_BF16 || cap > kSkBM || p.d % kSk8K != 0 || p.d_ff % kSk8K != 0) return hipErrorInvalidValue;
+    const int64_t mt = mtile_bound(max_rows, cap, p.E, kSkBM);
+    hipError_t ev = hipSuccess;
+    if (qfmt == MOE_Q_INT8)
+        launch_q8<kQInt8>(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);
+    else
+        launch_q8<kQE4M3>(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);
+    if (ev != hipSuccess) return ev;
     return hipGetLastError();
 }
 

@@ -87,11 +87,12 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
-// Expert weights of a forward pass: matrices of the layer's dtype, or E4M3
-// codes with fp32 row scales (s1 non-null).
+// Expert weights of a forward pass: matrices of the layer's dtype, or
+// one-byte codes (E4M3 or INT8, qfmt) with fp32 row scales (s1 non-null).
 struct FfnWeights {
     const void *w1, *w3, *w2;
     const float *s1, *s3, *s2;
+    int qfmt = MOE_Q_E4M3;
 };
 
 int fp8_weights_ok(const moe_params &p, const FfnWeights &w) {
@@ -109,7 +110,7 @@ hipError_t launch_ffn(const moe_params &p, int64_t R, int64_t C, const void *a, 
     if (w.s1)
         return launch_expert_ffn_fp8(p, R, C, a, a_rows, offsets, static_cast<const uint8_t *>(w.w1), w.s1,
                                      static_cast<const uint8_t *>(w.w3), w.s3,
-                                     static_cast<const uint8_t *>(w.w2), w.s2, h, down, mid, st);
+                                     static_cast<const uint8_t *>(w.w2), w.s2, h, down, mid, w.qfmt, st);
     return launch_expert_ffn(p, R, C, a, a_rows, offsets, w.w1, w.w3, w.w2, h, down, claim, mid, st);
 }
 
@@ -339,12 +340,14 @@ int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offse
                                        static_cast<const float *>(workspace), S - 1, st));
 }
 
-int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *offsets,
-                       const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
-                       const uint8_t *w2, const float *s2, void *h, void *y_perm, void *stream) {
+}  // extern "C"
+
+namespace {
+
+int expert_ffn_q8(const moe_params *p, const void *x_perm, const int32_t *offsets, const FfnWeights &w, void *h,
+                  void *y_perm, void *stream) {
     int rc = check_params(p);
     if (rc != MOE_OK) return rc;
-    const FfnWeights w{w1, w3, w2, s1, s3, s2};
     const int64_t R = max_rows_of(*p);
     if (!offsets) return MOE_ERR_INVALID_ARG;
     if ((rc = fp8_weights_ok(*p, w)) != MOE_OK) return rc;
@@ -353,6 +356,22 @@ int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *o
     const GemmOut down{y_perm, nullptr, 0, nullptr};
     return hip_status(launch_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w, h, down, nullptr, nullptr,
                                  static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                       const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
+                       const uint8_t *w2, const float *s2, void *h, void *y_perm, void *stream) {
+    return expert_ffn_q8(p, x_perm, offsets, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_E4M3}, h, y_perm, stream);
+}
+
+int moe_expert_ffn_i8(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                      const int8_t *w1, const float *s1, const int8_t *w3, const float *s3,
+                      const int8_t *w2, const float *s2, void *h, void *y_perm, void *stream) {
+    return expert_ffn_q8(p, x_perm, offsets, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_INT8}, h, y_perm, stream);
 }
 
 int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
@@ -462,7 +481,16 @@ int moe_forward_fp8(const moe_params *p, const void *x, const void *w_router, co
                     const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
                     moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
     if (!s1 || !s3 || !s2) return MOE_ERR_INVALID_ARG;
-    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, s1, s3, s2}, y, logits, r,
+    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_E4M3}, y, logits, r,
+                        workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_forward_i8(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                   const float *load, const int8_t *w1, const float *s1, const int8_t *w3,
+                   const float *s3, const int8_t *w2, const float *s2, void *y, float *logits,
+                   moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
+    if (!s1 || !s3 || !s2) return MOE_ERR_INVALID_ARG;
+    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_INT8}, y, logits, r,
                         workspace, ws_bytes, stream, nullptr);
 }
 

@@ -1,6 +1,7 @@
-"""GPU parity of the one-byte (OCP E4M3) expert weights: moe_expert_ffn_fp8
-and moe_forward_fp8 through the C ABI against the oracle, which dequantises
-the same codes and scales exactly (double) and runs its plain SwiGLU FFN.
+"""GPU parity of the one-byte expert weights, OCP E4M3 codes
+(moe_expert_ffn_fp8, moe_forward_fp8) and INT8 codes (moe_expert_ffn_i8,
+moe_forward_i8), through the C ABI against the oracle, which dequantises the
+same codes and scales exactly (double) and runs its plain SwiGLU FFN.
 
 Tolerances as for the bf16 layer: h (rounded once to fp16) within one fp16
 ulp per element plus 1e-4 * RMS for fp32 accumulation; y_perm and the layer
@@ -44,19 +45,25 @@ def bf16_as_double(t):
 
 
 class Fp8Layer:
-    """A bf16 layer's inputs with the expert weights replaced by E4M3 codes
-    and row scales; the oracle's copies are the exact dequantised weights."""
+    """A bf16 layer's inputs with the expert weights replaced by one-byte
+    codes (E4M3 or INT8) and row scales; the oracle's copies are the exact
+    dequantised weights."""
 
-    def __init__(self, cfg, seed=0):
+    def __init__(self, cfg, seed=0, fmt="e4m3"):
         self.cfg = cfg
-        say(f"[gen] {cfg.name} T={cfg.T} d={cfg.d} E={cfg.E} d_ff={cfg.d_ff} cf={cfg.cf}")
+        self.fmt = fmt
+        say(f"[gen] {cfg.name} {fmt} T={cfg.T} d={cfg.d} E={cfg.E} d_ff={cfg.d_ff} cf={cfg.cf}")
         g = moe_synth.make_layer(cfg, DEV, seed=seed)
         self.x, self.wr, self.bias = g["x"], g["w_router"], g["bias"]
         self.q, self.s, self.wd = {}, {}, {}
         for n in ("w1", "w3", "w2"):
-            q, s = moe_synth.quantize_rows_e4m3(g[n])
+            if fmt == "int8":
+                q, s = moe_synth.quantize_rows_int8(g[n])
+                self.wd[n] = oracle.dequant_rows_i8(q.cpu().numpy(), s.cpu().numpy())
+            else:
+                q, s = moe_synth.quantize_rows_e4m3(g[n])
+                self.wd[n] = oracle.dequant_rows(q.cpu().numpy(), s.cpu().numpy())
             self.q[n], self.s[n] = q, s
-            self.wd[n] = oracle.dequant_rows(q.cpu().numpy(), s.cpu().numpy())
         del g
         torch.cuda.synchronize()
         self.xd = bf16_as_double(self.x)
@@ -65,6 +72,12 @@ class Fp8Layer:
 
     def weights(self):
         return (self.q["w1"], self.s["w1"], self.q["w3"], self.s["w3"], self.q["w2"], self.s["w2"])
+
+    def expert_ffn(self, *a):
+        (moe.expert_ffn_i8 if self.fmt == "int8" else moe.expert_ffn_fp8)(*a)
+
+    def forward(self, *a):
+        (moe.forward_i8 if self.fmt == "int8" else moe.forward_fp8)(*a)
 
 
 def routing_exact(p, rc, logits):
@@ -89,7 +102,7 @@ def check_layer(L, full=True, rows_sample=None):
     h = torch.empty((max(R, 1), dff), dtype=torch.float16, device=DEV)
     y_perm = moe.alloc_y_perm(p, DEV)
     say(f"[expert_ffn_fp8] T={T} R={R}")
-    moe.expert_ffn_fp8(p, x_perm, r.offsets, *L.weights(), h, y_perm)
+    L.expert_ffn(p, x_perm, r.offsets, *L.weights(), h, y_perm)
     torch.cuda.synchronize()
     rc = r.cpu()
     gl = logits.cpu().numpy()
@@ -116,7 +129,7 @@ def check_layer(L, full=True, rows_sample=None):
     r2 = moe.Routing(p, DEV)
     y2 = torch.empty((T, d), dtype=torch.bfloat16, device=DEV)
     logits2 = torch.empty((T, p.E), dtype=torch.float32, device=DEV)
-    moe.forward_fp8(p, L.x, L.wr, L.bias, None, *L.weights(), y2, logits2, r2, moe.alloc_workspace(p, DEV))
+    L.forward(p, L.x, L.wr, L.bias, None, *L.weights(), y2, logits2, r2, moe.alloc_workspace(p, DEV))
     torch.cuda.synchronize()
     ys, y2f = y.float().cpu().numpy().astype(np.float64), y2.float().cpu().numpy().astype(np.float64)
     bad = np.abs(y2f - ys) > 2.0 ** -7 * np.abs(ys) + 2.0 ** -7 * rms(ys)
@@ -154,12 +167,14 @@ CASES = {
 }
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
 @pytest.mark.parametrize("case", sorted(CASES))
-def test_fp8_cases(case):
-    check_layer(Fp8Layer(cfg(name=case, **CASES[case])))
+def test_fp8_cases(case, fmt):
+    check_layer(Fp8Layer(cfg(name=case, **CASES[case]), fmt=fmt))
 
 
-def test_fp8_decode_full_size():
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+def test_fp8_decode_full_size(fmt):
     """The decode workload (T 64, d 4096, E 8, d_ff 14336) with one-byte
     weights, sampled rows at each expert's ends and middle."""
     c = moe_synth.CONFIGS["decode"]
@@ -171,7 +186,7 @@ def test_fp8_decode_full_size():
             rows.update(r for r in (b, en - 1, (b + en) // 2) if b <= r < en)
         return np.array(sorted(rows), np.int32)
 
-    check_layer(Fp8Layer(c), full=True, rows_sample=sample)
+    check_layer(Fp8Layer(c, fmt=fmt), full=True, rows_sample=sample)
 
 
 def test_fp8_empty_batch():

@@ -53,6 +53,7 @@ MUTATIONS = {
                                     "            for (int r = 0; r < K1; r++) {\n                const int c = cand[(size_t)t * K1 + r];"),
     "load_window_over_batch": ("((double)cnt[e] / ((double)k * n));", "((double)cnt[e] / ((double)k * T));"),
     "load_window_full_last": ("const int n = T - t0 < window ? T - t0 : window;", "const int n = window;"),
+    "i8_codes_read_unsigned": ("(double)scale[r] * (double)q[r * cols + c];", "(double)scale[r] * (double)(uint8_t)q[r * cols + c];"),
     # backward pass
     "bwd_silu_derivative_first_term_only": ("const double da = dh * b[j] * sg * (1.0 + a[j] * (1.0 - sg));",
                                             "const double da = dh * b[j] * sg;"),
@@ -83,7 +84,7 @@ CHECKS = [
     ("router_glu", pins.check_router_glu), ("fp8_decode", pins.check_fp8_decode),
     ("dynamic_capacity", pins.check_dynamic_capacity),
     ("dequant_rows", pins.check_dequant_rows), ("ffn_double_elements", pins.check_ffn_double_elements),
-    ("load_window", pins.check_load_window),
+    ("load_window", pins.check_load_window), ("dequant_rows_i8", pins.check_dequant_rows_i8),
     ("backward_autograd", bwd.check_backward_autograd),
     ("backward_finite_differences", bwd.check_backward_finite_differences),
     ("backward_invariants", bwd.check_backward_invariants),

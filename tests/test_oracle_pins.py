@@ -777,3 +777,20 @@ def check_load_window(o):
 
 def test_load_window(oracle_mod):
     check_load_window(oracle_mod)
+
+
+def check_dequant_rows_i8(o):
+    """INT8 codes (two's complement) with fp32 row scales: every code at
+    scale 1 is its integer value (numpy's own int8 conversion), and a scaled
+    row is the exact product scale * code (exact in double)."""
+    codes = np.arange(-128, 128, dtype=np.int8).reshape(2, 128)
+    w = o.dequant_rows_i8(codes, np.ones(2, np.float32))
+    assert np.array_equal(w, codes.astype(np.float64))
+    s = np.array([0.0123, -3.5], np.float32)
+    w = o.dequant_rows_i8(codes, s)
+    assert np.array_equal(w, codes.astype(np.float64) * s.astype(np.float64)[:, None])
+    assert w[0, 0] == -128 * float(s[0]) and w[1, -1] == 127 * float(s[1])
+
+
+def test_dequant_rows_i8(oracle_mod):
+    check_dequant_rows_i8(oracle_mod)
