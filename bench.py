@@ -56,14 +56,15 @@ STAGE_KERNELS = {"route": ("route_",), "dispatch": ("dispatch_",), "expert_ffn":
                  "combine": ("combine_", "zero_fill")}
 
 
-def counter_traffic(workload, fp8=False):
+def counter_traffic(workload, qfmt=None):
     """HBM-side bytes (fetched + written) per forward pass of each stage's
     kernels, from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE summary of
     this workload, scaled by its copy calibration.  A stage is left out when
     its kernel source changed since the counters were taken."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}{'_fp8' if fp8 else ''}_traffic.md")
+    suffix = {None: "", "e4m3": "_fp8", "int8": "_int8"}[qfmt]
+    path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}{suffix}_traffic.md")
     if not os.path.exists(path):
         return {}
     m = re.search(r"```json\n(.*?)\n```", open(path).read(), re.S)
@@ -225,7 +226,7 @@ def main():
     rows = int(totals[0])
     active = int((kept > 0).sum())
     work = stage_work(cfg, rows, active, fp8=bool(fp8))
-    traffic = counter_traffic(args.workload, fp8=bool(fp8))
+    traffic = counter_traffic(args.workload, qfmt=fp8["fmt"] if fp8 else None)
     layer_flops = work["route_flops"] + work["gemm_flops"]
 
     def hbm(nbytes, ms, stage):
