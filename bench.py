@@ -20,6 +20,7 @@ sys.path.insert(0, ROOT)
 METRIC = "MoE-layer tokens/sec + expert-GEMM MFMA util %, Mixtral-shape E=8 top-2 bf16"
 PEAK_MFMA_TFLOPS = 2516.6   # bf16 / fp16 dense matrix peak, MI355X
 PEAK_HBM_GBS = 8000.0       # HBM3E
+PEAK_F32_TFLOPS = 157.3     # fp32 vector ALU peak (the fp32 layer's GEMM runs on the VALU)
 
 
 def parse():
@@ -52,8 +53,10 @@ CSRC = os.path.join(ROOT, "sparse_mixture_experts_gemm_amd", "csrc")
 # for a stage only while that file still has the hash recorded with it
 STAGE_SOURCE = {"route": "route.hip", "dispatch": "dispatch.hip", "expert_ffn": "expert_gemm.hip",
                 "combine": "combine.hip"}
-STAGE_KERNELS = {"route": ("route_",), "dispatch": ("dispatch_",), "expert_ffn": ("grouped_gemm",),
-                 "combine": ("combine_", "zero_fill")}
+# the kernels moe_forward launches per stage (moe_dispatch's gather is not one)
+STAGE_KERNELS = {"route": ("route_",), "dispatch": ("dispatch_hist", "dispatch_primary", "dispatch_finalize",
+                                                    "dispatch_single"),
+                 "expert_ffn": ("grouped_gemm",), "combine": ("combine_", "zero_fill")}
 
 
 def counter_traffic(workload, qfmt=None):
@@ -245,7 +248,8 @@ def main():
             "route": hbm(work["route_bytes"], st_ms["route"], "route"),
             "dispatch": hbm(work["dispatch_bytes"], st_ms["dispatch"], "dispatch"),
             "expert_ffn": {"us": t_ffn * 1e3, "gate_up_us": st_ms["gate_up"] * 1e3, "down_us": st_ms["down"] * 1e3,
-                           "TFLOP/s": gemm_tflops, "mfma_frac": gemm_tflops / PEAK_MFMA_TFLOPS,
+                           "TFLOP/s": gemm_tflops, "mfma_frac": gemm_tflops / PEAK_MFMA_TFLOPS
+                           if cfg.dtype == "bf16" else None,
                            "gate_up_TFLOP/s": work["gemm_flops"] * 2 / 3 / (st_ms["gate_up"] * 1e-3) / 1e12,
                            "down_TFLOP/s": work["gemm_flops"] / 3 / (st_ms["down"] * 1e-3) / 1e12,
                            "weight_bytes": work["gemm_weight_bytes"],
@@ -275,9 +279,12 @@ def main():
                     "per_launch_work": f"{work['gemm_weight_bytes']} weight bytes ({active} active experts x 3 x d x d_ff)"}
     else:
         tf = work["gemm_flops"] / (achieved_ms * 1e-3) / 1e12
+        # bf16 layers multiply on the matrix cores; the fp32 layer's GEMM is a
+        # vector-ALU kernel, priced against the fp32 vector peak
+        bound, peak = ("mfma", PEAK_MFMA_TFLOPS) if cfg.dtype == "bf16" else ("alu", PEAK_F32_TFLOPS)
         roofline = {"kernel": "expert grouped GEMM, gate-up + down launches of moe_forward",
-                    "bound": "mfma", "achieved": tf, "peak": PEAK_MFMA_TFLOPS, "unit": "TFLOP/s",
-                    "frac": tf / PEAK_MFMA_TFLOPS, "traffic": traffic.get("expert_ffn"),
+                    "bound": bound, "achieved": tf, "peak": peak, "unit": "TFLOP/s",
+                    "frac": tf / peak, "traffic": traffic.get("expert_ffn"),
                     "per_launch_work": f"{work['gemm_flops']:.4g} flop ({rows} kept rows x 6 x d x d_ff)"}
 
     backward = None

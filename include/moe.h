@@ -41,7 +41,10 @@
  *   - Every output element listed for an entry point is written on every call.
  *   - NaN or Inf inputs are outside the contract.
  *   - Calls on different streams that share no output buffer may run
- *     concurrently; the library has no global mutable state.
+ *     concurrently.  The only global mutable state is the static scratch
+ *     array of moe_forward_noalloc (one per GPU): calls of that entry point
+ *     that overlap on one GPU race; every other entry point works in the
+ *     caller's buffers only.
  *
  * Return codes: MOE_OK (0) on success, or a negative MOE_ERR_* code; nothing
  * is enqueued when an argument check fails.  moe_strerror() names the code.
