@@ -32,267 +32,102 @@
 namespace moe {
 namespace {
 
-constexpr int kBt = 256;        // threads of a GEMM block (4 waves, 2 x 2)
-constexpr int kTm = 128;        // tile rows (M)
-constexpr int kTn = 128;        // tile columns (N)
-constexpr int kTk = 32;         // K per step
-constexpr int kRowB = 80;       // LDS bytes per tile row: 32 bf16 + 16 bytes of padding (conflict-free reads)
-constexpr int kTileB = kTm * kRowB;
+// The grouped GEMMs (grouped_gemm_bf16<kPlain> and grouped_gemm_wgrad) take
+// both operands K-contiguous, the MFMA fragments' natural layout.  Operands
+// that are not (W2 and W1/W3 for the input gradients; the kept rows, whose
+// K axis is the row index, for the weight gradients) are transposed once
+// into the workspace by the kernels below, through 64 x 64 LDS tiles.
 
-__device__ __forceinline__ f32x16_t mfma_bf16(uint4 a, uint4 b, f32x16_t c) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b),
-                                                   c, 0, 0, 0);
-}
-
-// An operand tile staged as 128 LDS rows of 32 K elements.
-//   K-contiguous source (row-major [row][k]): a thread moves 16 bytes (8 K
-//   elements) of one row per pass, two passes.
-//   Row-contiguous source ([k][row], the tile's rows along the source row):
-//   a thread reads 8 consecutive tile rows at two consecutive k and writes
-//   them as 8 pairs, transposing into the K-contiguous layout.
-// `valid` bounds the tile rows (rows past it, and K past kvalid, are zero).
-struct KcontigSrc {
-    const uint16_t *base;   // element (row, k) at base[src(row) * ld + k]
-    const int32_t *gather;  // src(row) = gather[row0 + row] or row0 + row
-    int64_t ld;
-};
-struct RowcontigSrc {
-    const uint16_t *base;   // element (k, n) at base[src(k) * ld + n]
-    const int32_t *gather;  // src(k) = gather[k] or k (k absolute)
-    int64_t ld;
-};
-
-struct Regs2 {
-    uint4 v[2];
-};
-
-__device__ __forceinline__ Regs2 load_kcontig(const KcontigSrc &s, int row0, int valid, int k0) {
-    Regs2 r;
-    const int t = threadIdx.x;
+// dst[e][c][col0 + r] = src[e][r][c]: one 64 x 64 tile of an expert's
+// [rows][cols] matrix per block (rows and cols multiples of 64); dst rows
+// hold dst_ld elements, experts cols * dst_ld apart.
+__global__ __launch_bounds__(256) void transpose_w(const uint16_t *__restrict__ src, int rows, int cols,
+                                                   uint16_t *__restrict__ dst, int dst_ld, int col0) {
+    __shared__ uint16_t t[64][66];
+    const int tr = rows / 64, tc = cols / 64;
+    const int e = blockIdx.x / (tr * tc), rem = blockIdx.x % (tr * tc);
+    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 64;
+    const int tid = threadIdx.x, q = (tid & 7) * 8;
+    const uint16_t *s = src + (size_t)e * rows * cols;
 #pragma unroll
     for (int ps = 0; ps < 2; ps++) {
-        const int row = ps * 64 + (t >> 2), kc = (t & 3) * 8;
-        r.v[ps] = make_uint4(0, 0, 0, 0);
-        if (row < valid) {
-            const int64_t sr = s.gather ? s.gather[row0 + row] : row0 + row;
-            r.v[ps] = *reinterpret_cast<const uint4 *>(s.base + sr * s.ld + k0 + kc);
-        }
+        const int rr = (tid >> 3) + 32 * ps;
+        const uint4 v = *reinterpret_cast<const uint4 *>(s + (size_t)(r0 + rr) * cols + c0 + q);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int i = 0; i < 4; i++) *reinterpret_cast<uint32_t *>(&t[rr][q + 2 * i]) = w[i];
     }
-    return r;
-}
-
-__device__ __forceinline__ void store_kcontig(char *tile, const Regs2 &r) {
-    const int t = threadIdx.x;
-#pragma unroll
-    for (int ps = 0; ps < 2; ps++) {
-        const int row = ps * 64 + (t >> 2), kc = (t & 3) * 8;
-        *reinterpret_cast<uint4 *>(tile + row * kRowB + kc * 2) = r.v[ps];
-    }
-}
-
-// k in [k0, k0 + 32) with k < kend valid; tile rows n0 + [0, 128) with n < nend.
-__device__ __forceinline__ Regs2 load_rowcontig(const RowcontigSrc &s, int k0, int kend, int n0, int nend) {
-    Regs2 r;
-    const int t = threadIdx.x;
-    const int kp = t >> 4, nc = (t & 15) * 8;
-#pragma unroll
-    for (int h = 0; h < 2; h++) {
-        const int k = k0 + 2 * kp + h;
-        r.v[h] = make_uint4(0, 0, 0, 0);
-        if (k < kend && n0 + nc < nend) {
-            const int64_t sr = s.gather ? s.gather[k] : k;
-            r.v[h] = *reinterpret_cast<const uint4 *>(s.base + sr * s.ld + n0 + nc);
-        }
-    }
-    return r;
-}
-
-__device__ __forceinline__ void store_rowcontig(char *tile, const Regs2 &r) {
-    const int t = threadIdx.x;
-    const int kp = t >> 4, nc = (t & 15) * 8;
-    const uint32_t lo[4] = {r.v[0].x, r.v[0].y, r.v[0].z, r.v[0].w};
-    const uint32_t hi[4] = {r.v[1].x, r.v[1].y, r.v[1].z, r.v[1].w};
-#pragma unroll
-    for (int j = 0; j < 8; j++) {
-        const uint32_t a = (lo[j >> 1] >> ((j & 1) * 16)) & 0xFFFF, b = (hi[j >> 1] >> ((j & 1) * 16)) & 0xFFFF;
-        *reinterpret_cast<uint32_t *>(tile + (nc + j) * kRowB + kp * 4) = a | (b << 16);
-    }
-}
-
-// Which operand of a GEMM comes as a hi/lo pair of bf16 tiles.
-enum { kSplitNone = 0, kSplitA = 1, kSplitB = 2 };
-
-// MFMAs of one 32-wide K step: the wave's 64 x 64 block (2 x 2 blocks of
-// 32).  tl is the lo tile of the split operand (SPLIT A or B): its products
-// with the other operand go into the same accumulators.
-template <int SPLIT>
-__device__ __forceinline__ void tile_mfma(const char *ta, const char *tb, const char *tl, int wm, int wn, int lane,
-                                          f32x16_t (&acc)[2][2]) {
-    const int l5 = lane & 31, hk = (lane >> 5) * 16;
-#pragma unroll
-    for (int ss = 0; ss < 2; ss++) {
-        uint4 a[2], b[2], lo[2];
-#pragma unroll
-        for (int i = 0; i < 2; i++) {
-            a[i] = *reinterpret_cast<const uint4 *>(ta + (wm * 64 + i * 32 + l5) * kRowB + ss * 32 + hk);
-            if (SPLIT == kSplitA)
-                lo[i] = *reinterpret_cast<const uint4 *>(tl + (wm * 64 + i * 32 + l5) * kRowB + ss * 32 + hk);
-        }
-#pragma unroll
-        for (int j = 0; j < 2; j++) {
-            b[j] = *reinterpret_cast<const uint4 *>(tb + (wn * 64 + j * 32 + l5) * kRowB + ss * 32 + hk);
-            if (SPLIT == kSplitB)
-                lo[j] = *reinterpret_cast<const uint4 *>(tl + (wn * 64 + j * 32 + l5) * kRowB + ss * 32 + hk);
-        }
-#pragma unroll
-        for (int i = 0; i < 2; i++)
-#pragma unroll
-            for (int j = 0; j < 2; j++) {
-                acc[i][j] = mfma_bf16(a[i], b[j], acc[i][j]);
-                if (SPLIT == kSplitA) acc[i][j] = mfma_bf16(lo[i], b[j], acc[i][j]);
-                if (SPLIT == kSplitB) acc[i][j] = mfma_bf16(a[i], lo[j], acc[i][j]);
-            }
-    }
-}
-
-// fp32 tile store: element (row, col) at c[row * ldc + col], rows < mvalid,
-// cols < nvalid (tile-relative).  The lane holds column l5 of each 32 x 32
-// block, rows 8 (q / 4) + 4 (lane / 32) + q % 4.
-__device__ __forceinline__ void store_acc(float *c, int64_t ldc, int mvalid, int nvalid, int wm, int wn, int lane,
-                                          const f32x16_t (&acc)[2][2]) {
-    const int l5 = lane & 31, hi = lane >> 5;
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int q = 0; q < 16; q++) {
-                const int row = wm * 64 + i * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
-                const int col = wn * 64 + j * 32 + l5;
-                if (row < mvalid && col < nvalid) c[(int64_t)row * ldc + col] = acc[i][j][q];
-            }
-}
-
-// Grouped "NN" GEMM over the permuted rows: for the rows r of expert e,
-//   C[r][n] = sum_k A[src(r)][k] B_e[k][n]  (+ sum_k A2[r][k] B2_e[k][n])
-// A K-contiguous (rows gathered through a_rows, or the permuted rows), B_e
-// row-major [K][N] (N-contiguous, transposed while staged).  C fp32 [R][N].
-// SPLIT == kSplitA: A and A2 are hi/lo pairs, the lo part lo_off elements
-// after the hi part.
-template <int SPLIT>
-__global__ __launch_bounds__(kBt) void grouped_nn(const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
-                                                  const uint16_t *__restrict__ B, const uint16_t *__restrict__ A2,
-                                                  const uint16_t *__restrict__ B2, size_t lo_off,
-                                                  const int32_t *__restrict__ offsets, int E, int K, int N,
-                                                  int ntiles_n, float *__restrict__ C) {
-    __shared__ __attribute__((aligned(16))) char lds[2][3][kTileB];
-    TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kTm, 1, blockIdx.x, nullptr, nullptr, ti)) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-    const int n0 = ti.nt * kTn, valid = ti.mend - ti.m0;
-    const int pairs = A2 ? 2 : 1;
-    const int nk = K / kTk, steps = nk * pairs;
-    f32x16_t acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; i++)
-#pragma unroll
-        for (int j = 0; j < 2; j++)
-#pragma unroll
-            for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
-    auto srcs = [&](int st, KcontigSrc &sa, RowcontigSrc &sb, int &k0) {
-        const bool second = st >= nk;
-        k0 = (second ? st - nk : st) * kTk;
-        sa = KcontigSrc{second ? A2 : A, second ? nullptr : a_rows, K};
-        sb = RowcontigSrc{(second ? B2 : B) + (size_t)ti.e * K * N, nullptr, N};
-    };
-    auto lo_of = [&](KcontigSrc a) {
-        a.base += lo_off;
-        return a;
-    };
-    KcontigSrc sa;
-    RowcontigSrc sb;
-    int k0;
-    srcs(0, sa, sb, k0);
-    Regs2 ra = load_kcontig(sa, ti.m0, valid, k0), rb = load_rowcontig(sb, k0, K, n0, N), rl;
-    if (SPLIT == kSplitA) rl = load_kcontig(lo_of(sa), ti.m0, valid, k0);
-    store_kcontig(lds[0][0], ra);
-    store_rowcontig(lds[0][1], rb);
-    if (SPLIT == kSplitA) store_kcontig(lds[0][2], rl);
     __syncthreads();
-    for (int st = 0; st < steps; st++) {
-        const int cur = st & 1;
-        if (st + 1 < steps) {
-            srcs(st + 1, sa, sb, k0);
-            ra = load_kcontig(sa, ti.m0, valid, k0);
-            rb = load_rowcontig(sb, k0, K, n0, N);
-            if (SPLIT == kSplitA) rl = load_kcontig(lo_of(sa), ti.m0, valid, k0);
-        }
-        tile_mfma<SPLIT>(lds[cur][0], lds[cur][1], lds[cur][2], wm, wn, lane, acc);
-        if (st + 1 < steps) {
-            store_kcontig(lds[cur ^ 1][0], ra);
-            store_rowcontig(lds[cur ^ 1][1], rb);
-            if (SPLIT == kSplitA) store_kcontig(lds[cur ^ 1][2], rl);
-        }
-        __syncthreads();
+    uint16_t *d = dst + (size_t)e * cols * dst_ld;
+#pragma unroll
+    for (int ps = 0; ps < 2; ps++) {
+        const int cc = (tid >> 3) + 32 * ps;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) w[i] = (uint32_t)t[q + 2 * i][cc] | ((uint32_t)t[q + 2 * i + 1][cc] << 16);
+        *reinterpret_cast<uint4 *>(d + (size_t)(c0 + cc) * dst_ld + col0 + r0 + q) = make_uint4(w[0], w[1], w[2], w[3]);
     }
-    store_acc(C + (size_t)ti.m0 * N + n0, N, valid, N - n0, wm, wn, lane, acc);
 }
 
-// Grouped-K "TN" GEMM, one output matrix per expert: for block (e, m, n),
-//   C_e[m][n] = sum over the rows r of expert e of A[srcA(r)][m] B[srcB(r)][n]
-// A and B row-major over the rows (M- and N-contiguous), transposed while
-// staged.  C fp32 [E][M][N]; an expert without rows gets zeros.  SPLIT: A
-// (kSplitA) or B (kSplitB) is a hi/lo pair, the lo part lo_off elements after
-// the hi part.
-template <int SPLIT>
-__global__ __launch_bounds__(kBt) void grouped_tn(const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows,
-                                                  int64_t lda, const uint16_t *__restrict__ B,
-                                                  const int32_t *__restrict__ b_rows, int64_t ldb, size_t lo_off,
-                                                  const int32_t *__restrict__ offsets, int M, int N, int mt, int nt,
-                                                  float *__restrict__ C) {
-    __shared__ __attribute__((aligned(16))) char lds[2][3][kTileB];
-    const int e = blockIdx.x / (mt * nt), rem = blockIdx.x % (mt * nt);
-    const int m0 = (rem / nt) * kTm, n0 = (rem % nt) * kTn;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, wm = wave >> 1, wn = wave & 1;
-    const int rbeg = offsets[e], rend = offsets[e + 1];
-    const RowcontigSrc sa{A, a_rows, lda}, sb{B, b_rows, ldb};
-    // the lo part of the split operand (same rows, same layout)
-    const RowcontigSrc sl = SPLIT == kSplitA ? RowcontigSrc{A + lo_off, a_rows, lda}
-                                             : RowcontigSrc{B + lo_off, b_rows, ldb};
-    const int l0 = SPLIT == kSplitA ? m0 : n0, lend = SPLIT == kSplitA ? M : N;
-    f32x16_t acc[2][2];
+// The kept rows of each expert, transposed into its K window (kwin_start):
+//   dst[c][kwin_e + koff + j] = src[src_row(offsets[e] + j)][col0 + c]
+// for j < rows_e, zeros for rows_e <= j < Kp_e (Kp_e = rows_e rounded up to
+// 64); koff = half * Kp_e, or both halves (dup).  src_row(r) = gather[r] or
+// r; src rows hold src_ld elements.  Blocks: (expert, 64 kept rows, 64
+// columns), found like the GEMM's tiles.
+__global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ src, int64_t src_ld,
+                                                 const int32_t *__restrict__ gather, int col0, int ncols,
+                                                 const int32_t *__restrict__ offsets, int E,
+                                                 uint16_t *__restrict__ dst, int64_t ldk, int half, int dup) {
+    __shared__ uint16_t t[64][66];
+    TileInfo ti;
+    if (!find_tile(offsets, E, ncols / 64, 64, 1, blockIdx.x, nullptr, nullptr, ti)) return;
+    const int rbeg = offsets[ti.e], rows = ti.mend - rbeg;
+    const int kp = (rows + 63) & ~63;
+    const int j0 = ti.m0 - rbeg, c0 = ti.nt * 64;
+    const int tid = threadIdx.x, q = (tid & 7) * 8;
 #pragma unroll
-    for (int i = 0; i < 2; i++)
+    for (int ps = 0; ps < 2; ps++) {
+        const int rr = (tid >> 3) + 32 * ps, r = ti.m0 + rr;
+        uint4 v = make_uint4(0, 0, 0, 0);
+        if (r < ti.mend) {
+            const int64_t sr = gather ? gather[r] : r;
+            v = *reinterpret_cast<const uint4 *>(src + sr * src_ld + col0 + c0 + q);
+        }
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int j = 0; j < 2; j++)
+        for (int i = 0; i < 4; i++) *reinterpret_cast<uint32_t *>(&t[rr][q + 2 * i]) = w[i];
+    }
+    __syncthreads();
+    const int64_t kw = kwin_start(rbeg, ti.e) + j0 + q;
 #pragma unroll
-            for (int q = 0; q < 16; q++) acc[i][j][q] = 0.0f;
-    const int steps = (rend - rbeg + kTk - 1) / kTk;
-    if (steps > 0) {
-        Regs2 ra = load_rowcontig(sa, rbeg, rend, m0, M), rb = load_rowcontig(sb, rbeg, rend, n0, N), rl;
-        if (SPLIT != kSplitNone) rl = load_rowcontig(sl, rbeg, rend, l0, lend);
-        store_rowcontig(lds[0][0], ra);
-        store_rowcontig(lds[0][1], rb);
-        if (SPLIT != kSplitNone) store_rowcontig(lds[0][2], rl);
-        __syncthreads();
-        for (int st = 0; st < steps; st++) {
-            const int cur = st & 1;
-            if (st + 1 < steps) {
-                const int k0 = rbeg + (st + 1) * kTk;
-                ra = load_rowcontig(sa, k0, rend, m0, M);
-                rb = load_rowcontig(sb, k0, rend, n0, N);
-                if (SPLIT != kSplitNone) rl = load_rowcontig(sl, k0, rend, l0, lend);
-            }
-            tile_mfma<SPLIT>(lds[cur][0], lds[cur][1], lds[cur][2], wm, wn, lane, acc);
-            if (st + 1 < steps) {
-                store_rowcontig(lds[cur ^ 1][0], ra);
-                store_rowcontig(lds[cur ^ 1][1], rb);
-                if (SPLIT != kSplitNone) store_rowcontig(lds[cur ^ 1][2], rl);
-            }
-            __syncthreads();
+    for (int ps = 0; ps < 2; ps++) {
+        const int cc = (tid >> 3) + 32 * ps;
+        uint32_t w[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) w[i] = (uint32_t)t[q + 2 * i][cc] | ((uint32_t)t[q + 2 * i + 1][cc] << 16);
+        const uint4 v = make_uint4(w[0], w[1], w[2], w[3]);
+        uint16_t *d = dst + (size_t)(c0 + cc) * ldk + kw;
+        if (dup) {
+            *reinterpret_cast<uint4 *>(d) = v;
+            *reinterpret_cast<uint4 *>(d + kp) = v;
+        } else {
+            *reinterpret_cast<uint4 *>(d + (size_t)half * kp) = v;
         }
     }
-    store_acc(C + ((size_t)e * M + m0) * N + n0, N, M - m0, N - n0, wm, wn, lane, acc);
+}
+
+// unit_offsets: e * m1 (e = 0..E), then e * m2: the uniform row ranges of
+// the weight-gradient GEMMs' outputs.
+__global__ __launch_bounds__(256) void unit_offsets_kernel(int32_t *__restrict__ o, int E, int m1, int m2) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i > E) return;
+    o[i] = i * m1;
+    o[E + 1 + i] = i * m2;
+}
+
+__global__ __launch_bounds__(256) void fill_zero(float *__restrict__ p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0.0f;
 }
 
 // Two fp32 values as bf16 hi = bf16(v) at p and lo = bf16(v - hi) at p + lo_off.
@@ -313,20 +148,21 @@ __global__ __launch_bounds__(256) void row_gates(const int32_t *__restrict__ row
 }
 
 // Per kept row (one block): h = silu(a) b, dg = u . h (fixed-order block
-// reduction), da = g u b silu'(a), db = g u silu(a), hg = g h, each stored as
-// a bf16 hi/lo pair (lo at lo_off elements after hi).
+// reduction), da = g u b silu'(a), db = g u silu(a), hg = g h, each as a
+// bf16 hi/lo pair: acat row [da hi | db hi | da lo | db lo] (4 d_ff), hg row
+// [hi | lo] (2 d_ff).
 __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__ a, const float *__restrict__ b,
                                                        const float *__restrict__ u,
                                                        const float *__restrict__ gate_of_row,
                                                        const int32_t *__restrict__ offsets, int E, int dff,
-                                                       size_t lo_off, uint16_t *__restrict__ da,
-                                                       uint16_t *__restrict__ db, uint16_t *__restrict__ hg,
+                                                       uint16_t *__restrict__ acat, uint16_t *__restrict__ hg,
                                                        float *__restrict__ dg) {
     __shared__ float part[256];
     const int r = blockIdx.x;
     if (r >= offsets[E]) return;
     const float g = gate_of_row[r];
     const size_t o = (size_t)r * dff;
+    uint16_t *ar = acat + 4 * o, *hr = hg + 2 * o;
     float s = 0.0f;
     for (int f = threadIdx.x * 2; f < dff; f += 512) {
         float dav[2], dbv[2], hv[2];
@@ -340,9 +176,9 @@ __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__
             dbv[i] = dh * silu;
             hv[i] = g * h;
         }
-        store_hi_lo(da + o + f, lo_off, dav);
-        store_hi_lo(db + o + f, lo_off, dbv);
-        store_hi_lo(hg + o + f, lo_off, hv);
+        store_hi_lo(ar + f, 2 * (size_t)dff, dav);
+        store_hi_lo(ar + dff + f, 2 * (size_t)dff, dbv);
+        store_hi_lo(hr + f, (size_t)dff, hv);
     }
     part[threadIdx.x] = s;
     __syncthreads();
@@ -442,63 +278,87 @@ __global__ __launch_bounds__(256) void router_wgrad(const uint16_t *__restrict__
 hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, const BackwardArgs &a, hipStream_t st) {
     const int T = p.T, d = p.d, E = p.E, k = p.k, dff = p.d_ff;
     const int64_t R = max_rows;
-    const int mt1 = (int)ceil_div(dff, kTm), nt1 = (int)ceil_div(d, kTn);  // dW1, dW3: [d_ff][d]
-    const int mt2 = (int)ceil_div(d, kTm), nt2 = (int)ceil_div(dff, kTn);  // dW2: [d][d_ff]
-    if (T == 0) {
-        // no tokens: every weight gradient is zero (no expert has rows)
-        const uint16_t *none = nullptr;
-        const int32_t *nrow = nullptr;
-        hipLaunchKernelGGL(grouped_tn<kSplitNone>, dim3((unsigned)(E * mt1 * nt1)), dim3(kBt), 0, st, none, nrow,
-                           (int64_t)0, none, nrow, (int64_t)0, (size_t)0, a.offsets, dff, d, mt1, nt1, a.dw1);
-        hipLaunchKernelGGL(grouped_tn<kSplitNone>, dim3((unsigned)(E * mt1 * nt1)), dim3(kBt), 0, st, none, nrow,
-                           (int64_t)0, none, nrow, (int64_t)0, (size_t)0, a.offsets, dff, d, mt1, nt1, a.dw3);
-        hipLaunchKernelGGL(grouped_tn<kSplitNone>, dim3((unsigned)(E * mt2 * nt2)), dim3(kBt), 0, st, none, nrow,
-                           (int64_t)0, none, nrow, (int64_t)0, (size_t)0, a.offsets, d, dff, mt2, nt2, a.dw2);
-        hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * ceil_div(d, 256))), dim3(256), 0, st,
-                           static_cast<const uint16_t *>(a.x), a.token_of_row, a.ds_of_row, a.offsets, d,
-                           (int)ceil_div(d, 256), a.dw_router, a.dbias);
+    const uint16_t *x = static_cast<const uint16_t *>(a.x);
+    const uint16_t *dy = static_cast<const uint16_t *>(a.dy);
+    const int nchunk = (int)ceil_div(d, 256);
+    if (T == 0 || R == 0) {
+        // no kept rows: every weight gradient is zero
+        const size_t nw = (size_t)E * dff * d;
+        const int grid = (int)std::min<int64_t>(ceil_div((int64_t)nw, 256), 8192);
+        hipLaunchKernelGGL(fill_zero, dim3(grid), dim3(256), 0, st, a.dw1, nw);
+        hipLaunchKernelGGL(fill_zero, dim3(grid), dim3(256), 0, st, a.dw3, nw);
+        hipLaunchKernelGGL(fill_zero, dim3(grid), dim3(256), 0, st, a.dw2, nw);
+        if (T > 0) {
+            // tokens, none kept: dlogits and dx are zero too
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)std::min<int64_t>(ceil_div((int64_t)T * E, 256), 8192)),
+                               dim3(256), 0, st, a.dlogits, (size_t)T * E);
+            hipLaunchKernelGGL(fill_zero, dim3((unsigned)std::min<int64_t>(ceil_div((int64_t)T * d, 256), 8192)),
+                               dim3(256), 0, st, a.dx, (size_t)T * d);
+        }
+        hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * nchunk)), dim3(256), 0, st, x, a.token_of_row,
+                           a.ds_of_row, a.offsets, d, nchunk, a.dw_router, a.dbias);
         return hipGetLastError();
     }
     const float inv_tau = 1.0f / (p.gate_temperature > 0.0f ? p.gate_temperature : 1.0f);
-    const uint16_t *x = static_cast<const uint16_t *>(a.x);
-    const uint16_t *dy = static_cast<const uint16_t *>(a.dy);
-    const size_t lo_off = (size_t)R * dff;  // lo parts of da, db, hg follow their hi parts
-    const int64_t mt = std::min<int64_t>(R / kTm + E, (int64_t)E * ceil_div(cap, kTm));
-    // 1. the rows' gates; a and b recomputed by the gate-up GEMM
+    const int64_t ldk = a.ldk;
+    const int32_t *uo_f = a.unit_offsets, *uo_d = a.unit_offsets + E + 1;
+    // bound on the 64-row tiles of the kept rows, for the transposes' grids
+    const int64_t mt64 = std::min<int64_t>(R / 64 + E, (int64_t)E * ceil_div(cap, 64));
+    auto kmajor = [&](const uint16_t *src, int64_t src_ld, const int32_t *gather, int col0, int ncols,
+                      uint16_t *dst, int half, int dup) {
+        hipLaunchKernelGGL(to_kmajor, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, st, src, src_ld, gather,
+                           col0, ncols, a.offsets, E, dst, ldk, half, dup);
+    };
+    // 1. the rows' gates, the weight-gradient row ranges, the transposed
+    //    weights; a and b recomputed by the gate-up GEMM
     hipLaunchKernelGGL(row_gates, dim3((unsigned)ceil_div((int64_t)T * k, 256)), dim3(256), 0, st, a.row, a.gate,
                        T * k, a.gate_of_row);
+    hipLaunchKernelGGL(unit_offsets_kernel, dim3((unsigned)ceil_div(E + 1, 256)), dim3(256), 0, st, a.unit_offsets,
+                       E, dff, d);
+    const unsigned wtiles = (unsigned)((int64_t)E * (d / 64) * (dff / 64));
+    hipLaunchKernelGGL(transpose_w, dim3(wtiles), dim3(256), 0, st, static_cast<const uint16_t *>(a.w2), d, dff,
+                       a.w2t, d, 0);
+    hipLaunchKernelGGL(transpose_w, dim3(wtiles), dim3(256), 0, st, static_cast<const uint16_t *>(a.w1), dff, d,
+                       a.w13t, 2 * dff, 0);
+    hipLaunchKernelGGL(transpose_w, dim3(wtiles), dim3(256), 0, st, static_cast<const uint16_t *>(a.w3), dff, d,
+                       a.w13t, 2 * dff, dff);
     hipError_t e = launch_gate_up_raw(p, R, cap, a.x, a.token_of_row, a.offsets, a.w1, a.w3, a.a, a.b, st);
     if (e != hipSuccess) return e;
-    // 2. u = W2_e^T dy_t for every kept row
-    const int nt_u = (int)ceil_div(dff, kTn);
-    hipLaunchKernelGGL(grouped_nn<kSplitNone>, dim3((unsigned)(mt * nt_u)), dim3(kBt), 0, st, dy, a.token_of_row,
-                       static_cast<const uint16_t *>(a.w2), (const uint16_t *)nullptr, (const uint16_t *)nullptr,
-                       (size_t)0, a.offsets, E, d, dff, nt_u, a.u);
+    // 2. u = W2_e^T dy_t for every kept row (dy rows gathered by token)
+    e = launch_plain_gemm(R, cap, E, dy, a.token_of_row, (int64_t)T * d * 2, a.offsets, a.w2t, dff, d, d, 1, a.u,
+                          nullptr, st);
+    if (e != hipSuccess) return e;
     // 3. SwiGLU backward per row, 4. gate softmax backward per token
     hipLaunchKernelGGL(swiglu_backward, dim3((unsigned)R), dim3(256), 0, st, a.a, a.b, a.u, a.gate_of_row, a.offsets,
-                       E, dff, lo_off, a.da, a.db, a.hg, a.dg);
+                       E, dff, a.acat, a.hg, a.dg);
     hipLaunchKernelGGL(gate_backward, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st, a.row, a.eid, a.gate, a.dg,
                        T, E, k, inv_tau, a.dlogits, a.ds_of_row);
-    // 5. dx_perm = W1_e^T da + W3_e^T db, 6. dx
-    const int nt_x = (int)ceil_div(d, kTn);
-    hipLaunchKernelGGL(grouped_nn<kSplitA>, dim3((unsigned)(mt * nt_x)), dim3(kBt), 0, st, (const uint16_t *)a.da,
-                       (const int32_t *)nullptr, static_cast<const uint16_t *>(a.w1), (const uint16_t *)a.db,
-                       static_cast<const uint16_t *>(a.w3), lo_off, a.offsets, E, dff, d, nt_x, a.dx_perm);
+    // 5. dx_perm = [da | db] [W1 | W3] over the hi parts and the lo parts
+    //    (K slices of their own, sharing the one transposed weight copy),
+    //    6. dx
+    e = launch_plain_gemm(R, cap, E, a.acat, nullptr, 0, a.offsets, a.w13t, d, 4 * dff, 2 * dff, a.dx_splits,
+                          a.dx_perm, a.dx_rest, st);
+    if (e != hipSuccess) return e;
     hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,
                        static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, k, d, a.dx);
-    // 7. dW1 = da^T x, dW3 = db^T x, dW2 = dy^T (g h)
-    hipLaunchKernelGGL(grouped_tn<kSplitA>, dim3((unsigned)(E * mt1 * nt1)), dim3(kBt), 0, st, (const uint16_t *)a.da,
-                       (const int32_t *)nullptr, (int64_t)dff, x, a.token_of_row, (int64_t)d, lo_off, a.offsets, dff,
-                       d, mt1, nt1, a.dw1);
-    hipLaunchKernelGGL(grouped_tn<kSplitA>, dim3((unsigned)(E * mt1 * nt1)), dim3(kBt), 0, st, (const uint16_t *)a.db,
-                       (const int32_t *)nullptr, (int64_t)dff, x, a.token_of_row, (int64_t)d, lo_off, a.offsets, dff,
-                       d, mt1, nt1, a.dw3);
-    hipLaunchKernelGGL(grouped_tn<kSplitB>, dim3((unsigned)(E * mt2 * nt2)), dim3(kBt), 0, st, dy, a.token_of_row,
-                       (int64_t)d, (const uint16_t *)a.hg, (const int32_t *)nullptr, (int64_t)dff, lo_off, a.offsets,
-                       d, dff, mt2, nt2, a.dw2);
-    // 8. router weight and bias gradients
-    hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * ceil_div(d, 256))), dim3(256), 0, st, x, a.token_of_row,
-                       a.ds_of_row, a.offsets, d, (int)ceil_div(d, 256), a.dw_router, a.dbias);
+    // 7. the kept rows transposed into their experts' K windows: da and db
+    //    (hi, lo), x (twice), dy (twice), g h (hi, lo)
+    kmajor(a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0);
+    kmajor(a.acat, 4 * (int64_t)dff, nullptr, 2 * dff, 2 * dff, a.dat, 1, 0);
+    kmajor(x, d, a.token_of_row, 0, d, a.xt, 0, 1);
+    kmajor(dy, d, a.token_of_row, 0, d, a.dyt, 0, 1);
+    kmajor(a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0);
+    kmajor(a.hg, 2 * (int64_t)dff, nullptr, dff, dff, a.hgt, 1, 0);
+    // 8. dW1 = da^T x, dW3 = db^T x, dW2 = dy^T (g h), each expert over its rows
+    e = launch_wgrad_gemm(E, a.dat, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw1, st);
+    if (e != hipSuccess) return e;
+    e = launch_wgrad_gemm(E, a.dat + (size_t)dff * ldk, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw3, st);
+    if (e != hipSuccess) return e;
+    e = launch_wgrad_gemm(E, a.dyt, a.hgt, a.offsets, uo_d, d, dff, (int)ldk, a.dw2, st);
+    if (e != hipSuccess) return e;
+    // 9. router weight and bias gradients
+    hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * nchunk)), dim3(256), 0, st, x, a.token_of_row,
+                       a.ds_of_row, a.offsets, d, nchunk, a.dw_router, a.dbias);
     return hipGetLastError();
 }
 

@@ -53,7 +53,14 @@ constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (
 
 // kGateUpRaw: the gate-up GEMM storing its two products a = x W1^T and
 // b = x W3^T in fp32 instead of silu(a) * b (the backward pass needs them).
-enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2 };
+// kPlain: one bf16 x bf16 product C = A B^T stored in fp32 (the backward
+// pass's GEMMs, K-split like the down projection).
+enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2, kPlain = 3 };
+
+// The B tile is 128 rows of W1 and the same 128 rows of W3 (gate-up modes),
+// or 256 rows of one matrix.
+template <int MODE>
+__device__ __forceinline__ constexpr bool two_b() { return MODE == kGateUp || MODE == kGateUpRaw; }
 
 
 template <typename T>
@@ -147,7 +154,7 @@ struct GemmThread {
 
 template <int MODE>
 __device__ __forceinline__ int b_imm(int jn) {
-    if (MODE != kDown) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * kRowBytes;
+    if (two_b<MODE>()) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * kRowBytes;
     return jn * 32 * kRowBytes;
 }
 
@@ -537,8 +544,8 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
 template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
-    const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n,
-    int splits, uint32_t a_bytes, int32_t *claim, GemmOut out) {
+    const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ldb,
+    int ntiles_n, int splits, uint32_t a_bytes, int32_t *claim, GemmOut out) {
     __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
@@ -552,8 +559,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     TileInfo ti;
     if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti))
         return;
-    const int n0 = MODE != kDown ? ti.nt * (kBN / 2) : ti.nt * kBN;
-    const size_t wexp = (size_t)ti.e * N * K;
+    const int n0 = two_b<MODE>() ? ti.nt * (kBN / 2) : ti.nt * kBN;
+    const size_t wexp = (size_t)ti.e * N * ldb;
     const int ks = K / splits;              // K elements of this split
     const int k_first = ti.split * ks;      // first K element of this split
 
@@ -566,9 +573,12 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     // (below 4 GiB, also checked).
     g.a_rsrc = a_rows ? make_rsrc(A, a_bytes)
                       : make_rsrc(A + (size_t)ti.m0 * K, (uint32_t)(g.a_valid < kBM ? g.a_valid : kBM) * K * 2);
-    const uint32_t w_bytes = (uint32_t)((size_t)N * K * 2);
+    const uint32_t w_bytes = (uint32_t)((size_t)N * ldb * 2);
     // gate-up: waves 0-1 load B rows 0..127 (W1), waves 2-3 rows 128..255 (W3)
-    g.b_rsrc = make_rsrc((MODE != kDown && wave >= 2 ? B1 : B0) + wexp, w_bytes);
+    g.b_rsrc = make_rsrc((two_b<MODE>() && wave >= 2 ? B1 : B0) + wexp, w_bytes);
+    // B's K position of this split: B rows of ldb elements, read periodically
+    // when the splits of A's K range share one B (ldb < K, a multiple of ks)
+    const int kb_first = k_first % ldb;
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; j++) {
         const int grp = wave * kLoadsPerOperand + j;
@@ -577,13 +587,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         const int gm = min(ti.m0 + row, ti.mend - 1);
         const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
         g.a_off[j] = grp * kRowsPerLoad < g.a_valid ? ((uint32_t)ar * K + k_first + c * 8) * 2 : kPastEnd;
-        int gn = MODE != kDown ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
+        int gn = two_b<MODE>() ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
         gn = min(gn, N - 1);
-        g.b_off[j] = ((uint32_t)gn * K + k_first + c * 8) * 2;
+        g.b_off[j] = ((uint32_t)gn * ldb + kb_first + c * 8) * 2;
     }
     const int l5 = lane & 31, hi = lane >> 5;
     const int sw0 = swz(l5);  // swizzle of row base + l5 is sw0 ^ 4 * parity(base / 32)
-    const int b_rbase = MODE != kDown ? wn * 64 : wn * 128;
+    const int b_rbase = two_b<MODE>() ? wn * 64 : wn * 128;
 #pragma unroll
     for (int pp = 0; pp < 2; pp++)
 #pragma unroll
@@ -606,6 +616,89 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
             run_tile<MODE, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane,     \
                                      out);                                                                       \
     } while (0)
+    switch (nact) {
+        case 4: MOE_TILE(4); break;
+        case 3: MOE_TILE(3); break;
+        case 2: MOE_TILE(2); break;
+        case 1: MOE_TILE(1); break;
+        default: MOE_TILE(0); break;
+    }
+#undef MOE_TILE
+}
+
+// Weight gradients of the backward pass: for every expert e,
+//   C_e[m][n] = sum over the expert's K window of A[m][k] B[n][k],
+// A bf16 [M][ldk], B bf16 [N][ldk], C fp32 [E][M][N].  The K axis of A and
+// B holds every expert's kept rows (transposed by the backward pass): expert
+// e's window starts at kwin_start(offsets, e) and spans 2 Kp_e elements, Kp_e
+// its row count rounded up to 64 (the rows, zero padding, then the same for
+// the second operand of a hi/lo pair).  Work items are (expert, n tile, m
+// tile) over uniform row ranges (unit_offsets[e] = e M); an expert without
+// rows gets zeros.  The main loop, LDS layout and epilogue are those of
+// grouped_gemm_bf16<kPlain>.
+__global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_wgrad(
+    const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const int32_t *__restrict__ offsets,
+    const int32_t *__restrict__ unit_offsets, int E, int M, int N, int ldk, int ntiles_n, float *__restrict__ C) {
+    __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_b1[kTileBytes];
+    __shared__ __attribute__((aligned(1024))) char lds_b2[kTileBytes];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+
+    TileInfo ti;
+    if (!find_tile(unit_offsets, E, ntiles_n, kBM, 1, blockIdx.x, nullptr, nullptr, ti)) return;
+    const int e = ti.e;
+    const int rbeg = offsets[e], rows = offsets[e + 1] - rbeg;
+    const int kp = (rows + kBK - 1) / kBK * kBK;
+    const int kwin = kwin_start(rbeg, e);
+    const int nk = __builtin_amdgcn_readfirstlane(2 * kp / kBK);
+    const int m_rel = ti.m0 - e * M;
+    const int n0 = ti.nt * kBN;
+    const GemmOut out{C, nullptr, 0, nullptr};
+    if (nk == 0) {
+        // no rows: the tile of C_e is zero (16-byte stores, N a multiple of 64)
+        const int mv = min(kBM, M - m_rel), nv = min(kBN, N - n0);
+        for (int i = tid; i < mv * (kBN / 4); i += kGemmThreads) {
+            const int r = i / (kBN / 4), c = (i % (kBN / 4)) * 4;
+            if (c < nv)
+                *reinterpret_cast<float4 *>(C + (size_t)(ti.m0 + r) * N + n0 + c) = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+        return;
+    }
+
+    GemmThread g;
+    g.wave = wave;
+    g.a_valid = min(kBM, M - m_rel);
+    const int b_valid = min(kBN, N - n0);
+    // per-tile buffer resources at the tile's first row and the expert's
+    // window: 256 rows of ldk elements stay below 2 GiB (checked on the host)
+    g.a_rsrc = make_rsrc(A + (size_t)m_rel * ldk + kwin, (uint32_t)g.a_valid * ldk * 2);
+    g.b_rsrc = make_rsrc(B + (size_t)n0 * ldk + kwin, (uint32_t)b_valid * ldk * 2);
+#pragma unroll
+    for (int j = 0; j < kLoadsPerOperand; j++) {
+        const int grp = wave * kLoadsPerOperand + j;
+        const int row = grp * kRowsPerLoad + (lane >> 3);
+        const int c = (lane & 7) ^ swz(row);
+        g.a_off[j] = grp * kRowsPerLoad < g.a_valid ? ((uint32_t)min(row, g.a_valid - 1) * ldk + c * 8) * 2
+                                                     : kPastEnd;
+        g.b_off[j] = ((uint32_t)min(row, b_valid - 1) * ldk + c * 8) * 2;
+    }
+    const int l5 = lane & 31, hi = lane >> 5;
+    const int sw0 = swz(l5);
+#pragma unroll
+    for (int pp = 0; pp < 2; pp++)
+#pragma unroll
+        for (int ss = 0; ss < 4; ss++) {
+            const uint32_t sw = (uint32_t)(((2 * ss + hi) ^ sw0 ^ (4 * pp)) << 4);
+            g.fa[pp][ss] = (uint32_t)(wm * 128 + l5) * kRowBytes + sw;
+            g.fb[pp][ss] = (uint32_t)(wn * 128 + l5) * kRowBytes + sw;
+        }
+    const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, (g.a_valid - wm * 128 + 31) / 32)));
+#define MOE_TILE(n) run_tile<kPlain, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane, out)
     switch (nact) {
         case 4: MOE_TILE(4); break;
         case 3: MOE_TILE(3); break;
@@ -1248,12 +1341,12 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(x_perm), a_rows,
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
-                           offsets, E, dff, d, nt_up, 1, (uint32_t)a_bytes, claim, up);
+                           offsets, E, dff, d, d, nt_up, 1, (uint32_t)a_bytes, claim, up);
         if (mid && hipEventRecord(mid, st) != hipSuccess) return hipErrorLaunchFailure;
         hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
-                           offsets, E, d, dff, nt_dn, S, (uint32_t)0,
+                           offsets, E, d, dff, dff, nt_dn, S, (uint32_t)0,
                            claim ? claim + 8 : nullptr, down);
     } else {
         const int64_t mt = max_rows / kF32BM + E;
@@ -1282,8 +1375,47 @@ hipError_t launch_gate_up_raw(const moe_params &p, int64_t max_rows, int64_t cap
     const int nt_up = (int)ceil_div(p.d_ff, kBN / 2);
     hipLaunchKernelGGL(grouped_gemm_bf16<kGateUpRaw>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads), 0, st,
                        static_cast<const uint16_t *>(x), a_rows, static_cast<const uint16_t *>(w1),
-                       static_cast<const uint16_t *>(w3), offsets, p.E, p.d_ff, p.d, nt_up, 1, (uint32_t)a_bytes,
-                       (int32_t *)nullptr, GemmOut{a, b, 0, nullptr});
+                       static_cast<const uint16_t *>(w3), offsets, p.E, p.d_ff, p.d, p.d, nt_up, 1,
+                       (uint32_t)a_bytes, (int32_t *)nullptr, GemmOut{a, b, 0, nullptr});
+    return hipGetLastError();
+}
+
+int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb) {
+    const int64_t tiles = (max_rows / kBM + E) * ceil_div(N, kBN);
+    int s = 1;
+    while (K / s > ldb) s *= 2;  // each slice's K range lies within one period of B
+    while (s < 8 && tiles * s < 3 * 256 && (K / (2 * s)) % kBK == 0) s *= 2;
+    return s;
+}
+
+hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
+                             int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, int N, int K, int ldb,
+                             int S, float *C, float *rest, hipStream_t st) {
+    if (max_rows <= 0) return hipSuccess;
+    if (S < 1 || K % S != 0 || (K / S) % kBK != 0 || ldb % (K / S) != 0 || N % 64 != 0 ||
+        a_span_bytes >= ((int64_t)1 << 31) || (int64_t)N * ldb * 2 >= ((int64_t)1 << 32))
+        return hipErrorInvalidValue;
+    const int64_t mt = mtile_bound(max_rows, cap, E, kBM);
+    const int nt = (int)ceil_div(N, kBN);
+    hipLaunchKernelGGL(grouped_gemm_bf16<kPlain>, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A, a_rows,
+                       B, B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes, (int32_t *)nullptr,
+                       GemmOut{C, rest, (size_t)max_rows * N, nullptr});
+    if (S > 1) {
+        const int64_t n4 = max_rows * (N / 4);
+        const int grid = (int)std::min<int64_t>(ceil_div(n4, 256), 4096);
+        hipLaunchKernelGGL(ffn_fixup, dim3(grid), dim3(256), 0, st, C, rest, S - 1, (size_t)max_rows * N, offsets,
+                           E, N);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_wgrad_gemm(int E, const uint16_t *A, const uint16_t *B, const int32_t *offsets,
+                             const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st) {
+    if (E <= 0 || M <= 0 || N <= 0) return hipSuccess;
+    if (N % 64 != 0 || (int64_t)kBM * ldk * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
+    const int mt = (int)ceil_div(M, kBM), nt = (int)ceil_div(N, kBN);
+    hipLaunchKernelGGL(grouped_gemm_wgrad, dim3((unsigned)((int64_t)E * mt * nt)), dim3(kGemmThreads), 0, st, A, B,
+                       offsets, unit_offsets, E, M, N, ldk, nt, C);
     return hipGetLastError();
 }
 

@@ -128,6 +128,34 @@ hipError_t launch_gate_up_raw(const moe_params &p, int64_t max_rows, int64_t cap
                               const int32_t *a_rows, const int32_t *offsets, const void *w1, const void *w3,
                               float *a, float *b, hipStream_t st);
 
+// C = A B_e^T over the kept rows of every expert, bf16 operands, fp32
+// result (the backward pass's grouped GEMMs): A [rows][K] (the permuted
+// rows, or rows of a matrix spanning a_span_bytes < 2 GiB through a_rows),
+// B [E][N][ldb], C [max_rows][N].  K is cut into S slices (K / S a multiple
+// of 64 that divides ldb); slice s reads B at K position (s K / S) mod ldb,
+// so slices can share one B; slice s > 0 stores its partial product at
+// rest + (s - 1) max_rows N, and a fix-up adds the slices into C in order.
+int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb);
+hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
+                             int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, int N, int K, int ldb,
+                             int S, float *C, float *rest, hipStream_t st);
+
+// Per-expert K windows of the backward's transposed operands: the kept rows
+// of expert e (rows_e of them, from offsets[e]) become K positions
+// [kwin_start, kwin_start + 2 Kp_e) of a matrix with ldk columns, Kp_e =
+// rows_e rounded up to 64: the rows and zero padding, then the same for the
+// lo part of a hi/lo pair (or a second copy).  Windows of consecutive experts
+// never overlap, and all fit in backward_ldk(max_rows, E) columns.
+constexpr int kwin_start(int rbeg, int e) { return 2 * (((rbeg + 63) & ~63) + 64 * e); }
+constexpr int64_t backward_ldk(int64_t max_rows, int E) { return 2 * (((max_rows + 63) & ~(int64_t)63) + 64 * (int64_t)E); }
+
+// Weight gradients: C_e = A_e B_e^T over expert e's K window, A [M][ldk],
+// B [N][ldk] bf16, C fp32 [E][M][N] (zeros for an expert without rows);
+// unit_offsets[e] = e M (E + 1 ints).  256 rows of ldk elements must stay
+// below 2 GiB.
+hipError_t launch_wgrad_gemm(int E, const uint16_t *A, const uint16_t *B, const int32_t *offsets,
+                             const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st);
+
 // Backward pass of a bf16 layer: inputs, the forward's routing, gradients
 // (fp32) and the workspace buffers.
 struct BackwardArgs {
@@ -137,8 +165,18 @@ struct BackwardArgs {
     float *dx, *dlogits, *dw_router, *dbias, *dw1, *dw3, *dw2;
     float *gate_of_row, *ds_of_row, *dg;  // [R]
     float *a, *b, *u;                     // [R][d_ff]
-    uint16_t *da, *db, *hg;               // [2][R][d_ff] bf16: hi parts, then lo parts
+    uint16_t *acat;                       // [R][4 d_ff] bf16: da hi, db hi, da lo, db lo
+    uint16_t *hg;                         // [R][2 d_ff] bf16: (g h) hi, lo
     float *dx_perm;                       // [R][d]
+    float *dx_rest;                       // [S - 1][R][d]: the dx GEMM's other K slices
+    uint16_t *w2t;                        // [E][d_ff][d]: W2 transposed
+    uint16_t *w13t;                       // [E][d][2 d_ff]: W1^T | W3^T
+    uint16_t *dat;                        // [2 d_ff][ldk]: da^T then db^T, per-expert K windows (hi, lo)
+    uint16_t *xt, *dyt;                   // [d][ldk]: x^T, dy^T of the kept rows (twice per window)
+    uint16_t *hgt;                        // [d_ff][ldk]: (g h)^T (hi, lo)
+    int32_t *unit_offsets;                // [2][E + 1]: e 2 d_ff, then e d
+    int64_t ldk;
+    int dx_splits;
 };
 hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, const BackwardArgs &a,
                            hipStream_t st);
