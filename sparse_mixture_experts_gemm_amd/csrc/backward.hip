@@ -254,23 +254,54 @@ __global__ __launch_bounds__(256) void input_grad(const float *__restrict__ dx_p
     }
 }
 
-// dW_r[e][c] = sum over the rows r of expert e of ds_r x[tok_r][c] (row
-// order); block (e, column chunk of 256); dbias[e] = sum_r ds_r.
-__global__ __launch_bounds__(256) void router_wgrad(const uint16_t *__restrict__ x,
-                                                    const int32_t *__restrict__ token_of_row,
+// dW_r[e][c] = sum over the kept rows r of expert e of ds_r x[tok_r][c] and
+// dbias[e] = sum_r ds_r, from the kept rows' transposed x (xt, the expert's
+// K window: rows_e values then zero padding).  Block (e, 64 columns), a wave
+// per 16 columns: lane l accumulates window positions 8l .. 8l+7 of every
+// 512 in order, then a fixed butterfly over the lanes adds the partial sums.
+__global__ __launch_bounds__(256) void router_wgrad(const uint16_t *__restrict__ xt, int64_t ldk,
                                                     const float *__restrict__ ds_of_row,
-                                                    const int32_t *__restrict__ offsets, int d, int nchunk,
+                                                    const int32_t *__restrict__ offsets, int d,
                                                     float *__restrict__ dwr, float *__restrict__ dbias) {
-    const int e = blockIdx.x / nchunk, c = (blockIdx.x % nchunk) * 256 + threadIdx.x;
-    const int rb = offsets[e], re = offsets[e + 1];
-    float acc = 0.0f, sb = 0.0f;
-    for (int r = rb; r < re; r++) {
-        const float ds = ds_of_row[r];
-        sb += ds;
-        if (c < d) acc = fmaf(ds, bf16_bits_to_f32(x[(size_t)token_of_row[r] * d + c]), acc);
+    const int nc = d / 64;
+    const int e = blockIdx.x / nc, c0 = (blockIdx.x % nc) * 64 + (threadIdx.x >> 6) * 16;
+    const int lane = threadIdx.x & 63;
+    const int rbeg = offsets[e], rows = offsets[e + 1] - rbeg;
+    const int kp = (rows + 63) & ~63;
+    const uint16_t *xw = xt + kwin_start(rbeg, e);
+    float acc[16], sb = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 16; c++) acc[c] = 0.0f;
+    for (int j0 = lane * 8; j0 < kp; j0 += 512) {
+        float ds[8];
+#pragma unroll
+        for (int i = 0; i < 8; i++) ds[i] = j0 + i < rows ? ds_of_row[rbeg + j0 + i] : 0.0f;
+#pragma unroll
+        for (int i = 0; i < 8; i++) sb += ds[i];
+#pragma unroll
+        for (int c = 0; c < 16; c++) {
+            const uint4 v = *reinterpret_cast<const uint4 *>(xw + (size_t)(c0 + c) * ldk + j0);
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                acc[c] = fmaf(ds[2 * i], bf16_bits_to_f32(w[i] & 0xFFFF), acc[c]);
+                acc[c] = fmaf(ds[2 * i + 1], bf16_bits_to_f32(w[i] >> 16), acc[c]);
+            }
+        }
     }
-    if (c < d) dwr[(size_t)e * d + c] = acc;
-    if (blockIdx.x % nchunk == 0 && threadIdx.x == 0) dbias[e] = sb;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+#pragma unroll
+        for (int c = 0; c < 16; c++) acc[c] += __shfl_xor(acc[c], off, 64);
+        sb += __shfl_xor(sb, off, 64);
+    }
+    if (lane < 16) {
+        float v = acc[0];
+#pragma unroll
+        for (int c = 1; c < 16; c++) v = lane == c ? acc[c] : v;
+        dwr[(size_t)e * d + c0 + lane] = v;
+    }
+    if (blockIdx.x % nc == 0 && threadIdx.x == 0) dbias[e] = sb;
 }
 
 }  // namespace
@@ -280,7 +311,6 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     const int64_t R = max_rows;
     const uint16_t *x = static_cast<const uint16_t *>(a.x);
     const uint16_t *dy = static_cast<const uint16_t *>(a.dy);
-    const int nchunk = (int)ceil_div(d, 256);
     if (T == 0 || R == 0) {
         // no kept rows: every weight gradient is zero
         const size_t nw = (size_t)E * dff * d;
@@ -295,8 +325,8 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
             hipLaunchKernelGGL(fill_zero, dim3((unsigned)std::min<int64_t>(ceil_div((int64_t)T * d, 256), 8192)),
                                dim3(256), 0, st, a.dx, (size_t)T * d);
         }
-        hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * nchunk)), dim3(256), 0, st, x, a.token_of_row,
-                           a.ds_of_row, a.offsets, d, nchunk, a.dw_router, a.dbias);
+        hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * (d / 64))), dim3(256), 0, st, a.xt, a.ldk,
+                           a.ds_of_row, a.offsets, d, a.dw_router, a.dbias);
         return hipGetLastError();
     }
     const float inv_tau = 1.0f / (p.gate_temperature > 0.0f ? p.gate_temperature : 1.0f);
@@ -357,8 +387,8 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     e = launch_wgrad_gemm(E, a.dyt, a.hgt, a.offsets, uo_d, d, dff, (int)ldk, a.dw2, st);
     if (e != hipSuccess) return e;
     // 9. router weight and bias gradients
-    hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * nchunk)), dim3(256), 0, st, x, a.token_of_row,
-                       a.ds_of_row, a.offsets, d, nchunk, a.dw_router, a.dbias);
+    hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * (d / 64))), dim3(256), 0, st, a.xt, ldk, a.ds_of_row,
+                       a.offsets, d, a.dw_router, a.dbias);
     return hipGetLastError();
 }
 
