@@ -141,9 +141,10 @@ def main():
     fp8 = None
     qfmt = "int8" if args.int8_weights else "e4m3" if args.fp8_weights else None
     if qfmt:
-        if not (p.dtype == moe.MOE_BF16 and moe.capacity(p) <= 32 and d % 128 == 0 and cfg.d_ff % 128 == 0):
-            print(f"bench.py: one-byte weights need a bf16 layer with capacity <= 32 and d, d_ff multiples of 128; "
-                  f"{cfg.name} has capacity {moe.capacity(p)}", file=sys.stderr)
+        small = moe.capacity(p) <= 32
+        if not (p.dtype == moe.MOE_BF16 and (not small or (d % 128 == 0 and cfg.d_ff % 128 == 0))):
+            print(f"bench.py: one-byte weights need a bf16 layer (with d, d_ff multiples of 128 when every expert "
+                  f"holds at most 32 rows); {cfg.name} is {cfg.dtype}", file=sys.stderr)
             sys.exit(2)
         fp8 = {"fmt": qfmt}
         quant = moe_synth.quantize_rows_int8 if qfmt == "int8" else moe_synth.quantize_rows_e4m3
@@ -267,7 +268,7 @@ def main():
     else:
         achieved_ms = None
 
-    if args.workload == "decode" or fp8:
+    if args.workload == "decode" or (fp8 and moe.capacity(p) <= 32):
         # weight streaming: the expert weights' bytes against HBM bandwidth.  With
         # one-byte weights there is no events variant; the whole step bounds it.
         t = achieved_ms if achieved_ms is not None else ms_per_step
@@ -278,11 +279,15 @@ def main():
                     "traffic": traffic.get("expert_ffn"),
                     "per_launch_work": f"{work['gemm_weight_bytes']} weight bytes ({active} active experts x 3 x d x d_ff)"}
     else:
-        tf = work["gemm_flops"] / (achieved_ms * 1e-3) / 1e12
+        # one-byte weights on the matrix-core tile: no events variant, so the
+        # whole step bounds the GEMM's time (an underestimate of its rate)
+        t = achieved_ms if achieved_ms is not None else ms_per_step
+        tf = work["gemm_flops"] / (t * 1e-3) / 1e12
         # bf16 layers multiply on the matrix cores; the fp32 layer's GEMM is a
         # vector-ALU kernel, priced against the fp32 vector peak
         bound, peak = ("mfma", PEAK_MFMA_TFLOPS) if cfg.dtype == "bf16" else ("alu", PEAK_F32_TFLOPS)
-        roofline = {"kernel": "expert grouped GEMM, gate-up + down launches of moe_forward",
+        roofline = {"kernel": "expert grouped GEMM, gate-up + down launches of moe_forward"
+                              + (f" ({fp8['fmt']} weights; timed over the whole step)" if fp8 else ""),
                     "bound": bound, "achieved": tf, "peak": peak, "unit": "TFLOP/s",
                     "frac": tf / peak, "traffic": traffic.get("expert_ffn"),
                     "per_launch_work": f"{work['gemm_flops']:.4g} flop ({rows} kept rows x 6 x d x d_ff)"}

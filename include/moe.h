@@ -296,11 +296,15 @@ int moe_forward_events(const moe_params *p, const void *x, const void *w_router,
  *   q1, q3 [E][d_ff][d] bytes, s1, s3 [E][d_ff] fp32; q2 [E][d][d_ff] bytes,
  *   s2 [E][d] fp32; q pointers 16-byte aligned, scales 4-byte aligned.
  * The activations are as for the bf16 layer (x_perm bf16, h fp16, y_perm
- * [R][d] fp32; the scaled weights are not narrowed).  Built for the
- * weight-streaming (decode) regime:
- * dtype MOE_BF16, capacity C = moe_capacity(p) <= 32, d and d_ff multiples
- * of 128; other layers get MOE_ERR_UNSUPPORTED.  Otherwise as moe_expert_ffn
- * (the down projection is never split, so no workspace is needed).
+ * [R][d] fp32); the codes are widened exactly (to bf16 for W1/W3, to fp16
+ * for W2) and the scales multiply the fp32 accumulators, so the weights are
+ * not narrowed.  dtype MOE_BF16 only (else MOE_ERR_UNSUPPORTED).  Layers
+ * whose experts hold at most 32 rows (capacity C = moe_capacity(p) <= 32)
+ * run the weight-streaming kernel and need d and d_ff to be multiples of
+ * 128; larger groups run the 256 x 256 matrix-core tile (d and d_ff
+ * multiples of 64).  Otherwise as moe_expert_ffn, except that the down
+ * projection is computed in one K slice here, so no workspace is needed
+ * (moe_forward_fp8 splits it like moe_forward).
  */
 int moe_expert_ffn_fp8(const moe_params *p, const void *x_perm, const int32_t *offsets,
                        const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,

@@ -55,12 +55,42 @@ constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (
 // b = x W3^T in fp32 instead of silu(a) * b (the backward pass needs them).
 // kPlain: one bf16 x bf16 product C = A B^T stored in fp32 (the backward
 // pass's GEMMs, K-split like the down projection).
-enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2, kPlain = 3 };
+// kGateUpE4M3 / kDownE4M3, kGateUpI8 / kDownI8: kGateUp / kDown with
+// one-byte weight codes (OCP E4M3 or INT8) and one fp32 scale per weight
+// row: the B tile holds the codes (64-byte rows), the fragments are widened
+// exactly in registers, and the row scales multiply the fp32 accumulators
+// in the epilogue (a weight row's scale factors out of its dot products).
+enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2, kPlain = 3, kGateUpE4M3 = 4, kDownE4M3 = 5, kGateUpI8 = 6,
+       kDownI8 = 7 };
 
+// one-byte weight codes: OCP E4M3 or INT8
+enum { kQE4M3 = 0, kQInt8 = 1 };
+
+template <int MODE>
+__device__ __forceinline__ constexpr bool q_mode() { return MODE >= kGateUpE4M3; }
+template <int MODE>
+__device__ __forceinline__ constexpr int q_fmt() { return MODE >= kGateUpI8 ? kQInt8 : kQE4M3; }
+// The SwiGLU epilogue (h = silu(a) * b, fp16)
+template <int MODE>
+__device__ __forceinline__ constexpr bool gate_up() { return MODE == kGateUp || MODE == kGateUpE4M3 || MODE == kGateUpI8; }
 // The B tile is 128 rows of W1 and the same 128 rows of W3 (gate-up modes),
 // or 256 rows of one matrix.
 template <int MODE>
-__device__ __forceinline__ constexpr bool two_b() { return MODE == kGateUp || MODE == kGateUpRaw; }
+__device__ __forceinline__ constexpr bool two_b() { return gate_up<MODE>() || MODE == kGateUpRaw; }
+// The down projection: A = h (fp16), fp16 matrix cores
+template <int MODE>
+__device__ __forceinline__ constexpr bool down_mode() { return MODE == kDown || MODE == kDownE4M3 || MODE == kDownI8; }
+// Bytes of one B tile row (64 K elements) in LDS, and this wave's B loads
+// of 1 KiB per K step
+template <int MODE>
+__device__ __forceinline__ constexpr int b_row_bytes() { return q_mode<MODE>() ? 64 : 128; }
+template <int MODE>
+__device__ __forceinline__ constexpr int b_loads() { return q_mode<MODE>() ? 4 : 8; }
+// Chunk swizzle of a 64-byte B row of codes (four 16-byte chunks): a
+// fragment read takes 8 bytes of one chunk from 32 consecutive rows, which
+// this spreads over 16 of the four chunk positions x four rows' bank
+// groups (two lanes per bank pair)
+__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
 
 
 template <typename T>
@@ -91,6 +121,38 @@ __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
 __device__ __forceinline__ uint16_t f32_to_f16_sat(float v) {
     v = fminf(fmaxf(v, -65504.0f), 65504.0f);
     return __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// eight INT8 values (two's complement) -> eight bf16 (gate-up) or fp16
+// (down), element i from byte i: sign-extended, converted to fp32 and packed.
+// Every value in [-128, 127] is exact in both types; for bf16 the fp32 bits
+// of such an integer end in 16 zero bits, so the upper halves are packed.
+template <bool F16>
+__device__ __forceinline__ uint32_t i8x2_widen(uint32_t w, int byte0) {
+    const float a = (float)(int32_t)__builtin_amdgcn_sbfe(w, 8 * byte0, 8),
+                b = (float)(int32_t)__builtin_amdgcn_sbfe(w, 8 * byte0 + 8, 8);
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    else return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+// eight one-byte codes -> eight bf16 (gate-up) or fp16 (down), element i
+// from byte i
+template <bool F16, int FMT = kQE4M3>
+__device__ __forceinline__ uint4 fp8x8_widen(uint2 q) {
+    if constexpr (FMT == kQInt8) {
+        return make_uint4(i8x2_widen<F16>(q.x, 0), i8x2_widen<F16>(q.x, 2), i8x2_widen<F16>(q.y, 0),
+                          i8x2_widen<F16>(q.y, 2));
+    } else if constexpr (F16) {
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.y, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.y, 1.0f, true)));
+    } else {
+        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false)),
+                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true)));
+    }
 }
 
 // One MFMA step on 8-element fragments held as raw 16-byte words.
@@ -154,8 +216,8 @@ struct GemmThread {
 
 template <int MODE>
 __device__ __forceinline__ int b_imm(int jn) {
-    if (two_b<MODE>()) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * kRowBytes;
-    return jn * 32 * kRowBytes;
+    if (two_b<MODE>()) return ((jn < 2 ? 0 : kBN / 2) + (jn & 1) * 32) * b_row_bytes<MODE>();
+    return jn * 32 * b_row_bytes<MODE>();
 }
 
 // Issue this wave's global -> LDS loads of one operand (HALF 0: A, 1: B) of
@@ -164,13 +226,22 @@ __device__ __forceinline__ int b_imm(int jn) {
 // groups wholly past it carry an offset beyond the buffer extent, so their
 // loads fetch nothing and write zeros (those LDS rows feed only discarded
 // outputs), with no branch in the loop.
-template <int HALF>
+template <int MODE, int HALF>
 __device__ __forceinline__ void issue_loads(const GemmThread &g, char *buf, uint32_t kb) {
+    if (HALF == 0 || !q_mode<MODE>()) {
 #pragma unroll
-    for (int j = 0; j < kLoadsPerOperand; j++) {
-        const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group
-        if (HALF == 0) buf2lds16(g.a_rsrc, g.a_off[j], kb, buf + grp * 1024);
-        else buf2lds16(g.b_rsrc, g.b_off[j], kb, buf + grp * 1024);
+        for (int j = 0; j < kLoadsPerOperand; j++) {
+            const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group
+            if (HALF == 0) buf2lds16(g.a_rsrc, g.a_off[j], kb, buf + grp * 1024);
+            else buf2lds16(g.b_rsrc, g.b_off[j], kb, buf + grp * 1024);
+        }
+    } else {
+        // one-byte codes: 16-row groups of 64-byte rows, the K step is 64 bytes
+#pragma unroll
+        for (int j = 0; j < b_loads<MODE>(); j++) {
+            const int grp = g.wave * b_loads<MODE>() + j;
+            buf2lds16(g.b_rsrc, g.b_off[j], kb >> 1, buf + grp * 1024);
+        }
     }
 }
 
@@ -186,15 +257,28 @@ __device__ __forceinline__ void load_frags(const GemmThread &g, const char *abuf
 #pragma unroll
     for (int i = 0; i < 4; i++) f.a[i] = lds_read16(abuf + g.fa[i & 1][ss] + i * 32 * kRowBytes);
 #pragma unroll
-    for (int jn = 0; jn < 4; jn++) f.b[jn] = lds_read16(bbuf + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
+    for (int jn = 0; jn < 4; jn++) {
+        if constexpr (q_mode<MODE>()) {
+            // eight codes, widened after the read has landed (widen_b)
+            const uint2 v = *reinterpret_cast<const uint2 *>(bbuf + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
+            f.b[jn] = make_uint4(v.x, v.y, 0u, 0u);
+        } else {
+            f.b[jn] = lds_read16(bbuf + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
+        }
+    }
 }
 
-// Down GEMM: W2 fragments (bf16) widened to fp16 for the fp16 MFMA.
+// Down GEMM: W2 fragments (bf16) widened to fp16 for the fp16 MFMA; one-byte
+// codes widened exactly to bf16 (gate-up) or fp16 (down).
 template <int MODE>
 __device__ __forceinline__ void widen_b(Frags &f) {
-    if (MODE == kDown) {
+    if constexpr (MODE == kDown) {
 #pragma unroll
         for (int jn = 0; jn < 4; jn++) f.b[jn] = bf16x8_to_f16x8(f.b[jn]);
+    } else if constexpr (q_mode<MODE>()) {
+#pragma unroll
+        for (int jn = 0; jn < 4; jn++)
+            f.b[jn] = fp8x8_widen<down_mode<MODE>(), q_fmt<MODE>()>(make_uint2(f.b[jn].x, f.b[jn].y));
     }
 }
 
@@ -211,7 +295,7 @@ __device__ __forceinline__ void zero_a_if(bool pad, Frags &f) {
 // straight-line.
 template <int MODE, int NACT, int I0, int I1>
 __device__ __forceinline__ void mfma_blocks(const Frags &f, f32x16_t (&acc)[4][4]) {
-    constexpr bool kF16 = MODE == kDown;
+    constexpr bool kF16 = down_mode<MODE>();
 #pragma unroll
     for (int i = I0; i < (I1 < NACT ? I1 : NACT); i++) {
 #pragma unroll
@@ -245,6 +329,7 @@ __device__ __forceinline__ void sched_half() {
             if (HALF == 0) SCHED_DSR(1);
             if (HALF == 1 && LOADS) SCHED_VMEM(1);
             if (HALF == 1 && MODE == kDown) SCHED_VALU(6);
+            if (HALF == 1 && q_mode<MODE>()) SCHED_VALU(q_fmt<MODE>() == kQInt8 ? 6 : 2);
         }
     }
 }
@@ -258,8 +343,8 @@ __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, c
     sched_half<MODE, NACT, 0, false>();
     __builtin_amdgcn_sched_barrier(0);
     if (LOADS_HALF1) {
-        if (ld_operand == 0) issue_loads<0>(g, ld_buf, kb);
-        else issue_loads<1>(g, ld_buf, kb);
+        if (ld_operand == 0) issue_loads<MODE, 0>(g, ld_buf, kb);
+        else issue_loads<MODE, 1>(g, ld_buf, kb);
     }
     widen_b<MODE>(nextf);
     mfma_blocks<MODE, NACT, 2, 4>(f, acc);
@@ -272,7 +357,7 @@ __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, c
 // before its use); two for the down GEMM, which has no registers to spare
 // for the addresses of a third.
 template <int MODE>
-__device__ __forceinline__ constexpr int b_buffers() { return MODE != kDown ? 3 : 2; }
+__device__ __forceinline__ constexpr int b_buffers() { return down_mode<MODE>() ? 2 : 3; }
 
 // One K step (4 sub-steps of 16) on the A buffer `ca` and B buffer `cb`.
 // LDS holds two A buffers and NB B buffers (distinct objects, so the compiler
@@ -302,7 +387,7 @@ __device__ __forceinline__ void kstep(const GemmThread &g, char *ca, char *cb, c
     substep<MODE, NACT, false>(g, ca, cb, 2, f0, f1, nullptr, 0, 0, acc);
     if (MAYBE_PAD) zero_a_if(pad, f0);
     substep<MODE, NACT, false>(g, ca, cb, 3, f1, f0, nullptr, 0, 0, acc);
-    WAIT_VMCNT_LGKM0(kRing ? kLoadsPerOperand : 0);
+    WAIT_VMCNT_LGKM0(kRing ? b_loads<MODE>() : 0);
     block_sync();
     __builtin_amdgcn_sched_barrier(0);
     if (MAYBE_PAD) zero_a_if(pad, f1);
@@ -332,15 +417,15 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *a0, char *a
                                           int nk, f32x16_t (&acc)[4][4]) {
     constexpr int NB = b_buffers<MODE>();
     auto kb = [nk](int k) -> uint32_t { return (uint32_t)min(k, nk - 1) * kRowBytes; };
-    issue_loads<0>(g, a0, kb(0));
-    issue_loads<1>(g, b0, kb(0));
-    if (NB == 3) issue_loads<1>(g, b1, kb(1));
-    WAIT_VMCNT(NB == 3 ? kLoadsPerOperand : 0);
+    issue_loads<MODE, 0>(g, a0, kb(0));
+    issue_loads<MODE, 1>(g, b0, kb(0));
+    if (NB == 3) issue_loads<MODE, 1>(g, b1, kb(1));
+    WAIT_VMCNT(NB == 3 ? b_loads<MODE>() : 0);
     block_sync();
     Frags f0;
     load_frags<MODE>(g, a0, b0, 0, f0);
     widen_b<MODE>(f0);
-    issue_loads<0>(g, a1, kb(1));
+    issue_loads<MODE, 0>(g, a1, kb(1));
 #define MOE_KSTEP(I, K) kstep_at<MODE, NACT, I>(g, a0, a1, b0, b1, b2, kb((K) + 1), kb((K) + 2), false, f0, acc)
     if constexpr (NB == 3) {
         const int nk6 = nk - nk % 6;
@@ -389,12 +474,25 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *a0, char *a
 // 128-byte row segment.  Only the wave's own LDS region is touched, so no
 // barrier is needed between the LDS writes and reads.
 // Down: fp32 partial products, 32 lanes store one 128-byte row segment.
+// One-byte weights: the accumulators of weight row n are multiplied by its
+// scale (sc0 for W1 or W2 rows, sc1 for W3 rows; [E][N]) first.
 template <int MODE, int NACT>
 __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, int wm, int wn, int lane,
-                                           const GemmOut &out, const f32x16_t (&acc)[4][4], char *w) {
+                                           const GemmOut &out, const float *sc0, const float *sc1,
+                                           const f32x16_t (&acc)[4][4], char *w) {
     const int l5 = lane & 31, hi = lane >> 5;
-    if (MODE == kGateUp) {
+    if (gate_up<MODE>()) {
         uint16_t *out_h = static_cast<uint16_t *>(out.y0);
+        // the scales of this lane's two h columns (W1 rows and W3 rows)
+        float s1c[2] = {1.0f, 1.0f}, s3c[2] = {1.0f, 1.0f};
+        if constexpr (q_mode<MODE>()) {
+#pragma unroll
+            for (int jn = 0; jn < 2; jn++) {
+                const size_t col = (size_t)ti.e * N + min(n0 + wn * 64 + jn * 32 + l5, N - 1);
+                s1c[jn] = sc0[col];
+                s3c[jn] = sc1[col];
+            }
+        }
 #pragma unroll
         for (int i = 0; i < NACT; i++)
 #pragma unroll
@@ -404,8 +502,10 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
                     const int row = i * 32 + 8 * (q >> 2) + 4 * hi + (q & 3);
                     const int col = jn * 32 + l5;
                     const int chunk = (col >> 3) ^ (row & 7);
+                    const float av = q_mode<MODE>() ? acc[i][jn][q] * s1c[jn] : acc[i][jn][q];
+                    const float bv = q_mode<MODE>() ? acc[i][jn + 2][q] * s3c[jn] : acc[i][jn + 2][q];
                     *reinterpret_cast<uint16_t *>(w + row * kRowBytes + chunk * 16 + (col & 7) * 2) =
-                        f32_to_f16_sat(silu_mul(acc[i][jn][q], acc[i][jn + 2][q]));
+                        f32_to_f16_sat(silu_mul(av, bv));
                     // one 16-value block at a time keeps the live register set small
                     if (q == 15) __builtin_amdgcn_sched_barrier(0);
                 }
@@ -455,6 +555,12 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
         // row gates, 8-byte stores of the fp16 gated values
         const int cb = n0 + wn * 128;  // first column of this wave's block (N is a multiple of 64)
         const bool gated = out.row_gate != nullptr;
+        // one-byte weights: the scales of this lane's four output columns
+        float s2c[4] = {1.0f, 1.0f, 1.0f, 1.0f};
+        if constexpr (q_mode<MODE>()) {
+#pragma unroll
+            for (int jn = 0; jn < 4; jn++) s2c[jn] = sc0[(size_t)ti.e * N + min(cb + jn * 32 + l5, N - 1)];
+        }
         // gates of the wave's 128 rows: row l of the wave in g_lo of lane l,
         // row 64 + l in g_hi (rows past the expert's end read its last row)
         float g_lo = 0.0f, g_hi = 0.0f;
@@ -472,7 +578,8 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
                     const int row = 8 * (q >> 2) + 4 * hi + (q & 3);
                     const int col = jn * 32 + l5;
                     const int chunk = (col >> 2) ^ (((row >> 2) & 1) << 3);
-                    *reinterpret_cast<float *>(w + row * 512 + chunk * 16 + (col & 3) * 4) = acc[i][jn][q];
+                    *reinterpret_cast<float *>(w + row * 512 + chunk * 16 + (col & 3) * 4) =
+                        q_mode<MODE>() ? acc[i][jn][q] * s2c[jn] : acc[i][jn][q];
                 }
 #pragma unroll
             for (int rd = 0; rd < 16; rd++) {
@@ -503,7 +610,7 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
 template <int MODE, int NACT, bool ODD>
 __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti, char *a0, char *a1, char *b0,
                                          char *b1, char *b2, int nk, int n0, int N, int wm, int wn, int lane,
-                                         const GemmOut &out) {
+                                         const GemmOut &out, const float *sc0 = nullptr, const float *sc1 = nullptr) {
     f32x16_t acc[4][4];
 #pragma unroll
     for (int i = 0; i < 4; i++)
@@ -516,7 +623,7 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
     // wave before the epilogue reuses the A buffers (16 KiB per wave)
     WAIT_VM_LGKM0();
     block_sync();
-    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, out, acc,
+    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, out, sc0, sc1, acc,
                            (g.wave < 2 ? a0 : a1) + (g.wave & 1) * (kTileBytes / 2));
 }
 
@@ -545,7 +652,8 @@ template <int MODE>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ldb,
-    int ntiles_n, int splits, uint32_t a_bytes, int32_t *claim, GemmOut out) {
+    int ntiles_n, int splits, uint32_t a_bytes, int32_t *claim, GemmOut out, const float *__restrict__ S0 = nullptr,
+    const float *__restrict__ S1 = nullptr) {
     __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
@@ -560,7 +668,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti))
         return;
     const int n0 = two_b<MODE>() ? ti.nt * (kBN / 2) : ti.nt * kBN;
-    const size_t wexp = (size_t)ti.e * N * ldb;
+    // bytes per weight element: 2 (bf16) or 1 (one-byte codes)
+    constexpr int kWb = q_mode<MODE>() ? 1 : 2;
+    const size_t wexp = (size_t)ti.e * N * ldb * kWb;
     const int ks = K / splits;              // K elements of this split
     const int k_first = ti.split * ks;      // first K element of this split
 
@@ -573,9 +683,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     // (below 4 GiB, also checked).
     g.a_rsrc = a_rows ? make_rsrc(A, a_bytes)
                       : make_rsrc(A + (size_t)ti.m0 * K, (uint32_t)(g.a_valid < kBM ? g.a_valid : kBM) * K * 2);
-    const uint32_t w_bytes = (uint32_t)((size_t)N * ldb * 2);
+    const uint32_t w_bytes = (uint32_t)((size_t)N * ldb * kWb);
     // gate-up: waves 0-1 load B rows 0..127 (W1), waves 2-3 rows 128..255 (W3)
-    g.b_rsrc = make_rsrc((two_b<MODE>() && wave >= 2 ? B1 : B0) + wexp, w_bytes);
+    g.b_rsrc = make_rsrc(reinterpret_cast<const char *>(two_b<MODE>() && wave >= 2 ? B1 : B0) + wexp, w_bytes);
     // B's K position of this split: B rows of ldb elements, read periodically
     // when the splits of A's K range share one B (ldb < K, a multiple of ks)
     const int kb_first = k_first % ldb;
@@ -587,9 +697,25 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         const int gm = min(ti.m0 + row, ti.mend - 1);
         const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
         g.a_off[j] = grp * kRowsPerLoad < g.a_valid ? ((uint32_t)ar * K + k_first + c * 8) * 2 : kPastEnd;
-        int gn = two_b<MODE>() ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
-        gn = min(gn, N - 1);
-        g.b_off[j] = ((uint32_t)gn * ldb + kb_first + c * 8) * 2;
+        if constexpr (!q_mode<MODE>()) {
+            int gn = two_b<MODE>() ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
+            gn = min(gn, N - 1);
+            g.b_off[j] = ((uint32_t)gn * ldb + kb_first + c * 8) * 2;
+        }
+    }
+    if constexpr (q_mode<MODE>()) {
+        // one-byte codes: wave w loads 16-row groups 4w .. 4w+3 of 64-byte
+        // rows; lane l takes row 16g + l/4 and the logical 16-byte chunk that
+        // lands at position l%4
+#pragma unroll
+        for (int j = 0; j < b_loads<MODE>(); j++) {
+            const int grp = wave * b_loads<MODE>() + j;
+            const int row = grp * 16 + (lane >> 2);
+            const int c = (lane & 3) ^ swz4(row);
+            int gn = two_b<MODE>() ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
+            gn = min(gn, N - 1);
+            g.b_off[j] = (uint32_t)gn * ldb + kb_first + c * 16;
+        }
     }
     const int l5 = lane & 31, hi = lane >> 5;
     const int sw0 = swz(l5);  // swizzle of row base + l5 is sw0 ^ 4 * parity(base / 32)
@@ -600,7 +726,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         for (int ss = 0; ss < 4; ss++) {
             const uint32_t sw = (uint32_t)(((2 * ss + hi) ^ sw0 ^ (4 * pp)) << 4);
             g.fa[pp][ss] = (uint32_t)(wm * 128 + l5) * kRowBytes + sw;
-            g.fb[pp][ss] = (uint32_t)(b_rbase + l5) * kRowBytes + sw;
+            // one-byte codes: 8 bytes (the lane's 8 K values) of logical chunk
+            // ss; row base + l5 has swizzle swz4(l5) for any base % 32 == 0
+            g.fb[pp][ss] = q_mode<MODE>() ? (uint32_t)(b_rbase + l5) * 64 + ((ss ^ swz4(l5)) << 4) + hi * 8
+                                          : (uint32_t)(b_rbase + l5) * kRowBytes + sw;
         }
     // active 32-row blocks of this wave (uniform)
     const int nact_raw = (ti.mend - (ti.m0 + wm * 128) + 31) / 32;
@@ -611,10 +740,10 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     do {                                                                                                         \
         if (b_buffers<MODE>() == 2 && (nk & 1))                                                                  \
             run_tile<MODE, n, b_buffers<MODE>() == 2>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N,  \
-                                                      wm, wn, lane, out);                                        \
+                                                      wm, wn, lane, out, S0, S1);                                \
         else                                                                                                     \
             run_tile<MODE, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane,     \
-                                     out);                                                                       \
+                                     out, S0, S1);                                                               \
     } while (0)
     switch (nact) {
         case 4: MOE_TILE(4); break;
@@ -964,40 +1093,6 @@ __device__ __forceinline__ void sk8_issue(const Sk8Thread &g, char *stage, int k
     }
 }
 
-// eight INT8 values (two's complement) -> eight bf16 (gate-up) or fp16
-// (down), element i from byte i: sign-extended, converted to fp32 and packed.
-// Every value in [-128, 127] is exact in both types; for bf16 the fp32 bits
-// of such an integer end in 16 zero bits, so the upper halves are packed.
-template <bool F16>
-__device__ __forceinline__ uint32_t i8x2_widen(uint32_t w, int byte0) {
-    const float a = (float)(int32_t)__builtin_amdgcn_sbfe(w, 8 * byte0, 8),
-                b = (float)(int32_t)__builtin_amdgcn_sbfe(w, 8 * byte0 + 8, 8);
-    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
-    else return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
-}
-
-// one-byte weight codes: OCP E4M3 or INT8
-enum { kQE4M3 = 0, kQInt8 = 1 };
-
-// eight one-byte codes -> eight bf16 (gate-up) or fp16 (down), element i
-// from byte i
-template <bool F16, int FMT = kQE4M3>
-__device__ __forceinline__ uint4 fp8x8_widen(uint2 q) {
-    if constexpr (FMT == kQInt8) {
-        return make_uint4(i8x2_widen<F16>(q.x, 0), i8x2_widen<F16>(q.x, 2), i8x2_widen<F16>(q.y, 0),
-                          i8x2_widen<F16>(q.y, 2));
-    } else if constexpr (F16) {
-        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, false)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.x, 1.0f, true)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.y, 1.0f, false)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(q.y, 1.0f, true)));
-    } else {
-        return make_uint4(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, false)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.x, 1.0f, true)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, false)),
-                          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(q.y, 1.0f, true)));
-    }
-}
 
 template <int MODE, int NB, int FMT>
 __device__ __forceinline__ void sk8_compute(const char *stage, int wave, int lane, f32x4_t (&acc)[2][2]) {
@@ -1247,7 +1342,8 @@ static int64_t mtile_bound(int64_t max_rows, int64_t cap, int E, int bm) {
 }
 
 bool fp8_ffn_supported(const moe_params &p) {
-    return p.dtype == MOE_BF16 && capacity_rows(p) <= kSkBM && p.d % kSk8K == 0 && p.d_ff % kSk8K == 0;
+    // the weight-streaming kernel (at most 32 rows per expert) steps K by 128
+    return p.dtype == MOE_BF16 && (capacity_rows(p) > kSkBM || (p.d % kSk8K == 0 && p.d_ff % kSk8K == 0));
 }
 
 namespace {
@@ -1291,18 +1387,53 @@ static void launch_q8(const moe_params &p, int64_t mt, const void *x_perm, const
                        dff, nt_dn, down);
 }
 
+// One-byte weights on the 256 x 256 MFMA tile (groups of more than 32 rows).
+template <int GU, int DN>
+static void launch_q8_mfma(const moe_params &p, int64_t mt, const void *x_perm, const int32_t *a_rows,
+                           int64_t a_bytes, const int32_t *offsets, const uint8_t *w1, const float *s1,
+                           const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
+                           const GemmOut &down, int splits, int32_t *claim, hipEvent_t mid, hipError_t &ev,
+                           hipStream_t st) {
+    const int E = p.E, d = p.d, dff = p.d_ff;
+    const int nt_up = (int)ceil_div(dff, kBN / 2);
+    const int nt_dn = (int)ceil_div(d, kBN);
+    hipLaunchKernelGGL(grouped_gemm_bf16<GU>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads), 0, st,
+                       static_cast<const uint16_t *>(x_perm), a_rows, reinterpret_cast<const uint16_t *>(w1),
+                       reinterpret_cast<const uint16_t *>(w3), offsets, E, dff, d, d, nt_up, 1, (uint32_t)a_bytes,
+                       claim, GemmOut{h, nullptr, 0, nullptr}, s1, s3);
+    if (mid) ev = hipEventRecord(mid, st);
+    hipLaunchKernelGGL(grouped_gemm_bf16<DN>, dim3((unsigned)(mt * nt_dn * splits)), dim3(kGemmThreads), 0, st,
+                       static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
+                       reinterpret_cast<const uint16_t *>(w2), reinterpret_cast<const uint16_t *>(w2), offsets, E,
+                       d, dff, dff, nt_dn, splits, (uint32_t)0, claim ? claim + 8 : nullptr, down, s2, s2);
+}
+
 hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                                  const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
                                  const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
-                                 const GemmOut &down, hipEvent_t mid, int qfmt, hipStream_t st) {
+                                 const GemmOut &down, int splits, int32_t *claim, hipEvent_t mid, int qfmt,
+                                 hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
-    if (p.dtype != MOE_BF16 || cap > kSkBM || p.d % kSk8K != 0 || p.d_ff % kSk8K != 0) return hipErrorInvalidValue;
-    const int64_t mt = mtile_bound(max_rows, cap, p.E, kSkBM);
+    if (!fp8_ffn_supported(p)) return hipErrorInvalidValue;
     hipError_t ev = hipSuccess;
-    if (qfmt == MOE_Q_INT8)
-        launch_q8<kQInt8>(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);
-    else
-        launch_q8<kQE4M3>(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);
+    if (cap <= kSkBM) {
+        const int64_t mt = mtile_bound(max_rows, cap, p.E, kSkBM);
+        if (qfmt == MOE_Q_INT8)
+            launch_q8<kQInt8>(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);
+        else
+            launch_q8<kQE4M3>(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);
+    } else {
+        // gathered A rows are read from x through a buffer extent below 2 GiB
+        const int64_t a_bytes = a_rows ? (int64_t)p.T * p.d * 2 : 0;
+        if (a_bytes >= ((int64_t)1 << 31) || splits < 1 || (p.d_ff / kBK) % splits != 0) return hipErrorInvalidValue;
+        const int64_t mt = mtile_bound(max_rows, cap, p.E, kBM);
+        if (qfmt == MOE_Q_INT8)
+            launch_q8_mfma<kGateUpI8, kDownI8>(p, mt, x_perm, a_rows, a_bytes, offsets, w1, s1, w3, s3, w2, s2, h,
+                                               down, splits, claim, mid, ev, st);
+        else
+            launch_q8_mfma<kGateUpE4M3, kDownE4M3>(p, mt, x_perm, a_rows, a_bytes, offsets, w1, s1, w3, s3, w2, s2,
+                                                   h, down, splits, claim, mid, ev, st);
+    }
     if (ev != hipSuccess) return ev;
     return hipGetLastError();
 }

@@ -104,13 +104,16 @@ int fp8_weights_ok(const moe_params &p, const FfnWeights &w) {
     return MOE_OK;
 }
 
+// splits: the down projection's K slices for one-byte weights (moe_forward:
+// ffn_splits, as the combine expects; the staged entry points: 1).
 hipError_t launch_ffn(const moe_params &p, int64_t R, int64_t C, const void *a, const int32_t *a_rows,
                       const int32_t *offsets, const FfnWeights &w, void *h, const GemmOut &down, int32_t *claim,
-                      hipEvent_t mid, hipStream_t st) {
+                      hipEvent_t mid, hipStream_t st, int splits = 1) {
     if (w.s1)
         return launch_expert_ffn_fp8(p, R, C, a, a_rows, offsets, static_cast<const uint8_t *>(w.w1), w.s1,
                                      static_cast<const uint8_t *>(w.w3), w.s3,
-                                     static_cast<const uint8_t *>(w.w2), w.s2, h, down, mid, w.qfmt, st);
+                                     static_cast<const uint8_t *>(w.w2), w.s2, h, down, splits, claim, mid, w.qfmt,
+                                     st);
     return launch_expert_ffn(p, R, C, a, a_rows, offsets, w.w1, w.w3, w.w2, h, down, claim, mid, st);
 }
 
@@ -467,9 +470,9 @@ int forward_impl(const moe_params *p, const void *x, const void *w_router, const
                              : GemmOut{f.y, nullptr, stride, nullptr};
     hipEvent_t mid = events ? static_cast<hipEvent_t>(events[3]) : nullptr;
     if (f.x_perm)
-        e = launch_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w, f.h, down, f.claim, mid, st);
+        e = launch_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w, f.h, down, f.claim, mid, st, S);
     else
-        e = launch_ffn(*p, R, C, x, r->token_of_row, r->offsets, w, f.h, down, f.claim, mid, st);
+        e = launch_ffn(*p, R, C, x, r->token_of_row, r->offsets, w, f.h, down, f.claim, mid, st, S);
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
     if (p->dtype == MOE_BF16)

@@ -110,16 +110,20 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
 hipError_t launch_ffn_fixup(const moe_params &p, int64_t max_rows, const int32_t *offsets, float *y_perm,
                             const float *rest, int nrest, hipStream_t st);
 
-// One-byte (E4M3 or INT8) expert weights with fp32 row scales: the weight-streaming
-// kernel only (bf16 layer, cap <= 32 rows per expert, d and d_ff multiples of
-// 128).  fp8_ffn_supported tells whether a layer qualifies.
+// One-byte (E4M3 or INT8) expert weights with fp32 row scales, bf16 layers:
+// the weight-streaming kernel when every expert holds at most 32 rows (d and
+// d_ff multiples of 128), else the 256 x 256 MFMA tile with the codes widened
+// in registers, the down projection cut into `splits` K slices as for bf16
+// weights (ffn_splits) and claim counters as for launch_expert_ffn.
+// fp8_ffn_supported tells whether a layer qualifies.
 bool fp8_ffn_supported(const moe_params &p);
 // one-byte weight code formats
 enum { MOE_Q_E4M3 = 0, MOE_Q_INT8 = 1 };
 hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                                  const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
                                  const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,
-                                 const GemmOut &down, hipEvent_t mid, int qfmt, hipStream_t st);
+                                 const GemmOut &down, int splits, int32_t *claim, hipEvent_t mid, int qfmt,
+                                 hipStream_t st);
 
 // The gate-up GEMM storing its two products a = x W1^T and b = x W3^T
 // (fp32 [R][d_ff] each) for the kept rows; rows read from x through a_rows

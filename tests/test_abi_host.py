@@ -197,19 +197,26 @@ def fp8_ffn_rc(p, s_ptr=256):
 
 
 def test_fp8_weights_limits_rejected():
-    """One-byte expert weights: bf16 layers of capacity <= 32 with d and d_ff
-    multiples of 128 only; missing scales are an invalid argument.  The
-    checks come before any launch (the fake addresses are never touched)."""
+    """One-byte expert weights: bf16 layers only; groups of at most 32 rows
+    per expert (the weight-streaming kernel) need d and d_ff multiples of
+    128, larger groups (the matrix-core tile) multiples of 64; missing scales
+    are an invalid argument.  The checks come before any launch (the fake
+    addresses are never touched)."""
     ok = dict(T=64, d=512, E=8, k=2, d_ff=1024, capacity_factor=1.25, dtype=moe.MOE_BF16)
     assert moe.capacity(P(**ok)) == 20
     assert fp8_ffn_rc(P(**ok), s_ptr=None) == moe.MOE_ERR_INVALID_ARG
-    for bad in (dict(dtype=moe.MOE_F32), dict(T=256, capacity_factor=1.0), dict(d=448), dict(d_ff=960),
-                dict(capacity_factor=0.0)):
+    for bad in (dict(dtype=moe.MOE_F32), dict(d=448), dict(d_ff=960), dict(T=256, capacity_factor=1.0,
+                                                                              dtype=moe.MOE_F32)):
         kw = dict(ok)
         kw.update(bad)
         assert fp8_ffn_rc(P(**kw)) == moe.MOE_ERR_UNSUPPORTED, bad
+    # groups of more than 32 rows take d and d_ff multiples of 64: the missing
+    # scale is then the first error found
+    big = dict(ok, T=256, capacity_factor=1.0, d=448, d_ff=960)
+    assert moe.capacity(P(**big)) == 64
+    assert fp8_ffn_rc(P(**big), s_ptr=None) == moe.MOE_ERR_INVALID_ARG
     r = moe.MoeRouting(*[256] * len(moe.Routing.NAMES))
-    p = P(**dict(ok, T=256, capacity_factor=1.0))
+    p = P(**dict(ok, T=256, capacity_factor=1.0, dtype=moe.MOE_F32))
     rc = moe.lib().moe_forward_fp8(ctypes.byref(p.c()), 256, 256, None, None, 256, 256, 256, 256, 256, 256,
                                    256, 256, ctypes.byref(r), 256, moe.workspace_bytes(p), None)
     assert rc == moe.MOE_ERR_UNSUPPORTED

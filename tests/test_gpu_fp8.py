@@ -3,6 +3,9 @@
 moe_forward_i8), through the C ABI against the oracle, which dequantises the
 same codes and scales exactly (double) and runs its plain SwiGLU FFN.
 
+Groups of at most 32 rows per expert run the weight-streaming kernel, larger
+ones the 256 x 256 MFMA tile; both are covered.
+
 Tolerances as for the bf16 layer: h (rounded once to fp16) within one fp16
 ulp per element plus 1e-4 * RMS for fp32 accumulation; y_perm and the layer
 output within 2e-2 * RMS (the output beyond one bf16 unit roundoff of |ref|
@@ -164,6 +167,17 @@ CASES = {
     "top1_many_experts": dict(T=200, E=24, k=1, d=256, d_ff=256, cf=1.0),
     "long_k": dict(T=40, d=2048, d_ff=1536, E=4, k=2, cf=1.5),
     "drops": dict(T=96, E=8, k=2, cf=0.5, d=256, d_ff=512),
+    # more than 32 rows per expert: the 256 x 256 MFMA tile with the codes
+    # widened in registers.  C = 350: two m tiles per expert, the second
+    # ragged; the forward's down projection in two K slices (d_ff 512)
+    "mfma_two_mtiles_split": dict(T=700, E=4, k=2, d=256, d_ff=512, cf=1.0),
+    # ragged N tiles: gate-up 1.5 tiles of 128 h columns, down 256 + 64
+    # output columns; C = 334
+    "mfma_ragged_n": dict(T=500, E=3, k=2, d=320, d_ff=192, cf=1.0),
+    # long K (d 2048), one m tile of 150 rows per expert, top-1
+    "mfma_long_k": dict(T=300, E=2, k=1, d=2048, d_ff=1024, cf=1.0),
+    # dropping capacity (C = 75) with re-routes, eight experts
+    "mfma_drops": dict(T=600, E=8, k=2, cf=0.5, d=256, d_ff=256),
 }
 
 
@@ -189,6 +203,23 @@ def test_fp8_decode_full_size(fmt):
     check_layer(Fp8Layer(c, fmt=fmt), full=True, rows_sample=sample)
 
 
+@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+@pytest.mark.parametrize("name", ["skew", "mixtral"])
+def test_fp8_prefill_full_size(name, fmt):
+    """Prefill workloads with one-byte weights (the MFMA tile): sampled rows
+    at each expert's ends, m-tile boundaries and middle; sampled tokens."""
+    c = moe_synth.CONFIGS[name]
+
+    def sample(offs):
+        rows = set()
+        for e in range(len(offs) - 1):
+            b, en = int(offs[e]), int(offs[e + 1])
+            rows.update(r for r in (b, en - 1, (b + en) // 2, b + 255, b + 256) if b <= r < en)
+        return np.array(sorted(rows), np.int32)
+
+    check_layer(Fp8Layer(c, fmt=fmt), full=False, rows_sample=sample)
+
+
 def test_fp8_empty_batch():
     L = Fp8Layer(cfg(T=4))
     p = moe.Params(T=0, d=512, E=8, k=2, d_ff=1024, capacity_factor=1.25, dtype=moe.MOE_BF16)
@@ -200,12 +231,13 @@ def test_fp8_empty_batch():
     assert int(r.offsets.cpu()[-1]) == 0
 
 
-def test_fp8_unsupported_capacity_raises():
-    """Capacity above 32 rows per expert is outside the weight-streaming kernel."""
+def test_fp8_fp32_layer_unsupported():
+    """One-byte weights serve bf16 layers only."""
     L = Fp8Layer(cfg(T=4))
-    p = moe.Params(T=256, d=512, E=8, k=2, d_ff=1024, capacity_factor=1.0, dtype=moe.MOE_BF16)
-    x = torch.zeros((256, 512), dtype=torch.bfloat16, device=DEV)
+    p = moe.Params(T=64, d=512, E=8, k=2, d_ff=1024, capacity_factor=1.0, dtype=moe.MOE_F32)
+    x = torch.zeros((64, 512), dtype=torch.float32, device=DEV)
     r = moe.Routing(p, DEV)
-    with pytest.raises(moe.MoEError):
-        moe.forward_fp8(p, x, L.wr, None, None, *L.weights(), torch.empty_like(x),
-                        torch.empty((256, 8), device=DEV), r, moe.alloc_workspace(p, DEV))
+    with pytest.raises(moe.MoEError) as ei:
+        moe.forward_fp8(p, x, L.wr.float(), None, None, *L.weights(), torch.empty_like(x),
+                        torch.empty((64, 8), device=DEV), r, moe.alloc_workspace(p, DEV))
+    assert ei.value.code == moe.MOE_ERR_UNSUPPORTED
