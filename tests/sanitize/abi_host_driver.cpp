@@ -94,8 +94,8 @@ int main() {
                                                   nullptr) == MOE_ERR_INVALID_ARG);
                                 CHECK(moe_dispatch(&p, fp, &rf, fp, fp, wd - 1, nullptr) == MOE_ERR_INVALID_ARG);
                             }
-    // one-byte weights: only bf16 layers of capacity <= 32
-    moe_params big = P(4096, 4096, 8, 2, 14336, 1.25f, MOE_BF16);
+    // one-byte weights: bf16 layers only
+    moe_params big = P(4096, 4096, 8, 2, 14336, 1.25f, MOE_F32);
     void *fp = reinterpret_cast<void *>(4096);
     const uint8_t *q = reinterpret_cast<const uint8_t *>(4096);
     const float *s = reinterpret_cast<const float *>(4096);
