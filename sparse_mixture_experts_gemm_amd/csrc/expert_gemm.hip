@@ -352,12 +352,12 @@ __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, c
     __builtin_amdgcn_sched_barrier(0);
 }
 
-// B buffers of each GEMM: three for the gate-up GEMM, whose weight tiles
-// arrive from HBM (the third buffer lets a tile start almost two K steps
-// before its use); two for the down GEMM, which has no registers to spare
-// for the addresses of a third.
+// B buffers of each GEMM: three (the third lets a weight tile start almost
+// two K steps before its use; measured 1.6% on the Mixtral-shape down
+// projection), two for the one-byte down projections, whose widening leaves
+// no registers for the addresses of a third.
 template <int MODE>
-__device__ __forceinline__ constexpr int b_buffers() { return down_mode<MODE>() ? 2 : 3; }
+__device__ __forceinline__ constexpr int b_buffers() { return (MODE == kDownE4M3 || MODE == kDownI8) ? 2 : 3; }
 
 // One K step (4 sub-steps of 16) on the A buffer `ca` and B buffer `cb`.
 // LDS holds two A buffers and NB B buffers (distinct objects, so the compiler
