@@ -109,6 +109,17 @@ BWD_SMALL = {
     "dense_E1": dict(T=100, d=128, E=1, k=1, d_ff=256, cf=0.0),
     "one_token": dict(T=1, d=256, E=4, k=2, d_ff=128),
     "ragged": dict(T=333, d=192, E=5, k=2, d_ff=320, cf=1.3),
+    # the forward's edge cases: every expert picked (k = E), capacity 1,
+    # uncapped, dropping without re-route, 256 experts with top-8 (most
+    # experts get a few rows or none: zero weight-gradient tiles), the
+    # minimum dims (one partial 64-row tile), the top-2 gap threshold
+    "k_equals_E": dict(E=2, k=2, T=300, cf=0.6),
+    "capacity_one": dict(T=200, cf=1e-6),
+    "uncapped": dict(T=300, cf=0.0),
+    "no_reroute": dict(T=400, cf=0.5, reroute=0),
+    "many_experts_top8": dict(E=256, k=8, T=512, d=64, d_ff=64, cf=1.0),
+    "min_dims": dict(T=77, d=64, d_ff=64, E=3, k=1),
+    "top2_gap": dict(T=600, E=8, k=2, cf=1.0, gap=0.1),
 }
 
 
