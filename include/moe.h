@@ -370,10 +370,10 @@ size_t moe_backward_workspace_bytes(const moe_params *p);
  * operands and the fp32 SwiGLU gradients and g * h as a pair of bf16 values
  * (hi = bf16(v), lo = bf16(v - hi), about 2^-17 relative) whose products
  * accumulate together.  Deterministic (no atomics).  MOE_ERR_UNSUPPORTED: an
- * fp32 layer, the two-layer router, x of 2 GiB and more, 4 d d_ff bytes of
- * 4 GiB and more (one expert's W1^T | W3^T), or 2 GiB and more in 256 rows
- * of the kept rows' transposed K axis (1024 (R + 64 E) bytes, R the kept
- * row bound moe_max_rows rounded up to 64: about two million kept rows).
+ * fp32 layer, the two-layer router, x of 2 GiB and more, or 2 GiB and more
+ * in 256 rows of the kept rows' transposed K axis (1024 (R + 64 E) bytes, R
+ * the kept row bound moe_max_rows rounded up to 64: about two million kept
+ * rows).
  */
 int moe_backward(const moe_params *p, const void *x, const void *w_router, const void *w1, const void *w3,
                  const void *w2, const moe_routing *r, const void *dy, float *dx, float *dlogits,

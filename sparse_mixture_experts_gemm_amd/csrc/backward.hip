@@ -32,42 +32,11 @@
 namespace moe {
 namespace {
 
-// The grouped GEMMs (grouped_gemm_bf16<kPlain> and grouped_gemm_wgrad) take
-// both operands K-contiguous, the MFMA fragments' natural layout.  Operands
-// that are not (W2 and W1/W3 for the input gradients; the kept rows, whose
-// K axis is the row index, for the weight gradients) are transposed once
-// into the workspace by the kernels below, through 64 x 64 LDS tiles.
-
-// dst[e][c][col0 + r] = src[e][r][c]: one 64 x 64 tile of an expert's
-// [rows][cols] matrix per block (rows and cols multiples of 64); dst rows
-// hold dst_ld elements, experts cols * dst_ld apart.
-__global__ __launch_bounds__(256) void transpose_w(const uint16_t *__restrict__ src, int rows, int cols,
-                                                   uint16_t *__restrict__ dst, int dst_ld, int col0) {
-    __shared__ uint16_t t[64][66];
-    const int tr = rows / 64, tc = cols / 64;
-    const int e = blockIdx.x / (tr * tc), rem = blockIdx.x % (tr * tc);
-    const int r0 = (rem / tc) * 64, c0 = (rem % tc) * 64;
-    const int tid = threadIdx.x, q = (tid & 7) * 8;
-    const uint16_t *s = src + (size_t)e * rows * cols;
-#pragma unroll
-    for (int ps = 0; ps < 2; ps++) {
-        const int rr = (tid >> 3) + 32 * ps;
-        const uint4 v = *reinterpret_cast<const uint4 *>(s + (size_t)(r0 + rr) * cols + c0 + q);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-        for (int i = 0; i < 4; i++) *reinterpret_cast<uint32_t *>(&t[rr][q + 2 * i]) = w[i];
-    }
-    __syncthreads();
-    uint16_t *d = dst + (size_t)e * cols * dst_ld;
-#pragma unroll
-    for (int ps = 0; ps < 2; ps++) {
-        const int cc = (tid >> 3) + 32 * ps;
-        uint32_t w[4];
-#pragma unroll
-        for (int i = 0; i < 4; i++) w[i] = (uint32_t)t[q + 2 * i][cc] | ((uint32_t)t[q + 2 * i + 1][cc] << 16);
-        *reinterpret_cast<uint4 *>(d + (size_t)(c0 + cc) * dst_ld + col0 + r0 + q) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
-}
+// The grouped GEMMs take A K-contiguous.  The weights of u and dx enter as
+// they are (grouped_gemm_bf16<kPlainBT> reads N-contiguous B tiles with the
+// transposing LDS read); the weight gradients' operands, whose K axis is the
+// kept row, are transposed once into the workspace by to_kmajor, through
+// 64 x 64 LDS tiles, for grouped_gemm_wgrad.
 
 // The kept rows of each expert, transposed into its K window (kwin_start):
 //   dst[c][kwin_e + koff + j] = src[src_row(offsets[e] + j)][col0 + c]
@@ -339,34 +308,30 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
         hipLaunchKernelGGL(to_kmajor, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, st, src, src_ld, gather,
                            col0, ncols, a.offsets, E, dst, ldk, half, dup);
     };
-    // 1. the rows' gates, the weight-gradient row ranges, the transposed
-    //    weights; a and b recomputed by the gate-up GEMM
+    // 1. the rows' gates, the weight-gradient row ranges; a and b
+    //    recomputed by the gate-up GEMM
     hipLaunchKernelGGL(row_gates, dim3((unsigned)ceil_div((int64_t)T * k, 256)), dim3(256), 0, st, a.row, a.gate,
                        T * k, a.gate_of_row);
     hipLaunchKernelGGL(unit_offsets_kernel, dim3((unsigned)ceil_div(E + 1, 256)), dim3(256), 0, st, a.unit_offsets,
                        E, dff, d);
-    const unsigned wtiles = (unsigned)((int64_t)E * (d / 64) * (dff / 64));
-    hipLaunchKernelGGL(transpose_w, dim3(wtiles), dim3(256), 0, st, static_cast<const uint16_t *>(a.w2), d, dff,
-                       a.w2t, d, 0);
-    hipLaunchKernelGGL(transpose_w, dim3(wtiles), dim3(256), 0, st, static_cast<const uint16_t *>(a.w1), dff, d,
-                       a.w13t, 2 * dff, 0);
-    hipLaunchKernelGGL(transpose_w, dim3(wtiles), dim3(256), 0, st, static_cast<const uint16_t *>(a.w3), dff, d,
-                       a.w13t, 2 * dff, dff);
     hipError_t e = launch_gate_up_raw(p, R, cap, a.x, a.token_of_row, a.offsets, a.w1, a.w3, a.a, a.b, st);
     if (e != hipSuccess) return e;
-    // 2. u = W2_e^T dy_t for every kept row (dy rows gathered by token)
-    e = launch_plain_gemm(R, cap, E, dy, a.token_of_row, (int64_t)T * d * 2, a.offsets, a.w2t, dff, d, d, 1, a.u,
-                          nullptr, st);
+    // 2. u = W2_e^T dy_t for every kept row (dy rows gathered by token; W2
+    //    [d][d_ff] read as it is, N-contiguous)
+    const uint16_t *w1 = static_cast<const uint16_t *>(a.w1), *w3 = static_cast<const uint16_t *>(a.w3),
+                   *w2 = static_cast<const uint16_t *>(a.w2);
+    e = launch_plain_gemm(R, cap, E, dy, a.token_of_row, (int64_t)T * d * 2, a.offsets, w2, nullptr, true, dff, d, d,
+                          1, a.u, nullptr, st);
     if (e != hipSuccess) return e;
     // 3. SwiGLU backward per row, 4. gate softmax backward per token
     hipLaunchKernelGGL(swiglu_backward, dim3((unsigned)R), dim3(256), 0, st, a.a, a.b, a.u, a.gate_of_row, a.offsets,
                        E, dff, a.acat, a.hg, a.dg);
     hipLaunchKernelGGL(gate_backward, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st, a.row, a.eid, a.gate, a.dg,
                        T, E, k, inv_tau, a.dlogits, a.ds_of_row);
-    // 5. dx_perm = [da | db] [W1 | W3] over the hi parts and the lo parts
-    //    (K slices of their own, sharing the one transposed weight copy),
-    //    6. dx
-    e = launch_plain_gemm(R, cap, E, a.acat, nullptr, 0, a.offsets, a.w13t, d, 4 * dff, 2 * dff, a.dx_splits,
+    // 5. dx_perm = da_hi W1 + db_hi W3 + da_lo W1 + db_lo W3: K periods of
+    //    d_ff over the concatenated acat row, W1 and W3 ([d_ff][d],
+    //    N-contiguous) in turn, at least one K slice per period; 6. dx
+    e = launch_plain_gemm(R, cap, E, a.acat, nullptr, 0, a.offsets, w1, w3, true, d, 4 * dff, dff, a.dx_splits,
                           a.dx_perm, a.dx_rest, st);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,

@@ -60,16 +60,22 @@ constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (
 // row: the B tile holds the codes (64-byte rows), the fragments are widened
 // exactly in registers, and the row scales multiply the fp32 accumulators
 // in the epilogue (a weight row's scale factors out of its dot products).
+// kPlainBT: kPlain with B given N-contiguous ([K][N] row-major per expert,
+// the natural layout of W2 for u = dy W2 and of W1 / W3 for the input
+// gradient): a B stage holds 64 K rows of the tile's 256 columns and the
+// fragments are read with the transposing LDS read (ds_read_b64_tr_b16).
 enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2, kPlain = 3, kGateUpE4M3 = 4, kDownE4M3 = 5, kGateUpI8 = 6,
-       kDownI8 = 7 };
+       kDownI8 = 7, kPlainBT = 8 };
 
 // one-byte weight codes: OCP E4M3 or INT8
 enum { kQE4M3 = 0, kQInt8 = 1 };
 
 template <int MODE>
-__device__ __forceinline__ constexpr bool q_mode() { return MODE >= kGateUpE4M3; }
+__device__ __forceinline__ constexpr bool q_mode() { return MODE >= kGateUpE4M3 && MODE <= kDownI8; }
 template <int MODE>
 __device__ __forceinline__ constexpr int q_fmt() { return MODE >= kGateUpI8 ? kQInt8 : kQE4M3; }
+template <int MODE>
+__device__ __forceinline__ constexpr bool b_trans() { return MODE == kPlainBT; }
 // The SwiGLU epilogue (h = silu(a) * b, fp16)
 template <int MODE>
 __device__ __forceinline__ constexpr bool gate_up() { return MODE == kGateUp || MODE == kGateUpE4M3 || MODE == kGateUpI8; }
@@ -185,6 +191,14 @@ __device__ __forceinline__ void buf2lds16(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 __device__ __forceinline__ uint4 lds_read16(const char *p) { return *reinterpret_cast<const uint4 *>(p); }
 
+// gfx950's transposing LDS read of 16-bit elements: within each group of 16
+// lanes, lane 4a + b receives element b of the four-element rows addressed
+// by lanes a, a + 4, a + 8 and a + 12 (as elements 0..3).
+typedef short u16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u16x4_t ds_read_tr16(const char *p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) u16x4_t *)(p));
+}
+
 // LDS read issued as inline assembly, for the weight-streaming kernels: the
 // compiler's wait-count pass then does not take it for a read of a buffer
 // that a stage load in flight may still write, and adds no wait for all loads
@@ -211,6 +225,8 @@ struct GemmThread {
     __amdgpu_buffer_rsrc_t b_rsrc;  // this wave's weight rows: W1 / W3 (gate-up) or W2
     int a_valid;                          // valid rows of the tile (uniform)
     uint32_t fa[2][4], fb[2][4];  // LDS byte offsets of fragments [block parity][sub-step]
+                                  // (kPlainBT: fb[0][jn] is block jn's base, see load_frags)
+    uint32_t b_kstep;             // kPlainBT: bytes between the B rows of consecutive K steps
     int wave;
 };
 
@@ -229,11 +245,13 @@ __device__ __forceinline__ int b_imm(int jn) {
 template <int MODE, int HALF>
 __device__ __forceinline__ void issue_loads(const GemmThread &g, char *buf, uint32_t kb) {
     if (HALF == 0 || !q_mode<MODE>()) {
+        // kPlainBT: the K step advances 64 B rows, not 128 bytes along a row
+        const uint32_t kbb = b_trans<MODE>() ? (kb / kRowBytes) * g.b_kstep : kb;
 #pragma unroll
         for (int j = 0; j < kLoadsPerOperand; j++) {
-            const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group
+            const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group (kPlainBT: 2 K rows)
             if (HALF == 0) buf2lds16(g.a_rsrc, g.a_off[j], kb, buf + grp * 1024);
-            else buf2lds16(g.b_rsrc, g.b_off[j], kb, buf + grp * 1024);
+            else buf2lds16(g.b_rsrc, g.b_off[j], kbb, buf + grp * 1024);
         }
     } else {
         // one-byte codes: 16-row groups of 64-byte rows, the K step is 64 bytes
@@ -258,7 +276,14 @@ __device__ __forceinline__ void load_frags(const GemmThread &g, const char *abuf
     for (int i = 0; i < 4; i++) f.a[i] = lds_read16(abuf + g.fa[i & 1][ss] + i * 32 * kRowBytes);
 #pragma unroll
     for (int jn = 0; jn < 4; jn++) {
-        if constexpr (q_mode<MODE>()) {
+        if constexpr (b_trans<MODE>()) {
+            // two transposing reads: K rows 16 ss + 8 (lane / 32) + 0..3, then
+            // + 4..7 (2 KiB further), of the lane's column
+            const char *p = bbuf + g.fb[0][jn] + ss * 16 * 512;
+            const u16x4_t v0 = ds_read_tr16(p), v1 = ds_read_tr16(p + 4 * 512);
+            const uint2 w0 = __builtin_bit_cast(uint2, v0), w1 = __builtin_bit_cast(uint2, v1);
+            f.b[jn] = make_uint4(w0.x, w0.y, w1.x, w1.y);
+        } else if constexpr (q_mode<MODE>()) {
             // eight codes, widened after the read has landed (widen_b)
             const uint2 v = *reinterpret_cast<const uint2 *>(bbuf + g.fb[jn & 1][ss] + b_imm<MODE>(jn));
             f.b[jn] = make_uint4(v.x, v.y, 0u, 0u);
@@ -684,11 +709,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     g.a_rsrc = a_rows ? make_rsrc(A, a_bytes)
                       : make_rsrc(A + (size_t)ti.m0 * K, (uint32_t)(g.a_valid < kBM ? g.a_valid : kBM) * K * 2);
     const uint32_t w_bytes = (uint32_t)((size_t)N * ldb * kWb);
-    // gate-up: waves 0-1 load B rows 0..127 (W1), waves 2-3 rows 128..255 (W3)
-    g.b_rsrc = make_rsrc(reinterpret_cast<const char *>(two_b<MODE>() && wave >= 2 ? B1 : B0) + wexp, w_bytes);
     // B's K position of this split: B rows of ldb elements, read periodically
-    // when the splits of A's K range share one B (ldb < K, a multiple of ks)
+    // when the splits of A's K range share one B (ldb < K, a multiple of ks);
+    // kPlainBT: ldb is the K extent of each of B0 and B1 ([ldb][N] per
+    // expert), taken in turn by consecutive K periods
     const int kb_first = k_first % ldb;
+    const uint16_t *bsel = b_trans<MODE>() ? (((k_first / ldb) & 1) ? B1 : B0)
+                                           : (two_b<MODE>() && wave >= 2 ? B1 : B0);
+    // gate-up: waves 0-1 load B rows 0..127 (W1), waves 2-3 rows 128..255 (W3)
+    g.b_rsrc = make_rsrc(reinterpret_cast<const char *>(bsel) + wexp, w_bytes);
 #pragma unroll
     for (int j = 0; j < kLoadsPerOperand; j++) {
         const int grp = wave * kLoadsPerOperand + j;
@@ -697,12 +726,21 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
         const int gm = min(ti.m0 + row, ti.mend - 1);
         const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
         g.a_off[j] = grp * kRowsPerLoad < g.a_valid ? ((uint32_t)ar * K + k_first + c * 8) * 2 : kPastEnd;
-        if constexpr (!q_mode<MODE>()) {
+        if constexpr (b_trans<MODE>()) {
+            // K rows 2 grp, 2 grp + 1 of the stage (512 bytes each); lane l
+            // takes the logical 16-byte chunk that lands at position l % 32,
+            // chunks XOR-swizzled by 4 (row % 4)
+            const int kr = 2 * grp + (lane >> 5);
+            const int cl = (lane & 31) ^ (4 * (kr & 3));
+            const int gc = min(n0 + 8 * cl, N - 8);
+            g.b_off[j] = ((uint32_t)(kb_first + kr) * N + gc) * 2;
+        } else if constexpr (!q_mode<MODE>()) {
             int gn = two_b<MODE>() ? n0 + (row & (kBN / 2 - 1)) : n0 + row;
             gn = min(gn, N - 1);
             g.b_off[j] = ((uint32_t)gn * ldb + kb_first + c * 8) * 2;
         }
     }
+    g.b_kstep = (uint32_t)kBK * N * 2;
     if constexpr (q_mode<MODE>()) {
         // one-byte codes: wave w loads 16-row groups 4w .. 4w+3 of 64-byte
         // rows; lane l takes row 16g + l/4 and the logical 16-byte chunk that
@@ -731,6 +769,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
             g.fb[pp][ss] = q_mode<MODE>() ? (uint32_t)(b_rbase + l5) * 64 + ((ss ^ swz4(l5)) << 4) + hi * 8
                                           : (uint32_t)(b_rbase + l5) * kRowBytes + sw;
         }
+    if constexpr (b_trans<MODE>()) {
+        // block jn's base for the transposing reads: lane 16 g + 4 j' + a'
+        // addresses K row 8 (g / 2) + j' (then + 4) and columns wn 128 +
+        // jn 32 + 16 (g % 2) + 4 a' .. + 3, in the chunk swizzled by 4 j'
+        const int gq = lane >> 4, jq = (lane >> 2) & 3, aq = lane & 3;
+#pragma unroll
+        for (int jn = 0; jn < 4; jn++)
+            g.fb[0][jn] = (uint32_t)((8 * (gq >> 1) + jq) * 512 + 256 * wn + 64 * (jn ^ jq) + 32 * (gq & 1) + 8 * aq);
+    }
     // active 32-row blocks of this wave (uniform)
     const int nact_raw = (ti.mend - (ti.m0 + wm * 128) + 31) / 32;
     const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
@@ -1520,17 +1567,22 @@ int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb) {
 }
 
 hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
-                             int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, int N, int K, int ldb,
-                             int S, float *C, float *rest, hipStream_t st) {
+                             int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, const uint16_t *B1,
+                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
     if (S < 1 || K % S != 0 || (K / S) % kBK != 0 || ldb % (K / S) != 0 || N % 64 != 0 ||
         a_span_bytes >= ((int64_t)1 << 31) || (int64_t)N * ldb * 2 >= ((int64_t)1 << 32))
         return hipErrorInvalidValue;
     const int64_t mt = mtile_bound(max_rows, cap, E, kBM);
     const int nt = (int)ceil_div(N, kBN);
-    hipLaunchKernelGGL(grouped_gemm_bf16<kPlain>, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A, a_rows,
-                       B, B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes, (int32_t *)nullptr,
-                       GemmOut{C, rest, (size_t)max_rows * N, nullptr});
+    if (b_n_contig)
+        hipLaunchKernelGGL(grouped_gemm_bf16<kPlainBT>, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A,
+                           a_rows, B, B1 ? B1 : B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes,
+                           (int32_t *)nullptr, GemmOut{C, rest, (size_t)max_rows * N, nullptr});
+    else
+        hipLaunchKernelGGL(grouped_gemm_bf16<kPlain>, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A,
+                           a_rows, B, B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes, (int32_t *)nullptr,
+                           GemmOut{C, rest, (size_t)max_rows * N, nullptr});
     if (S > 1) {
         const int64_t n4 = max_rows * (N / 4);
         const int grid = (int)std::min<int64_t>(ceil_div(n4, 256), 4096);

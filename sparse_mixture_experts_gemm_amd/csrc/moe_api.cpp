@@ -181,9 +181,9 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
 // Workspace layout of moe_backward (sizes in bytes, each 256-aligned):
 // gate_of_row, ds_of_row, dg [R] fp32; a, b, u [R][d_ff] fp32; acat
 // [R][4 d_ff] and hg [R][2 d_ff] bf16; dx_perm [S][R][d] fp32 (S K slices
-// of the dx GEMM); W2^T [E][d_ff][d] and W1^T | W3^T [E][d][2 d_ff] bf16;
-// the K-major copies of the kept rows, [2 d_ff], [d], [d] and [d_ff] rows of
-// ldk bf16; two sets of E + 1 unit offsets.
+// of the dx GEMM, at least one per d_ff period of its K); the K-major
+// copies of the kept rows, [2 d_ff], [d], [d] and [d_ff] rows of ldk bf16;
+// two sets of E + 1 unit offsets.
 struct BackwardSizes {
     size_t R, F, D, E, ldk;
     int S;
@@ -196,15 +196,15 @@ BackwardSizes backward_sizes(const moe_params &p) {
     z.D = (size_t)p.d;
     z.E = (size_t)p.E;
     z.ldk = (size_t)backward_ldk((int64_t)z.R, p.E);
-    z.S = plain_gemm_splits((int64_t)z.R, p.E, p.d, 4 * p.d_ff, 2 * p.d_ff);
+    z.S = plain_gemm_splits((int64_t)z.R, p.E, p.d, 4 * p.d_ff, p.d_ff);
     return z;
 }
 
 size_t backward_ws_bytes(const moe_params &p) {
     const BackwardSizes z = backward_sizes(p);
     return 3 * align256(z.R * 4) + 3 * align256(z.R * z.F * 4) + align256(z.R * 4 * z.F * 2) +
-           align256(z.R * 2 * z.F * 2) + align256((size_t)z.S * z.R * z.D * 4) + align256(z.E * z.F * z.D * 2) +
-           align256(z.E * z.D * 2 * z.F * 2) + align256(2 * z.F * z.ldk * 2) + 2 * align256(z.D * z.ldk * 2) +
+           align256(z.R * 2 * z.F * 2) + align256((size_t)z.S * z.R * z.D * 4) + align256(2 * z.F * z.ldk * 2) +
+           2 * align256(z.D * z.ldk * 2) +
            align256(z.F * z.ldk * 2) + align256(2 * (z.E + 1) * 4);
 }
 
@@ -226,8 +226,6 @@ void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
     a.hg = reinterpret_cast<uint16_t *>(take(z.R * 2 * z.F * 2));
     a.dx_perm = reinterpret_cast<float *>(take((size_t)z.S * z.R * z.D * 4));
     a.dx_rest = a.dx_perm + z.R * z.D;
-    a.w2t = reinterpret_cast<uint16_t *>(take(z.E * z.F * z.D * 2));
-    a.w13t = reinterpret_cast<uint16_t *>(take(z.E * z.D * 2 * z.F * 2));
     a.dat = reinterpret_cast<uint16_t *>(take(2 * z.F * z.ldk * 2));
     a.xt = reinterpret_cast<uint16_t *>(take(z.D * z.ldk * 2));
     a.dyt = reinterpret_cast<uint16_t *>(take(z.D * z.ldk * 2));
@@ -272,11 +270,8 @@ int moe_backward(const moe_params *p, const void *x, const void *w_router, const
     if (p->dtype != MOE_BF16 || p->router_hidden != 0 || (int64_t)p->T * p->d * 2 >= ((int64_t)1 << 31))
         return MOE_ERR_UNSUPPORTED;
     const int64_t R = max_rows_of(*p);
-    // the transposed operands: 256 rows of the kept rows' K axis below 2 GiB,
-    // and the transposed W1 | W3 of one expert below 4 GiB
-    if (256 * backward_ldk(R, p->E) * 2 >= ((int64_t)1 << 31) ||
-        (int64_t)p->d * 2 * p->d_ff * 2 >= ((int64_t)1 << 32))
-        return MOE_ERR_UNSUPPORTED;
+    // the transposed kept rows: 256 rows of their K axis below 2 GiB
+    if (256 * backward_ldk(R, p->E) * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     if (!r || !r->offsets || !w_router || !w1 || !w3 || !w2 || !dw_router || !dbias || !dw1 || !dw3 || !dw2 ||
         !workspace)
         return MOE_ERR_INVALID_ARG;

@@ -135,14 +135,16 @@ hipError_t launch_gate_up_raw(const moe_params &p, int64_t max_rows, int64_t cap
 // C = A B_e^T over the kept rows of every expert, bf16 operands, fp32
 // result (the backward pass's grouped GEMMs): A [rows][K] (the permuted
 // rows, or rows of a matrix spanning a_span_bytes < 2 GiB through a_rows),
-// B [E][N][ldb], C [max_rows][N].  K is cut into S slices (K / S a multiple
+// C [max_rows][N].  B is [E][N][ldb] (K-contiguous), or with b_n_contig
+// [E][ldb][N] (N-contiguous: C = A B_e) with B and B1 taken in turn by
+// consecutive K periods of ldb.  K is cut into S slices (K / S a multiple
 // of 64 that divides ldb); slice s reads B at K position (s K / S) mod ldb,
 // so slices can share one B; slice s > 0 stores its partial product at
 // rest + (s - 1) max_rows N, and a fix-up adds the slices into C in order.
 int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb);
 hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
-                             int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, int N, int K, int ldb,
-                             int S, float *C, float *rest, hipStream_t st);
+                             int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, const uint16_t *B1,
+                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st);
 
 // Per-expert K windows of the backward's transposed operands: the kept rows
 // of expert e (rows_e of them, from offsets[e]) become K positions
@@ -173,8 +175,6 @@ struct BackwardArgs {
     uint16_t *hg;                         // [R][2 d_ff] bf16: (g h) hi, lo
     float *dx_perm;                       // [R][d]
     float *dx_rest;                       // [S - 1][R][d]: the dx GEMM's other K slices
-    uint16_t *w2t;                        // [E][d_ff][d]: W2 transposed
-    uint16_t *w13t;                       // [E][d][2 d_ff]: W1^T | W3^T
     uint16_t *dat;                        // [2 d_ff][ldk]: da^T then db^T, per-expert K windows (hi, lo)
     uint16_t *xt, *dyt;                   // [d][ldk]: x^T, dy^T of the kept rows (twice per window)
     uint16_t *hgt;                        // [d_ff][ldk]: (g h)^T (hi, lo)
