@@ -217,9 +217,10 @@ def main():
     # distribution of single-step times (events around each step, no sync in
     # between), then cold-cache steps: a 1 GiB fill before each one evicts
     # x, the weights and the workspace from L2 and the 256 MiB last-level cache
-    step_ms = cold_ms = gpu_state = None
+    step_ms = cold_ms = gpu_state = graph_ms = None
     if not args.no_extras:
         step_ms = step_times(step, max(20, args.steps), torch)
+        graph_ms = graph_step_ms(step, args.steps, torch)
         scratch = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         cold_ms = step_times(step, 10, torch, before=lambda i: scratch.fill_(float(i)))
         del scratch
@@ -319,6 +320,7 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": wall,
         "step_ms": step_ms,
+        "graph_ms_per_step": graph_ms,
         "cold_step_ms": cold_ms,
         "gpu_state": gpu_state,
     }
@@ -357,6 +359,35 @@ def bench_backward(moe, moe_synth, torch, np, p, cfg, L, r, rows, dev, n):
     del gr, wsb
     torch.cuda.empty_cache()
     return out
+
+
+def graph_step_ms(step, n, torch):
+    """The forward pass captured once in a HIP graph (torch.cuda.graph) and
+    replayed n times on the current stream: mean ms per replay (the eager
+    step's launch gaps removed), or None if the capture fails."""
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            step()
+        torch.cuda.synchronize()
+        g.replay()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record()
+        for _ in range(n):
+            g.replay()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n
+    except Exception as e:  # the eager measurement stands on its own
+        print(f"[bench] graph capture failed: {e}", file=sys.stderr, flush=True)
+        return None
 
 
 def step_times(step, n, torch, before=None):
