@@ -1366,26 +1366,45 @@ __global__ __launch_bounds__(256) void grouped_gemm_f32(const float *__restrict_
 
 }  // namespace
 
-int ffn_splits(const moe_params &p, int64_t max_rows) {
-    if (p.dtype != MOE_BF16 || max_rows <= 0) return 1;
-    // small groups run the weight-streaming kernel, whose down projection is
-    // one slice (a CU per 128 output columns of an expert already fills the
-    // chip, and longer tiles stream better)
-    if (capacity_rows(p) <= kSkBM) return 1;
-    // down GEMM work items before splitting (upper bound); aim for at least
-    // three per compute unit
-    const int64_t tiles = (max_rows / kBM + p.E) * ceil_div(p.d, kBN);
-    const int64_t steps = p.d_ff / kBK;
-    int s = 1;
-    while (s < 8 && tiles * s < 3 * 256 && steps % (4 * s) == 0) s *= 2;
-    return s;
-}
-
 // Bound on sum_e ceil(rows_e / bm), the m tiles of all experts: every
 // expert holds at most cap rows, and all of them at most max_rows.  The grid
 // is sized by it, so a tight bound leaves few blocks without work.
 static int64_t mtile_bound(int64_t max_rows, int64_t cap, int E, int bm) {
     return std::min<int64_t>(max_rows / bm + E, (int64_t)E * ((cap + bm - 1) / bm));
+}
+
+// Slices of a K reduction of `steps` K steps over (at most) `tiles` output
+// tiles, among the doublings of s_min that allowed(s) accepts (at most 8):
+// the count with the least cost in K steps per compute unit.  The work items
+// (tiles x S) run in rounds of one per CU; an item costs its K / S steps plus
+// about six steps of prologue and epilogue; fewer items than CUs leave CUs
+// idle, which costs in proportion.  (Mixtral-shape down projection: 2 slices,
+// 1031 us against 1134-1151 with 1 and 1042-1046 with 4; 16 experts of about
+// 250 rows and K = 5632: 2 slices, 113 us against 138 with 4 and 161 with 1.)
+template <typename Allowed>
+static int pick_splits(int64_t tiles, int64_t steps, int s_min, Allowed allowed) {
+    constexpr int64_t kCUs = 256;
+    int best = s_min;
+    double best_cost = -1.0;
+    for (int s = s_min; s <= 8 && (s == s_min || allowed(s)); s *= 2) {
+        const int64_t items = std::max<int64_t>(tiles * s, 1);
+        double cost = (double)ceil_div(items, kCUs) * ((double)steps / s + 6.0);
+        if (items < kCUs) cost *= (double)kCUs / (double)items;
+        if (best_cost < 0.0 || cost < best_cost) best = s, best_cost = cost;
+    }
+    return best;
+}
+
+int ffn_splits(const moe_params &p, int64_t max_rows) {
+    if (p.dtype != MOE_BF16 || max_rows <= 0) return 1;
+    // small groups run the weight-streaming kernel, whose down projection is
+    // one slice (a CU per 128 output columns of an expert already fills the
+    // chip, and longer tiles stream better)
+    const int64_t cap = capacity_rows(p);
+    if (cap <= kSkBM) return 1;
+    const int64_t tiles = mtile_bound(max_rows, cap, p.E, kBM) * ceil_div(p.d, kBN);
+    const int64_t steps = p.d_ff / kBK;
+    return pick_splits(tiles, steps, 1, [steps](int s) { return steps % (4 * s) == 0; });
 }
 
 bool fp8_ffn_supported(const moe_params &p) {

@@ -80,13 +80,14 @@ def test_workspace_sizes_cover_buffers():
 
 def test_ffn_workspace_only_for_split_down_projections():
     """The expert FFN needs scratch only where its down projection is split
-    (few row tiles for the chip): the Mixtral-shape layer (2 slices) and the
-    skewed layer (4), not the fine-grained layer, the decode shape or fp32."""
+    (few row tiles for the chip): the Mixtral-shape layer and the skewed
+    layer (2 slices each), not the fine-grained layer, the decode shape or
+    fp32."""
     mix = P(T=4096, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
     skew = P(T=2048, d=2048, E=16, k=2, d_ff=5632, capacity_factor=1.0, dtype=moe.MOE_BF16)
     fine = P(T=8192, d=4096, E=64, k=2, d_ff=2048, capacity_factor=1.0, dtype=moe.MOE_BF16)
     dec = P(T=64, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
-    assert (splits_of(mix), splits_of(skew), splits_of(fine), splits_of(dec)) == (2, 4, 1, 1)
+    assert (splits_of(mix), splits_of(skew), splits_of(fine), splits_of(dec)) == (2, 2, 1, 1)
     assert moe.ffn_workspace_bytes(fine) == moe.ffn_workspace_bytes(dec) == 0
 
 
