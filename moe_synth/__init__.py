@@ -209,6 +209,20 @@ def quantize_rows_int8(w: torch.Tensor):
     return q.contiguous(), s.contiguous()
 
 
+def quantize_rows_int4(w: torch.Tensor):
+    """Synthetic INT4 weights from a weight tensor [..., rows, cols] (cols
+    even): an fp32 scale per row, amax / 7 (1 for an all-zero row), the codes
+    round-half-even(w / scale) in [-7, 7], packed two per byte, element 2j in
+    the low nibble of byte j (two's complement nibbles).  Returns (packed
+    uint8 [..., rows, cols / 2], scales fp32 [..., rows])."""
+    wf = w.float()
+    amax = wf.abs().amax(dim=-1)
+    s = torch.where(amax > 0, amax / 7.0, torch.ones_like(amax))
+    q = torch.round(wf / s[..., None]).clamp_(-7, 7).to(torch.int32) & 15
+    packed = (q[..., 0::2] | (q[..., 1::2] << 4)).to(torch.uint8)
+    return packed.contiguous(), s.contiguous()
+
+
 def upstream_grad(cfg: MoEConfig, device="cpu", seed: int = 0, T: Optional[int] = None) -> torch.Tensor:
     """Upstream gradient dy [T, d] of the layer output for the backward pass:
     N(0, 1) in the layer's dtype, substream "dy"."""

@@ -63,6 +63,8 @@ def lib():
         L.oracle_dequant_rows.argtypes = [i64, i64, P, P, P]
         L.oracle_dequant_rows_i8.argtypes = [i64, i64, P, P, P]
         L.oracle_dequant_rows_i8.restype = None
+        L.oracle_dequant_rows_i4.argtypes = [i64, i64, P, P, P]
+        L.oracle_dequant_rows_i4.restype = None
         L.oracle_backward_tokens.argtypes = [i32, P, i32, i32, i32, i32, i32, f64, P, P, P, P, P, P, P, P, P, P]
         L.oracle_backward_expert_units.argtypes = [i32, i32, P, i32, P, P, i32, i32, i32, P, P, P, P, P, P, P, P]
         L.oracle_router_wgrad.argtypes = [i32, i32, i32, i32, P, P, P, P]
@@ -245,6 +247,19 @@ def dequant_rows_i8(q, scale) -> np.ndarray:
     assert scale.shape == q.shape[:-1]
     w = np.empty(q.shape, np.float64)
     lib().oracle_dequant_rows_i8(scale.size, q.shape[-1], _p(q), _p(scale), _p(w))
+    return w
+
+
+def dequant_rows_i4(q, scale) -> np.ndarray:
+    """w[..., r, c] = scale[..., r] * q[..., r, c] in double, q INT4 codes
+    packed two per byte (element 2j in the low nibble of byte j): q has
+    cols / 2 bytes per row, w has cols elements."""
+    q = np.ascontiguousarray(_np(q), dtype=np.uint8)
+    scale = np.ascontiguousarray(_np(scale), dtype=np.float32)
+    assert scale.shape == q.shape[:-1]
+    cols = 2 * q.shape[-1]
+    w = np.empty(q.shape[:-1] + (cols,), np.float64)
+    lib().oracle_dequant_rows_i4(scale.size, cols, _p(q), _p(scale), _p(w))
     return w
 
 

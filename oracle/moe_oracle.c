@@ -125,6 +125,28 @@ void oracle_dequant_rows_i8(int64_t rows, int64_t cols, const int8_t *q, const f
             w[r * cols + c] = (double)scale[r] * (double)q[r * cols + c];
 }
 
+/*
+ * INT4 expert weights (P5 §5.1 quantises the weights of some experts to INT4;
+ * P3 §5.4 lists INT4 expert weights as the remedy for a bandwidth-bound
+ * dispatch).  Reading: a code is a two's complement nibble, value -8..7; a
+ * weight row of `cols` elements (cols even) is held in cols / 2 bytes, byte j
+ * carrying element 2j in its low nibble and element 2j + 1 in its high
+ * nibble; w[r][c] = scale[r] * q[r][c] with one fp32 scale per output row, as
+ * for the one-byte codes above; exact in double.
+ */
+static int nibble_value(uint8_t byte, int high)
+{
+    const int v = high ? (byte >> 4) & 15 : byte & 15;
+    return v >= 8 ? v - 16 : v;
+}
+
+void oracle_dequant_rows_i4(int64_t rows, int64_t cols, const uint8_t *q, const float *scale, double *w)
+{
+    for (int64_t r = 0; r < rows; r++)
+        for (int64_t c = 0; c < cols; c++)
+            w[r * cols + c] = (double)scale[r] * (double)nibble_value(q[r * (cols / 2) + c / 2], (int)(c & 1));
+}
+
 double oracle_dynamic_capacity_factor(int64_t T)
 {
     if (T < 1)

@@ -54,6 +54,9 @@ MUTATIONS = {
     "load_window_over_batch": ("((double)cnt[e] / ((double)k * n));", "((double)cnt[e] / ((double)k * T));"),
     "load_window_full_last": ("const int n = T - t0 < window ? T - t0 : window;", "const int n = window;"),
     "i8_codes_read_unsigned": ("(double)scale[r] * (double)q[r * cols + c];", "(double)scale[r] * (double)(uint8_t)q[r * cols + c];"),
+    "i4_nibbles_swapped": ("nibble_value(q[r * (cols / 2) + c / 2], (int)(c & 1))", "nibble_value(q[r * (cols / 2) + c / 2], (int)!(c & 1))"),
+    "i4_codes_read_unsigned": ("    return v >= 8 ? v - 16 : v;", "    return v;"),
+    "i4_offset_binary": ("    return v >= 8 ? v - 16 : v;", "    return v - 8;"),
     # backward pass
     "bwd_silu_derivative_first_term_only": ("const double da = dh * b[j] * sg * (1.0 + a[j] * (1.0 - sg));",
                                             "const double da = dh * b[j] * sg;"),
@@ -85,6 +88,7 @@ CHECKS = [
     ("dynamic_capacity", pins.check_dynamic_capacity),
     ("dequant_rows", pins.check_dequant_rows), ("ffn_double_elements", pins.check_ffn_double_elements),
     ("load_window", pins.check_load_window), ("dequant_rows_i8", pins.check_dequant_rows_i8),
+    ("dequant_rows_i4", pins.check_dequant_rows_i4),
     ("backward_autograd", bwd.check_backward_autograd),
     ("backward_finite_differences", bwd.check_backward_finite_differences),
     ("backward_invariants", bwd.check_backward_invariants),

@@ -794,3 +794,29 @@ def check_dequant_rows_i8(o):
 
 def test_dequant_rows_i8(oracle_mod):
     check_dequant_rows_i8(oracle_mod)
+
+
+def check_dequant_rows_i4(o):
+    """INT4 codes, two per byte: every nibble value at scale 1 is the two's
+    complement integer it spells (0x0..0x7 -> 0..7, 0x8..0xF -> -8..-1,
+    written out), in either half of a byte; the low nibble is the earlier
+    element (a byte 0x21 holds 1 then 2); a scaled row is the exact product
+    scale * code."""
+    spelled = [0, 1, 2, 3, 4, 5, 6, 7, -8, -7, -6, -5, -4, -3, -2, -1]
+    # row 0: byte j = (j, 0): the low nibbles run through 0..15 (high 0);
+    # row 1: byte j = (0, j): the high nibbles do
+    q = np.array([[j for j in range(16)], [j << 4 for j in range(16)]], np.uint8)
+    w = o.dequant_rows_i4(q, np.ones(2, np.float32))
+    assert w.shape == (2, 32)
+    assert w[0, 0::2].tolist() == spelled and w[0, 1::2].tolist() == [0.0] * 16
+    assert w[1, 1::2].tolist() == spelled and w[1, 0::2].tolist() == [0.0] * 16
+    w = o.dequant_rows_i4(np.array([[0x21, 0x8F]], np.uint8), np.ones(1, np.float32))
+    assert w.tolist() == [[1.0, 2.0, -1.0, -8.0]]
+    s = np.array([0.0123, -3.5], np.float32)
+    w = o.dequant_rows_i4(q, s)
+    assert w[0, 16] == -8 * float(s[0]) and w[1, 15] == 7 * float(s[1])
+    assert np.array_equal(w[:, 0::2][0], np.array(spelled, np.float64) * float(s[0]))
+
+
+def test_dequant_rows_i4(oracle_mod):
+    check_dequant_rows_i4(oracle_mod)
