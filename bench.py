@@ -37,6 +37,9 @@ def parse():
     ap.add_argument("--int8-weights", action="store_true",
                     help="expert weights as INT8 codes with fp32 row scales (weight-streaming layers: "
                          "capacity <= 32 rows per expert)")
+    ap.add_argument("--int4-weights", action="store_true",
+                    help="expert weights as INT4 codes, two per byte, with fp32 row scales (weight-streaming "
+                         "layers only: capacity <= 32 rows per expert)")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the step-time distribution, cold-cache steps and amd-smi sampling "
                          "(for runs under a profiler)")
@@ -66,7 +69,7 @@ def counter_traffic(workload, qfmt=None):
     its kernel source changed since the counters were taken."""
     import hashlib
     import re
-    suffix = {None: "", "e4m3": "_fp8", "int8": "_int8"}[qfmt]
+    suffix = {None: "", "e4m3": "_fp8", "int8": "_int8", "int4": "_int4"}[qfmt]
     path = os.path.join(ROOT, "profiles", f"moe_forward_{workload}{suffix}_traffic.md")
     if not os.path.exists(path):
         return {}
@@ -85,11 +88,11 @@ def counter_traffic(workload, qfmt=None):
     return out
 
 
-def stage_work(cfg, rows, active_experts, fp8=False):
+def stage_work(cfg, rows, active_experts, fp8=False, code_bits=8):
     """Algorithmic work per stage of one forward pass: what the method must
     touch (kept rows, active experts, one read of x, one write of y), not
-    what this implementation moves.  fp8: expert weights of one byte plus an
-    fp32 scale per weight row."""
+    what this implementation moves.  fp8: expert weights as codes of
+    code_bits bits (8 or 4) plus an fp32 scale per weight row."""
     T, d, E, dff, k = cfg.T, cfg.d, cfg.E, cfg.d_ff, cfg.k
     es = 2 if cfg.dtype == "bf16" else 4
     k1 = k + 1
@@ -99,7 +102,8 @@ def stage_work(cfg, rows, active_experts, fp8=False):
     # token_of_row written (moe_forward gathers x inside the GEMM, so no copy)
     dispatch_bytes = T * k1 * 8 + T * k * 17 + rows * 4
     gemm_flops = rows * 6.0 * d * dff
-    gemm_weight_bytes = active_experts * (3 * d * dff + (2 * dff + d) * 4 if fp8 else 3 * d * dff * es)
+    gemm_weight_bytes = active_experts * (3 * d * dff * code_bits // 8 + (2 * dff + d) * 4 if fp8
+                                          else 3 * d * dff * es)
     # combine: each kept row's expert output (layer dtype) read once, y written,
     # the slot arrays read
     combine_bytes = rows * d * es + T * d * es + T * k * 8
@@ -139,15 +143,20 @@ def main():
     dt = p.torch_dtype
     T, d, E, k = cfg.T, cfg.d, cfg.E, cfg.k
     fp8 = None
-    qfmt = "int8" if args.int8_weights else "e4m3" if args.fp8_weights else None
+    qfmt = "int4" if args.int4_weights else "int8" if args.int8_weights else "e4m3" if args.fp8_weights else None
     if qfmt:
         small = moe.capacity(p) <= 32
         if not (p.dtype == moe.MOE_BF16 and (not small or (d % 128 == 0 and cfg.d_ff % 128 == 0))):
-            print(f"bench.py: one-byte weights need a bf16 layer (with d, d_ff multiples of 128 when every expert "
+            print(f"bench.py: quantised weights need a bf16 layer (with d, d_ff multiples of 128 when every expert "
                   f"holds at most 32 rows); {cfg.name} is {cfg.dtype}", file=sys.stderr)
             sys.exit(2)
+        if qfmt == "int4" and not (small and d % 128 == 0 and cfg.d_ff % 128 == 0):
+            print(f"bench.py: INT4 weights run on the weight-streaming kernel only (at most 32 rows per expert, "
+                  f"d and d_ff multiples of 128); {cfg.name} has capacity {moe.capacity(p)}", file=sys.stderr)
+            sys.exit(2)
         fp8 = {"fmt": qfmt}
-        quant = moe_synth.quantize_rows_int8 if qfmt == "int8" else moe_synth.quantize_rows_e4m3
+        quant = {"int4": moe_synth.quantize_rows_int4, "int8": moe_synth.quantize_rows_int8,
+                 "e4m3": moe_synth.quantize_rows_e4m3}[qfmt]
         for n in ("w1", "w3", "w2"):
             fp8["q" + n[1]], fp8["s" + n[1]] = quant(L[n])
             L[n] = None
@@ -173,7 +182,7 @@ def main():
 
     def step(events=None):
         if fp8:
-            (moe.forward_i8 if fp8["fmt"] == "int8" else moe.forward_fp8)(
+            {"int4": moe.forward_i4, "int8": moe.forward_i8, "e4m3": moe.forward_fp8}[fp8["fmt"]](
                 p, L["x"], L["w_router"], L["bias"], load, fp8["q1"], fp8["s1"], fp8["q3"], fp8["s3"], fp8["q2"],
                 fp8["s2"], y, logits, r, ws)
         elif events is not None:
@@ -230,7 +239,7 @@ def main():
     kept = r.kept.cpu()
     rows = int(totals[0])
     active = int((kept > 0).sum())
-    work = stage_work(cfg, rows, active, fp8=bool(fp8))
+    work = stage_work(cfg, rows, active, fp8=bool(fp8), code_bits=4 if fp8 and fp8["fmt"] == "int4" else 8)
     traffic = counter_traffic(args.workload, qfmt=fp8["fmt"] if fp8 else None)
     layer_flops = work["route_flops"] + work["gemm_flops"]
 
@@ -467,7 +476,8 @@ def cpu_baseline(cfg, L, load, target_s, fp8=None):
     c = {n: (oracle._np(v) if v is not None else None) for n, v in L.items()}
     xe = c["x"]
     if fp8:
-        deq = oracle.dequant_rows_i8 if fp8["fmt"] == "int8" else oracle.dequant_rows
+        deq = {"int4": oracle.dequant_rows_i4, "int8": oracle.dequant_rows_i8,
+               "e4m3": oracle.dequant_rows}[fp8["fmt"]]
         for j in ("1", "3", "2"):
             c["w" + j] = deq(fp8["q" + j].cpu().numpy(), fp8["s" + j].cpu().numpy())
         xe = L["x"].float().cpu().numpy().astype(np.float64)

@@ -397,6 +397,32 @@ int moe_forward_i8(const moe_params *p, const void *x, const void *w_router, con
                    const float *s3, const int8_t *w2, const float *s2, void *y, float *logits,
                    moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * INT4 expert weights: two's complement codes -8..7, two per byte (element 2j
+ * of a row in the low nibble of byte j, 2j + 1 in the high nibble), with one
+ * fp32 scale per output row: W[e][j][i] = s[e][j] * q[e][j][i]
+ * ("企业官网建设流程全解析" page §5.1 quantises some experts to INT4;
+ * "MoE稀疏激活原理与工程实践" §5.4 names INT4 expert weights as the remedy
+ * for a bandwidth-bound dispatch).  The scale granularity is not on the
+ * pages; one scale per output row keeps each dot product a scaled sum, as for
+ * the one-byte codes.
+ *   q1, q3 [E][d_ff][d/2] bytes, s1, s3 [E][d_ff] fp32; q2 [E][d][d_ff/2]
+ *   bytes, s2 [E][d] fp32; q pointers 16-byte aligned, scales 4-byte aligned.
+ * The codes are widened exactly to bf16 (W1/W3) or fp16 (W2) in registers
+ * and the scales multiply the fp32 accumulators.  Activations and outputs as
+ * for moe_expert_ffn_fp8 / moe_forward_fp8 (same workspace size).  Only the
+ * weight-streaming kernel takes INT4 codes: dtype MOE_BF16, every expert at
+ * most 32 rows (moe_capacity(p) <= 32) and d, d_ff multiples of 128, else
+ * MOE_ERR_UNSUPPORTED.
+ */
+int moe_expert_ffn_i4(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                      const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
+                      const uint8_t *w2, const float *s2, void *h, void *y_perm, void *stream);
+int moe_forward_i4(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                   const float *load, const uint8_t *w1, const float *s1, const uint8_t *w3,
+                   const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
+                   moe_routing *r, void *workspace, size_t ws_bytes, void *stream);
+
 /* Static description of a return code. */
 const char *moe_strerror(int code);
 

@@ -88,6 +88,8 @@ def lib():
         L.moe_forward_fp8.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, PR, P, ctypes.c_size_t, P]
         L.moe_expert_ffn_i8.argtypes = L.moe_expert_ffn_fp8.argtypes
         L.moe_forward_i8.argtypes = L.moe_forward_fp8.argtypes
+        L.moe_expert_ffn_i4.argtypes = L.moe_expert_ffn_fp8.argtypes
+        L.moe_forward_i4.argtypes = L.moe_forward_fp8.argtypes
         for f in (L.moe_expert_ffn_i8, L.moe_forward_i8):
             f.restype = ctypes.c_int
         for f in (L.moe_route, L.moe_dispatch, L.moe_expert_ffn, L.moe_combine, L.moe_forward,
@@ -298,6 +300,25 @@ def forward_i8(p: Params, x, w_router, bias, load, q1, s1, q3, s3, q2, s2, y, lo
                               _ptr(logits), ctypes.byref(r.c()), _ptr(workspace),
                               workspace.numel() * workspace.element_size(), _stream(stream))
     _check(rc, "moe_forward_i8")
+
+
+def expert_ffn_i4(p: Params, x_perm, offsets, q1, s1, q3, s3, q2, s2, h, y_perm, stream=None):
+    """Stage 3 with INT4 expert weights (two codes per byte) and fp32 row
+    scales."""
+    rc = lib().moe_expert_ffn_i4(ctypes.byref(p.c()), _ptr(x_perm), _ptr(offsets), _ptr(q1), _ptr(s1),
+                                 _ptr(q3), _ptr(s3), _ptr(q2), _ptr(s2), _ptr(h), _ptr(y_perm), _stream(stream))
+    _check(rc, "moe_expert_ffn_i4")
+
+
+def forward_i4(p: Params, x, w_router, bias, load, q1, s1, q3, s3, q2, s2, y, logits, r: Routing,
+               workspace, stream=None):
+    """The layer with INT4 expert weights (two codes per byte) and fp32 row
+    scales."""
+    rc = lib().moe_forward_i4(ctypes.byref(p.c()), _ptr(x), _ptr(w_router), _ptr(bias), _ptr(load),
+                              _ptr(q1), _ptr(s1), _ptr(q3), _ptr(s3), _ptr(q2), _ptr(s2), _ptr(y),
+                              _ptr(logits), ctypes.byref(r.c()), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), _stream(stream))
+    _check(rc, "moe_forward_i4")
 
 
 def alloc_workspace(p: Params, device="cuda", dispatch_only: bool = False, ffn_only: bool = False) -> torch.Tensor:

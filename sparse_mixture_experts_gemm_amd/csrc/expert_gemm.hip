@@ -1305,6 +1305,230 @@ __global__ __launch_bounds__(kSkThreads, 2) void grouped_gemm_skinny_fp8(
         }
 }
 
+// ------------------------------------------------------ skinny, INT4 W ----
+// INT4 expert weights with one fp32 scale per weight row, W[n][k] = s[n] *
+// q[n][k], q a two's complement nibble (-8..7), two per byte (element 2j in
+// the low nibble of byte j), in the weight-streaming regime (every expert at
+// most 32 rows).  The tile is that of the one-byte kernel (32 rows x 128
+// weight rows) and a stage again spans 128 K elements: the A part is the
+// one-byte kernel's (x or h rows of 256 bytes), the weight rows are 64 bytes.
+// Five stages of 16 KiB per block and two blocks per CU keep up to eight
+// stages (64 KiB of codes) in flight per CU, as the one-byte kernel does.
+// The down projection takes 64 output columns per tile (one weight fragment
+// per wave): with 128, a decode layer's down projection has one tile per CU
+// and streams at the latency of a single block.
+//
+// Widening, per 32-bit word of eight codes: the word masked to its high
+// nibbles holds the odd elements, and the word shifted up by four and masked
+// likewise the even ones, each as a signed byte 16 q; one conversion with a
+// sign-extending byte select turns such a byte into fp32, exactly, and two
+// of them are packed to bf16 (gate-up) or fp16 (down), both exact for
+// |16 q| <= 128.  The factor 16 leaves with the row scale in the epilogue.
+constexpr int kSk4BNd = 64;               // output columns per down tile
+constexpr int kSk4B = 2 * kSkBN * 64;     // B part: 128 weight rows x 64 bytes (8 KiB; down: 4 KiB used)
+constexpr int kSk4Stage = kSk8A + kSk4B;  // 16 KiB
+constexpr int kSk4Stages = 5;
+// weight fragments per wave (16 columns each): gate-up W1 and W3, down one
+template <int MODE>
+__device__ __forceinline__ constexpr int sk4_nf() { return MODE == kGateUp ? 2 : 1; }
+
+struct Sk4Thread {
+    const char *a_base;
+    const char *b_base[2];
+    uint32_t a_off[2];  // wave w loads A rows 8w .. 8w+7, four per load
+    uint32_t b_off[2];  // wave w loads B rows 16 nf w .. + 16 nf - 1, sixteen per load
+    int wave;
+};
+
+// eight INT4 codes of one word -> eight values 16 q as bf16 (gate-up) or
+// fp16 (down), element i from nibble i
+template <bool F16>
+__device__ __forceinline__ uint32_t i4x2_widen(uint32_t ev, uint32_t od, int byte) {
+    const float a = (float)(int32_t)__builtin_amdgcn_sbfe(ev, 8 * byte, 8),
+                b = (float)(int32_t)__builtin_amdgcn_sbfe(od, 8 * byte, 8);
+    if constexpr (F16) return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+    else return __builtin_amdgcn_perm(__float_as_uint(b), __float_as_uint(a), 0x07060302u);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint4 i4x8_widen(uint32_t w) {
+    const uint32_t ev = (w << 4) & 0xF0F0F0F0u, od = w & 0xF0F0F0F0u;
+    return make_uint4(i4x2_widen<F16>(ev, od, 0), i4x2_widen<F16>(ev, od, 1), i4x2_widen<F16>(ev, od, 2),
+                      i4x2_widen<F16>(ev, od, 3));
+}
+
+template <int MODE>
+__device__ __forceinline__ void sk4_issue(const Sk4Thread &g, char *stage, int k) {
+    const uint32_t ka = (uint32_t)k * kSk8K * 2, kq = (uint32_t)k * (kSk8K / 2);
+    g2lds16(g.a_base + g.a_off[0] + ka, stage + (2 * g.wave) * 1024);
+    g2lds16(g.a_base + g.a_off[1] + ka, stage + (2 * g.wave + 1) * 1024);
+#pragma unroll
+    for (int j = 0; j < sk4_nf<MODE>(); j++) {
+        const int grp = g.wave * sk4_nf<MODE>() + j;     // 16-row group of the B part
+        const int src = MODE == kGateUp ? grp >> 2 : 0;  // gate-up: groups 4.. are W3
+        g2lds16((src ? g.b_base[1] : g.b_base[0]) + g.b_off[j] + kq, stage + kSk8A + grp * 1024);
+    }
+}
+
+template <int MODE, int NB>
+__device__ __forceinline__ void sk4_compute(const char *stage, int wave, int lane, f32x4_t (&acc)[2][2]) {
+    constexpr bool kF16 = MODE == kDown;
+    const int r16 = lane & 15, kq = lane >> 4;
+    constexpr int NF = sk4_nf<MODE>();
+    const int rb0 = 16 * wave + r16;          // W1 rows (gate-up) or W2 rows (down)
+    const int rb1 = kSkBN + 16 * wave + r16;  // gate-up: the same rows of W3
+    // The stage's K elements in an order of their own (both operands follow
+    // it): lane quarter kq takes elements 32 kq .. 32 kq + 31, one 16-byte
+    // chunk of each weight row (64-byte rows, chunks XOR-swizzled by
+    // swz4(row)), eight of them (one word) per sub-step; the x fragments are
+    // the same eight elements, chunk 4 kq + ss of the 256-byte row.
+    u32x4_t q[2], a[4][2];  // [weight fragment], [sub-step][16-row block]
+    q[0] = lds_read16_async(stage + kSk8A + rb0 * 64 + ((kq ^ swz4(rb0)) << 4));
+    q[1] = NF == 2 ? lds_read16_async(stage + kSk8A + rb1 * 64 + ((kq ^ swz4(rb1)) << 4)) : q[0];
+#pragma unroll
+    for (int ss = 0; ss < 4; ss++) {
+        const int c = 4 * kq + ss;
+#pragma unroll
+        for (int ib = 0; ib < 2; ib++) {
+            const int row = ib * 16 + r16;
+            a[ss][ib] = lds_read16_async(stage + row * 256 + ((c ^ swz16(row)) << 4));
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(q[0]), "+v"(q[1]), "+v"(a[0][0]), "+v"(a[0][1]), "+v"(a[1][0]), "+v"(a[1][1]),
+                   "+v"(a[2][0]), "+v"(a[2][1]), "+v"(a[3][0]), "+v"(a[3][1])
+                 :
+                 : "memory");
+#pragma unroll
+    for (int ss = 0; ss < 4; ss++) {
+        const uint4 b0 = i4x8_widen<kF16>(q[0][ss]);
+        const uint4 b1 = NF == 2 ? i4x8_widen<kF16>(q[1][ss]) : b0;
+#pragma unroll
+        for (int ib = 0; ib < NB; ib++) {
+            const uint4 av = __builtin_bit_cast(uint4, a[ss][ib]);
+            acc[ib][0] = mfma16<kF16>(av, b0, acc[ib][0]);
+            if (NF == 2) acc[ib][1] = mfma16<kF16>(av, b1, acc[ib][1]);
+        }
+    }
+}
+
+#define SK4_STEP(I, cur, nxt)                                                            \
+    do {                                                                                 \
+        if (k0 + (I) >= nk) goto done;                                                   \
+        WAIT_VMCNT((2 + sk4_nf<MODE>()) * (kSk4Stages - 2));                             \
+        block_sync();                                                                    \
+        sk4_issue<MODE>(g, nxt, min(k0 + (I) + kSk4Stages - 1, nk - 1));                 \
+        sk4_compute<MODE, NB>(cur, g.wave, lane, acc);                                   \
+    } while (0)
+
+// The K loop over a ring of five stages of 128 K elements: when stage k is
+// computed, stages k+1 .. k+3 are in flight and stage k+4 is issued into the
+// buffer stage k-1 used (free: every wave passed the barrier after it).
+// Loads past the last stage re-read the last K slice.
+template <int MODE, int NB>
+__device__ __forceinline__ void sk4_main(const Sk4Thread &g, int nk, int lane, char *b0, char *b1, char *b2,
+                                         char *b3, char *b4, f32x4_t (&acc)[2][2]) {
+    sk4_issue<MODE>(g, b0, 0);
+    sk4_issue<MODE>(g, b1, min(1, nk - 1));
+    sk4_issue<MODE>(g, b2, min(2, nk - 1));
+    sk4_issue<MODE>(g, b3, min(3, nk - 1));
+    for (int k0 = 0;; k0 += kSk4Stages) {
+        SK4_STEP(0, b0, b4);
+        SK4_STEP(1, b1, b0);
+        SK4_STEP(2, b2, b1);
+        SK4_STEP(3, b3, b2);
+        SK4_STEP(4, b4, b3);
+    }
+done:
+    WAIT_VMCNT(0);
+}
+#undef SK4_STEP
+
+template <int MODE>
+__global__ __launch_bounds__(kSkThreads, 2) void grouped_gemm_skinny_i4(
+    const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint8_t *__restrict__ B0,
+    const uint8_t *__restrict__ B1, const float *__restrict__ S0, const float *__restrict__ S1,
+    const int32_t *__restrict__ offsets, int E, int N, int K, int ntiles_n, GemmOut out) {
+    __shared__ __attribute__((aligned(1024))) char sb0[kSk4Stage];
+    __shared__ __attribute__((aligned(1024))) char sb1[kSk4Stage];
+    __shared__ __attribute__((aligned(1024))) char sb2[kSk4Stage];
+    __shared__ __attribute__((aligned(1024))) char sb3[kSk4Stage];
+    __shared__ __attribute__((aligned(1024))) char sb4[kSk4Stage];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    TileInfo ti;
+    if (!find_tile(offsets, E, ntiles_n, kSkBM, 1, blockIdx.x, nullptr, nullptr, ti)) return;
+    const int n0 = ti.nt * (MODE == kGateUp ? kSkBN : kSk4BNd);
+    const size_t wexp = (size_t)ti.e * N * (K / 2);  // bytes: two codes per byte
+
+    Sk4Thread g;
+    g.wave = wave;
+    g.a_base = reinterpret_cast<const char *>(a_rows ? A : A + (size_t)ti.m0 * K);
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const int row = (2 * wave + j) * 4 + (lane >> 4);
+        const int c = (lane & 15) ^ swz16(row);
+        const int gm = min(ti.m0 + row, ti.mend - 1);
+        const int ar = a_rows ? a_rows[gm] : gm - ti.m0;
+        g.a_off[j] = ((uint32_t)ar * K + c * 8) * 2;
+    }
+    g.b_base[0] = reinterpret_cast<const char *>(B0 + wexp);
+    g.b_base[1] = reinterpret_cast<const char *>((MODE == kGateUp ? B1 : B0) + wexp);
+#pragma unroll
+    for (int j = 0; j < sk4_nf<MODE>(); j++) {
+        // 16-row group of 64-byte rows; lane l takes row 16 grp + l / 4 and
+        // the logical chunk that lands at position l % 4
+        const int grp = wave * sk4_nf<MODE>() + j;
+        const int row = grp * 16 + (lane >> 2);
+        const int c = (lane & 3) ^ swz4(row);
+        const int gn = min(n0 + (MODE == kGateUp ? (row & (kSkBN - 1)) : row), N - 1);
+        g.b_off[j] = (uint32_t)gn * (K / 2) + c * 16;
+    }
+    // the row scales of the lane's output columns (divided by the 16 of the
+    // widening), fetched before the K loop
+    const float *s0e = S0 + (size_t)ti.e * N, *s1e = (MODE == kGateUp ? S1 : S0) + (size_t)ti.e * N;
+    float sc[2];
+#pragma unroll
+    for (int jb = 0; jb < 2; jb++) {
+        const int col = n0 + wave * 16 + (lane & 15);
+        sc[jb] = (MODE == kGateUp && jb == 1 ? s1e : s0e)[min(col, N - 1)] * 0.0625f;
+    }
+    const int nk = K / kSk8K;
+    f32x4_t acc[2][2];
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+        for (int jb = 0; jb < 2; jb++) acc[ib][jb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+    const int nb = ti.mend - ti.m0 > 16 ? 2 : 1;  // active 16-row blocks (uniform)
+    if (nb == 2)
+        sk4_main<MODE, 2>(g, nk, lane, sb0, sb1, sb2, sb3, sb4, acc);
+    else
+        sk4_main<MODE, 1>(g, nk, lane, sb0, sb1, sb2, sb3, sb4, acc);
+
+    // epilogue: the lane holds column lane % 16, rows 4 * (lane / 16) + q
+#pragma unroll
+    for (int ib = 0; ib < 2; ib++)
+#pragma unroll
+        for (int q = 0; q < 4; q++) {
+            const int m = ti.m0 + ib * 16 + 4 * (lane >> 4) + q;
+            if (m >= ti.mend) continue;
+            if (MODE == kGateUp) {
+                const int col = n0 + wave * 16 + (lane & 15);
+                if (col < N)
+                    static_cast<uint16_t *>(out.y0)[(size_t)m * N + col] =
+                        f32_to_f16_sat(silu_mul(acc[ib][0][q] * sc[0], acc[ib][1][q] * sc[1]));
+            } else {
+                const int col = n0 + wave * 16 + (lane & 15);
+                if (col >= N) continue;
+                if (out.row_gate)
+                    static_cast<uint16_t *>(out.y0)[(size_t)m * N + col] =
+                        f32_to_f16_sat(out.row_gate[m] * (acc[ib][0][q] * sc[0]));
+                else
+                    static_cast<float *>(out.y0)[(size_t)m * N + col] = acc[ib][0][q] * sc[0];
+            }
+        }
+}
+
 // ---------------------------------------------------------------- fp32 ----
 constexpr int kF32BM = 64, kF32BN = 64, kF32BK = 16;
 
@@ -1407,6 +1631,12 @@ int ffn_splits(const moe_params &p, int64_t max_rows) {
     return pick_splits(tiles, steps, 1, [steps](int s) { return steps % (4 * s) == 0; });
 }
 
+bool q4_ffn_supported(const moe_params &p) {
+    // the weight-streaming kernel only (at most 32 rows per expert), which
+    // steps K by 128
+    return p.dtype == MOE_BF16 && capacity_rows(p) <= kSkBM && p.d % kSk8K == 0 && p.d_ff % kSk8K == 0;
+}
+
 bool fp8_ffn_supported(const moe_params &p) {
     // the weight-streaming kernel (at most 32 rows per expert) steps K by 128
     return p.dtype == MOE_BF16 && (capacity_rows(p) > kSkBM || (p.d % kSk8K == 0 && p.d_ff % kSk8K == 0));
@@ -1453,6 +1683,22 @@ static void launch_q8(const moe_params &p, int64_t mt, const void *x_perm, const
                        dff, nt_dn, down);
 }
 
+static void launch_q4(const moe_params &p, int64_t mt, const void *x_perm, const int32_t *a_rows,
+                      const int32_t *offsets, const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
+                      const uint8_t *w2, const float *s2, void *h, const GemmOut &down, hipEvent_t mid,
+                      hipError_t &ev, hipStream_t st) {
+    const int E = p.E, d = p.d, dff = p.d_ff;
+    const int nt_up = (int)ceil_div(dff, kSkBN);
+    const int nt_dn = (int)ceil_div(d, kSk4BNd);
+    hipLaunchKernelGGL(grouped_gemm_skinny_i4<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
+                       static_cast<const uint16_t *>(x_perm), a_rows, w1, w3, s1, s3, offsets, E, dff, d, nt_up,
+                       GemmOut{h, nullptr, 0, nullptr});
+    if (mid) ev = hipEventRecord(mid, st);
+    hipLaunchKernelGGL(grouped_gemm_skinny_i4<kDown>, dim3((unsigned)(mt * nt_dn)), dim3(kSkThreads), 0, st,
+                       static_cast<const uint16_t *>(h), (const int32_t *)nullptr, w2, w2, s2, s2, offsets, E, d,
+                       dff, nt_dn, down);
+}
+
 // One-byte weights on the 256 x 256 MFMA tile (groups of more than 32 rows).
 template <int GU, int DN>
 static void launch_q8_mfma(const moe_params &p, int64_t mt, const void *x_perm, const int32_t *a_rows,
@@ -1480,9 +1726,12 @@ hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t 
                                  const GemmOut &down, int splits, int32_t *claim, hipEvent_t mid, int qfmt,
                                  hipStream_t st) {
     if (max_rows <= 0) return hipSuccess;
-    if (!fp8_ffn_supported(p)) return hipErrorInvalidValue;
+    if (qfmt == MOE_Q_INT4 ? !q4_ffn_supported(p) : !fp8_ffn_supported(p)) return hipErrorInvalidValue;
     hipError_t ev = hipSuccess;
-    if (cap <= kSkBM) {
+    if (qfmt == MOE_Q_INT4) {
+        const int64_t mt = mtile_bound(max_rows, cap, p.E, kSkBM);
+        launch_q4(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);
+    } else if (cap <= kSkBM) {
         const int64_t mt = mtile_bound(max_rows, cap, p.E, kSkBM);
         if (qfmt == MOE_Q_INT8)
             launch_q8<kQInt8>(p, mt, x_perm, a_rows, offsets, w1, s1, w3, s3, w2, s2, h, down, mid, ev, st);

@@ -87,8 +87,8 @@ int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 bool aligned4(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
-// Expert weights of a forward pass: matrices of the layer's dtype, or
-// one-byte codes (E4M3 or INT8, qfmt) with fp32 row scales (s1 non-null).
+// Expert weights of a forward pass: matrices of the layer's dtype, or codes
+// (E4M3, INT8 or INT4, qfmt) with fp32 row scales (s1 non-null).
 struct FfnWeights {
     const void *w1, *w3, *w2;
     const float *s1, *s3, *s2;
@@ -97,7 +97,7 @@ struct FfnWeights {
 
 int fp8_weights_ok(const moe_params &p, const FfnWeights &w) {
     if (!w.w1 || !w.w3 || !w.w2 || !w.s1 || !w.s3 || !w.s2) return MOE_ERR_INVALID_ARG;
-    if (!fp8_ffn_supported(p)) return MOE_ERR_UNSUPPORTED;
+    if (w.qfmt == MOE_Q_INT4 ? !q4_ffn_supported(p) : !fp8_ffn_supported(p)) return MOE_ERR_UNSUPPORTED;
     if (!aligned16(w.w1) || !aligned16(w.w3) || !aligned16(w.w2) || !aligned4(w.s1) || !aligned4(w.s3) ||
         !aligned4(w.s2))
         return MOE_ERR_UNSUPPORTED;
@@ -408,6 +408,12 @@ int moe_expert_ffn_i8(const moe_params *p, const void *x_perm, const int32_t *of
     return expert_ffn_q8(p, x_perm, offsets, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_INT8}, h, y_perm, stream);
 }
 
+int moe_expert_ffn_i4(const moe_params *p, const void *x_perm, const int32_t *offsets,
+                      const uint8_t *w1, const float *s1, const uint8_t *w3, const float *s3,
+                      const uint8_t *w2, const float *s2, void *h, void *y_perm, void *stream) {
+    return expert_ffn_q8(p, x_perm, offsets, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_INT4}, h, y_perm, stream);
+}
+
 int moe_combine(const moe_params *p, const void *y_perm, const int32_t *row, const float *gate,
                 void *y, void *stream) {
     int rc = check_params(p);
@@ -525,6 +531,15 @@ int moe_forward_i8(const moe_params *p, const void *x, const void *w_router, con
                    moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
     if (!s1 || !s3 || !s2) return MOE_ERR_INVALID_ARG;
     return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_INT8}, y, logits, r,
+                        workspace, ws_bytes, stream, nullptr);
+}
+
+int moe_forward_i4(const moe_params *p, const void *x, const void *w_router, const float *bias,
+                   const float *load, const uint8_t *w1, const float *s1, const uint8_t *w3,
+                   const float *s3, const uint8_t *w2, const float *s2, void *y, float *logits,
+                   moe_routing *r, void *workspace, size_t ws_bytes, void *stream) {
+    if (!s1 || !s3 || !s2) return MOE_ERR_INVALID_ARG;
+    return forward_impl(p, x, w_router, bias, load, FfnWeights{w1, w3, w2, s1, s3, s2, MOE_Q_INT4}, y, logits, r,
                         workspace, ws_bytes, stream, nullptr);
 }
 

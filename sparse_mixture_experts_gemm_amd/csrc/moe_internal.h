@@ -117,8 +117,11 @@ hipError_t launch_ffn_fixup(const moe_params &p, int64_t max_rows, const int32_t
 // weights (ffn_splits) and claim counters as for launch_expert_ffn.
 // fp8_ffn_supported tells whether a layer qualifies.
 bool fp8_ffn_supported(const moe_params &p);
-// one-byte weight code formats
-enum { MOE_Q_E4M3 = 0, MOE_Q_INT8 = 1 };
+// INT4 codes (two per byte): the weight-streaming kernel only, so every
+// expert must hold at most 32 rows (d and d_ff multiples of 128)
+bool q4_ffn_supported(const moe_params &p);
+// weight code formats
+enum { MOE_Q_E4M3 = 0, MOE_Q_INT8 = 1, MOE_Q_INT4 = 2 };
 hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                                  const int32_t *a_rows, const int32_t *offsets, const uint8_t *w1, const float *s1,
                                  const uint8_t *w3, const float *s3, const uint8_t *w2, const float *s2, void *h,

@@ -192,6 +192,36 @@ def test_dynamic_capacity_matches_oracle(oracle_mod):
     assert rc == moe.MOE_ERR_INVALID_ARG
 
 
+def i4_ffn_rc(p, s_ptr=256):
+    return moe.lib().moe_expert_ffn_i4(ctypes.byref(p.c()), 256, 256, 256, s_ptr, 256, s_ptr, 256, s_ptr,
+                                       256, 256, None)
+
+
+def test_int4_weights_limits_rejected():
+    """INT4 expert weights run on the weight-streaming kernel only: bf16
+    layers whose experts hold at most 32 rows, d and d_ff multiples of 128;
+    a layer with larger groups is unsupported (not an invalid argument) and
+    missing scales are an invalid argument.  Every case is rejected before
+    any launch (the fake addresses are never touched)."""
+    ok = dict(T=64, d=512, E=8, k=2, d_ff=1024, capacity_factor=1.25, dtype=moe.MOE_BF16)
+    assert moe.capacity(P(**ok)) == 20
+    assert i4_ffn_rc(P(**ok), s_ptr=None) == moe.MOE_ERR_INVALID_ARG
+    for bad in (dict(dtype=moe.MOE_F32), dict(d=448), dict(d_ff=960), dict(T=256, capacity_factor=1.0),
+                dict(capacity_factor=-1.0)):
+        kw = dict(ok)
+        kw.update(bad)
+        assert i4_ffn_rc(P(**kw)) == moe.MOE_ERR_UNSUPPORTED, bad
+    r = moe.MoeRouting(*[256] * len(moe.Routing.NAMES))
+    big = P(**dict(ok, T=256, capacity_factor=1.0))
+    assert moe.capacity(big) == 64
+    rc = moe.lib().moe_forward_i4(ctypes.byref(big.c()), 256, 256, None, None, 256, 256, 256, 256, 256, 256,
+                                  256, 256, ctypes.byref(r), 256, moe.workspace_bytes(big), None)
+    assert rc == moe.MOE_ERR_UNSUPPORTED
+    rc = moe.lib().moe_forward_i4(ctypes.byref(P(**ok).c()), 256, 256, None, None, 256, None, 256, 256, 256,
+                                  256, 256, 256, ctypes.byref(r), 256, 1 << 30, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+
+
 def fp8_ffn_rc(p, s_ptr=256):
     return moe.lib().moe_expert_ffn_fp8(ctypes.byref(p.c()), 256, 256, 256, s_ptr, 256, s_ptr, 256, s_ptr,
                                         256, 256, None)

@@ -1,10 +1,12 @@
-"""GPU parity of the one-byte expert weights, OCP E4M3 codes
-(moe_expert_ffn_fp8, moe_forward_fp8) and INT8 codes (moe_expert_ffn_i8,
-moe_forward_i8), through the C ABI against the oracle, which dequantises the
+"""GPU parity of the quantised expert weights, OCP E4M3 codes
+(moe_expert_ffn_fp8, moe_forward_fp8), INT8 codes (moe_expert_ffn_i8,
+moe_forward_i8) and INT4 codes two per byte (moe_expert_ffn_i4,
+moe_forward_i4), through the C ABI against the oracle, which dequantises the
 same codes and scales exactly (double) and runs its plain SwiGLU FFN.
 
 Groups of at most 32 rows per expert run the weight-streaming kernel, larger
-ones the 256 x 256 MFMA tile; both are covered.
+ones the 256 x 256 MFMA tile; both are covered for the one-byte codes, the
+weight-streaming kernel (the only one INT4 codes run on) for INT4.
 
 Tolerances as for the bf16 layer: h (rounded once to fp16) within one fp16
 ulp per element plus 1e-4 * RMS for fp32 accumulation; y_perm and the layer
@@ -48,8 +50,8 @@ def bf16_as_double(t):
 
 
 class Fp8Layer:
-    """A bf16 layer's inputs with the expert weights replaced by one-byte
-    codes (E4M3 or INT8) and row scales; the oracle's copies are the exact
+    """A bf16 layer's inputs with the expert weights replaced by codes (E4M3,
+    INT8 or INT4) and row scales; the oracle's copies are the exact
     dequantised weights."""
 
     def __init__(self, cfg, seed=0, fmt="e4m3"):
@@ -63,6 +65,9 @@ class Fp8Layer:
             if fmt == "int8":
                 q, s = moe_synth.quantize_rows_int8(g[n])
                 self.wd[n] = oracle.dequant_rows_i8(q.cpu().numpy(), s.cpu().numpy())
+            elif fmt == "int4":
+                q, s = moe_synth.quantize_rows_int4(g[n])
+                self.wd[n] = oracle.dequant_rows_i4(q.cpu().numpy(), s.cpu().numpy())
             else:
                 q, s = moe_synth.quantize_rows_e4m3(g[n])
                 self.wd[n] = oracle.dequant_rows(q.cpu().numpy(), s.cpu().numpy())
@@ -77,10 +82,10 @@ class Fp8Layer:
         return (self.q["w1"], self.s["w1"], self.q["w3"], self.s["w3"], self.q["w2"], self.s["w2"])
 
     def expert_ffn(self, *a):
-        (moe.expert_ffn_i8 if self.fmt == "int8" else moe.expert_ffn_fp8)(*a)
+        {"int8": moe.expert_ffn_i8, "int4": moe.expert_ffn_i4, "e4m3": moe.expert_ffn_fp8}[self.fmt](*a)
 
     def forward(self, *a):
-        (moe.forward_i8 if self.fmt == "int8" else moe.forward_fp8)(*a)
+        {"int8": moe.forward_i8, "int4": moe.forward_i4, "e4m3": moe.forward_fp8}[self.fmt](*a)
 
 
 def routing_exact(p, rc, logits):
@@ -187,7 +192,14 @@ def test_fp8_cases(case, fmt):
     check_layer(Fp8Layer(cfg(name=case, **CASES[case]), fmt=fmt))
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "int8"])
+@pytest.mark.parametrize("case", sorted(c for c in CASES if not c.startswith("mfma_")))
+def test_int4_cases(case):
+    """INT4 codes on the weight-streaming kernel (at most 32 rows per
+    expert): the same cases as the one-byte codes there."""
+    check_layer(Fp8Layer(cfg(name=case, **CASES[case]), fmt="int4"))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "int8", "int4"])
 def test_fp8_decode_full_size(fmt):
     """The decode workload (T 64, d 4096, E 8, d_ff 14336) with one-byte
     weights, sampled rows at each expert's ends and middle."""
