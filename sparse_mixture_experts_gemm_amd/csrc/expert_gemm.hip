@@ -242,13 +242,13 @@ __device__ __forceinline__ int b_imm(int jn) {
 // groups wholly past it carry an offset beyond the buffer extent, so their
 // loads fetch nothing and write zeros (those LDS rows feed only discarded
 // outputs), with no branch in the loop.
-template <int MODE, int HALF>
+template <int MODE, int HALF, int J0 = 0, int J1 = kLoadsPerOperand>
 __device__ __forceinline__ void issue_loads(const GemmThread &g, char *buf, uint32_t kb) {
     if (HALF == 0 || !q_mode<MODE>()) {
         // kPlainBT: the K step advances 64 B rows, not 128 bytes along a row
         const uint32_t kbb = b_trans<MODE>() ? (kb / kRowBytes) * g.b_kstep : kb;
 #pragma unroll
-        for (int j = 0; j < kLoadsPerOperand; j++) {
+        for (int j = J0; j < J1; j++) {
             const int grp = g.wave * kLoadsPerOperand + j;  // 8-row group (kPlainBT: 2 K rows)
             if (HALF == 0) buf2lds16(g.a_rsrc, g.a_off[j], kb, buf + grp * 1024);
             else buf2lds16(g.b_rsrc, g.b_off[j], kbb, buf + grp * 1024);
@@ -343,7 +343,7 @@ __device__ __forceinline__ void block_sync() { asm volatile("s_barrier" ::: "mem
 // the MFMAs of blocks 2-3 with the global loads (if any) and, for the down
 // GEMM, the fp16 widening of the fragments just read (by then the reads
 // have landed, so the widening does not wait on the LDS latency).
-template <int MODE, int NACT, int HALF, bool LOADS>
+template <int MODE, int NACT, int HALF, bool LOADS, int NV = 8>
 __device__ __forceinline__ void sched_half() {
     constexpr int kLo = NACT < 2 ? NACT : 2;
     constexpr int kM = 4 * (HALF == 0 ? kLo : NACT - kLo);  // MFMAs in this half
@@ -352,30 +352,46 @@ __device__ __forceinline__ void sched_half() {
         for (int q = 0; q < 8; q++) {
             if (q < kM) SCHED_MFMA(1);
             if (HALF == 0) SCHED_DSR(1);
-            if (HALF == 1 && LOADS) SCHED_VMEM(1);
+            if (HALF == 0 && LOADS && (q * NV) / 8 != ((q + 1) * NV) / 8) SCHED_VMEM(1);
+            if (HALF == 1 && LOADS && (q * NV) / 8 != ((q + 1) * NV) / 8) SCHED_VMEM(1);
             if (HALF == 1 && MODE == kDown) SCHED_VALU(6);
             if (HALF == 1 && q_mode<MODE>()) SCHED_VALU(q_fmt<MODE>() == kQInt8 ? 6 : 2);
         }
     }
 }
 
-template <int MODE, int NACT, bool LOADS_HALF1>
+template <int MODE, int NACT, bool LOADS_HALF1, int J0 = 0, int J1 = kLoadsPerOperand, int AJ0 = 0,
+          int AJ1 = 0>
 __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, const char *rd_b, int rd_ss,
                                         Frags &nextf, const Frags &f, char *ld_buf, uint32_t kb, int ld_operand,
-                                        f32x16_t (&acc)[4][4]) {
+                                        f32x16_t (&acc)[4][4], char *a_buf = nullptr, uint32_t a_kb = 0) {
+    // first half: optionally A loads AJ0 .. AJ1 - 1 into a_buf
+    if (AJ1 > AJ0) issue_loads<MODE, 0, AJ0, AJ1>(g, a_buf, a_kb);
     load_frags<MODE>(g, rd_a, rd_b, rd_ss, nextf);
     mfma_blocks<MODE, NACT, 0, 2>(f, acc);
-    sched_half<MODE, NACT, 0, false>();
+    sched_half<MODE, NACT, 0, (AJ1 > AJ0), AJ1 - AJ0>();
     __builtin_amdgcn_sched_barrier(0);
     if (LOADS_HALF1) {
-        if (ld_operand == 0) issue_loads<MODE, 0>(g, ld_buf, kb);
-        else issue_loads<MODE, 1>(g, ld_buf, kb);
+        if (ld_operand == 0) issue_loads<MODE, 0, J0, J1>(g, ld_buf, kb);
+        else issue_loads<MODE, 1, J0, J1>(g, ld_buf, kb);
     }
     widen_b<MODE>(nextf);
     mfma_blocks<MODE, NACT, 2, 4>(f, acc);
-    sched_half<MODE, NACT, 1, LOADS_HALF1>();
+    sched_half<MODE, NACT, 1, LOADS_HALF1, J1 - J0>();
     __builtin_amdgcn_sched_barrier(0);
 }
+
+// Loads spread over the sub-steps (bf16 gate-up and down GEMMs): a wave
+// issues its weight-tile loads in three parts, 0-2 in sub-step 1, 3-5 in
+// sub-step 2 and 6-7 in sub-step 3, and its A-tile loads in two, 0-3 after
+// the barrier that frees the buffer (the last sub-step of the step) and 4-7
+// in the first half of the next step's sub-step 1.  Eight 1 KiB loads per
+// wave in one half sub-step (64 per CU) queue at the texture path and hold
+// up the in-order issue of the MFMAs behind them; spread, they cost the
+// Mixtral-shape layer 2.70 -> 2.52-2.58 ms (gate-up launch -5%, down -8%).
+template <int MODE>
+__device__ __forceinline__ constexpr bool split_b_loads() { return MODE == kGateUp || MODE == kDown; }
+constexpr int kB1 = 3, kB2 = 6, kA1 = 4;
 
 // B buffers of each GEMM: three (the third lets a weight tile start almost
 // two K steps before its use; measured 1.6% on the Mixtral-shape down
@@ -390,13 +406,15 @@ __device__ __forceinline__ constexpr int b_buffers() { return (MODE == kDownE4M3
 // sub-step 0's fragments are in f0; the A tile of the next step (into `na`)
 // is already streaming, and with NB = 3 its B tile (into `nb`) too.
 // Sub-step 0 starts a B tile: with NB = 3 that of the step after next, into
-// the free third buffer `fb`; with NB = 2 that of the next step, into `nb`.
-// After sub-step 2 every wave waits for its loads (but the eight just
-// issued, with NB = 3) and its LDS reads and meets the others at a barrier:
-// the next step's tiles are then complete and no wave reads `ca` or `cb` any
-// more, so sub-step 3 (whose fragments are already in registers) overlaps
-// the first LDS reads of the next step and the A loads of the step after
-// next into `ca`.  Fences between the halves of the sub-steps keep the
+// the free third buffer `fb`; with NB = 2 that of the next step, into `nb`
+// (the bf16 gate-up and down GEMMs spread it over sub-steps 0-2 and finish
+// the next step's A tile in sub-step 0's first half, see kB1).
+// After sub-step 2 every wave waits for its loads (but the eight B loads of
+// this step, with NB = 3) and its LDS reads and meets the others at a
+// barrier: the next step's tiles are then complete and no wave reads `ca` or
+// `cb` any more, so sub-step 3 (whose fragments are already in registers)
+// overlaps the first LDS reads of the next step and the A loads of the step
+// after next into `ca`.  Fences between the halves of the sub-steps keep the
 // compiler from chaining dependent MFMAs on one accumulator.
 // MAYBE_PAD: the step may be the padding step past an odd step count
 // (two B buffers only), which must add zero.
@@ -407,16 +425,21 @@ __device__ __forceinline__ void kstep(const GemmThread &g, char *ca, char *cb, c
     Frags f1;
     if (MAYBE_PAD) zero_a_if(pad, f0);
     __builtin_amdgcn_sched_barrier(0);
-    substep<MODE, NACT, true>(g, ca, cb, 1, f1, f0, kRing ? fb : nb, kRing ? kb2 : kb1, 1, acc);
+    constexpr bool kSplit = kRing && split_b_loads<MODE>();
+    constexpr int kE1 = kSplit ? kB1 : kLoadsPerOperand;
+    constexpr int kAE = kSplit ? kA1 : kLoadsPerOperand;  // A loads issued after the barrier
+    substep<MODE, NACT, true, 0, kE1, kAE, kLoadsPerOperand>(g, ca, cb, 1, f1, f0, kRing ? fb : nb,
+                                                             kRing ? kb2 : kb1, 1, acc, na, kb1);
     if (MAYBE_PAD) zero_a_if(pad, f1);
-    substep<MODE, NACT, false>(g, ca, cb, 2, f0, f1, nullptr, 0, 0, acc);
+    substep<MODE, NACT, (kSplit && kB2 > kB1), kB1, kB2>(g, ca, cb, 2, f0, f1, fb, kb2, 1, acc);
     if (MAYBE_PAD) zero_a_if(pad, f0);
-    substep<MODE, NACT, false>(g, ca, cb, 3, f1, f0, nullptr, 0, 0, acc);
+    substep<MODE, NACT, (kSplit && kB2 < kLoadsPerOperand), kB2, kLoadsPerOperand>(g, ca, cb, 3, f1, f0, fb, kb2, 1,
+                                                                                    acc);
     WAIT_VMCNT_LGKM0(kRing ? b_loads<MODE>() : 0);
     block_sync();
     __builtin_amdgcn_sched_barrier(0);
     if (MAYBE_PAD) zero_a_if(pad, f1);
-    substep<MODE, NACT, true>(g, na, nb, 0, f0, f1, ca, kb2, 0, acc);
+    substep<MODE, NACT, true, 0, kAE>(g, na, nb, 0, f0, f1, ca, kb2, 0, acc);
 }
 
 // Step I of a buffer rotation: A alternates over two buffers, B rotates over
@@ -450,7 +473,9 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *a0, char *a
     Frags f0;
     load_frags<MODE>(g, a0, b0, 0, f0);
     widen_b<MODE>(f0);
-    issue_loads<MODE, 0>(g, a1, kb(1));
+    // A(1): the loads the first step's sub-step 1 does not issue
+    issue_loads<MODE, 0, 0, (b_buffers<MODE>() == 3 && split_b_loads<MODE>()) ? kA1 : kLoadsPerOperand>(g, a1,
+                                                                                                         kb(1));
 #define MOE_KSTEP(I, K) kstep_at<MODE, NACT, I>(g, a0, a1, b0, b1, b2, kb((K) + 1), kb((K) + 2), false, f0, acc)
     if constexpr (NB == 3) {
         const int nk6 = nk - nk % 6;
