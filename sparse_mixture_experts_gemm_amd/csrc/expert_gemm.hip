@@ -390,7 +390,7 @@ __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, c
 // up the in-order issue of the MFMAs behind them; spread, they cost the
 // Mixtral-shape layer 2.70 -> 2.52-2.58 ms (gate-up launch -5%, down -8%).
 template <int MODE>
-__device__ __forceinline__ constexpr bool split_b_loads() { return MODE == kGateUp || MODE == kDown; }
+__device__ __forceinline__ constexpr bool split_b_loads() { return !q_mode<MODE>(); }
 constexpr int kB1 = 3, kB2 = 6, kA1 = 4;
 
 // B buffers of each GEMM: three (the third lets a weight tile start almost
