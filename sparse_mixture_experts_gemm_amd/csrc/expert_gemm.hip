@@ -256,7 +256,7 @@ __device__ __forceinline__ void issue_loads(const GemmThread &g, char *buf, uint
     } else {
         // one-byte codes: 16-row groups of 64-byte rows, the K step is 64 bytes
 #pragma unroll
-        for (int j = 0; j < b_loads<MODE>(); j++) {
+        for (int j = J0; j < (J1 < b_loads<MODE>() ? J1 : b_loads<MODE>()); j++) {
             const int grp = g.wave * b_loads<MODE>() + j;
             buf2lds16(g.b_rsrc, g.b_off[j], kb >> 1, buf + grp * 1024);
         }
@@ -390,8 +390,11 @@ __device__ __forceinline__ void substep(const GemmThread &g, const char *rd_a, c
 // up the in-order issue of the MFMAs behind them; spread, they cost the
 // Mixtral-shape layer 2.70 -> 2.52-2.58 ms (gate-up launch -5%, down -8%).
 template <int MODE>
-__device__ __forceinline__ constexpr bool split_b_loads() { return !q_mode<MODE>(); }
-constexpr int kB1 = 3, kB2 = 6, kA1 = 4;
+__device__ __forceinline__ constexpr bool split_b_loads() { return true; }
+constexpr int kA1 = 4;
+// weight-tile parts: loads [0, b_part<1>), [b_part<1>, b_part<2>), [b_part<2>, b_loads)
+template <int MODE, int P>
+__device__ __forceinline__ constexpr int b_part() { return q_mode<MODE>() ? 2 * P : 3 * P; }
 
 // B buffers of each GEMM: three (the third lets a weight tile start almost
 // two K steps before its use; measured 1.6% on the Mixtral-shape down
@@ -426,6 +429,7 @@ __device__ __forceinline__ void kstep(const GemmThread &g, char *ca, char *cb, c
     if (MAYBE_PAD) zero_a_if(pad, f0);
     __builtin_amdgcn_sched_barrier(0);
     constexpr bool kSplit = kRing && split_b_loads<MODE>();
+    constexpr int kB1 = b_part<MODE, 1>(), kB2 = b_part<MODE, 2>(), kBL = b_loads<MODE>();
     constexpr int kE1 = kSplit ? kB1 : kLoadsPerOperand;
     constexpr int kAE = kSplit ? kA1 : kLoadsPerOperand;  // A loads issued after the barrier
     substep<MODE, NACT, true, 0, kE1, kAE, kLoadsPerOperand>(g, ca, cb, 1, f1, f0, kRing ? fb : nb,
@@ -433,8 +437,7 @@ __device__ __forceinline__ void kstep(const GemmThread &g, char *ca, char *cb, c
     if (MAYBE_PAD) zero_a_if(pad, f1);
     substep<MODE, NACT, (kSplit && kB2 > kB1), kB1, kB2>(g, ca, cb, 2, f0, f1, fb, kb2, 1, acc);
     if (MAYBE_PAD) zero_a_if(pad, f0);
-    substep<MODE, NACT, (kSplit && kB2 < kLoadsPerOperand), kB2, kLoadsPerOperand>(g, ca, cb, 3, f1, f0, fb, kb2, 1,
-                                                                                    acc);
+    substep<MODE, NACT, (kSplit && kB2 < kBL), kB2, kBL>(g, ca, cb, 3, f1, f0, fb, kb2, 1, acc);
     WAIT_VMCNT_LGKM0(kRing ? b_loads<MODE>() : 0);
     block_sync();
     __builtin_amdgcn_sched_barrier(0);
