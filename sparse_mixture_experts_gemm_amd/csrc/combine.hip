@@ -8,10 +8,14 @@
 // Two sources:
 //   * y_perm [R][d] fp32 with the gates applied here (moe_combine, and the
 //     fp32 layer's forward pass);
-//   * gated rows: S fp16 slices [S][R][d] holding gate * (partial product of
-//     d_ff slice s), written by the down projection's epilogue in a bf16
-//     layer's forward pass.  The combine is then a plain sum of the k rows'
-//     slices (slot order, then slice order), read at half the bytes of fp32.
+//   * gated rows: fp16 slices holding gate * (partial product of d_ff slice
+//     s), written by the down projection's epilogue in a bf16 layer's
+//     forward pass.  The combine is then a plain sum of the k rows' slices
+//     (slot order, then slice order), read at half the bytes of fp32.  Either
+//     every row has S slices ([S][R][d]), or the down projection's split
+//     plan holds: slice 0 of every row in [R][d], and slices 1 .. S-1 only
+//     for the split rows r >= row0, at rest + ((s - 1) srows + r - row0) d,
+//     with {row0, S, srows} read from the plan the down projection stored.
 // HBM-bound gather: 16-byte loads and stores, each source row read once.
 #include <algorithm>
 
@@ -85,7 +89,9 @@ struct SrcOf<uint16_t> {
 // threads, the loads of one slot's slices issued together.  GATED: the
 // sources are gated fp16 slices and no gate is applied here.
 template <typename TE, typename TY, bool GATED>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const TY *__restrict__ src, const int32_t *__restrict__ row,
+__global__ __launch_bounds__(kThreads) void combine_kernel(const TY *__restrict__ src, const TY *__restrict__ rest,
+                                                           const int32_t *__restrict__ plan,
+                                                           const int32_t *__restrict__ row,
                                                            const float *__restrict__ gate, int T, int k, int d,
                                                            int tpb, int splits, size_t stride,
                                                            TE *__restrict__ y) {
@@ -100,6 +106,7 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TY *__restrict_
         rws[r] = row[(size_t)t * k + r];
         gs[r] = GATED ? 1.0f : gate[(size_t)t * k + r];
     }
+    const int row0 = plan ? plan[0] : 0, srows = plan ? plan[2] : 0;
     const int groups = d / 8;
     for (int c = lt; c < groups; c += per_tok) {
         float a[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -107,9 +114,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TY *__restrict_
             if (rws[r] < 0) continue;
             float u[8];
             widen8(load8(src + (size_t)rws[r] * d, c), u);
-            for (int sl = 1; sl < splits; sl++) {
+            const int ns = !plan ? splits : (rws[r] >= row0 ? plan[1] : 1);
+            for (int sl = 1; sl < ns; sl++) {
                 float v[8];
-                widen8(load8(src + sl * stride + (size_t)rws[r] * d, c), v);
+                const TY *sp = plan ? rest + ((size_t)(sl - 1) * srows + (rws[r] - row0)) * d
+                                    : src + sl * stride + (size_t)rws[r] * d;
+                widen8(load8(sp, c), v);
 #pragma unroll
                 for (int i = 0; i < 8; i++) u[i] += v[i];
             }
@@ -126,8 +136,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const TY *__restrict_
 // a whole token row's worth of reads in flight.  A dropped slot reads row 0
 // and is discarded by a select, so no branch splits the batch and an
 // uninitialised row can never leak a NaN into the sum (R >= 1 here).
-template <typename TE, typename TY, bool GATED, int K, int S, int G>
-__global__ __launch_bounds__(kThreads) void combine_fixed(const TY *__restrict__ src, const int32_t *__restrict__ row,
+// PLAN: slice 0 of every row is read first, then slices 1 .. S-1 of the
+// split rows (a minority: the rows of the last round's m tiles).
+template <typename TE, typename TY, bool GATED, int K, int S, int G, bool PLAN>
+__global__ __launch_bounds__(kThreads) void combine_fixed(const TY *__restrict__ src, const TY *__restrict__ rest,
+                                                          const int32_t *__restrict__ plan,
+                                                          const int32_t *__restrict__ row,
                                                           const float *__restrict__ gate, int T, int d, size_t stride,
                                                           TE *__restrict__ y) {
     typedef typename SrcOf<TY>::type Src;
@@ -164,6 +178,17 @@ __global__ __launch_bounds__(kThreads) void combine_fixed(const TY *__restrict__
 #pragma unroll
                 for (int i = 0; i < 8; i++) p[i] += q[i];
             }
+            if (PLAN && rws[r] >= plan[0]) {
+                // a split row (rare): its further slices one at a time
+                const TY *sp = rest + (size_t)(rws[r] - plan[0]) * d;
+                const size_t sstride = (size_t)plan[2] * d;
+                for (int sl = 1; sl < plan[1]; sl++) {
+                    float q[8];
+                    widen8(load8(sp + (sl - 1) * sstride, lt + gi * per_tok), q);
+#pragma unroll
+                    for (int i = 0; i < 8; i++) p[i] += q[i];
+                }
+            }
             const bool kept = rws[r] >= 0;
 #pragma unroll
             for (int i = 0; i < 8; i++) a[i] += kept ? (GATED ? p[i] : gs[r] * p[i]) : 0.0f;
@@ -178,9 +203,9 @@ __global__ __launch_bounds__(kThreads) void zero_fill(uint4 *__restrict__ y, siz
         y[i] = make_uint4(0, 0, 0, 0);
 }
 
-template <typename TE, typename TY, bool GATED, int K, int S>
-bool launch_fixed(const moe_params &p, size_t stride, const TY *src, const int32_t *row, const float *gate, void *y,
-                  hipStream_t st) {
+template <typename TE, typename TY, bool GATED, int K, int S, bool PLAN = false>
+bool launch_fixed(const moe_params &p, size_t stride, const TY *src, const TY *rest, const int32_t *plan,
+                  const int32_t *row, const float *gate, void *y, hipStream_t st) {
     // G = 2 groups per thread when a token row has at least 512 groups
     const int groups = p.d / 8;
     const int G = groups >= 2 * kThreads ? 2 : 1;
@@ -189,22 +214,32 @@ bool launch_fixed(const moe_params &p, size_t stride, const TY *src, const int32
     const int tpb = kThreads / per_tok;
     const int grid = (int)ceil_div(p.T, tpb);
     if (G == 2)
-        hipLaunchKernelGGL((combine_fixed<TE, TY, GATED, K, S, 2>), dim3(grid), dim3(kThreads), 0, st, src, row, gate,
-                           p.T, p.d, stride, static_cast<TE *>(y));
+        hipLaunchKernelGGL((combine_fixed<TE, TY, GATED, K, S, 2, PLAN>), dim3(grid), dim3(kThreads), 0, st, src, rest,
+                           plan, row, gate, p.T, p.d, stride, static_cast<TE *>(y));
     else
-        hipLaunchKernelGGL((combine_fixed<TE, TY, GATED, K, S, 1>), dim3(grid), dim3(kThreads), 0, st, src, row, gate,
-                           p.T, p.d, stride, static_cast<TE *>(y));
+        hipLaunchKernelGGL((combine_fixed<TE, TY, GATED, K, S, 1, PLAN>), dim3(grid), dim3(kThreads), 0, st, src, rest,
+                           plan, row, gate, p.T, p.d, stride, static_cast<TE *>(y));
     return true;
 }
 
+// plan: null (every row has `splits` slices, `stride` elements apart), or
+// the down projection's split plan (splits is then 1, see the header).
 template <typename TE, typename TY, bool GATED>
-hipError_t launch_any(const moe_params &p, int splits, size_t stride, const TY *src, const int32_t *row,
-                      const float *gate, void *y, hipStream_t st) {
+hipError_t launch_any(const moe_params &p, int splits, size_t stride, const TY *src, const TY *rest,
+                      const int32_t *plan, const int32_t *row, const float *gate, void *y, hipStream_t st) {
     bool fixed = false;
-    if (p.k == 2 && splits == 1) fixed = launch_fixed<TE, TY, GATED, 2, 1>(p, stride, src, row, gate, y, st);
-    else if (p.k == 2 && splits == 2) fixed = launch_fixed<TE, TY, GATED, 2, 2>(p, stride, src, row, gate, y, st);
-    else if (p.k == 2 && splits == 4) fixed = launch_fixed<TE, TY, GATED, 2, 4>(p, stride, src, row, gate, y, st);
-    else if (p.k == 1 && splits == 1) fixed = launch_fixed<TE, TY, GATED, 1, 1>(p, stride, src, row, gate, y, st);
+    if (plan) {
+        if (p.k == 2) fixed = launch_fixed<TE, TY, GATED, 2, 1, true>(p, stride, src, rest, plan, row, gate, y, st);
+        else if (p.k == 1) fixed = launch_fixed<TE, TY, GATED, 1, 1, true>(p, stride, src, rest, plan, row, gate, y, st);
+    } else if (p.k == 2 && splits == 1) {
+        fixed = launch_fixed<TE, TY, GATED, 2, 1>(p, stride, src, rest, plan, row, gate, y, st);
+    } else if (p.k == 2 && splits == 2) {
+        fixed = launch_fixed<TE, TY, GATED, 2, 2>(p, stride, src, rest, plan, row, gate, y, st);
+    } else if (p.k == 2 && splits == 4) {
+        fixed = launch_fixed<TE, TY, GATED, 2, 4>(p, stride, src, rest, plan, row, gate, y, st);
+    } else if (p.k == 1 && splits == 1) {
+        fixed = launch_fixed<TE, TY, GATED, 1, 1>(p, stride, src, rest, plan, row, gate, y, st);
+    }
     if (fixed) return hipGetLastError();
     const int groups = p.d / 8;
     // tokens per block: enough threads per token to cover its row in one pass
@@ -212,8 +247,8 @@ hipError_t launch_any(const moe_params &p, int splits, size_t stride, const TY *
     int tpb = kThreads / per_tok;
     if (tpb < 1) tpb = 1;
     const int grid = (int)ceil_div(p.T, tpb);
-    hipLaunchKernelGGL((combine_kernel<TE, TY, GATED>), dim3(grid), dim3(kThreads), 0, st, src, row, gate, p.T, p.k,
-                       p.d, tpb, splits, stride, static_cast<TE *>(y));
+    hipLaunchKernelGGL((combine_kernel<TE, TY, GATED>), dim3(grid), dim3(kThreads), 0, st, src, rest, plan, row, gate,
+                       p.T, p.k, p.d, tpb, splits, stride, static_cast<TE *>(y));
     return hipGetLastError();
 }
 
@@ -230,16 +265,18 @@ hipError_t launch_combine(const moe_params &p, int64_t max_rows, const float *y_
                           const float *gate, void *y, hipStream_t st) {
     if (p.T == 0) return hipSuccess;
     if (max_rows <= 0) return launch_zero(p, y, st);
-    if (p.dtype == MOE_BF16) return launch_any<uint16_t, float, false>(p, 1, 0, y_perm, row, gate, y, st);
-    return launch_any<float, float, false>(p, 1, 0, y_perm, row, gate, y, st);
+    if (p.dtype == MOE_BF16)
+        return launch_any<uint16_t, float, false>(p, 1, 0, y_perm, y_perm, nullptr, row, gate, y, st);
+    return launch_any<float, float, false>(p, 1, 0, y_perm, y_perm, nullptr, row, gate, y, st);
 }
 
 hipError_t launch_combine_gated(const moe_params &p, int64_t max_rows, int splits, const uint16_t *yg,
-                                const int32_t *row, void *y, hipStream_t st) {
+                                const uint16_t *yrest, const int32_t *plan, const int32_t *row, void *y,
+                                hipStream_t st) {
     if (p.T == 0) return hipSuccess;
     if (max_rows <= 0) return launch_zero(p, y, st);
     const size_t stride = (size_t)max_rows * p.d;
-    return launch_any<uint16_t, uint16_t, true>(p, splits, stride, yg, row, nullptr, y, st);
+    return launch_any<uint16_t, uint16_t, true>(p, plan ? 1 : splits, stride, yg, yrest, plan, row, nullptr, y, st);
 }
 
 }  // namespace moe

@@ -104,6 +104,15 @@ __device__ __forceinline__ T *slice_ptr(const GemmOut &o, int split) {
     return split == 0 ? static_cast<T *>(o.y0) : static_cast<T *>(o.y_rest) + (size_t)(split - 1) * o.stride;
 }
 
+// Row m of the tile's slice (GemmOut): the uniform layout, or (PLAN) the
+// split plan's, whose slices 1.. hold only the split rows.
+template <typename T, bool PLAN>
+__device__ __forceinline__ T *slice_row(const GemmOut &o, const TileInfo &ti, int m, int N) {
+    if (!PLAN) return slice_ptr<T>(o, ti.split) + (size_t)m * N;
+    if (ti.split == 0) return static_cast<T *>(o.y0) + (size_t)m * N;
+    return static_cast<T *>(o.y_rest) + ((size_t)(ti.split - 1) * ti.srows + (m - ti.row0)) * N;
+}
+
 // silu(a) * b with the hardware exp and reciprocal (about 1 ulp each in
 // fp32, far below the fp16 / fp32 rounding of the stored result).  Large
 // negative a gives exp -> inf, rcp -> 0, so silu -> -0.
@@ -529,7 +538,7 @@ __device__ __forceinline__ void main_loop(const GemmThread &g, char *a0, char *a
 // Down: fp32 partial products, 32 lanes store one 128-byte row segment.
 // One-byte weights: the accumulators of weight row n are multiplied by its
 // scale (sc0 for W1 or W2 rows, sc1 for W3 rows; [E][N]) first.
-template <int MODE, int NACT>
+template <int MODE, int NACT, bool PLAN = false>
 __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, int wm, int wn, int lane,
                                            const GemmOut &out, const float *sc0, const float *sc1,
                                            const f32x16_t (&acc)[4][4], char *w) {
@@ -648,10 +657,10 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
                     const uint32_t hi2 = (uint32_t)f32_to_f16_sat(g * __uint_as_float(v.z)) |
                                          ((uint32_t)f32_to_f16_sat(g * __uint_as_float(v.w)) << 16);
                     if (m < ti.mend && col < N)
-                        *reinterpret_cast<uint2 *>(slice_ptr<uint16_t>(out, ti.split) + (size_t)m * N + col) =
+                        *reinterpret_cast<uint2 *>(slice_row<uint16_t, PLAN>(out, ti, m, N) + col) =
                             make_uint2(lo, hi2);
                 } else if (m < ti.mend && col < N) {
-                    *reinterpret_cast<uint4 *>(slice_ptr<float>(out, ti.split) + (size_t)m * N + col) = v;
+                    *reinterpret_cast<uint4 *>(slice_row<float, PLAN>(out, ti, m, N) + col) = v;
                 }
             }
         }
@@ -660,7 +669,7 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
 
 // A whole tile for one active-block count: the accumulators live only
 // inside this function, so the variants never merge.
-template <int MODE, int NACT, bool ODD>
+template <int MODE, int NACT, bool ODD, bool PLAN = false>
 __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti, char *a0, char *a1, char *b0,
                                          char *b1, char *b2, int nk, int n0, int N, int wm, int wn, int lane,
                                          const GemmOut &out, const float *sc0 = nullptr, const float *sc1 = nullptr) {
@@ -676,7 +685,7 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
     // wave before the epilogue reuses the A buffers (16 KiB per wave)
     WAIT_VM_LGKM0();
     block_sync();
-    store_tile<MODE, NACT>(ti, n0, N, wm, wn, lane, out, sc0, sc1, acc,
+    store_tile<MODE, NACT, PLAN>(ti, n0, N, wm, wn, lane, out, sc0, sc1, acc,
                            (g.wave < 2 ? a0 : a1) + (g.wave & 1) * (kTileBytes / 2));
 }
 
@@ -701,7 +710,9 @@ __device__ __forceinline__ void run_tile(const GemmThread &g, const TileInfo &ti
 // l%8, so every wave load reads whole 128-byte lines.  Fragments: lane l
 // reads row base + l%32 (base a multiple of 32), logical chunk 2s + l/32 of
 // sub-step s; the swizzle of such a row is swz(l%32) ^ 4 * parity(base/32).
-template <int MODE>
+// PLAN (down projections of moe_forward): the device-side split plan
+// (find_tile_planned, out.plan) instead of `splits` uniform slices.
+template <int MODE, bool PLAN = false>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const uint16_t *__restrict__ A, const int32_t *__restrict__ a_rows, const uint16_t *__restrict__ B0,
     const uint16_t *__restrict__ B1, const int32_t *__restrict__ offsets, int E, int N, int K, int ldb,
@@ -718,14 +729,22 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const int wm = wave >> 1, wn = wave & 1;
 
     TileInfo ti;
-    if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti))
-        return;
+    int k0s, nks;  // first K step and K steps of this item
+    if constexpr (PLAN) {
+        if (!find_tile_planned(offsets, E, ntiles_n, kBM, K / kBK, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0),
+                               out.plan, ti, k0s, nks))
+            return;
+    } else {
+        if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti))
+            return;
+        nks = K / splits / kBK;
+        k0s = ti.split * nks;
+    }
     const int n0 = two_b<MODE>() ? ti.nt * (kBN / 2) : ti.nt * kBN;
     // bytes per weight element: 2 (bf16) or 1 (one-byte codes)
     constexpr int kWb = q_mode<MODE>() ? 1 : 2;
     const size_t wexp = (size_t)ti.e * N * ldb * kWb;
-    const int ks = K / splits;              // K elements of this split
-    const int k_first = ti.split * ks;      // first K element of this split
+    const int k_first = k0s * kBK;  // first K element of this item
 
     GemmThread g;
     g.wave = wave;
@@ -810,15 +829,15 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
     const int nact_raw = (ti.mend - (ti.m0 + wm * 128) + 31) / 32;
     const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, nact_raw)));
 
-    const int nk = ks / kBK;
+    const int nk = nks;
 #define MOE_TILE(n)                                                                                              \
     do {                                                                                                         \
         if (b_buffers<MODE>() == 2 && (nk & 1))                                                                  \
-            run_tile<MODE, n, b_buffers<MODE>() == 2>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N,  \
-                                                      wm, wn, lane, out, S0, S1);                                \
+            run_tile<MODE, n, b_buffers<MODE>() == 2, PLAN>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, \
+                                                            N, wm, wn, lane, out, S0, S1);                     \
         else                                                                                                     \
-            run_tile<MODE, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane,     \
-                                     out, S0, S1);                                                               \
+            run_tile<MODE, n, false, PLAN>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn,     \
+                                           lane, out, S0, S1);                                                 \
     } while (0)
     switch (nact) {
         case 4: MOE_TILE(4); break;
@@ -1659,6 +1678,23 @@ int ffn_splits(const moe_params &p, int64_t max_rows) {
     return pick_splits(tiles, steps, 1, [steps](int s) { return steps % (4 * s) == 0; });
 }
 
+// moe_forward's down projection on the 256-row GEMM: the split plan for
+// the bound on the m tiles.  No split there (the tiles fill whole rounds):
+// one slice; every tile split: that many uniform slices (when they divide
+// the K steps); only a partial split runs the planned kernel, which
+// re-plans for the actual m tiles on the device.  (The uniform kernel is
+// the leaner one: its epilogue keeps one register fewer through the K loop.)
+DownSplit forward_down_split(const moe_params &p, int64_t max_rows) {
+    if (p.dtype != MOE_BF16 || max_rows <= 0 || capacity_rows(p) <= kSkBM) return DownSplit{false, 1};
+    const int64_t mt = mtile_bound(max_rows, capacity_rows(p), p.E, kBM);
+    const int ntn = (int)ceil_div(p.d, kBN), nk = p.d_ff / kBK;
+    int G, S;
+    split_plan((int)mt, ntn, nk, G, S);
+    if (G == 0) return DownSplit{false, 1};
+    if (G == mt && nk % S == 0) return DownSplit{false, S};
+    return DownSplit{true, 1};
+}
+
 bool q4_ffn_supported(const moe_params &p) {
     // the weight-streaming kernel only (at most 32 rows per expert), which
     // steps K by 128
@@ -1727,6 +1763,16 @@ static void launch_q4(const moe_params &p, int64_t mt, const void *x_perm, const
                        dff, nt_dn, down);
 }
 
+// Grid of a planned down projection over at most `tiles` tiles: the plan
+// never exceeds whole rounds of kPlanCUs items (with M tiles = 256 k + r,
+// 0 < r < 256: at most 256 k bulk items and 256 split items), so blocks
+// beyond that would only find no work, after the claim attempts on every
+// XCD's counter, at the end of the launch.  Without claim counters each XCD
+// takes its own share (rounded up per XCD: 16 more).
+static int64_t planned_grid(int64_t tiles, const int32_t *claim) {
+    return ceil_div(tiles, (int64_t)kPlanCUs) * kPlanCUs + (claim ? 0 : 16);
+}
+
 // One-byte weights on the 256 x 256 MFMA tile (groups of more than 32 rows).
 template <int GU, int DN>
 static void launch_q8_mfma(const moe_params &p, int64_t mt, const void *x_perm, const int32_t *a_rows,
@@ -1742,7 +1788,9 @@ static void launch_q8_mfma(const moe_params &p, int64_t mt, const void *x_perm, 
                        reinterpret_cast<const uint16_t *>(w3), offsets, E, dff, d, d, nt_up, 1, (uint32_t)a_bytes,
                        claim, GemmOut{h, nullptr, 0, nullptr}, s1, s3);
     if (mid) ev = hipEventRecord(mid, st);
-    hipLaunchKernelGGL(grouped_gemm_bf16<DN>, dim3((unsigned)(mt * nt_dn * splits)), dim3(kGemmThreads), 0, st,
+    const int64_t dn_items = down.plan ? planned_grid(mt * nt_dn, claim) : mt * nt_dn * splits;
+    auto *dn = down.plan ? grouped_gemm_bf16<DN, true> : grouped_gemm_bf16<DN, false>;
+    hipLaunchKernelGGL(dn, dim3((unsigned)dn_items), dim3(kGemmThreads), 0, st,
                        static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                        reinterpret_cast<const uint16_t *>(w2), reinterpret_cast<const uint16_t *>(w2), offsets, E,
                        d, dff, dff, nt_dn, splits, (uint32_t)0, claim ? claim + 8 : nullptr, down, s2, s2);
@@ -1784,7 +1832,7 @@ hipError_t launch_expert_ffn_fp8(const moe_params &p, int64_t max_rows, int64_t 
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
                              const void *w3, const void *w2, void *h, const GemmOut &down, int32_t *claim,
-                             hipEvent_t mid, hipStream_t st) {
+                             hipEvent_t mid, hipStream_t st, int splits) {
     if (max_rows <= 0) return hipSuccess;
     const int E = p.E, d = p.d, dff = p.d_ff;
     const GemmOut up{h, nullptr, 0, nullptr};
@@ -1793,7 +1841,7 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         const int64_t mt = mtile_bound(max_rows, cap, E, kSkBM);
         const int nt_up = (int)ceil_div(dff, kSkBN);
         const int nt_dn = (int)ceil_div(d, kSkBNd);
-        const int S = ffn_splits(p, max_rows);
+        const int S = splits;
         hipLaunchKernelGGL(grouped_gemm_skinny<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kSkThreads), 0, st,
                            static_cast<const uint16_t *>(x_perm), a_rows, static_cast<const uint16_t *>(w1),
                            static_cast<const uint16_t *>(w3), offsets, E, dff, d, nt_up, 1, up);
@@ -1811,17 +1859,22 @@ hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap,
         const int64_t mt = mtile_bound(max_rows, cap, E, kBM);
         const int nt_up = (int)ceil_div(dff, kBN / 2);
         const int nt_dn = (int)ceil_div(d, kBN);
-        const int S = ffn_splits(p, max_rows);
+        // the split plan (down.plan) is chosen on the device: at most one
+        // extra round of items; the claim counters hand them out
+        const int S = down.plan ? 1 : splits;
+        if (S < 1 || (dff / kBK) % S != 0) return hipErrorInvalidValue;
+        const int64_t dn_items = down.plan ? planned_grid(mt * nt_dn, claim) : mt * nt_dn * S;
+        auto *dn = down.plan ? grouped_gemm_bf16<kDown, true> : grouped_gemm_bf16<kDown, false>;
         hipLaunchKernelGGL(grouped_gemm_bf16<kGateUp>, dim3((unsigned)(mt * nt_up)), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(x_perm), a_rows,
                            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w3),
                            offsets, E, dff, d, d, nt_up, 1, (uint32_t)a_bytes, claim, up);
         if (mid && hipEventRecord(mid, st) != hipSuccess) return hipErrorLaunchFailure;
-        hipLaunchKernelGGL(grouped_gemm_bf16<kDown>, dim3((unsigned)(mt * nt_dn * S)), dim3(kGemmThreads),
+        hipLaunchKernelGGL(dn, dim3((unsigned)dn_items), dim3(kGemmThreads),
                            0, st, static_cast<const uint16_t *>(h), (const int32_t *)nullptr,
                            static_cast<const uint16_t *>(w2), static_cast<const uint16_t *>(w2),
                            offsets, E, d, dff, dff, nt_dn, S, (uint32_t)0,
-                           claim ? claim + 8 : nullptr, down);
+                           claim ? claim + 8 : nullptr, down, (const float *)nullptr, (const float *)nullptr);
     } else {
         const int64_t mt = max_rows / kF32BM + E;
         const int nt_up = (int)ceil_div(dff, kF32BN);

@@ -104,8 +104,8 @@ int fp8_weights_ok(const moe_params &p, const FfnWeights &w) {
     return MOE_OK;
 }
 
-// splits: the down projection's K slices for one-byte weights (moe_forward:
-// ffn_splits, as the combine expects; the staged entry points: 1).
+// splits: the down projection's uniform K slices (moe_forward: its down
+// split, as the combine expects; the staged one-byte entry points: 1).
 hipError_t launch_ffn(const moe_params &p, int64_t R, int64_t C, const void *a, const int32_t *a_rows,
                       const int32_t *offsets, const FfnWeights &w, void *h, const GemmOut &down, int32_t *claim,
                       hipEvent_t mid, hipStream_t st, int splits = 1) {
@@ -114,7 +114,7 @@ hipError_t launch_ffn(const moe_params &p, int64_t R, int64_t C, const void *a, 
                                      static_cast<const uint8_t *>(w.w3), w.s3,
                                      static_cast<const uint8_t *>(w.w2), w.s2, h, down, splits, claim, mid, w.qfmt,
                                      st);
-    return launch_expert_ffn(p, R, C, a, a_rows, offsets, w.w1, w.w3, w.w2, h, down, claim, mid, st);
+    return launch_expert_ffn(p, R, C, a, a_rows, offsets, w.w1, w.w3, w.w2, h, down, claim, mid, st, splits);
 }
 
 // moe_forward folds the dispatch gather into the gate-up GEMM (A rows read
@@ -136,14 +136,21 @@ size_t ffn_ws_bytes(const moe_params &p) {
 // Workspace layout of moe_forward.
 struct ForwardWs {
     void *dispatch, *x_perm, *h;  // x_perm null when the GEMM gathers
-    void *y;                      // bf16: gated fp16 slices [S][R][d]; fp32: y_perm [R][d]
+    void *y;                      // bf16: gated fp16 slice 0 [R][d], then the split rows' further
+                                  // slices (split plan); fp32: y_perm [R][d]
     float *gate_of_row;           // bf16: [R] each row's gate, for the down epilogue; fp32: null
-    int32_t *claim;               // the expert GEMM's work-claim counters
+    int32_t *claim;               // the expert GEMM's work-claim counters, then the split plan (4 ints)
 };
 
 size_t forward_y_bytes(const moe_params &p) {
     const size_t R = (size_t)max_rows_of(p);
-    return p.dtype == MOE_BF16 ? (size_t)splits_of(p) * R * p.d * 2 : R * p.d * sizeof(float);
+    if (p.dtype != MOE_BF16) return R * p.d * sizeof(float);
+    // slices past the first: the split plan's (or S - 1 uniform ones of R x d
+    // each, which the same bound covers: (S - 1) R <= (S - 1) G 256 <= 256^3 / d
+    // and S <= plan_max_splits)
+    const DownSplit ds = forward_down_split(p, (int64_t)R);
+    const size_t extra = ds.planned || ds.S > 1 ? plan_extra_elems((int64_t)R, p.d, p.d_ff) : 0;
+    return (R * p.d + extra) * 2;
 }
 
 size_t forward_ws_bytes(const moe_params &p) {
@@ -151,7 +158,7 @@ size_t forward_ws_bytes(const moe_params &p) {
     const size_t xp = gather_in_gemm(p) ? 0 : align256(R * p.d * esize(p));
     const size_t gr = p.dtype == MOE_BF16 ? align256(R * sizeof(float)) : 0;
     return align256(dispatch_scratch_bytes(p.T, p.E, p.k)) + xp + align256(R * p.d_ff * esize(p)) +
-           align256(forward_y_bytes(p)) + gr + align256(sizeof(int32_t) * kClaimCounters);
+           align256(forward_y_bytes(p)) + gr + align256(sizeof(int32_t) * (kClaimCounters + 4));
 }
 
 ForwardWs carve_forward(void *ws, const moe_params &p) {
@@ -368,7 +375,7 @@ int moe_expert_ffn(const moe_params *p, const void *x_perm, const int32_t *offse
     const int S = splits_of(*p);
     const GemmOut down{y_perm, workspace, (size_t)R * p->d, nullptr};
     hipError_t e = launch_expert_ffn(*p, R, capacity_of(*p), x_perm, nullptr, offsets, w1, w3, w2, h, down,
-                                     nullptr, nullptr, st);
+                                     nullptr, nullptr, st, S);
     if (e != hipSuccess) return MOE_ERR_HIP;
     return hip_status(launch_ffn_fixup(*p, R, offsets, static_cast<float *>(y_perm),
                                        static_cast<const float *>(workspace), S - 1, st));
@@ -452,7 +459,10 @@ int forward_impl(const moe_params *p, const void *x, const void *w_router, const
     const ForwardWs f = carve_forward(workspace, *p);
     const int64_t C = capacity_of(*p);
     const int64_t R = max_rows_of(*p);
-    const int S = splits_of(*p);
+    // down-projection slices: uniform, or chosen on the device by the split
+    // plan (the weight-streaming kernel and fp32 layers: one)
+    const DownSplit dsp = forward_down_split(*p, R);
+    const int S = dsp.planned ? 1 : dsp.S;
     if (!mark(0)) return MOE_ERR_HIP;
     hipError_t e = launch_route(*p, x, w_router, bias, load, logits, r->cand, r->cand_score, st);
     if (e != hipSuccess) return MOE_ERR_HIP;
@@ -464,11 +474,14 @@ int forward_impl(const moe_params *p, const void *x, const void *w_router, const
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (!mark(2)) return MOE_ERR_HIP;
     // bf16: the down projection folds each row's gate in and stores fp16
-    // slices; fp32: y_perm [R][d] in fp32, gates applied by the combine
+    // slices (the 256-row GEMM after its device-side split plan, the
+    // weight-streaming kernel as one slice); fp32: y_perm [R][d] in fp32,
+    // gates applied by the combine
     const size_t stride = (size_t)R * p->d;
-    const GemmOut down = p->dtype == MOE_BF16
-                             ? GemmOut{f.y, static_cast<uint16_t *>(f.y) + stride, stride, f.gate_of_row}
-                             : GemmOut{f.y, nullptr, stride, nullptr};
+    int32_t *plan = dsp.planned ? f.claim + kClaimCounters : nullptr;
+    uint16_t *yrest = static_cast<uint16_t *>(f.y) + stride;
+    const GemmOut down = p->dtype == MOE_BF16 ? GemmOut{f.y, yrest, stride, f.gate_of_row, plan}
+                                              : GemmOut{f.y, nullptr, stride, nullptr};
     hipEvent_t mid = events ? static_cast<hipEvent_t>(events[3]) : nullptr;
     if (f.x_perm)
         e = launch_ffn(*p, R, C, f.x_perm, nullptr, r->offsets, w, f.h, down, f.claim, mid, st, S);
@@ -477,7 +490,7 @@ int forward_impl(const moe_params *p, const void *x, const void *w_router, const
     if (e != hipSuccess) return MOE_ERR_HIP;
     if (!mark(4)) return MOE_ERR_HIP;
     if (p->dtype == MOE_BF16)
-        e = launch_combine_gated(*p, R, S, static_cast<const uint16_t *>(f.y), r->row, y, st);
+        e = launch_combine_gated(*p, R, S, static_cast<const uint16_t *>(f.y), yrest, plan, r->row, y, st);
     else
         e = launch_combine(*p, R, static_cast<const float *>(f.y), r->row, r->gate, y, st);
     if (e != hipSuccess) return MOE_ERR_HIP;

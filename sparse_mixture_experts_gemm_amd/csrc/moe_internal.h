@@ -29,6 +29,10 @@ struct DispatchScratch {
 
 // Work-claim counters of the expert GEMM (one per XCD, gate-up then down).
 constexpr int kClaimCounters = 16;
+// The down projection's split plan (find_tile_planned): items per round
+// (the chip's CUs) and the most K slices of a split tile.
+constexpr int kPlanCUs = 256;
+constexpr int kPlanMaxS = 8;
 
 inline size_t dispatch_scratch_bytes(int T, int E, int k) {
     int64_t nb = ceil_div(T > 0 ? T : 1, kDispatchBlock);
@@ -86,12 +90,28 @@ int ffn_splits(const moe_params &p, int64_t max_rows);
 // elements; with row_gate null each partial is stored in fp32 (the layer's
 // element type for fp32 layers), otherwise as the fp16 of row_gate[row] *
 // partial (the combine weight folded in, saturated at +-65504; bf16 layers).
+// With plan set (the 256-row down GEMM of moe_forward), the slices follow
+// the device-side split plan of find_tile_planned instead: slice 0 of every
+// row at y0, slice s >= 1 of a split row r at y_rest + ((s - 1) * srows +
+// r - row0) * d elements, and plan[0..2] = {row0, S, srows} is stored for
+// the combine.  At most plan_extra_elems(...) elements past y_rest are used.
 struct GemmOut {
     void *y0;
     void *y_rest;
     size_t stride;
     const float *row_gate;
+    int32_t *plan = nullptr;
 };
+
+// Elements of the planned down projection's second slice buffer: (S - 1)
+// split rows of d each, with S G ntn <= 256 and S <= plan_max_splits: at most
+// 256 * 256 * 256 (d <= 256 ntn) and at most (plan_max_splits - 1) R d.
+inline size_t plan_extra_elems(int64_t max_rows, int d, int d_ff) {
+    const int64_t nk = d_ff / 64;
+    const int64_t smax = nk / 8 < 1 ? 1 : (nk / 8 > 8 ? 8 : nk / 8);
+    const int64_t a = (smax - 1) * max_rows * d, b = (int64_t)1 << 24;
+    return (size_t)(a < b ? a : b);
+}
 
 // a_rows == nullptr: A is x_perm.  Otherwise A is the unpermuted x and packed
 // row m is x row a_rows[m] (token_of_row); x must span less than 2 GiB.
@@ -99,10 +119,12 @@ struct GemmOut {
 // kClaimCounters zeroed ints through which the 256-row GEMM's blocks claim
 // their work items (an XCD whose range is done takes items of another).
 // mid: null, or an event recorded between the gate-up and down launches.
+// splits: the down projection's uniform slices (ignored with down.plan; the
+// weight-streaming kernel's down projection honours it too).
 hipError_t launch_expert_ffn(const moe_params &p, int64_t max_rows, int64_t cap, const void *x_perm,
                              const int32_t *a_rows, const int32_t *offsets, const void *w1,
                              const void *w3, const void *w2, void *h, const GemmOut &down, int32_t *claim,
-                             hipEvent_t mid, hipStream_t st);
+                             hipEvent_t mid, hipStream_t st, int splits);
 
 // y_perm[r] += rest[0][r] + ... + rest[nrest-1][r] (slices max_rows * d
 // apart) for the rows below offsets[E]: a split down projection reduced in
@@ -193,9 +215,22 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
 hipError_t launch_combine(const moe_params &p, int64_t max_rows, const float *y_perm, const int32_t *row,
                           const float *gate, void *y, hipStream_t st);
 
-// bf16 layers: y[t] = sum over kept slots j and slices s of yg[s][row[t][j]],
-// yg the down projection's gated fp16 slices [splits][max_rows][d].
+// bf16 layers: y[t] = sum over kept slots j and slices s of the gated fp16
+// slices of row[t][j]: with plan null, yg[s][row] ([splits][max_rows][d],
+// yrest = yg + max_rows d); otherwise the down projection's split plan
+// (GemmOut): slice 0 in yg [max_rows][d], slices 1.. of the split rows at
+// yrest.
 hipError_t launch_combine_gated(const moe_params &p, int64_t max_rows, int splits, const uint16_t *yg,
-                                const int32_t *row, void *y, hipStream_t st);
+                                const uint16_t *yrest, const int32_t *plan, const int32_t *row, void *y,
+                                hipStream_t st);
+
+// moe_forward's down projection (bf16 layers): the 256-row MFMA GEMM with
+// the device-side split plan (planned), or S uniform slices (S = 1 for the
+// weight-streaming kernel, groups of at most 32 rows).
+struct DownSplit {
+    bool planned;
+    int S;
+};
+DownSplit forward_down_split(const moe_params &p, int64_t max_rows);
 
 }  // namespace moe

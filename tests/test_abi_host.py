@@ -50,6 +50,42 @@ def splits_of(p):
     return 1 + moe.ffn_workspace_bytes(p) // (R * p.d * 4)
 
 
+def down_split(p, R):
+    """moe_forward's down-projection split on the 256-row GEMM (more than 32
+    rows per expert), restated: the split plan for the bound on the m tiles
+    (min(R / 256 + E, E ceil(C / 256))) of ntn = ceil(d / 256) n tiles: the
+    tiles fill whole rounds of 256 -> one slice; else G = the last round's
+    m tiles rounded up, S = min(256 / (G ntn), clamp(d_ff / 512, 1, 8));
+    S = 1 -> one slice; G = every m tile -> S uniform slices; otherwise the
+    device-side plan."""
+    C = moe.capacity(p)
+    if C <= 32:
+        return "uniform", 1
+    mt = min(R // 256 + p.E, p.E * -(-C // 256))
+    ntn, nk = -(-p.d // 256), p.d_ff // 64
+    rem = (mt * ntn) % 256
+    if rem == 0:
+        return "uniform", 1
+    G = min(mt, -(-rem // ntn))
+    S = min(256 // (G * ntn), min(8, max(1, nk // 8)))
+    if S <= 1:
+        return "uniform", 1
+    if G == mt and nk % S == 0:
+        return "uniform", S
+    return "planned", 1
+
+
+def gated_rows_bytes(p, R):
+    """moe_forward's gated fp16 rows: slice 0 [R][d], plus (when the down
+    projection is split) the further slices, at most min(2^24, (S_max - 1) R d)
+    elements, S_max = clamp(d_ff / 512, 1, 8)."""
+    extra = 0
+    if down_split(p, R) != ("uniform", 1):
+        smax = min(8, max(1, p.d_ff // 64 // 8))
+        extra = min(1 << 24, (smax - 1) * R * p.d)
+    return (R * p.d + extra) * 2
+
+
 def test_workspace_sizes_cover_buffers():
     p = P(T=4096, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
     R = moe.max_rows(p)
@@ -57,10 +93,13 @@ def test_workspace_sizes_cover_buffers():
     ws = moe.workspace_bytes(p)
     S = splits_of(p)
     assert S == 2 and moe.ffn_workspace_bytes(p) == (S - 1) * R * 4096 * 4
-    # h [R][d_ff] (fp16), the gated rows [S][R][d] (fp16) and the row gates [R];
+    # h [R][d_ff] (fp16), the gated rows (slice 0 [R][d] fp16 and at most
+    # 2^24 elements of the split rows' further slices) and the row gates [R];
     # x spans less than 2 GiB, so moe_forward reads the gate-up rows from x and
     # needs no x_perm
-    base = R * 14336 * 2 + S * R * 4096 * 2 + R * 4 + moe.dispatch_workspace_bytes(p)
+    assert down_split(p, R) == ("planned", 1)
+    assert gated_rows_bytes(p, R) == (R * 4096 + (1 << 24)) * 2
+    base = R * 14336 * 2 + gated_rows_bytes(p, R) + R * 4 + moe.dispatch_workspace_bytes(p)
     assert base <= ws < base + R * 4096 * 2
     assert moe.dispatch_workspace_bytes(p) > 0
     # an fp32 layer keeps y_perm [R][d] in fp32 and needs no row gates
@@ -72,10 +111,29 @@ def test_workspace_sizes_cover_buffers():
     # x of 2 GiB and more: moe_forward writes x_perm [R][d] into its workspace
     for T, has_xp in (((1 << 18) - 1, False), (1 << 18, True)):
         q = P(T=T, d=4096, E=8, k=2, d_ff=1024, capacity_factor=1.0, dtype=moe.MOE_BF16)
-        Rq, Sq = moe.max_rows(q), splits_of(q)
-        base = Rq * 1024 * 2 + Sq * Rq * 4096 * 2 + Rq * 4 + moe.dispatch_workspace_bytes(q)
+        Rq = moe.max_rows(q)
+        base = Rq * 1024 * 2 + gated_rows_bytes(q, Rq) + Rq * 4 + moe.dispatch_workspace_bytes(q)
         wq = moe.workspace_bytes(q)
         assert (wq >= base + Rq * 4096 * 2) == has_xp and wq >= base, (T, wq, base)
+
+
+def test_forward_down_split_choice():
+    """Which down projection moe_forward runs, read back from its workspace
+    size: the Mixtral-shape layer the planned split (the last round's m tiles
+    split), the skewed layer two uniform slices (every tile split), the
+    fine-grained layer one slice (the tiles fill whole rounds), decode the
+    weight-streaming kernel's one slice."""
+    mix = P(T=4096, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
+    skew = P(T=2048, d=2048, E=16, k=2, d_ff=5632, capacity_factor=1.0, dtype=moe.MOE_BF16)
+    fine = P(T=8192, d=4096, E=64, k=2, d_ff=2048, capacity_factor=1.0, dtype=moe.MOE_BF16)
+    dec = P(T=64, d=4096, E=8, k=2, d_ff=14336, capacity_factor=1.25, dtype=moe.MOE_BF16)
+    want = {"mix": ("planned", 1), "skew": ("uniform", 2), "fine": ("uniform", 1), "dec": ("uniform", 1)}
+    for name, q in (("mix", mix), ("skew", skew), ("fine", fine), ("dec", dec)):
+        R = moe.max_rows(q)
+        assert down_split(q, R) == want[name], name
+        # the workspace holds exactly the gated rows the choice needs
+        rest = moe.workspace_bytes(q) - gated_rows_bytes(q, R)
+        assert 0 < rest - q.d_ff * R * 2 - R * 4 - moe.dispatch_workspace_bytes(q) < 8 * 256, name
 
 
 def test_ffn_workspace_only_for_split_down_projections():

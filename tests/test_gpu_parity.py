@@ -171,7 +171,7 @@ def sample_rows(offsets, n_per, rng, cap=48):
     return np.array(sorted(rows), np.int32)
 
 
-def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False, stored=False):
+def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False, stored=False, extra_toks=None):
     """Run the four stage entry points, check each against the oracle, then
     moe_forward end to end (stored: see assert_close)."""
     cfg = L.cfg
@@ -260,6 +260,8 @@ def run_stages(L, p, full_rows=False, n_tok=16, rms_kept_rows=False, stored=Fals
     rc2 = r2.cpu()
     ref2 = routing_vs_oracle(p, rc2, gl2, L.load, p.lam)
     toks = np.arange(T, dtype=np.int32) if (full_rows or T <= 64) else sample_tokens(ref2, T, n_tok, rng)
+    if extra_toks is not None:
+        toks = np.union1d(toks, extra_toks(ref2)).astype(np.int32)
     yref = oracle.layer_tokens(toks, L.c["x"], L.c["w1"], L.c["w3"], L.c["w2"], ref2["eid"], ref2["gate64"])
     kept_rows = (ref2["flag"][toks] != 2).any(axis=1) if rms_kept_rows else None
     rel = assert_close(y2.float().cpu().numpy()[toks], yref, p.dtype, "layer output", kept_rows, stored=stored)
@@ -277,6 +279,59 @@ def test_workload_parity(name):
     L = Layer(cfg)
     p = params(cfg)
     run_stages(L, p, full_rows=(name == "tiny"))
+
+
+def split_plan_row0(offsets, d, d_ff):
+    """The down projection's split plan for the actual m tiles (restated from
+    its definition: the tiles past whole rounds of 256 items, rounded up to
+    whole m tiles, are split in K into as many slices as fit one round, at
+    most clamp(d_ff / 512, 1, 8)): (G split m tiles, S slices, first split
+    row)."""
+    mts = [-(-(int(offsets[e + 1]) - int(offsets[e])) // 256) for e in range(len(offsets) - 1)]
+    M, ntn, nk = sum(mts), -(-d // 256), d_ff // 64
+    rem = (M * ntn) % 256
+    G = 0 if rem == 0 else min(M, -(-rem // ntn))
+    S = min(256 // (G * ntn), min(8, max(1, nk // 8))) if G else 1
+    if S <= 1:
+        return 0, 1, int(offsets[-1])
+    pre = 0
+    for e, m in enumerate(mts):
+        if pre + m > M - G:
+            return G, S, int(offsets[e]) + 256 * max(M - G - pre, 0)
+        pre += m
+
+
+# moe_forward's planned down projection (the last round's m tiles split in
+# K): the device plans for the actual m tiles, here one fewer than the host's
+# bound (2 slices; 3 uneven slices of 26 K steps), or none left to split.
+PLANNED = {
+    "plan_s2": (dict(T=2176, d=4096, E=4, k=2, d_ff=1024, cf=1.25), (4, 2)),
+    "plan_s3_uneven": (dict(T=2176, d=4096, E=4, k=2, d_ff=1664, cf=1.25), (4, 3)),
+    "plan_none_at_runtime": (dict(T=2000, d=4096, E=4, k=2, d_ff=1024, cf=1.25), (0, 1)),
+}
+
+
+@pytest.mark.parametrize("case", list(PLANNED))
+def test_down_split_plan(case):
+    kw, want = PLANNED[case]
+    cfg = small_cfg(**kw)
+    L = Layer(cfg)
+    p = params(cfg)
+
+    def around_split(ref):
+        # tokens with a kept row on each side of the first split row, and in
+        # the last m tile
+        G, S, row0 = split_plan_row0(ref["offsets"], cfg.d, cfg.d_ff)
+        assert (G, S) == want, (G, S)
+        rows = ref["row"]
+        end = int(ref["offsets"][-1])
+        picks = []
+        for lo, hi in ((row0 - 8, row0), (row0, row0 + 8), (end - 8, end)):
+            picks += np.nonzero(((rows >= lo) & (rows < hi)).any(axis=1))[0][:6].tolist()
+        return np.array(picks, np.int32)
+
+    say(f"[case] split plan {case}")
+    run_stages(L, p, n_tok=24, extra_toks=around_split)
 
 
 def small_cfg(**kw):
