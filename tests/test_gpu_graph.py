@@ -59,8 +59,10 @@ def snapshot(r, y, logits):
     return r.cpu(), y.cpu(), logits.cpu()
 
 
+# skew: two uniform down slices; fine64: one; mixtral at T 2100: the
+# device-side split plan (8 of 24 m tiles split in two)
 @pytest.mark.parametrize("entry,name,T", [("forward", "skew", None), ("forward", "fine64", 2048),
-                                          ("noalloc", "mixtral", 128)])
+                                          ("forward", "mixtral", 2100), ("noalloc", "mixtral", 128)])
 def test_forward_graph_replay(entry, name, T):
     cfg = moe_synth.CONFIGS[name]
     T = cfg.T if T is None else T
