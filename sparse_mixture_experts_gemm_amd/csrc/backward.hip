@@ -15,14 +15,19 @@
 //   dx_t = sum_j (W1_e^T da + W3_e^T db)[row_j] + sum_j ds_j W_r[e_j]
 //   dW1_e = sum_r da_r x_t^T,  dW3_e = sum_r db_r x_t^T,  dW2_e = sum_r dy_t hg_r^T
 //   dW_r[e] = sum_r ds_r x_t,  dbias[e] = sum_r ds_r
-// Every gradient is fp32.  The GEMMs run on bf16 MFMA (32x32x16) with fp32
-// accumulation.  x, dy and the weights are exact bf16 operands; da, db and hg
-// are computed in fp32 and kept as a pair of bf16 values, hi = bf16(v) and
-// lo = bf16(v - hi) (v to about 2^-17 relative), whose two MFMAs against the
-// same partner fragment accumulate into one result: a single bf16 rounding of
-// these operands would put up to 2^-9 of the largest terms into the weight
-// gradients.  All reductions run in a fixed order: the results are the same
-// on every run.
+// Every gradient is fp32.  The GEMMs run on bf16 or fp16 MFMA (32x32x16)
+// with fp32 accumulation.  x, dy and the weights are exact bf16 operands; da,
+// db and hg are computed in fp32 and kept as a pair of bf16 values, hi =
+// bf16(v) and lo = bf16(v - hi) (v to about 2^-17 relative), whose two MFMAs
+// against the same partner fragment accumulate into one result: a single
+// bf16 rounding of these operands would put up to 2^-9 of the largest terms
+// into the weight gradients.  dW1 and dW3 take da and db as one fp16 value
+// each instead (2^-12 relative, an eighth of a bf16 rounding), scaled per
+// expert by a power of 2 that keeps the expert's largest |da|, |db| inside
+// fp16's range (grad_scale_exp), against x in fp16 (exact for |x| below
+// 65504 down to 2^-14, then fp16's subnormal steps of 2^-24); the epilogue
+// undoes the scale.  This halves the K of those two GEMMs.  All reductions
+// run in a fixed order: the results are the same on every run.
 #include <algorithm>
 
 #include "device_common.h"
@@ -39,15 +44,25 @@ namespace {
 // 64 x 64 LDS tiles, for grouped_gemm_wgrad.
 
 // The kept rows of each expert, transposed into its K window (kwin_start):
-//   dst[c][kwin_e + koff + j] = src[src_row(offsets[e] + j)][col0 + c]
+//   dst[c][kwin_e + koff + j] = conv(src[src_row(offsets[e] + j)][col0 + c])
 // for j < rows_e, zeros for rows_e <= j < Kp_e (Kp_e = rows_e rounded up to
 // 64); koff = half * Kp_e, or both halves (dup).  src_row(r) = gather[r] or
-// r; src rows hold src_ld elements.  Blocks: (expert, 64 kept rows, 64
-// columns), found like the GEMM's tiles.
+// r; src rows hold src_ld elements.  conv: CONV 0 copies the 16-bit value;
+// CONV 1 takes a bf16 value to fp16 (round to nearest even); CONV 2 adds the
+// bf16 hi value and its lo partner lo_off elements further, scales the sum
+// by 2^grad_scale_exp(amax[e]) and rounds it to fp16.  Blocks: (expert, 64
+// kept rows, 64 columns), found like the GEMM's tiles.
+__device__ __forceinline__ uint32_t f16x2_bits(float a, float b) {
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
+}
+
+template <int CONV>
 __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ src, int64_t src_ld,
                                                  const int32_t *__restrict__ gather, int col0, int ncols,
                                                  const int32_t *__restrict__ offsets, int E,
-                                                 uint16_t *__restrict__ dst, int64_t ldk, int half, int dup) {
+                                                 uint16_t *__restrict__ dst, int64_t ldk, int half, int dup,
+                                                 int64_t lo_off, const uint32_t *__restrict__ amax) {
     __shared__ uint16_t t[64][66];
     TileInfo ti;
     if (!find_tile(offsets, E, ncols / 64, 64, 1, blockIdx.x, nullptr, nullptr, ti)) return;
@@ -55,15 +70,29 @@ __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ sr
     const int kp = (rows + 63) & ~63;
     const int j0 = ti.m0 - rbeg, c0 = ti.nt * 64;
     const int tid = threadIdx.x, q = (tid & 7) * 8;
+    const int kscale = CONV == 2 ? grad_scale_exp(amax[ti.e]) : 0;
 #pragma unroll
     for (int ps = 0; ps < 2; ps++) {
         const int rr = (tid >> 3) + 32 * ps, r = ti.m0 + rr;
-        uint4 v = make_uint4(0, 0, 0, 0);
+        uint4 v = make_uint4(0, 0, 0, 0), lo = make_uint4(0, 0, 0, 0);
         if (r < ti.mend) {
             const int64_t sr = gather ? gather[r] : r;
             v = *reinterpret_cast<const uint4 *>(src + sr * src_ld + col0 + c0 + q);
+            if (CONV == 2) lo = *reinterpret_cast<const uint4 *>(src + sr * src_ld + col0 + c0 + q + lo_off);
         }
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        if (CONV != 0) {
+            const uint32_t l[4] = {lo.x, lo.y, lo.z, lo.w};
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                float f0 = bf16_bits_to_f32(w[i] & 0xFFFF), f1 = bf16_bits_to_f32(w[i] >> 16);
+                if (CONV == 2) {
+                    f0 = ldexpf(f0 + bf16_bits_to_f32(l[i] & 0xFFFF), kscale);
+                    f1 = ldexpf(f1 + bf16_bits_to_f32(l[i] >> 16), kscale);
+                }
+                w[i] = f16x2_bits(f0, f1);
+            }
+        }
 #pragma unroll
         for (int i = 0; i < 4; i++) *reinterpret_cast<uint32_t *>(&t[rr][q + 2 * i]) = w[i];
     }
@@ -88,11 +117,14 @@ __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ sr
 
 // unit_offsets: e * m1 (e = 0..E), then e * m2: the uniform row ranges of
 // the weight-gradient GEMMs' outputs.
-__global__ __launch_bounds__(256) void unit_offsets_kernel(int32_t *__restrict__ o, int E, int m1, int m2) {
+// (and amax[e] = 0, for swiglu_backward's maxima)
+__global__ __launch_bounds__(256) void unit_offsets_kernel(int32_t *__restrict__ o, int E, int m1, int m2,
+                                                           uint32_t *__restrict__ amax) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i > E) return;
     o[i] = i * m1;
     o[E + 1 + i] = i * m2;
+    if (i < E) amax[i] = 0u;
 }
 
 __global__ __launch_bounds__(256) void fill_zero(float *__restrict__ p, size_t n) {
@@ -119,20 +151,24 @@ __global__ __launch_bounds__(256) void row_gates(const int32_t *__restrict__ row
 // Per kept row (one block): h = silu(a) b, dg = u . h (fixed-order block
 // reduction), da = g u b silu'(a), db = g u silu(a), hg = g h, each as a
 // bf16 hi/lo pair: acat row [da hi | db hi | da lo | db lo] (4 d_ff), hg row
-// [hi | lo] (2 d_ff).
+// [hi | lo] (2 d_ff).  The row's largest |da|, |db| goes into amax[e] of its
+// expert (an atomic maximum of the fp32 bits, which order non-negative
+// values: the same result in any order).
 __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__ a, const float *__restrict__ b,
                                                        const float *__restrict__ u,
                                                        const float *__restrict__ gate_of_row,
                                                        const int32_t *__restrict__ offsets, int E, int dff,
                                                        uint16_t *__restrict__ acat, uint16_t *__restrict__ hg,
-                                                       float *__restrict__ dg) {
+                                                       float *__restrict__ dg, uint32_t *__restrict__ amax) {
     __shared__ float part[256];
+    __shared__ uint32_t pmax[256];
     const int r = blockIdx.x;
     if (r >= offsets[E]) return;
     const float g = gate_of_row[r];
     const size_t o = (size_t)r * dff;
     uint16_t *ar = acat + 4 * o, *hr = hg + 2 * o;
     float s = 0.0f;
+    uint32_t mx = 0u;
     for (int f = threadIdx.x * 2; f < dff; f += 512) {
         float dav[2], dbv[2], hv[2];
 #pragma unroll
@@ -144,18 +180,33 @@ __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__
             dav[i] = dh * bv * sg * (1.0f + av * (1.0f - sg));
             dbv[i] = dh * silu;
             hv[i] = g * h;
+            mx = max(mx, max(__float_as_uint(fabsf(dav[i])), __float_as_uint(fabsf(dbv[i]))));
         }
         store_hi_lo(ar + f, 2 * (size_t)dff, dav);
         store_hi_lo(ar + dff + f, 2 * (size_t)dff, dbv);
         store_hi_lo(hr + f, (size_t)dff, hv);
     }
     part[threadIdx.x] = s;
+    pmax[threadIdx.x] = mx;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
-        if (threadIdx.x < w) part[threadIdx.x] += part[threadIdx.x + w];
+        if (threadIdx.x < w) {
+            part[threadIdx.x] += part[threadIdx.x + w];
+            pmax[threadIdx.x] = max(pmax[threadIdx.x], pmax[threadIdx.x + w]);
+        }
         __syncthreads();
     }
-    if (threadIdx.x == 0) dg[r] = part[0];
+    if (threadIdx.x == 0) {
+        dg[r] = part[0];
+        // the row's expert: the last e with offsets[e] <= r
+        int lo = 0, hi = E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (offsets[mid] <= r) lo = mid;
+            else hi = mid;
+        }
+        atomicMax(&amax[lo], pmax[0]);
+    }
 }
 
 // Gate softmax backward, one thread per token: ds_j = g_j (dg_j - sum_l g_l
@@ -224,8 +275,8 @@ __global__ __launch_bounds__(256) void input_grad(const float *__restrict__ dx_p
 }
 
 // dW_r[e][c] = sum over the kept rows r of expert e of ds_r x[tok_r][c] and
-// dbias[e] = sum_r ds_r, from the kept rows' transposed x (xt, the expert's
-// K window: rows_e values then zero padding).  Block (e, 64 columns), a wave
+// dbias[e] = sum_r ds_r, from the kept rows' transposed x (xt in fp16, the
+// expert's K window: rows_e values then zero padding).  Block (e, 64 columns), a wave
 // per 16 columns: lane l accumulates window positions 8l .. 8l+7 of every
 // 512 in order, then a fixed butterfly over the lanes adds the partial sums.
 __global__ __launch_bounds__(256) void router_wgrad(const uint16_t *__restrict__ xt, int64_t ldk,
@@ -253,8 +304,8 @@ __global__ __launch_bounds__(256) void router_wgrad(const uint16_t *__restrict__
             const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
             for (int i = 0; i < 4; i++) {
-                acc[c] = fmaf(ds[2 * i], bf16_bits_to_f32(w[i] & 0xFFFF), acc[c]);
-                acc[c] = fmaf(ds[2 * i + 1], bf16_bits_to_f32(w[i] >> 16), acc[c]);
+                acc[c] = fmaf(ds[2 * i], (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] & 0xFFFF)), acc[c]);
+                acc[c] = fmaf(ds[2 * i + 1], (float)__builtin_bit_cast(_Float16, (uint16_t)(w[i] >> 16)), acc[c]);
             }
         }
     }
@@ -303,17 +354,17 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     const int32_t *uo_f = a.unit_offsets, *uo_d = a.unit_offsets + E + 1;
     // bound on the 64-row tiles of the kept rows, for the transposes' grids
     const int64_t mt64 = std::min<int64_t>(R / 64 + E, (int64_t)E * ceil_div(cap, 64));
-    auto kmajor = [&](const uint16_t *src, int64_t src_ld, const int32_t *gather, int col0, int ncols,
-                      uint16_t *dst, int half, int dup) {
-        hipLaunchKernelGGL(to_kmajor, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, st, src, src_ld, gather,
-                           col0, ncols, a.offsets, E, dst, ldk, half, dup);
+    auto kmajor = [&](auto kern, const uint16_t *src, int64_t src_ld, const int32_t *gather, int col0, int ncols,
+                      uint16_t *dst, int half, int dup, int64_t lo_off) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, st, src, src_ld, gather, col0,
+                           ncols, a.offsets, E, dst, ldk, half, dup, lo_off, (const uint32_t *)a.amax);
     };
     // 1. the rows' gates, the weight-gradient row ranges; a and b
     //    recomputed by the gate-up GEMM
     hipLaunchKernelGGL(row_gates, dim3((unsigned)ceil_div((int64_t)T * k, 256)), dim3(256), 0, st, a.row, a.gate,
                        T * k, a.gate_of_row);
     hipLaunchKernelGGL(unit_offsets_kernel, dim3((unsigned)ceil_div(E + 1, 256)), dim3(256), 0, st, a.unit_offsets,
-                       E, dff, d);
+                       E, dff, d, a.amax);
     hipError_t e = launch_gate_up_raw(p, R, cap, a.x, a.token_of_row, a.offsets, a.w1, a.w3, a.a, a.b, st);
     if (e != hipSuccess) return e;
     // 2. u = W2_e^T dy_t for every kept row (dy rows gathered by token; W2
@@ -325,7 +376,7 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     if (e != hipSuccess) return e;
     // 3. SwiGLU backward per row, 4. gate softmax backward per token
     hipLaunchKernelGGL(swiglu_backward, dim3((unsigned)R), dim3(256), 0, st, a.a, a.b, a.u, a.gate_of_row, a.offsets,
-                       E, dff, a.acat, a.hg, a.dg);
+                       E, dff, a.acat, a.hg, a.dg, a.amax);
     hipLaunchKernelGGL(gate_backward, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st, a.row, a.eid, a.gate, a.dg,
                        T, E, k, inv_tau, a.dlogits, a.ds_of_row);
     // 5. dx_perm = da_hi W1 + db_hi W3 + da_lo W1 + db_lo W3: K periods of
@@ -337,17 +388,19 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,
                        static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, k, d, a.dx);
     // 7. the kept rows transposed into their experts' K windows: da and db
-    //    (hi, lo), x (twice), dy (twice), g h (hi, lo)
-    kmajor(a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0);
-    kmajor(a.acat, 4 * (int64_t)dff, nullptr, 2 * dff, 2 * dff, a.dat, 1, 0);
-    kmajor(x, d, a.token_of_row, 0, d, a.xt, 0, 1);
-    kmajor(dy, d, a.token_of_row, 0, d, a.dyt, 0, 1);
-    kmajor(a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0);
-    kmajor(a.hg, 2 * (int64_t)dff, nullptr, dff, dff, a.hgt, 1, 0);
-    // 8. dW1 = da^T x, dW3 = db^T x, dW2 = dy^T (g h), each expert over its rows
-    e = launch_wgrad_gemm(E, a.dat, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw1, st);
+    //    (scaled fp16 from their hi/lo pairs), x (fp16), dy (twice), g h (hi,
+    //    lo)
+    kmajor(to_kmajor<2>, a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0, 2 * (int64_t)dff);
+    kmajor(to_kmajor<1>, x, d, a.token_of_row, 0, d, a.xt, 0, 0, 0);
+    kmajor(to_kmajor<0>, dy, d, a.token_of_row, 0, d, a.dyt, 0, 1, 0);
+    kmajor(to_kmajor<0>, a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0, 0);
+    kmajor(to_kmajor<0>, a.hg, 2 * (int64_t)dff, nullptr, dff, dff, a.hgt, 1, 0, 0);
+    // 8. dW1 = da^T x, dW3 = db^T x (fp16), dW2 = dy^T (g h), each expert over
+    //    its rows
+    e = launch_wgrad_gemm(E, a.dat, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw1, st, a.amax);
     if (e != hipSuccess) return e;
-    e = launch_wgrad_gemm(E, a.dat + (size_t)dff * ldk, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw3, st);
+    e = launch_wgrad_gemm(E, a.dat + (size_t)dff * ldk, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw3, st,
+                          a.amax);
     if (e != hipSuccess) return e;
     e = launch_wgrad_gemm(E, a.dyt, a.hgt, a.offsets, uo_d, d, dff, (int)ldk, a.dw2, st);
     if (e != hipSuccess) return e;

@@ -64,8 +64,11 @@ constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (
 // the natural layout of W2 for u = dy W2 and of W1 / W3 for the input
 // gradient): a B stage holds 64 K rows of the tile's 256 columns and the
 // fragments are read with the transposing LDS read (ds_read_b64_tr_b16).
+// kPlainH: kPlain on fp16 operands (the weight gradients dW1 and dW3: the
+// scaled fp16 da or db against fp16 x), its fp32 result multiplied by
+// GemmOut::scale in the epilogue.
 enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2, kPlain = 3, kGateUpE4M3 = 4, kDownE4M3 = 5, kGateUpI8 = 6,
-       kDownI8 = 7, kPlainBT = 8 };
+       kDownI8 = 7, kPlainBT = 8, kPlainH = 9 };
 
 // one-byte weight codes: OCP E4M3 or INT8
 enum { kQE4M3 = 0, kQInt8 = 1 };
@@ -329,7 +332,7 @@ __device__ __forceinline__ void zero_a_if(bool pad, Frags &f) {
 // straight-line.
 template <int MODE, int NACT, int I0, int I1>
 __device__ __forceinline__ void mfma_blocks(const Frags &f, f32x16_t (&acc)[4][4]) {
-    constexpr bool kF16 = down_mode<MODE>();
+    constexpr bool kF16 = down_mode<MODE>() || MODE == kPlainH;
 #pragma unroll
     for (int i = I0; i < (I1 < NACT ? I1 : NACT); i++) {
 #pragma unroll
@@ -660,7 +663,13 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
                         *reinterpret_cast<uint2 *>(slice_row<uint16_t, PLAN>(out, ti, m, N) + col) =
                             make_uint2(lo, hi2);
                 } else if (m < ti.mend && col < N) {
-                    *reinterpret_cast<uint4 *>(slice_row<float, PLAN>(out, ti, m, N) + col) = v;
+                    uint4 o = v;
+                    if constexpr (MODE == kPlainH)
+                        o = make_uint4(__float_as_uint(out.scale * __uint_as_float(v.x)),
+                                       __float_as_uint(out.scale * __uint_as_float(v.y)),
+                                       __float_as_uint(out.scale * __uint_as_float(v.z)),
+                                       __float_as_uint(out.scale * __uint_as_float(v.w)));
+                    *reinterpret_cast<uint4 *>(slice_row<float, PLAN>(out, ti, m, N) + col) = o;
                 }
             }
         }
@@ -859,9 +868,14 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
 // tile) over uniform row ranges (unit_offsets[e] = e M); an expert without
 // rows gets zeros.  The main loop, LDS layout and epilogue are those of
 // grouped_gemm_bf16<kPlain>.
+// H: fp16 operands holding only the first half of each window (kPlainH),
+// A scaled by 2^k_e per expert (k_e = grad_scale_exp(amax[e])), undone in the
+// epilogue.
+template <bool H>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_wgrad(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ unit_offsets, int E, int M, int N, int ldk, int ntiles_n, float *__restrict__ C) {
+    const int32_t *__restrict__ unit_offsets, int E, int M, int N, int ldk, int ntiles_n, float *__restrict__ C,
+    const uint32_t *__restrict__ amax) {
     __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
@@ -878,10 +892,11 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_wgrad(
     const int rbeg = offsets[e], rows = offsets[e + 1] - rbeg;
     const int kp = (rows + kBK - 1) / kBK * kBK;
     const int kwin = kwin_start(rbeg, e);
-    const int nk = __builtin_amdgcn_readfirstlane(2 * kp / kBK);
+    const int nk = __builtin_amdgcn_readfirstlane((H ? 1 : 2) * kp / kBK);
     const int m_rel = ti.m0 - e * M;
     const int n0 = ti.nt * kBN;
-    const GemmOut out{C, nullptr, 0, nullptr};
+    GemmOut out{C, nullptr, 0, nullptr};
+    if constexpr (H) out.scale = ldexpf(1.0f, -grad_scale_exp(amax[e]));
     if (nk == 0) {
         // no rows: the tile of C_e is zero (16-byte stores, N a multiple of 64)
         const int mv = min(kBM, M - m_rel), nv = min(kBN, N - n0);
@@ -921,7 +936,9 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_wgrad(
             g.fb[pp][ss] = (uint32_t)(wn * 128 + l5) * kRowBytes + sw;
         }
     const int nact = __builtin_amdgcn_readfirstlane(max(0, min(4, (g.a_valid - wm * 128 + 31) / 32)));
-#define MOE_TILE(n) run_tile<kPlain, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane, out)
+#define MOE_TILE(n)                                                                                              \
+    run_tile<H ? kPlainH : kPlain, n, false>(g, ti, lds_a0, lds_a1, lds_b0, lds_b1, lds_b2, nk, n0, N, wm, wn, lane, \
+                                             out)
     switch (nact) {
         case 4: MOE_TILE(4); break;
         case 3: MOE_TILE(3); break;
@@ -1942,12 +1959,14 @@ hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_
 }
 
 hipError_t launch_wgrad_gemm(int E, const uint16_t *A, const uint16_t *B, const int32_t *offsets,
-                             const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st) {
+                             const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st,
+                             const uint32_t *amax) {
     if (E <= 0 || M <= 0 || N <= 0) return hipSuccess;
     if (N % 64 != 0 || (int64_t)kBM * ldk * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int mt = (int)ceil_div(M, kBM), nt = (int)ceil_div(N, kBN);
-    hipLaunchKernelGGL(grouped_gemm_wgrad, dim3((unsigned)((int64_t)E * mt * nt)), dim3(kGemmThreads), 0, st, A, B,
-                       offsets, unit_offsets, E, M, N, ldk, nt, C);
+    auto *kern = amax ? grouped_gemm_wgrad<true> : grouped_gemm_wgrad<false>;
+    hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)E * mt * nt)), dim3(kGemmThreads), 0, st, A, B, offsets,
+                       unit_offsets, E, M, N, ldk, nt, C, amax);
     return hipGetLastError();
 }
 

@@ -189,8 +189,9 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
 // gate_of_row, ds_of_row, dg [R] fp32; a, b, u [R][d_ff] fp32; acat
 // [R][4 d_ff] and hg [R][2 d_ff] bf16; dx_perm [S][R][d] fp32 (S K slices
 // of the dx GEMM, at least one per d_ff period of its K); the K-major
-// copies of the kept rows, [2 d_ff], [d], [d] and [d_ff] rows of ldk bf16;
-// two sets of E + 1 unit offsets.
+// copies of the kept rows, [2 d_ff], [d], [d] and [d_ff] rows of ldk 16-bit
+// values (da, db and x in fp16); two sets of E + 1 unit offsets; the
+// experts' largest |da|, |db| [E].
 struct BackwardSizes {
     size_t R, F, D, E, ldk;
     int S;
@@ -212,7 +213,7 @@ size_t backward_ws_bytes(const moe_params &p) {
     return 3 * align256(z.R * 4) + 3 * align256(z.R * z.F * 4) + align256(z.R * 4 * z.F * 2) +
            align256(z.R * 2 * z.F * 2) + align256((size_t)z.S * z.R * z.D * 4) + align256(2 * z.F * z.ldk * 2) +
            2 * align256(z.D * z.ldk * 2) +
-           align256(z.F * z.ldk * 2) + align256(2 * (z.E + 1) * 4);
+           align256(z.F * z.ldk * 2) + align256(2 * (z.E + 1) * 4) + align256(z.E * 4);
 }
 
 void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
@@ -238,6 +239,7 @@ void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
     a.dyt = reinterpret_cast<uint16_t *>(take(z.D * z.ldk * 2));
     a.hgt = reinterpret_cast<uint16_t *>(take(z.F * z.ldk * 2));
     a.unit_offsets = reinterpret_cast<int32_t *>(take(2 * (z.E + 1) * 4));
+    a.amax = reinterpret_cast<uint32_t *>(take(z.E * 4));
     a.ldk = (int64_t)z.ldk;
     a.dx_splits = z.S;
 }

@@ -101,6 +101,7 @@ struct GemmOut {
     size_t stride;
     const float *row_gate;
     int32_t *plan = nullptr;
+    float scale = 1.0f;  // kPlainH (weight gradients on scaled fp16): the epilogue's factor
 };
 
 // Elements of the planned down projection's second slice buffer: (S - 1)
@@ -183,9 +184,22 @@ constexpr int64_t backward_ldk(int64_t max_rows, int E) { return 2 * (((max_rows
 // Weight gradients: C_e = A_e B_e^T over expert e's K window, A [M][ldk],
 // B [N][ldk] bf16, C fp32 [E][M][N] (zeros for an expert without rows);
 // unit_offsets[e] = e M (E + 1 ints).  256 rows of ldk elements must stay
-// below 2 GiB.
+// below 2 GiB.  With amax: A and B fp16 over the first half of each window
+// only, A scaled by 2^grad_scale_exp(amax[e]), which C undoes.
 hipError_t launch_wgrad_gemm(int E, const uint16_t *A, const uint16_t *B, const int32_t *offsets,
-                             const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st);
+                             const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st,
+                             const uint32_t *amax = nullptr);
+
+// Power-of-2 exponent k of a scaled fp16 gradient operand whose largest
+// magnitude has the fp32 bits amax_bits: 2^k maps that magnitude into
+// [2^14, 2^15), inside fp16's range with 2^28 of headroom below it for the
+// smaller elements' normal numbers (fp16 keeps 11 significant bits there,
+// against bf16's 8).  No scaling for a zero, subnormal, infinite or NaN
+// maximum (which the fp16 values then carry as they are).
+__host__ __device__ inline int grad_scale_exp(uint32_t amax_bits) {
+    const int ex = (int)((amax_bits >> 23) & 0xFF);
+    return (ex == 0 || ex == 255) ? 0 : 141 - ex;
+}
 
 // Backward pass of a bf16 layer: inputs, the forward's routing, gradients
 // (fp32) and the workspace buffers.
@@ -200,8 +214,11 @@ struct BackwardArgs {
     uint16_t *hg;                         // [R][2 d_ff] bf16: (g h) hi, lo
     float *dx_perm;                       // [R][d]
     float *dx_rest;                       // [S - 1][R][d]: the dx GEMM's other K slices
-    uint16_t *dat;                        // [2 d_ff][ldk]: da^T then db^T, per-expert K windows (hi, lo)
-    uint16_t *xt, *dyt;                   // [d][ldk]: x^T, dy^T of the kept rows (twice per window)
+    uint16_t *dat;                        // [2 d_ff][ldk]: da^T then db^T, fp16 scaled by 2^k_e (first half
+                                          // of each expert's K window)
+    uint16_t *xt;                         // [d][ldk]: x^T of the kept rows in fp16 (first half of each window)
+    uint16_t *dyt;                        // [d][ldk]: dy^T of the kept rows (twice per window)
+    uint32_t *amax;                       // [E]: largest |da|, |db| of each expert's rows (fp32 bits)
     uint16_t *hgt;                        // [d_ff][ldk]: (g h)^T (hi, lo)
     int32_t *unit_offsets;                // [2][E + 1]: e 2 d_ff, then e d
     int64_t ldk;
