@@ -21,12 +21,13 @@
 // bf16(v) and lo = bf16(v - hi) (v to about 2^-17 relative), whose two MFMAs
 // against the same partner fragment accumulate into one result: a single
 // bf16 rounding of these operands would put up to 2^-9 of the largest terms
-// into the weight gradients.  dW1 and dW3 take da and db as one fp16 value
-// each instead (2^-12 relative, an eighth of a bf16 rounding), scaled per
-// expert by a power of 2 that keeps the expert's largest |da|, |db| inside
-// fp16's range (grad_scale_exp), against x in fp16 (exact for |x| below
-// 65504 down to 2^-14, then fp16's subnormal steps of 2^-24); the epilogue
-// undoes the scale.  This halves the K of those two GEMMs.  All reductions
+// into the weight gradients.  dW1, dW3 and dx take da and db as one fp16
+// value each instead (2^-12 relative, an eighth of a bf16 rounding), scaled
+// per expert by a power of 2 that keeps the expert's largest |da|, |db|
+// inside fp16's range (grad_scale_exp), against x in fp16 (exact for |x|
+// below 65504 down to 2^-14, then fp16's subnormal steps of 2^-24) or W1, W3
+// in fp16 (the same range, as the forward's W2); the weight gradients'
+// epilogue and input_grad undo the scale.  This halves the K of those GEMMs.  All reductions
 // run in a fixed order: the results are the same on every run.
 #include <algorithm>
 
@@ -50,8 +51,9 @@ namespace {
 // r; src rows hold src_ld elements.  conv: CONV 0 copies the 16-bit value;
 // CONV 1 takes a bf16 value to fp16 (round to nearest even); CONV 2 adds the
 // bf16 hi value and its lo partner lo_off elements further, scales the sum
-// by 2^grad_scale_exp(amax[e]) and rounds it to fp16.  Blocks: (expert, 64
-// kept rows, 64 columns), found like the GEMM's tiles.
+// by 2^grad_scale_exp(amax[e]) and rounds it to fp16, which it also stores
+// untransposed at rm[r][c] (rows of ncols).  Blocks: (expert, 64 kept rows,
+// 64 columns), found like the GEMM's tiles.
 __device__ __forceinline__ uint32_t f16x2_bits(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
@@ -62,7 +64,8 @@ __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ sr
                                                  const int32_t *__restrict__ gather, int col0, int ncols,
                                                  const int32_t *__restrict__ offsets, int E,
                                                  uint16_t *__restrict__ dst, int64_t ldk, int half, int dup,
-                                                 int64_t lo_off, const uint32_t *__restrict__ amax) {
+                                                 int64_t lo_off, const uint32_t *__restrict__ amax,
+                                                 uint16_t *__restrict__ rm) {
     __shared__ uint16_t t[64][66];
     TileInfo ti;
     if (!find_tile(offsets, E, ncols / 64, 64, 1, blockIdx.x, nullptr, nullptr, ti)) return;
@@ -92,6 +95,8 @@ __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ sr
                 }
                 w[i] = f16x2_bits(f0, f1);
             }
+            if (CONV == 2 && r < ti.mend)
+                *reinterpret_cast<uint4 *>(rm + (size_t)r * ncols + c0 + q) = make_uint4(w[0], w[1], w[2], w[3]);
         }
 #pragma unroll
         for (int i = 0; i < 4; i++) *reinterpret_cast<uint32_t *>(&t[rr][q + 2 * i]) = w[i];
@@ -239,15 +244,18 @@ __global__ __launch_bounds__(256) void gate_backward(const int32_t *__restrict__
 // order), fp32; 8 columns per thread.
 __global__ __launch_bounds__(256) void input_grad(const float *__restrict__ dx_perm, const uint16_t *__restrict__ wr,
                                                   const int32_t *__restrict__ row, const int32_t *__restrict__ eid,
-                                                  const float *__restrict__ ds_of_row, int k, int d,
+                                                  const float *__restrict__ ds_of_row,
+                                                  const uint32_t *__restrict__ amax, int k, int d,
                                                   float *__restrict__ dx) {
     const int t = blockIdx.x;
     int rws[kMaxTopK], es[kMaxTopK];
-    float ds[kMaxTopK];
+    float ds[kMaxTopK], sc[kMaxTopK];
     for (int j = 0; j < k; j++) {
         rws[j] = row[(size_t)t * k + j];
         es[j] = eid[(size_t)t * k + j];
         ds[j] = rws[j] >= 0 ? ds_of_row[rws[j]] : 0.0f;
+        // dx_perm rows hold W1^T da + W3^T db scaled by their expert's 2^k
+        sc[j] = rws[j] >= 0 ? ldexpf(1.0f, -grad_scale_exp(amax[es[j]])) : 0.0f;
     }
     for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
         float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -255,8 +263,9 @@ __global__ __launch_bounds__(256) void input_grad(const float *__restrict__ dx_p
             if (rws[j] < 0) continue;
             const float4 *p = reinterpret_cast<const float4 *>(dx_perm + (size_t)rws[j] * d + c);
             const float4 v0 = p[0], v1 = p[1];
-            acc[0] += v0.x; acc[1] += v0.y; acc[2] += v0.z; acc[3] += v0.w;
-            acc[4] += v1.x; acc[5] += v1.y; acc[6] += v1.z; acc[7] += v1.w;
+            const float s = sc[j];
+            acc[0] += s * v0.x; acc[1] += s * v0.y; acc[2] += s * v0.z; acc[3] += s * v0.w;
+            acc[4] += s * v1.x; acc[5] += s * v1.y; acc[6] += s * v1.z; acc[7] += s * v1.w;
         }
         for (int j = 0; j < k; j++) {
             if (rws[j] < 0) continue;
@@ -357,7 +366,7 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     auto kmajor = [&](auto kern, const uint16_t *src, int64_t src_ld, const int32_t *gather, int col0, int ncols,
                       uint16_t *dst, int half, int dup, int64_t lo_off) {
         hipLaunchKernelGGL(kern, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, st, src, src_ld, gather, col0,
-                           ncols, a.offsets, E, dst, ldk, half, dup, lo_off, (const uint32_t *)a.amax);
+                           ncols, a.offsets, E, dst, ldk, half, dup, lo_off, (const uint32_t *)a.amax, a.dab16);
     };
     // 1. the rows' gates, the weight-gradient row ranges; a and b
     //    recomputed by the gate-up GEMM
@@ -379,18 +388,20 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
                        E, dff, a.acat, a.hg, a.dg, a.amax);
     hipLaunchKernelGGL(gate_backward, dim3((unsigned)ceil_div(T, 256)), dim3(256), 0, st, a.row, a.eid, a.gate, a.dg,
                        T, E, k, inv_tau, a.dlogits, a.ds_of_row);
-    // 5. dx_perm = da_hi W1 + db_hi W3 + da_lo W1 + db_lo W3: K periods of
-    //    d_ff over the concatenated acat row, W1 and W3 ([d_ff][d],
-    //    N-contiguous) in turn, at least one K slice per period; 6. dx
-    e = launch_plain_gemm(R, cap, E, a.acat, nullptr, 0, a.offsets, w1, w3, true, d, 4 * dff, dff, a.dx_splits,
-                          a.dx_perm, a.dx_rest, st);
+    // 5. da and db as scaled fp16 from their hi/lo pairs, K-major in their
+    //    experts' K windows (dat) and row-major (dab16)
+    kmajor(to_kmajor<2>, a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0, 2 * (int64_t)dff);
+    // 6. dx_perm = 2^k_e (da W1 + db W3): two K periods of d_ff over the
+    //    dab16 row, W1 and W3 ([d_ff][d], N-contiguous, widened to fp16) in
+    //    turn, at least one K slice per period; dx, the scale undone per slot
+    e = launch_plain_gemm(R, cap, E, a.dab16, nullptr, 0, a.offsets, w1, w3, true, d, 2 * dff, dff, a.dx_splits,
+                          a.dx_perm, a.dx_rest, st, true);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,
-                       static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, k, d, a.dx);
-    // 7. the kept rows transposed into their experts' K windows: da and db
-    //    (scaled fp16 from their hi/lo pairs), x (fp16), dy (twice), g h (hi,
-    //    lo)
-    kmajor(to_kmajor<2>, a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0, 2 * (int64_t)dff);
+                       static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, (const uint32_t *)a.amax,
+                       k, d, a.dx);
+    // 7. the kept rows transposed into their experts' K windows: x (fp16),
+    //    dy (twice), g h (hi, lo)
     kmajor(to_kmajor<1>, x, d, a.token_of_row, 0, d, a.xt, 0, 0, 0);
     kmajor(to_kmajor<0>, dy, d, a.token_of_row, 0, d, a.dyt, 0, 1, 0);
     kmajor(to_kmajor<0>, a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0, 0);

@@ -67,8 +67,10 @@ constexpr int kRowsPerLoad = 1024 / kRowBytes;           // rows per wave load (
 // kPlainH: kPlain on fp16 operands (the weight gradients dW1 and dW3: the
 // scaled fp16 da or db against fp16 x), its fp32 result multiplied by
 // GemmOut::scale in the epilogue.
+// kPlainBTH: kPlainBT with A in fp16 (the input gradient: the scaled fp16 da
+// and db against W1 and W3), B widened to fp16 after the transposing read.
 enum { kGateUp = 0, kDown = 1, kGateUpRaw = 2, kPlain = 3, kGateUpE4M3 = 4, kDownE4M3 = 5, kGateUpI8 = 6,
-       kDownI8 = 7, kPlainBT = 8, kPlainH = 9 };
+       kDownI8 = 7, kPlainBT = 8, kPlainH = 9, kPlainBTH = 10 };
 
 // one-byte weight codes: OCP E4M3 or INT8
 enum { kQE4M3 = 0, kQInt8 = 1 };
@@ -78,7 +80,7 @@ __device__ __forceinline__ constexpr bool q_mode() { return MODE >= kGateUpE4M3 
 template <int MODE>
 __device__ __forceinline__ constexpr int q_fmt() { return MODE >= kGateUpI8 ? kQInt8 : kQE4M3; }
 template <int MODE>
-__device__ __forceinline__ constexpr bool b_trans() { return MODE == kPlainBT; }
+__device__ __forceinline__ constexpr bool b_trans() { return MODE == kPlainBT || MODE == kPlainBTH; }
 // The SwiGLU epilogue (h = silu(a) * b, fp16)
 template <int MODE>
 __device__ __forceinline__ constexpr bool gate_up() { return MODE == kGateUp || MODE == kGateUpE4M3 || MODE == kGateUpI8; }
@@ -309,7 +311,7 @@ __device__ __forceinline__ void load_frags(const GemmThread &g, const char *abuf
 // codes widened exactly to bf16 (gate-up) or fp16 (down).
 template <int MODE>
 __device__ __forceinline__ void widen_b(Frags &f) {
-    if constexpr (MODE == kDown) {
+    if constexpr (MODE == kDown || MODE == kPlainBTH) {
 #pragma unroll
         for (int jn = 0; jn < 4; jn++) f.b[jn] = bf16x8_to_f16x8(f.b[jn]);
     } else if constexpr (q_mode<MODE>()) {
@@ -332,7 +334,7 @@ __device__ __forceinline__ void zero_a_if(bool pad, Frags &f) {
 // straight-line.
 template <int MODE, int NACT, int I0, int I1>
 __device__ __forceinline__ void mfma_blocks(const Frags &f, f32x16_t (&acc)[4][4]) {
-    constexpr bool kF16 = down_mode<MODE>() || MODE == kPlainH;
+    constexpr bool kF16 = down_mode<MODE>() || MODE == kPlainH || MODE == kPlainBTH;
 #pragma unroll
     for (int i = I0; i < (I1 < NACT ? I1 : NACT); i++) {
 #pragma unroll
@@ -366,7 +368,7 @@ __device__ __forceinline__ void sched_half() {
             if (HALF == 0) SCHED_DSR(1);
             if (HALF == 0 && LOADS && (q * NV) / 8 != ((q + 1) * NV) / 8) SCHED_VMEM(1);
             if (HALF == 1 && LOADS && (q * NV) / 8 != ((q + 1) * NV) / 8) SCHED_VMEM(1);
-            if (HALF == 1 && MODE == kDown) SCHED_VALU(6);
+            if (HALF == 1 && (MODE == kDown || MODE == kPlainBTH)) SCHED_VALU(6);
             if (HALF == 1 && q_mode<MODE>()) SCHED_VALU(q_fmt<MODE>() == kQInt8 ? 6 : 2);
         }
     }
@@ -1934,18 +1936,21 @@ int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb) {
 
 hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
                              int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, const uint16_t *B1,
-                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st) {
+                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st,
+                             bool a_f16) {
     if (max_rows <= 0) return hipSuccess;
     if (S < 1 || K % S != 0 || (K / S) % kBK != 0 || ldb % (K / S) != 0 || N % 64 != 0 ||
         a_span_bytes >= ((int64_t)1 << 31) || (int64_t)N * ldb * 2 >= ((int64_t)1 << 32))
         return hipErrorInvalidValue;
     const int64_t mt = mtile_bound(max_rows, cap, E, kBM);
     const int nt = (int)ceil_div(N, kBN);
-    if (b_n_contig)
-        hipLaunchKernelGGL(grouped_gemm_bf16<kPlainBT>, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A,
-                           a_rows, B, B1 ? B1 : B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes,
-                           (int32_t *)nullptr, GemmOut{C, rest, (size_t)max_rows * N, nullptr});
-    else
+    if (b_n_contig) {
+        auto *kern = a_f16 ? grouped_gemm_bf16<kPlainBTH, false> : grouped_gemm_bf16<kPlainBT, false>;
+        hipLaunchKernelGGL(kern, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A, a_rows, B,
+                           B1 ? B1 : B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes, (int32_t *)nullptr,
+                           GemmOut{C, rest, (size_t)max_rows * N, nullptr}, (const float *)nullptr,
+                           (const float *)nullptr);
+    } else
         hipLaunchKernelGGL(grouped_gemm_bf16<kPlain>, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A,
                            a_rows, B, B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes, (int32_t *)nullptr,
                            GemmOut{C, rest, (size_t)max_rows * N, nullptr});

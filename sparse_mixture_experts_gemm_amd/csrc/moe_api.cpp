@@ -186,8 +186,9 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
 }
 
 // Workspace layout of moe_backward (sizes in bytes, each 256-aligned):
-// gate_of_row, ds_of_row, dg [R] fp32; a, b, u [R][d_ff] fp32; acat
-// [R][4 d_ff] and hg [R][2 d_ff] bf16; dx_perm [S][R][d] fp32 (S K slices
+// gate_of_row, ds_of_row, dg [R] fp32; a, b, u [R][d_ff] fp32 (a's bytes
+// then hold the scaled fp16 da, db [R][2 d_ff]); acat [R][4 d_ff] and hg
+// [R][2 d_ff] bf16; dx_perm [S][R][d] fp32 (S K slices
 // of the dx GEMM, at least one per d_ff period of its K); the K-major
 // copies of the kept rows, [2 d_ff], [d], [d] and [d_ff] rows of ldk 16-bit
 // values (da, db and x in fp16); two sets of E + 1 unit offsets; the
@@ -204,7 +205,7 @@ BackwardSizes backward_sizes(const moe_params &p) {
     z.D = (size_t)p.d;
     z.E = (size_t)p.E;
     z.ldk = (size_t)backward_ldk((int64_t)z.R, p.E);
-    z.S = plain_gemm_splits((int64_t)z.R, p.E, p.d, 4 * p.d_ff, p.d_ff);
+    z.S = plain_gemm_splits((int64_t)z.R, p.E, p.d, 2 * p.d_ff, p.d_ff);
     return z;
 }
 
@@ -231,6 +232,7 @@ void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
     a.b = reinterpret_cast<float *>(take(z.R * z.F * 4));
     a.u = reinterpret_cast<float *>(take(z.R * z.F * 4));
     a.acat = reinterpret_cast<uint16_t *>(take(z.R * 4 * z.F * 2));
+    a.dab16 = reinterpret_cast<uint16_t *>(a.a);  // a is read only by swiglu_backward, before
     a.hg = reinterpret_cast<uint16_t *>(take(z.R * 2 * z.F * 2));
     a.dx_perm = reinterpret_cast<float *>(take((size_t)z.S * z.R * z.D * 4));
     a.dx_rest = a.dx_perm + z.R * z.D;

@@ -167,10 +167,11 @@ hipError_t launch_gate_up_raw(const moe_params &p, int64_t max_rows, int64_t cap
 // of 64 that divides ldb); slice s reads B at K position (s K / S) mod ldb,
 // so slices can share one B; slice s > 0 stores its partial product at
 // rest + (s - 1) max_rows N, and a fix-up adds the slices into C in order.
+// a_f16 (with b_n_contig): A holds fp16 values, and B is widened to fp16.
 int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb);
 hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
                              int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, const uint16_t *B1,
-                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st);
+                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st, bool a_f16 = false);
 
 // Per-expert K windows of the backward's transposed operands: the kept rows
 // of expert e (rows_e of them, from offsets[e]) become K positions
@@ -211,6 +212,7 @@ struct BackwardArgs {
     float *gate_of_row, *ds_of_row, *dg;  // [R]
     float *a, *b, *u;                     // [R][d_ff]
     uint16_t *acat;                       // [R][4 d_ff] bf16: da hi, db hi, da lo, db lo
+    uint16_t *dab16;                      // [R][2 d_ff] fp16: da, db scaled by 2^k_e (over a, once free)
     uint16_t *hg;                         // [R][2 d_ff] bf16: (g h) hi, lo
     float *dx_perm;                       // [R][d]
     float *dx_rest;                       // [S - 1][R][d]: the dx GEMM's other K slices
