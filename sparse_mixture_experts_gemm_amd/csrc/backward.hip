@@ -49,11 +49,12 @@ namespace {
 // for j < rows_e, zeros for rows_e <= j < Kp_e (Kp_e = rows_e rounded up to
 // 64); koff = half * Kp_e, or both halves (dup).  src_row(r) = gather[r] or
 // r; src rows hold src_ld elements.  conv: CONV 0 copies the 16-bit value;
-// CONV 1 takes a bf16 value to fp16 (round to nearest even); CONV 2 adds the
-// bf16 hi value and its lo partner lo_off elements further, scales the sum
-// by 2^grad_scale_exp(amax[e]) and rounds it to fp16, which it also stores
-// untransposed at rm[r][c] (rows of ncols).  Blocks: (expert, 64 kept rows,
-// 64 columns), found like the GEMM's tiles.
+// CONV 1 scales a bf16 value by 2^grad_scale_exp(amax[0]) (amax null: 1) and
+// rounds it to fp16 (to nearest even); CONV 2 adds the bf16 hi value and its
+// lo partner lo_off elements further, scales the sum by
+// 2^grad_scale_exp(amax[e]) and rounds it to fp16, which it also stores
+// untransposed at rm[r][c] (rows of ncols) when rm is given.  Blocks:
+// (expert, 64 kept rows, 64 columns), found like the GEMM's tiles.
 __device__ __forceinline__ uint32_t f16x2_bits(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ sr
     const int kp = (rows + 63) & ~63;
     const int j0 = ti.m0 - rbeg, c0 = ti.nt * 64;
     const int tid = threadIdx.x, q = (tid & 7) * 8;
-    const int kscale = CONV == 2 ? grad_scale_exp(amax[ti.e]) : 0;
+    const int kscale = CONV == 2 ? grad_scale_exp(amax[ti.e]) : (CONV == 1 && amax ? grad_scale_exp(amax[0]) : 0);
 #pragma unroll
     for (int ps = 0; ps < 2; ps++) {
         const int rr = (tid >> 3) + 32 * ps, r = ti.m0 + rr;
@@ -90,12 +91,14 @@ __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ sr
             for (int i = 0; i < 4; i++) {
                 float f0 = bf16_bits_to_f32(w[i] & 0xFFFF), f1 = bf16_bits_to_f32(w[i] >> 16);
                 if (CONV == 2) {
-                    f0 = ldexpf(f0 + bf16_bits_to_f32(l[i] & 0xFFFF), kscale);
-                    f1 = ldexpf(f1 + bf16_bits_to_f32(l[i] >> 16), kscale);
+                    f0 += bf16_bits_to_f32(l[i] & 0xFFFF);
+                    f1 += bf16_bits_to_f32(l[i] >> 16);
                 }
+                f0 = ldexpf(f0, kscale);
+                f1 = ldexpf(f1, kscale);
                 w[i] = f16x2_bits(f0, f1);
             }
-            if (CONV == 2 && r < ti.mend)
+            if (CONV == 2 && rm && r < ti.mend)
                 *reinterpret_cast<uint4 *>(rm + (size_t)r * ncols + c0 + q) = make_uint4(w[0], w[1], w[2], w[3]);
         }
 #pragma unroll
@@ -122,14 +125,35 @@ __global__ __launch_bounds__(256) void to_kmajor(const uint16_t *__restrict__ sr
 
 // unit_offsets: e * m1 (e = 0..E), then e * m2: the uniform row ranges of
 // the weight-gradient GEMMs' outputs.
-// (and amax[e] = 0, for swiglu_backward's maxima)
+// (and the 2 E + 1 maxima zeroed, for swiglu_backward and abs_max)
 __global__ __launch_bounds__(256) void unit_offsets_kernel(int32_t *__restrict__ o, int E, int m1, int m2,
                                                            uint32_t *__restrict__ amax) {
     const int i = blockIdx.x * 256 + threadIdx.x;
     if (i > E) return;
     o[i] = i * m1;
     o[E + 1 + i] = i * m2;
-    if (i < E) amax[i] = 0u;
+    if (i < E) {
+        amax[i] = 0u;
+        amax[E + i] = 0u;
+    } else {
+        amax[2 * E] = 0u;
+    }
+}
+
+// *out = max(*out, the largest |v| of n bf16 values), as fp32 bits (an
+// atomic maximum, the same in any order).
+__global__ __launch_bounds__(256) void abs_max(const uint16_t *__restrict__ v, size_t n, uint32_t *__restrict__ out) {
+    __shared__ uint32_t part[256];
+    uint32_t m = 0u;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256)
+        m = max(m, (uint32_t)(v[i] & 0x7FFF) << 16);
+    part[threadIdx.x] = m;
+    __syncthreads();
+    for (int w = 128; w > 0; w >>= 1) {
+        if (threadIdx.x < w) part[threadIdx.x] = max(part[threadIdx.x], part[threadIdx.x + w]);
+        __syncthreads();
+    }
+    if (threadIdx.x == 0) atomicMax(out, part[0]);
 }
 
 __global__ __launch_bounds__(256) void fill_zero(float *__restrict__ p, size_t n) {
@@ -157,8 +181,8 @@ __global__ __launch_bounds__(256) void row_gates(const int32_t *__restrict__ row
 // reduction), da = g u b silu'(a), db = g u silu(a), hg = g h, each as a
 // bf16 hi/lo pair: acat row [da hi | db hi | da lo | db lo] (4 d_ff), hg row
 // [hi | lo] (2 d_ff).  The row's largest |da|, |db| goes into amax[e] of its
-// expert (an atomic maximum of the fp32 bits, which order non-negative
-// values: the same result in any order).
+// expert and its largest |g h| into amax[E + e] (atomic maxima of the fp32
+// bits, which order non-negative values: the same result in any order).
 __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__ a, const float *__restrict__ b,
                                                        const float *__restrict__ u,
                                                        const float *__restrict__ gate_of_row,
@@ -166,14 +190,14 @@ __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__
                                                        uint16_t *__restrict__ acat, uint16_t *__restrict__ hg,
                                                        float *__restrict__ dg, uint32_t *__restrict__ amax) {
     __shared__ float part[256];
-    __shared__ uint32_t pmax[256];
+    __shared__ uint32_t pmax[256], pmaxh[256];
     const int r = blockIdx.x;
     if (r >= offsets[E]) return;
     const float g = gate_of_row[r];
     const size_t o = (size_t)r * dff;
     uint16_t *ar = acat + 4 * o, *hr = hg + 2 * o;
     float s = 0.0f;
-    uint32_t mx = 0u;
+    uint32_t mx = 0u, mh = 0u;
     for (int f = threadIdx.x * 2; f < dff; f += 512) {
         float dav[2], dbv[2], hv[2];
 #pragma unroll
@@ -186,6 +210,7 @@ __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__
             dbv[i] = dh * silu;
             hv[i] = g * h;
             mx = max(mx, max(__float_as_uint(fabsf(dav[i])), __float_as_uint(fabsf(dbv[i]))));
+            mh = max(mh, __float_as_uint(fabsf(hv[i])));
         }
         store_hi_lo(ar + f, 2 * (size_t)dff, dav);
         store_hi_lo(ar + dff + f, 2 * (size_t)dff, dbv);
@@ -193,11 +218,13 @@ __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__
     }
     part[threadIdx.x] = s;
     pmax[threadIdx.x] = mx;
+    pmaxh[threadIdx.x] = mh;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
         if (threadIdx.x < w) {
             part[threadIdx.x] += part[threadIdx.x + w];
             pmax[threadIdx.x] = max(pmax[threadIdx.x], pmax[threadIdx.x + w]);
+            pmaxh[threadIdx.x] = max(pmaxh[threadIdx.x], pmaxh[threadIdx.x + w]);
         }
         __syncthreads();
     }
@@ -211,6 +238,7 @@ __global__ __launch_bounds__(256) void swiglu_backward(const float *__restrict__
             else hi = mid;
         }
         atomicMax(&amax[lo], pmax[0]);
+        atomicMax(&amax[E + lo], pmaxh[0]);
     }
 }
 
@@ -364,16 +392,19 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     // bound on the 64-row tiles of the kept rows, for the transposes' grids
     const int64_t mt64 = std::min<int64_t>(R / 64 + E, (int64_t)E * ceil_div(cap, 64));
     auto kmajor = [&](auto kern, const uint16_t *src, int64_t src_ld, const int32_t *gather, int col0, int ncols,
-                      uint16_t *dst, int half, int dup, int64_t lo_off) {
+                      uint16_t *dst, int half, int dup, int64_t lo_off, const uint32_t *amax, uint16_t *rm) {
         hipLaunchKernelGGL(kern, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, st, src, src_ld, gather, col0,
-                           ncols, a.offsets, E, dst, ldk, half, dup, lo_off, (const uint32_t *)a.amax, a.dab16);
+                           ncols, a.offsets, E, dst, ldk, half, dup, lo_off, amax, rm);
     };
+    const uint32_t *amax_dab = a.amax, *amax_hg = a.amax + E, *amax_dy = a.amax + 2 * E;
     // 1. the rows' gates, the weight-gradient row ranges; a and b
     //    recomputed by the gate-up GEMM
     hipLaunchKernelGGL(row_gates, dim3((unsigned)ceil_div((int64_t)T * k, 256)), dim3(256), 0, st, a.row, a.gate,
                        T * k, a.gate_of_row);
     hipLaunchKernelGGL(unit_offsets_kernel, dim3((unsigned)ceil_div(E + 1, 256)), dim3(256), 0, st, a.unit_offsets,
                        E, dff, d, a.amax);
+    hipLaunchKernelGGL(abs_max, dim3((unsigned)std::min<int64_t>(ceil_div((int64_t)T * d, 256 * 8), 1024)), dim3(256), 0,
+                       st, dy, (size_t)T * d, a.amax + 2 * E);
     hipError_t e = launch_gate_up_raw(p, R, cap, a.x, a.token_of_row, a.offsets, a.w1, a.w3, a.a, a.b, st);
     if (e != hipSuccess) return e;
     // 2. u = W2_e^T dy_t for every kept row (dy rows gathered by token; W2
@@ -390,7 +421,8 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
                        T, E, k, inv_tau, a.dlogits, a.ds_of_row);
     // 5. da and db as scaled fp16 from their hi/lo pairs, K-major in their
     //    experts' K windows (dat) and row-major (dab16)
-    kmajor(to_kmajor<2>, a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0, 2 * (int64_t)dff);
+    kmajor(to_kmajor<2>, a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0, 2 * (int64_t)dff, amax_dab,
+           a.dab16);
     // 6. dx_perm = 2^k_e (da W1 + db W3): two K periods of d_ff over the
     //    dab16 row, W1 and W3 ([d_ff][d], N-contiguous, widened to fp16) in
     //    turn, at least one K slice per period; dx, the scale undone per slot
@@ -398,22 +430,20 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
                           a.dx_perm, a.dx_rest, st, true);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,
-                       static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, (const uint32_t *)a.amax,
-                       k, d, a.dx);
-    // 7. the kept rows transposed into their experts' K windows: x (fp16),
-    //    dy (twice), g h (hi, lo)
-    kmajor(to_kmajor<1>, x, d, a.token_of_row, 0, d, a.xt, 0, 0, 0);
-    kmajor(to_kmajor<0>, dy, d, a.token_of_row, 0, d, a.dyt, 0, 1, 0);
-    kmajor(to_kmajor<0>, a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0, 0);
-    kmajor(to_kmajor<0>, a.hg, 2 * (int64_t)dff, nullptr, dff, dff, a.hgt, 1, 0, 0);
-    // 8. dW1 = da^T x, dW3 = db^T x (fp16), dW2 = dy^T (g h), each expert over
-    //    its rows
-    e = launch_wgrad_gemm(E, a.dat, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw1, st, a.amax);
+                       static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, amax_dab, k, d, a.dx);
+    // 7. the kept rows transposed into their experts' K windows, fp16: x,
+    //    dy (scaled by 2^k_dy), g h (from its hi/lo pair, scaled per expert)
+    kmajor(to_kmajor<1>, x, d, a.token_of_row, 0, d, a.xt, 0, 0, 0, nullptr, nullptr);
+    kmajor(to_kmajor<1>, dy, d, a.token_of_row, 0, d, a.dyt, 0, 0, 0, amax_dy, nullptr);
+    kmajor(to_kmajor<2>, a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0, dff, amax_hg, nullptr);
+    // 8. dW1 = da^T x, dW3 = db^T x, dW2 = dy^T (g h), each expert over its
+    //    rows, the scales undone in the epilogue
+    e = launch_wgrad_gemm(E, a.dat, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw1, st, amax_dab);
     if (e != hipSuccess) return e;
     e = launch_wgrad_gemm(E, a.dat + (size_t)dff * ldk, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw3, st,
-                          a.amax);
+                          amax_dab);
     if (e != hipSuccess) return e;
-    e = launch_wgrad_gemm(E, a.dyt, a.hgt, a.offsets, uo_d, d, dff, (int)ldk, a.dw2, st);
+    e = launch_wgrad_gemm(E, a.dyt, a.hgt, a.offsets, uo_d, d, dff, (int)ldk, a.dw2, st, amax_hg, amax_dy);
     if (e != hipSuccess) return e;
     // 9. router weight and bias gradients
     hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * (d / 64))), dim3(256), 0, st, a.xt, ldk, a.ds_of_row,

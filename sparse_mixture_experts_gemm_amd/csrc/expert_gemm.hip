@@ -871,13 +871,13 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
 // rows gets zeros.  The main loop, LDS layout and epilogue are those of
 // grouped_gemm_bf16<kPlain>.
 // H: fp16 operands holding only the first half of each window (kPlainH),
-// A scaled by 2^k_e per expert (k_e = grad_scale_exp(amax[e])), undone in the
-// epilogue.
+// one scaled by 2^k_e per expert (k_e = grad_scale_exp(amax[e])) and, with
+// gmax, the other by 2^grad_scale_exp(*gmax); the epilogue undoes both.
 template <bool H>
 __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_wgrad(
     const uint16_t *__restrict__ A, const uint16_t *__restrict__ B, const int32_t *__restrict__ offsets,
     const int32_t *__restrict__ unit_offsets, int E, int M, int N, int ldk, int ntiles_n, float *__restrict__ C,
-    const uint32_t *__restrict__ amax) {
+    const uint32_t *__restrict__ amax, const uint32_t *__restrict__ gmax) {
     __shared__ __attribute__((aligned(1024))) char lds_a0[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_a1[kTileBytes];
     __shared__ __attribute__((aligned(1024))) char lds_b0[kTileBytes];
@@ -898,7 +898,7 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_wgrad(
     const int m_rel = ti.m0 - e * M;
     const int n0 = ti.nt * kBN;
     GemmOut out{C, nullptr, 0, nullptr};
-    if constexpr (H) out.scale = ldexpf(1.0f, -grad_scale_exp(amax[e]));
+    if constexpr (H) out.scale = ldexpf(1.0f, -grad_scale_exp(amax[e]) - (gmax ? grad_scale_exp(*gmax) : 0));
     if (nk == 0) {
         // no rows: the tile of C_e is zero (16-byte stores, N a multiple of 64)
         const int mv = min(kBM, M - m_rel), nv = min(kBN, N - n0);
@@ -1965,13 +1965,13 @@ hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_
 
 hipError_t launch_wgrad_gemm(int E, const uint16_t *A, const uint16_t *B, const int32_t *offsets,
                              const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st,
-                             const uint32_t *amax) {
+                             const uint32_t *amax, const uint32_t *gmax) {
     if (E <= 0 || M <= 0 || N <= 0) return hipSuccess;
     if (N % 64 != 0 || (int64_t)kBM * ldk * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
     const int mt = (int)ceil_div(M, kBM), nt = (int)ceil_div(N, kBN);
     auto *kern = amax ? grouped_gemm_wgrad<true> : grouped_gemm_wgrad<false>;
     hipLaunchKernelGGL(kern, dim3((unsigned)((int64_t)E * mt * nt)), dim3(kGemmThreads), 0, st, A, B, offsets,
-                       unit_offsets, E, M, N, ldk, nt, C, amax);
+                       unit_offsets, E, M, N, ldk, nt, C, amax, gmax);
     return hipGetLastError();
 }
 

@@ -191,8 +191,8 @@ ForwardWs carve_forward(void *ws, const moe_params &p) {
 // [R][2 d_ff] bf16; dx_perm [S][R][d] fp32 (S K slices
 // of the dx GEMM, at least one per d_ff period of its K); the K-major
 // copies of the kept rows, [2 d_ff], [d], [d] and [d_ff] rows of ldk 16-bit
-// values (da, db and x in fp16); two sets of E + 1 unit offsets; the
-// experts' largest |da|, |db| [E].
+// values (da, db, x, dy and g h in fp16); two sets of E + 1 unit offsets;
+// the largest magnitudes that set the fp16 scales [2 E + 1].
 struct BackwardSizes {
     size_t R, F, D, E, ldk;
     int S;
@@ -214,7 +214,7 @@ size_t backward_ws_bytes(const moe_params &p) {
     return 3 * align256(z.R * 4) + 3 * align256(z.R * z.F * 4) + align256(z.R * 4 * z.F * 2) +
            align256(z.R * 2 * z.F * 2) + align256((size_t)z.S * z.R * z.D * 4) + align256(2 * z.F * z.ldk * 2) +
            2 * align256(z.D * z.ldk * 2) +
-           align256(z.F * z.ldk * 2) + align256(2 * (z.E + 1) * 4) + align256(z.E * 4);
+           align256(z.F * z.ldk * 2) + align256(2 * (z.E + 1) * 4) + align256((2 * z.E + 1) * 4);
 }
 
 void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
@@ -241,7 +241,7 @@ void carve_backward(void *ws, const moe_params &p, BackwardArgs &a) {
     a.dyt = reinterpret_cast<uint16_t *>(take(z.D * z.ldk * 2));
     a.hgt = reinterpret_cast<uint16_t *>(take(z.F * z.ldk * 2));
     a.unit_offsets = reinterpret_cast<int32_t *>(take(2 * (z.E + 1) * 4));
-    a.amax = reinterpret_cast<uint32_t *>(take(z.E * 4));
+    a.amax = reinterpret_cast<uint32_t *>(take((2 * z.E + 1) * 4));
     a.ldk = (int64_t)z.ldk;
     a.dx_splits = z.S;
 }

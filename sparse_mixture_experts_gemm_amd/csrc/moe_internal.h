@@ -186,10 +186,11 @@ constexpr int64_t backward_ldk(int64_t max_rows, int E) { return 2 * (((max_rows
 // B [N][ldk] bf16, C fp32 [E][M][N] (zeros for an expert without rows);
 // unit_offsets[e] = e M (E + 1 ints).  256 rows of ldk elements must stay
 // below 2 GiB.  With amax: A and B fp16 over the first half of each window
-// only, A scaled by 2^grad_scale_exp(amax[e]), which C undoes.
+// only, one of them scaled by 2^grad_scale_exp(amax[e]) and, with gmax, the
+// other by 2^grad_scale_exp(*gmax), which C undoes.
 hipError_t launch_wgrad_gemm(int E, const uint16_t *A, const uint16_t *B, const int32_t *offsets,
                              const int32_t *unit_offsets, int M, int N, int ldk, float *C, hipStream_t st,
-                             const uint32_t *amax = nullptr);
+                             const uint32_t *amax = nullptr, const uint32_t *gmax = nullptr);
 
 // Power-of-2 exponent k of a scaled fp16 gradient operand whose largest
 // magnitude has the fp32 bits amax_bits: 2^k maps that magnitude into
@@ -219,9 +220,10 @@ struct BackwardArgs {
     uint16_t *dat;                        // [2 d_ff][ldk]: da^T then db^T, fp16 scaled by 2^k_e (first half
                                           // of each expert's K window)
     uint16_t *xt;                         // [d][ldk]: x^T of the kept rows in fp16 (first half of each window)
-    uint16_t *dyt;                        // [d][ldk]: dy^T of the kept rows (twice per window)
-    uint32_t *amax;                       // [E]: largest |da|, |db| of each expert's rows (fp32 bits)
-    uint16_t *hgt;                        // [d_ff][ldk]: (g h)^T (hi, lo)
+    uint16_t *dyt;                        // [d][ldk]: dy^T of the kept rows in fp16 scaled by 2^k_dy (first half)
+    uint32_t *amax;                       // [2 E + 1] fp32 bits: each expert's largest |da|, |db|; each
+                                          // expert's largest |g h|; the largest |dy|
+    uint16_t *hgt;                        // [d_ff][ldk]: (g h)^T in fp16 scaled by 2^k_e (first half)
     int32_t *unit_offsets;                // [2][E + 1]: e 2 d_ff, then e d
     int64_t ldk;
     int dx_splits;
