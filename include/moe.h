@@ -365,11 +365,21 @@ size_t moe_backward_workspace_bytes(const moe_params *p);
  *   gradient of a per-expert router bias); dw1, dw3 [E][d_ff][d]; dw2
  *   [E][d][d_ff].  An expert without rows gets zero weight gradients.
  *   workspace: at least moe_backward_workspace_bytes(p) bytes, 256-B aligned.
- * The a = x W1^T, b = x W3^T products are recomputed; the GEMMs run on bf16
- * matrix cores with fp32 accumulation, x, dy and the weights as exact bf16
- * operands and the fp32 SwiGLU gradients and g * h as a pair of bf16 values
- * (hi = bf16(v), lo = bf16(v - hi), about 2^-17 relative) whose products
- * accumulate together.  Deterministic (no atomics).  MOE_ERR_UNSUPPORTED: an
+ * The a = x W1^T, b = x W3^T products are recomputed.  The GEMMs run on
+ * matrix cores with fp32 accumulation:
+ *   - u = dy W2 on bf16 (dy and W2 exact);
+ *   - dx, dw1, dw3 and dw2 on fp16.  The fp32 SwiGLU gradients da, db and
+ *     g * h are rounded once to fp16 (2^-12 relative), after scaling by a
+ *     power of 2 per expert that puts the expert's largest magnitude in
+ *     [2^14, 2^15).  dy is scaled likewise by its largest magnitude.  x, W1
+ *     and W3 enter as fp16 conversions of their bf16 values: exact for
+ *     magnitudes from 2^-14 up to 65504, fp16 subnormal steps of 2^-24
+ *     below, and infinite above (the forward pass already takes W2 and h on
+ *     the same range).
+ * Measured against the oracle, the weight and input gradients stay within
+ * 0.8% of their RMS.  Deterministic: the per-expert maxima are atomic
+ * maxima, the same in any order, and every sum runs in a fixed order.
+ * MOE_ERR_UNSUPPORTED: an
  * fp32 layer, the two-layer router, x of 2 GiB and more, or 2 GiB and more
  * in 256 rows of the kept rows' transposed K axis (1024 (R + 64 E) bytes, R
  * the kept row bound moe_max_rows rounded up to 64: about two million kept
