@@ -15,20 +15,21 @@
 //   dx_t = sum_j (W1_e^T da + W3_e^T db)[row_j] + sum_j ds_j W_r[e_j]
 //   dW1_e = sum_r da_r x_t^T,  dW3_e = sum_r db_r x_t^T,  dW2_e = sum_r dy_t hg_r^T
 //   dW_r[e] = sum_r ds_r x_t,  dbias[e] = sum_r ds_r
-// Every gradient is fp32.  The GEMMs run on bf16 or fp16 MFMA (32x32x16)
-// with fp32 accumulation.  x, dy and the weights are exact bf16 operands; da,
-// db and hg are computed in fp32 and kept as a pair of bf16 values, hi =
-// bf16(v) and lo = bf16(v - hi) (v to about 2^-17 relative), whose two MFMAs
-// against the same partner fragment accumulate into one result: a single
-// bf16 rounding of these operands would put up to 2^-9 of the largest terms
-// into the weight gradients.  dW1, dW3 and dx take da and db as one fp16
-// value each instead (2^-12 relative, an eighth of a bf16 rounding), scaled
-// per expert by a power of 2 that keeps the expert's largest |da|, |db|
-// inside fp16's range (grad_scale_exp), against x in fp16 (exact for |x|
-// below 65504 down to 2^-14, then fp16's subnormal steps of 2^-24) or W1, W3
-// in fp16 (the same range, as the forward's W2); the weight gradients'
-// epilogue and input_grad undo the scale.  This halves the K of those GEMMs.  All reductions
-// run in a fixed order: the results are the same on every run.
+// Every gradient is fp32.  The GEMMs run on MFMA (32x32x16) with fp32
+// accumulation: u = W2^T dy on bf16 (both exact), the others on fp16.  da,
+// db and hg are computed in fp32; a single bf16 rounding of them would put
+// up to 2^-9 of the largest terms into the gradients, so they were kept as
+// hi = bf16(v) and lo = bf16(v - hi) pairs (about 2^-17 relative, two MFMAs
+// per product).  They now enter as one fp16 value each (2^-12 relative, an
+// eighth of a bf16 rounding), hi + lo scaled by a power of 2 per expert that
+// keeps the expert's largest |da|, |db| (or |hg|) inside fp16's range
+// (grad_scale_exp); dy is scaled by its largest magnitude in the same way.
+// x, W1 and W3 enter as fp16 (exact from 2^-14 up to 65504, fp16's subnormal
+// steps of 2^-24 below; the forward's W2 has the same range).  The weight
+// gradients' epilogue and input_grad undo the scales.  This halves the K of
+// the dx and weight-gradient GEMMs.  All sums run in a fixed order and the
+// maxima are atomic maxima (the same in any order): the results are the same
+// on every run.
 #include <algorithm>
 
 #include "device_common.h"
