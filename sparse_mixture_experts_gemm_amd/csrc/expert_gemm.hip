@@ -45,6 +45,7 @@ namespace {
 constexpr int kGemmThreads = 256;
 constexpr int kBM = 256;   // rows per tile
 constexpr int kBN = 256;   // weight rows per tile (gate-up: 128 of W1 + 128 of W3)
+constexpr int kWgradGroupM = 8;  // m tiles per group in the weight-gradient tile order
 constexpr int kBK = 64;    // K per pipeline step: 128-byte row segments (one cache line)
 constexpr int kRowBytes = kBK * 2;           // one tile row in LDS
 constexpr int kTileBytes = kBM * kRowBytes;  // one operand tile (32 KiB)
@@ -891,6 +892,20 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_wgrad(
     TileInfo ti;
     if (!find_tile(unit_offsets, E, ntiles_n, kBM, 1, blockIdx.x, nullptr, nullptr, ti)) return;
     const int e = ti.e;
+    {
+        // Reorder an expert's tiles in groups of kWgradGroupM m tiles, n
+        // tiles outer and m inner inside a group, so that the 32 tiles an
+        // XCD runs together span about 8 m tiles by 4 n tiles and share
+        // both operands in its L2 (m fastest over all 56 m tiles of a
+        // d_ff-sized M would fetch a distinct A tile per block).
+        const int mt = (M + kBM - 1) / kBM;
+        const int rem = ti.nt * mt + (ti.m0 - e * M) / kBM;
+        const int grp = rem / (kWgradGroupM * ntiles_n);
+        const int gm = min(kWgradGroupM, mt - grp * kWgradGroupM);
+        const int j = rem - grp * kWgradGroupM * ntiles_n;
+        ti.nt = __builtin_amdgcn_readfirstlane(j / gm);
+        ti.m0 = __builtin_amdgcn_readfirstlane(e * M + (grp * kWgradGroupM + j % gm) * kBM);
+    }
     const int rbeg = offsets[e], rows = offsets[e + 1] - rbeg;
     const int kp = (rows + kBK - 1) / kBK * kBK;
     const int kwin = kwin_start(rbeg, e);
