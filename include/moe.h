@@ -44,7 +44,13 @@
  *     concurrently.  The only global mutable state is the static scratch
  *     array of moe_forward_noalloc (one per GPU): calls of that entry point
  *     that overlap on one GPU race; every other entry point works in the
- *     caller's buffers only.
+ *     caller's buffers only.  moe_backward runs part of its work on a second
+ *     stream of the library's own (made on its first call on a device,
+ *     default priority, kept until the process ends), forked from and
+ *     joined back to `stream` with events, so its outputs are still valid
+ *     once `stream` has reached the call's end; where that stream cannot be
+ *     made (e.g. first called inside a graph capture) all its work runs on
+ *     `stream`.
  *
  * Return codes: MOE_OK (0) on success, or a negative MOE_ERR_* code; nothing
  * is enqueued when an argument check fails.  moe_strerror() names the code.

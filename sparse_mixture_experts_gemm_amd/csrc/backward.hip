@@ -31,6 +31,7 @@
 // maxima are atomic maxima (the same in any order): the results are the same
 // on every run.
 #include <algorithm>
+#include <mutex>
 
 #include "device_common.h"
 #include "grouped_tiles.h"
@@ -362,6 +363,52 @@ __global__ __launch_bounds__(256) void router_wgrad(const uint16_t *__restrict__
     if (blockIdx.x % nc == 0 && threadIdx.x == 0) dbias[e] = sb;
 }
 
+// The weight-gradient half of the backward (the transposes of x, dy and
+// g h, the three weight-gradient GEMMs and the router gradients) and its
+// input-gradient half (the dx GEMM and input_grad) read the same inputs and
+// write disjoint buffers.  The weight-gradient half runs on a second stream
+// of the device, forked from the caller's stream and joined back to it by
+// two events, so that its memory-bound transposes and the weight gradients'
+// fp32 stores overlap the dx GEMM's matrix work.  The stream (default
+// priority) and events are made on first use per device and kept until the
+// process ends; where that fails (e.g. inside a graph capture), both halves
+// run in order on the caller's stream.  side_mu is held from the fork to the
+// join, so calls from several host threads never swap each other's events.
+struct SideStream {
+    hipStream_t s = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+constexpr int kMaxSideDevices = 64;
+std::mutex side_mu;
+SideStream side_streams[kMaxSideDevices];
+
+// The current device's side stream, or null; side_mu held.
+const SideStream *side_stream() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxSideDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    SideStream &ss = side_streams[dev];
+    if (!ss.s) {
+        hipStream_t s = nullptr;
+        hipEvent_t f = nullptr, j = nullptr;
+        if (hipStreamCreateWithFlags(&s, hipStreamNonBlocking) == hipSuccess &&
+            hipEventCreateWithFlags(&f, hipEventDisableTiming) == hipSuccess &&
+            hipEventCreateWithFlags(&j, hipEventDisableTiming) == hipSuccess) {
+            ss.fork = f;
+            ss.join = j;
+            ss.s = s;
+        } else {
+            if (j) (void)hipEventDestroy(j);
+            if (f) (void)hipEventDestroy(f);
+            if (s) (void)hipStreamDestroy(s);
+            (void)hipGetLastError();
+        }
+    }
+    return ss.s ? &ss : nullptr;
+}
+
 }  // namespace
 
 hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, const BackwardArgs &a, hipStream_t st) {
@@ -393,8 +440,9 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     // bound on the 64-row tiles of the kept rows, for the transposes' grids
     const int64_t mt64 = std::min<int64_t>(R / 64 + E, (int64_t)E * ceil_div(cap, 64));
     auto kmajor = [&](auto kern, const uint16_t *src, int64_t src_ld, const int32_t *gather, int col0, int ncols,
-                      uint16_t *dst, int half, int dup, int64_t lo_off, const uint32_t *amax, uint16_t *rm) {
-        hipLaunchKernelGGL(kern, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, st, src, src_ld, gather, col0,
+                      uint16_t *dst, int half, int dup, int64_t lo_off, const uint32_t *amax, uint16_t *rm,
+                      hipStream_t s) {
+        hipLaunchKernelGGL(kern, dim3((unsigned)(mt64 * (ncols / 64))), dim3(256), 0, s, src, src_ld, gather, col0,
                            ncols, a.offsets, E, dst, ldk, half, dup, lo_off, amax, rm);
     };
     const uint32_t *amax_dab = a.amax, *amax_hg = a.amax + E, *amax_dy = a.amax + 2 * E;
@@ -423,33 +471,56 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     // 5. da and db as scaled fp16 from their hi/lo pairs, K-major in their
     //    experts' K windows (dat) and row-major (dab16)
     kmajor(to_kmajor<2>, a.acat, 4 * (int64_t)dff, nullptr, 0, 2 * dff, a.dat, 0, 0, 2 * (int64_t)dff, amax_dab,
-           a.dab16);
+           a.dab16, st);
+    // fork: the weight-gradient half (7-9) on the side stream sw
+    std::lock_guard<std::mutex> lock(side_mu);
+    const SideStream *ss = side_stream();
+    hipStream_t sw = st;
+    if (ss) {
+        if (hipEventRecord(ss->fork, st) == hipSuccess && hipStreamWaitEvent(ss->s, ss->fork, 0) == hipSuccess)
+            sw = ss->s;
+        else
+            (void)hipGetLastError();
+    }
+    // (the side half is enqueued first, so that its transposes start at once
+    // and its short weight-gradient tiles interleave with the dx GEMM's)
+    // 7. the kept rows transposed into their experts' K windows, fp16: x,
+    //    dy (scaled by 2^k_dy), g h (from its hi/lo pair, scaled per expert)
+    kmajor(to_kmajor<1>, x, d, a.token_of_row, 0, d, a.xt, 0, 0, 0, nullptr, nullptr, sw);
+    kmajor(to_kmajor<1>, dy, d, a.token_of_row, 0, d, a.dyt, 0, 0, 0, amax_dy, nullptr, sw);
+    kmajor(to_kmajor<2>, a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0, dff, amax_hg, nullptr, sw);
+    // 8. dW1 = da^T x, dW3 = db^T x, dW2 = dy^T (g h), each expert over its
+    //    rows, the scales undone in the epilogue
+    hipError_t ew = launch_wgrad_gemm(E, a.dat, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw1, sw, amax_dab);
+    if (ew == hipSuccess)
+        ew = launch_wgrad_gemm(E, a.dat + (size_t)dff * ldk, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw3, sw,
+                               amax_dab);
+    if (ew == hipSuccess)
+        ew = launch_wgrad_gemm(E, a.dyt, a.hgt, a.offsets, uo_d, d, dff, (int)ldk, a.dw2, sw, amax_hg, amax_dy);
+    // 9. router weight and bias gradients
+    if (ew == hipSuccess)
+        hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * (d / 64))), dim3(256), 0, sw, a.xt, ldk, a.ds_of_row,
+                           a.offsets, d, a.dw_router, a.dbias);
     // 6. dx_perm = 2^k_e (da W1 + db W3): two K periods of d_ff over the
     //    dab16 row, W1 and W3 ([d_ff][d], N-contiguous, widened to fp16) in
     //    turn, at least one K slice per period; dx, the scale undone per slot
     e = launch_plain_gemm(R, cap, E, a.dab16, nullptr, 0, a.offsets, w1, w3, true, d, 2 * dff, dff, a.dx_splits,
                           a.dx_perm, a.dx_rest, st, true);
+    if (e == hipSuccess)
+        hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,
+                           static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, amax_dab, k, d, a.dx);
+    // join: the caller's stream waits for the side stream's work, also after
+    // an error, so that nothing of this call is left running unordered
+    const hipError_t el = hipGetLastError();
+    hipError_t ej = hipSuccess;
+    if (sw != st) {
+        ej = hipEventRecord(ss->join, sw);
+        if (ej == hipSuccess) ej = hipStreamWaitEvent(st, ss->join, 0);
+        if (ej != hipSuccess) ej = hipDeviceSynchronize() == hipSuccess ? hipSuccess : ej;
+    }
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,
-                       static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, amax_dab, k, d, a.dx);
-    // 7. the kept rows transposed into their experts' K windows, fp16: x,
-    //    dy (scaled by 2^k_dy), g h (from its hi/lo pair, scaled per expert)
-    kmajor(to_kmajor<1>, x, d, a.token_of_row, 0, d, a.xt, 0, 0, 0, nullptr, nullptr);
-    kmajor(to_kmajor<1>, dy, d, a.token_of_row, 0, d, a.dyt, 0, 0, 0, amax_dy, nullptr);
-    kmajor(to_kmajor<2>, a.hg, 2 * (int64_t)dff, nullptr, 0, dff, a.hgt, 0, 0, dff, amax_hg, nullptr);
-    // 8. dW1 = da^T x, dW3 = db^T x, dW2 = dy^T (g h), each expert over its
-    //    rows, the scales undone in the epilogue
-    e = launch_wgrad_gemm(E, a.dat, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw1, st, amax_dab);
-    if (e != hipSuccess) return e;
-    e = launch_wgrad_gemm(E, a.dat + (size_t)dff * ldk, a.xt, a.offsets, uo_f, dff, d, (int)ldk, a.dw3, st,
-                          amax_dab);
-    if (e != hipSuccess) return e;
-    e = launch_wgrad_gemm(E, a.dyt, a.hgt, a.offsets, uo_d, d, dff, (int)ldk, a.dw2, st, amax_hg, amax_dy);
-    if (e != hipSuccess) return e;
-    // 9. router weight and bias gradients
-    hipLaunchKernelGGL(router_wgrad, dim3((unsigned)(E * (d / 64))), dim3(256), 0, st, a.xt, ldk, a.ds_of_row,
-                       a.offsets, d, a.dw_router, a.dbias);
-    return hipGetLastError();
+    if (ew != hipSuccess) return ew;
+    return el != hipSuccess ? el : ej;
 }
 
 }  // namespace moe
