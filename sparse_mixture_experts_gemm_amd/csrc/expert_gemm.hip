@@ -666,13 +666,16 @@ __device__ __forceinline__ void store_tile(const TileInfo &ti, int n0, int N, in
                         *reinterpret_cast<uint2 *>(slice_row<uint16_t, PLAN>(out, ti, m, N) + col) =
                             make_uint2(lo, hi2);
                 } else if (m < ti.mend && col < N) {
-                    uint4 o = v;
-                    if constexpr (MODE == kPlainH)
-                        o = make_uint4(__float_as_uint(out.scale * __uint_as_float(v.x)),
-                                       __float_as_uint(out.scale * __uint_as_float(v.y)),
-                                       __float_as_uint(out.scale * __uint_as_float(v.z)),
-                                       __float_as_uint(out.scale * __uint_as_float(v.w)));
-                    *reinterpret_cast<uint4 *>(slice_row<float, PLAN>(out, ti, m, N) + col) = o;
+                    if constexpr (MODE == kPlainH) {
+                        // weight gradients: written once, never read here, so
+                        // the stores bypass L2 and leave it to the operands
+                        const f32x4_t o = {out.scale * __uint_as_float(v.x), out.scale * __uint_as_float(v.y),
+                                           out.scale * __uint_as_float(v.z), out.scale * __uint_as_float(v.w)};
+                        __builtin_nontemporal_store(
+                            o, reinterpret_cast<f32x4_t *>(slice_row<float, PLAN>(out, ti, m, N) + col));
+                    } else {
+                        *reinterpret_cast<uint4 *>(slice_row<float, PLAN>(out, ti, m, N) + col) = v;
+                    }
                 }
             }
         }
