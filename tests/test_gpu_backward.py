@@ -161,6 +161,35 @@ def test_backward_deterministic():
         assert torch.equal(a.view(torch.int32), b.view(torch.int32)), n
 
 
+def test_backward_stream_order():
+    """moe_backward runs its weight-gradient half on a stream of its own and
+    joins it back to the caller's stream: work enqueued after the call on
+    that stream (here copies of every output, with no synchronisation in
+    between) sees the finished gradients, on a non-default stream too."""
+    cfg = moe_synth.CONFIGS["skew"]
+    L = Layer(cfg, T=1024)
+    p = params(cfg, T=1024)
+    ref = forward_and_backward(L, p)
+    g = L.g
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        gr = moe.Grads(p, DEV)
+        for n in moe.Grads.NAMES:
+            getattr(gr, n).fill_(float("nan"))
+        ws = moe.alloc_backward_workspace(p, DEV)
+        copies = {}
+        for _ in range(2):
+            moe.backward(p, g["x"], g["w_router"], g["w1"], g["w3"], g["w2"], ref[0], ref[2], gr, ws, stream=s)
+            copies = {n: getattr(gr, n).clone() for n in moe.Grads.NAMES}
+            for n in moe.Grads.NAMES:  # the next call must overwrite every element again
+                getattr(gr, n).fill_(float("nan"))
+    torch.cuda.synchronize()
+    for n in moe.Grads.NAMES:
+        a, b = copies[n], getattr(ref[3], n)
+        assert torch.equal(a.view(torch.int32), b.view(torch.int32)), n
+
+
 @pytest.mark.parametrize("over", [dict(dtype="f32"), dict(router_hidden=16)])
 def test_backward_unsupported(over):
     cfg = small_cfg(T=64, dtype=over.get("dtype", "bf16"))
