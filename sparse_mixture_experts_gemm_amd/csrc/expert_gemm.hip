@@ -750,7 +750,8 @@ __global__ __launch_bounds__(kGemmThreads, 1) void grouped_gemm_bf16(
                                out.plan, ti, k0s, nks))
             return;
     } else {
-        if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti))
+        if (!find_tile(offsets, E, ntiles_n, kBM, splits, blockIdx.x, claim, reinterpret_cast<int *>(lds_a0), ti,
+                       true))
             return;
         nks = K / splits / kBK;
         k0s = ti.split * nks;

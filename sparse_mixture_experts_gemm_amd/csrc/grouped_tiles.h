@@ -16,6 +16,18 @@ struct TileInfo {
     int row0, srows;  // planned split (find_tile_planned): first split row, split rows
 };
 
+// First row (relative to the expert's first row) of m tile t when an
+// expert's n rows are cut into mt = ceil(n / bm) balanced tiles: the first
+// n % mt tiles take n / mt + 1 rows, the others n / mt, so no tile exceeds
+// bm rows and none is a sliver.  (Tiles of exactly bm rows and a short
+// last one cost nearly a full tile for the last: its weight tile streams
+// whole, and finishing early it pulls the blocks behind it out of step, so
+// they stop sharing weight tiles in L2.)
+__host__ __device__ __forceinline__ int balanced_start(int n, int mt, int t) {
+    const int q = n / mt, r = n % mt;
+    return t * q + (t < r ? t : r);
+}
+
 // Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).
 // The grid is sized by a bound on the work count; the real count comes from
 // the device-side offsets.  Each XCD is given an equal, contiguous range of
@@ -31,10 +43,12 @@ struct TileInfo {
 // claimed index passes through `slot` (one int of LDS that nothing else uses
 // until the second barrier).  Wave-parallel: lane l owns experts
 // 4l .. 4l+3 (E <= 256).  Returns false for blocks with no work (uniformly
-// over the block).
+// over the block).  balanced: the expert's rows are cut into balanced m
+// tiles (balanced_start) and ti.mend is the tile's end; otherwise tile t
+// starts at row t bm and ti.mend is the expert's end.
 __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, int E, int ntiles_n,
                                           int bm, int splits, int blk, int32_t *claim, int *slot,
-                                          TileInfo &ti) {
+                                          TileInfo &ti, bool balanced = false) {
     const int lane = lane_id();
     const int e0 = lane * 4;
     const int xcd = blk & 7, local = blk >> 3;
@@ -119,8 +133,14 @@ __device__ __forceinline__ bool find_tile(const int32_t *__restrict__ offsets, i
     ti.split = local_e / per_split;
     const int rem = local_e % per_split;
     ti.nt = rem / mt;
-    ti.m0 = beg + (rem % mt) * bm;
-    ti.mend = end;
+    if (balanced) {
+        const int t = rem % mt;
+        ti.m0 = beg + balanced_start(end - beg, mt, t);
+        ti.mend = beg + balanced_start(end - beg, mt, t + 1);
+    } else {
+        ti.m0 = beg + (rem % mt) * bm;
+        ti.mend = end;
+    }
     ti.row0 = 0;
     ti.srows = 0;
     return true;
@@ -210,11 +230,11 @@ __device__ __forceinline__ bool find_tile_planned(const int32_t *__restrict__ of
     const int nbulk = Mb * ntn;
     const int nsplit = G * ntn * S;
     // first split row: in the first expert that has split m tiles, after its
-    // bulk ones (offsets[E] when nothing is split)
+    // bulk ones (offsets[E] when nothing is split); m tiles are balanced
     int r0 = 0x7fffffff;
 #pragma unroll
     for (int j = 3; j >= 0; j--)
-        if (ml[j] > 0) r0 = ofs[j] + bm * mb[j];
+        if (ml[j] > 0) r0 = ofs[j] + balanced_start(ofs[j + 1] - ofs[j], mts[j], mb[j]);
     const uint64_t has = ballot64(ct > 0);
     const int rows_end = __builtin_amdgcn_readlane(ofs[4], 63);  // offsets[E] (lane 63's experts lie past E)
     const int row0 = has ? __builtin_amdgcn_readlane(r0, __builtin_ctzll(has)) : rows_end;
@@ -270,8 +290,9 @@ __device__ __forceinline__ bool find_tile_planned(const int32_t *__restrict__ of
                 const int r2 = rem % (cm * ntn);
                 sp_sel = rem / (cm * ntn);
                 nt_sel = r2 / cm;
-                m0_sel = ofs[j] + bm * ((split ? mb[j] : 0) + r2 % cm);
-                mend_sel = ofs[j + 1];
+                const int t = (split ? mb[j] : 0) + r2 % cm;
+                m0_sel = ofs[j] + balanced_start(ofs[j + 1] - ofs[j], mts[j], t);
+                mend_sel = ofs[j] + balanced_start(ofs[j + 1] - ofs[j], mts[j], t + 1);
                 e_sel = e0 + j;
             }
             b += cnt;

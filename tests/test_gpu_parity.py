@@ -285,8 +285,9 @@ def split_plan_row0(offsets, d, d_ff):
     """The down projection's split plan for the actual m tiles (restated from
     its definition: the tiles past whole rounds of 256 items, rounded up to
     whole m tiles, are split in K into as many slices as fit one round, at
-    most clamp(d_ff / 512, 1, 8)): (G split m tiles, S slices, first split
-    row)."""
+    most clamp(d_ff / 512, 1, 8); an expert's n rows form ceil(n / 256)
+    balanced m tiles, the first n % mt of n // mt + 1 rows, the rest of
+    n // mt): (G split m tiles, S slices, first split row)."""
     mts = [-(-(int(offsets[e + 1]) - int(offsets[e])) // 256) for e in range(len(offsets) - 1)]
     M, ntn, nk = sum(mts), -(-d // 256), d_ff // 64
     rem = (M * ntn) % 256
@@ -297,7 +298,8 @@ def split_plan_row0(offsets, d, d_ff):
     pre = 0
     for e, m in enumerate(mts):
         if pre + m > M - G:
-            return G, S, int(offsets[e]) + 256 * max(M - G - pre, 0)
+            n, t = int(offsets[e + 1]) - int(offsets[e]), max(M - G - pre, 0)
+            return G, S, int(offsets[e]) + t * (n // m) + min(t, n % m)
         pre += m
 
 
