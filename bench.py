@@ -54,8 +54,8 @@ def parse():
 CSRC = os.path.join(ROOT, "sparse_mixture_experts_gemm_amd", "csrc")
 # the source file of each stage's kernels: a committed counter summary is used
 # for a stage only while that file still has the hash recorded with it
-STAGE_SOURCE = {"route": "route.hip", "dispatch": "dispatch.hip", "expert_ffn": "expert_gemm.hip",
-                "combine": "combine.hip"}
+STAGE_SOURCE = {"route": ("route.hip",), "dispatch": ("dispatch.hip",),
+                "expert_ffn": ("expert_gemm.hip", "grouped_tiles.h"), "combine": ("combine.hip",)}
 # the kernels moe_forward launches per stage (moe_dispatch's gather is not one)
 STAGE_KERNELS = {"route": ("route_",), "dispatch": ("dispatch_hist", "dispatch_primary", "dispatch_finalize",
                                                     "dispatch_single"),
@@ -78,9 +78,9 @@ def counter_traffic(workload, qfmt=None):
         return {}
     blob = json.loads(m.group(1))
     out = {}
-    for stage, src in STAGE_SOURCE.items():
-        sha = hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
-        if blob.get("sources", {}).get(src) != sha:
+    for stage, srcs in STAGE_SOURCE.items():
+        if any(blob.get("sources", {}).get(src) != hashlib.sha256(open(os.path.join(CSRC, src), "rb").read()).hexdigest()
+               for src in srcs):
             continue
         ks = [v for k, v in blob["kernels"].items() if k.startswith(STAGE_KERNELS[stage])]
         if ks:

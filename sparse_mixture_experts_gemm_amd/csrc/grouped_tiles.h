@@ -17,15 +17,17 @@ struct TileInfo {
 };
 
 // First row (relative to the expert's first row) of m tile t when an
-// expert's n rows are cut into mt = ceil(n / bm) balanced tiles: the first
-// n % mt tiles take n / mt + 1 rows, the others n / mt, so no tile exceeds
-// bm rows and none is a sliver.  (Tiles of exactly bm rows and a short
-// last one cost nearly a full tile for the last: its weight tile streams
-// whole, and finishing early it pulls the blocks behind it out of step, so
-// they stop sharing weight tiles in L2.)
+// expert's n rows are cut into mt = ceil(n / bm) balanced tiles (bm = 256):
+// the nb = ceil(n / 32) blocks of 32 rows (the MFMA row block) are dealt
+// out evenly, the first nb % mt tiles taking nb / mt + 1 blocks and the
+// others nb / mt, and the last tile ends at row n.  No tile exceeds bm rows,
+// none is a sliver, and the tiles hold nb row blocks in all, as many as
+// tiles of bm rows would.  (Tiles of bm rows and a short last one cost
+// nearly a full tile for the last: its weight tile streams whole.)
 __host__ __device__ __forceinline__ int balanced_start(int n, int mt, int t) {
-    const int q = n / mt, r = n % mt;
-    return t * q + (t < r ? t : r);
+    const int nb = (n + 31) >> 5, q = nb / mt, r = nb % mt;
+    const int row = 32 * (t * q + (t < r ? t : r));
+    return row < n ? row : n;
 }
 
 // Blocks are dealt round-robin over the 8 XCDs (block b runs on XCD b % 8).

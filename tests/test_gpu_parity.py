@@ -285,9 +285,10 @@ def split_plan_row0(offsets, d, d_ff):
     """The down projection's split plan for the actual m tiles (restated from
     its definition: the tiles past whole rounds of 256 items, rounded up to
     whole m tiles, are split in K into as many slices as fit one round, at
-    most clamp(d_ff / 512, 1, 8); an expert's n rows form ceil(n / 256)
-    balanced m tiles, the first n % mt of n // mt + 1 rows, the rest of
-    n // mt): (G split m tiles, S slices, first split row)."""
+    most clamp(d_ff / 512, 1, 8); an expert's n rows form mt = ceil(n / 256)
+    m tiles over its ceil(n / 32) blocks of 32 rows, the first nb % mt tiles
+    of nb // mt + 1 blocks, the rest of nb // mt, the last ending at row n):
+    (G split m tiles, S slices, first split row)."""
     mts = [-(-(int(offsets[e + 1]) - int(offsets[e])) // 256) for e in range(len(offsets) - 1)]
     M, ntn, nk = sum(mts), -(-d // 256), d_ff // 64
     rem = (M * ntn) % 256
@@ -299,7 +300,8 @@ def split_plan_row0(offsets, d, d_ff):
     for e, m in enumerate(mts):
         if pre + m > M - G:
             n, t = int(offsets[e + 1]) - int(offsets[e]), max(M - G - pre, 0)
-            return G, S, int(offsets[e]) + t * (n // m) + min(t, n % m)
+            nb = -(-n // 32)
+            return G, S, int(offsets[e]) + min(n, 32 * (t * (nb // m) + min(t, nb % m)))
         pre += m
 
 
