@@ -272,7 +272,8 @@ __global__ __launch_bounds__(256) void gate_backward(const int32_t *__restrict__
 
 // dx[t] = sum over kept slots j of dx_perm[row_j] + ds_j W_r[e_j] (slot
 // order), fp32; 8 columns per thread.
-__global__ __launch_bounds__(256) void input_grad(const float *__restrict__ dx_perm, const uint16_t *__restrict__ wr,
+__global__ __launch_bounds__(256) void input_grad(const float *__restrict__ dx_perm, const float *__restrict__ rest,
+                                                  int nrest, size_t stride, const uint16_t *__restrict__ wr,
                                                   const int32_t *__restrict__ row, const int32_t *__restrict__ eid,
                                                   const float *__restrict__ ds_of_row,
                                                   const uint32_t *__restrict__ amax, int k, int d,
@@ -292,7 +293,14 @@ __global__ __launch_bounds__(256) void input_grad(const float *__restrict__ dx_p
         for (int j = 0; j < k; j++) {
             if (rws[j] < 0) continue;
             const float4 *p = reinterpret_cast<const float4 *>(dx_perm + (size_t)rws[j] * d + c);
-            const float4 v0 = p[0], v1 = p[1];
+            float4 v0 = p[0], v1 = p[1];
+            // the row's further K slices, added in slice order
+            for (int sl = 0; sl < nrest; sl++) {
+                const float4 *q = reinterpret_cast<const float4 *>(rest + sl * stride + (size_t)rws[j] * d + c);
+                const float4 u0 = q[0], u1 = q[1];
+                v0.x += u0.x; v0.y += u0.y; v0.z += u0.z; v0.w += u0.w;
+                v1.x += u1.x; v1.y += u1.y; v1.z += u1.z; v1.w += u1.w;
+            }
             const float s = sc[j];
             acc[0] += s * v0.x; acc[1] += s * v0.y; acc[2] += s * v0.z; acc[3] += s * v0.w;
             acc[4] += s * v1.x; acc[5] += s * v1.y; acc[6] += s * v1.z; acc[7] += s * v1.w;
@@ -504,11 +512,14 @@ hipError_t launch_backward(const moe_params &p, int64_t max_rows, int64_t cap, c
     // 6. dx_perm = 2^k_e (da W1 + db W3): two K periods of d_ff over the
     //    dab16 row, W1 and W3 ([d_ff][d], N-contiguous, widened to fp16) in
     //    turn, at least one K slice per period; dx, the scale undone per slot
+    //    (its K slices are left apart: input_grad adds a row's slices in
+    //    order as it reads the row, which saves the fix-up's pass)
     e = launch_plain_gemm(R, cap, E, a.dab16, nullptr, 0, a.offsets, w1, w3, true, d, 2 * dff, dff, a.dx_splits,
-                          a.dx_perm, a.dx_rest, st, true);
+                          a.dx_perm, a.dx_rest, st, true, false);
     if (e == hipSuccess)
-        hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm,
-                           static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row, amax_dab, k, d, a.dx);
+        hipLaunchKernelGGL(input_grad, dim3((unsigned)T), dim3(256), 0, st, a.dx_perm, a.dx_rest, a.dx_splits - 1,
+                           (size_t)R * d, static_cast<const uint16_t *>(a.w_router), a.row, a.eid, a.ds_of_row,
+                           amax_dab, k, d, a.dx);
     // join: the caller's stream waits for the side stream's work, also after
     // an error, so that nothing of this call is left running unordered
     const hipError_t el = hipGetLastError();

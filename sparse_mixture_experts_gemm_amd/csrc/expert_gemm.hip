@@ -1956,7 +1956,7 @@ int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb) {
 hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
                              int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, const uint16_t *B1,
                              bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st,
-                             bool a_f16) {
+                             bool a_f16, bool fixup) {
     if (max_rows <= 0) return hipSuccess;
     if (S < 1 || K % S != 0 || (K / S) % kBK != 0 || ldb % (K / S) != 0 || N % 64 != 0 ||
         a_span_bytes >= ((int64_t)1 << 31) || (int64_t)N * ldb * 2 >= ((int64_t)1 << 32))
@@ -1973,7 +1973,7 @@ hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_
         hipLaunchKernelGGL(grouped_gemm_bf16<kPlain>, dim3((unsigned)(mt * nt * S)), dim3(kGemmThreads), 0, st, A,
                            a_rows, B, B, offsets, E, N, K, ldb, nt, S, (uint32_t)a_span_bytes, (int32_t *)nullptr,
                            GemmOut{C, rest, (size_t)max_rows * N, nullptr});
-    if (S > 1) {
+    if (S > 1 && fixup) {
         const int64_t n4 = max_rows * (N / 4);
         const int grid = (int)std::min<int64_t>(ceil_div(n4, 256), 4096);
         hipLaunchKernelGGL(ffn_fixup, dim3(grid), dim3(256), 0, st, C, rest, S - 1, (size_t)max_rows * N, offsets,

@@ -168,10 +168,12 @@ hipError_t launch_gate_up_raw(const moe_params &p, int64_t max_rows, int64_t cap
 // so slices can share one B; slice s > 0 stores its partial product at
 // rest + (s - 1) max_rows N, and a fix-up adds the slices into C in order.
 // a_f16 (with b_n_contig): A holds fp16 values, and B is widened to fp16.
+// fixup false: the slices are left apart for the caller to add in order.
 int plain_gemm_splits(int64_t max_rows, int E, int N, int K, int ldb);
 hipError_t launch_plain_gemm(int64_t max_rows, int64_t cap, int E, const uint16_t *A, const int32_t *a_rows,
                              int64_t a_span_bytes, const int32_t *offsets, const uint16_t *B, const uint16_t *B1,
-                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st, bool a_f16 = false);
+                             bool b_n_contig, int N, int K, int ldb, int S, float *C, float *rest, hipStream_t st,
+                             bool a_f16 = false, bool fixup = true);
 
 // Per-expert K windows of the backward's transposed operands: the kept rows
 // of expert e (rows_e of them, from offsets[e]) become K positions
